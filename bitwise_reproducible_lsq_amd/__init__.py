@@ -1,0 +1,234 @@
+"""Python binding of libbrlsq, the bit-exact int8 LSQ linear layer and ordered
+gradient reduction for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI in include/brlsq.h.  PyTorch provides device memory
+(outputs and workspaces are torch tensors) and streams (the current torch
+stream is passed to every call).  There is no fallback: if the library is not
+built or cannot load, every call raises.
+
+Names follow the C ABI: qat_linear_fwd, qat_linear_bwd, ordered_reduce,
+grad_l2norm_clip.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbrlsq.so")
+
+BRL_OK, BRL_EINVAL, BRL_ESHAPE, BRL_EORDER, BRL_EDEVICE, BRL_EWORKSPACE = 0, -1, -2, -3, -4, -5
+EPILOGUE_NONE, EPILOGUE_SWIGLU = 0, 1
+OP_FWD, OP_BWD, OP_NORM = 0, 1, 2
+TUNE_BWD_CHUNK_LOG2, TUNE_REDUCE_WG_BLOCKS, TUNE_STREAM_WGS = 0, 1, 2
+MAX_REPLICAS = 64
+
+PROBE_OPS = {"add": 0, "sub": 1, "mul": 2, "div": 3, "sqrt": 4, "i2f": 5, "rne": 6, "exp": 7}
+
+
+class BrlError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"brlsq status {status}: {msg}")
+        self.status = status
+
+
+class ReduceStateC(C.Structure):
+    _fields_ = [("replicas", C.c_int32), ("shards", C.c_int32), ("len", C.c_int64),
+                ("next", C.c_int32), ("reserved", C.c_int32),
+                ("acc", C.c_void_p * MAX_REPLICAS)]
+
+
+_lib = None
+P, i64, i32, f32, sz = C.c_void_p, C.c_int64, C.c_int32, C.c_float, C.c_size_t
+
+_SIGS = {
+    "brl_workspace_bytes": (sz, [i32, i64, i64, i64]),
+    "qat_linear_fwd": (i32, [P, P, i64, i64, i64, f32, P, i32, P, P, P, P, sz, P]),
+    "qat_linear_bwd": (i32, [P, P, P, P, i64, i64, i64, f32, i32, P, P, i32, P, sz, P]),
+    "brl_reduce_init": (i32, [C.POINTER(ReduceStateC), i32, i32, i64, P]),
+    "ordered_reduce": (i32, [C.POINTER(ReduceStateC), P, P, P]),
+    "grad_l2norm_clip": (i32, [P, i64, f32, f32, P, P, sz, P]),
+    "brl_probe_f32": (i32, [i32, P, P, P, i64, P]),
+    "brl_set_tuning": (i64, [i32, i64]),
+    "brl_status_string": (C.c_char_p, [i32]),
+    "brl_last_error": (C.c_char_p, []),
+}
+
+
+def lib() -> C.CDLL:
+    """Load libbrlsq.so (built in-tree by build.py); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "or python bitwise_reproducible_lsq_amd/build.py")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != BRL_OK:
+        L = lib()
+        raise BrlError(status, f"{L.brl_status_string(status).decode()}: {L.brl_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("brlsq tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("brlsq tensors must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _f32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return t
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+_ws_cache: dict = {}
+
+
+def workspace(op: int, M: int, K: int, N: int, device) -> torch.Tensor:
+    """Workspace for one call (cached per device; grows as needed)."""
+    n = int(lib().brl_workspace_bytes(op, M, K, N))
+    if n == 0:
+        raise BrlError(BRL_ESHAPE, f"no workspace size for op={op} M={M} K={K} N={N}")
+    dev = torch.device(device)
+    key = (dev.type, dev.index, op)
+    w = _ws_cache.get(key)
+    if w is None or w.numel() < n:
+        w = torch.empty(n, dtype=torch.uint8, device=dev)
+        _ws_cache[key] = w
+    return w
+
+
+def workspace_bytes(op: int, M: int, K: int, N: int) -> int:
+    return int(lib().brl_workspace_bytes(op, M, K, N))
+
+
+def qat_linear_fwd(X: torch.Tensor, W: torch.Tensor, s_x: float, addend: Optional[torch.Tensor] = None,
+                   epilogue: int = EPILOGUE_NONE, want_ypre: bool = True, Y: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None, stream=None):
+    """Y = dequant(int8 GEMM) (+ addend), or the SwiGLU activation.
+    Returns (Y, Ypre or None, s_w as a 1-element device tensor)."""
+    _f32(X, "X"), _f32(W, "W")
+    M, K = X.shape
+    N, K2 = W.shape
+    if K2 != K:
+        raise ValueError("X and W disagree on K")
+    n_out = N // 2 if epilogue == EPILOGUE_SWIGLU else N
+    if Y is None:
+        Y = torch.empty((M, n_out), dtype=torch.float32, device=X.device)
+    Ypre = None
+    if epilogue == EPILOGUE_SWIGLU and want_ypre:
+        Ypre = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    s_w = torch.empty(1, dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = workspace(OP_FWD, M, K, N, X.device)
+    st = lib().qat_linear_fwd(_ptr(X), _ptr(W), M, K, N, float(s_x), _ptr(addend), epilogue, _ptr(Y),
+                              _ptr(Ypre), _ptr(s_w), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st)
+    return Y, Ypre, s_w
+
+
+def qat_linear_bwd(dOut: torch.Tensor, X: torch.Tensor, W: torch.Tensor, s_x: float,
+                   Ypre: Optional[torch.Tensor] = None, epilogue: int = EPILOGUE_NONE,
+                   need_dX: bool = True, need_dW: bool = True, dW: Optional[torch.Tensor] = None,
+                   dW_accumulate: bool = False, dX: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None, stream=None):
+    """Straight-through backward; returns (dX or None, dW or None)."""
+    M, K = X.shape
+    N = W.shape[0]
+    if need_dX and dX is None:
+        dX = torch.empty((M, K), dtype=torch.float32, device=X.device)
+    if not need_dX:
+        dX = None
+    if need_dW and dW is None:
+        if dW_accumulate:
+            raise ValueError("dW_accumulate needs the running dW")
+        dW = torch.empty((N, K), dtype=torch.float32, device=X.device)
+    if not need_dW:
+        dW = None
+    if ws is None:
+        ws = workspace(OP_BWD, M, K, N, X.device)
+    st = lib().qat_linear_bwd(_ptr(dOut), _ptr(X), _ptr(W), _ptr(Ypre), M, K, N, float(s_x), epilogue,
+                              _ptr(dX), _ptr(dW), 1 if dW_accumulate else 0, _ptr(ws), ws.numel(),
+                              _stream(stream))
+    _check(st)
+    return dX, dW
+
+
+class ReduceState:
+    """Host-side replay state: R replica accumulators A_r of `length` floats
+    (device tensors owned here) and the next virtual rank in mesh order."""
+
+    def __init__(self, replicas: int, shards: int, length: int, device="cuda",
+                 acc: Optional[Sequence[torch.Tensor]] = None):
+        if acc is None:
+            acc = [torch.empty(length, dtype=torch.float32, device=device) for _ in range(replicas)]
+        self.acc = list(acc)
+        self.c = ReduceStateC()
+        ptrs = (C.c_void_p * replicas)(*[a.data_ptr() for a in self.acc])
+        _check(lib().brl_reduce_init(C.byref(self.c), replicas, shards, length,
+                                     C.cast(ptrs, C.c_void_p)))
+
+    @property
+    def next(self) -> int:
+        return int(self.c.next)
+
+    @property
+    def total(self) -> int:
+        return int(self.c.replicas) * int(self.c.shards)
+
+    def reset(self):
+        self.c.next = 0
+
+
+def ordered_reduce(state: ReduceState, partial: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   stream=None) -> Optional[torch.Tensor]:
+    """Feed G_v for v = state.next; after the last rank returns the TreeFold."""
+    last = state.next == state.total - 1
+    if last and out is None:
+        out = torch.empty(int(state.c.len), dtype=torch.float32, device=partial.device)
+    _check(lib().ordered_reduce(C.byref(state.c), _ptr(partial), _ptr(out), _stream(stream)))
+    return out if last else None
+
+
+def grad_l2norm_clip(g: torch.Tensor, max_norm: float = 1.0, eps: float = 0.0,
+                     ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """In-place clip of g; returns the pre-clip norm as a 1-element device tensor."""
+    n = g.numel()
+    nu = torch.empty(1, dtype=torch.float32, device=g.device)
+    if ws is None:
+        ws = workspace(OP_NORM, n, 0, 0, g.device)
+    _check(lib().grad_l2norm_clip(_ptr(g), n, float(max_norm), float(eps), _ptr(nu), _ptr(ws), ws.numel(),
+                                  _stream(stream)))
+    return nu
+
+
+def probe_f32(op: str, a: torch.Tensor, b: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    out = torch.empty_like(a)
+    _check(lib().brl_probe_f32(PROBE_OPS[op], _ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)))
+    return out
+
+
+def set_tuning(knob: int, value: int) -> int:
+    """Change a launch-shape knob (never the results); returns the old value."""
+    return int(lib().brl_set_tuning(knob, value))

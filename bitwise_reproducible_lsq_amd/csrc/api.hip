@@ -1,0 +1,371 @@
+// api.hip -- the C ABI of libbrlsq (declared in include/brlsq.h): argument
+// checks, workspace carving and the launch sequence of each call.  No call
+// allocates device memory or synchronises the host.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "internal.hpp"
+
+namespace brl {
+
+// ---- tuning knobs (launch shapes only) -----------------------------------------
+static std::atomic<int64_t> g_tune[3] = {{0}, {0}, {0}};
+static const int64_t kTuneDefault[3] = {5, 256, 4096};
+
+int bwd_chunk_log2() {
+    int64_t v = g_tune[BRL_TUNE_BWD_CHUNK_LOG2].load();
+    return (int)(v > 0 ? v : kTuneDefault[BRL_TUNE_BWD_CHUNK_LOG2]);
+}
+int reduce_wg_blocks() {
+    int64_t v = g_tune[BRL_TUNE_REDUCE_WG_BLOCKS].load();
+    return (int)(v > 0 ? v : kTuneDefault[BRL_TUNE_REDUCE_WG_BLOCKS]);
+}
+int stream_wgs() {
+    int64_t v = g_tune[BRL_TUNE_STREAM_WGS].load();
+    return (int)(v > 0 ? v : kTuneDefault[BRL_TUNE_STREAM_WGS]);
+}
+
+// ---- the SwiGLU exp constants, derived from ln 2 ---------------------------------
+ExpConsts exp_constants() {
+    ExpConsts k;
+    const long double ln2 = logl(2.0L);
+    k.l2e = (float)(1.0L / ln2);
+    const long double head = floorl(ln2 * 65536.0L) / 65536.0L;   // 16 significant bits
+    k.ln2_hi = (float)head;
+    k.ln2_lo = (float)(ln2 - head);
+    long double fact = 1.0L;
+    for (int i = 0; i < 8; ++i) {
+        if (i > 1) fact *= (long double)i;
+        k.c[i] = (float)(1.0L / fact);
+    }
+    return k;
+}
+
+static thread_local char g_err[512];
+
+static brl_status fail(brl_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+static brl_status fail(brl_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+static brl_status check_hip(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(BRL_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+    return BRL_OK;
+}
+
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+// ---- workspace layout --------------------------------------------------------------
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <class T> T* take(size_t count) {
+        off = (off + 255) & ~(size_t)255;
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+struct FwdLayout {
+    int64_t Kp, Mp, Nvp;
+    Scalars* scal;
+    float* partials;
+    int8_t* qx;
+    int8_t* qw;
+    size_t bytes;
+};
+
+static FwdLayout fwd_layout(void* ws, int64_t M, int64_t K, int64_t N, int epilogue) {
+    FwdLayout L;
+    L.Kp = round_up(K, kKPad);
+    L.Mp = round_up(M, kRowPad);
+    const int64_t nv = epilogue == BRL_EPILOGUE_SWIGLU ? 2 * round_up(N / 2, kSwigluGroup) : N;
+    L.Nvp = round_up(nv, kRowPad);
+    Carver c(ws);
+    L.scal = c.take<Scalars>(1);
+    L.partials = c.take<float>((size_t)canon_partials(N * K));
+    L.qx = c.take<int8_t>((size_t)(L.Mp * L.Kp));
+    L.qw = c.take<int8_t>((size_t)(L.Nvp * L.Kp));
+    L.bytes = c.off + 256;
+    return L;
+}
+
+struct BwdLayout {
+    int64_t Kp, Mp, Np;
+    Scalars* scal;
+    float* partials;
+    int8_t* qx;
+    int8_t* qw;
+    float* G;
+    float* roots;
+    size_t bytes;
+};
+
+static BwdLayout bwd_layout(void* ws, int64_t M, int64_t K, int64_t N, int epilogue) {
+    BwdLayout L;
+    L.Kp = round_up(K, kKPad);
+    L.Mp = round_up(M, kRowPad);
+    L.Np = round_up(N, kRowPad);
+    Carver c(ws);
+    L.scal = c.take<Scalars>(1);
+    L.partials = c.take<float>((size_t)canon_partials(N * K));
+    L.qx = c.take<int8_t>((size_t)(L.Mp * L.Kp));
+    L.qw = c.take<int8_t>((size_t)(L.Np * L.Kp));
+    L.G = epilogue == BRL_EPILOGUE_SWIGLU ? c.take<float>((size_t)(M * N)) : nullptr;
+    int64_t r1 = ste_root_floats(M, N, K);   // dX: I = M, R = N
+    int64_t r2 = ste_root_floats(N, M, K);   // dW: I = N, R = M
+    L.roots = c.take<float>((size_t)(r1 > r2 ? r1 : r2));
+    L.bytes = c.off + 256;
+    return L;
+}
+
+static size_t norm_bytes(int64_t len) {
+    Carver c(nullptr);
+    c.take<Scalars>(1);
+    c.take<float>((size_t)canon_partials(len));
+    return c.off + 256;
+}
+
+static bool sizes_ok(int64_t M, int64_t K, int64_t N) {
+    const int64_t lim = (int64_t)1 << 40;
+    return M >= 0 && K >= 1 && N >= 1 && M < lim && K < lim && N < lim && M * K < lim &&
+           N * K < lim && M * N < lim;
+}
+
+}  // namespace brl
+
+using namespace brl;
+
+extern "C" {
+
+size_t brl_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N) {
+    switch (op) {
+        case BRL_OP_FWD: return sizes_ok(M, K, N) ? fwd_layout(nullptr, M, K, N, BRL_EPILOGUE_SWIGLU).bytes : 0;
+        case BRL_OP_BWD: return sizes_ok(M, K, N) ? bwd_layout(nullptr, M, K, N, BRL_EPILOGUE_SWIGLU).bytes : 0;
+        case BRL_OP_NORM: return M >= 0 ? norm_bytes(M) : 0;
+        default: return 0;
+    }
+}
+
+brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, int64_t N, float s_x,
+                          const float* addend, int32_t epilogue, float* Y, float* Ypre, float* s_w_out,
+                          void* ws, size_t ws_bytes, void* stream) {
+    if (!sizes_ok(M, K, N)) return fail(BRL_ESHAPE, "qat_linear_fwd: bad sizes M=%lld K=%lld N=%lld",
+                                        (long long)M, (long long)K, (long long)N);
+    if (K > 133144) return fail(BRL_ESHAPE, "qat_linear_fwd: K=%lld could overflow int32 accumulators", (long long)K);
+    if (epilogue != BRL_EPILOGUE_NONE && epilogue != BRL_EPILOGUE_SWIGLU)
+        return fail(BRL_EINVAL, "qat_linear_fwd: unknown epilogue %d", epilogue);
+    if (epilogue == BRL_EPILOGUE_SWIGLU && (N & 1)) return fail(BRL_ESHAPE, "qat_linear_fwd: SwiGLU needs even N");
+    if (!(s_x > 0.0f) || !isfinite(s_x)) return fail(BRL_EINVAL, "qat_linear_fwd: s_x must be finite and > 0");
+    if (!W || (M > 0 && (!X || !Y))) return fail(BRL_EINVAL, "qat_linear_fwd: null tensor");
+    if (!aligned4(X) || !aligned4(W) || !aligned4(Y) || !aligned4(addend) || !aligned4(Ypre) || !aligned4(s_w_out))
+        return fail(BRL_EINVAL, "qat_linear_fwd: pointers must be 4-byte aligned");
+    const FwdLayout need = fwd_layout(nullptr, M, K, N, BRL_EPILOGUE_SWIGLU);
+    if (!ws || ws_bytes < need.bytes)
+        return fail(BRL_EWORKSPACE, "qat_linear_fwd: workspace %zu < %zu bytes", ws_bytes, need.bytes);
+    FwdLayout L = fwd_layout(ws, M, K, N, epilogue);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    CanonFinishArgs fin{};
+    fin.mode = kFinishScale;
+    fin.count_f = (float)(double)(N * K);
+    fin.s_x = s_x;
+    fin.scal = L.scal;
+    fin.s_w_out = s_w_out;
+    brl_status s = check_hip(launch_canon(kMapAbs, W, N * K, L.partials, fin, st), "weight step");
+    if (s || M == 0) return s;
+    s = check_hip(launch_quantize(W, N, K, &L.scal->s_w, 0.0f, L.qw, L.Nvp, L.Kp,
+                                  epilogue == BRL_EPILOGUE_SWIGLU ? N / 2 : 0, st), "quantize W");
+    if (s) return s;
+    s = check_hip(launch_quantize(X, M, K, nullptr, s_x, L.qx, L.Mp, L.Kp, 0, st), "quantize X");
+    if (s) return s;
+    GemmArgs g{};
+    g.qx = L.qx; g.qw = L.qw; g.M = M; g.N = N; g.Kp = L.Kp; g.Mp = L.Mp; g.Nvp = L.Nvp;
+    g.scal = L.scal; g.addend = addend; g.Y = Y; g.Ypre = Ypre; g.epilogue = epilogue;
+    g.ek = exp_constants();
+    return check_hip(launch_gemm_i8(g, st), "int8 GEMM");
+}
+
+brl_status qat_linear_bwd(const float* dOut, const float* X, const float* W, const float* Ypre,
+                          int64_t M, int64_t K, int64_t N, float s_x, int32_t epilogue, float* dX,
+                          float* dW, int32_t dW_accumulate, void* ws, size_t ws_bytes, void* stream) {
+    if (!sizes_ok(M, K, N)) return fail(BRL_ESHAPE, "qat_linear_bwd: bad sizes M=%lld K=%lld N=%lld",
+                                        (long long)M, (long long)K, (long long)N);
+    if (epilogue != BRL_EPILOGUE_NONE && epilogue != BRL_EPILOGUE_SWIGLU)
+        return fail(BRL_EINVAL, "qat_linear_bwd: unknown epilogue %d", epilogue);
+    if (epilogue == BRL_EPILOGUE_SWIGLU && (N & 1)) return fail(BRL_ESHAPE, "qat_linear_bwd: SwiGLU needs even N");
+    if (!(s_x > 0.0f) || !isfinite(s_x)) return fail(BRL_EINVAL, "qat_linear_bwd: s_x must be finite and > 0");
+    if (!W || (M > 0 && (!X || !dOut)) || (epilogue == BRL_EPILOGUE_SWIGLU && M > 0 && !Ypre))
+        return fail(BRL_EINVAL, "qat_linear_bwd: null tensor");
+    if (dW_accumulate != 0 && dW_accumulate != 1) return fail(BRL_EINVAL, "qat_linear_bwd: dW_accumulate must be 0 or 1");
+    if (!aligned4(dOut) || !aligned4(X) || !aligned4(W) || !aligned4(Ypre) || !aligned4(dX) || !aligned4(dW))
+        return fail(BRL_EINVAL, "qat_linear_bwd: pointers must be 4-byte aligned");
+    const int64_t Qx = ste_chunks(N), Qw = ste_chunks(M);
+    if (Qx > 1024 || Qw > 1024)
+        return fail(BRL_ESHAPE, "qat_linear_bwd: reduction too long for the chunk setting (%lld, %lld chunks)",
+                    (long long)Qx, (long long)Qw);
+    const BwdLayout need = bwd_layout(nullptr, M, K, N, BRL_EPILOGUE_SWIGLU);
+    if (!ws || ws_bytes < need.bytes)
+        return fail(BRL_EWORKSPACE, "qat_linear_bwd: workspace %zu < %zu bytes", ws_bytes, need.bytes);
+    BwdLayout L = bwd_layout(ws, M, K, N, epilogue);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    CanonFinishArgs fin{};
+    fin.mode = kFinishScale;
+    fin.count_f = (float)(double)(N * K);
+    fin.s_x = s_x;
+    fin.scal = L.scal;
+    brl_status s = check_hip(launch_canon(kMapAbs, W, N * K, L.partials, fin, st), "weight step");
+    if (s) return s;
+    s = check_hip(launch_quantize(W, N, K, &L.scal->s_w, 0.0f, L.qw, L.Np, L.Kp, 0, st), "quantize W");
+    if (s) return s;
+    s = check_hip(launch_quantize(X, M, K, nullptr, s_x, L.qx, L.Mp, L.Kp, 0, st), "quantize X");
+    if (s) return s;
+    const float* G = dOut;
+    if (epilogue == BRL_EPILOGUE_SWIGLU && M > 0) {
+        s = check_hip(launch_swiglu_bwd(dOut, Ypre, M, N, L.G, exp_constants(), st), "SwiGLU backward");
+        if (s) return s;
+        G = L.G;
+    }
+    if (dX && M > 0) {
+        SteArgs a{};
+        a.A = G; a.lda = N; a.a_rmaj = true; a.I = M; a.R = N; a.Jn = K;
+        a.Bq = L.qw; a.ldb = L.Kp; a.b_scale_dev = &L.scal->s_w;
+        a.mask_src = X; a.mask_scale_dev = nullptr; a.mask_scale_host = s_x;
+        a.out = dX; a.accumulate = 0; a.roots = L.roots;
+        s = check_hip(launch_ste(a, st), "dX");
+        if (s) return s;
+    }
+    if (dW) {
+        SteArgs a{};
+        a.A = G; a.lda = N; a.a_rmaj = false; a.I = N; a.R = M; a.Jn = K;
+        a.Bq = L.qx; a.ldb = L.Kp; a.b_scale_dev = nullptr; a.b_scale_host = s_x;
+        a.mask_src = W; a.mask_scale_dev = &L.scal->s_w;
+        a.out = dW; a.accumulate = dW_accumulate; a.roots = L.roots;
+        s = check_hip(launch_ste(a, st), "dW");
+        if (s) return s;
+    }
+    return BRL_OK;
+}
+
+brl_status brl_reduce_init(brl_reduce_state* st, int32_t replicas, int32_t shards, int64_t len,
+                           float* const* acc) {
+    if (!st || !acc) return fail(BRL_EINVAL, "brl_reduce_init: null argument");
+    if (replicas < 1 || replicas > BRL_MAX_REPLICAS || shards < 1 || len < 0 ||
+        (int64_t)replicas * shards > (int64_t)1 << 30)
+        return fail(BRL_ESHAPE, "brl_reduce_init: bad mesh %d x %d or length", replicas, shards);
+    memset(st, 0, sizeof(*st));
+    st->replicas = replicas;
+    st->shards = shards;
+    st->len = len;
+    st->next = 0;
+    for (int r = 0; r < replicas; ++r) {
+        if (!acc[r] && len > 0) return fail(BRL_EINVAL, "brl_reduce_init: null buffer for replica %d", r);
+        if (!aligned4(acc[r])) return fail(BRL_EINVAL, "brl_reduce_init: misaligned buffer");
+        st->acc[r] = acc[r];
+    }
+    return BRL_OK;
+}
+
+brl_status ordered_reduce(brl_reduce_state* sp, const float* partial, float* out, void* stream) {
+    if (!sp) return fail(BRL_EINVAL, "ordered_reduce: null state");
+    const int R = sp->replicas, S = sp->shards;
+    if (R < 1 || R > BRL_MAX_REPLICAS || S < 1 || sp->len < 0)
+        return fail(BRL_EINVAL, "ordered_reduce: state not initialised");
+    const int64_t total = (int64_t)R * S;
+    if (sp->next < 0 || sp->next >= total)
+        return fail(BRL_EORDER, "ordered_reduce: all %lld virtual ranks already reduced", (long long)total);
+    const int64_t v = sp->next;
+    const int r = (int)(v / S), s = (int)(v % S);
+    const bool last = v == total - 1;
+    const int64_t n = sp->len;
+    if (n > 0 && !partial) return fail(BRL_EINVAL, "ordered_reduce: null partial");
+    if (last && n > 0 && !out) return fail(BRL_EINVAL, "ordered_reduce: last rank needs out");
+    if (!aligned4(partial) || !aligned4(out)) return fail(BRL_EINVAL, "ordered_reduce: misaligned pointer");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    brl_status rc = BRL_OK;
+    if (n > 0) {
+        if (!last) {
+            if (s == 0)
+                rc = check_hip(hipMemcpyAsync(sp->acc[r], partial, (size_t)n * sizeof(float),
+                                              hipMemcpyDeviceToDevice, st), "running sum (first shard)");
+            else
+                rc = check_hip(launch_accumulate(sp->acc[r], partial, n, st), "running sum");
+        } else {
+            FoldPtrs p{};
+            for (int i = 0; i < R; ++i) p.a[i] = sp->acc[i];
+            const float* g_last = partial;
+            if (s == 0) { p.a[R - 1] = partial; g_last = nullptr; }
+            rc = check_hip(launch_fold(p, R, g_last, out, n, st), "TreeFold");
+        }
+    }
+    if (rc == BRL_OK) sp->next = (int32_t)(v + 1);
+    return rc;
+}
+
+brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float eps, float* norm_out, void* ws,
+                            size_t ws_bytes, void* stream) {
+    if (len < 0 || len > ((int64_t)1 << 40)) return fail(BRL_ESHAPE, "grad_l2norm_clip: bad length");
+    if (len > 0 && !g) return fail(BRL_EINVAL, "grad_l2norm_clip: null gradient");
+    if (!(max_norm > 0.0f) || !isfinite(max_norm) || !(eps >= 0.0f) || !isfinite(eps))
+        return fail(BRL_EINVAL, "grad_l2norm_clip: max_norm must be finite > 0 and eps finite >= 0");
+    if (!aligned4(g) || !aligned4(norm_out)) return fail(BRL_EINVAL, "grad_l2norm_clip: misaligned pointer");
+    const size_t need = norm_bytes(len);
+    if (!ws || ws_bytes < need)
+        return fail(BRL_EWORKSPACE, "grad_l2norm_clip: workspace %zu < %zu bytes", ws_bytes, need);
+    Carver c(ws);
+    Scalars* scal = c.take<Scalars>(1);
+    float* partials = c.take<float>((size_t)canon_partials(len));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    CanonFinishArgs fin{};
+    fin.mode = kFinishNorm;
+    fin.max_norm = max_norm;
+    fin.eps = eps;
+    fin.scal = scal;
+    fin.nu_out = norm_out;
+    brl_status s = check_hip(launch_canon(kMapSquare, g, len, partials, fin, st), "squared norm");
+    if (s) return s;
+    return check_hip(launch_clip(g, len, scal, st), "clip");
+}
+
+brl_status brl_probe_f32(int32_t op, const float* a, const float* b, float* out, int64_t n, void* stream) {
+    if (op < 0 || op > 7) return fail(BRL_EINVAL, "brl_probe_f32: unknown op %d", op);
+    if (n < 0) return fail(BRL_ESHAPE, "brl_probe_f32: n < 0");
+    if (n > 0 && (!a || !out || (op <= 3 && !b))) return fail(BRL_EINVAL, "brl_probe_f32: null pointer");
+    return check_hip(launch_probe(op, a, b, out, n, exp_constants(), static_cast<hipStream_t>(stream)), "probe");
+}
+
+int64_t brl_set_tuning(int32_t knob, int64_t value) {
+    if (knob < 0 || knob > 2) return -1;
+    if (knob == BRL_TUNE_BWD_CHUNK_LOG2 && value > 6) value = 6;
+    if (knob == BRL_TUNE_REDUCE_WG_BLOCKS && value > 0 && value != 64 && value != 128 && value != 256)
+        value = 256;
+    int64_t old = g_tune[knob].exchange(value > 0 ? value : 0);
+    return old > 0 ? old : kTuneDefault[knob];
+}
+
+const char* brl_status_string(brl_status s) {
+    switch (s) {
+        case BRL_OK: return "ok";
+        case BRL_EINVAL: return "invalid argument";
+        case BRL_ESHAPE: return "bad shape";
+        case BRL_EORDER: return "out of mesh order";
+        case BRL_EDEVICE: return "device error";
+        case BRL_EWORKSPACE: return "workspace too small";
+        default: return "unknown status";
+    }
+}
+
+const char* brl_last_error(void) { return g_err; }
+
+}  // extern "C"

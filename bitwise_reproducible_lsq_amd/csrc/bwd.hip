@@ -1,0 +1,302 @@
+// bwd.hip -- straight-through backward of the int8 LSQ linear layer on gfx950.
+//
+// dX[m,k] = in_x ? CanonSum_n(G[m,n] * What[n,k]) : +0
+// dW[n,k] = in_w ? CanonSum_m(G[m,n] * Xhat[m,k]) : +0
+// with What = fl(q_w*s_w), Xhat = fl(q_x*s_x) and CanonSum the method's fixed
+// order (Open-1B summary on onedev.kr, "How": one reduction order, multiply
+// and add never fused, FTZ).  Every product is rounded on its own and every
+// add is one binary32 add in a fixed sequence, so the matrix cores cannot be
+// used; this is a register-blocked VALU contraction.
+//
+// Kernel ste_chunk_kernel<A_RMAJ, D>: a workgroup of 256 threads owns a 64x64
+// output tile and one chunk of 2^D consecutive 32-blocks of the reduction.
+// Each thread holds 4x4 outputs.  Per 32-block it streams the block's 32
+// reduction steps from LDS (A as [i][r] with pitch 36, B as [r][j] with pitch
+// 68, both double-buffered), forming the 16 block sums left to right from the
+// first product; finished block sums enter a binary-counter stack of depth D
+// held in registers, which builds exactly the pairwise tree of the chunk.  An
+// aligned run of 2^D blocks is a complete subtree of the canonical tree (a
+// short last run is the canonical tree of its own blocks), so the chunk roots
+// combined by the same pairwise tree (ste_finish_kernel) give the canonical
+// result for any D.  Reduction steps past the end read A = -0 and B = +0,
+// whose product -0 leaves every binary32 sum unchanged.
+#include "internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace brl {
+
+constexpr int kTile = 64;         // output tile edge per workgroup
+constexpr int kPitchA = 36;       // floats per LDS row of A ([i][32 r] + pad)
+constexpr int kPitchB = 68;       // floats per LDS row of B ([r][64 j] + pad)
+constexpr int kFinishLevels = 10; // finish pass handles up to 2^10 chunk roots
+
+// Binary-counter stack: after block index bi (0-based) completes with value t,
+// merge it with the stored subtrees of equal size.  st[L] is valid while bit L
+// of the completed-block count is set.
+template <int NV, int L, int D>
+__device__ __forceinline__ void stack_push(float (&st)[D + 1][NV], float (&t)[NV], unsigned bi) {
+    if constexpr (L == D) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) st[D][k] = t[k];
+    } else {
+        if (bi & (1u << L)) {
+#pragma unroll
+            for (int k = 0; k < NV; ++k) t[k] = f_add(st[L][k], t[k]);
+            stack_push<NV, L + 1, D>(st, t, bi);
+        } else {
+#pragma unroll
+            for (int k = 0; k < NV; ++k) st[L][k] = t[k];
+        }
+    }
+}
+
+// Final right-to-left merge of the stored subtrees for `count` blocks.
+template <int NV, int D>
+__device__ __forceinline__ void stack_final(float (&st)[D + 1][NV], unsigned count, float (&root)[NV]) {
+    bool have = false;
+#pragma unroll
+    for (int L = 0; L <= D; ++L) {
+        if (count & (1u << L)) {
+#pragma unroll
+            for (int k = 0; k < NV; ++k) root[k] = have ? f_add(st[L][k], root[k]) : st[L][k];
+            have = true;
+        }
+    }
+}
+
+__device__ __forceinline__ float mask_select(float v, const float* src, int64_t idx,
+                                             const float* s_dev, float s_host) {
+    const float s = s_dev ? *s_dev : s_host;
+    return quantize_in_range(src[idx], s) ? v : 0.0f;
+}
+
+template <bool A_RMAJ, int D>
+__global__ __launch_bounds__(256) void ste_chunk_kernel(SteArgs a, int64_t nblk, int final_out) {
+    __shared__ __attribute__((aligned(16))) float As[2][kTile * kPitchA];
+    __shared__ __attribute__((aligned(16))) float Bs[2][kBlock * kPitchB];
+
+    const int tid = threadIdx.x;
+    const int tj = tid & 15, ti = tid >> 4;
+    const int64_t j0 = (int64_t)blockIdx.x * kTile;
+    const int64_t i0 = (int64_t)blockIdx.y * kTile;
+    const int64_t chunk = blockIdx.z;
+    const int64_t b_begin = chunk << D;
+    const int64_t b_end = (b_begin + (1 << D)) < nblk ? (b_begin + (1 << D)) : nblk;
+    const float bscale = a.b_scale_dev ? *a.b_scale_dev : a.b_scale_host;
+
+    // global -> register staging for one 32-block
+    float ra[8];
+    uint2 rb;
+    auto gload = [&](int64_t blk) {
+        const int64_t r0 = blk * kBlock;
+        if constexpr (A_RMAJ) {
+            // A(r, i) = A[i*lda + r]: row ii, 8 consecutive r
+            const int ii = tid >> 2, seg = (tid & 3) * 8;
+            const int64_t i = i0 + ii, r = r0 + seg;
+            const float* p = a.A + i * a.lda + r;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ra[e] = (i < a.I && r + e < a.R) ? p[e] : -0.0f;
+        } else {
+            // A(r, i) = A[r*lda + i]: row rr, 8 consecutive i
+            const int rr = tid >> 3, seg = (tid & 7) * 8;
+            const int64_t r = r0 + rr, i = i0 + seg;
+            const float* p = a.A + r * a.lda + i;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ra[e] = (r < a.R && i + e < a.I) ? p[e] : -0.0f;
+        }
+        {
+            const int rr = tid >> 3, seg = (tid & 7) * 8;
+            rb = *reinterpret_cast<const uint2*>(a.Bq + (r0 + rr) * a.ldb + j0 + seg);
+        }
+    };
+    auto sstore = [&](int buf) {
+        if constexpr (A_RMAJ) {
+            const int ii = tid >> 2, seg = (tid & 3) * 8;
+            float4* d = reinterpret_cast<float4*>(&As[buf][ii * kPitchA + seg]);
+            d[0] = make_float4(ra[0], ra[1], ra[2], ra[3]);
+            d[1] = make_float4(ra[4], ra[5], ra[6], ra[7]);
+        } else {
+            const int rr = tid >> 3, seg = (tid & 7) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) As[buf][(seg + e) * kPitchA + rr] = ra[e];
+        }
+        {
+            const int rr = tid >> 3, seg = (tid & 7) * 8;
+            float f[8];
+            const uint32_t w0 = rb.x, w1 = rb.y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[e] = f_mul((float)(int8_t)(w0 >> (8 * e)), bscale);
+                f[4 + e] = f_mul((float)(int8_t)(w1 >> (8 * e)), bscale);
+            }
+            float4* d = reinterpret_cast<float4*>(&Bs[buf][rr * kPitchB + seg]);
+            d[0] = make_float4(f[0], f[1], f[2], f[3]);
+            d[1] = make_float4(f[4], f[5], f[6], f[7]);
+        }
+    };
+
+    float st[D + 1][16];
+    float acc[16];
+
+    gload(b_begin);
+    sstore(0);
+    __syncthreads();
+
+    for (int64_t blk = b_begin; blk < b_end; ++blk) {
+        const int cur = (int)((blk - b_begin) & 1);
+        if (blk + 1 < b_end) gload(blk + 1);
+        const float* Ab = &As[cur][0];
+        const float* Bb = &Bs[cur][tj * 4];
+#pragma unroll
+        for (int rs = 0; rs < kBlock; rs += 4) {
+            float4 av[4], bv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) av[q] = *reinterpret_cast<const float4*>(Ab + (ti + 16 * q) * kPitchA + rs);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) bv[s] = *reinterpret_cast<const float4*>(Bb + (rs + s) * kPitchB);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float x = s == 0 ? av[q].x : s == 1 ? av[q].y : s == 2 ? av[q].z : av[q].w;
+                    const float p0 = f_mul(x, bv[s].x), p1 = f_mul(x, bv[s].y);
+                    const float p2 = f_mul(x, bv[s].z), p3 = f_mul(x, bv[s].w);
+                    if (rs == 0 && s == 0) {
+                        acc[4 * q + 0] = p0; acc[4 * q + 1] = p1;
+                        acc[4 * q + 2] = p2; acc[4 * q + 3] = p3;
+                    } else {
+                        acc[4 * q + 0] = f_add(acc[4 * q + 0], p0);
+                        acc[4 * q + 1] = f_add(acc[4 * q + 1], p1);
+                        acc[4 * q + 2] = f_add(acc[4 * q + 2], p2);
+                        acc[4 * q + 3] = f_add(acc[4 * q + 3], p3);
+                    }
+                }
+            }
+        }
+        stack_push<16, 0, D>(st, acc, (unsigned)(blk - b_begin));
+        if (blk + 1 < b_end) sstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    float root[16];
+    stack_final<16, D>(st, (unsigned)(b_end - b_begin), root);
+
+    const int64_t plane = a.I * a.Jn;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t i = i0 + ti + 16 * q;
+        if (i >= a.I) continue;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int64_t j = j0 + tj * 4 + c;
+            if (j >= a.Jn) continue;
+            const int64_t idx = i * a.Jn + j;
+            float v = root[4 * q + c];
+            if (final_out) {
+                v = mask_select(v, a.mask_src, idx, a.mask_scale_dev, a.mask_scale_host);
+                if (a.accumulate) v = f_add(a.out[idx], v);
+                a.out[idx] = v;
+            } else {
+                a.roots[chunk * plane + idx] = v;
+            }
+        }
+    }
+}
+
+// Pairwise tree over the Q chunk roots of each output, then mask (+ running sum).
+__global__ __launch_bounds__(256) void ste_finish_kernel(SteArgs a, int64_t Q) {
+    const int64_t plane = a.I * a.Jn;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= plane) return;
+    float st[kFinishLevels + 1][1];
+    for (int64_t c = 0; c < Q; ++c) {
+        float t[1] = {a.roots[c * plane + idx]};
+        stack_push<1, 0, kFinishLevels>(st, t, (unsigned)c);
+    }
+    float root[1];
+    stack_final<1, kFinishLevels>(st, (unsigned)Q, root);
+    float v = mask_select(root[0], a.mask_src, idx, a.mask_scale_dev, a.mask_scale_host);
+    if (a.accumulate) v = f_add(a.out[idx], v);
+    a.out[idx] = v;
+}
+
+int64_t ste_chunks(int64_t R) {
+    return ceil_div(ceil_div(R, kBlock), (int64_t)1 << bwd_chunk_log2());
+}
+
+int64_t ste_root_floats(int64_t I, int64_t R, int64_t Jn) {
+    const int64_t Q = ste_chunks(R);
+    return Q > 1 ? Q * I * Jn : 0;
+}
+
+// Empty reduction (no rows): every output is CanonSum of nothing = +0.
+__global__ __launch_bounds__(256) void ste_empty_kernel(float* __restrict__ out, int64_t n, int accumulate) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= n) return;
+    out[idx] = accumulate ? f_add(out[idx], 0.0f) : 0.0f;
+}
+
+template <bool A_RMAJ>
+static void ste_launch_chunk(const SteArgs& a, int D, dim3 grid, int64_t nblk, int final_out, hipStream_t st) {
+    switch (D) {
+        case 1: hipLaunchKernelGGL((ste_chunk_kernel<A_RMAJ, 1>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+        case 2: hipLaunchKernelGGL((ste_chunk_kernel<A_RMAJ, 2>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+        case 3: hipLaunchKernelGGL((ste_chunk_kernel<A_RMAJ, 3>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+        case 4: hipLaunchKernelGGL((ste_chunk_kernel<A_RMAJ, 4>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+        case 6: hipLaunchKernelGGL((ste_chunk_kernel<A_RMAJ, 6>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+        default: hipLaunchKernelGGL((ste_chunk_kernel<A_RMAJ, 5>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+    }
+}
+
+hipError_t launch_ste(const SteArgs& a, hipStream_t st) {
+    if (a.I <= 0 || a.Jn <= 0) return hipSuccess;
+    const int D = bwd_chunk_log2();
+    const int64_t nblk = ceil_div(a.R, kBlock);
+    if (nblk == 0) {
+        const int64_t plane = a.I * a.Jn;
+        hipLaunchKernelGGL(ste_empty_kernel, dim3((unsigned)ceil_div(plane, 256)), dim3(256), 0, st,
+                           a.out, plane, a.accumulate);
+        return hipGetLastError();
+    }
+    const int64_t Q = ceil_div(nblk, (int64_t)1 << D);
+    dim3 grid((unsigned)ceil_div(a.Jn, kTile), (unsigned)ceil_div(a.I, kTile), (unsigned)Q);
+    const int final_out = Q == 1;
+    if (a.a_rmaj) ste_launch_chunk<true>(a, D, grid, nblk, final_out, st);
+    else ste_launch_chunk<false>(a, D, grid, nblk, final_out, st);
+    if (!final_out) {
+        const int64_t plane = a.I * a.Jn;
+        hipLaunchKernelGGL(ste_finish_kernel, dim3((unsigned)ceil_div(plane, 256)), dim3(256), 0, st, a, Q);
+    }
+    return hipGetLastError();
+}
+
+// ---- SwiGLU backward (pre-activation gradient) ---------------------------------
+// du = dA*h, dg = (dA*u) * (s*(1 + g*(1 - s))), s = 1/(1 + E(-g)), h = g*s.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ dA,
+                                                         const float* __restrict__ ypre, int64_t M,
+                                                         int64_t N, float* __restrict__ G, ExpConsts ek) {
+    const int64_t H = N / 2;
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= H) return;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        const float g = ypre[m * N + j], u = ypre[m * N + H + j], d = dA[m * H + j];
+        const float s = swiglu_sigma(g, ek);
+        const float h = f_mul(g, s);
+        G[m * N + H + j] = f_mul(d, h);
+        const float ds = f_mul(s, f_add(1.0f, f_mul(g, f_sub(1.0f, s))));
+        G[m * N + j] = f_mul(f_mul(d, u), ds);
+    }
+}
+
+hipError_t launch_swiglu_bwd(const float* dA, const float* ypre, int64_t M, int64_t N, float* G,
+                             const ExpConsts& ek, hipStream_t st) {
+    const int64_t H = N / 2;
+    if (M <= 0 || H <= 0) return hipSuccess;
+    const unsigned gy = (unsigned)(M < 65535 ? M : 65535);
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)ceil_div(H, 256), gy), dim3(256), 0, st, dA,
+                       ypre, M, N, G, ek);
+    return hipGetLastError();
+}
+
+}  // namespace brl

@@ -1,0 +1,145 @@
+// canon.hip -- CanonSum of a flat vector (weight-step mean of |w|, gradient
+// squared norm), in the order the method fixes for every reduction (Open-1B
+// summary on onedev.kr, "How"): 32-wide blocks summed left to right from their
+// first term, then a level-by-level pairwise tree over the block sums.
+//
+// Work split: pass 1 gives each workgroup an aligned run of WGB block sums and
+// reduces them to one subtree root; later passes reduce aligned runs of WGB
+// roots.  Aligned power-of-two runs are complete subtrees of the canonical
+// tree (and a short final run is the canonical tree of its own leaves), so the
+// result is independent of WGB.  The last pass also computes the scalar that
+// follows the sum (weight step, or norm and clip coefficient).
+#include "internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace brl {
+
+template <int MAP>
+__device__ __forceinline__ float canon_map(float v) {
+    if constexpr (MAP == kMapAbs) return __builtin_fabsf(v);
+    else return f_mul(v, v);
+}
+
+__device__ void canon_finish(float S, const CanonFinishArgs& f) {
+    if (f.mode == kFinishScale) {
+        float mu = f_div(S, f.count_f);
+        float s_w = f_div(f_mul(2.0f, mu), f_sqrt((float)kQmax));
+        f.scal->s_w = s_w;
+        f.scal->s_y = f_mul(f.s_x, s_w);
+        if (f.s_w_out) *f.s_w_out = s_w;
+    } else {
+        float nu = f_sqrt(S);
+        int clip = nu > f.max_norm;
+        f.scal->nu = nu;
+        f.scal->clip = clip;
+        f.scal->kappa = clip ? f_div(f.max_norm, f_add(nu, f.eps)) : 1.0f;
+        if (f.nu_out) *f.nu_out = nu;
+    }
+}
+
+// Pass 1: thread t of workgroup w sums block j = w*WGB + t.
+template <int MAP, int WGB>
+__global__ __launch_bounds__(WGB) void canon_pass1_kernel(const float* __restrict__ x, int64_t n,
+                                                         float* __restrict__ roots, int last,
+                                                         CanonFinishArgs fin) {
+    __shared__ float lds[WGB];
+    const int64_t J = (n + kBlock - 1) / kBlock;
+    const int64_t j = (int64_t)blockIdx.x * WGB + threadIdx.x;
+    float s = 0.0f;
+    if (j < J) {
+        const int64_t base = j * kBlock;
+        const float* p = x + base;
+        const int64_t len = (n - base) < kBlock ? (n - base) : kBlock;
+        if (len == kBlock && ((reinterpret_cast<uintptr_t>(p) & 15) == 0)) {
+            const vf4* p4 = reinterpret_cast<const vf4*>(p);
+            vf4 v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = __builtin_nontemporal_load(p4 + q);
+            s = canon_map<MAP>(v[0].x);
+            s = f_add(s, canon_map<MAP>(v[0].y));
+            s = f_add(s, canon_map<MAP>(v[0].z));
+            s = f_add(s, canon_map<MAP>(v[0].w));
+#pragma unroll
+            for (int q = 1; q < 8; ++q) {
+                s = f_add(s, canon_map<MAP>(v[q].x));
+                s = f_add(s, canon_map<MAP>(v[q].y));
+                s = f_add(s, canon_map<MAP>(v[q].z));
+                s = f_add(s, canon_map<MAP>(v[q].w));
+            }
+        } else {
+            s = canon_map<MAP>(p[0]);
+            for (int64_t i = 1; i < len; ++i) s = f_add(s, canon_map<MAP>(p[i]));
+        }
+    }
+    int64_t rem = J - (int64_t)blockIdx.x * WGB;
+    const int count = rem < WGB ? (int)(rem < 0 ? 0 : rem) : WGB;
+    float r = wg_pair_tree(s, count, lds);
+    if (threadIdx.x == 0) {
+        if (last) canon_finish(r, fin);
+        else roots[blockIdx.x] = r;
+    }
+}
+
+// Later passes: aligned runs of WGB roots.
+template <int WGB>
+__global__ __launch_bounds__(WGB) void canon_tree_kernel(const float* __restrict__ in, int64_t Q,
+                                                        float* __restrict__ out, int last,
+                                                        CanonFinishArgs fin) {
+    __shared__ float lds[WGB];
+    const int64_t j = (int64_t)blockIdx.x * WGB + threadIdx.x;
+    float s = j < Q ? in[j] : 0.0f;
+    int64_t rem = Q - (int64_t)blockIdx.x * WGB;
+    const int count = rem < WGB ? (int)rem : WGB;
+    float r = wg_pair_tree(s, count, lds);
+    if (threadIdx.x == 0) {
+        if (last) canon_finish(r, fin);
+        else out[blockIdx.x] = r;
+    }
+}
+
+int64_t canon_partials(int64_t n) {
+    const int64_t wgb = 64;   // smallest allowed WGB gives the largest count
+    int64_t J = ceil_div(n, kBlock);
+    int64_t q = ceil_div(J, wgb);
+    int64_t total = q + 1;
+    while (q > 1) { q = ceil_div(q, wgb); total += q + 1; }
+    return total + 64;
+}
+
+template <int WGB>
+static hipError_t canon_run(int map, const float* x, int64_t n, float* partials,
+                            const CanonFinishArgs& fin, hipStream_t st) {
+    const int64_t J = ceil_div(n, kBlock);
+    int64_t q = J > 0 ? ceil_div(J, WGB) : 1;
+    int last = q == 1;
+    if (map == kMapAbs)
+        hipLaunchKernelGGL((canon_pass1_kernel<kMapAbs, WGB>), dim3((unsigned)q), dim3(WGB), 0, st,
+                           x, n, partials, last, fin);
+    else
+        hipLaunchKernelGGL((canon_pass1_kernel<kMapSquare, WGB>), dim3((unsigned)q), dim3(WGB), 0, st,
+                           x, n, partials, last, fin);
+    float* in = partials;
+    float* out = partials + q + 1;
+    while (q > 1) {
+        int64_t nq = ceil_div(q, WGB);
+        last = nq == 1;
+        hipLaunchKernelGGL((canon_tree_kernel<WGB>), dim3((unsigned)nq), dim3(WGB), 0, st,
+                           in, q, out, last, fin);
+        in = out;
+        out = out + nq + 1;
+        q = nq;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_canon(int map, const float* x, int64_t n, float* partials,
+                        const CanonFinishArgs& fin, hipStream_t st) {
+    switch (reduce_wg_blocks()) {
+        case 64: return canon_run<64>(map, x, n, partials, fin, st);
+        case 128: return canon_run<128>(map, x, n, partials, fin, st);
+        default: return canon_run<256>(map, x, n, partials, fin, st);
+    }
+}
+
+}  // namespace brl

@@ -1,0 +1,120 @@
+// device.hpp -- binary32 building blocks shared by the gfx950 kernels.
+//
+// Numerics (Open-1B summary on onedev.kr, section "How"): one fixed reduction
+// order, multiply and add never fused, subnormals flushed to zero.  The
+// kernels are compiled with the f32 denormal mode "flush inputs and outputs"
+// and contraction off, so a plain `a + b` / `a * b` is one v_add_f32 /
+// v_mul_f32 that rounds to nearest even and flushes.  Division and square
+// root go through binary64 (correctly rounded there, and 53 >= 2*24+2 makes
+// the second rounding to binary32 innocuous) with explicit flushing on both
+// sides, so no fp32 fused multiply-add appears anywhere in the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#pragma clang fp contract(off)
+
+namespace brl {
+
+typedef float vf4 __attribute__((ext_vector_type(4)));   // 16-byte vector
+
+constexpr int kBlock = 32;      // CanonSum block width
+constexpr int kQmax = 127;      // int8 quantiser range [-127, 127]
+
+__device__ __forceinline__ float flush_f32(float x) {
+    return (__builtin_fabsf(x) < 1.17549435e-38f) ? __builtin_copysignf(0.0f, x) : x;
+}
+
+__device__ __forceinline__ float f_add(float a, float b) { return a + b; }
+__device__ __forceinline__ float f_sub(float a, float b) { return a - b; }
+__device__ __forceinline__ float f_mul(float a, float b) { return a * b; }
+
+__device__ __forceinline__ float f_div(float a, float b) {
+    double q = (double)flush_f32(a) / (double)flush_f32(b);
+    return flush_f32((float)q);
+}
+
+__device__ __forceinline__ float f_sqrt(float a) {
+    double r = __builtin_sqrt((double)flush_f32(a));
+    return flush_f32((float)r);
+}
+
+__device__ __forceinline__ float f_rne(float t) { return __builtin_rintf(t); }
+
+// Quantise one value with step s: q = clamp(rne(v/s), -127, 127),
+// in = (-127 <= v/s <= 127).  A zero step maps everything to q = 0, in range.
+__device__ __forceinline__ int quantize_q(float v, float s, bool* in_range) {
+    if (s == 0.0f) { *in_range = true; return 0; }
+    float t = f_div(v, s);
+    *in_range = (t >= -(float)kQmax) && (t <= (float)kQmax);
+    float r = f_rne(t);
+    r = r > (float)kQmax ? (float)kQmax : r;
+    r = r < -(float)kQmax ? -(float)kQmax : r;
+    return (int)r;
+}
+
+__device__ __forceinline__ bool quantize_in_range(float v, float s) {
+    if (s == 0.0f) return true;
+    float t = f_div(v, s);
+    return (t >= -(float)kQmax) && (t <= (float)kQmax);
+}
+
+// ---- the library's own binary32 exp (SwiGLU) ------------------------------
+// E(x): Cody-Waite reduction x = k*ln2 + r with k = rne(x * log2(e)), ln2
+// split into a 16-bit head (so k*head is exact) and a binary32 tail; degree-7
+// Taylor polynomial sum r^i/i! in Horner form; scaling by 2^k as two exact
+// power-of-two multiplies.  x > 89 gives +inf, x < -104 gives +0.
+struct ExpConsts {
+    float l2e, ln2_hi, ln2_lo;
+    float c[8];
+};
+
+__device__ __forceinline__ float pow2_f32(int e) {   // -126 <= e <= 127
+    return __int_as_float((e + 127) << 23);
+}
+
+__device__ __forceinline__ float own_exp(float x, const ExpConsts& K) {
+    if (x != x) return x;
+    if (x > 89.0f) return __int_as_float(0x7f800000);
+    if (x < -104.0f) return 0.0f;
+    float k = f_rne(f_mul(x, K.l2e));
+    float r = f_sub(f_sub(x, f_mul(k, K.ln2_hi)), f_mul(k, K.ln2_lo));
+    float p = K.c[7];
+#pragma unroll
+    for (int i = 6; i >= 0; --i) p = f_add(f_mul(p, r), K.c[i]);
+    int ki = (int)k;
+    int k1 = ki / 2;
+    int k2 = ki - k1;
+    return f_mul(f_mul(p, pow2_f32(k1)), pow2_f32(k2));
+}
+
+// SwiGLU forward pieces: s = 1/(1 + E(-g)), h = g*s, a = h*u.
+__device__ __forceinline__ float swiglu_sigma(float g, const ExpConsts& K) {
+    float e = own_exp(-g, K);
+    return f_div(1.0f, f_add(1.0f, e));
+}
+
+// ---- CanonSum helpers -------------------------------------------------------
+// Pairwise tree, level by level with odd carry, over `count` values held in
+// LDS (count <= blockDim.x).  Every thread of the workgroup must call it.
+// Returns the root in thread 0 (other threads get unspecified values).
+__device__ __forceinline__ float wg_pair_tree(float v, int count, float* lds) {
+    const int t = threadIdx.x;
+    lds[t] = v;
+    __syncthreads();
+    while (count > 1) {
+        const int h = count >> 1;
+        float nv = 0.0f;
+        if (t < h) nv = f_add(lds[2 * t], lds[2 * t + 1]);
+        else if (t == h && (count & 1)) nv = lds[count - 1];
+        __syncthreads();
+        if (t < h || (t == h && (count & 1))) lds[t] = nv;
+        __syncthreads();
+        count = h + (count & 1);
+    }
+    float r = lds[0];
+    __syncthreads();
+    return r;
+}
+
+}  // namespace brl

@@ -1,0 +1,116 @@
+// internal.hpp -- host-side launchers shared between the translation units of
+// libbrlsq.  Nothing here is part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "device.hpp"
+#include "brlsq.h"
+
+namespace brl {
+
+// Scalars kept in device memory by one call (never read back by the host).
+struct Scalars {
+    float s_w;      // weight step
+    float s_y;      // s_x * s_w
+    float nu;       // global norm
+    float kappa;    // clip coefficient (1 when not clipping)
+    int32_t clip;   // 1 when kappa applies
+    int32_t pad[11];
+};
+
+inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Launch-shape knobs (never change results).
+int bwd_chunk_log2();          // 32-blocks per backward chunk = 2^value
+int reduce_wg_blocks();        // 32-blocks per workgroup in CanonSum passes
+int stream_wgs();              // workgroups for streaming kernels
+
+// ---- CanonSum over a flat vector -------------------------------------------
+enum CanonMap { kMapAbs = 0, kMapSquare = 1 };
+enum CanonFinish { kFinishScale = 0, kFinishNorm = 1 };
+
+struct CanonFinishArgs {
+    int mode;               // CanonFinish
+    float count_f;          // fl(number of summed elements) (scale)
+    float s_x;              // activation step (scale)
+    float max_norm, eps;    // (norm)
+    Scalars* scal;          // receives s_w/s_y or nu/kappa/clip
+    float* s_w_out;         // optional copy of s_w
+    float* nu_out;          // optional copy of nu
+};
+
+// Partial buffer floats needed by launch_canon for n elements.
+int64_t canon_partials(int64_t n);
+hipError_t launch_canon(int map, const float* x, int64_t n, float* partials,
+                        const CanonFinishArgs& fin, hipStream_t st);
+
+// ---- quantisation and the int8 GEMM ------------------------------------------
+// GEMM tiling (forward): K padded to kKPad, rows of both operands to kRowPad.
+constexpr int kKPad = 64;
+constexpr int kRowPad = 256;
+constexpr int kSwigluGroup = 64;   // gate/up columns interleaved in groups of 64
+
+// q[r_out, :] for every padded output row r_out < rows_p (zero rows and
+// columns past the data).  swiglu_half > 0 interleaves rows in groups of
+// kSwigluGroup: output rows [128t, 128t+64) = gate rows [64t, 64t+64),
+// [128t+64, 128t+128) = up rows half + [64t, 64t+64).
+hipError_t launch_quantize(const float* v, int64_t rows, int64_t cols, const float* s_dev,
+                           float s_host, int8_t* q, int64_t rows_p, int64_t cols_p,
+                           int64_t swiglu_half, hipStream_t st);
+
+struct GemmArgs {
+    const int8_t* qx;     // [Mp, Kp]
+    const int8_t* qw;     // [Nvp, Kp] (interleaved for SwiGLU)
+    int64_t M, N, Kp;     // N = true stacked width
+    int64_t Mp, Nvp;      // padded row counts
+    const Scalars* scal;  // s_y
+    const float* addend;  // [M, N] or null
+    float* Y;             // [M, N] or [M, N/2]
+    float* Ypre;          // SwiGLU pre-activation [M, N] or null
+    int epilogue;
+    ExpConsts ek;
+};
+hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t st);
+
+// ---- straight-through backward ---------------------------------------------
+struct SteArgs {
+    // C[i][j] = CanonSum_r A(r,i) * B(r,j) for r in [0, R)
+    const float* A;        // dY / G
+    int64_t lda;
+    bool a_rmaj;           // A(r,i) = A[i*lda + r] (dX) else A[r*lda + i] (dW)
+    int64_t I, R, Jn;
+    const int8_t* Bq;      // [>= round_up(R,32), ldb] int8, zero padded
+    int64_t ldb;
+    const float* b_scale_dev;  // step of B (device) or null
+    float b_scale_host;
+    // mask and output
+    const float* mask_src; // [I, Jn] values whose in-range decides the mask
+    const float* mask_scale_dev;
+    float mask_scale_host;
+    float* out;            // [I, Jn]
+    int accumulate;
+    float* roots;          // workspace for chunk roots [Q, I, Jn]
+};
+int64_t ste_chunks(int64_t R);
+int64_t ste_root_floats(int64_t I, int64_t R, int64_t Jn);
+hipError_t launch_ste(const SteArgs& a, hipStream_t st);
+
+hipError_t launch_swiglu_bwd(const float* dA, const float* ypre, int64_t M, int64_t N, float* G,
+                             const ExpConsts& ek, hipStream_t st);
+
+// ---- replay -------------------------------------------------------------------
+hipError_t launch_accumulate(float* A, const float* G, int64_t n, hipStream_t st);
+struct FoldPtrs { const float* a[64]; };
+hipError_t launch_fold(const FoldPtrs& p, int R, const float* g_last, float* out, int64_t n,
+                       hipStream_t st);
+hipError_t launch_clip(float* g, int64_t n, const Scalars* scal, hipStream_t st);
+
+hipError_t launch_probe(int op, const float* a, const float* b, float* out, int64_t n,
+                        const ExpConsts& ek, hipStream_t st);
+
+ExpConsts exp_constants();
+
+}  // namespace brl

@@ -1,0 +1,196 @@
+/*
+ * brlsq.h -- C ABI of the bit-exact int8 LSQ linear layer and ordered
+ * gradient reduction for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed follows "OPEN-1B: A Fully Auditable Training Run"
+ * (Donaghy et al., Gensyn), as summarised on onedev.kr:
+ *   - section "How": every reduction in one fixed order, multiply and add
+ *     never fused, subnormals flushed to zero on every backend;
+ *   - section "Use": LSQ int8 QAT on every attention/FFN linear (8-bit
+ *     weights and activations), weight step 2*mean(|w|)/sqrt(q_max) recomputed
+ *     from the weights every step, SwiGLU gate and up as one GEMM;
+ *   - section "Limits", recipe paragraph: global L2 gradient-norm clip at 1.0;
+ *   - section "Limits", audit paragraph: single-device replay of the gradient
+ *     reduction -- running-sum reduce-scatter over virtual ranks in mesh order
+ *     (replica-major, shard-minor), then TreeFold over replicas in the
+ *     pairing order of a recursive-doubling all-reduce.
+ *
+ * Numerics contract (every output, bit for bit, on every call):
+ *   binary32 add/sub/mul/div/sqrt are each rounded to nearest even and then
+ *   flushed to a zero of the same sign when the rounded result is below
+ *   2^-126; subnormal operands read as zeros of the same sign; no operation is
+ *   fused.  CanonSum(p_0..p_{n-1}) = sequential left-to-right sums of 32-wide
+ *   blocks (each starting from its first term), then a pairwise tree over the
+ *   block sums, level by level, (0,1),(2,3),..., an odd last node carried up
+ *   unchanged; CanonSum of nothing is +0.  Results do not depend on tile
+ *   sizes, launch shapes or the number of compute units.
+ *
+ * Memory and ownership.  All tensor pointers are device pointers, row-major,
+ * dense (row pitch = the row length).  The caller owns every buffer,
+ * including the workspace, whose size comes from brl_workspace_bytes().  The
+ * library allocates no device memory.  Every call is asynchronous on the given
+ * HIP stream (a hipStream_t passed as void*; NULL = the null stream) and never
+ * synchronises the host.  Pointers must be 4-byte aligned.
+ *
+ * Errors.  Arguments are checked before anything is launched; a bad argument
+ * returns a negative status and launches nothing.  A failed launch returns
+ * BRL_EDEVICE.  brl_last_error() gives a message for the calling thread.
+ * Inputs must be finite; NaN and Inf propagate by IEEE rules and are not
+ * checked.
+ */
+#ifndef BRLSQ_H
+#define BRLSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define BRL_API __attribute__((visibility("default")))
+#else
+#define BRL_API
+#endif
+
+typedef int32_t brl_status;
+
+#define BRL_OK          0
+#define BRL_EINVAL     (-1)   /* null pointer, bad scalar, bad enum */
+#define BRL_ESHAPE     (-2)   /* non-positive or inconsistent sizes, overflow risk */
+#define BRL_EORDER     (-3)   /* ordered_reduce called out of mesh order */
+#define BRL_EDEVICE    (-4)   /* HIP launch or runtime error */
+#define BRL_EWORKSPACE (-5)   /* workspace missing or too small */
+
+/* Epilogues of the forward (and the matching backward prologue). */
+#define BRL_EPILOGUE_NONE   0
+/* Stacked SwiGLU: W rows [0, N/2) are the gate, rows [N/2, N) the up
+ * projection (the pages' "gate and up as one GEMM").  The activation is
+ * A[m,j] = (g * sigma(g)) * u with g = Y[m,j], u = Y[m,j+N/2],
+ * sigma(g) = 1 / (1 + E(-g)) and E the library's own binary32 exp (Cody-Waite
+ * reduction with ln2 split at 16 bits, degree-7 Taylor polynomial in Horner
+ * form, scaling by 2^k in two exact steps; every step one binary32 op). */
+#define BRL_EPILOGUE_SWIGLU 1
+
+/* Workspace query operations. */
+#define BRL_OP_FWD  0
+#define BRL_OP_BWD  1
+#define BRL_OP_NORM 2
+
+/* Bytes of device workspace needed by an operation.  For BRL_OP_FWD and
+ * BRL_OP_BWD, M, K, N are the layer sizes (N = stacked width for SwiGLU);
+ * for BRL_OP_NORM, M is the vector length and K, N are ignored. */
+BRL_API size_t brl_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N);
+
+/*
+ * qat_linear_fwd -- LSQ int8 quantisation-aware linear forward.
+ *   s_w = (2 * mu) / fl(sqrt(127)),  mu = CanonSum(|W|) / fl(N*K) over
+ *         row-major W, recomputed on every call;
+ *   q_w = clamp(rne(W / s_w), -127, 127), q_x = clamp(rne(X / s_x), -127, 127)
+ *         (a zero s_w quantises every weight to 0);
+ *   acc = q_x . q_w^T in exact int32 (int8 matrix cores);
+ *   Y   = fl(acc) * (s_x * s_w), then Y + addend when addend != NULL
+ *         (a separate rounding; never fused).
+ * X [M,K], W [N,K] (nn.Linear layout), addend [M,N] or NULL.
+ * epilogue NONE: Y [M,N]; Ypre ignored.
+ * epilogue SWIGLU: N even; Y [M,N/2] receives the activation and, when
+ *   Ypre != NULL, Ypre [M,N] receives the pre-activation (needed by the
+ *   backward).  addend (if any) is added before the activation.
+ * s_x: the activation step, finite and > 0.
+ * s_w_out: NULL or a device float that receives s_w.
+ * Requires |acc| < 2^31, guaranteed for K <= 133144.
+ */
+BRL_API brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, int64_t N,
+                          float s_x, const float* addend, int32_t epilogue,
+                          float* Y, float* Ypre, float* s_w_out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qat_linear_bwd -- straight-through backward of qat_linear_fwd.
+ *   G   = dOut [M,N] (epilogue NONE), or for SWIGLU the pre-activation
+ *         gradient from dOut [M,N/2] and Ypre [M,N]:
+ *           du = dA*h,  dg = (dA*u) * (s*(1 + g*(1 - s))),  s = sigma(g), h = g*s;
+ *   What = fl(q_w * s_w), Xhat = fl(q_x * s_x)   (recomputed from W, X, s_x);
+ *   dX[m,k] = in_x[m,k] ? CanonSum_n(G[m,n] * What[n,k]) : +0
+ *   dW[n,k] = in_w[n,k] ? CanonSum_m(G[m,n] * Xhat[m,k]) : +0
+ *   with in_v = (-127 <= v/s <= 127) for the value's own step.
+ * dX [M,K] and dW [N,K] may each be NULL (not computed).
+ * dW_accumulate = 1: dW <- dW + (new dW), one binary32 add per element (the
+ *   ascending microbatch running sum); 0: dW is overwritten.
+ */
+BRL_API brl_status qat_linear_bwd(const float* dOut, const float* X, const float* W, const float* Ypre,
+                          int64_t M, int64_t K, int64_t N, float s_x, int32_t epilogue,
+                          float* dX, float* dW, int32_t dW_accumulate,
+                          void* ws, size_t ws_bytes, void* stream);
+
+#define BRL_MAX_REPLICAS 64
+
+/* Caller-owned host struct describing one replay.  acc[r] are device
+ * buffers of len floats (A_r), owned by the caller; next is the virtual rank
+ * v = r*shards + s that ordered_reduce expects next. */
+typedef struct brl_reduce_state {
+    int32_t replicas;
+    int32_t shards;
+    int64_t len;
+    int32_t next;
+    int32_t reserved;
+    float* acc[BRL_MAX_REPLICAS];
+} brl_reduce_state;
+
+/* Fill a reduce state: 1 <= replicas <= 64, shards >= 1, len >= 0, acc[0..replicas)
+ * non-NULL device buffers of len floats.  Sets next = 0. */
+BRL_API brl_status brl_reduce_init(brl_reduce_state* st, int32_t replicas, int32_t shards, int64_t len,
+                           float* const* acc);
+
+/*
+ * ordered_reduce -- one step of the audit replay of the gradient reduction.
+ * Takes the partial gradient G_v [len] of virtual rank v = st->next,
+ * r = v / shards, s = v % shards (mesh order: replica-major, shard-minor):
+ *   s == 0: A_r = G_v;   s > 0: A_r = A_r + G_v   (binary32, elementwise).
+ * After the last rank (v = replicas*shards - 1) it writes the TreeFold of
+ * A_0..A_{R-1} to out [len]: with p the largest power of two <= R, leaves
+ * L_i = A_i + A_{i+p} for i < R - p, else A_i, then the pairwise tree over
+ * L_0..L_{p-1} -- the value every rank of a recursive-doubling all-reduce
+ * holds.  For R = 6: ((A0+A4)+(A1+A5))+(A2+A3).  out may be NULL before the
+ * last rank and must be non-NULL for it; the last A_r is not written back.
+ * Advances st->next; a call with st->next >= replicas*shards returns
+ * BRL_EORDER and launches nothing.  partial is only read during the call's
+ * stream-ordered work and may be reused after it.
+ */
+BRL_API brl_status ordered_reduce(brl_reduce_state* st, const float* partial, float* out, void* stream);
+
+/*
+ * grad_l2norm_clip -- global L2 norm and clip of one flat gradient.
+ *   nu = fl(sqrt(CanonSum(g_i * g_i))) over g [len];
+ *   when nu > max_norm: kappa = max_norm / (nu + eps), g_i <- g_i * kappa;
+ *   otherwise g is left unchanged.
+ * norm_out: NULL or a device float receiving nu (before clipping).
+ * max_norm > 0 and eps >= 0, both finite.
+ */
+BRL_API brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float eps, float* norm_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Conformance probe of the device's binary32 operations, as the kernels use
+ * them: out[i] = op(a[i], b[i]) for op 0 add, 1 sub, 2 mul, 3 div, 4 sqrt (a),
+ * 5 int32 bits of a -> float, 6 round-to-nearest-even integral (a),
+ * 7 the SwiGLU exp E(a).  Device pointers, n >= 0. */
+BRL_API brl_status brl_probe_f32(int32_t op, const float* a, const float* b, float* out, int64_t n,
+                         void* stream);
+
+/* Launch-shape tuning knobs.  They change only how work is split across
+ * workgroups, never the results.  Returns the previous value, or -1 for an
+ * unknown knob; value <= 0 restores the default.  Process-wide. */
+#define BRL_TUNE_BWD_CHUNK_LOG2   0   /* 32-blocks per backward reduction chunk: 2^v, 1..6 */
+#define BRL_TUNE_REDUCE_WG_BLOCKS 1   /* 32-blocks per workgroup in CanonSum passes: 64,128,256 */
+#define BRL_TUNE_STREAM_WGS       2   /* workgroups of the streaming kernels */
+BRL_API int64_t brl_set_tuning(int32_t knob, int64_t value);
+
+BRL_API const char* brl_status_string(brl_status s);
+BRL_API const char* brl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BRLSQ_H */

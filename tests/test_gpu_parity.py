@@ -1,0 +1,314 @@
+"""GPU parity of the HIP path against the CPU oracle, element by element, at
+0 ULP (bitwise equality of every output).  Small and ragged sizes that span
+several tiles; every call goes through the C ABI.
+
+Tolerance: none.  The method defines each output by its exact sequence of
+binary32 operations (Open-1B summary on onedev.kr, "How"), so the only
+correct result is the oracle's bit pattern.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bitwise_reproducible_lsq_amd as brl
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _bits(x):
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(x, np.float32).view(np.uint32)
+
+
+def assert_bitwise(got, want, what):
+    g, w = _bits(got), _bits(want)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    bad = np.flatnonzero(g.ravel() != w.ravel())
+    if bad.size:
+        i = bad[0]
+        raise AssertionError(f"{what}: {bad.size} of {g.size} differ; first at flat {i}: "
+                             f"got {g.ravel()[i]:#010x} want {w.ravel()[i]:#010x}")
+
+
+def _cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _case_inputs(M, K, N, seed, sub=0.0, swiglu=False, x_kind="normal"):
+    case = synth.small_case(f"s{seed}", seed, M, K, N, subnormal_frac=sub, swiglu=swiglu, x_kind=x_kind)
+    return synth.linear_inputs(case)
+
+
+# ---- binary32 conformance of the device operations --------------------------------
+def _probe_inputs(n, seed):
+    g = np.random.default_rng(seed)
+    a = (g.standard_normal(n) * np.exp(g.uniform(-40, 40, n))).astype(np.float32)
+    b = (g.standard_normal(n) * np.exp(g.uniform(-40, 40, n))).astype(np.float32)
+    tiny = np.float32(np.finfo(np.float32).tiny)
+    directed = [
+        (np.float32(1 - 2.0 ** -24), tiny),          # product rounds up to 2^-126 (kept)
+        (np.float32(1 - 2.0 ** -23), tiny),          # exact subnormal product (flushed)
+        (np.float32(1e-20), np.float32(-1e-20)),     # -0 after flush
+        (np.float32(1.5) * tiny, -tiny),             # exact subnormal sum
+        (np.float32(1e-40), np.float32(1.0)),        # subnormal operand
+        (np.float32(-1e-40), np.float32(-0.0)),
+        (tiny, np.float32(1.0 + 2.0 ** -23)),        # quotient just below 2^-126 (div)
+        (np.float32(3.0), np.float32(7.0)),
+        (np.float32(1.0 + 2.0 ** -12), np.float32(1.0 + 2.0 ** -12)),
+    ]
+    for i, (x, y) in enumerate(directed):
+        a[i], b[i] = x, y
+    return a, b
+
+
+@pytest.mark.parametrize("op", ["add", "sub", "mul", "div", "sqrt", "rne", "exp"])
+def test_device_binary32_ops_match_oracle(op):
+    a, b = _probe_inputs(20000, 3)
+    if op == "sqrt":
+        a = np.abs(a)
+    if op == "rne":
+        a = (np.random.default_rng(5).standard_normal(20000) * 300).astype(np.float32)
+        a[:521] = (np.arange(-260, 261) / 2).astype(np.float32)
+    if op == "exp":
+        a = np.random.default_rng(6).uniform(-110, 95, 20000).astype(np.float32)
+    got = brl.probe_f32(op, _cuda(a), _cuda(b)).cpu().numpy()
+    fn = {"add": oracle.add, "sub": oracle.sub, "mul": oracle.mul, "div": oracle.div,
+          "sqrt": lambda x, y: oracle.sqrt(x), "rne": lambda x, y: oracle.rne(x),
+          "exp": lambda x, y: oracle.exp(x)}[op]
+    want = np.array([fn(x, y) for x, y in zip(a, b)], np.float32)
+    nan = np.isnan(got) & np.isnan(want)
+    bad = np.flatnonzero((_bits(got) != _bits(want)) & ~nan)
+    assert bad.size == 0, [(a[i], b[i], got[i], want[i]) for i in bad[:5]]
+
+
+def test_device_int_to_float_rne():
+    ints = np.array([0, 1, -1, 2**24 + 1, 2**24 + 3, 2**31 - 1, -2**31, 90_832_001, -16_777_217], np.int32)
+    got = brl.probe_f32("i2f", _cuda(ints.view(np.float32))).cpu().numpy()
+    want = np.array([oracle.i2f(int(v)) for v in ints], np.float32)
+    assert_bitwise(got, want, "i2f")
+
+
+# ---- linear layer: forward ------------------------------------------------------------
+SHAPES = [
+    (256, 512, 512),     # the tiny workload's shape
+    (300, 200, 130),     # ragged in every dimension
+    (1, 7, 3),
+    (257, 64, 256),
+    (64, 1000, 96),
+    (513, 96, 300),
+]
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_fwd_parity(M, K, N):
+    inp = _case_inputs(M, K, N, seed=M + K + N)
+    X, W = _cuda(inp.X), _cuda(inp.W)
+    Y, _, s_w = brl.qat_linear_fwd(X, W, synth.S_X)
+    torch.cuda.synchronize()
+    assert_bitwise(s_w, np.array([oracle.weight_scale(inp.W)]), "s_w")
+    assert_bitwise(Y, oracle.linear_fwd(inp.X, inp.W, synth.S_X), "Y")
+
+
+def test_fwd_tiny_workload():
+    inp = synth.linear_inputs(synth.CASES["tiny"])
+    Y, _, s_w = brl.qat_linear_fwd(_cuda(inp.X), _cuda(inp.W), synth.S_X)
+    assert_bitwise(Y, oracle.linear_fwd(inp.X, inp.W, synth.S_X), "Y")
+
+
+def test_fwd_addend():
+    inp = _case_inputs(130, 70, 90, seed=9)
+    add = np.random.default_rng(1).standard_normal((130, 90)).astype(np.float32)
+    Y, _, _ = brl.qat_linear_fwd(_cuda(inp.X), _cuda(inp.W), synth.S_X, addend=_cuda(add))
+    assert_bitwise(Y, oracle.linear_fwd(inp.X, inp.W, synth.S_X, addend=add), "Y+C")
+
+
+@pytest.mark.parametrize("M,K,N", [(200, 96, 256), (70, 64, 198), (256, 512, 512)])
+def test_fwd_swiglu_parity(M, K, N):
+    inp = _case_inputs(M, K, N, seed=11, swiglu=True)
+    Y, Ypre, _ = brl.qat_linear_fwd(_cuda(inp.X), _cuda(inp.W), synth.S_X, epilogue=brl.EPILOGUE_SWIGLU)
+    wantY, wantPre = oracle.linear_fwd(inp.X, inp.W, synth.S_X, epilogue=1)
+    assert_bitwise(Ypre, wantPre, "Ypre")
+    assert_bitwise(Y, wantY, "SwiGLU(Y)")
+
+
+def test_fwd_zero_weights_and_empty_rows():
+    X = np.random.default_rng(0).standard_normal((40, 32)).astype(np.float32)
+    W = np.zeros((24, 32), np.float32)
+    Y, _, s_w = brl.qat_linear_fwd(_cuda(X), _cuda(W), synth.S_X)
+    assert float(s_w.item()) == 0.0
+    assert_bitwise(Y, oracle.linear_fwd(X, W, synth.S_X), "Y (zero W)")
+    W = np.random.default_rng(1).standard_normal((24, 32)).astype(np.float32)
+    Y, _, s_w = brl.qat_linear_fwd(_cuda(np.zeros((0, 32), np.float32)), _cuda(W), synth.S_X)
+    assert Y.shape == (0, 24)
+    assert_bitwise(s_w, np.array([oracle.weight_scale(W)]), "s_w (M=0)")
+
+
+# ---- linear layer: backward -----------------------------------------------------------
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_bwd_parity(M, K, N):
+    inp = _case_inputs(M, K, N, seed=M * 3 + K + N, sub=0.01)
+    dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), _cuda(inp.X), _cuda(inp.W), synth.S_X)
+    wX, wW = oracle.linear_bwd(inp.dY, inp.X, inp.W, synth.S_X)
+    assert_bitwise(dX, wX, "dX")
+    assert_bitwise(dW, wW, "dW")
+
+
+def test_bwd_tiny_workload():
+    inp = synth.linear_inputs(synth.CASES["tiny"])
+    dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), _cuda(inp.X), _cuda(inp.W), synth.S_X)
+    wX, wW = oracle.linear_bwd(inp.dY, inp.X, inp.W, synth.S_X)
+    assert_bitwise(dX, wX, "dX")
+    assert_bitwise(dW, wW, "dW")
+
+
+def test_bwd_long_reductions_and_masks():
+    """Reductions of many blocks (several chunks and a ragged tail) and
+    activations that clip (mask false)."""
+    M, K, N = 2100, 40, 1100
+    inp = _case_inputs(M, K, N, seed=21, x_kind="silu_x_normal")
+    X = inp.X * np.float32(2.0)
+    assert (np.abs(X / synth.S_X) > 127).any()
+    dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), _cuda(X), _cuda(inp.W), synth.S_X)
+    wX, wW = oracle.linear_bwd(inp.dY, X, inp.W, synth.S_X)
+    assert_bitwise(dX, wX, "dX")
+    assert_bitwise(dW, wW, "dW")
+
+
+def test_bwd_swiglu_parity():
+    M, K, N = 160, 96, 192
+    inp = _case_inputs(M, K, N, seed=31, swiglu=True)
+    X, W = _cuda(inp.X), _cuda(inp.W)
+    _, Ypre, _ = brl.qat_linear_fwd(X, W, synth.S_X, epilogue=brl.EPILOGUE_SWIGLU)
+    dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), X, W, synth.S_X, Ypre=Ypre, epilogue=brl.EPILOGUE_SWIGLU)
+    _, wPre = oracle.linear_fwd(inp.X, inp.W, synth.S_X, epilogue=1)
+    G = oracle.swiglu_bwd(wPre, inp.dY)
+    wX, wW = oracle.linear_bwd(G, inp.X, inp.W, synth.S_X)
+    assert_bitwise(dX, wX, "dX")
+    assert_bitwise(dW, wW, "dW")
+
+
+def test_bwd_microbatch_running_sum():
+    M, K, N, B = 4 * 96, 72, 80, 4
+    inp = _case_inputs(M, K, N, seed=41)
+    X, W, dY = _cuda(inp.X), _cuda(inp.W), _cuda(inp.dY)
+    mb = M // B
+    dW = None
+    for b in range(B):
+        _, dW = brl.qat_linear_bwd(dY[b * mb:(b + 1) * mb], X[b * mb:(b + 1) * mb], W, synth.S_X,
+                                   need_dX=False, dW=dW, dW_accumulate=b > 0)
+    want = oracle.dw_rows(np.ascontiguousarray(inp.dY.T), inp.X, inp.W, synth.S_X, np.arange(N), mb=mb)
+    assert_bitwise(dW, want, "dW (4 microbatches)")
+
+
+def test_bwd_empty_rows():
+    W = np.random.default_rng(2).standard_normal((24, 32)).astype(np.float32) * np.float32(0.02)
+    z = np.zeros((0, 32), np.float32)
+    dX, dW = brl.qat_linear_bwd(_cuda(np.zeros((0, 24), np.float32)), _cuda(z), _cuda(W), synth.S_X)
+    assert dX.shape == (0, 32)
+    assert_bitwise(dW, np.zeros((24, 32), np.float32), "dW (M=0)")
+
+
+def test_bwd_launch_shape_invariance():
+    """The chunking of the reduction and the CanonSum workgroup size change
+    only the launch shape: every setting gives the oracle's bits."""
+    M, K, N = 1500, 64, 700
+    inp = _case_inputs(M, K, N, seed=51)
+    wX, wW = oracle.linear_bwd(inp.dY, inp.X, inp.W, synth.S_X)
+    X, W, dY = _cuda(inp.X), _cuda(inp.W), _cuda(inp.dY)
+    old_c = brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, 0)
+    old_r = brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, 0)
+    try:
+        for c, r in [(1, 64), (2, 128), (3, 256), (4, 64), (5, 128), (6, 256)]:
+            brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, c)
+            brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, r)
+            dX, dW = brl.qat_linear_bwd(dY, X, W, synth.S_X)
+            assert_bitwise(dX, wX, f"dX chunk=2^{c} wg={r}")
+            assert_bitwise(dW, wW, f"dW chunk=2^{c} wg={r}")
+    finally:
+        brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, old_c)
+        brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, old_r)
+
+
+def test_repeat_runs_identical():
+    inp = _case_inputs(700, 128, 300, seed=61)
+    X, W, dY = _cuda(inp.X), _cuda(inp.W), _cuda(inp.dY)
+    ref = None
+    for _ in range(5):
+        Y, _, _ = brl.qat_linear_fwd(X, W, synth.S_X)
+        dX, dW = brl.qat_linear_bwd(dY, X, W, synth.S_X)
+        cur = [_bits(t).copy() for t in (Y, dX, dW)]
+        if ref is None:
+            ref = cur
+        for a, b in zip(ref, cur):
+            assert (a == b).all()
+
+
+# ---- replay -----------------------------------------------------------------------------
+def _replay_gpu(partials_np, R, S, max_norm=1.0):
+    L = partials_np[0].size
+    st = brl.ReduceState(R, S, L, device=DEV)
+    out = None
+    for v in range(R * S):
+        out = brl.ordered_reduce(st, _cuda(partials_np[v]))
+    nu = brl.grad_l2norm_clip(out, max_norm)
+    return out, nu, st
+
+
+@pytest.mark.parametrize("R,S,L", [(6, 8, 65536 + 5), (1, 1, 1000), (2, 3, 4097), (3, 2, 333),
+                                   (5, 1, 1024), (7, 2, 100), (16, 2, 2048), (6, 8, 3)])
+def test_replay_parity(R, S, L):
+    parts = [synth.replay_partial_host(4, v, L, std=1e-2) for v in range(R * S)]
+    out, nu, st = _replay_gpu(parts, R, S)
+    T, wnu, A = oracle.replay(parts, R, S)
+    assert_bitwise(nu, np.array([wnu]), "nu")
+    assert_bitwise(out, T, "clipped TreeFold")
+    for r in range(R - 1):      # the last replica's running sum is fused into the fold
+        if S > 1 or r < R - 1:
+            assert_bitwise(st.acc[r], A[r], f"A_{r}")
+    with pytest.raises(brl.BrlError) as e:
+        brl.ordered_reduce(st, _cuda(parts[0]))
+    assert e.value.status == brl.BRL_EORDER
+
+
+def test_replay_no_clip_and_empty():
+    parts = [synth.replay_partial_host(5, v, 5000, std=1e-5) for v in range(4)]
+    out, nu, _ = _replay_gpu(parts, 2, 2)
+    T, wnu, _ = oracle.replay(parts, 2, 2)
+    assert float(wnu) <= 1.0
+    assert_bitwise(out, T, "TreeFold (no clip)")
+    assert_bitwise(nu, np.array([wnu]), "nu")
+    g = torch.zeros(0, dtype=torch.float32, device=DEV)
+    nu0 = brl.grad_l2norm_clip(g)
+    assert float(nu0.item()) == 0.0
+
+
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 8191, 8192 * 256 + 77, 3 * 2**20])
+def test_norm_clip_parity(n):
+    g = np.random.default_rng(n).standard_normal(n).astype(np.float32) * np.float32(0.01)
+    g[: min(n, 10)] = np.float32(1e-40)       # subnormals read as zero
+    t = _cuda(g)
+    nu = brl.grad_l2norm_clip(t, 1.0)
+    wnu = oracle.l2norm(g)
+    w = g.copy()
+    oracle.clip(w, wnu, 1.0, 0.0)
+    assert_bitwise(nu, np.array([wnu]), "nu")
+    assert_bitwise(t, w, "clipped g")
+
+
+def test_norm_reduce_wg_invariance():
+    n = 5_000_003
+    g = np.random.default_rng(7).standard_normal(n).astype(np.float32)
+    wnu = oracle.l2norm(g)
+    old = brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, 0)
+    try:
+        for wg in (64, 128, 256):
+            brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, wg)
+            nu = brl.grad_l2norm_clip(_cuda(g), 1e30)
+            assert_bitwise(nu, np.array([wnu]), f"nu wg={wg}")
+    finally:
+        brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, old)

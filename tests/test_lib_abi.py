@@ -1,0 +1,139 @@
+"""CPU checks of the C-ABI library: it loads, exports every function that
+include/brlsq.h declares, validates arguments before touching the device,
+and its gfx950 code contains no fused or packed fp32 arithmetic outside the
+correctly rounded division sequence.  No kernel is launched here."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import bitwise_reproducible_lsq_amd as brl
+from bitwise_reproducible_lsq_amd import build as brl_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "brlsq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"BRL_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("qat_linear_fwd", "qat_linear_bwd", "ordered_reduce", "grad_l2norm_clip"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = C.CDLL(brl.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_workspace_query_is_host_only():
+    assert brl.workspace_bytes(brl.OP_FWD, 256, 512, 512) > 0
+    assert brl.workspace_bytes(brl.OP_BWD, 256, 512, 512) > 0
+    assert brl.workspace_bytes(brl.OP_NORM, 1000, 0, 0) > 0
+    assert brl.workspace_bytes(brl.OP_FWD, 256, 0, 512) == 0
+    assert brl.workspace_bytes(7, 1, 1, 1) == 0
+
+
+def _fwd(M=4, K=4, N=4, s_x=0.05, X=1, W=1, Y=1, ws=1, ws_bytes=1 << 20, epi=0):
+    L = brl.lib()
+    p = lambda v: C.c_void_p(0x10000) if v else None
+    return L.qat_linear_fwd(p(X), p(W), M, K, N, s_x, None, epi, p(Y), None, None, p(ws), ws_bytes, None)
+
+
+def test_fwd_rejects_bad_arguments_without_launching():
+    assert _fwd(M=-1) == brl.BRL_ESHAPE
+    assert _fwd(K=0) == brl.BRL_ESHAPE
+    assert _fwd(K=200_000) == brl.BRL_ESHAPE
+    assert _fwd(s_x=0.0) == brl.BRL_EINVAL
+    assert _fwd(s_x=float("inf")) == brl.BRL_EINVAL
+    assert _fwd(s_x=float("nan")) == brl.BRL_EINVAL
+    assert _fwd(W=0) == brl.BRL_EINVAL
+    assert _fwd(epi=3) == brl.BRL_EINVAL
+    assert _fwd(N=5, epi=1) == brl.BRL_ESHAPE
+    assert _fwd(ws_bytes=16) == brl.BRL_EWORKSPACE
+    assert _fwd(ws=0) == brl.BRL_EWORKSPACE
+    assert b"workspace" in brl.lib().brl_last_error()
+
+
+def test_bwd_rejects_bad_arguments_without_launching():
+    L = brl.lib()
+    p = C.c_void_p(0x10000)
+    assert L.qat_linear_bwd(p, p, p, None, 4, 4, 4, 0.05, 1, p, p, 0, p, 1 << 20, None) == brl.BRL_EINVAL
+    assert L.qat_linear_bwd(p, p, p, None, 4, 4, 4, 0.05, 0, p, p, 2, p, 1 << 20, None) == brl.BRL_EINVAL
+    assert L.qat_linear_bwd(p, p, p, None, 4, -4, 4, 0.05, 0, p, p, 0, p, 1 << 20, None) == brl.BRL_ESHAPE
+    assert L.qat_linear_bwd(p, p, p, None, 4, 4, 4, 0.05, 0, p, p, 0, p, 8, None) == brl.BRL_EWORKSPACE
+
+
+def test_reduce_state_order_is_enforced_on_the_host():
+    L = brl.lib()
+    st = brl.ReduceStateC()
+    bufs = (C.c_void_p * 6)(*([0x10000] * 6))
+    assert L.brl_reduce_init(C.byref(st), 0, 8, 16, C.cast(bufs, C.c_void_p)) == brl.BRL_ESHAPE
+    assert L.brl_reduce_init(C.byref(st), 65, 8, 16, C.cast(bufs, C.c_void_p)) == brl.BRL_ESHAPE
+    assert L.brl_reduce_init(C.byref(st), 6, 8, 16, C.cast(bufs, C.c_void_p)) == brl.BRL_OK
+    assert st.next == 0 and st.replicas == 6 and st.shards == 8
+    st.next = 48
+    assert L.ordered_reduce(C.byref(st), C.c_void_p(0x10000), C.c_void_p(0x10000), None) == brl.BRL_EORDER
+    st.next = 47
+    assert L.ordered_reduce(C.byref(st), C.c_void_p(0x10000), None, None) == brl.BRL_EINVAL  # last needs out
+    assert st.next == 47
+
+
+def test_norm_rejects_bad_arguments():
+    L = brl.lib()
+    p = C.c_void_p(0x10000)
+    assert L.grad_l2norm_clip(p, 16, 0.0, 0.0, None, p, 1 << 20, None) == brl.BRL_EINVAL
+    assert L.grad_l2norm_clip(p, 16, 1.0, -1.0, None, p, 1 << 20, None) == brl.BRL_EINVAL
+    assert L.grad_l2norm_clip(p, -1, 1.0, 0.0, None, p, 1 << 20, None) == brl.BRL_ESHAPE
+    assert L.grad_l2norm_clip(p, 16, 1.0, 0.0, None, p, 4, None) == brl.BRL_EWORKSPACE
+
+
+def test_tuning_knobs():
+    old = brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, 3)
+    assert brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, old) == 3
+    assert brl.set_tuning(9, 1) == -1
+
+
+# ---- generated gfx950 code -------------------------------------------------------
+FUSED = re.compile(r"v_(fma|fmac|fmamk|fmaak|mad|mac)_f32|v_pk_\w*f32|v_fma_mix|v_mad_mix|v_dot\w*f32")
+
+
+def test_no_fused_or_packed_fp32_outside_division():
+    """Every fp32 multiply-add in the device code sits inside the correctly
+    rounded division sequence (between v_div_scale_f32 and v_div_fixup_f32);
+    no packed fp32 instruction appears at all."""
+    files = brl_build.asm_files()
+    assert all(os.path.exists(f) for f in files), "build first"
+    bad = {}
+    for f in files:
+        fn, in_div = None, False
+        for line in open(f):
+            m = re.match(r"^(_Z\w+):", line)
+            if m:
+                fn, in_div = m.group(1), False
+                continue
+            if not line.startswith("\t"):
+                continue
+            ins = line.strip().split(" ")[0]
+            if ins.startswith("v_div_scale_f32"):
+                in_div = True
+            elif ins.startswith("v_div_fixup_f32"):
+                in_div = False
+            elif FUSED.match(ins) and not in_div:
+                bad.setdefault(fn, []).append(line.strip())
+    assert not bad, bad
+
+
+def test_hot_loops_use_plain_mul_and_add():
+    """The backward contraction kernels are made of v_mul_f32 + v_add_f32."""
+    text = open([f for f in brl_build.asm_files() if "bwd" in f][0]).read()
+    body = text.split("_ZN3brl16ste_chunk_kernelILb1ELi5EEEvNS_7SteArgsEli:")[1].split("s_endpgm")[0]
+    n_mul = len(re.findall(r"\tv_mul_f32", body))
+    n_add = len(re.findall(r"\tv_add_f32", body))
+    assert n_mul >= 512 and n_add >= 480, (n_mul, n_add)
