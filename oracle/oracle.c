@@ -26,9 +26,10 @@
  * Arithmetic model.  Every binary32 operation (add, sub, mul, div, sqrt) is
  * computed in IEEE double from the (DAZ-flushed) float operands and rounded
  * once to float.  Because 53 >= 2*24+2 that double rounding is innocuous, so
- * the result is the correctly rounded binary32 result.  A result whose
- * rounded magnitude is below 2^-126 is then replaced by a zero of the same
- * sign (FTZ).  Nothing relies on the x87/SSE control word except the
+ * the result is the correctly rounded binary32 result.  A result that is tiny
+ * (below 2^-126 after rounding to 24 bits with an unbounded exponent, the
+ * IEEE 754 after-rounding definition) is replaced by a zero of the same sign
+ * (FTZ).  Nothing relies on the x87/SSE control word except the
  * round-to-nearest-even mode, which each entry point resets explicitly.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.
@@ -59,15 +60,30 @@ static void fp_env_default(void) { _mm_setcsr(0x1F80u); }
 /* binary32 primitives (onedev.kr, "How": FTZ everywhere, no fusion)        */
 /* ------------------------------------------------------------------------ */
 static inline float flush(float x) {
-    /* subnormal -> zero of the same sign; zeros, normals, inf, nan pass */
+    /* subnormal operand -> zero of the same sign; zeros, normals, inf, nan pass */
     return (fabsf(x) < FLT_MIN) ? copysignf(0.0f, x) : x;
 }
 
-float or_add(float a, float b) { return flush((float)((double)flush(a) + (double)flush(b))); }
-float or_sub(float a, float b) { return flush((float)((double)flush(a) - (double)flush(b))); }
-float or_mul(float a, float b) { return flush((float)((double)flush(a) * (double)flush(b))); }
-float or_div(float a, float b) { return flush((float)((double)flush(a) / (double)flush(b))); }
-float or_sqrt(float a) { return flush((float)sqrt((double)flush(a))); }
+/* Round a binary64 value to binary32 with flush-to-zero.  x is the exact
+ * result (add, sub, mul of binary32 operands are exact in binary64) or its
+ * binary64 rounding (div, sqrt; innocuous, see the header).  Tininess is
+ * detected after rounding, as IEEE 754 defines it: x is first rounded to 24
+ * significant bits as if the exponent range were unbounded, and a result of
+ * magnitude below 2^-126 becomes a zero of the same sign. */
+static float round_flush(double x) {
+    if (fabs(x) < 0x1p-100) {
+        float r = (float)(x * 0x1p100);          /* exact scaling, then 24-bit rounding */
+        if (fabsf(r) < 0x1p-26f) return signbit(x) ? -0.0f : 0.0f;
+        return (float)((double)r * 0x1p-100);    /* exact: a normal binary32 */
+    }
+    return (float)x;
+}
+
+float or_add(float a, float b) { return round_flush((double)flush(a) + (double)flush(b)); }
+float or_sub(float a, float b) { return round_flush((double)flush(a) - (double)flush(b)); }
+float or_mul(float a, float b) { return round_flush((double)flush(a) * (double)flush(b)); }
+float or_div(float a, float b) { return round_flush((double)flush(a) / (double)flush(b)); }
+float or_sqrt(float a) { return round_flush(sqrt((double)flush(a))); }
 
 /* int32 -> binary32, round to nearest even (exact for |x| <= 2^24). */
 float or_i2f(int32_t x) { return (float)(double)x; }

@@ -51,8 +51,10 @@ def _probe_inputs(n, seed):
     b = (g.standard_normal(n) * np.exp(g.uniform(-40, 40, n))).astype(np.float32)
     tiny = np.float32(np.finfo(np.float32).tiny)
     directed = [
-        (np.float32(1 - 2.0 ** -24), tiny),          # product rounds up to 2^-126 (kept)
+        (np.float32(1 - 2.0 ** -24), tiny),          # tiny at 24 bits: flushed
         (np.float32(1 - 2.0 ** -23), tiny),          # exact subnormal product (flushed)
+        (np.float32(0.96875), np.float32(1082401 * 2.0 ** -146)),   # 2^-126(1-2^-25): rounds up, kept
+        (np.float32(-0.96875), np.float32(1082401 * 2.0 ** -146)),
         (np.float32(1e-20), np.float32(-1e-20)),     # -0 after flush
         (np.float32(1.5) * tiny, -tiny),             # exact subnormal sum
         (np.float32(1e-40), np.float32(1.0)),        # subnormal operand

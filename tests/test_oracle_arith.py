@@ -41,6 +41,13 @@ def test_primitives_match_ieee_binary32_with_flush(op, npop):
     b[50:100] = -(np.arange(1, 51, dtype=np.uint32) * 7919).view(np.float32)
     with np.errstate(all="ignore"):
         want = _flush(npop(_flush(a), _flush(b)))
+    # host binary32 rounds tiny results at subnormal precision; the two rules
+    # can only differ for results within half a 24-bit ulp below 2^-126, which
+    # these random operands never produce (checked here)
+    with np.errstate(all="ignore"):
+        exact = npop(_flush(a).astype(np.float64), _flush(b).astype(np.float64))
+    near = (np.abs(exact) < float(TINY)) & (np.abs(exact) > float(TINY) * (1 - 2.0 ** -24))
+    assert not near.any()
     fn = getattr(oracle, op)
     got = np.array([fn(x, y) for x, y in zip(a, b)], np.float32)
     same = (_bits(got) == _bits(want)) | (np.isnan(got) & np.isnan(want))
@@ -71,16 +78,20 @@ def test_flush_keeps_sign_and_daz():
     assert oracle.add(sub, np.float32(1.0)) == 1.0
 
 
-def test_ftz_corner_rounds_first():
-    """A product whose exact value lies just below 2^-126 but rounds (at
-    subnormal precision) to 2^-126 is kept: flush is decided on the rounded
-    result.  (1 - 2^-24) * 2^-126 = (2^24 - 1)/2^24 * 2^-126."""
-    a = np.float32(1.0 - 2.0 ** -24)          # 0x3F7FFFFF
-    b = TINY
-    assert oracle.mul(a, b) == TINY
-    # just below the tie: flushed
-    a2 = np.float32(np.nextafter(a, np.float32(0)))
-    assert oracle.mul(a2, b) == 0.0
+def test_ftz_tininess_after_rounding():
+    """Flush is decided on the result rounded to 24 bits with an unbounded
+    exponent (IEEE 754 tininess after rounding).  Hand-derived cases:
+    (1 - 2^-24) * 2^-126 is exactly representable at 24 bits and below
+    2^-126, so it is flushed; 31 * 1082401 = 2^25 - 1, so
+    0.96875 * (1082401 * 2^-146) = 2^-126 (1 - 2^-25), which ties to the even
+    24-bit value 2^-126 and is kept."""
+    assert _bits(oracle.mul(np.float32(1.0 - 2.0 ** -24), TINY)) == 0
+    b = np.float32(1082401 * 2.0 ** -146)
+    assert oracle.mul(np.float32(0.96875), b) == TINY
+    assert _bits(oracle.mul(np.float32(-0.96875), b)) == _bits(-TINY)
+    # just above the tie: 2^-126 (1 - 2^-25) is the exact value, so a product
+    # one step further below is flushed
+    assert oracle.mul(np.float32(0.96875), np.float32(np.nextafter(b, np.float32(0)))) == 0.0
 
 
 def test_no_fusion():
