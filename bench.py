@@ -1,0 +1,298 @@
+"""Benchmark of the bit-exact int8 LSQ linear layer and the ordered gradient
+reduction on one MI355X.
+
+One step = the whole hot path on synthetic inputs already resident in HBM:
+  (1) qat_linear_fwd + qat_linear_bwd of the attention QKV projection
+      (GQA 16 query / 4 KV heads of 128: X [16384, 2048], W [3072, 2048],
+      dY [16384, 3072], seed 1), and
+  (2) the single-device replay of one step's gradient reduction: 48 virtual
+      ranks (6 replicas x 8 shards) of 201,326,592 fp32 each, fed in mesh
+      order to ordered_reduce, then grad_l2norm_clip (max norm 1.0).
+value = fwd+bwd int8-QAT linear throughput in TOPS (6*M*N*K ops / time);
+ordered_reduce_GBps = algorithmic replay bytes / replay time.
+
+Prints one JSON line.  --gpus above 1 is refused (one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "bit-exact int8 QAT linear TOPS fwd+bwd (M=16384); ordered-reduce GB/s"
+
+# MI355X published peaks (dense) and the derived fp32 VALU rate without FMA
+# or packed instructions: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz.
+PEAK_HBM_GBPS = 8000.0
+PEAK_I8_TOPS = 5030.0
+PEAK_VALU_F32_TOPS = 256 * 64 * 2.4e9 / 1e12          # 39.32 T ops/s
+
+# Replay bytes per element index that the method must move with one partial
+# resident at a time: per replica, shard 0 copies (read G, write A: 8 B) and
+# shards 1..7 add (read A, read G, write A: 12 B each) -> 6 * (8 + 84) = 552;
+# TreeFold reads 6 accumulators and writes T (28 B, the squared-norm pass
+# fused into it would read nothing more); clip reads and writes T (8 B).
+REPLAY_BYTES_PER_ELEM = 6 * (8 + 7 * 12) + 28 + 8      # 588
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--replay-length", type=int, default=None, help="override the partial length")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=20.0, help="rough budget for the oracle sample")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events on the current stream around a region; summed per name."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.t = {}
+        self.n = {}
+
+    def region(self, name):
+        torch = self.torch
+        timer = self
+
+        class _R:
+            def __enter__(self):
+                self.a = torch.cuda.Event(enable_timing=True)
+                self.b = torch.cuda.Event(enable_timing=True)
+                self.a.record()
+                return self
+
+            def __exit__(self, *exc):
+                self.b.record()
+                timer.t.setdefault(name, []).append((self.a, self.b))
+                return False
+
+        return _R()
+
+    def ms(self, name):
+        pairs = self.t.get(name, [])
+        if not pairs:
+            return 0.0, 0
+        return sum(a.elapsed_time(b) for a, b in pairs), len(pairs)
+
+    def clear(self):
+        self.t.clear()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the replay of the "
+              "cluster's reduction is itself a single-device computation", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bitwise_reproducible_lsq_amd as brl
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = synth.CASES["qkv"]
+    rcase = synth.REPLAY
+    L = args.replay_length or rcase.length
+    R, S = rcase.replicas, rcase.shards
+    M, K, N = case.M, case.K, case.N
+
+    # ---- inputs, resident before timing ------------------------------------------
+    inp = synth.linear_inputs(case)
+    X = torch.from_numpy(inp.X).to(dev)
+    W = torch.from_numpy(inp.W).to(dev)
+    dY = torch.from_numpy(inp.dY).to(dev)
+    partials = [synth.replay_partial(rcase, v, device=dev, length=L) for v in range(R * S)]
+    state = brl.ReduceState(R, S, L, device=dev)
+    out = torch.empty(L, dtype=torch.float32, device=dev)
+    ws_f = brl.workspace(brl.OP_FWD, M, K, N, dev)
+    ws_b = brl.workspace(brl.OP_BWD, M, K, N, dev)
+    ws_n = brl.workspace(brl.OP_NORM, L, 0, 0, dev)
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    dX = torch.empty((M, K), dtype=torch.float32, device=dev)
+    dW = torch.empty((N, K), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    timer = Timer(torch)
+
+    def step(timed: bool):
+        with timer.region("linear"):
+            with timer.region("fwd"):
+                brl.qat_linear_fwd(X, W, synth.S_X, Y=Y, ws=ws_f)
+            with timer.region("bwd"):
+                brl.qat_linear_bwd(dY, X, W, synth.S_X, dX=dX, dW=dW, ws=ws_b)
+        state.reset()
+        with timer.region("replay"):
+            for v in range(R * S):
+                s = v % S
+                last = v == R * S - 1
+                if s == 0 or last:
+                    brl.ordered_reduce(state, partials[v], out=out)
+                else:
+                    with timer.region("accumulate"):
+                        brl.ordered_reduce(state, partials[v], out=out)
+            with timer.region("norm_clip"):
+                brl.grad_l2norm_clip(out, rcase.max_norm, ws=ws_n)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    timer.clear()
+
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    K_ = args.steps
+    lin_ms = timer.ms("linear")[0] / K_
+    fwd_ms = timer.ms("fwd")[0] / K_
+    bwd_ms = timer.ms("bwd")[0] / K_
+    rep_ms = timer.ms("replay")[0] / K_
+    acc_ms, acc_n = timer.ms("accumulate")
+    nc_ms = timer.ms("norm_clip")[0] / K_
+    acc_avg_ms = acc_ms / max(acc_n, 1)
+
+    # phase split of the backward (separate, after the timed steps)
+    def avg_call(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    pre_ms = avg_call(lambda: brl.qat_linear_bwd(dY, X, W, synth.S_X, need_dX=False, need_dW=False, ws=ws_b))
+    dx_ms = avg_call(lambda: brl.qat_linear_bwd(dY, X, W, synth.S_X, dX=dX, need_dW=False, ws=ws_b)) - pre_ms
+    dw_ms = avg_call(lambda: brl.qat_linear_bwd(dY, X, W, synth.S_X, dW=dW, need_dX=False, ws=ws_b)) - pre_ms
+
+    ops = 2.0 * M * N * K
+    tops = 3 * ops / (lin_ms * 1e-3) / 1e12
+    replay_bytes = REPLAY_BYTES_PER_ELEM * L
+    replay_gbps = replay_bytes / (rep_ms * 1e-3) / 1e9
+    acc_bytes = 12.0 * L
+    acc_gbps = acc_bytes / (acc_avg_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(tops, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": K_,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K_ * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8->i32 fwd GEMM; f32 bwd and replay",
+        "data": "synthetic (seeded Philox Gaussians; device-generated replay partials)",
+        "config": {
+            "workload": "QKV projection M=16384 K=2048 N=3072 fwd+bwd (seed 1) + replay 6x8 ranks "
+                        f"x {L} fp32 (seed 4), clip 1.0",
+            "M": M, "K": K, "N": N, "s_x": synth.S_X,
+            "replicas": R, "shards": S, "replay_length": L,
+        },
+        "ordered_reduce_GBps": round(replay_gbps, 1),
+        "phases_ms": {
+            "fwd": round(fwd_ms, 4), "bwd": round(bwd_ms, 4), "bwd_prelude": round(pre_ms, 4),
+            "dX": round(dx_ms, 4), "dW": round(dw_ms, 4), "linear_fwd_bwd": round(lin_ms, 4),
+            "replay": round(rep_ms, 4), "accumulate_avg": round(acc_avg_ms, 5),
+            "norm_clip": round(nc_ms, 4),
+        },
+        "roofline": {
+            "kernel": "accumulate_v4_kernel (ordered_reduce running sum, 41 launches per step)",
+            "bound": "hbm",
+            "achieved": round(acc_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(acc_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": None,
+        },
+        "rooflines_other": {
+            "replay_total": {"bound": "hbm", "achieved": round(replay_gbps, 1), "peak": PEAK_HBM_GBPS,
+                             "unit": "GB/s", "frac": round(replay_gbps / PEAK_HBM_GBPS, 4)},
+            "fwd_call": {"bound": "mfma", "achieved": round(ops / (fwd_ms * 1e-3) / 1e12, 2),
+                         "peak": PEAK_I8_TOPS, "unit": "TOPS",
+                         "frac": round(ops / (fwd_ms * 1e-3) / 1e12 / PEAK_I8_TOPS, 4)},
+            "dX": {"bound": "alu", "achieved": round(ops / (dx_ms * 1e-3) / 1e12, 3),
+                   "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
+                   "frac": round(ops / (dx_ms * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4)},
+            "dW": {"bound": "alu", "achieved": round(ops / (dw_ms * 1e-3) / 1e12, 3),
+                   "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
+                   "frac": round(ops / (dw_ms * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    some rows of Y and dX and some rows of dW of the QKV layer, and the replay
+    over a prefix of the element range."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    M, K = inp.X.shape
+    N = inp.W.shape[0]
+    s_w = oracle.weight_scale(inp.W)
+    g = np.random.default_rng(0)
+
+    def run(n_rows, n_wrows):
+        rows = np.sort(g.choice(M, n_rows, replace=False))
+        wr = np.sort(g.choice(N, n_wrows, replace=False))
+        t0 = time.perf_counter()
+        oracle.fwd_rows(inp.X, inp.W, synth.S_X, rows=rows, s_w=s_w)
+        oracle.dx_rows(inp.dY[rows], inp.X, inp.W, synth.S_X, rows, s_w=s_w)
+        oracle.dw_rows(np.ascontiguousarray(inp.dY[:, wr].T), inp.X, inp.W, synth.S_X, wr, s_w=s_w)
+        dt = time.perf_counter() - t0
+        return dt, 2.0 * K * N * n_rows * 2 + 2.0 * M * K * n_wrows
+
+    # calibrate on a small sample, then size the measured one to the budget
+    dt, _ = run(8, 2)
+    scale = max(1.0, 0.8 * budget_s / max(dt, 1e-3))
+    n_rows = int(min(M, 8 * scale))
+    n_wrows = int(min(N, 2 * scale))
+    t_lin, ops = run(n_rows, n_wrows)
+    rows, wr = range(n_rows), range(n_wrows)
+    # replay over 2^24 elements of each of the 48 ranks (8 distinct partials,
+    # each fed to six ranks: the oracle's cost does not depend on the values)
+    Ls = 1 << 24
+    distinct = [synth.replay_partial_host(synth.REPLAY.seed, v, Ls) for v in range(8)]
+    parts = [distinct[v % 8] for v in range(48)]
+    t0 = time.perf_counter()
+    oracle.replay(parts, 6, 8)
+    t_rep = time.perf_counter() - t0
+    return {
+        "value": round(ops / t_lin / 1e12, 6),
+        "unit": "TOPS",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"QKV layer: {len(rows)} rows of Y and dX, {len(wr)} rows of dW "
+                   f"({ops / 1e9:.1f} G ops, {t_lin:.1f} s); replay of 48 ranks x {Ls} elements "
+                   f"(8 distinct partials reused, {t_rep:.2f} s)"),
+        "ordered_reduce_GBps": round(REPLAY_BYTES_PER_ELEM * Ls / t_rep / 1e9, 3),
+    }
+
+
+if __name__ == "__main__":
+    main()
