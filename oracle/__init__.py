@@ -57,6 +57,7 @@ def lib():
         "or_swiglu_fwd": (None, [P, i64, i64, P]),
         "or_swiglu_bwd": (None, [P, P, i64, i64, P]),
         "or_fwd_rows": (i32, [P, P, i64, i64, i64, f32, f32, P, i32, P, i64, P, P]),
+        "or_fwd_cols": (i32, [P, P, i64, i64, i64, f32, f32, P, i64, P]),
         "or_dx_rows": (None, [P, P, P, i64, i64, f32, f32, P, i64, P]),
         "or_dw_rows": (None, [P, P, P, i64, i64, f32, f32, P, i64, i64, P]),
         "or_replay_accumulate": (None, [P, P, i64, i32]),
@@ -156,6 +157,21 @@ def fwd_rows(X, W, s_x, rows=None, addend=None, epilogue=0, s_w=None):
     if rc != 0:
         raise OverflowError("int32 accumulator overflow in the oracle GEMM")
     return (Y, ypre) if epilogue == 1 else Y
+
+
+def fwd_cols(X, W, s_x, cols, s_w=None):
+    """Y[:, cols] (pre-activation) as a [len(cols), M] array."""
+    X, W = _f32(X), _f32(W)
+    M, K = X.shape
+    N = W.shape[0]
+    if s_w is None:
+        s_w = weight_scale(W)
+    cols = np.ascontiguousarray(cols, np.int64)
+    out = np.empty((cols.size, M), np.float32)
+    rc = lib().or_fwd_cols(_p(X), _p(W), M, K, N, float(s_x), float(s_w), _p(cols), cols.size, _p(out))
+    if rc != 0:
+        raise OverflowError("int32 accumulator overflow in the oracle GEMM")
+    return out
 
 
 def swiglu_fwd(ypre):

@@ -360,6 +360,36 @@ int or_fwd_rows(const float* X, const float* W, int64_t M, int64_t K, int64_t N,
     return bad ? -1 : 0;
 }
 
+/* Y[:, n] for n in cols (no activation): the same definition column-wise,
+ * for sampling columns of a large product.  Ycols is [ncols, M]. */
+int or_fwd_cols(const float* X, const float* W, int64_t M, int64_t K, int64_t N, float s_x,
+                float s_w, const int64_t* cols, int64_t ncols, float* Ycols) {
+    (void)N;
+    fp_env_default();
+    int8_t* qx = (int8_t*)malloc((size_t)(M * K > 0 ? M * K : 1));
+    uint8_t* inx = (uint8_t*)malloc((size_t)(M * K > 0 ? M * K : 1));
+    or_quantize(X, M * K, s_x, qx, inx);
+    float s_y = or_mul(s_x, s_w);
+    int bad = 0;
+    PARALLEL_BEGIN
+    int8_t* qw = (int8_t*)malloc((size_t)K);
+    #pragma omp for schedule(dynamic, 1)
+    for (int64_t c = 0; c < ncols; ++c) {
+        int64_t n = cols[c];
+        for (int64_t k = 0; k < K; ++k) { uint8_t in; quantize_one(W[n * K + k], s_w, &qw[k], &in); }
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k) acc += (int64_t)qx[m * K + k] * (int64_t)qw[k];
+            if (acc >= 2147483648LL || acc < -2147483648LL) bad = 1;
+            Ycols[c * M + m] = or_mul(or_i2f((int32_t)acc), s_y);
+        }
+    }
+    free(qw);
+    PARALLEL_END
+    free(qx); free(inx);
+    return bad ? -1 : 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Straight-through backward                                                 */
 /* ------------------------------------------------------------------------ */

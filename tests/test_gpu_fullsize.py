@@ -1,0 +1,154 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times, against the oracle on sampled outputs it can compute one by one
+(rows of Y and dX, rows of dW) -- and for the replay, on every element.
+
+Workloads (seeded, synthetic; shapes of the Open-1B recipe on the onedev.kr
+summary, "Use" and "Limits": 16,384 tokens per GPU microbatch, GQA with 16
+query and 4 KV heads, SwiGLU gate+up as one GEMM, 6x8 replay mesh):
+  qkv             X [16384,2048], W [3072,2048], dY [16384,3072]
+  swiglu_gate_up  X [16384,2048], W [11264,2048] (gate rows 0..5631, up rows
+                  5632..11263), dA [16384,5632]
+  down_proj       H [16384,5632] ~ SiLU(a)*b, W [2048,5632], dY [16384,2048],
+                  dW accumulated over 4 microbatches of 4096 rows
+  replay_6x8      48 partials of 201,326,592 fp32 ~ N(0, 1e-4)
+Tolerance 0 ULP everywhere.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bitwise_reproducible_lsq_amd as brl
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _bits(x):
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(x, np.float32).view(np.uint32)
+
+
+def assert_bitwise(got, want, what):
+    g, w = _bits(got), _bits(want)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    bad = np.flatnonzero(g.ravel() != w.ravel())
+    if bad.size:
+        i = bad[0]
+        raise AssertionError(f"{what}: {bad.size} of {g.size} differ; first at flat {i}: "
+                             f"got {g.ravel()[i]:#010x} want {w.ravel()[i]:#010x}")
+
+
+def _sample(n, edges, k, seed):
+    g = np.random.default_rng(seed)
+    s = set(e for e in edges if 0 <= e < n)
+    s.update(int(x) for x in g.choice(n, k, replace=False))
+    return np.array(sorted(s), np.int64)
+
+
+def _cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+TILE_EDGES_M = [0, 1, 63, 64, 255, 256, 4095, 4096, 8191, 16383]
+
+
+def test_qkv_full_size():
+    case = synth.CASES["qkv"]
+    inp = synth.linear_inputs(case)
+    X, W, dY = _cuda(inp.X), _cuda(inp.W), _cuda(inp.dY)
+    Y, _, s_w = brl.qat_linear_fwd(X, W, case.s_x)
+    dX, dW = brl.qat_linear_bwd(dY, X, W, case.s_x)
+    torch.cuda.synchronize()
+    w_sw = oracle.weight_scale(inp.W)
+    assert_bitwise(s_w, np.array([w_sw]), "s_w")
+    rows = _sample(case.M, TILE_EDGES_M, 8, 1)
+    assert_bitwise(Y[rows], oracle.fwd_rows(inp.X, inp.W, case.s_x, rows=rows, s_w=w_sw), "Y rows")
+    assert_bitwise(dX[rows], oracle.dx_rows(inp.dY[rows], inp.X, inp.W, case.s_x, rows, s_w=w_sw), "dX rows")
+    wr = _sample(case.N, [0, 1, 2047, 2048, 2559, 2560, 3071], 5, 2)
+    want = oracle.dw_rows(np.ascontiguousarray(inp.dY[:, wr].T), inp.X, inp.W, case.s_x, wr, s_w=w_sw)
+    assert_bitwise(dW[wr], want, "dW rows")
+
+
+def test_swiglu_gate_up_full_size():
+    case = synth.CASES["swiglu_gate_up"]
+    inp = synth.linear_inputs(case)
+    H = case.N // 2
+    X, W, dA = _cuda(inp.X), _cuda(inp.W), _cuda(inp.dY)
+    A, Ypre, s_w = brl.qat_linear_fwd(X, W, case.s_x, epilogue=brl.EPILOGUE_SWIGLU)
+    dX, dW = brl.qat_linear_bwd(dA, X, W, case.s_x, Ypre=Ypre, epilogue=brl.EPILOGUE_SWIGLU)
+    torch.cuda.synchronize()
+    w_sw = oracle.weight_scale(inp.W)
+    assert_bitwise(s_w, np.array([w_sw]), "s_w")
+    rows = _sample(case.M, TILE_EDGES_M, 4, 3)
+    wA, wPre = oracle.fwd_rows(inp.X, inp.W, case.s_x, rows=rows, epilogue=1, s_w=w_sw)
+    assert_bitwise(Ypre[rows], wPre, "Ypre rows")
+    assert_bitwise(A[rows], wA, "SwiGLU rows")
+    G_rows = oracle.swiglu_bwd(wPre, inp.dY[rows])
+    assert_bitwise(dX[rows], oracle.dx_rows(G_rows, inp.X, inp.W, case.s_x, rows, s_w=w_sw), "dX rows")
+    js = _sample(H, [0, 63, 64, 5631], 2, 4)
+    cols = np.concatenate([js, js + H])
+    Yc = oracle.fwd_cols(inp.X, inp.W, case.s_x, cols, s_w=w_sw)          # [2J, M]
+    Gc = []
+    for t, j in enumerate(js):
+        pair = np.ascontiguousarray(np.stack([Yc[t], Yc[t + len(js)]], axis=1))   # [M, 2] = (g, u)
+        d = oracle.swiglu_bwd(pair, np.ascontiguousarray(inp.dY[:, j:j + 1]))
+        Gc.append((d[:, 0].copy(), d[:, 1].copy()))
+    dY_cols = np.stack([g for g, _ in Gc] + [u for _, u in Gc])
+    want = oracle.dw_rows(dY_cols, inp.X, inp.W, case.s_x, cols, s_w=w_sw)
+    assert_bitwise(dW[cols], want, "dW rows (gate and up)")
+
+
+def test_down_proj_full_size_microbatches():
+    case = synth.CASES["down_proj"]
+    inp = synth.linear_inputs(case)
+    X, W, dY = _cuda(inp.X), _cuda(inp.W), _cuda(inp.dY)
+    B = case.microbatches
+    mb = case.M // B
+    Y, _, s_w = brl.qat_linear_fwd(X, W, case.s_x)
+    dX = torch.empty_like(X)
+    dW = None
+    for b in range(B):
+        sl = slice(b * mb, (b + 1) * mb)
+        dXb, dW = brl.qat_linear_bwd(dY[sl], X[sl], W, case.s_x, dX=dX[sl], dW=dW, dW_accumulate=b > 0)
+    torch.cuda.synchronize()
+    w_sw = oracle.weight_scale(inp.W)
+    assert (np.abs(inp.X / case.s_x) > 127).any(), "some activations should clip"
+    rows = _sample(case.M, TILE_EDGES_M, 6, 5)
+    assert_bitwise(Y[rows], oracle.fwd_rows(inp.X, inp.W, case.s_x, rows=rows, s_w=w_sw), "Y rows")
+    assert_bitwise(dX[rows], oracle.dx_rows(inp.dY[rows], inp.X, inp.W, case.s_x, rows, s_w=w_sw), "dX rows")
+    wr = _sample(case.N, [0, 1, 2047], 3, 6)
+    want = oracle.dw_rows(np.ascontiguousarray(inp.dY[:, wr].T), inp.X, inp.W, case.s_x, wr, mb=mb, s_w=w_sw)
+    assert_bitwise(dW[wr], want, "dW rows (4 microbatches)")
+
+
+def test_replay_full_size():
+    """All 48 ranks at 201,326,592 elements; every element of the clipped
+    TreeFold and the norm are compared."""
+    rc = synth.REPLAY
+    R, S, L = rc.replicas, rc.shards, rc.length
+    st = brl.ReduceState(R, S, L, device=DEV)
+    out = torch.empty(L, dtype=torch.float32, device=DEV)
+    A = [np.empty(L, np.float32) for _ in range(R)]
+    host = np.empty(L, np.float32)
+    last_part = None
+    for v in range(R * S):
+        G = synth.replay_partial(rc, v, device=DEV)
+        brl.ordered_reduce(st, G, out=out)
+        torch.cuda.synchronize()
+        host[:] = G.cpu().numpy()
+        r, s = divmod(v, S)
+        oracle.replay_accumulate(A[r], host, first=(s == 0))
+        del G
+    nu = brl.grad_l2norm_clip(out, rc.max_norm)
+    torch.cuda.synchronize()
+    T = oracle.treefold(A)
+    wnu = oracle.l2norm(T)
+    oracle.clip(T, wnu, rc.max_norm, 0.0)
+    assert_bitwise(nu, np.array([wnu]), "nu")
+    assert float(wnu) > 1.0
+    assert_bitwise(out, T, "clipped TreeFold")
+    for r in range(R - 1):
+        assert_bitwise(st.acc[r], A[r], f"A_{r}")

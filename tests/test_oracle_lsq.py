@@ -316,3 +316,11 @@ def test_fwd_swiglu_epilogue():
     Y, ypre = oracle.linear_fwd(X, W, s_x, epilogue=1)
     assert (_bits(ypre) == _bits(oracle.linear_fwd(X, W, s_x))).all()
     assert (_bits(Y) == _bits(oracle.swiglu_fwd(ypre))).all()
+
+
+def test_fwd_columns_match_rows():
+    """Column sampling of Y is the same definition as row sampling."""
+    X, W = _small_inputs(50, 40, 30)
+    Y = oracle.linear_fwd(X, W, np.float32(0.05))
+    cols = [0, 7, 29]
+    assert (_bits(oracle.fwd_cols(X, W, np.float32(0.05), cols)) == _bits(Y[:, cols].T)).all()
