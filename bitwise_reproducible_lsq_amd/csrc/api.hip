@@ -14,7 +14,7 @@ namespace brl {
 
 // ---- tuning knobs (launch shapes only) -----------------------------------------
 static std::atomic<int64_t> g_tune[3] = {{0}, {0}, {0}};
-static const int64_t kTuneDefault[3] = {5, 256, 4096};
+static const int64_t kTuneDefault[3] = {5, 256, 1};
 
 int bwd_chunk_log2() {
     int64_t v = g_tune[BRL_TUNE_BWD_CHUNK_LOG2].load();
@@ -24,9 +24,9 @@ int reduce_wg_blocks() {
     int64_t v = g_tune[BRL_TUNE_REDUCE_WG_BLOCKS].load();
     return (int)(v > 0 ? v : kTuneDefault[BRL_TUNE_REDUCE_WG_BLOCKS]);
 }
-int stream_wgs() {
-    int64_t v = g_tune[BRL_TUNE_STREAM_WGS].load();
-    return (int)(v > 0 ? v : kTuneDefault[BRL_TUNE_STREAM_WGS]);
+int stream_vec() {
+    int64_t v = g_tune[BRL_TUNE_STREAM_VEC].load();
+    return (int)(v > 0 ? v : kTuneDefault[BRL_TUNE_STREAM_VEC]);
 }
 
 // ---- the SwiGLU exp constants, derived from ln 2 ---------------------------------
@@ -296,11 +296,8 @@ brl_status ordered_reduce(brl_reduce_state* sp, const float* partial, float* out
     brl_status rc = BRL_OK;
     if (n > 0) {
         if (!last) {
-            if (s == 0)
-                rc = check_hip(hipMemcpyAsync(sp->acc[r], partial, (size_t)n * sizeof(float),
-                                              hipMemcpyDeviceToDevice, st), "running sum (first shard)");
-            else
-                rc = check_hip(launch_accumulate(sp->acc[r], partial, n, st), "running sum");
+            rc = check_hip(launch_accumulate(sp->acc[r], partial, n, s == 0, st),
+                           s == 0 ? "running sum (first shard)" : "running sum");
         } else {
             FoldPtrs p{};
             for (int i = 0; i < R; ++i) p.a[i] = sp->acc[i];
@@ -350,6 +347,7 @@ int64_t brl_set_tuning(int32_t knob, int64_t value) {
     if (knob == BRL_TUNE_BWD_CHUNK_LOG2 && value > 6) value = 6;
     if (knob == BRL_TUNE_REDUCE_WG_BLOCKS && value > 0 && value != 64 && value != 128 && value != 256)
         value = 256;
+    if (knob == BRL_TUNE_STREAM_VEC && value > 0 && value != 1 && value != 2 && value != 4) value = 1;
     int64_t old = g_tune[knob].exchange(value > 0 ? value : 0);
     return old > 0 ? old : kTuneDefault[knob];
 }

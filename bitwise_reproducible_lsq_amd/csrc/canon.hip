@@ -38,44 +38,53 @@ __device__ void canon_finish(float S, const CanonFinishArgs& f) {
     }
 }
 
-// Pass 1: thread t of workgroup w sums block j = w*WGB + t.
+// Pass 1: thread t of workgroup w sums block j = w*WGB + t.  The workgroup's
+// WGB*32 elements are loaded coalesced (16-byte vectors when aligned) and
+// transposed through LDS rows of 33 floats, so that each thread then walks
+// its own 32 consecutive elements left to right without bank conflicts.
 template <int MAP, int WGB>
 __global__ __launch_bounds__(WGB) void canon_pass1_kernel(const float* __restrict__ x, int64_t n,
                                                          float* __restrict__ roots, int last,
                                                          CanonFinishArgs fin) {
+    constexpr int kRow = kBlock + 1;
+    __shared__ float tile[WGB * kRow];
     __shared__ float lds[WGB];
-    const int64_t J = (n + kBlock - 1) / kBlock;
-    const int64_t j = (int64_t)blockIdx.x * WGB + threadIdx.x;
+    const int t = threadIdx.x;
+    const int64_t base = (int64_t)blockIdx.x * WGB * kBlock;
+    const int64_t avail = n - base;
+    const int span = avail < (int64_t)WGB * kBlock ? (int)avail : WGB * kBlock;
+    const float* src = x + base;
+    if (span == WGB * kBlock && ((reinterpret_cast<uintptr_t>(src) & 15) == 0)) {
+        const vf4* s4 = reinterpret_cast<const vf4*>(src);
+#pragma unroll
+        for (int k = 0; k < kBlock / 4; ++k) {
+            const int v = t + k * WGB;              // vector index in the span
+            const vf4 q = __builtin_nontemporal_load(s4 + v);
+            const int e = 4 * v, b = e >> 5, o = e & 31;
+            float* d = &tile[b * kRow + o];
+            d[0] = q.x; d[1] = q.y; d[2] = q.z; d[3] = q.w;
+        }
+    } else {
+        for (int e = t; e < span; e += WGB) tile[(e >> 5) * kRow + (e & 31)] = src[e];
+    }
+    __syncthreads();
     float s = 0.0f;
-    if (j < J) {
-        const int64_t base = j * kBlock;
-        const float* p = x + base;
-        const int64_t len = (n - base) < kBlock ? (n - base) : kBlock;
-        if (len == kBlock && ((reinterpret_cast<uintptr_t>(p) & 15) == 0)) {
-            const vf4* p4 = reinterpret_cast<const vf4*>(p);
-            vf4 v[8];
+    const int len = span - t * kBlock;               // elements of this thread's block
+    if (len > 0) {
+        const float* p = &tile[t * kRow];
+        s = canon_map<MAP>(p[0]);
+        if (len >= kBlock) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = __builtin_nontemporal_load(p4 + q);
-            s = canon_map<MAP>(v[0].x);
-            s = f_add(s, canon_map<MAP>(v[0].y));
-            s = f_add(s, canon_map<MAP>(v[0].z));
-            s = f_add(s, canon_map<MAP>(v[0].w));
-#pragma unroll
-            for (int q = 1; q < 8; ++q) {
-                s = f_add(s, canon_map<MAP>(v[q].x));
-                s = f_add(s, canon_map<MAP>(v[q].y));
-                s = f_add(s, canon_map<MAP>(v[q].z));
-                s = f_add(s, canon_map<MAP>(v[q].w));
-            }
+            for (int i = 1; i < kBlock; ++i) s = f_add(s, canon_map<MAP>(p[i]));
         } else {
-            s = canon_map<MAP>(p[0]);
-            for (int64_t i = 1; i < len; ++i) s = f_add(s, canon_map<MAP>(p[i]));
+            for (int i = 1; i < len; ++i) s = f_add(s, canon_map<MAP>(p[i]));
         }
     }
-    int64_t rem = J - (int64_t)blockIdx.x * WGB;
+    const int64_t J = (n + kBlock - 1) / kBlock;
+    const int64_t rem = J - (int64_t)blockIdx.x * WGB;
     const int count = rem < WGB ? (int)(rem < 0 ? 0 : rem) : WGB;
     float r = wg_pair_tree(s, count, lds);
-    if (threadIdx.x == 0) {
+    if (t == 0) {
         if (last) canon_finish(r, fin);
         else roots[blockIdx.x] = r;
     }

@@ -86,34 +86,50 @@ hipError_t launch_quantize(const float* v, int64_t rows, int64_t cols, const flo
 }
 
 // ---- int8 GEMM ---------------------------------------------------------------------
-// Workgroup tile BM x BN, K step 64 (two MFMA k-steps of 32), waves of WM x WN,
-// each wave a (WM/32) x (WN/32) grid of 32x32 MFMA tiles.
-// LDS rows are 64 bytes of k padded to 80 so that 16-byte fragment reads of
-// consecutive rows fall in distinct banks.
+// Workgroup tile BM x BN (256 x 256), K step 64 bytes (two MFMA k-steps of 32),
+// 4 waves of 128 x 128, each a 4 x 4 grid of v_mfma_i32_32x32x32_i8 tiles.
+// Operand tiles move global -> LDS with global_load_lds_dwordx4 (no staging
+// registers) through a ring of kStages LDS stages, so loads run kStages-1
+// tiles ahead of the MFMAs.  LDS rows are 64 bytes, unpadded; the four
+// 16-byte chunks of row r are stored XOR-swizzled by (r >> 1) & 3, which puts
+// the 16-byte fragment reads of 8 consecutive rows in 8 distinct bank groups.
 constexpr int kBK = 64;
-constexpr int kLdsPitch = 80;
+constexpr int kStages = 4;
 
 template <int BM, int BN, int WM, int WN>
 struct GemmCfg {
     static constexpr int kWavesM = BM / WM, kWavesN = BN / WN;
     static constexpr int kThreads = kWavesM * kWavesN * 64;
+    static constexpr int kWaves = kThreads / 64;
     static constexpr int kTM = WM / 32, kTN = WN / 32;
-    static constexpr int kAChunks = BM * (kBK / 16) / kThreads;   // 16-byte chunks per thread
-    static constexpr int kBChunks = BN * (kBK / 16) / kThreads;
-    static constexpr int kLdsA = BM * kLdsPitch, kLdsB = BN * kLdsPitch;
+    static constexpr int kTileA = BM * kBK, kTileB = BN * kBK;      // bytes per stage
+    static constexpr int kStage = kTileA + kTileB;
+    // one load instruction moves 64 lanes x 16 bytes = 16 rows of 64 bytes
+    static constexpr int kLoadsA = BM / 16 / kWaves, kLoadsB = BN / 16 / kWaves;
+    static constexpr int kLoads = kLoadsA + kLoadsB;                // per wave per stage
 };
 
-template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+
+// s_waitcnt with vmcnt <= n (n a multiple of the per-stage load count),
+// expcnt and lgkmcnt left unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(GemmArgs a) {
     using C = GemmCfg<BM, BN, WM, WN>;
     static_assert(C::kThreads == 256, "the GEMM runs 4 waves per workgroup");
     extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-    int8_t* As = smem;                       // [2][BM][pitch]
-    int8_t* Bs = smem + 2 * C::kLdsA;        // [2][BN][pitch]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave index kept wave-uniform (scalar), so LDS bases for the direct
+    // loads are computed on the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::kWavesN, wn = wave % C::kWavesN;
 
     // tile of this workgroup; consecutive ids walk down M inside a column of
@@ -125,35 +141,27 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(GemmArgs a) {
 
     const int8_t* gA = a.qx + m0 * a.Kp;
     const int8_t* gB = a.qw + n0 * a.Kp;
-    const int64_t KT = a.Kp / kBK;
+    const int KT = (int)(a.Kp / kBK);
 
-    v4i ra[C::kAChunks], rb[C::kBChunks];
-    auto gload = [&](int64_t kt) {
+    // this lane's share of one load instruction: row (lane >> 2) of a 16-row
+    // group, LDS slot (lane & 3), holding global chunk swz(row, slot)
+    const int lrow = lane >> 2, lslot = lane & 3;
+    auto issue = [&](int kt, int stage) {
+        int8_t* sA = smem + stage * C::kStage;
+        int8_t* sB = sA + C::kTileA;
 #pragma unroll
-        for (int c = 0; c < C::kAChunks; ++c) {
-            const int idx = tid + c * C::kThreads;
-            const int row = idx >> 2, seg = (idx & 3) * 16;
-            ra[c] = *reinterpret_cast<const v4i*>(gA + row * a.Kp + kt * kBK + seg);
+        for (int i = 0; i < C::kLoadsA; ++i) {
+            const int r0 = (wave * C::kLoadsA + i) * 16;
+            const int r = r0 + lrow;
+            const int8_t* g = gA + (int64_t)r * a.Kp + kt * kBK + 16 * swz(r, lslot);
+            __builtin_amdgcn_global_load_lds(g, sA + r0 * kBK, 16, 0, 0);
         }
 #pragma unroll
-        for (int c = 0; c < C::kBChunks; ++c) {
-            const int idx = tid + c * C::kThreads;
-            const int row = idx >> 2, seg = (idx & 3) * 16;
-            rb[c] = *reinterpret_cast<const v4i*>(gB + row * a.Kp + kt * kBK + seg);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < C::kAChunks; ++c) {
-            const int idx = tid + c * C::kThreads;
-            const int row = idx >> 2, seg = (idx & 3) * 16;
-            *reinterpret_cast<v4i*>(As + buf * C::kLdsA + row * kLdsPitch + seg) = ra[c];
-        }
-#pragma unroll
-        for (int c = 0; c < C::kBChunks; ++c) {
-            const int idx = tid + c * C::kThreads;
-            const int row = idx >> 2, seg = (idx & 3) * 16;
-            *reinterpret_cast<v4i*>(Bs + buf * C::kLdsB + row * kLdsPitch + seg) = rb[c];
+        for (int i = 0; i < C::kLoadsB; ++i) {
+            const int r0 = (wave * C::kLoadsB + i) * 16;
+            const int r = r0 + lrow;
+            const int8_t* g = gB + (int64_t)r * a.Kp + kt * kBK + 16 * swz(r, lslot);
+            __builtin_amdgcn_global_load_lds(g, sB + r0 * kBK, 16, 0, 0);
         }
     };
 
@@ -165,41 +173,76 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(GemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
     const int frow = lane & 31;            // fragment row (A) / column (B)
-    const int fk = (lane >> 5) * 16;       // byte offset of this lane's 16 k-values
-    for (int64_t kt = 0; kt < KT; ++kt) {
-        const int cur = (int)(kt & 1);
-        if (kt + 1 < KT) gload(kt + 1);
-        const int8_t* Ab = As + cur * C::kLdsA + (wm * WM + frow) * kLdsPitch + fk;
-        const int8_t* Bb = Bs + cur * C::kLdsB + (wn * WN + frow) * kLdsPitch + fk;
+    const int fchunk = lane >> 5;          // this lane's 16-byte k chunk within a 32-k step
+    // Fragments of one 32-k step (4 of A, 4 of B) live in registers.  The
+    // reads of the next step are issued before the 16 MFMAs of the current
+    // one, so LDS latency hides behind matrix work; the barrier that lands
+    // the next tile sits between a tile's two steps, with MFMAs in flight.
+    using Frag = v4i[C::kTM + C::kTN];
+    auto read_frags = [&](int stage, int ks, Frag& F) {
+        const int8_t* sA = smem + stage * C::kStage;
+        const int8_t* sB = sA + C::kTileA;
+        const int chunk = fchunk + 2 * ks;
 #pragma unroll
-        for (int kk = 0; kk < kBK; kk += 32) {
-            v4i fa[C::kTM], fb[C::kTN];
+        for (int i = 0; i < C::kTM; ++i) {
+            const int r = wm * WM + i * 32 + frow;
+            F[i] = *reinterpret_cast<const v4i*>(sA + r * kBK + 16 * swz(r, chunk));
+        }
 #pragma unroll
-            for (int i = 0; i < C::kTM; ++i)
-                fa[i] = *reinterpret_cast<const v4i*>(Ab + i * 32 * kLdsPitch + kk);
+        for (int j = 0; j < C::kTN; ++j) {
+            const int r = wn * WN + j * 32 + frow;
+            F[C::kTM + j] = *reinterpret_cast<const v4i*>(sB + r * kBK + 16 * swz(r, chunk));
+        }
+    };
+    auto mfmas = [&](const Frag& F) {
+#pragma unroll
+        for (int i = 0; i < C::kTM; ++i)
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j)
-                fb[j] = *reinterpret_cast<const v4i*>(Bb + j * 32 * kLdsPitch + kk);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[i], F[C::kTM + j], acc[i][j], 0, 0, 0);
+    };
+    // wait until tile t has landed in LDS for every wave (loads of the tiles
+    // after it, up to min(KT-1, newest), may stay in flight), then barrier
+    auto land = [&](int t, int newest) {
+        const int last = newest < KT - 1 ? newest : KT - 1;
+        const int ahead = last - t;
+        if (ahead >= 2) wait_vmcnt<2 * C::kLoads>();
+        else if (ahead == 1) wait_vmcnt<C::kLoads>();
+        else wait_vmcnt<0>();
+        // bare barrier: a fence here would wait for every load in flight
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    };
+
+    static_assert(kBK == 64, "two k-steps per tile");
+    Frag F0, F1;
 #pragma unroll
-            for (int i = 0; i < C::kTM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::kTN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < KT) sstore(cur ^ 1);
-        __syncthreads();
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < KT) issue(s, s);
+    land(0, kStages - 2);
+    read_frags(0, 0, F0);
+    // every tile but the last hands over to the next one; the last is peeled
+    // so that the loop body has no branch between LDS reads and their use
+    for (int kt = 0; kt < KT - 1; ++kt) {
+        read_frags(kt % kStages, 1, F1);
+        mfmas(F0);
+        // tile kt-1's stage is free once every wave passes this barrier
+        land(kt + 1, kt + kStages - 2);
+        if (kt + kStages - 1 < KT) issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
+        read_frags((kt + 1) % kStages, 0, F0);
+        mfmas(F1);
     }
+    read_frags((KT - 1) % kStages, 1, F1);
+    mfmas(F0);
+    mfmas(F1);
 
     // ---- epilogue: Y = fl(acc) * s_y (+ addend), or the SwiGLU activation ----
     const float s_y = a.scal->s_y;
     const int col_l = lane & 31;
     const int row_q = (lane >> 5) * 4;
-    if (a.epilogue == BRL_EPILOGUE_SWIGLU) {
+    if constexpr (EPI == BRL_EPILOGUE_SWIGLU) {
         // wave columns: tiles [0, kTN/2) are gate, [kTN/2, kTN) the matching up
         const int64_t H = a.N / 2;
 #pragma unroll
@@ -228,40 +271,60 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(GemmArgs a) {
                 }
             }
     } else {
+        // whole tile inside Y and no addend: branch-free stores
+        const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N) && !a.addend;
+        if (full) {
+            float* Yw = a.Y + (m0 + wm * WM + row_q) * a.N + n0 + wn * WN + col_l;
 #pragma unroll
-        for (int i = 0; i < C::kTM; ++i)
+            for (int i = 0; i < C::kTM; ++i)
 #pragma unroll
-            for (int j = 0; j < C::kTN; ++j) {
-                const int64_t col = n0 + wn * WN + j * 32 + col_l;
+                for (int j = 0; j < C::kTN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = m0 + wm * WM + i * 32 + (r >> 2) * 8 + row_q + (r & 3);
-                    if (row < a.M && col < a.N) {
-                        float y = f_mul((float)acc[i][j][r], s_y);
-                        if (a.addend) y = f_add(y, a.addend[row * a.N + col]);
-                        a.Y[row * a.N + col] = y;
+                    for (int r = 0; r < 16; ++r)
+                        Yw[(int64_t)(i * 32 + (r >> 2) * 8 + (r & 3)) * a.N + j * 32] =
+                            f_mul((float)acc[i][j][r], s_y);
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::kTN; ++j) {
+                    const int64_t col = n0 + wn * WN + j * 32 + col_l;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t row = m0 + wm * WM + i * 32 + (r >> 2) * 8 + row_q + (r & 3);
+                        if (row < a.M && col < a.N) {
+                            float y = f_mul((float)acc[i][j][r], s_y);
+                            if (a.addend) y = f_add(y, a.addend[row * a.N + col]);
+                            a.Y[row * a.N + col] = y;
+                        }
                     }
                 }
-            }
+        }
     }
 }
 
-hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t st) {
+template <int EPI>
+static hipError_t launch_gemm_epi(const GemmArgs& a, hipStream_t st) {
     constexpr int BM = 256, BN = 256, WM = 128, WN = 128;
     using C = GemmCfg<BM, BN, WM, WN>;
-    static_assert(C::kAChunks * C::kThreads == BM * 4, "A tile load split");
-    static_assert(C::kBChunks * C::kThreads == BN * 4, "B tile load split");
-    const size_t lds = 2 * (size_t)(C::kLdsA + C::kLdsB);
+    static_assert(C::kLoadsA * C::kWaves * 16 == BM && C::kLoadsB * C::kWaves * 16 == BN, "load split");
+    static_assert(2 * C::kLoads < 64, "vmcnt range");
+    const size_t lds = (size_t)kStages * C::kStage;
     static bool attr = false;
     if (!attr) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_i8_kernel<BM, BN, WM, WN>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_i8_kernel<BM, BN, WM, WN, EPI>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         attr = true;
     }
     const int64_t tiles = (a.Mp / BM) * (a.Nvp / BN);
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN>), dim3((unsigned)tiles), dim3(C::kThreads), lds,
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, EPI>), dim3((unsigned)tiles), dim3(C::kThreads), lds,
                        st, a);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t st) {
+    if (a.epilogue == BRL_EPILOGUE_SWIGLU) return launch_gemm_epi<BRL_EPILOGUE_SWIGLU>(a, st);
+    return launch_gemm_epi<BRL_EPILOGUE_NONE>(a, st);
 }
 
 }  // namespace brl

@@ -26,7 +26,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Launch-shape knobs (never change results).
 int bwd_chunk_log2();          // 32-blocks per backward chunk = 2^value
 int reduce_wg_blocks();        // 32-blocks per workgroup in CanonSum passes
-int stream_wgs();              // workgroups for streaming kernels
+int stream_vec();              // 16-byte vectors per thread in streaming kernels (1, 2, 4)
 
 // ---- CanonSum over a flat vector -------------------------------------------
 enum CanonMap { kMapAbs = 0, kMapSquare = 1 };
@@ -102,7 +102,8 @@ hipError_t launch_swiglu_bwd(const float* dA, const float* ypre, int64_t M, int6
                              const ExpConsts& ek, hipStream_t st);
 
 // ---- replay -------------------------------------------------------------------
-hipError_t launch_accumulate(float* A, const float* G, int64_t n, hipStream_t st);
+// first = 1: A <- G; otherwise A <- A + G.
+hipError_t launch_accumulate(float* A, const float* G, int64_t n, int first, hipStream_t st);
 struct FoldPtrs { const float* a[64]; };
 hipError_t launch_fold(const FoldPtrs& p, int R, const float* g_last, float* out, int64_t n,
                        hipStream_t st);

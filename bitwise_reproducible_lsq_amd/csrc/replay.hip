@@ -4,9 +4,10 @@
 // across replicas in recursive-doubling pairing order, and the clip scale
 // pass of the global-norm clip (same page, recipe paragraph).
 //
-// All three are elementwise and bound by HBM: 16-byte vector loads and
-// stores, non-temporal (each byte is touched once per pass), grid-stride
-// loops over a fixed number of workgroups.
+// All are elementwise and bound by HBM: 16-byte non-temporal vector loads and
+// stores (each byte is touched once per pass) in one-shot grids, one vector
+// per thread by default -- the fastest shape measured on MI355X for these
+// read/write mixes.
 #include "internal.hpp"
 
 #pragma clang fp contract(off)
@@ -15,54 +16,94 @@ namespace brl {
 
 constexpr int kStreamThreads = 256;
 
-static unsigned stream_grid(int64_t n4) {
-    int64_t want = ceil_div(n4, kStreamThreads);
-    int64_t cap = stream_wgs();
-    if (want > cap) want = cap;
-    if (want < 1) want = 1;
-    return (unsigned)want;
+// One-shot grids: each thread handles V 16-byte vectors, V = the stream
+// vector knob (1 by default: the fastest shape measured on MI355X).
+static unsigned stream_grid(int64_t n4, int V) {
+    int64_t g = ceil_div(n4, (int64_t)kStreamThreads * V);
+    return (unsigned)(g < 1 ? 1 : g);
 }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+template <int V>
+__device__ __forceinline__ int64_t vec_index(int u) {
+    return ((int64_t)blockIdx.x * V + u) * kStreamThreads + threadIdx.x;
+}
+
 // A <- A + G
+template <int V>
 __global__ __launch_bounds__(kStreamThreads) void accumulate_v4_kernel(vf4* __restrict__ A,
                                                                        const vf4* __restrict__ G,
                                                                        int64_t n4) {
-    const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n4; i += stride) {
-        vf4 a = __builtin_nontemporal_load(A + i);
-        vf4 g = __builtin_nontemporal_load(G + i);
-        a.x = f_add(a.x, g.x);
-        a.y = f_add(a.y, g.y);
-        a.z = f_add(a.z, g.z);
-        a.w = f_add(a.w, g.w);
-        __builtin_nontemporal_store(a, A + i);
+    vf4 a[V], g[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int64_t i = vec_index<V>(u);
+        if (i < n4) { a[u] = __builtin_nontemporal_load(A + i); g[u] = __builtin_nontemporal_load(G + i); }
+    }
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int64_t i = vec_index<V>(u);
+        if (i < n4) {
+            vf4 r;
+            r.x = f_add(a[u].x, g[u].x);
+            r.y = f_add(a[u].y, g[u].y);
+            r.z = f_add(a[u].z, g[u].z);
+            r.w = f_add(a[u].w, g[u].w);
+            __builtin_nontemporal_store(r, A + i);
+        }
+    }
+}
+
+// A <- G (the first shard of a replica)
+template <int V>
+__global__ __launch_bounds__(kStreamThreads) void copy_v4_kernel(vf4* __restrict__ A, const vf4* __restrict__ G,
+                                                                 int64_t n4) {
+    vf4 g[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int64_t i = vec_index<V>(u);
+        if (i < n4) g[u] = __builtin_nontemporal_load(G + i);
+    }
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int64_t i = vec_index<V>(u);
+        if (i < n4) __builtin_nontemporal_store(g[u], A + i);
     }
 }
 
 __global__ __launch_bounds__(kStreamThreads) void accumulate_scalar_kernel(float* __restrict__ A,
                                                                            const float* __restrict__ G,
-                                                                           int64_t n) {
-    const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride)
-        A[i] = f_add(A[i], G[i]);
+                                                                           int64_t n, int first) {
+    const int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+    if (i < n) A[i] = first ? G[i] : f_add(A[i], G[i]);
 }
 
-hipError_t launch_accumulate(float* A, const float* G, int64_t n, hipStream_t st) {
+hipError_t launch_accumulate(float* A, const float* G, int64_t n, int first, hipStream_t st) {
     if (n <= 0) return hipSuccess;
+    int64_t done = 0;
     if (aligned16(A) && aligned16(G)) {
-        int64_t n4 = n / 4;
-        if (n4 > 0)
-            hipLaunchKernelGGL(accumulate_v4_kernel, dim3(stream_grid(n4)), dim3(kStreamThreads), 0,
-                               st, reinterpret_cast<vf4*>(A), reinterpret_cast<const vf4*>(G), n4);
-        if (n - n4 * 4 > 0)
-            hipLaunchKernelGGL(accumulate_scalar_kernel, dim3(1), dim3(kStreamThreads), 0, st,
-                               A + n4 * 4, G + n4 * 4, n - n4 * 4);
-    } else {
-        hipLaunchKernelGGL(accumulate_scalar_kernel, dim3(stream_grid(ceil_div(n, 4))),
-                           dim3(kStreamThreads), 0, st, A, G, n);
+        const int64_t n4 = n / 4;
+        const int V = stream_vec();
+        if (n4 > 0) {
+            vf4* a4 = reinterpret_cast<vf4*>(A);
+            const vf4* g4 = reinterpret_cast<const vf4*>(G);
+            const dim3 grid(stream_grid(n4, V)), blk(kStreamThreads);
+            if (first) {
+                if (V == 4) hipLaunchKernelGGL(copy_v4_kernel<4>, grid, blk, 0, st, a4, g4, n4);
+                else if (V == 2) hipLaunchKernelGGL(copy_v4_kernel<2>, grid, blk, 0, st, a4, g4, n4);
+                else hipLaunchKernelGGL(copy_v4_kernel<1>, grid, blk, 0, st, a4, g4, n4);
+            } else {
+                if (V == 4) hipLaunchKernelGGL(accumulate_v4_kernel<4>, grid, blk, 0, st, a4, g4, n4);
+                else if (V == 2) hipLaunchKernelGGL(accumulate_v4_kernel<2>, grid, blk, 0, st, a4, g4, n4);
+                else hipLaunchKernelGGL(accumulate_v4_kernel<1>, grid, blk, 0, st, a4, g4, n4);
+            }
+        }
+        done = n4 * 4;
     }
+    if (done < n)
+        hipLaunchKernelGGL(accumulate_scalar_kernel, dim3((unsigned)ceil_div(n - done, kStreamThreads)),
+                           dim3(kStreamThreads), 0, st, A + done, G + done, n - done, first);
     return hipGetLastError();
 }
 
@@ -93,37 +134,36 @@ __device__ __forceinline__ float fold_one(const FoldPtrs& p, int R, const float*
 template <int P>
 __global__ __launch_bounds__(kStreamThreads) void fold_kernel(FoldPtrs p, int R, const float* g_last,
                                                               float* __restrict__ out, int64_t n) {
-    const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
-    for (int64_t e = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; e < n; e += stride)
-        out[e] = fold_one<P>(p, R, g_last, e);
+    const int64_t e = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+    if (e < n) out[e] = fold_one<P>(p, R, g_last, e);
 }
 
-// Vector version for R = 6 (the replay's mesh): 16-byte loads.
+// Vector version for R = 6 (the replay's mesh): one 16-byte vector of each
+// input per thread.  T = ((A0+A4)+(A1+A5))+(A2+A3), A5 first completed with
+// the last partial when it is given.
 __global__ __launch_bounds__(kStreamThreads) void fold6_v4_kernel(FoldPtrs p, const float* g_last,
                                                                   vf4* __restrict__ out, int64_t n4) {
-    const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
+    const int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+    if (i >= n4) return;
     const vf4* a0 = reinterpret_cast<const vf4*>(p.a[0]);
     const vf4* a1 = reinterpret_cast<const vf4*>(p.a[1]);
     const vf4* a2 = reinterpret_cast<const vf4*>(p.a[2]);
     const vf4* a3 = reinterpret_cast<const vf4*>(p.a[3]);
     const vf4* a4 = reinterpret_cast<const vf4*>(p.a[4]);
     const vf4* a5 = reinterpret_cast<const vf4*>(p.a[5]);
-    const vf4* gl = reinterpret_cast<const vf4*>(g_last);
-    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n4; i += stride) {
-        vf4 v0 = __builtin_nontemporal_load(a0 + i), v1 = __builtin_nontemporal_load(a1 + i);
-        vf4 v2 = __builtin_nontemporal_load(a2 + i), v3 = __builtin_nontemporal_load(a3 + i);
-        vf4 v4 = __builtin_nontemporal_load(a4 + i), v5 = __builtin_nontemporal_load(a5 + i);
-        if (gl) {
-            vf4 g = __builtin_nontemporal_load(gl + i);
-            v5.x = f_add(v5.x, g.x); v5.y = f_add(v5.y, g.y);
-            v5.z = f_add(v5.z, g.z); v5.w = f_add(v5.w, g.w);
-        }
-        vf4 r;
-#define FOLD6(c) r.c = f_add(f_add(f_add(v0.c, v4.c), f_add(v1.c, v5.c)), f_add(v2.c, v3.c))
-        FOLD6(x); FOLD6(y); FOLD6(z); FOLD6(w);
-#undef FOLD6
-        __builtin_nontemporal_store(r, out + i);
+    vf4 v0 = __builtin_nontemporal_load(a0 + i), v1 = __builtin_nontemporal_load(a1 + i);
+    vf4 v2 = __builtin_nontemporal_load(a2 + i), v3 = __builtin_nontemporal_load(a3 + i);
+    vf4 v4 = __builtin_nontemporal_load(a4 + i), v5 = __builtin_nontemporal_load(a5 + i);
+    if (g_last) {
+        const vf4 g = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(g_last) + i);
+        v5.x = f_add(v5.x, g.x); v5.y = f_add(v5.y, g.y);
+        v5.z = f_add(v5.z, g.z); v5.w = f_add(v5.w, g.w);
     }
+    vf4 r;
+#define FOLD6(c) r.c = f_add(f_add(f_add(v0.c, v4.c), f_add(v1.c, v5.c)), f_add(v2.c, v3.c))
+    FOLD6(x); FOLD6(y); FOLD6(z); FOLD6(w);
+#undef FOLD6
+    __builtin_nontemporal_store(r, out + i);
 }
 
 hipError_t launch_fold(const FoldPtrs& p, int R, const float* g_last, float* out, int64_t n,
@@ -133,8 +173,8 @@ hipError_t launch_fold(const FoldPtrs& p, int R, const float* g_last, float* out
     for (int i = 0; i < R; ++i) al = al && aligned16(p.a[i]);
     int64_t done = 0;
     if (R == 6 && al && n >= 4) {
-        int64_t n4 = n / 4;
-        hipLaunchKernelGGL(fold6_v4_kernel, dim3(stream_grid(n4)), dim3(kStreamThreads), 0, st, p,
+        const int64_t n4 = n / 4;
+        hipLaunchKernelGGL(fold6_v4_kernel, dim3(stream_grid(n4, 1)), dim3(kStreamThreads), 0, st, p,
                            g_last, reinterpret_cast<vf4*>(out), n4);
         done = n4 * 4;
     }
@@ -142,8 +182,8 @@ hipError_t launch_fold(const FoldPtrs& p, int R, const float* g_last, float* out
         FoldPtrs q = p;
         for (int i = 0; i < R; ++i) q.a[i] = p.a[i] + done;
         const float* gl = g_last ? g_last + done : nullptr;
-        int64_t m = n - done;
-        dim3 grid(stream_grid(ceil_div(m, 4))), blk(kStreamThreads);
+        const int64_t m = n - done;
+        const dim3 grid((unsigned)ceil_div(m, kStreamThreads)), blk(kStreamThreads);
         int P = 1;
         while (P * 2 <= R) P *= 2;
         switch (P) {
@@ -160,39 +200,52 @@ hipError_t launch_fold(const FoldPtrs& p, int R, const float* g_last, float* out
 }
 
 // g <- g * kappa when the norm exceeded the bound (decided on the device).
+template <int V>
 __global__ __launch_bounds__(kStreamThreads) void clip_v4_kernel(vf4* __restrict__ g, int64_t n4,
                                                                  const Scalars* __restrict__ s) {
     if (!s->clip) return;
     const float k = s->kappa;
-    const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n4; i += stride) {
-        vf4 v = __builtin_nontemporal_load(g + i);
-        v.x = f_mul(v.x, k); v.y = f_mul(v.y, k); v.z = f_mul(v.z, k); v.w = f_mul(v.w, k);
-        __builtin_nontemporal_store(v, g + i);
+    vf4 v[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int64_t i = vec_index<V>(u);
+        if (i < n4) v[u] = __builtin_nontemporal_load(g + i);
+    }
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int64_t i = vec_index<V>(u);
+        if (i < n4) {
+            vf4 r;
+            r.x = f_mul(v[u].x, k); r.y = f_mul(v[u].y, k); r.z = f_mul(v[u].z, k); r.w = f_mul(v[u].w, k);
+            __builtin_nontemporal_store(r, g + i);
+        }
     }
 }
 
 __global__ __launch_bounds__(kStreamThreads) void clip_scalar_kernel(float* __restrict__ g, int64_t n,
                                                                      const Scalars* __restrict__ s) {
     if (!s->clip) return;
-    const float k = s->kappa;
-    const int64_t stride = (int64_t)gridDim.x * kStreamThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x; i < n; i += stride)
-        g[i] = f_mul(g[i], k);
+    const int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+    if (i < n) g[i] = f_mul(g[i], s->kappa);
 }
 
 hipError_t launch_clip(float* g, int64_t n, const Scalars* scal, hipStream_t st) {
     if (n <= 0) return hipSuccess;
     int64_t done = 0;
     if (aligned16(g)) {
-        int64_t n4 = n / 4;
-        if (n4 > 0)
-            hipLaunchKernelGGL(clip_v4_kernel, dim3(stream_grid(n4)), dim3(kStreamThreads), 0, st,
-                               reinterpret_cast<vf4*>(g), n4, scal);
+        const int64_t n4 = n / 4;
+        const int V = stream_vec();
+        if (n4 > 0) {
+            vf4* g4 = reinterpret_cast<vf4*>(g);
+            const dim3 grid(stream_grid(n4, V)), blk(kStreamThreads);
+            if (V == 4) hipLaunchKernelGGL(clip_v4_kernel<4>, grid, blk, 0, st, g4, n4, scal);
+            else if (V == 2) hipLaunchKernelGGL(clip_v4_kernel<2>, grid, blk, 0, st, g4, n4, scal);
+            else hipLaunchKernelGGL(clip_v4_kernel<1>, grid, blk, 0, st, g4, n4, scal);
+        }
         done = n4 * 4;
     }
     if (done < n)
-        hipLaunchKernelGGL(clip_scalar_kernel, dim3(stream_grid(ceil_div(n - done, 4))),
+        hipLaunchKernelGGL(clip_scalar_kernel, dim3((unsigned)ceil_div(n - done, kStreamThreads)),
                            dim3(kStreamThreads), 0, st, g + done, n - done, scal);
     return hipGetLastError();
 }

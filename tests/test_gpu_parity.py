@@ -314,3 +314,20 @@ def test_norm_reduce_wg_invariance():
             assert_bitwise(nu, np.array([wnu]), f"nu wg={wg}")
     finally:
         brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, old)
+
+
+def test_replay_stream_shape_invariance():
+    """The number of 16-byte vectors per thread in the streaming kernels
+    changes only the launch shape."""
+    R, S, L = 6, 3, 100_003
+    parts = [synth.replay_partial_host(9, v, L, std=1e-2) for v in range(R * S)]
+    T, wnu, _ = oracle.replay(parts, R, S)
+    old = brl.set_tuning(brl.TUNE_STREAM_VEC, 0)
+    try:
+        for vec in (1, 2, 4):
+            brl.set_tuning(brl.TUNE_STREAM_VEC, vec)
+            out, nu, _ = _replay_gpu(parts, R, S)
+            assert_bitwise(out, T, f"TreeFold vec={vec}")
+            assert_bitwise(nu, np.array([wnu]), f"nu vec={vec}")
+    finally:
+        brl.set_tuning(brl.TUNE_STREAM_VEC, old)
