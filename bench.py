@@ -27,10 +27,12 @@ sys.path.insert(0, ROOT)
 METRIC = "bit-exact int8 QAT linear TOPS fwd+bwd (M=16384); ordered-reduce GB/s"
 
 # MI355X published peaks (dense) and the derived fp32 VALU rate without FMA
-# or packed instructions: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz.
+# or packed instructions: 256 CU x 4 SIMD x 32 lanes per clock x 2.4 GHz
+# (a wave64 v_add_f32 / v_mul_f32 retires in two clocks; measured 62-65 T
+# ops/s sustained on MI355X).  The published 157.3 TFLOP/s counts packed FMA.
 PEAK_HBM_GBPS = 8000.0
 PEAK_I8_TOPS = 5030.0
-PEAK_VALU_F32_TOPS = 256 * 64 * 2.4e9 / 1e12          # 39.32 T ops/s
+PEAK_VALU_F32_TOPS = 256 * 128 * 2.4e9 / 1e12         # 78.64 T ops/s
 
 # Replay bytes per element index that the method must move with one partial
 # resident at a time: per replica, shard 0 copies (read G, write A: 8 B) and

@@ -40,13 +40,21 @@ def _run(cmd):
     return err
 
 
+# Per-unit extra flags.  The backward's binary-counter stack stores each
+# finished subtree to a level chosen by a uniform branch; sinking those
+# stores into one store through a pointer phi would keep the stack in
+# scratch memory instead of registers.
+EXTRA = {"bwd.hip": ["-mllvm", "-simplifycfg-sink-common=false"]}
+
+
 def _compile(src: str) -> str:
     name = os.path.splitext(src)[0]
     obj = os.path.join(BUILD, name + ".o")
     asm = os.path.join(BUILD, name + ".gfx950.s")
     path = os.path.join(CSRC, src)
-    _run([HIPCC, *FLAGS, "-c", path, "-o", obj])
-    _run([HIPCC, *FLAGS, "--offload-device-only", "-S", path, "-o", asm])
+    flags = FLAGS + EXTRA.get(src, [])
+    _run([HIPCC, *flags, "-c", path, "-o", obj])
+    _run([HIPCC, *flags, "--offload-device-only", "-S", path, "-o", asm])
     return obj
 
 

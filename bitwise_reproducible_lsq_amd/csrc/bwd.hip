@@ -27,43 +27,43 @@
 namespace brl {
 
 constexpr int kTile = 64;         // output tile edge per workgroup
-constexpr int kPitchA = 36;       // floats per LDS row of A ([i][32 r] + pad)
+constexpr int kPitchA = 36;       // floats per LDS row of A when i-major ([i][32 r] + pad)
+constexpr int kPitchAr = 68;      // floats per LDS row of A when r-major ([r][64 i] + pad)
+constexpr int kLdsA = kTile * kPitchA > kBlock * kPitchAr ? kTile * kPitchA : kBlock * kPitchAr;
 constexpr int kPitchB = 68;       // floats per LDS row of B ([r][64 j] + pad)
 constexpr int kFinishLevels = 10; // finish pass handles up to 2^10 chunk roots
 
 // Binary-counter stack: after block index bi (0-based) completes with value t,
 // merge it with the stored subtrees of equal size.  st[L] is valid while bit L
-// of the completed-block count is set.
-template <int NV, int L, int D>
-__device__ __forceinline__ void stack_push(float (&st)[D + 1][NV], float (&t)[NV], unsigned bi) {
+// of the completed-block count is set.  V is a float or a clang float vector
+// (elementwise binary32 adds).
+template <class V, int L, int D>
+__device__ __forceinline__ void stack_push(V (&st)[D + 1], V& t, unsigned bi) {
     if constexpr (L == D) {
-#pragma unroll
-        for (int k = 0; k < NV; ++k) st[D][k] = t[k];
+        st[D] = t;
     } else {
         if (bi & (1u << L)) {
-#pragma unroll
-            for (int k = 0; k < NV; ++k) t[k] = f_add(st[L][k], t[k]);
-            stack_push<NV, L + 1, D>(st, t, bi);
+            t = st[L] + t;
+            stack_push<V, L + 1, D>(st, t, bi);
         } else {
-#pragma unroll
-            for (int k = 0; k < NV; ++k) st[L][k] = t[k];
+            st[L] = t;
         }
     }
 }
 
 // Final right-to-left merge of the stored subtrees for `count` blocks.
-template <int NV, int D>
-__device__ __forceinline__ void stack_final(float (&st)[D + 1][NV], unsigned count, float (&root)[NV]) {
-    bool have = false;
-#pragma unroll
-    for (int L = 0; L <= D; ++L) {
+template <class V, int L, int D>
+__device__ __forceinline__ void stack_final(const V (&st)[D + 1], unsigned count, V& root, bool have) {
+    if constexpr (L <= D) {
         if (count & (1u << L)) {
-#pragma unroll
-            for (int k = 0; k < NV; ++k) root[k] = have ? f_add(st[L][k], root[k]) : st[L][k];
+            root = have ? st[L] + root : st[L];
             have = true;
         }
+        stack_final<V, L + 1, D>(st, count, root, have);
     }
 }
+
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float mask_select(float v, const float* src, int64_t idx,
                                              const float* s_dev, float s_host) {
@@ -73,7 +73,7 @@ __device__ __forceinline__ float mask_select(float v, const float* src, int64_t 
 
 template <bool A_RMAJ, int D>
 __global__ __launch_bounds__(256) void ste_chunk_kernel(SteArgs a, int64_t nblk, int final_out) {
-    __shared__ __attribute__((aligned(16))) float As[2][kTile * kPitchA];
+    __shared__ __attribute__((aligned(16))) float As[2][kLdsA];
     __shared__ __attribute__((aligned(16))) float Bs[2][kBlock * kPitchB];
 
     const int tid = threadIdx.x;
@@ -117,9 +117,11 @@ __global__ __launch_bounds__(256) void ste_chunk_kernel(SteArgs a, int64_t nblk,
             d[0] = make_float4(ra[0], ra[1], ra[2], ra[3]);
             d[1] = make_float4(ra[4], ra[5], ra[6], ra[7]);
         } else {
+            // r-major like the source: row rr, 8 consecutive i
             const int rr = tid >> 3, seg = (tid & 7) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) As[buf][(seg + e) * kPitchA + rr] = ra[e];
+            float4* d = reinterpret_cast<float4*>(&As[buf][rr * kPitchAr + seg]);
+            d[0] = make_float4(ra[0], ra[1], ra[2], ra[3]);
+            d[1] = make_float4(ra[4], ra[5], ra[6], ra[7]);
         }
         {
             const int rr = tid >> 3, seg = (tid & 7) * 8;
@@ -136,8 +138,8 @@ __global__ __launch_bounds__(256) void ste_chunk_kernel(SteArgs a, int64_t nblk,
         }
     };
 
-    float st[D + 1][16];
-    float acc[16];
+    v16f st[D + 1];
+    v16f acc;
 
     gload(b_begin);
     sstore(0);
@@ -150,16 +152,25 @@ __global__ __launch_bounds__(256) void ste_chunk_kernel(SteArgs a, int64_t nblk,
         const float* Bb = &Bs[cur][tj * 4];
 #pragma unroll
         for (int rs = 0; rs < kBlock; rs += 4) {
+            // av[q] holds A for this thread's row q at the 4 steps rs..rs+3
+            // (i-major A), or A for the 4 rows at step rs+q (r-major A)
             float4 av[4], bv[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) av[q] = *reinterpret_cast<const float4*>(Ab + (ti + 16 * q) * kPitchA + rs);
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (A_RMAJ)
+                    av[q] = *reinterpret_cast<const float4*>(Ab + (ti + 16 * q) * kPitchA + rs);
+                else
+                    av[q] = *reinterpret_cast<const float4*>(Ab + (rs + q) * kPitchAr + 4 * ti);
+            }
 #pragma unroll
             for (int s = 0; s < 4; ++s) bv[s] = *reinterpret_cast<const float4*>(Bb + (rs + s) * kPitchB);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float x = s == 0 ? av[q].x : s == 1 ? av[q].y : s == 2 ? av[q].z : av[q].w;
+                    const float4 asrc = A_RMAJ ? av[q] : av[s];
+                    const int e = A_RMAJ ? s : q;
+                    const float x = e == 0 ? asrc.x : e == 1 ? asrc.y : e == 2 ? asrc.z : asrc.w;
                     const float p0 = f_mul(x, bv[s].x), p1 = f_mul(x, bv[s].y);
                     const float p2 = f_mul(x, bv[s].z), p3 = f_mul(x, bv[s].w);
                     if (rs == 0 && s == 0) {
@@ -174,18 +185,18 @@ __global__ __launch_bounds__(256) void ste_chunk_kernel(SteArgs a, int64_t nblk,
                 }
             }
         }
-        stack_push<16, 0, D>(st, acc, (unsigned)(blk - b_begin));
+        stack_push<v16f, 0, D>(st, acc, (unsigned)(blk - b_begin));
         if (blk + 1 < b_end) sstore(cur ^ 1);
         __syncthreads();
     }
 
-    float root[16];
-    stack_final<16, D>(st, (unsigned)(b_end - b_begin), root);
+    v16f root;
+    stack_final<v16f, 0, D>(st, (unsigned)(b_end - b_begin), root, false);
 
     const int64_t plane = a.I * a.Jn;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int64_t i = i0 + ti + 16 * q;
+        const int64_t i = i0 + (A_RMAJ ? ti + 16 * q : 4 * ti + q);
         if (i >= a.I) continue;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -209,14 +220,14 @@ __global__ __launch_bounds__(256) void ste_finish_kernel(SteArgs a, int64_t Q) {
     const int64_t plane = a.I * a.Jn;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= plane) return;
-    float st[kFinishLevels + 1][1];
+    float st[kFinishLevels + 1];
     for (int64_t c = 0; c < Q; ++c) {
-        float t[1] = {a.roots[c * plane + idx]};
-        stack_push<1, 0, kFinishLevels>(st, t, (unsigned)c);
+        float t = a.roots[c * plane + idx];
+        stack_push<float, 0, kFinishLevels>(st, t, (unsigned)c);
     }
-    float root[1];
-    stack_final<1, kFinishLevels>(st, (unsigned)Q, root);
-    float v = mask_select(root[0], a.mask_src, idx, a.mask_scale_dev, a.mask_scale_host);
+    float root;
+    stack_final<float, 0, kFinishLevels>(st, (unsigned)Q, root, false);
+    float v = mask_select(root, a.mask_src, idx, a.mask_scale_dev, a.mask_scale_host);
     if (a.accumulate) v = f_add(a.out[idx], v);
     a.out[idx] = v;
 }
