@@ -237,9 +237,10 @@ brl_status qat_linear_bwd(const float* dOut, const float* X, const float* W, con
         if (s) return s;
         G = L.G;
     }
+    const bool g_vec = N % 4 == 0 && (reinterpret_cast<uintptr_t>(G) & 15) == 0;
     if (dX && M > 0) {
         SteArgs a{};
-        a.A = G; a.lda = N; a.a_rmaj = true; a.I = M; a.R = N; a.Jn = K;
+        a.A = G; a.lda = N; a.a_rmaj = true; a.a_vec = g_vec; a.I = M; a.R = N; a.Jn = K;
         a.Bq = L.qw; a.ldb = L.Kp; a.b_scale_dev = &L.scal->s_w;
         a.mask_src = X; a.mask_scale_dev = nullptr; a.mask_scale_host = s_x;
         a.out = dX; a.accumulate = 0; a.roots = L.roots;
@@ -248,7 +249,7 @@ brl_status qat_linear_bwd(const float* dOut, const float* X, const float* W, con
     }
     if (dW) {
         SteArgs a{};
-        a.A = G; a.lda = N; a.a_rmaj = false; a.I = N; a.R = M; a.Jn = K;
+        a.A = G; a.lda = N; a.a_rmaj = false; a.a_vec = g_vec; a.I = N; a.R = M; a.Jn = K;
         a.Bq = L.qx; a.ldb = L.Kp; a.b_scale_dev = nullptr; a.b_scale_host = s_x;
         a.mask_src = W; a.mask_scale_dev = &L.scal->s_w;
         a.out = dW; a.accumulate = dW_accumulate; a.roots = L.roots;

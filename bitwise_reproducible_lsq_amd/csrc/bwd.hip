@@ -64,6 +64,7 @@ __device__ __forceinline__ void stack_final(const V (&st)[D + 1], unsigned count
 }
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float vf1 __attribute__((ext_vector_type(1)));
 
 __device__ __forceinline__ float mask_select(float v, const float* src, int64_t idx,
                                              const float* s_dev, float s_host) {
@@ -88,9 +89,28 @@ __global__ __launch_bounds__(256) void ste_chunk_kernel(SteArgs a, int64_t nblk,
     // global -> register staging for one 32-block
     float ra[8];
     uint2 rb;
+    // A whole 32-block inside the operand (every row of the tile, every
+    // reduction step) loads without per-element predicates; 16-byte vectors
+    // when the host saw the rows 16-byte aligned.
+    const bool rows_full = i0 + kTile <= a.I;
     auto gload = [&](int64_t blk) {
         const int64_t r0 = blk * kBlock;
-        if constexpr (A_RMAJ) {
+        if (rows_full && r0 + kBlock <= a.R) {
+            const float* p;
+            if constexpr (A_RMAJ)
+                p = a.A + (i0 + (tid >> 2)) * a.lda + r0 + (tid & 3) * 8;
+            else
+                p = a.A + (r0 + (tid >> 3)) * a.lda + i0 + (tid & 7) * 8;
+            if (a.a_vec) {
+                const float4 u = reinterpret_cast<const float4*>(p)[0];
+                const float4 v = reinterpret_cast<const float4*>(p)[1];
+                ra[0] = u.x; ra[1] = u.y; ra[2] = u.z; ra[3] = u.w;
+                ra[4] = v.x; ra[5] = v.y; ra[6] = v.z; ra[7] = v.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ra[e] = p[e];
+            }
+        } else if constexpr (A_RMAJ) {
             // A(r, i) = A[i*lda + r]: row ii, 8 consecutive r
             const int ii = tid >> 2, seg = (tid & 3) * 8;
             const int64_t i = i0 + ii, r = r0 + seg;
@@ -215,21 +235,33 @@ __global__ __launch_bounds__(256) void ste_chunk_kernel(SteArgs a, int64_t nblk,
     }
 }
 
-// Pairwise tree over the Q chunk roots of each output, then mask (+ running sum).
+// Pairwise tree over the Q chunk roots of each output, then mask (+ running
+// sum).  V consecutive outputs per thread (V = 4 needs the plane size to be a
+// multiple of 4 so that every root vector is 16-byte aligned); the roots of
+// up to 8 chunks are loaded before they enter the stack.
+template <class T, int V>
 __global__ __launch_bounds__(256) void ste_finish_kernel(SteArgs a, int64_t Q) {
     const int64_t plane = a.I * a.Jn;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
     if (idx >= plane) return;
-    float st[kFinishLevels + 1];
-    for (int64_t c = 0; c < Q; ++c) {
-        float t = a.roots[c * plane + idx];
-        stack_push<float, 0, kFinishLevels>(st, t, (unsigned)c);
+    T st[kFinishLevels + 1];
+    for (int64_t c0 = 0; c0 < Q; c0 += 8) {
+        T t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (c0 + u < Q) t[u] = *reinterpret_cast<const T*>(a.roots + (c0 + u) * plane + idx);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (c0 + u < Q) stack_push<T, 0, kFinishLevels>(st, t[u], (unsigned)(c0 + u));
     }
-    float root;
-    stack_final<float, 0, kFinishLevels>(st, (unsigned)Q, root, false);
-    float v = mask_select(root, a.mask_src, idx, a.mask_scale_dev, a.mask_scale_host);
-    if (a.accumulate) v = f_add(a.out[idx], v);
-    a.out[idx] = v;
+    T root;
+    stack_final<T, 0, kFinishLevels>(st, (unsigned)Q, root, false);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        float v = mask_select(root[e], a.mask_src, idx + e, a.mask_scale_dev, a.mask_scale_host);
+        if (a.accumulate) v = f_add(a.out[idx + e], v);
+        a.out[idx + e] = v;
+    }
 }
 
 int64_t ste_chunks(int64_t R) {
@@ -277,7 +309,12 @@ hipError_t launch_ste(const SteArgs& a, hipStream_t st) {
     else ste_launch_chunk<false>(a, D, grid, nblk, final_out, st);
     if (!final_out) {
         const int64_t plane = a.I * a.Jn;
-        hipLaunchKernelGGL(ste_finish_kernel, dim3((unsigned)ceil_div(plane, 256)), dim3(256), 0, st, a, Q);
+        if (plane % 4 == 0)
+            hipLaunchKernelGGL((ste_finish_kernel<vf4, 4>), dim3((unsigned)ceil_div(plane / 4, 256)), dim3(256), 0,
+                               st, a, Q);
+        else
+            hipLaunchKernelGGL((ste_finish_kernel<vf1, 1>), dim3((unsigned)ceil_div(plane, 256)), dim3(256), 0, st,
+                               a, Q);
     }
     return hipGetLastError();
 }

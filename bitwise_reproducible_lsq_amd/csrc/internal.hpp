@@ -81,6 +81,7 @@ struct SteArgs {
     const float* A;        // dY / G
     int64_t lda;
     bool a_rmaj;           // A(r,i) = A[i*lda + r] (dX) else A[r*lda + i] (dW)
+    bool a_vec;            // A and lda allow 16-byte row loads
     int64_t I, R, Jn;
     const int8_t* Bq;      // [>= round_up(R,32), ldb] int8, zero padded
     int64_t ldb;
