@@ -10,9 +10,10 @@
 //
 // Kernel ste_chunk_kernel<A_RMAJ, D>: a workgroup of 256 threads owns a 64x64
 // output tile and one chunk of 2^D consecutive 32-blocks of the reduction.
-// Each thread holds 4x4 outputs.  Per 32-block it streams the block's 32
-// reduction steps from LDS (A as [i][r] with pitch 36, B as [r][j] with pitch
-// 68, both double-buffered), forming the 16 block sums left to right from the
+// Each thread holds 4x4 outputs (4 consecutive rows, 4 consecutive columns).
+// Per 32-block it streams the block's 32 reduction steps from LDS (A as
+// [r][i] and B as [r][j], pitch 68, both double-buffered; dX's A arrives
+// i-major and is transposed on the LDS store), forming the 16 block sums left to right from the
 // first product; finished block sums enter a binary-counter stack of depth D
 // held in registers, which builds exactly the pairwise tree of the chunk.  An
 // aligned run of 2^D blocks is a complete subtree of the canonical tree (a
@@ -27,9 +28,8 @@
 namespace brl {
 
 constexpr int kTile = 64;         // output tile edge per workgroup
-constexpr int kPitchA = 36;       // floats per LDS row of A when i-major ([i][32 r] + pad)
-constexpr int kPitchAr = 68;      // floats per LDS row of A when r-major ([r][64 i] + pad)
-constexpr int kLdsA = kTile * kPitchA > kBlock * kPitchAr ? kTile * kPitchA : kBlock * kPitchAr;
+constexpr int kPitchAr = 68;      // floats per LDS row of A ([r][64 i] + pad)
+constexpr int kLdsA = kBlock * kPitchAr;
 constexpr int kPitchB = 68;       // floats per LDS row of B ([r][64 j] + pad)
 constexpr int kFinishLevels = 10; // finish pass handles up to 2^10 chunk roots
 
@@ -132,10 +132,10 @@ __global__ __launch_bounds__(256) void ste_chunk_kernel(SteArgs a, int64_t nblk,
     };
     auto sstore = [&](int buf) {
         if constexpr (A_RMAJ) {
+            // transpose into the r-major tile: 8 consecutive r of row ii
             const int ii = tid >> 2, seg = (tid & 3) * 8;
-            float4* d = reinterpret_cast<float4*>(&As[buf][ii * kPitchA + seg]);
-            d[0] = make_float4(ra[0], ra[1], ra[2], ra[3]);
-            d[1] = make_float4(ra[4], ra[5], ra[6], ra[7]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) As[buf][(seg + e) * kPitchAr + ii] = ra[e];
         } else {
             // r-major like the source: row rr, 8 consecutive i
             const int rr = tid >> 3, seg = (tid & 7) * 8;
@@ -172,25 +172,18 @@ __global__ __launch_bounds__(256) void ste_chunk_kernel(SteArgs a, int64_t nblk,
         const float* Bb = &Bs[cur][tj * 4];
 #pragma unroll
         for (int rs = 0; rs < kBlock; rs += 4) {
-            // av[q] holds A for this thread's row q at the 4 steps rs..rs+3
-            // (i-major A), or A for the 4 rows at step rs+q (r-major A)
+            // av[s]: A of this thread's 4 rows at step rs+s; bv[s]: its 4 columns of B
             float4 av[4], bv[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if constexpr (A_RMAJ)
-                    av[q] = *reinterpret_cast<const float4*>(Ab + (ti + 16 * q) * kPitchA + rs);
-                else
-                    av[q] = *reinterpret_cast<const float4*>(Ab + (rs + q) * kPitchAr + 4 * ti);
-            }
+            for (int s = 0; s < 4; ++s) av[s] = *reinterpret_cast<const float4*>(Ab + (rs + s) * kPitchAr + 4 * ti);
 #pragma unroll
             for (int s = 0; s < 4; ++s) bv[s] = *reinterpret_cast<const float4*>(Bb + (rs + s) * kPitchB);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float4 asrc = A_RMAJ ? av[q] : av[s];
-                    const int e = A_RMAJ ? s : q;
-                    const float x = e == 0 ? asrc.x : e == 1 ? asrc.y : e == 2 ? asrc.z : asrc.w;
+                    const float4 asrc = av[s];
+                    const float x = q == 0 ? asrc.x : q == 1 ? asrc.y : q == 2 ? asrc.z : asrc.w;
                     const float p0 = f_mul(x, bv[s].x), p1 = f_mul(x, bv[s].y);
                     const float p2 = f_mul(x, bv[s].z), p3 = f_mul(x, bv[s].w);
                     if (rs == 0 && s == 0) {
@@ -216,7 +209,7 @@ __global__ __launch_bounds__(256) void ste_chunk_kernel(SteArgs a, int64_t nblk,
     const int64_t plane = a.I * a.Jn;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int64_t i = i0 + (A_RMAJ ? ti + 16 * q : 4 * ti + q);
+        const int64_t i = i0 + 4 * ti + q;
         if (i >= a.I) continue;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {

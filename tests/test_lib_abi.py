@@ -133,7 +133,10 @@ def test_no_fused_or_packed_fp32_outside_division():
 def test_hot_loops_use_plain_mul_and_add():
     """The backward contraction kernels are made of v_mul_f32 + v_add_f32."""
     text = open([f for f in brl_build.asm_files() if "bwd" in f][0]).read()
-    body = text.split("_ZN3brl16ste_chunk_kernelILb1ELi5EEEvNS_7SteArgsEli:")[1].split("s_endpgm")[0]
-    n_mul = len(re.findall(r"\tv_mul_f32", body))
-    n_add = len(re.findall(r"\tv_add_f32", body))
-    assert n_mul >= 512 and n_add >= 480, (n_mul, n_add)
+    names = sorted(set(re.findall(r"^(_ZN3brl16ste_chunk_kernel\w+):", text, re.M)))
+    assert len(names) >= 12, names
+    for name in names:
+        body = text.split(name + ":")[1].split("s_endpgm")[0]
+        n_mul = len(re.findall(r"\tv_mul_f32", body))
+        n_add = len(re.findall(r"\tv_add_f32", body))
+        assert n_mul >= 512 and n_add >= 480, (name, n_mul, n_add)
