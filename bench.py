@@ -42,6 +42,23 @@ PEAK_VALU_F32_TOPS = 256 * 128 * 2.4e9 / 1e12         # 78.64 T ops/s
 REPLAY_BYTES_PER_ELEM = 6 * (8 + 7 * 12) + 28 + 8      # 588
 
 
+def measured_traffic(kernel: str):
+    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE passes, calibrated with a copy kernel of
+    known size), or None when the kernel sources changed since they were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    for src, digest in rec.get("sources_sha256", {}).items():
+        f = os.path.join(ROOT, src)
+        if not os.path.exists(f) or hashlib.sha256(open(f, "rb").read()).hexdigest() != digest:
+            return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else int(round(k["bytes"]))
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -224,7 +241,8 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(acc_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("brl::accumulate_v4_kernel<1>") if L == rcase.length else None,
+            "traffic_unit": "bytes per launch",
         },
         "rooflines_other": {
             "replay_total": {"bound": "hbm", "achieved": round(replay_gbps, 1), "peak": PEAK_HBM_GBPS,

@@ -44,7 +44,7 @@ def _run(cmd):
 # finished subtree to a level chosen by a uniform branch; sinking those
 # stores into one store through a pointer phi would keep the stack in
 # scratch memory instead of registers.
-EXTRA = {"bwd.hip": ["-mllvm", "-simplifycfg-sink-common=false"]}
+EXTRA = {"bwd.hip": ["-mllvm", "-simplifycfg-sink-common=false", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -13,8 +13,8 @@
 namespace brl {
 
 // ---- tuning knobs (launch shapes only) -----------------------------------------
-static std::atomic<int64_t> g_tune[3] = {{0}, {0}, {0}};
-static const int64_t kTuneDefault[3] = {4, 256, 1};
+static std::atomic<int64_t> g_tune[4] = {{0}, {0}, {0}, {0}};
+static const int64_t kTuneDefault[4] = {4, 256, 1, 2};
 
 int bwd_chunk_log2() {
     int64_t v = g_tune[BRL_TUNE_BWD_CHUNK_LOG2].load();
@@ -27,6 +27,10 @@ int reduce_wg_blocks() {
 int stream_vec() {
     int64_t v = g_tune[BRL_TUNE_STREAM_VEC].load();
     return (int)(v > 0 ? v : kTuneDefault[BRL_TUNE_STREAM_VEC]);
+}
+int bwd_engine() {
+    int64_t v = g_tune[BRL_TUNE_BWD_ENGINE].load();
+    return (int)(v > 0 ? v : kTuneDefault[BRL_TUNE_BWD_ENGINE]);
 }
 
 // ---- the SwiGLU exp constants, derived from ln 2 ---------------------------------
@@ -104,8 +108,8 @@ struct BwdLayout {
     int64_t Kp, Mp, Np;
     Scalars* scal;
     float* partials;
-    int8_t* qx;
-    int8_t* qw;
+    void* bx;      // X operand: int8 q_x (VALU engine) or fp32 fl(q_x*s_x) (matrix-core engine), [Mp, Kp]
+    void* bw;      // W operand likewise, [Np, Kp]
     float* G;
     float* roots;
     size_t bytes;
@@ -119,8 +123,8 @@ static BwdLayout bwd_layout(void* ws, int64_t M, int64_t K, int64_t N, int epilo
     Carver c(ws);
     L.scal = c.take<Scalars>(1);
     L.partials = c.take<float>((size_t)canon_partials(N * K));
-    L.qx = c.take<int8_t>((size_t)(L.Mp * L.Kp));
-    L.qw = c.take<int8_t>((size_t)(L.Np * L.Kp));
+    L.bx = c.take<float>((size_t)(L.Mp * L.Kp));
+    L.bw = c.take<float>((size_t)(L.Np * L.Kp));
     L.G = epilogue == BRL_EPILOGUE_SWIGLU ? c.take<float>((size_t)(M * N)) : nullptr;
     int64_t r1 = ste_root_floats(M, N, K);   // dX: I = M, R = N
     int64_t r2 = ste_root_floats(N, M, K);   // dW: I = N, R = M
@@ -227,33 +231,49 @@ brl_status qat_linear_bwd(const float* dOut, const float* X, const float* W, con
     fin.scal = L.scal;
     brl_status s = check_hip(launch_canon(kMapAbs, W, N * K, L.partials, fin, st), "weight step");
     if (s) return s;
-    s = check_hip(launch_quantize(W, N, K, &L.scal->s_w, 0.0f, L.qw, L.Np, L.Kp, 0, st), "quantize W");
-    if (s) return s;
-    s = check_hip(launch_quantize(X, M, K, nullptr, s_x, L.qx, L.Mp, L.Kp, 0, st), "quantize X");
-    if (s) return s;
     const float* G = dOut;
+    if (epilogue == BRL_EPILOGUE_SWIGLU && M > 0) G = L.G;
+    // The matrix-core engine loads 16-byte pieces of G rows directly into
+    // LDS: it needs N % 4 == 0 and a 16-byte aligned G; otherwise the VALU
+    // engine runs (same bits).
+    const bool g_vec = N % 4 == 0 && (reinterpret_cast<uintptr_t>(G) & 15) == 0;
+    const int engine = (bwd_engine() == 2 && g_vec) ? 2 : 1;
+    if (engine == 2) {
+        s = check_hip(launch_dequant(W, N, K, &L.scal->s_w, 0.0f, static_cast<float*>(L.bw), L.Np, L.Kp, st),
+                      "dequantise W");
+        if (s) return s;
+        s = check_hip(launch_dequant(X, M, K, nullptr, s_x, static_cast<float*>(L.bx), L.Mp, L.Kp, st),
+                      "dequantise X");
+    } else {
+        s = check_hip(launch_quantize(W, N, K, &L.scal->s_w, 0.0f, static_cast<int8_t*>(L.bw), L.Np, L.Kp, 0, st),
+                      "quantize W");
+        if (s) return s;
+        s = check_hip(launch_quantize(X, M, K, nullptr, s_x, static_cast<int8_t*>(L.bx), L.Mp, L.Kp, 0, st),
+                      "quantize X");
+    }
+    if (s) return s;
     if (epilogue == BRL_EPILOGUE_SWIGLU && M > 0) {
         s = check_hip(launch_swiglu_bwd(dOut, Ypre, M, N, L.G, exp_constants(), st), "SwiGLU backward");
         if (s) return s;
-        G = L.G;
     }
-    const bool g_vec = N % 4 == 0 && (reinterpret_cast<uintptr_t>(G) & 15) == 0;
     if (dX && M > 0) {
         SteArgs a{};
         a.A = G; a.lda = N; a.a_rmaj = true; a.a_vec = g_vec; a.I = M; a.R = N; a.Jn = K;
-        a.Bq = L.qw; a.ldb = L.Kp; a.b_scale_dev = &L.scal->s_w;
+        a.Bq = static_cast<const int8_t*>(L.bw); a.Bf = static_cast<const float*>(L.bw);
+        a.ldb = L.Kp; a.b_scale_dev = &L.scal->s_w;
         a.mask_src = X; a.mask_scale_dev = nullptr; a.mask_scale_host = s_x;
         a.out = dX; a.accumulate = 0; a.roots = L.roots;
-        s = check_hip(launch_ste(a, st), "dX");
+        s = check_hip(launch_ste(a, engine, st), "dX");
         if (s) return s;
     }
     if (dW) {
         SteArgs a{};
         a.A = G; a.lda = N; a.a_rmaj = false; a.a_vec = g_vec; a.I = N; a.R = M; a.Jn = K;
-        a.Bq = L.qx; a.ldb = L.Kp; a.b_scale_dev = nullptr; a.b_scale_host = s_x;
+        a.Bq = static_cast<const int8_t*>(L.bx); a.Bf = static_cast<const float*>(L.bx);
+        a.ldb = L.Kp; a.b_scale_dev = nullptr; a.b_scale_host = s_x;
         a.mask_src = W; a.mask_scale_dev = &L.scal->s_w;
         a.out = dW; a.accumulate = dW_accumulate; a.roots = L.roots;
-        s = check_hip(launch_ste(a, st), "dW");
+        s = check_hip(launch_ste(a, engine, st), "dW");
         if (s) return s;
     }
     return BRL_OK;
@@ -344,11 +364,12 @@ brl_status brl_probe_f32(int32_t op, const float* a, const float* b, float* out,
 }
 
 int64_t brl_set_tuning(int32_t knob, int64_t value) {
-    if (knob < 0 || knob > 2) return -1;
+    if (knob < 0 || knob > 3) return -1;
     if (knob == BRL_TUNE_BWD_CHUNK_LOG2 && value > 6) value = 6;
     if (knob == BRL_TUNE_REDUCE_WG_BLOCKS && value > 0 && value != 64 && value != 128 && value != 256)
         value = 256;
     if (knob == BRL_TUNE_STREAM_VEC && value > 0 && value != 1 && value != 2 && value != 4) value = 1;
+    if (knob == BRL_TUNE_BWD_ENGINE && value > 2) value = 2;
     int64_t old = g_tune[knob].exchange(value > 0 ? value : 0);
     return old > 0 ? old : kTuneDefault[knob];
 }

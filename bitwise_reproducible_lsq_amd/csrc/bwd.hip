@@ -5,17 +5,32 @@
 // with What = fl(q_w*s_w), Xhat = fl(q_x*s_x) and CanonSum the method's fixed
 // order (Open-1B summary on onedev.kr, "How": one reduction order, multiply
 // and add never fused, FTZ).  Every product is rounded on its own and every
-// add is one binary32 add in a fixed sequence, so the matrix cores cannot be
-// used; this is a register-blocked VALU contraction.
+// add is one binary32 add in a fixed sequence.
 //
-// Kernel ste_chunk_kernel<A_RMAJ, D>: a workgroup of 256 threads owns a 64x64
-// output tile and one chunk of 2^D consecutive 32-blocks of the reduction.
-// Each thread holds 4x4 outputs (4 consecutive rows, 4 consecutive columns).
-// Per 32-block it streams the block's 32 reduction steps from LDS (A as
-// [r][i] and B as [r][j], pitch 68, both double-buffered; dX's A arrives
-// i-major and is transposed on the LDS store), forming the 16 block sums left to right from the
-// first product; finished block sums enter a binary-counter stack of depth D
-// held in registers, which builds exactly the pairwise tree of the chunk.  An
+// Two engines give the same bits:
+//
+// ste_mfma_kernel<A_RMAJ, D> (matrix cores for the products): a 16x16x1 fp32
+// MFMA with a K of one and an accumulator input of -0 returns fl(a*b) for
+// each of its 1024 (a, b) pairs -- one product, one rounding, and -0 is the
+// exact additive identity -- which on gfx950 (FTZ mode) is bit-identical to
+// v_mul_f32, so the matrix cores form the products and the VALU only adds
+// them, in order, into the running block sums.  Workgroup tile 64x64, wave w
+// owns columns 16w..16w+15 of all 64 rows (4 MFMA blocks of 16x16 stacked
+// in rows sharing the B values); lane l feeds A row l and B column l % 16 and
+// receives 16 outputs.  Operand blocks move global -> LDS with direct loads
+// (no staging registers) through a 3-stage ring; B comes pre-dequantised.
+//
+// ste_chunk_kernel<A_RMAJ, D> (VALU products; any shape and alignment): a
+// workgroup of 256 threads owns a 64x64 output tile, each thread 4x4 outputs
+// (4 consecutive rows, 4 consecutive columns).  Per 32-block it streams the
+// block's 32 reduction steps from LDS (A as [r][i] and B as [r][j], pitch 68,
+// both double-buffered; dX's A arrives i-major and is transposed on the LDS
+// store, B is dequantised on the store), forming the block sums left to right
+// from the first product.
+//
+// Both: a workgroup owns one chunk of 2^D consecutive 32-blocks of the
+// reduction; finished block sums enter a binary-counter stack of depth D held
+// in registers, which builds exactly the pairwise tree of the chunk.  An
 // aligned run of 2^D blocks is a complete subtree of the canonical tree (a
 // short last run is the canonical tree of its own blocks), so the chunk roots
 // combined by the same pairwise tree (ste_finish_kernel) give the canonical
@@ -228,6 +243,154 @@ __global__ __launch_bounds__(256) void ste_chunk_kernel(SteArgs a, int64_t nblk,
     }
 }
 
+// ---- matrix-core products ---------------------------------------------------------
+constexpr int kMStages = 3;                       // LDS ring depth (blocks in flight: 2)
+constexpr int kMTileA = kTile * kBlock;           // floats of A per block (64 x 32)
+constexpr int kMTileB = kBlock * kTile;           // floats of B per block (32 x 64)
+constexpr int kMStage = kMTileA + kMTileB;        // 16 KB
+
+// i-major A tile: row i holds 8 chunks of 4 reduction steps, chunk c stored
+// at slot c ^ ((i >> 1) & 7), so the 16-byte reads of 16 consecutive rows hit
+// 16 distinct bank groups.
+__device__ __forceinline__ int mswz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+template <bool A_RMAJ, int D>
+__global__ __launch_bounds__(256) void ste_mfma_kernel(SteArgs a, int64_t nblk, int final_out) {
+    __shared__ __attribute__((aligned(16))) float smem[kMStages * kMStage];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t j0 = (int64_t)blockIdx.x * kTile;
+    const int64_t i0 = (int64_t)blockIdx.y * kTile;
+    const int64_t chunk = blockIdx.z;
+    const int64_t b_begin = chunk << D;
+    const int64_t b_end = (b_begin + (1 << D)) < nblk ? (b_begin + (1 << D)) : nblk;
+
+    // Direct loads of one 32-block into a stage: per operand 8 KB = 8 groups
+    // of 1 KB, wave w moving groups w and w + 4 (64 lanes x 16 bytes each).
+    // Sources outside the operand are redirected to element 0 of a valid
+    // row: rows past I only feed outputs that are never stored, and reduction
+    // steps past R are overwritten with -0 before use.
+    auto issue = [&](int64_t blk, int stage) {
+        float* sA = smem + stage * kMStage;
+        float* sB = sA + kMTileA;
+        const int64_t r0 = blk * kBlock;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int g = k * 4 + wave;
+            const float* src;
+            if constexpr (A_RMAJ) {
+                // G[i][r]: group g = rows 8g..8g+7, lane -> (row, slot)
+                const int row = g * 8 + (lane >> 3), c = mswz(row, lane & 7);
+                int64_t i = i0 + row, r = r0 + 4 * c;
+                if (i >= a.I) i = a.I - 1;
+                if (r >= a.R) r = 0;
+                src = a.A + i * a.lda + r;
+            } else {
+                // G[r][i]: group g = reduction rows 4g..4g+3, 16 chunks each
+                const int row = g * 4 + (lane >> 4);
+                int64_t r = r0 + row, i = i0 + 4 * (lane & 15);
+                if (r >= a.R) r = 0;
+                if (i >= a.I) i = 0;
+                src = a.A + r * a.lda + i;
+            }
+            __builtin_amdgcn_global_load_lds(src, sA + g * 256, 16, 0, 0);
+            const int brow = g * 4 + (lane >> 4);
+            const float* bsrc = a.Bf + (r0 + brow) * a.ldb + j0 + 4 * (lane & 15);
+            __builtin_amdgcn_global_load_lds(bsrc, sB + g * 256, 16, 0, 0);
+        }
+    };
+    constexpr int kLoads = 4;   // direct loads per wave per block
+
+    v16f cneg;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cneg[r] = -0.0f;
+    v16f st[D + 1];
+    v16f acc;
+
+    const int bcol = 16 * wave + (lane & 15);
+    issue(b_begin, 0);
+    if (b_begin + 1 < b_end) issue(b_begin + 1, 1);
+
+    for (int64_t blk = b_begin; blk < b_end; ++blk) {
+        const int t = (int)(blk - b_begin);
+        const int stage = t % kMStages;
+        // block blk landed for this wave (the next one may stay in flight),
+        // then for every wave; the stage written next was read in the
+        // previous iteration, which every wave has finished
+        if (blk + 1 < b_end) wait_vmcnt<kLoads>();
+        else wait_vmcnt<0>();
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        if (blk + 2 < b_end) issue(blk + 2, (t + 2) % kMStages);
+
+        float* sA = smem + stage * kMStage;
+        const float* sB = sA + kMTileA;
+        const int64_t r0 = blk * kBlock;
+        if (r0 + kBlock > a.R) {
+            // the ragged last block: steps past R read A = -0
+            const int nvalid = (int)(a.R - r0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int idx = tid * 8 + e;
+                if constexpr (A_RMAJ) {
+                    const int row = idx >> 5, rr = idx & 31;
+                    if (rr >= nvalid) sA[row * kBlock + 4 * mswz(row, rr >> 2) + (rr & 3)] = -0.0f;
+                } else {
+                    const int rr = idx >> 6;
+                    if (rr >= nvalid) sA[idx] = -0.0f;
+                }
+            }
+            __syncthreads();
+        }
+
+#pragma unroll
+        for (int rs = 0; rs < kBlock; rs += 4) {
+            float av[4], bv[4];
+            if constexpr (A_RMAJ) {
+                const vf4 v = *reinterpret_cast<const vf4*>(sA + lane * kBlock + 4 * mswz(lane, rs >> 2));
+                av[0] = v.x; av[1] = v.y; av[2] = v.z; av[3] = v.w;
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) av[s] = sA[(rs + s) * kTile + lane];
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) bv[s] = sB[(rs + s) * kTile + bcol];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const v16f p = __builtin_amdgcn_mfma_f32_16x16x1f32(av[s], bv[s], cneg, 0, 0, 0);
+                if (rs == 0 && s == 0) acc = p;
+                else acc = acc + p;
+            }
+        }
+        stack_push<v16f, 0, D>(st, acc, (unsigned)t);
+    }
+
+    v16f root;
+    stack_final<v16f, 0, D>(st, (unsigned)(b_end - b_begin), root, false);
+
+    // lane l, register 4*beta + e holds row 16*beta + 4*(l / 16) + e, column l % 16
+    const int64_t plane = a.I * a.Jn;
+    const int64_t j = j0 + bcol;
+    if (j < a.Jn) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t i = i0 + 16 * (r >> 2) + 4 * (lane >> 4) + (r & 3);
+            if (i >= a.I) continue;
+            const int64_t idx = i * a.Jn + j;
+            float v = root[r];
+            if (final_out) {
+                v = mask_select(v, a.mask_src, idx, a.mask_scale_dev, a.mask_scale_host);
+                if (a.accumulate) v = f_add(a.out[idx], v);
+                a.out[idx] = v;
+            } else {
+                a.roots[chunk * plane + idx] = v;
+            }
+        }
+    }
+}
+
 // Pairwise tree over the Q chunk roots of each output, then mask (+ running
 // sum).  V consecutive outputs per thread (V = 4 needs the plane size to be a
 // multiple of 4 so that every root vector is 16-byte aligned); the roots of
@@ -285,7 +448,19 @@ static void ste_launch_chunk(const SteArgs& a, int D, dim3 grid, int64_t nblk, i
     }
 }
 
-hipError_t launch_ste(const SteArgs& a, hipStream_t st) {
+template <bool A_RMAJ>
+static void ste_launch_mfma(const SteArgs& a, int D, dim3 grid, int64_t nblk, int final_out, hipStream_t st) {
+    switch (D) {
+        case 1: hipLaunchKernelGGL((ste_mfma_kernel<A_RMAJ, 1>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+        case 2: hipLaunchKernelGGL((ste_mfma_kernel<A_RMAJ, 2>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+        case 3: hipLaunchKernelGGL((ste_mfma_kernel<A_RMAJ, 3>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+        case 4: hipLaunchKernelGGL((ste_mfma_kernel<A_RMAJ, 4>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+        case 6: hipLaunchKernelGGL((ste_mfma_kernel<A_RMAJ, 6>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+        default: hipLaunchKernelGGL((ste_mfma_kernel<A_RMAJ, 5>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+    }
+}
+
+hipError_t launch_ste(const SteArgs& a, int engine, hipStream_t st) {
     if (a.I <= 0 || a.Jn <= 0) return hipSuccess;
     const int D = bwd_chunk_log2();
     const int64_t nblk = ceil_div(a.R, kBlock);
@@ -298,8 +473,13 @@ hipError_t launch_ste(const SteArgs& a, hipStream_t st) {
     const int64_t Q = ceil_div(nblk, (int64_t)1 << D);
     dim3 grid((unsigned)ceil_div(a.Jn, kTile), (unsigned)ceil_div(a.I, kTile), (unsigned)Q);
     const int final_out = Q == 1;
-    if (a.a_rmaj) ste_launch_chunk<true>(a, D, grid, nblk, final_out, st);
-    else ste_launch_chunk<false>(a, D, grid, nblk, final_out, st);
+    if (engine == 2) {
+        if (a.a_rmaj) ste_launch_mfma<true>(a, D, grid, nblk, final_out, st);
+        else ste_launch_mfma<false>(a, D, grid, nblk, final_out, st);
+    } else {
+        if (a.a_rmaj) ste_launch_chunk<true>(a, D, grid, nblk, final_out, st);
+        else ste_launch_chunk<false>(a, D, grid, nblk, final_out, st);
+    }
     if (!final_out) {
         const int64_t plane = a.I * a.Jn;
         if (plane % 4 == 0)

@@ -21,6 +21,15 @@ typedef float vf4 __attribute__((ext_vector_type(4)));   // 16-byte vector
 constexpr int kBlock = 32;      // CanonSum block width
 constexpr int kQmax = 127;      // int8 quantiser range [-127, 127]
 
+// s_waitcnt with vmcnt <= N, expcnt and lgkmcnt left unconstrained (gfx9
+// encoding): waits for this wave's older global loads, including the direct
+// global -> LDS ones.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 __device__ __forceinline__ float flush_f32(float x) {
     return (__builtin_fabsf(x) < 1.17549435e-38f) ? __builtin_copysignf(0.0f, x) : x;
 }

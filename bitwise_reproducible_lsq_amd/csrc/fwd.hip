@@ -85,6 +85,47 @@ hipError_t launch_quantize(const float* v, int64_t rows, int64_t cols, const flo
     return hipGetLastError();
 }
 
+// ---- dequantised operand for the backward ------------------------------------------
+// out[r][c] = fl(q(v[r][c]) * s) with q the LSQ quantiser, zero rows and
+// columns past the data; thread -> 4 consecutive columns of one padded row.
+__global__ __launch_bounds__(256) void dequant_kernel(const float* __restrict__ v, int64_t rows, int64_t cols,
+                                                      const float* __restrict__ s_dev, float s_host,
+                                                      float* __restrict__ out, int64_t rows_p, int64_t cols_p) {
+    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (c0 >= cols_p) return;
+    const float s = s_dev ? *s_dev : s_host;
+    const bool vec_rows = ((cols & 3) == 0) && ((reinterpret_cast<uintptr_t>(v) & 15) == 0);
+    for (int64_t r = blockIdx.y; r < rows_p; r += gridDim.y) {
+        vf4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (r < rows) {
+            const float* src = v + r * cols;
+            bool in;
+            if (vec_rows && c0 + 4 <= cols) {
+                const vf4 x = *reinterpret_cast<const vf4*>(src + c0);
+                o.x = f_mul((float)quantize_q(x.x, s, &in), s);
+                o.y = f_mul((float)quantize_q(x.y, s, &in), s);
+                o.z = f_mul((float)quantize_q(x.z, s, &in), s);
+                o.w = f_mul((float)quantize_q(x.w, s, &in), s);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c0 + e < cols) o[e] = f_mul((float)quantize_q(src[c0 + e], s, &in), s);
+            }
+        }
+        *reinterpret_cast<vf4*>(out + r * cols_p + c0) = o;
+    }
+}
+
+hipError_t launch_dequant(const float* v, int64_t rows, int64_t cols, const float* s_dev, float s_host,
+                          float* out, int64_t rows_p, int64_t cols_p, hipStream_t st) {
+    if (rows_p <= 0 || cols_p <= 0) return hipSuccess;
+    const unsigned gx = (unsigned)ceil_div(cols_p / 4, 256);
+    const unsigned gy = (unsigned)(rows_p < 8192 ? rows_p : 8192);
+    hipLaunchKernelGGL(dequant_kernel, dim3(gx, gy), dim3(256), 0, st, v, rows, cols, s_dev, s_host, out,
+                       rows_p, cols_p);
+    return hipGetLastError();
+}
+
 // ---- int8 GEMM ---------------------------------------------------------------------
 // Workgroup tile BM x BN (256 x 256), K step 64 bytes (two MFMA k-steps of 32),
 // 4 waves of 128 x 128, each a 4 x 4 grid of v_mfma_i32_32x32x32_i8 tiles.
@@ -110,14 +151,6 @@ struct GemmCfg {
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
-
-// s_waitcnt with vmcnt <= n (n a multiple of the per-stage load count),
-// expcnt and lgkmcnt left unconstrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(GemmArgs a) {

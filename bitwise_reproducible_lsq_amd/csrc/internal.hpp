@@ -27,6 +27,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int bwd_chunk_log2();          // 32-blocks per backward chunk = 2^value
 int reduce_wg_blocks();        // 32-blocks per workgroup in CanonSum passes
 int stream_vec();              // 16-byte vectors per thread in streaming kernels (1, 2, 4)
+int bwd_engine();              // backward products: 1 VALU, 2 matrix cores (when the operands allow)
 
 // ---- CanonSum over a flat vector -------------------------------------------
 enum CanonMap { kMapAbs = 0, kMapSquare = 1 };
@@ -61,6 +62,11 @@ hipError_t launch_quantize(const float* v, int64_t rows, int64_t cols, const flo
                            float s_host, int8_t* q, int64_t rows_p, int64_t cols_p,
                            int64_t swiglu_half, hipStream_t st);
 
+// out[r][c] = fl(q(v[r][c]) * s) for r < rows, c < cols; +0 up to rows_p x cols_p
+// (cols_p a multiple of 4).
+hipError_t launch_dequant(const float* v, int64_t rows, int64_t cols, const float* s_dev, float s_host,
+                          float* out, int64_t rows_p, int64_t cols_p, hipStream_t st);
+
 struct GemmArgs {
     const int8_t* qx;     // [Mp, Kp]
     const int8_t* qw;     // [Nvp, Kp] (interleaved for SwiGLU)
@@ -83,7 +89,8 @@ struct SteArgs {
     bool a_rmaj;           // A(r,i) = A[i*lda + r] (dX) else A[r*lda + i] (dW)
     bool a_vec;            // A and lda allow 16-byte row loads
     int64_t I, R, Jn;
-    const int8_t* Bq;      // [>= round_up(R,32), ldb] int8, zero padded
+    const int8_t* Bq;      // [>= round_up(R,32), ldb] int8, zero padded (VALU engine)
+    const float* Bf;       // [>= round_up(R,32), ldb] fl(q*s), zero padded (matrix-core engine)
     int64_t ldb;
     const float* b_scale_dev;  // step of B (device) or null
     float b_scale_host;
@@ -97,7 +104,8 @@ struct SteArgs {
 };
 int64_t ste_chunks(int64_t R);
 int64_t ste_root_floats(int64_t I, int64_t R, int64_t Jn);
-hipError_t launch_ste(const SteArgs& a, hipStream_t st);
+// engine 2 needs Bf, a_vec and I % 4 == 0 when A is r-major, R % 4 == 0 when i-major
+hipError_t launch_ste(const SteArgs& a, int engine, hipStream_t st);
 
 hipError_t launch_swiglu_bwd(const float* dA, const float* ypre, int64_t M, int64_t N, float* G,
                              const ExpConsts& ek, hipStream_t st);

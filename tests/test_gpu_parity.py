@@ -151,13 +151,52 @@ def test_fwd_zero_weights_and_empty_rows():
 
 
 # ---- linear layer: backward -----------------------------------------------------------
+class tuning:
+    """Set a launch-shape knob for the duration of a with-block."""
+
+    def __init__(self, knob, value):
+        self.knob, self.value = knob, value
+
+    def __enter__(self):
+        self.old = brl.set_tuning(self.knob, self.value)
+
+    def __exit__(self, *exc):
+        brl.set_tuning(self.knob, self.old)
+
+
+ENGINES = [1, 2]   # products on the VALU / on the matrix cores
+
+
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("M,K,N", SHAPES)
-def test_bwd_parity(M, K, N):
+def test_bwd_parity(M, K, N, engine):
     inp = _case_inputs(M, K, N, seed=M * 3 + K + N, sub=0.01)
-    dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), _cuda(inp.X), _cuda(inp.W), synth.S_X)
+    with tuning(brl.TUNE_BWD_ENGINE, engine):
+        dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), _cuda(inp.X), _cuda(inp.W), synth.S_X)
     wX, wW = oracle.linear_bwd(inp.dY, inp.X, inp.W, synth.S_X)
-    assert_bitwise(dX, wX, "dX")
-    assert_bitwise(dW, wW, "dW")
+    assert_bitwise(dX, wX, f"dX (engine {engine})")
+    assert_bitwise(dW, wW, f"dW (engine {engine})")
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 200, 132), (97, 64, 36), (40, 256, 4)])
+def test_bwd_matrix_core_ragged_reductions(M, K, N):
+    """Reductions that end inside a 32-block (M and N not multiples of 32)
+    on the matrix-core engine (N % 4 == 0), and the same call with dY at a
+    4-byte but not 16-byte aligned address, which runs the VALU engine."""
+    inp = _case_inputs(M, K, N, seed=M + 7 * N, sub=0.01)
+    wX, wW = oracle.linear_bwd(inp.dY, inp.X, inp.W, synth.S_X)
+    X, W = _cuda(inp.X), _cuda(inp.W)
+    with tuning(brl.TUNE_BWD_ENGINE, 2):
+        dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), X, W, synth.S_X)
+        assert_bitwise(dX, wX, "dX")
+        assert_bitwise(dW, wW, "dW")
+        flat = torch.empty(M * N + 1, dtype=torch.float32, device="cuda")
+        dY_odd = flat[1:].view(M, N)
+        dY_odd.copy_(_cuda(inp.dY))
+        assert dY_odd.data_ptr() % 16 != 0
+        dX, dW = brl.qat_linear_bwd(dY_odd, X, W, synth.S_X)
+        assert_bitwise(dX, wX, "dX (unaligned dY)")
+        assert_bitwise(dW, wW, "dW (unaligned dY)")
 
 
 def test_bwd_tiny_workload():
@@ -168,25 +207,29 @@ def test_bwd_tiny_workload():
     assert_bitwise(dW, wW, "dW")
 
 
-def test_bwd_long_reductions_and_masks():
+@pytest.mark.parametrize("engine", ENGINES)
+def test_bwd_long_reductions_and_masks(engine):
     """Reductions of many blocks (several chunks and a ragged tail) and
     activations that clip (mask false)."""
     M, K, N = 2100, 40, 1100
     inp = _case_inputs(M, K, N, seed=21, x_kind="silu_x_normal")
     X = inp.X * np.float32(2.0)
     assert (np.abs(X / synth.S_X) > 127).any()
-    dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), _cuda(X), _cuda(inp.W), synth.S_X)
+    with tuning(brl.TUNE_BWD_ENGINE, engine):
+        dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), _cuda(X), _cuda(inp.W), synth.S_X)
     wX, wW = oracle.linear_bwd(inp.dY, X, inp.W, synth.S_X)
     assert_bitwise(dX, wX, "dX")
     assert_bitwise(dW, wW, "dW")
 
 
-def test_bwd_swiglu_parity():
+@pytest.mark.parametrize("engine", ENGINES)
+def test_bwd_swiglu_parity(engine):
     M, K, N = 160, 96, 192
     inp = _case_inputs(M, K, N, seed=31, swiglu=True)
     X, W = _cuda(inp.X), _cuda(inp.W)
     _, Ypre, _ = brl.qat_linear_fwd(X, W, synth.S_X, epilogue=brl.EPILOGUE_SWIGLU)
-    dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), X, W, synth.S_X, Ypre=Ypre, epilogue=brl.EPILOGUE_SWIGLU)
+    with tuning(brl.TUNE_BWD_ENGINE, engine):
+        dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), X, W, synth.S_X, Ypre=Ypre, epilogue=brl.EPILOGUE_SWIGLU)
     _, wPre = oracle.linear_fwd(inp.X, inp.W, synth.S_X, epilogue=1)
     G = oracle.swiglu_bwd(wPre, inp.dY)
     wX, wW = oracle.linear_bwd(G, inp.X, inp.W, synth.S_X)
@@ -194,15 +237,17 @@ def test_bwd_swiglu_parity():
     assert_bitwise(dW, wW, "dW")
 
 
-def test_bwd_microbatch_running_sum():
+@pytest.mark.parametrize("engine", ENGINES)
+def test_bwd_microbatch_running_sum(engine):
     M, K, N, B = 4 * 96, 72, 80, 4
     inp = _case_inputs(M, K, N, seed=41)
     X, W, dY = _cuda(inp.X), _cuda(inp.W), _cuda(inp.dY)
     mb = M // B
     dW = None
-    for b in range(B):
-        _, dW = brl.qat_linear_bwd(dY[b * mb:(b + 1) * mb], X[b * mb:(b + 1) * mb], W, synth.S_X,
-                                   need_dX=False, dW=dW, dW_accumulate=b > 0)
+    with tuning(brl.TUNE_BWD_ENGINE, engine):
+        for b in range(B):
+            _, dW = brl.qat_linear_bwd(dY[b * mb:(b + 1) * mb], X[b * mb:(b + 1) * mb], W, synth.S_X,
+                                       need_dX=False, dW=dW, dW_accumulate=b > 0)
     want = oracle.dw_rows(np.ascontiguousarray(inp.dY.T), inp.X, inp.W, synth.S_X, np.arange(N), mb=mb)
     assert_bitwise(dW, want, "dW (4 microbatches)")
 
@@ -224,16 +269,20 @@ def test_bwd_launch_shape_invariance():
     X, W, dY = _cuda(inp.X), _cuda(inp.W), _cuda(inp.dY)
     old_c = brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, 0)
     old_r = brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, 0)
+    old_e = brl.set_tuning(brl.TUNE_BWD_ENGINE, 0)
     try:
-        for c, r in [(1, 64), (2, 128), (3, 256), (4, 64), (5, 128), (6, 256)]:
-            brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, c)
-            brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, r)
-            dX, dW = brl.qat_linear_bwd(dY, X, W, synth.S_X)
-            assert_bitwise(dX, wX, f"dX chunk=2^{c} wg={r}")
-            assert_bitwise(dW, wW, f"dW chunk=2^{c} wg={r}")
+        for e in ENGINES:
+            brl.set_tuning(brl.TUNE_BWD_ENGINE, e)
+            for c, r in [(1, 64), (2, 128), (3, 256), (4, 64), (5, 128), (6, 256)]:
+                brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, c)
+                brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, r)
+                dX, dW = brl.qat_linear_bwd(dY, X, W, synth.S_X)
+                assert_bitwise(dX, wX, f"dX chunk=2^{c} wg={r} engine={e}")
+                assert_bitwise(dW, wW, f"dW chunk=2^{c} wg={r} engine={e}")
     finally:
         brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, old_c)
         brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, old_r)
+        brl.set_tuning(brl.TUNE_BWD_ENGINE, old_e)
 
 
 def test_repeat_runs_identical():

@@ -140,3 +140,17 @@ def test_hot_loops_use_plain_mul_and_add():
         n_mul = len(re.findall(r"\tv_mul_f32", body))
         n_add = len(re.findall(r"\tv_add_f32", body))
         assert n_mul >= 512 and n_add >= 480, (name, n_mul, n_add)
+
+def test_matrix_core_backward_keeps_products_in_vgprs():
+    """The matrix-core backward forms products with the K=1 fp32 MFMA and adds
+    them with v_add_f32 straight from VGPRs (no accumulator-register copies,
+    no fused add)."""
+    text = open([f for f in brl_build.asm_files() if "bwd" in f][0]).read()
+    names = sorted(set(re.findall(r"^(_ZN3brl15ste_mfma_kernel\w+):", text, re.M)))
+    assert len(names) >= 12, names
+    for name in names:
+        body = text.split(name + ":")[1].split("s_endpgm")[0]
+        assert len(re.findall(r"\tv_mfma_f32_16x16x1_4b_f32", body)) >= 32, name
+        assert len(re.findall(r"\tv_add_f32", body)) >= 512, name
+        assert "v_accvgpr_read" not in body, name
+        assert not re.search(r"\tv_mfma\S* a\[", body), name
