@@ -27,7 +27,7 @@ OP_FWD, OP_BWD, OP_NORM = 0, 1, 2
 TUNE_BWD_CHUNK_LOG2, TUNE_REDUCE_WG_BLOCKS, TUNE_STREAM_VEC, TUNE_BWD_ENGINE = 0, 1, 2, 3
 MAX_REPLICAS = 64
 
-PROBE_OPS = {"add": 0, "sub": 1, "mul": 2, "div": 3, "sqrt": 4, "i2f": 5, "rne": 6, "exp": 7}
+PROBE_OPS = {"add": 0, "sub": 1, "mul": 2, "div": 3, "sqrt": 4, "i2f": 5, "rne": 6, "exp": 7, "mfma_mul": 8}
 
 
 class BrlError(RuntimeError):

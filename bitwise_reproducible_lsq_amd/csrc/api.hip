@@ -357,9 +357,11 @@ brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float eps, fl
 }
 
 brl_status brl_probe_f32(int32_t op, const float* a, const float* b, float* out, int64_t n, void* stream) {
-    if (op < 0 || op > 7) return fail(BRL_EINVAL, "brl_probe_f32: unknown op %d", op);
+    if (op < 0 || op > 8) return fail(BRL_EINVAL, "brl_probe_f32: unknown op %d", op);
     if (n < 0) return fail(BRL_ESHAPE, "brl_probe_f32: n < 0");
-    if (n > 0 && (!a || !out || (op <= 3 && !b))) return fail(BRL_EINVAL, "brl_probe_f32: null pointer");
+    if (n > 0 && (!a || !out || ((op <= 3 || op == 8) && !b))) return fail(BRL_EINVAL, "brl_probe_f32: null pointer");
+    if (op == 8)
+        return check_hip(launch_probe_mfma(a, b, out, n, static_cast<hipStream_t>(stream)), "probe");
     return check_hip(launch_probe(op, a, b, out, n, exp_constants(), static_cast<hipStream_t>(stream)), "probe");
 }
 

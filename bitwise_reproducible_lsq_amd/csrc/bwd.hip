@@ -255,7 +255,7 @@ constexpr int kMStage = kMTileA + kMTileB;        // 16 KB
 __device__ __forceinline__ int mswz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 template <bool A_RMAJ, int D>
-__global__ __launch_bounds__(256) void ste_mfma_kernel(SteArgs a, int64_t nblk, int final_out) {
+__global__ __launch_bounds__(256, 3) void ste_mfma_kernel(SteArgs a, int64_t nblk, int final_out) {
     __shared__ __attribute__((aligned(16))) float smem[kMStages * kMStage];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -389,6 +389,39 @@ __global__ __launch_bounds__(256) void ste_mfma_kernel(SteArgs a, int64_t nblk, 
             }
         }
     }
+}
+
+// Conformance probe of the matrix-core product: each wave takes 64 pairs,
+// lane l feeding a[l] as A row l and b[l] as B column l % 16 of the 16x16x1
+// MFMA (four 16x16 blocks, block beta = lanes 16beta..16beta+15, C = -0).
+// The product of pair 16beta + t sits at row t, column t of block beta: lane
+// 16(t/4) + t, register 4beta + t%4.
+__global__ __launch_bounds__(64) void probe_mfma_kernel(const float* __restrict__ a, const float* __restrict__ b,
+                                                        float* __restrict__ out, int64_t n) {
+    const int lane = threadIdx.x;
+    const int64_t base = (int64_t)blockIdx.x * 64;
+    const float x = base + lane < n ? a[base + lane] : 0.0f;
+    // B column c of block beta comes from lane 16beta + c: give it b of pair 16beta + c
+    const float y = base + lane < n ? b[base + lane] : 0.0f;
+    v16f cneg;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cneg[r] = -0.0f;
+    const v16f d = __builtin_amdgcn_mfma_f32_16x16x1f32(x, y, cneg, 0, 0, 0);
+    const int t = lane & 15;
+    if (lane == 16 * (t >> 2) + t) {
+#pragma unroll
+        for (int beta = 0; beta < 4; ++beta) {
+            const int64_t i = base + 16 * beta + t;
+            const int r = 4 * beta + (t & 3);
+            if (i < n) out[i] = d[r];
+        }
+    }
+}
+
+hipError_t launch_probe_mfma(const float* a, const float* b, float* out, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)ceil_div(n, 64)), dim3(64), 0, st, a, b, out, n);
+    return hipGetLastError();
 }
 
 // Pairwise tree over the Q chunk roots of each output, then mask (+ running

@@ -118,6 +118,8 @@ hipError_t launch_fold(const FoldPtrs& p, int R, const float* g_last, float* out
                        hipStream_t st);
 hipError_t launch_clip(float* g, int64_t n, const Scalars* scal, hipStream_t st);
 
+// out[i] = a[i] * b[i] formed by the matrix-core product of the backward
+hipError_t launch_probe_mfma(const float* a, const float* b, float* out, int64_t n, hipStream_t st);
 hipError_t launch_probe(int op, const float* a, const float* b, float* out, int64_t n,
                         const ExpConsts& ek, hipStream_t st);
 

@@ -174,7 +174,9 @@ BRL_API brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float
 /* Conformance probe of the device's binary32 operations, as the kernels use
  * them: out[i] = op(a[i], b[i]) for op 0 add, 1 sub, 2 mul, 3 div, 4 sqrt (a),
  * 5 int32 bits of a -> float, 6 round-to-nearest-even integral (a),
- * 7 the SwiGLU exp E(a).  Device pointers, n >= 0. */
+ * 7 the SwiGLU exp E(a), 8 the product a*b as the backward's matrix-core
+ * engine forms it (K=1 fp32 MFMA with a -0 accumulator).  Device pointers,
+ * n >= 0. */
 BRL_API brl_status brl_probe_f32(int32_t op, const float* a, const float* b, float* out, int64_t n,
                          void* stream);
 

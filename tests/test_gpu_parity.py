@@ -68,7 +68,7 @@ def _probe_inputs(n, seed):
     return a, b
 
 
-@pytest.mark.parametrize("op", ["add", "sub", "mul", "div", "sqrt", "rne", "exp"])
+@pytest.mark.parametrize("op", ["add", "sub", "mul", "div", "sqrt", "rne", "exp", "mfma_mul"])
 def test_device_binary32_ops_match_oracle(op):
     a, b = _probe_inputs(20000, 3)
     if op == "sqrt":
@@ -79,13 +79,44 @@ def test_device_binary32_ops_match_oracle(op):
     if op == "exp":
         a = np.random.default_rng(6).uniform(-110, 95, 20000).astype(np.float32)
     got = brl.probe_f32(op, _cuda(a), _cuda(b)).cpu().numpy()
-    fn = {"add": oracle.add, "sub": oracle.sub, "mul": oracle.mul, "div": oracle.div,
+    fn = {"add": oracle.add, "sub": oracle.sub, "mul": oracle.mul, "mfma_mul": oracle.mul, "div": oracle.div,
           "sqrt": lambda x, y: oracle.sqrt(x), "rne": lambda x, y: oracle.rne(x),
           "exp": lambda x, y: oracle.exp(x)}[op]
     want = np.array([fn(x, y) for x, y in zip(a, b)], np.float32)
     nan = np.isnan(got) & np.isnan(want)
     bad = np.flatnonzero((_bits(got) != _bits(want)) & ~nan)
     assert bad.size == 0, [(a[i], b[i], got[i], want[i]) for i in bad[:5]]
+
+
+def test_matrix_core_products_on_crafted_classes():
+    """The matrix-core product equals the oracle's binary32 product on classes
+    aimed at its corners: random bit patterns, products around 2^-126 (the FTZ
+    band where tininess after rounding keeps a normal result), subnormal
+    operands, signed zeros, overflow, and products that are exact ties."""
+    g = np.random.default_rng(8)
+    n = 1 << 16
+    sign = lambda: g.integers(0, 2, n, dtype=np.uint32) << 31
+    man = lambda: g.integers(0, 1 << 23, n, dtype=np.uint32)
+    classes = []
+    ea = g.integers(1, 255, n, dtype=np.uint32); eb = g.integers(1, 255, n, dtype=np.uint32)
+    classes.append((sign() | (ea << 23) | man(), sign() | (eb << 23) | man()))
+    ea = g.integers(1, 127, n, dtype=np.uint32); eb = 127 - ea + g.integers(0, 3, n, dtype=np.uint32)
+    classes.append((sign() | (ea << 23) | man(), sign() | (eb << 23) | man()))
+    ea = np.where(g.integers(0, 2, n) == 1, 0, 100).astype(np.uint32)
+    classes.append((sign() | (ea << 23) | man(), sign() | (np.uint32(127) << 23) | man()))
+    z = np.where(g.integers(0, 3, n) == 0, 0, np.uint32(127) << 23).astype(np.uint32)
+    classes.append((sign() | z | np.where(z == 0, 0, man()).astype(np.uint32), sign() | (np.uint32(127) << 23) | man()))
+    ea = g.integers(190, 255, n, dtype=np.uint32)
+    classes.append((sign() | (ea << 23) | man(), sign() | (ea << 23) | man()))
+    ea = g.integers(120, 135, n, dtype=np.uint32)
+    classes.append((sign() | (ea << 23) | (man() & 0x7FF000), sign() | (ea << 23) | (man() & 0x7FF800)))
+    for i, (ua, ub) in enumerate(classes):
+        a, b = ua.view(np.float32), ub.view(np.float32)
+        got = brl.probe_f32("mfma_mul", _cuda(a), _cuda(b)).cpu().numpy()
+        want = np.array([oracle.mul(x, y) for x, y in zip(a, b)], np.float32)
+        nan = np.isnan(got) & np.isnan(want)
+        bad = np.flatnonzero((_bits(got) != _bits(want)) & ~nan)
+        assert bad.size == 0, (i, [(hex(ua[k]), hex(ub[k]), got[k], want[k]) for k in bad[:5]])
 
 
 def test_device_int_to_float_rne():
