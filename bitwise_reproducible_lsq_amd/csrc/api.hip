@@ -14,7 +14,7 @@ namespace brl {
 
 // ---- tuning knobs (launch shapes only) -----------------------------------------
 static std::atomic<int64_t> g_tune[4] = {{0}, {0}, {0}, {0}};
-static const int64_t kTuneDefault[4] = {4, 256, 1, 2};
+static const int64_t kTuneDefault[4] = {5, 256, 1, 2};
 
 int bwd_chunk_log2() {
     int64_t v = g_tune[BRL_TUNE_BWD_CHUNK_LOG2].load();

@@ -249,6 +249,9 @@ constexpr int kMTileA = kTile * kBlock;           // floats of A per block (64 x
 constexpr int kMTileB = kBlock * kTile;           // floats of B per block (32 x 64)
 constexpr int kMStage = kMTileA + kMTileB;        // 16 KB
 
+// Source of the 16-byte pieces of A past the end of the reduction.
+__device__ __attribute__((aligned(16))) float kNegZero4[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
+
 // i-major A tile: row i holds 8 chunks of 4 reduction steps, chunk c stored
 // at slot c ^ ((i >> 1) & 7), so the 16-byte reads of 16 consecutive rows hit
 // 16 distinct bank groups.
@@ -268,9 +271,12 @@ __global__ __launch_bounds__(256, 3) void ste_mfma_kernel(SteArgs a, int64_t nbl
 
     // Direct loads of one 32-block into a stage: per operand 8 KB = 8 groups
     // of 1 KB, wave w moving groups w and w + 4 (64 lanes x 16 bytes each).
-    // Sources outside the operand are redirected to element 0 of a valid
-    // row: rows past I only feed outputs that are never stored, and reduction
-    // steps past R are overwritten with -0 before use.
+    // A 16-byte piece of A holds 4 consecutive reduction steps (dX, R % 4 ==
+    // 0) or 4 consecutive rows (dW, I % 4 == 0), so each piece is wholly
+    // inside or outside the operand.  Pieces past R load four -0 from
+    // kNegZero4 (then A = -0 meets B = +0 in B's zero padding: product -0);
+    // pieces of rows past I load element 0 of a valid row and only feed
+    // outputs that are never stored.
     auto issue = [&](int64_t blk, int stage) {
         float* sA = smem + stage * kMStage;
         float* sB = sA + kMTileA;
@@ -282,17 +288,17 @@ __global__ __launch_bounds__(256, 3) void ste_mfma_kernel(SteArgs a, int64_t nbl
             if constexpr (A_RMAJ) {
                 // G[i][r]: group g = rows 8g..8g+7, lane -> (row, slot)
                 const int row = g * 8 + (lane >> 3), c = mswz(row, lane & 7);
-                int64_t i = i0 + row, r = r0 + 4 * c;
+                int64_t i = i0 + row;
+                const int64_t r = r0 + 4 * c;
                 if (i >= a.I) i = a.I - 1;
-                if (r >= a.R) r = 0;
-                src = a.A + i * a.lda + r;
+                src = r < a.R ? a.A + i * a.lda + r : kNegZero4;
             } else {
                 // G[r][i]: group g = reduction rows 4g..4g+3, 16 chunks each
                 const int row = g * 4 + (lane >> 4);
-                int64_t r = r0 + row, i = i0 + 4 * (lane & 15);
-                if (r >= a.R) r = 0;
+                const int64_t r = r0 + row;
+                int64_t i = i0 + 4 * (lane & 15);
                 if (i >= a.I) i = 0;
-                src = a.A + r * a.lda + i;
+                src = r < a.R ? a.A + r * a.lda + i : kNegZero4;
             }
             __builtin_amdgcn_global_load_lds(src, sA + g * 256, 16, 0, 0);
             const int brow = g * 4 + (lane >> 4);
@@ -325,25 +331,8 @@ __global__ __launch_bounds__(256, 3) void ste_mfma_kernel(SteArgs a, int64_t nbl
         __asm__ volatile("" ::: "memory");
         if (blk + 2 < b_end) issue(blk + 2, (t + 2) % kMStages);
 
-        float* sA = smem + stage * kMStage;
+        const float* sA = smem + stage * kMStage;
         const float* sB = sA + kMTileA;
-        const int64_t r0 = blk * kBlock;
-        if (r0 + kBlock > a.R) {
-            // the ragged last block: steps past R read A = -0
-            const int nvalid = (int)(a.R - r0);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int idx = tid * 8 + e;
-                if constexpr (A_RMAJ) {
-                    const int row = idx >> 5, rr = idx & 31;
-                    if (rr >= nvalid) sA[row * kBlock + 4 * mswz(row, rr >> 2) + (rr & 3)] = -0.0f;
-                } else {
-                    const int rr = idx >> 6;
-                    if (rr >= nvalid) sA[idx] = -0.0f;
-                }
-            }
-            __syncthreads();
-        }
 
 #pragma unroll
         for (int rs = 0; rs < kBlock; rs += 4) {
