@@ -14,11 +14,15 @@ namespace brl {
 
 // ---- tuning knobs (launch shapes only) -----------------------------------------
 static std::atomic<int64_t> g_tune[4] = {{0}, {0}, {0}, {0}};
-static const int64_t kTuneDefault[4] = {5, 256, 1, 2};
+static const int64_t kTuneDefault[4] = {0, 256, 1, 2};   // chunk depth 0: per engine
 
-int bwd_chunk_log2() {
+int bwd_chunk_log2(int engine) {
     int64_t v = g_tune[BRL_TUNE_BWD_CHUNK_LOG2].load();
-    return (int)(v > 0 ? v : kTuneDefault[BRL_TUNE_BWD_CHUNK_LOG2]);
+    if (v > 0) return (int)v;
+    // defaults: the deepest stack that keeps 3 workgroups per CU
+    if (engine == 2) return 5;
+    if (engine == 1) return 4;
+    return 4;   // any engine: the smaller depth (more chunk roots) bounds the workspace
 }
 int reduce_wg_blocks() {
     int64_t v = g_tune[BRL_TUNE_REDUCE_WG_BLOCKS].load();
@@ -214,7 +218,7 @@ brl_status qat_linear_bwd(const float* dOut, const float* X, const float* W, con
     if (dW_accumulate != 0 && dW_accumulate != 1) return fail(BRL_EINVAL, "qat_linear_bwd: dW_accumulate must be 0 or 1");
     if (!aligned4(dOut) || !aligned4(X) || !aligned4(W) || !aligned4(Ypre) || !aligned4(dX) || !aligned4(dW))
         return fail(BRL_EINVAL, "qat_linear_bwd: pointers must be 4-byte aligned");
-    const int64_t Qx = ste_chunks(N), Qw = ste_chunks(M);
+    const int64_t Qx = ste_chunks(N, 0), Qw = ste_chunks(M, 0);
     if (Qx > 1024 || Qw > 1024)
         return fail(BRL_ESHAPE, "qat_linear_bwd: reduction too long for the chunk setting (%lld, %lld chunks)",
                     (long long)Qx, (long long)Qw);

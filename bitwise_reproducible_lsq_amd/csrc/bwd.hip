@@ -334,24 +334,30 @@ __global__ __launch_bounds__(256, 3) void ste_mfma_kernel(SteArgs a, int64_t nbl
         const float* sA = smem + stage * kMStage;
         const float* sB = sA + kMTileA;
 
-#pragma unroll
-        for (int rs = 0; rs < kBlock; rs += 4) {
-            float av[4], bv[4];
+        // operands of 4 steps are read one group ahead; the product of step
+        // s+1 is formed (into the other of two product buffers) before the
+        // adds of step s, so matrix-core and VALU work of one wave interleave
+        float av[kBlock], bv[kBlock];
+        auto read_group = [&](int rs) {
             if constexpr (A_RMAJ) {
                 const vf4 v = *reinterpret_cast<const vf4*>(sA + lane * kBlock + 4 * mswz(lane, rs >> 2));
-                av[0] = v.x; av[1] = v.y; av[2] = v.z; av[3] = v.w;
+                av[rs] = v.x; av[rs + 1] = v.y; av[rs + 2] = v.z; av[rs + 3] = v.w;
             } else {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) av[s] = sA[(rs + s) * kTile + lane];
+                for (int s = 0; s < 4; ++s) av[rs + s] = sA[(rs + s) * kTile + lane];
             }
 #pragma unroll
-            for (int s = 0; s < 4; ++s) bv[s] = sB[(rs + s) * kTile + bcol];
+            for (int s = 0; s < 4; ++s) bv[rs + s] = sB[(rs + s) * kTile + bcol];
+        };
+        v16f p[2];
+        read_group(0);
+        p[0] = __builtin_amdgcn_mfma_f32_16x16x1f32(av[0], bv[0], cneg, 0, 0, 0);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const v16f p = __builtin_amdgcn_mfma_f32_16x16x1f32(av[s], bv[s], cneg, 0, 0, 0);
-                if (rs == 0 && s == 0) acc = p;
-                else acc = acc + p;
-            }
+        for (int s = 0; s < kBlock; ++s) {
+            if ((s & 3) == 0 && s + 4 < kBlock) read_group(s + 4);
+            if (s + 1 < kBlock) p[(s + 1) & 1] = __builtin_amdgcn_mfma_f32_16x16x1f32(av[s + 1], bv[s + 1], cneg, 0, 0, 0);
+            if (s == 0) acc = p[0];
+            else acc = acc + p[s & 1];
         }
         stack_push<v16f, 0, D>(st, acc, (unsigned)t);
     }
@@ -442,12 +448,12 @@ __global__ __launch_bounds__(256) void ste_finish_kernel(SteArgs a, int64_t Q) {
     }
 }
 
-int64_t ste_chunks(int64_t R) {
-    return ceil_div(ceil_div(R, kBlock), (int64_t)1 << bwd_chunk_log2());
+int64_t ste_chunks(int64_t R, int engine) {
+    return ceil_div(ceil_div(R, kBlock), (int64_t)1 << bwd_chunk_log2(engine));
 }
 
 int64_t ste_root_floats(int64_t I, int64_t R, int64_t Jn) {
-    const int64_t Q = ste_chunks(R);
+    const int64_t Q = ste_chunks(R, 0);
     return Q > 1 ? Q * I * Jn : 0;
 }
 
@@ -484,7 +490,7 @@ static void ste_launch_mfma(const SteArgs& a, int D, dim3 grid, int64_t nblk, in
 
 hipError_t launch_ste(const SteArgs& a, int engine, hipStream_t st) {
     if (a.I <= 0 || a.Jn <= 0) return hipSuccess;
-    const int D = bwd_chunk_log2();
+    const int D = bwd_chunk_log2(engine);
     const int64_t nblk = ceil_div(a.R, kBlock);
     if (nblk == 0) {
         const int64_t plane = a.I * a.Jn;

@@ -24,7 +24,7 @@ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Launch-shape knobs (never change results).
-int bwd_chunk_log2();          // 32-blocks per backward chunk = 2^value
+int bwd_chunk_log2(int engine); // 32-blocks per backward chunk = 2^value (engine 0: workspace bound)
 int reduce_wg_blocks();        // 32-blocks per workgroup in CanonSum passes
 int stream_vec();              // 16-byte vectors per thread in streaming kernels (1, 2, 4)
 int bwd_engine();              // backward products: 1 VALU, 2 matrix cores (when the operands allow)
@@ -102,8 +102,8 @@ struct SteArgs {
     int accumulate;
     float* roots;          // workspace for chunk roots [Q, I, Jn]
 };
-int64_t ste_chunks(int64_t R);
-int64_t ste_root_floats(int64_t I, int64_t R, int64_t Jn);
+int64_t ste_chunks(int64_t R, int engine);
+int64_t ste_root_floats(int64_t I, int64_t R, int64_t Jn);   // bound over engines
 // engine 2 needs Bf, a_vec and I % 4 == 0 when A is r-major, R % 4 == 0 when i-major
 hipError_t launch_ste(const SteArgs& a, int engine, hipStream_t st);
 
