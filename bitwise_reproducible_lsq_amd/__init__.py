@@ -8,7 +8,7 @@ stream is passed to every call).  There is no fallback: if the library is not
 built or cannot load, every call raises.
 
 Names follow the C ABI: qat_linear_fwd, qat_linear_bwd, ordered_reduce,
-grad_l2norm_clip.
+grad_l2norm_clip, state_hash (brl_state_hash).
 """
 from __future__ import annotations
 
@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libbrlsq.so")
 
 BRL_OK, BRL_EINVAL, BRL_ESHAPE, BRL_EORDER, BRL_EDEVICE, BRL_EWORKSPACE = 0, -1, -2, -3, -4, -5
 EPILOGUE_NONE, EPILOGUE_SWIGLU = 0, 1
-OP_FWD, OP_BWD, OP_NORM = 0, 1, 2
+OP_FWD, OP_BWD, OP_NORM, OP_HASH = 0, 1, 2, 3
 TUNE_BWD_CHUNK_LOG2, TUNE_REDUCE_WG_BLOCKS, TUNE_STREAM_VEC, TUNE_BWD_ENGINE = 0, 1, 2, 3
 MAX_REPLICAS = 64
 
@@ -53,6 +53,7 @@ _SIGS = {
     "ordered_reduce": (i32, [C.POINTER(ReduceStateC), P, P, P]),
     "grad_l2norm_clip": (i32, [P, i64, f32, f32, P, P, sz, P]),
     "brl_probe_f32": (i32, [i32, P, P, P, i64, P]),
+    "brl_state_hash": (i32, [P, P, i32, P, P, sz, P]),
     "brl_set_tuning": (i64, [i32, i64]),
     "brl_status_string": (C.c_char_p, [i32]),
     "brl_last_error": (C.c_char_p, []),
@@ -221,6 +222,30 @@ def grad_l2norm_clip(g: torch.Tensor, max_norm: float = 1.0, eps: float = 0.0,
     _check(lib().grad_l2norm_clip(_ptr(g), n, float(max_norm), float(eps), _ptr(nu), _ptr(ws), ws.numel(),
                                   _stream(stream)))
     return nu
+
+
+def state_hash(tensors: Sequence[torch.Tensor], ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """SHA-256 tree hash of the tensors' raw bytes, in order (brl_state_hash);
+    returns the 32-byte digest as a uint8 device tensor."""
+    if len(tensors) == 0:
+        raise ValueError("the state has at least one tensor")
+    dev = tensors[0].device
+    n = len(tensors)
+    ptrs = (C.c_void_p * n)(*[(_ptr(t).value if t.numel() > 0 else None) for t in tensors])
+    nbytes = (C.c_int64 * n)(*[t.numel() * t.element_size() for t in tensors])
+    total = sum(nbytes)
+    need = int(lib().brl_workspace_bytes(OP_HASH, total, n, 0))
+    if ws is None:
+        key = (dev.type, dev.index, OP_HASH)
+        w = _ws_cache.get(key)
+        if w is None or w.numel() < need:
+            w = torch.empty(need, dtype=torch.uint8, device=dev)
+            _ws_cache[key] = w
+        ws = w
+    out = torch.empty(32, dtype=torch.uint8, device=dev)
+    _check(lib().brl_state_hash(C.cast(ptrs, C.c_void_p), C.cast(nbytes, C.c_void_p), n, _ptr(out), _ptr(ws),
+                                ws.numel(), _stream(stream)))
+    return out
 
 
 def probe_f32(op: str, a: torch.Tensor, b: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

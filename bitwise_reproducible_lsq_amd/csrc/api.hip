@@ -156,8 +156,38 @@ using namespace brl;
 
 extern "C" {
 
+// State hash workspace: every level of digests (level 0 = the leaves) and
+// the tensor lengths.
+struct HashLayout {
+    int64_t levels[24];      // digests per level
+    uint8_t* level_ptr[24];
+    int nlev;
+    int64_t* lens;
+    size_t bytes;
+};
+
+static HashLayout hash_layout(void* ws, int64_t leaves, int64_t count) {
+    HashLayout L{};
+    Carver c(ws);
+    int64_t n = leaves;
+    L.nlev = 0;
+    while (true) {
+        L.levels[L.nlev] = n;
+        L.level_ptr[L.nlev] = c.take<uint8_t>((size_t)(n * 32));
+        ++L.nlev;
+        if (n <= 1) break;
+        n = ceil_div(n, kHashFanIn);
+    }
+    L.lens = c.take<int64_t>((size_t)count);
+    L.bytes = c.off + 256;
+    return L;
+}
+
 size_t brl_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N) {
     switch (op) {
+        case BRL_OP_HASH:
+            if (M < 0 || K < 1 || K > ((int64_t)1 << 31)) return 0;
+            return hash_layout(nullptr, M / kHashLeafBytes + K, K).bytes;
         case BRL_OP_FWD: return sizes_ok(M, K, N) ? fwd_layout(nullptr, M, K, N, BRL_EPILOGUE_SWIGLU).bytes : 0;
         case BRL_OP_BWD: return sizes_ok(M, K, N) ? bwd_layout(nullptr, M, K, N, BRL_EPILOGUE_SWIGLU).bytes : 0;
         case BRL_OP_NORM: return M >= 0 ? norm_bytes(M) : 0;
@@ -367,6 +397,53 @@ brl_status brl_probe_f32(int32_t op, const float* a, const float* b, float* out,
     if (op == 8)
         return check_hip(launch_probe_mfma(a, b, out, n, static_cast<hipStream_t>(stream)), "probe");
     return check_hip(launch_probe(op, a, b, out, n, exp_constants(), static_cast<hipStream_t>(stream)), "probe");
+}
+
+brl_status brl_state_hash(const void* const* tensors, const int64_t* nbytes, int32_t count, uint8_t* digest,
+                          void* ws, size_t ws_bytes, void* stream) {
+    if (count < 1 || !tensors || !nbytes) return fail(BRL_EINVAL, "brl_state_hash: need count >= 1 tensors");
+    if (!digest) return fail(BRL_EINVAL, "brl_state_hash: null digest");
+    int64_t total = 0, leaves = 0;
+    bool vec = true;
+    for (int32_t i = 0; i < count; ++i) {
+        if (nbytes[i] < 0) return fail(BRL_ESHAPE, "brl_state_hash: nbytes[%d] < 0", (int)i);
+        if (nbytes[i] > 0 && !tensors[i]) return fail(BRL_EINVAL, "brl_state_hash: tensor %d is null", (int)i);
+        if (!aligned4(tensors[i])) return fail(BRL_EINVAL, "brl_state_hash: tensor %d not 4-byte aligned", (int)i);
+        if ((reinterpret_cast<uintptr_t>(tensors[i]) & 15) != 0) vec = false;
+        total += nbytes[i];
+        leaves += nbytes[i] == 0 ? 1 : ceil_div(nbytes[i], kHashLeafBytes);
+    }
+    const HashLayout need = hash_layout(nullptr, leaves, count);
+    if (!ws || ws_bytes < need.bytes)
+        return fail(BRL_EWORKSPACE, "brl_state_hash: workspace %zu < %zu bytes", ws_bytes, need.bytes);
+    HashLayout L = hash_layout(ws, leaves, count);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // leaves, 64 tensors per launch
+    int64_t leaf_base = 0;
+    for (int32_t t0 = 0; t0 < count; t0 += kHashBatch) {
+        HashBatch hb{};
+        hb.n = (count - t0) < kHashBatch ? (count - t0) : kHashBatch;
+        hb.first_tensor = t0;
+        hb.leaf_base = leaf_base;
+        int64_t acc = 0;
+        for (int i = 0; i < hb.n; ++i) {
+            hb.ptr[i] = tensors[t0 + i];
+            hb.len[i] = nbytes[t0 + i];
+            hb.first_leaf[i] = acc;
+            acc += nbytes[t0 + i] == 0 ? 1 : ceil_div(nbytes[t0 + i], kHashLeafBytes);
+        }
+        hb.leaves = acc;
+        brl_status s = check_hip(launch_hash_leaves(hb, vec, L.level_ptr[0], L.lens, st), "hash leaves");
+        if (s) return s;
+        leaf_base += acc;
+    }
+    for (int l = 1; l < L.nlev; ++l) {
+        brl_status s = check_hip(launch_hash_nodes(L.level_ptr[l - 1], L.levels[l - 1], L.level_ptr[l], st),
+                                 "hash nodes");
+        if (s) return s;
+    }
+    (void)total;
+    return check_hip(launch_hash_root(L.level_ptr[L.nlev - 1], L.lens, count, digest, st), "hash root");
 }
 
 int64_t brl_set_tuning(int32_t knob, int64_t value) {

@@ -110,6 +110,25 @@ hipError_t launch_ste(const SteArgs& a, int engine, hipStream_t st);
 hipError_t launch_swiglu_bwd(const float* dA, const float* ypre, int64_t M, int64_t N, float* G,
                              const ExpConsts& ek, hipStream_t st);
 
+// ---- state hash (SHA-256 tree) -------------------------------------------------
+constexpr int64_t kHashLeafBytes = 16384;   // bytes of a tensor per leaf
+constexpr int64_t kHashFanIn = 512;         // digests per node
+constexpr int kHashBatch = 64;              // tensors per leaf launch
+struct HashBatch {
+    const void* ptr[kHashBatch];
+    int64_t len[kHashBatch];
+    int64_t first_leaf[kHashBatch];   // first leaf of each tensor, counted from the batch's first leaf
+    int32_t n;                        // tensors in the batch
+    int32_t pad;
+    int64_t first_tensor;             // index of ptr[0] in the state
+    int64_t leaf_base;                // index of the batch's first leaf among all leaves
+    int64_t leaves;                   // leaves in the batch
+};
+hipError_t launch_hash_leaves(const HashBatch& hb, bool vec, uint8_t* digests, int64_t* lens, hipStream_t st);
+hipError_t launch_hash_nodes(const uint8_t* in, int64_t n_in, uint8_t* out, hipStream_t st);
+hipError_t launch_hash_root(const uint8_t* top, const int64_t* lens, int64_t count, uint8_t* out, hipStream_t st);
+void sha256_constants(uint32_t* k64, uint32_t* h8);
+
 // ---- replay -------------------------------------------------------------------
 // first = 1: A <- G; otherwise A <- A + G.
 hipError_t launch_accumulate(float* A, const float* G, int64_t n, int first, hipStream_t st);

@@ -77,10 +77,13 @@ typedef int32_t brl_status;
 #define BRL_OP_FWD  0
 #define BRL_OP_BWD  1
 #define BRL_OP_NORM 2
+#define BRL_OP_HASH 3
 
 /* Bytes of device workspace needed by an operation.  For BRL_OP_FWD and
  * BRL_OP_BWD, M, K, N are the layer sizes (N = stacked width for SwiGLU);
- * for BRL_OP_NORM, M is the vector length and K, N are ignored. */
+ * for BRL_OP_NORM, M is the vector length and K, N are ignored; for
+ * BRL_OP_HASH, M is the total byte length of the state and K its tensor
+ * count (N ignored). */
 BRL_API size_t brl_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N);
 
 /*
@@ -170,6 +173,28 @@ BRL_API brl_status ordered_reduce(brl_reduce_state* st, const float* partial, fl
  */
 BRL_API brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float eps, float* norm_out,
                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * brl_state_hash -- on-device hash of a training state (a list of tensors).
+ * The pages store a hash of the state after every step and require a
+ * replayed step to reproduce it; they name moving that hashing from the host
+ * (about 6 s per step) onto the device as future work (onedev.kr summary,
+ * sections "Use" and "Limits"; rit.work article body).  They do not name the
+ * function; this library computes SHA-256 (FIPS 180-4) arranged as a tree:
+ *   leaf  = SHA-256(16 KiB piece of one tensor's bytes || 0x00), pieces in
+ *           order, the last piece of a tensor shorter, an empty tensor one
+ *           empty piece; the leaves of all tensors, tensor after tensor;
+ *   node  = SHA-256(512 consecutive digests (fewer for the last) || 0x01),
+ *           level after level until one digest remains;
+ *   root  = SHA-256(top || le64(count) || le64(nbytes[0]) ... || 0x02).
+ * tensors: count (>= 1) device pointers, 4-byte aligned, read as raw bytes
+ * (tensors[i] may be NULL when nbytes[i] == 0); nbytes: host array of byte
+ * lengths >= 0; digest: device pointer receiving the 32 root bytes.  The host
+ * arrays are read during the call only.  Workspace from
+ * brl_workspace_bytes(BRL_OP_HASH, sum of nbytes, count, 0).
+ */
+BRL_API brl_status brl_state_hash(const void* const* tensors, const int64_t* nbytes, int32_t count,
+                                  uint8_t* digest, void* ws, size_t ws_bytes, void* stream);
 
 /* Conformance probe of the device's binary32 operations, as the kernels use
  * them: out[i] = op(a[i], b[i]) for op 0 add, 1 sub, 2 mul, 3 div, 4 sqrt (a),

@@ -70,6 +70,26 @@ def test_bwd_rejects_bad_arguments_without_launching():
     assert L.qat_linear_bwd(p, p, p, None, 4, 4, 4, 0.05, 0, p, p, 0, p, 8, None) == brl.BRL_EWORKSPACE
 
 
+def test_state_hash_rejects_bad_arguments_without_launching():
+    L = brl.lib()
+    p = C.c_void_p(0x10000)
+
+    def call(ptrs, lens, count, digest=p, ws=p, ws_bytes=1 << 20):
+        P = (C.c_void_p * max(1, len(ptrs)))(*ptrs)
+        N = (C.c_int64 * max(1, len(lens)))(*lens)
+        return L.brl_state_hash(C.cast(P, C.c_void_p), C.cast(N, C.c_void_p), count, digest, ws, ws_bytes, None)
+
+    assert call([], [], 0) == brl.BRL_EINVAL
+    assert call([0x10000], [-1], 1) == brl.BRL_ESHAPE
+    assert call([None], [16], 1) == brl.BRL_EINVAL                 # null data with bytes
+    assert call([0x10002], [16], 1) == brl.BRL_EINVAL              # not 4-byte aligned
+    assert call([0x10000], [16], 1, digest=None) == brl.BRL_EINVAL
+    assert call([0x10000], [1 << 30], 1, ws_bytes=64) == brl.BRL_EWORKSPACE
+    need = brl.workspace_bytes(brl.OP_HASH, (1 << 30) + 5, 2, 0)
+    assert need >= 32 * ((1 << 30) // 16384 + 1)
+    assert brl.workspace_bytes(brl.OP_HASH, 10, 0, 0) == 0
+
+
 def test_reduce_state_order_is_enforced_on_the_host():
     L = brl.lib()
     st = brl.ReduceStateC()
