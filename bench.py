@@ -41,6 +41,17 @@ PEAK_VALU_F32_TOPS = 256 * 128 * 2.4e9 / 1e12         # 78.64 T ops/s
 # fused into it would read nothing more); clip reads and writes T (8 B).
 REPLAY_BYTES_PER_ELEM = 6 * (8 + 7 * 12) + 28 + 8      # 588
 
+# State hash (the next row after the hot path, measured beside it, not part of
+# `value`): the compiled SHA-256 block loop of the leaf kernel issues
+# HASH_VALU_PER_BLOCK VALU instructions per 64-byte block, HASH_ALIGNBIT_PER_BLOCK
+# of them v_alignbit_b32 (the rotations), which gfx950 issues at half the rate
+# of the other integer ops (measured: 34 vs 57-60 T lane-ops/s).  A CPU test
+# recounts both in the generated assembly.  VALU bound: 78.64e12 issue slots/s
+# over (2 x alignbit + the rest) slots per block, times 64 bytes.
+HASH_VALU_PER_BLOCK = 1561
+HASH_ALIGNBIT_PER_BLOCK = 576
+HASH_STATE_TENSORS = 8                                   # 8 x 805 MB = 6.44 GB
+
 
 def measured_traffic(kernel: str):
     """HBM bytes per dispatch of `kernel` from the committed rocprofv3 counter
@@ -197,6 +208,10 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
+    # state hash of a 6.44 GB state (the first 8 replay partials as its tensors)
+    hstate = partials[:HASH_STATE_TENSORS]
+    hash_bytes = sum(t.numel() * 4 for t in hstate)
+    hash_ms = avg_call(lambda: brl.state_hash(hstate), reps=3)
     pre_ms = avg_call(lambda: brl.qat_linear_bwd(dY, X, W, synth.S_X, need_dX=False, need_dW=False, ws=ws_b))
     dx_ms = avg_call(lambda: brl.qat_linear_bwd(dY, X, W, synth.S_X, dX=dX, need_dW=False, ws=ws_b)) - pre_ms
     dw_ms = avg_call(lambda: brl.qat_linear_bwd(dY, X, W, synth.S_X, dW=dW, need_dX=False, ws=ws_b)) - pre_ms
@@ -258,9 +273,29 @@ def main():
                    "frac": round(ops / (dw_ms * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4)},
         },
     }
+    hash_gbps = hash_bytes / (hash_ms * 1e-3) / 1e9
+    hash_slots = HASH_VALU_PER_BLOCK + HASH_ALIGNBIT_PER_BLOCK
+    hash_peak = PEAK_VALU_F32_TOPS * 1e12 / hash_slots * 64 / 1e9
+    result["state_hash"] = {
+        "bytes": hash_bytes, "ms": round(hash_ms, 4), "GBps": round(hash_gbps, 1),
+        "roofline": {"bound": "alu", "achieved": round(hash_gbps, 1), "peak": round(hash_peak, 1),
+                     "unit": "GB/s", "frac": round(hash_gbps / hash_peak, 4),
+                     "note": (f"{HASH_VALU_PER_BLOCK} VALU instructions per 64-byte SHA-256 block, "
+                              f"{HASH_ALIGNBIT_PER_BLOCK} of them half-rate rotations")},
+    }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        result["cpu_baseline"]["state_hash_GBps"] = cpu_hash_rate([p.cpu().numpy() for p in hstate[:1]])
     print(json.dumps(result), flush=True)
+
+
+def cpu_hash_rate(tensors) -> float:
+    """The state-hash oracle (hashlib, one thread, as it stands) on one 805 MB tensor."""
+    from oracle import state_hash as sh
+    t0 = time.perf_counter()
+    sh.state_hash(tensors)
+    dt = time.perf_counter() - t0
+    return round(sum(t.nbytes for t in tensors) / dt / 1e9, 3)
 
 
 def cpu_baseline(inp, budget_s: float):

@@ -7,10 +7,14 @@
 // name the function.  This library's reading, chosen so that every lane of
 // the GPU can hash its own piece:
 //
-//   leaves  each tensor's bytes cut into 16 KiB pieces (last one shorter, an
+//   leaves  each tensor's bytes cut into 4 KiB pieces (last one shorter, an
 //           empty tensor one empty piece): SHA-256(piece || 0x00)
-//   nodes   consecutive groups of 512 digests (16 KiB): SHA-256(group || 0x01),
+//   nodes   consecutive groups of 16 digests (512 bytes): SHA-256(group || 0x01),
 //           level after level until one digest remains
+//
+// Small leaves spread a state over many lanes (a lane's hash is one long
+// dependency chain, so lanes, not bytes per lane, give the throughput), and
+// a small fan-in keeps the upper levels, which have few lanes, short.
 //   root    SHA-256(top || le64(count) || le64(length of each tensor) || 0x02)
 //
 // One lane hashes one leaf or one node; the root is one lane.  SHA-256's
@@ -71,20 +75,33 @@ __device__ void sha_piece(const uint8_t* __restrict__ src, int64_t n, uint8_t ta
     for (int i = 0; i < 8; ++i) h[i] = c.h0[i];
     uint32_t w[16];
     const int64_t full = n >> 6;
-    for (int64_t blk = 0; blk < full; ++blk) {
-        const uint8_t* p = src + (blk << 6);
-        if constexpr (VEC) {
+    if constexpr (VEC) {
+        // the next block's 64 bytes load while this one is compressed
+        uint4 nxt[4];
+        if (full > 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) nxt[q] = reinterpret_cast<const uint4*>(src)[q];
+        }
+        for (int64_t blk = 0; blk < full; ++blk) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint4 v = reinterpret_cast<const uint4*>(p)[q];
-                w[4 * q + 0] = bswap(v.x); w[4 * q + 1] = bswap(v.y);
-                w[4 * q + 2] = bswap(v.z); w[4 * q + 3] = bswap(v.w);
+                w[4 * q + 0] = bswap(nxt[q].x); w[4 * q + 1] = bswap(nxt[q].y);
+                w[4 * q + 2] = bswap(nxt[q].z); w[4 * q + 3] = bswap(nxt[q].w);
             }
-        } else {
+            if (blk + 1 < full) {
+                const uint4* p = reinterpret_cast<const uint4*>(src + ((blk + 1) << 6));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) nxt[q] = p[q];
+            }
+            sha_block(h, w, c);
+        }
+    } else {
+        for (int64_t blk = 0; blk < full; ++blk) {
+            const uint8_t* p = src + (blk << 6);
 #pragma unroll
             for (int q = 0; q < 16; ++q) w[q] = bswap(reinterpret_cast<const uint32_t*>(p)[q]);
+            sha_block(h, w, c);
         }
-        sha_block(h, w, c);
     }
     // tail: rem message bytes, the tag, 0x80, zeros, 64-bit big-endian bit length
     const int rem = (int)(n & 63);
@@ -115,22 +132,30 @@ __device__ void sha_piece(const uint8_t* __restrict__ src, int64_t n, uint8_t ta
 }
 
 // ---- leaves -------------------------------------------------------------------------
-template <bool VEC>
-__global__ __launch_bounds__(256) void hash_leaf_kernel(HashBatch hb, ShaConsts c, uint8_t* __restrict__ digests,
-                                                        int64_t* __restrict__ lens_out) {
-    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;    // leaf index within the batch
-    if (blockIdx.x == 0 && threadIdx.x < hb.n) lens_out[hb.first_tensor + threadIdx.x] = hb.len[threadIdx.x];
-    if (g >= hb.leaves) return;
+struct LeafRef {
+    const uint8_t* src;
+    int64_t n;
+};
+
+__device__ __forceinline__ LeafRef leaf_ref(const HashBatch& hb, int64_t g) {
     // the tensor holding leaf g: last t with first_leaf[t] <= g
     int t = 0;
     for (int s = 32; s > 0; s >>= 1)
         if (t + s < hb.n && hb.first_leaf[t + s] <= g) t += s;
-    const int64_t piece = g - hb.first_leaf[t];
-    const int64_t off = piece * kHashLeafBytes;
+    const int64_t off = (g - hb.first_leaf[t]) * kHashLeafBytes;
     const int64_t left = hb.len[t] - off;
-    const int64_t n = left < kHashLeafBytes ? left : kHashLeafBytes;
-    sha_piece<VEC>(static_cast<const uint8_t*>(hb.ptr[t]) + off, n, 0x00, c,
-                   digests + (hb.leaf_base + g) * 32);
+    return {static_cast<const uint8_t*>(hb.ptr[t]) + off, left < kHashLeafBytes ? left : kHashLeafBytes};
+}
+
+// Lane -> leaf g of the batch.
+template <bool VEC>
+__global__ __launch_bounds__(256) void hash_leaf_kernel(HashBatch hb, ShaConsts c, uint8_t* __restrict__ digests,
+                                                        int64_t* __restrict__ lens_out) {
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (blockIdx.x == 0 && threadIdx.x < hb.n) lens_out[hb.first_tensor + threadIdx.x] = hb.len[threadIdx.x];
+    if (g >= hb.leaves) return;
+    const LeafRef l = leaf_ref(hb, g);
+    sha_piece<VEC>(l.src, l.n, 0x00, c, digests + (hb.leaf_base + g) * 32);
 }
 
 // ---- one level of nodes: groups of kHashFanIn digests -------------------------------

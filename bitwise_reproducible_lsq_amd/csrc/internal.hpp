@@ -111,8 +111,8 @@ hipError_t launch_swiglu_bwd(const float* dA, const float* ypre, int64_t M, int6
                              const ExpConsts& ek, hipStream_t st);
 
 // ---- state hash (SHA-256 tree) -------------------------------------------------
-constexpr int64_t kHashLeafBytes = 16384;   // bytes of a tensor per leaf
-constexpr int64_t kHashFanIn = 512;         // digests per node
+constexpr int64_t kHashLeafBytes = 4096;    // bytes of a tensor per leaf
+constexpr int64_t kHashFanIn = 16;          // digests per node
 constexpr int kHashBatch = 64;              // tensors per leaf launch
 struct HashBatch {
     const void* ptr[kHashBatch];

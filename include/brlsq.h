@@ -181,10 +181,10 @@ BRL_API brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float
  * (about 6 s per step) onto the device as future work (onedev.kr summary,
  * sections "Use" and "Limits"; rit.work article body).  They do not name the
  * function; this library computes SHA-256 (FIPS 180-4) arranged as a tree:
- *   leaf  = SHA-256(16 KiB piece of one tensor's bytes || 0x00), pieces in
+ *   leaf  = SHA-256(4 KiB piece of one tensor's bytes || 0x00), pieces in
  *           order, the last piece of a tensor shorter, an empty tensor one
  *           empty piece; the leaves of all tensors, tensor after tensor;
- *   node  = SHA-256(512 consecutive digests (fewer for the last) || 0x01),
+ *   node  = SHA-256(16 consecutive digests (fewer for the last) || 0x01),
  *           level after level until one digest remains;
  *   root  = SHA-256(top || le64(count) || le64(nbytes[0]) ... || 0x02).
  * tensors: count (>= 1) device pointers, 4-byte aligned, read as raw bytes

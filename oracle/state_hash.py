@@ -12,10 +12,10 @@ stream paragraph).  Reading taken here: SHA-256 (FIPS 180-4, Python's
 
 * the state is an ordered list of tensors, each taken as its raw bytes
   (little-endian, row-major);
-* each tensor is cut into consecutive 16 KiB leaves (the last may be shorter;
+* each tensor is cut into consecutive 4 KiB leaves (the last may be shorter;
   an empty tensor has one empty leaf); leaf digest = SHA-256(bytes || 0x00);
 * the leaf digests of all tensors, tensor after tensor, form level 0; each
-  higher level hashes consecutive groups of 512 digests (16 KiB) as
+  higher level hashes consecutive groups of 16 digests (512 bytes) as
   SHA-256(digests || 0x01) until one digest remains;
 * state hash = SHA-256(top || le64(tensor count) || le64(byte length of each
   tensor, in order) || 0x02).
@@ -29,8 +29,8 @@ import hashlib
 import struct
 from typing import Iterable, List
 
-LEAF_BYTES = 16384
-FAN_IN = 512
+LEAF_BYTES = 4096
+FAN_IN = 16
 
 
 def _sha(data: bytes) -> bytes:
@@ -44,7 +44,7 @@ def _leaf(chunk) -> bytes:
 
 
 def leaf_digests(tensor: memoryview) -> List[bytes]:
-    """SHA-256(chunk || 0x00) of each 16 KiB chunk of one tensor's bytes."""
+    """SHA-256(chunk || 0x00) of each 4 KiB chunk of one tensor's bytes."""
     if len(tensor) == 0:
         return [_leaf(b"")]
     return [_leaf(tensor[o:o + LEAF_BYTES]) for o in range(0, len(tensor), LEAF_BYTES)]

@@ -174,3 +174,27 @@ def test_matrix_core_backward_keeps_products_in_vgprs():
         assert len(re.findall(r"\tv_add_f32", body)) >= 512, name
         assert "v_accvgpr_read" not in body, name
         assert not re.search(r"\tv_mfma\S* a\[", body), name
+
+
+def test_state_hash_block_instruction_count_matches_bench():
+    """bench.py prices the state hash against the VALU bound of the compiled
+    SHA-256 block loop; recount that loop's VALU instructions here (every
+    basic block of the leaf kernel's first innermost loop)."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    text = open([f for f in brl_build.asm_files() if "hash" in f][0]).read()
+    body = text.split("_ZN3brl16hash_leaf_kernelILb1EEEvNS_9HashBatchENS_9ShaConstsEPhPl:")[1].split("s_endpgm")[0]
+    lines = body.splitlines()
+    hdr = next(m.group(1) for m in (re.match(r"\.L(BB\d+_\d+):\s*;\s*=>This Inner Loop Header", l) for l in lines) if m)
+    n_valu, n_align, inside = 0, 0, False
+    for l in lines:
+        m = re.match(r"\.L(BB\d+_\d+):(.*)", l)
+        if m:
+            inside = m.group(1) == hdr or f"Header={hdr} " in m.group(2) + " "
+            continue
+        if inside and re.match(r"\s+v_", l):
+            n_valu += 1
+            n_align += "v_alignbit_b32" in l
+    assert n_valu == bench.HASH_VALU_PER_BLOCK, n_valu
+    assert n_align == bench.HASH_ALIGNBIT_PER_BLOCK, n_align
