@@ -34,12 +34,13 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_I8_TOPS = 5030.0
 PEAK_VALU_F32_TOPS = 256 * 128 * 2.4e9 / 1e12         # 78.64 T ops/s
 
-# Replay bytes per element index that the method must move with one partial
-# resident at a time: per replica, shard 0 copies (read G, write A: 8 B) and
-# shards 1..7 add (read A, read G, write A: 12 B each) -> 6 * (8 + 84) = 552;
-# TreeFold reads 6 accumulators and writes T (28 B, the squared-norm pass
-# fused into it would read nothing more); clip reads and writes T (8 B).
-REPLAY_BYTES_PER_ELEM = 6 * (8 + 7 * 12) + 28 + 8      # 588
+# Replay bytes per element index that the method must move, with at most two
+# partials resident: per replica the first two shards combine in one pass and
+# every later shard is one add (read A, read G, write A: 12 B each) -> 6 * 7 *
+# 12 = 504; TreeFold reads 6 accumulators and writes T (28 B; the squared-norm
+# CanonSum could ride on that pass, so it adds nothing); clip reads and writes
+# T (8 B).
+REPLAY_BYTES_PER_ELEM = 6 * 7 * 12 + 28 + 8           # 540
 
 # State hash (the next row after the hot path, measured beside it, not part of
 # `value`): the compiled SHA-256 block loop of the leaf kernel issues
@@ -144,7 +145,8 @@ def main():
     W = torch.from_numpy(inp.W).to(dev)
     dY = torch.from_numpy(inp.dY).to(dev)
     partials = [synth.replay_partial(rcase, v, device=dev, length=L) for v in range(R * S)]
-    state = brl.ReduceState(R, S, L, device=dev)
+    # all partials stay resident, so each replica's first two shards combine in one pass
+    state = brl.ReduceState(R, S, L, device=dev, partials_persist=True)
     out = torch.empty(L, dtype=torch.float32, device=dev)
     ws_f = brl.workspace(brl.OP_FWD, M, K, N, dev)
     ws_b = brl.workspace(brl.OP_BWD, M, K, N, dev)

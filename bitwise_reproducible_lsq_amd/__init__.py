@@ -38,8 +38,11 @@ class BrlError(RuntimeError):
 
 class ReduceStateC(C.Structure):
     _fields_ = [("replicas", C.c_int32), ("shards", C.c_int32), ("len", C.c_int64),
-                ("next", C.c_int32), ("reserved", C.c_int32),
+                ("next", C.c_int32), ("flags", C.c_uint32), ("pending", C.c_void_p),
                 ("acc", C.c_void_p * MAX_REPLICAS)]
+
+
+REDUCE_PARTIALS_PERSIST = 1
 
 
 _lib = None
@@ -181,7 +184,7 @@ class ReduceState:
     (device tensors owned here) and the next virtual rank in mesh order."""
 
     def __init__(self, replicas: int, shards: int, length: int, device="cuda",
-                 acc: Optional[Sequence[torch.Tensor]] = None):
+                 acc: Optional[Sequence[torch.Tensor]] = None, partials_persist: bool = False):
         if acc is None:
             acc = [torch.empty(length, dtype=torch.float32, device=device) for _ in range(replicas)]
         self.acc = list(acc)
@@ -189,6 +192,9 @@ class ReduceState:
         ptrs = (C.c_void_p * replicas)(*[a.data_ptr() for a in self.acc])
         _check(lib().brl_reduce_init(C.byref(self.c), replicas, shards, length,
                                      C.cast(ptrs, C.c_void_p)))
+        # persist: the caller keeps each replica's shard-0 partial valid and
+        # unchanged until its shard-1 call has run (see the C header)
+        self.c.flags = REDUCE_PARTIALS_PERSIST if partials_persist else 0
 
     @property
     def next(self) -> int:
@@ -200,6 +206,7 @@ class ReduceState:
 
     def reset(self):
         self.c.next = 0
+        self.c.pending = None
 
 
 def ordered_reduce(state: ReduceState, partial: torch.Tensor, out: Optional[torch.Tensor] = None,

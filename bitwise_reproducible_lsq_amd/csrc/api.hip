@@ -349,18 +349,31 @@ brl_status ordered_reduce(brl_reduce_state* sp, const float* partial, float* out
     if (!aligned4(partial) || !aligned4(out)) return fail(BRL_EINVAL, "ordered_reduce: misaligned pointer");
     hipStream_t st = static_cast<hipStream_t>(stream);
     brl_status rc = BRL_OK;
+    const bool defer = (sp->flags & BRL_REDUCE_PARTIALS_PERSIST) && S > 1;
+    if (s == 0) sp->pending = nullptr;
     if (n > 0) {
-        if (!last) {
-            rc = check_hip(launch_accumulate(sp->acc[r], partial, n, s == 0, st),
+        if (s == 0 && defer) {
+            // A_r = G_{r,0} is formed together with the next shard's add
+            sp->pending = partial;
+        } else if (!last) {
+            const bool joint = s == 1 && sp->pending;
+            rc = check_hip(launch_accumulate(sp->acc[r], joint ? sp->pending : sp->acc[r], partial, n, s == 0, st),
                            s == 0 ? "running sum (first shard)" : "running sum");
         } else {
             FoldPtrs p{};
             for (int i = 0; i < R; ++i) p.a[i] = sp->acc[i];
             const float* g_last = partial;
-            if (s == 0) { p.a[R - 1] = partial; g_last = nullptr; }
-            rc = check_hip(launch_fold(p, R, g_last, out, n, st), "TreeFold");
+            if (s == 0) {
+                p.a[R - 1] = partial;
+                g_last = nullptr;
+            } else if (s == 1 && sp->pending) {
+                rc = check_hip(launch_accumulate(sp->acc[r], sp->pending, partial, n, 0, st), "running sum");
+                g_last = nullptr;
+            }
+            if (rc == BRL_OK) rc = check_hip(launch_fold(p, R, g_last, out, n, st), "TreeFold");
         }
     }
+    if (s >= 1) sp->pending = nullptr;
     if (rc == BRL_OK) sp->next = (int32_t)(v + 1);
     return rc;
 }

@@ -130,8 +130,8 @@ hipError_t launch_hash_root(const uint8_t* top, const int64_t* lens, int64_t cou
 void sha256_constants(uint32_t* k64, uint32_t* h8);
 
 // ---- replay -------------------------------------------------------------------
-// first = 1: A <- G; otherwise A <- A + G.
-hipError_t launch_accumulate(float* A, const float* G, int64_t n, int first, hipStream_t st);
+// first = 1: A <- G; otherwise A <- X + G (X = A, or a deferred first shard).
+hipError_t launch_accumulate(float* A, const float* X, const float* G, int64_t n, int first, hipStream_t st);
 struct FoldPtrs { const float* a[64]; };
 hipError_t launch_fold(const FoldPtrs& p, int R, const float* g_last, float* out, int64_t n,
                        hipStream_t st);

@@ -30,16 +30,16 @@ __device__ __forceinline__ int64_t vec_index(int u) {
     return ((int64_t)blockIdx.x * V + u) * kStreamThreads + threadIdx.x;
 }
 
-// A <- A + G
+// A <- X + G (X is A itself, or the deferred first shard of the replica)
 template <int V>
-__global__ __launch_bounds__(kStreamThreads) void accumulate_v4_kernel(vf4* __restrict__ A,
+__global__ __launch_bounds__(kStreamThreads) void accumulate_v4_kernel(vf4* A, const vf4* X,
                                                                        const vf4* __restrict__ G,
                                                                        int64_t n4) {
     vf4 a[V], g[V];
 #pragma unroll
     for (int u = 0; u < V; ++u) {
         const int64_t i = vec_index<V>(u);
-        if (i < n4) { a[u] = __builtin_nontemporal_load(A + i); g[u] = __builtin_nontemporal_load(G + i); }
+        if (i < n4) { a[u] = __builtin_nontemporal_load(X + i); g[u] = __builtin_nontemporal_load(G + i); }
     }
 #pragma unroll
     for (int u = 0; u < V; ++u) {
@@ -72,21 +72,22 @@ __global__ __launch_bounds__(kStreamThreads) void copy_v4_kernel(vf4* __restrict
     }
 }
 
-__global__ __launch_bounds__(kStreamThreads) void accumulate_scalar_kernel(float* __restrict__ A,
+__global__ __launch_bounds__(kStreamThreads) void accumulate_scalar_kernel(float* A, const float* X,
                                                                            const float* __restrict__ G,
                                                                            int64_t n, int first) {
     const int64_t i = (int64_t)blockIdx.x * kStreamThreads + threadIdx.x;
-    if (i < n) A[i] = first ? G[i] : f_add(A[i], G[i]);
+    if (i < n) A[i] = first ? G[i] : f_add(X[i], G[i]);
 }
 
-hipError_t launch_accumulate(float* A, const float* G, int64_t n, int first, hipStream_t st) {
+hipError_t launch_accumulate(float* A, const float* X, const float* G, int64_t n, int first, hipStream_t st) {
     if (n <= 0) return hipSuccess;
     int64_t done = 0;
-    if (aligned16(A) && aligned16(G)) {
+    if (aligned16(A) && aligned16(X) && aligned16(G)) {
         const int64_t n4 = n / 4;
         const int V = stream_vec();
         if (n4 > 0) {
             vf4* a4 = reinterpret_cast<vf4*>(A);
+            const vf4* x4 = reinterpret_cast<const vf4*>(X);
             const vf4* g4 = reinterpret_cast<const vf4*>(G);
             const dim3 grid(stream_grid(n4, V)), blk(kStreamThreads);
             if (first) {
@@ -94,16 +95,16 @@ hipError_t launch_accumulate(float* A, const float* G, int64_t n, int first, hip
                 else if (V == 2) hipLaunchKernelGGL(copy_v4_kernel<2>, grid, blk, 0, st, a4, g4, n4);
                 else hipLaunchKernelGGL(copy_v4_kernel<1>, grid, blk, 0, st, a4, g4, n4);
             } else {
-                if (V == 4) hipLaunchKernelGGL(accumulate_v4_kernel<4>, grid, blk, 0, st, a4, g4, n4);
-                else if (V == 2) hipLaunchKernelGGL(accumulate_v4_kernel<2>, grid, blk, 0, st, a4, g4, n4);
-                else hipLaunchKernelGGL(accumulate_v4_kernel<1>, grid, blk, 0, st, a4, g4, n4);
+                if (V == 4) hipLaunchKernelGGL(accumulate_v4_kernel<4>, grid, blk, 0, st, a4, x4, g4, n4);
+                else if (V == 2) hipLaunchKernelGGL(accumulate_v4_kernel<2>, grid, blk, 0, st, a4, x4, g4, n4);
+                else hipLaunchKernelGGL(accumulate_v4_kernel<1>, grid, blk, 0, st, a4, x4, g4, n4);
             }
         }
         done = n4 * 4;
     }
     if (done < n)
         hipLaunchKernelGGL(accumulate_scalar_kernel, dim3((unsigned)ceil_div(n - done, kStreamThreads)),
-                           dim3(kStreamThreads), 0, st, A + done, G + done, n - done, first);
+                           dim3(kStreamThreads), 0, st, A + done, X + done, G + done, n - done, first);
     return hipGetLastError();
 }
 

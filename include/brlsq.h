@@ -131,13 +131,17 @@ BRL_API brl_status qat_linear_bwd(const float* dOut, const float* X, const float
 
 /* Caller-owned host struct describing one replay.  acc[r] are device
  * buffers of len floats (A_r), owned by the caller; next is the virtual rank
- * v = r*shards + s that ordered_reduce expects next. */
+ * v = r*shards + s that ordered_reduce expects next.  flags: 0 or
+ * BRL_REDUCE_PARTIALS_PERSIST, set by the caller after brl_reduce_init;
+ * pending is the library's own bookkeeping. */
+#define BRL_REDUCE_PARTIALS_PERSIST 1u
 typedef struct brl_reduce_state {
     int32_t replicas;
     int32_t shards;
     int64_t len;
     int32_t next;
-    int32_t reserved;
+    uint32_t flags;
+    const float* pending;
     float* acc[BRL_MAX_REPLICAS];
 } brl_reduce_state;
 
@@ -159,7 +163,12 @@ BRL_API brl_status brl_reduce_init(brl_reduce_state* st, int32_t replicas, int32
  * last rank and must be non-NULL for it; the last A_r is not written back.
  * Advances st->next; a call with st->next >= replicas*shards returns
  * BRL_EORDER and launches nothing.  partial is only read during the call's
- * stream-ordered work and may be reused after it.
+ * stream-ordered work and may be reused after it -- except with
+ * BRL_REDUCE_PARTIALS_PERSIST in st->flags (and shards > 1): then the
+ * shard-0 partial of each replica must stay valid and unchanged until the
+ * shard-1 call of that replica has run on the stream; the shard-0 call
+ * launches nothing and the shard-1 call forms A_r = G_{r,0} + G_{r,1} in one
+ * pass (same bits, one copy pass fewer per replica).
  */
 BRL_API brl_status ordered_reduce(brl_reduce_state* st, const float* partial, float* out, void* stream);
 

@@ -331,21 +331,26 @@ def test_repeat_runs_identical():
 
 
 # ---- replay -----------------------------------------------------------------------------
-def _replay_gpu(partials_np, R, S, max_norm=1.0):
+def _replay_gpu(partials_np, R, S, max_norm=1.0, persist=False):
     L = partials_np[0].size
-    st = brl.ReduceState(R, S, L, device=DEV)
+    st = brl.ReduceState(R, S, L, device=DEV, partials_persist=persist)
     out = None
+    keep = []      # with persist the shard-0 partials must outlive the shard-1 call
     for v in range(R * S):
-        out = brl.ordered_reduce(st, _cuda(partials_np[v]))
+        g = _cuda(partials_np[v])
+        keep.append(g)
+        out = brl.ordered_reduce(st, g)
     nu = brl.grad_l2norm_clip(out, max_norm)
+    torch.cuda.synchronize()
     return out, nu, st
 
 
+@pytest.mark.parametrize("persist", [False, True])
 @pytest.mark.parametrize("R,S,L", [(6, 8, 65536 + 5), (1, 1, 1000), (2, 3, 4097), (3, 2, 333),
                                    (5, 1, 1024), (7, 2, 100), (16, 2, 2048), (6, 8, 3)])
-def test_replay_parity(R, S, L):
+def test_replay_parity(R, S, L, persist):
     parts = [synth.replay_partial_host(4, v, L, std=1e-2) for v in range(R * S)]
-    out, nu, st = _replay_gpu(parts, R, S)
+    out, nu, st = _replay_gpu(parts, R, S, persist=persist)
     T, wnu, A = oracle.replay(parts, R, S)
     assert_bitwise(nu, np.array([wnu]), "nu")
     assert_bitwise(out, T, "clipped TreeFold")
