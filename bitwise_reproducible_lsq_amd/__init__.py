@@ -57,6 +57,8 @@ _SIGS = {
     "grad_l2norm_clip": (i32, [P, i64, f32, f32, P, P, sz, P]),
     "brl_probe_f32": (i32, [i32, P, P, P, i64, P]),
     "brl_state_hash": (i32, [P, P, i32, P, P, sz, P]),
+    "brl_adamw_scalars_for_step": (i32, [i64, C.c_double, P, P]),
+    "adamw_step": (i32, [P, P, P, P, i64, P, i32, P]),
     "brl_set_tuning": (i64, [i32, i64]),
     "brl_status_string": (C.c_char_p, [i32]),
     "brl_last_error": (C.c_char_p, []),
@@ -253,6 +255,37 @@ def state_hash(tensors: Sequence[torch.Tensor], ws: Optional[torch.Tensor] = Non
     _check(lib().brl_state_hash(C.cast(ptrs, C.c_void_p), C.cast(nbytes, C.c_void_p), n, _ptr(out), _ptr(ws),
                                 ws.numel(), _stream(stream)))
     return out
+
+
+class AdamWConfig(C.Structure):
+    _fields_ = [(n, C.c_double) for n in ("beta1", "beta2", "eps", "wd", "peak_lr", "min_lr",
+                                          "warmup_tokens", "total_tokens")]
+
+
+class AdamWScalars(C.Structure):
+    _fields_ = [(n, C.c_float) for n in ("beta1", "beta2", "c1", "c2", "bc1", "bc2", "eps", "lr", "d")]
+
+    def as_dict(self) -> dict:
+        return {n: float(getattr(self, n)) for n, _ in self._fields_}
+
+
+def adamw_scalars_for_step(step: int, tokens: float, cfg: Optional[AdamWConfig] = None) -> AdamWScalars:
+    """The step's binary32 scalars (brl_adamw_scalars_for_step); cfg None = the recipe."""
+    out = AdamWScalars()
+    _check(lib().brl_adamw_scalars_for_step(step, float(tokens), C.byref(cfg) if cfg is not None else None,
+                                            C.byref(out)))
+    return out
+
+
+def adamw_step(p: torch.Tensor, g: torch.Tensor, m: torch.Tensor, v: torch.Tensor, sc: AdamWScalars,
+               decay: bool = True, stream=None) -> None:
+    """In-place AdamW update of p, m, v from g (adamw_step)."""
+    for t, name in ((p, "p"), (g, "g"), (m, "m"), (v, "v")):
+        _f32(t, name)
+        if t.numel() != p.numel():
+            raise ValueError("p, g, m, v must have the same size")
+    _check(lib().adamw_step(_ptr(p), _ptr(g), _ptr(m), _ptr(v), p.numel(), C.byref(sc), 1 if decay else 0,
+                            _stream(stream)))
 
 
 def probe_f32(op: str, a: torch.Tensor, b: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

@@ -459,6 +459,31 @@ brl_status brl_state_hash(const void* const* tensors, const int64_t* nbytes, int
     return check_hip(launch_hash_root(L.level_ptr[L.nlev - 1], L.lens, count, digest, st), "hash root");
 }
 
+brl_status brl_adamw_scalars_for_step(int64_t step, double tokens, const brl_adamw_config* cfg,
+                                      brl_adamw_scalars* out) {
+    static const brl_adamw_config recipe = {0.9, 0.95, 1e-8, 0.1, 4.5e-4, 4.5e-5, 2.1e9, 400e9};
+    const brl_adamw_config& c = cfg ? *cfg : recipe;
+    if (!out) return fail(BRL_EINVAL, "brl_adamw_scalars_for_step: null output");
+    if (step < 1) return fail(BRL_EINVAL, "brl_adamw_scalars_for_step: step must be >= 1");
+    if (!(tokens >= 0.0) || !isfinite(tokens)) return fail(BRL_EINVAL, "brl_adamw_scalars_for_step: bad token count");
+    if (!(c.beta1 >= 0.0 && c.beta1 < 1.0) || !(c.beta2 >= 0.0 && c.beta2 < 1.0) || !(c.eps > 0.0) ||
+        !(c.wd >= 0.0) || !(c.peak_lr >= 0.0) || !(c.min_lr >= 0.0) || !(c.warmup_tokens > 0.0) ||
+        !(c.total_tokens > c.warmup_tokens))
+        return fail(BRL_EINVAL, "brl_adamw_scalars_for_step: bad configuration");
+    adamw_scalars(step, tokens, c, out);
+    return BRL_OK;
+}
+
+brl_status adamw_step(float* p, const float* g, float* m, float* v, int64_t n, const brl_adamw_scalars* sc,
+                      int32_t decay, void* stream) {
+    if (n < 0) return fail(BRL_ESHAPE, "adamw_step: n < 0");
+    if (!sc) return fail(BRL_EINVAL, "adamw_step: null scalars");
+    if (n > 0 && (!p || !g || !m || !v)) return fail(BRL_EINVAL, "adamw_step: null tensor");
+    if (!aligned4(p) || !aligned4(g) || !aligned4(m) || !aligned4(v))
+        return fail(BRL_EINVAL, "adamw_step: pointers must be 4-byte aligned");
+    return check_hip(launch_adamw(p, g, m, v, n, *sc, decay != 0, static_cast<hipStream_t>(stream)), "AdamW");
+}
+
 int64_t brl_set_tuning(int32_t knob, int64_t value) {
     if (knob < 0 || knob > 3) return -1;
     if (knob == BRL_TUNE_BWD_CHUNK_LOG2 && value > 6) value = 6;

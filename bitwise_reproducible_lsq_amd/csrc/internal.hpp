@@ -129,6 +129,11 @@ hipError_t launch_hash_nodes(const uint8_t* in, int64_t n_in, uint8_t* out, hipS
 hipError_t launch_hash_root(const uint8_t* top, const int64_t* lens, int64_t count, uint8_t* out, hipStream_t st);
 void sha256_constants(uint32_t* k64, uint32_t* h8);
 
+// ---- AdamW --------------------------------------------------------------------
+hipError_t launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, const brl_adamw_scalars& s,
+                        int decay, hipStream_t st);
+void adamw_scalars(int64_t step, double tokens, const brl_adamw_config& c, brl_adamw_scalars* out);
+
 // ---- replay -------------------------------------------------------------------
 // first = 1: A <- G; otherwise A <- X + G (X = A, or a deferred first shard).
 hipError_t launch_accumulate(float* A, const float* X, const float* G, int64_t n, int first, hipStream_t st);

@@ -205,6 +205,37 @@ BRL_API brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float
 BRL_API brl_status brl_state_hash(const void* const* tensors, const int64_t* nbytes, int32_t count,
                                   uint8_t* digest, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * AdamW update in a fixed operation order (the step after the clip).  The
+ * recipe (onedev.kr summary, "Limits", recipe paragraph): AdamW with beta1
+ * 0.9, beta2 0.95, eps 1e-8, decoupled weight decay 0.1 except on the input
+ * embedding, the norm weights and the RoPE table; learning rate linear to
+ * 4.5e-4 over about 2.1B tokens, then one cosine decay to 10% of the peak at
+ * 400B tokens, keyed to consumed tokens.  The pages fix neither the operation
+ * order nor the scalars' arithmetic; this library's reading:
+ *   brl_adamw_scalars_for_step: lr(tokens) as above, c1 = 1 - beta1,
+ *   c2 = 1 - beta2, bc1 = 1 - beta1^step, bc2 = 1 - beta2^step, d = lr * wd,
+ *   each computed in binary64 and rounded once to binary32 (step >= 1);
+ *   adamw_step, per element, binary32 operations in this order:
+ *     m = (beta1 * m) + (c1 * g)
+ *     v = (beta2 * v) + (c2 * (g * g))
+ *     u = (m / bc1) / (sqrt(v / bc2) + eps)
+ *     p = p - (d * p)           only when decay != 0
+ *     p = p - (lr * u)
+ * p, m, v (updated in place) and g: device arrays of n floats; sc: host
+ * struct (copied into the launch).  cfg NULL selects the recipe.
+ */
+typedef struct brl_adamw_config {
+    double beta1, beta2, eps, wd, peak_lr, min_lr, warmup_tokens, total_tokens;
+} brl_adamw_config;
+typedef struct brl_adamw_scalars {
+    float beta1, beta2, c1, c2, bc1, bc2, eps, lr, d;
+} brl_adamw_scalars;
+BRL_API brl_status brl_adamw_scalars_for_step(int64_t step, double tokens, const brl_adamw_config* cfg,
+                                              brl_adamw_scalars* out);
+BRL_API brl_status adamw_step(float* p, const float* g, float* m, float* v, int64_t n,
+                              const brl_adamw_scalars* sc, int32_t decay, void* stream);
+
 /* Conformance probe of the device's binary32 operations, as the kernels use
  * them: out[i] = op(a[i], b[i]) for op 0 add, 1 sub, 2 mul, 3 div, 4 sqrt (a),
  * 5 int32 bits of a -> float, 6 round-to-nearest-even integral (a),

@@ -52,6 +52,7 @@ def lib():
         "or_exp": (f32, [f32]), "or_exp_constants": (None, [P]),
         "or_pair_tree": (f32, [P, i64]), "or_canon_sum": (f32, [P, i64]),
         "or_weight_scale": (f32, [P, i64]),
+        "or_adamw": (None, [P, P, P, P, i64, f32, f32, f32, f32, f32, f32, f32, f32, f32, i32]),
         "or_quantize": (None, [P, i64, f32, P, P]),
         "or_gemm_i8": (i64, [P, P, i64, i64, i64, P]),
         "or_swiglu_fwd": (None, [P, i64, i64, P]),
@@ -272,6 +273,44 @@ def replay(partials, R, S, max_norm=1.0, eps=0.0):
     nu = l2norm(T)
     clip(T, nu, max_norm, eps)
     return T, nu, A
+
+
+# ---- AdamW (NEXT-2) ---------------------------------------------------------------
+# Recipe (onedev.kr summary, "Limits", recipe paragraph): AdamW(0.9, 0.95, 1e-8),
+# decoupled weight decay 0.1 except input embedding, norm weights and RoPE table;
+# linear warm-up to 4.5e-4 over about 2.1B tokens, then one cosine decay to 10% of
+# the peak at 400B tokens, keyed to consumed tokens.  Reading R19 (see or_adamw in
+# oracle.c): the step's scalars in binary64, each rounded once to binary32.
+ADAMW = dict(beta1=0.9, beta2=0.95, eps=1e-8, wd=0.1, peak_lr=4.5e-4, min_lr=4.5e-5,
+             warmup_tokens=2.1e9, total_tokens=400e9)
+
+
+def lr_at(tokens: float, cfg=ADAMW) -> float:
+    """Learning rate (binary64) after `tokens` consumed tokens."""
+    import math
+    W, T = cfg["warmup_tokens"], cfg["total_tokens"]
+    if tokens < W:
+        return cfg["peak_lr"] * tokens / W
+    frac = min(1.0, (tokens - W) / (T - W))
+    return cfg["min_lr"] + (cfg["peak_lr"] - cfg["min_lr"]) * 0.5 * (1.0 + math.cos(math.pi * frac))
+
+
+def adamw_scalars(step: int, tokens: float, cfg=ADAMW) -> dict:
+    """The binary32 scalars of one step (each a binary64 value rounded once)."""
+    b1, b2 = cfg["beta1"], cfg["beta2"]
+    lr = lr_at(tokens, cfg)
+    f = lambda x: float(np.float32(x))
+    return dict(beta1=f(b1), beta2=f(b2), c1=f(1.0 - b1), c2=f(1.0 - b2), bc1=f(1.0 - b1 ** step),
+                bc2=f(1.0 - b2 ** step), eps=f(cfg["eps"]), lr=f(lr), d=f(lr * cfg["wd"]))
+
+
+def adamw(p, g, m, v, sc: dict, decay: bool = True):
+    """One AdamW update of (p, m, v) in place (float32 arrays) with scalars sc."""
+    for a in (p, m, v):
+        assert a.dtype == np.float32 and a.flags.c_contiguous
+    g = _f32(g)
+    lib().or_adamw(_p(p), _p(g), _p(m), _p(v), p.size, sc["beta1"], sc["beta2"], sc["c1"], sc["c2"],
+                   sc["bc1"], sc["bc2"], sc["eps"], sc["lr"], sc["d"], 1 if decay else 0)
 
 
 def num_threads() -> int:

@@ -548,6 +548,42 @@ float or_clip(float* T, int64_t len, float nu, float max_norm, float eps) {
     return kappa;
 }
 
+/* ---- AdamW update in a fixed operation order ---------------------------------
+ * Recipe: AdamW with beta1 0.9, beta2 0.95, eps 1e-8, decoupled weight decay
+ * 0.1 (not on the input embedding, the norm weights or the RoPE table), after
+ * the global clip; peak learning rate 4.5e-4 after a linear warm-up of about
+ * 2.1B tokens, then one cosine decay to 10% of the peak at the 400B-token
+ * budget, keyed to consumed tokens (onedev.kr summary, "Limits", recipe
+ * paragraph).  The pages fix neither the operation order nor how the step's
+ * scalars are formed; the reading taken (R19):
+ *   step scalars, in binary64 from the step t >= 1 and the tokens consumed,
+ *   each rounded once to binary32: lr, c1 = 1 - beta1, c2 = 1 - beta2,
+ *   bc1 = 1 - beta1^t, bc2 = 1 - beta2^t, d = lr * wd;
+ *   per element, each operation one binary32 operation (flushed), in order:
+ *     m = (beta1 * m) + (c1 * g)
+ *     v = (beta2 * v) + (c2 * (g * g))
+ *     u = (m / bc1) / (sqrt(v / bc2) + eps)
+ *     p = p - (d * p)            (only for tensors that decay)
+ *     p = p - (lr * u)                                                      */
+void or_adamw(float* p, const float* g, float* m, float* v, int64_t n, float beta1, float beta2, float c1,
+              float c2, float bc1, float bc2, float eps, float lr, float d, int decay) {
+    fp_env_default();
+    PARALLEL_BEGIN
+    #pragma omp for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const float mi = or_add(or_mul(beta1, m[i]), or_mul(c1, g[i]));
+        const float vi = or_add(or_mul(beta2, v[i]), or_mul(c2, or_mul(g[i], g[i])));
+        const float u = or_div(or_div(mi, bc1), or_add(or_sqrt(or_div(vi, bc2)), eps));
+        float pi = p[i];
+        if (decay) pi = or_sub(pi, or_mul(d, pi));
+        pi = or_sub(pi, or_mul(lr, u));
+        m[i] = mi;
+        v[i] = vi;
+        p[i] = pi;
+    }
+    PARALLEL_END
+}
+
 void or_set_threads(int n) {
 #ifdef _OPENMP
     if (n > 0) omp_set_num_threads(n);

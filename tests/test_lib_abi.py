@@ -198,3 +198,27 @@ def test_state_hash_block_instruction_count_matches_bench():
             n_align += "v_alignbit_b32" in l
     assert n_valu == bench.HASH_VALU_PER_BLOCK, n_valu
     assert n_align == bench.HASH_ALIGNBIT_PER_BLOCK, n_align
+
+
+def test_adamw_scalars_match_the_oracle():
+    """brl_adamw_scalars_for_step (host code of the library) gives the oracle's
+    binary32 scalars at warm-up, cosine and end-of-budget points."""
+    import oracle
+    for step, tokens in [(1, 0.0), (1, 1e6), (3, 1.05e9), (667, 2.1e9), (1000, 3e9), (60000, 2.01e11),
+                         (120000, 4e11), (200000, 5e11)]:
+        lib_s = brl.adamw_scalars_for_step(step, tokens).as_dict()
+        want = oracle.adamw_scalars(step, tokens)
+        for k, v in want.items():
+            assert lib_s[k] == v, (step, tokens, k, lib_s[k], v)
+
+
+def test_adamw_rejects_bad_arguments_without_launching():
+    L = brl.lib()
+    sc = brl.AdamWScalars()
+    p = C.c_void_p(0x10000)
+    assert L.adamw_step(p, p, p, p, -1, C.byref(sc), 1, None) == brl.BRL_ESHAPE
+    assert L.adamw_step(p, p, p, p, 4, None, 1, None) == brl.BRL_EINVAL
+    assert L.adamw_step(None, p, p, p, 4, C.byref(sc), 1, None) == brl.BRL_EINVAL
+    assert L.adamw_step(C.c_void_p(0x10001), p, p, p, 4, C.byref(sc), 1, None) == brl.BRL_EINVAL
+    assert L.brl_adamw_scalars_for_step(0, 1.0, None, C.byref(sc)) == brl.BRL_EINVAL
+    assert L.brl_adamw_scalars_for_step(1, float("nan"), None, C.byref(sc)) == brl.BRL_EINVAL
