@@ -51,7 +51,10 @@ REPLAY_BYTES_PER_ELEM = 6 * 7 * 12 + 28 + 8           # 540
 # over (2 x alignbit + the rest) slots per block, times 64 bytes.
 HASH_VALU_PER_BLOCK = 1561
 HASH_ALIGNBIT_PER_BLOCK = 576
-HASH_STATE_TENSORS = 8                                   # 8 x 805 MB = 6.44 GB
+HASH_STATE_TENSORS = 8
+# AdamW (the next row after the clip, measured beside the step): per parameter
+# read p, g, m, v and write p, m, v.
+ADAMW_BYTES_PER_ELEM = 28                                   # 8 x 805 MB = 6.44 GB
 
 
 def measured_traffic(kernel: str):
@@ -210,6 +213,14 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
+    # AdamW over the reduced, clipped gradient (L parameters; p, m, v synthetic)
+    ap = synth.replay_partial(rcase, 100, device=dev, length=L)
+    am = torch.zeros(L, dtype=torch.float32, device=dev)
+    av = torch.zeros(L, dtype=torch.float32, device=dev)
+    asc = brl.adamw_scalars_for_step(1000, 3.0e9)
+    adamw_ms = avg_call(lambda: brl.adamw_step(ap, out, am, av, asc), reps=3)
+    adamw_gbps = ADAMW_BYTES_PER_ELEM * L / (adamw_ms * 1e-3) / 1e9
+    del ap, am, av
     # state hash of a 6.44 GB state (the first 8 replay partials as its tensors)
     hstate = partials[:HASH_STATE_TENSORS]
     hash_bytes = sum(t.numel() * 4 for t in hstate)
@@ -274,6 +285,12 @@ def main():
                    "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
                    "frac": round(ops / (dw_ms * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4)},
         },
+    }
+    result["adamw"] = {
+        "params": L, "ms": round(adamw_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(adamw_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(adamw_gbps / PEAK_HBM_GBPS, 4),
+                     "note": f"{ADAMW_BYTES_PER_ELEM} B per parameter (read p, g, m, v; write p, m, v)"},
     }
     hash_gbps = hash_bytes / (hash_ms * 1e-3) / 1e9
     hash_slots = HASH_VALU_PER_BLOCK + HASH_ALIGNBIT_PER_BLOCK
