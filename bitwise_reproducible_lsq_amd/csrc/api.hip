@@ -20,7 +20,7 @@ int bwd_chunk_log2(int engine) {
     int64_t v = g_tune[BRL_TUNE_BWD_CHUNK_LOG2].load();
     if (v > 0) return (int)v;
     // defaults: the deepest stack that keeps 3 workgroups per CU
-    if (engine == 2) return 5;
+    if (engine == 2) return 6;
     if (engine == 1) return 4;
     return 4;   // any engine: the smaller depth (more chunk roots) bounds the workspace
 }
@@ -486,7 +486,7 @@ brl_status adamw_step(float* p, const float* g, float* m, float* v, int64_t n, c
 
 int64_t brl_set_tuning(int32_t knob, int64_t value) {
     if (knob < 0 || knob > 3) return -1;
-    if (knob == BRL_TUNE_BWD_CHUNK_LOG2 && value > 6) value = 6;
+    if (knob == BRL_TUNE_BWD_CHUNK_LOG2 && value > 7) value = 7;
     if (knob == BRL_TUNE_REDUCE_WG_BLOCKS && value > 0 && value != 64 && value != 128 && value != 256)
         value = 256;
     if (knob == BRL_TUNE_STREAM_VEC && value > 0 && value != 1 && value != 2 && value != 4) value = 1;

@@ -472,6 +472,7 @@ static void ste_launch_chunk(const SteArgs& a, int D, dim3 grid, int64_t nblk, i
         case 3: hipLaunchKernelGGL((ste_chunk_kernel<A_RMAJ, 3>), grid, dim3(256), 0, st, a, nblk, final_out); break;
         case 4: hipLaunchKernelGGL((ste_chunk_kernel<A_RMAJ, 4>), grid, dim3(256), 0, st, a, nblk, final_out); break;
         case 6: hipLaunchKernelGGL((ste_chunk_kernel<A_RMAJ, 6>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+        case 7: hipLaunchKernelGGL((ste_chunk_kernel<A_RMAJ, 7>), grid, dim3(256), 0, st, a, nblk, final_out); break;
         default: hipLaunchKernelGGL((ste_chunk_kernel<A_RMAJ, 5>), grid, dim3(256), 0, st, a, nblk, final_out); break;
     }
 }
@@ -484,6 +485,7 @@ static void ste_launch_mfma(const SteArgs& a, int D, dim3 grid, int64_t nblk, in
         case 3: hipLaunchKernelGGL((ste_mfma_kernel<A_RMAJ, 3>), grid, dim3(256), 0, st, a, nblk, final_out); break;
         case 4: hipLaunchKernelGGL((ste_mfma_kernel<A_RMAJ, 4>), grid, dim3(256), 0, st, a, nblk, final_out); break;
         case 6: hipLaunchKernelGGL((ste_mfma_kernel<A_RMAJ, 6>), grid, dim3(256), 0, st, a, nblk, final_out); break;
+        case 7: hipLaunchKernelGGL((ste_mfma_kernel<A_RMAJ, 7>), grid, dim3(256), 0, st, a, nblk, final_out); break;
         default: hipLaunchKernelGGL((ste_mfma_kernel<A_RMAJ, 5>), grid, dim3(256), 0, st, a, nblk, final_out); break;
     }
 }

@@ -248,8 +248,8 @@ BRL_API brl_status brl_probe_f32(int32_t op, const float* a, const float* b, flo
 /* Launch-shape tuning knobs.  They change only how work is split across
  * workgroups or which units form the products, never the results.  Returns the previous value, or -1 for an
  * unknown knob; value <= 0 restores the default.  Process-wide. */
-#define BRL_TUNE_BWD_CHUNK_LOG2   0   /* 32-blocks per backward reduction chunk: 2^v, 1..6 (default 0:
-                                         5 on the matrix-core engine, 4 on the VALU engine) */
+#define BRL_TUNE_BWD_CHUNK_LOG2   0   /* 32-blocks per backward reduction chunk: 2^v, 1..7 (default 0:
+                                         6 on the matrix-core engine, 4 on the VALU engine) */
 #define BRL_TUNE_REDUCE_WG_BLOCKS 1   /* 32-blocks per workgroup in CanonSum passes: 64,128,256 */
 #define BRL_TUNE_STREAM_VEC       2   /* 16-byte vectors per thread in streaming kernels: 1, 2, 4 */
 #define BRL_TUNE_BWD_ENGINE       3   /* backward products on 1 the VALU, 2 the matrix cores (default; needs

@@ -304,7 +304,7 @@ def test_bwd_launch_shape_invariance():
     try:
         for e in ENGINES:
             brl.set_tuning(brl.TUNE_BWD_ENGINE, e)
-            for c, r in [(1, 64), (2, 128), (3, 256), (4, 64), (5, 128), (6, 256)]:
+            for c, r in [(1, 64), (2, 128), (3, 256), (4, 64), (5, 128), (6, 256), (7, 64)]:
                 brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, c)
                 brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, r)
                 dX, dW = brl.qat_linear_bwd(dY, X, W, synth.S_X)
