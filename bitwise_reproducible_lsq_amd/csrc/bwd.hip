@@ -84,7 +84,7 @@ typedef float vf1 __attribute__((ext_vector_type(1)));
 __device__ __forceinline__ float mask_select(float v, const float* src, int64_t idx,
                                              const float* s_dev, float s_host) {
     const float s = s_dev ? *s_dev : s_host;
-    return quantize_in_range(src[idx], s) ? v : 0.0f;
+    return Quantizer(s).in_range(src[idx]) ? v : 0.0f;
 }
 
 template <bool A_RMAJ, int D>

@@ -43,6 +43,13 @@ __device__ __forceinline__ float f_div(float a, float b) {
     return flush_f32((float)q);
 }
 
+// a / b for a divisor b fixed across many calls, given rb = fl64(1/flush(b)):
+// the same correctly rounded binary32 quotient as f_div (see Quantizer below
+// for why the binary64 product lands in the right rounding interval).
+__device__ __forceinline__ float f_div_by(float a, double rb) {
+    return flush_f32((float)((double)flush_f32(a) * rb));
+}
+
 __device__ __forceinline__ float f_sqrt(float a) {
     double r = __builtin_sqrt((double)flush_f32(a));
     return flush_f32((float)r);
@@ -50,23 +57,38 @@ __device__ __forceinline__ float f_sqrt(float a) {
 
 __device__ __forceinline__ float f_rne(float t) { return __builtin_rintf(t); }
 
-// Quantise one value with step s: q = clamp(rne(v/s), -127, 127),
-// in = (-127 <= v/s <= 127).  A zero step maps everything to q = 0, in range.
-__device__ __forceinline__ int quantize_q(float v, float s, bool* in_range) {
-    if (s == 0.0f) { *in_range = true; return 0; }
-    float t = f_div(v, s);
-    *in_range = (t >= -(float)kQmax) && (t <= (float)kQmax);
-    float r = f_rne(t);
-    r = r > (float)kQmax ? (float)kQmax : r;
-    r = r < -(float)kQmax ? -(float)kQmax : r;
-    return (int)r;
-}
-
-__device__ __forceinline__ bool quantize_in_range(float v, float s) {
-    if (s == 0.0f) return true;
-    float t = f_div(v, s);
-    return (t >= -(float)kQmax) && (t <= (float)kQmax);
-}
+// LSQ quantiser with step s: q = clamp(rne(v/s), -127, 127),
+// in = (-127 <= v/s <= 127); a zero step maps everything to q = 0, in range.
+// The quotient comes from the binary64 reciprocal of the step:
+// fl32(fl64(v * fl64(1/s))) is the correctly rounded binary32 v/s.  The
+// binary64 product is within 2^-51.9 (relative) of v/s, while the exact
+// quotient of two binary32 numbers that is not itself a rounding boundary
+// is at least 2^-49 (relative) away from every one of them: the midpoints
+// between neighbouring binary32 values and the underflow threshold.  So the
+// product lies in the same rounding interval as v/s.
+struct Quantizer {
+    float s;
+    double rs;
+    __device__ __forceinline__ explicit Quantizer(float step)
+        : s(flush_f32(step)), rs(s == 0.0f ? 0.0 : 1.0 / (double)s) {}
+    __device__ __forceinline__ float quotient(float v) const {
+        return flush_f32((float)((double)flush_f32(v) * rs));
+    }
+    __device__ __forceinline__ int q(float v, bool* in_range) const {
+        if (s == 0.0f) { *in_range = true; return 0; }
+        const float t = quotient(v);
+        *in_range = (t >= -(float)kQmax) && (t <= (float)kQmax);
+        float r = f_rne(t);
+        r = r > (float)kQmax ? (float)kQmax : r;
+        r = r < -(float)kQmax ? -(float)kQmax : r;
+        return (int)r;
+    }
+    __device__ __forceinline__ bool in_range(float v) const {
+        if (s == 0.0f) return true;
+        const float t = quotient(v);
+        return (t >= -(float)kQmax) && (t <= (float)kQmax);
+    }
+};
 
 // ---- the library's own binary32 exp (SwiGLU) ------------------------------
 // E(x): Cody-Waite reduction x = k*ln2 + r with k = rne(x * log2(e)), ln2

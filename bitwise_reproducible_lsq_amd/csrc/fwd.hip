@@ -24,53 +24,66 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 // ---- quantiser ------------------------------------------------------------------
-// Thread -> 16 consecutive columns of one padded output row; grid x walks
-// the columns, grid y (with a stride loop) the rows.
+// Thread -> 4 consecutive columns (one 16-byte load, one 4-byte store) of
+// kQRows padded output rows, whose loads are all issued before any of them
+// is quantised; grid x walks the column quads, grid y (with a stride loop)
+// the row blocks.  A wave reads 1 KiB and writes 256 B contiguously.
+constexpr int kQRows = 4;
+
+__device__ __forceinline__ int64_t quantize_src_row(int64_t ro, int64_t rows, int64_t swiglu_half, bool* valid) {
+    if (swiglu_half > 0) {
+        // stacked gate/up weight rows interleaved in groups of kSwigluGroup
+        const int64_t t = ro >> 7, w = ro & (2 * kSwigluGroup - 1);
+        const int64_t j = t * kSwigluGroup + (w & (kSwigluGroup - 1));
+        *valid = j < swiglu_half;
+        return (w < kSwigluGroup) ? j : swiglu_half + j;
+    }
+    *valid = ro < rows;
+    return ro;
+}
+
 __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ v, int64_t rows,
                                                        int64_t cols, const float* __restrict__ s_dev,
                                                        float s_host, int8_t* __restrict__ q,
                                                        int64_t rows_p, int64_t cols_p,
                                                        int64_t swiglu_half) {
-    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;
+    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (c0 >= cols_p) return;
-    const float s = s_dev ? *s_dev : s_host;
-    const bool vec_rows = ((cols & 3) == 0) && ((reinterpret_cast<uintptr_t>(v) & 15) == 0);
-    for (int64_t ro = blockIdx.y; ro < rows_p; ro += gridDim.y) {
-        int64_t r = ro;
-        bool valid = ro < rows;
-        if (swiglu_half > 0) {
-            const int64_t t = ro >> 7, w = ro & (2 * kSwigluGroup - 1);
-            const int64_t j = t * kSwigluGroup + (w & (kSwigluGroup - 1));
-            valid = j < swiglu_half;
-            r = (w < kSwigluGroup) ? j : swiglu_half + j;
-        }
-        union { int8_t b[16]; v4i v; } out;
+    const Quantizer qz(s_dev ? *s_dev : s_host);
+    const bool vec = ((cols & 3) == 0) && ((reinterpret_cast<uintptr_t>(v) & 15) == 0) && c0 + 4 <= cols;
+    for (int64_t rb = (int64_t)blockIdx.y * kQRows; rb < rows_p; rb += (int64_t)gridDim.y * kQRows) {
+        vf4 x[kQRows];
+        bool ok[kQRows];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) out.b[e] = 0;
-        if (valid) {
+        for (int u = 0; u < kQRows; ++u) {
+            x[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
+            bool valid;
+            const int64_t r = quantize_src_row(rb + u, rows, swiglu_half, &valid);
+            ok[u] = valid && rb + u < rows_p;
+            if (!ok[u]) continue;
             const float* src = v + r * cols;
-            if (vec_rows && c0 + 16 <= cols) {
-                const vf4* s4 = reinterpret_cast<const vf4*>(src + c0);
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    vf4 x = s4[g];
-                    bool in;
-                    out.b[4 * g + 0] = (int8_t)quantize_q(x.x, s, &in);
-                    out.b[4 * g + 1] = (int8_t)quantize_q(x.y, s, &in);
-                    out.b[4 * g + 2] = (int8_t)quantize_q(x.z, s, &in);
-                    out.b[4 * g + 3] = (int8_t)quantize_q(x.w, s, &in);
-                }
+            if (vec) {
+                x[u] = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(src + c0));
             } else {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    if (c0 + e < cols) {
-                        bool in;
-                        out.b[e] = (int8_t)quantize_q(src[c0 + e], s, &in);
-                    }
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (c0 + e < cols) x[u][e] = src[c0 + e];
             }
         }
-        *reinterpret_cast<v4i*>(q + ro * cols_p + c0) = out.v;
+#pragma unroll
+        for (int u = 0; u < kQRows; ++u) {
+            if (rb + u >= rows_p) break;
+            uint32_t packed = 0;
+            if (ok[u]) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bool in;
+                    const int qv = (c0 + e < cols) ? qz.q(x[u][e], &in) : 0;
+                    packed |= (uint32_t)(uint8_t)(int8_t)qv << (8 * e);
+                }
+            }
+            *reinterpret_cast<uint32_t*>(q + (rb + u) * cols_p + c0) = packed;
+        }
     }
 }
 
@@ -78,8 +91,9 @@ hipError_t launch_quantize(const float* v, int64_t rows, int64_t cols, const flo
                            float s_host, int8_t* q, int64_t rows_p, int64_t cols_p,
                            int64_t swiglu_half, hipStream_t st) {
     if (rows_p <= 0 || cols_p <= 0) return hipSuccess;
-    const unsigned gx = (unsigned)ceil_div(cols_p / 16, 256);
-    const unsigned gy = (unsigned)(rows_p < 65535 ? rows_p : 65535);
+    const unsigned gx = (unsigned)ceil_div(cols_p / 4, 256);
+    const int64_t blocks = ceil_div(rows_p, kQRows);
+    const unsigned gy = (unsigned)(blocks < 65535 ? blocks : 65535);
     hipLaunchKernelGGL(quantize_kernel, dim3(gx, gy), dim3(256), 0, st, v, rows, cols, s_dev, s_host,
                        q, rows_p, cols_p, swiglu_half);
     return hipGetLastError();
@@ -94,6 +108,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const float* __restrict__ 
     const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (c0 >= cols_p) return;
     const float s = s_dev ? *s_dev : s_host;
+    const Quantizer qz(s);
     const bool vec_rows = ((cols & 3) == 0) && ((reinterpret_cast<uintptr_t>(v) & 15) == 0);
     for (int64_t r = blockIdx.y; r < rows_p; r += gridDim.y) {
         vf4 o = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -102,14 +117,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const float* __restrict__ 
             bool in;
             if (vec_rows && c0 + 4 <= cols) {
                 const vf4 x = *reinterpret_cast<const vf4*>(src + c0);
-                o.x = f_mul((float)quantize_q(x.x, s, &in), s);
-                o.y = f_mul((float)quantize_q(x.y, s, &in), s);
-                o.z = f_mul((float)quantize_q(x.z, s, &in), s);
-                o.w = f_mul((float)quantize_q(x.w, s, &in), s);
+                o.x = f_mul((float)qz.q(x.x, &in), s);
+                o.y = f_mul((float)qz.q(x.y, &in), s);
+                o.z = f_mul((float)qz.q(x.z, &in), s);
+                o.w = f_mul((float)qz.q(x.w, &in), s);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (c0 + e < cols) o[e] = f_mul((float)quantize_q(src[c0 + e], s, &in), s);
+                    if (c0 + e < cols) o[e] = f_mul((float)qz.q(src[c0 + e], &in), s);
             }
         }
         *reinterpret_cast<vf4*>(out + r * cols_p + c0) = o;
@@ -129,11 +144,21 @@ hipError_t launch_dequant(const float* v, int64_t rows, int64_t cols, const floa
 // ---- int8 GEMM ---------------------------------------------------------------------
 // Workgroup tile BM x BN (256 x 256), K step 64 bytes (two MFMA k-steps of 32),
 // 4 waves of 128 x 128, each a 4 x 4 grid of v_mfma_i32_32x32x32_i8 tiles.
-// Operand tiles move global -> LDS with global_load_lds_dwordx4 (no staging
-// registers) through a ring of kStages LDS stages, so loads run kStages-1
-// tiles ahead of the MFMAs.  LDS rows are 64 bytes, unpadded; the four
-// 16-byte chunks of row r are stored XOR-swizzled by (r >> 1) & 3, which puts
-// the 16-byte fragment reads of 8 consecutive rows in 8 distinct bank groups.
+// Operand tiles move global -> LDS with buffer_load_dwordx4 ... lds (no
+// staging registers; per-lane offsets fixed for the whole loop, the k offset
+// in a scalar register) through a ring of kStages LDS stages, so loads run
+// kStages-1 tiles ahead of the MFMAs.  LDS rows are 64 bytes, unpadded; the
+// four 16-byte chunks of row r are stored XOR-swizzled by (r >> 1) & 3, which
+// puts the 16-byte fragment reads of 8 consecutive rows in 8 distinct bank
+// groups.
+//
+// Schedule: with one wave per SIMD, any instruction that stalls the wave
+// idles its matrix core, so every k-step issues its 16 MFMAs with the
+// memory instructions of the pipeline placed between them (scheduling
+// barriers keep the compiler from regrouping them): the 8 fragment reads of
+// the next k-step, and in the second k-step of each tile the 8 loads of the
+// tile kStages-1 ahead.  Past the last tile those loads repeat the last tile
+// into a stage that is never read again, so the loop has no branch.
 constexpr int kBK = 64;
 constexpr int kStages = 4;
 
@@ -152,10 +177,23 @@ struct GemmCfg {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
 
+// 16 bytes per lane from base[off + soff] (a raw buffer over `bytes` bytes;
+// reads past the end return zero) into LDS at lds + 16 * lane
+__device__ __forceinline__ void gemm_load_lds(const int8_t* base, int bytes, uint32_t off, uint32_t soff,
+                                              int8_t* lds) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(base), (short)0, bytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, soff, 0, 0);
+}
+
+#define GEMM_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(GemmArgs a) {
     using C = GemmCfg<BM, BN, WM, WN>;
     static_assert(C::kThreads == 256, "the GEMM runs 4 waves per workgroup");
+    static_assert(C::kTM * C::kTN == 16 && C::kTM + C::kTN == 8 && C::kLoads == 8,
+                  "the k-step interleaves 8 reads and 8 loads with 16 MFMAs");
     extern __shared__ __attribute__((aligned(16))) int8_t smem[];
 
     const int tid = threadIdx.x;
@@ -174,27 +212,27 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(GemmArgs a) {
 
     const int8_t* gA = a.qx + m0 * a.Kp;
     const int8_t* gB = a.qw + n0 * a.Kp;
+    const int bytesA = (int)(BM * a.Kp), bytesB = (int)(BN * a.Kp);
     const int KT = (int)(a.Kp / kBK);
 
-    // this lane's share of one load instruction: row (lane >> 2) of a 16-row
+    // this lane's share of load instruction i: row (lane >> 2) of a 16-row
     // group, LDS slot (lane & 3), holding global chunk swz(row, slot)
     const int lrow = lane >> 2, lslot = lane & 3;
-    auto issue = [&](int kt, int stage) {
+    uint32_t off[C::kLoads];
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i) {
+        const int r = i < C::kLoadsA ? (wave * C::kLoadsA + i) * 16 + lrow
+                                     : (wave * C::kLoadsB + (i - C::kLoadsA)) * 16 + lrow;
+        off[i] = (uint32_t)(r * a.Kp + 16 * swz(r, lslot));
+    }
+    auto load1 = [&](int kt, int stage, int i) {
         int8_t* sA = smem + stage * C::kStage;
-        int8_t* sB = sA + C::kTileA;
-#pragma unroll
-        for (int i = 0; i < C::kLoadsA; ++i) {
+        if (i < C::kLoadsA) {
             const int r0 = (wave * C::kLoadsA + i) * 16;
-            const int r = r0 + lrow;
-            const int8_t* g = gA + (int64_t)r * a.Kp + kt * kBK + 16 * swz(r, lslot);
-            __builtin_amdgcn_global_load_lds(g, sA + r0 * kBK, 16, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < C::kLoadsB; ++i) {
-            const int r0 = (wave * C::kLoadsB + i) * 16;
-            const int r = r0 + lrow;
-            const int8_t* g = gB + (int64_t)r * a.Kp + kt * kBK + 16 * swz(r, lslot);
-            __builtin_amdgcn_global_load_lds(g, sB + r0 * kBK, 16, 0, 0);
+            gemm_load_lds(gA, bytesA, off[i], (uint32_t)(kt * kBK), sA + r0 * kBK);
+        } else {
+            const int r0 = (wave * C::kLoadsB + (i - C::kLoadsA)) * 16;
+            gemm_load_lds(gB, bytesB, off[i], (uint32_t)(kt * kBK), sA + C::kTileA + r0 * kBK);
         }
     };
 
@@ -208,41 +246,33 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(GemmArgs a) {
 
     const int frow = lane & 31;            // fragment row (A) / column (B)
     const int fchunk = lane >> 5;          // this lane's 16-byte k chunk within a 32-k step
-    // Fragments of one 32-k step (4 of A, 4 of B) live in registers.  The
-    // reads of the next step are issued before the 16 MFMAs of the current
-    // one, so LDS latency hides behind matrix work; the barrier that lands
-    // the next tile sits between a tile's two steps, with MFMAs in flight.
     using Frag = v4i[C::kTM + C::kTN];
-    auto read_frags = [&](int stage, int ks, Frag& F) {
+    // fragment q of k-step ks in `stage`: A rows for q < kTM, else B rows
+    auto read1 = [&](int stage, int ks, Frag& F, int q) {
         const int8_t* sA = smem + stage * C::kStage;
-        const int8_t* sB = sA + C::kTileA;
         const int chunk = fchunk + 2 * ks;
-#pragma unroll
-        for (int i = 0; i < C::kTM; ++i) {
-            const int r = wm * WM + i * 32 + frow;
-            F[i] = *reinterpret_cast<const v4i*>(sA + r * kBK + 16 * swz(r, chunk));
-        }
-#pragma unroll
-        for (int j = 0; j < C::kTN; ++j) {
-            const int r = wn * WN + j * 32 + frow;
-            F[C::kTM + j] = *reinterpret_cast<const v4i*>(sB + r * kBK + 16 * swz(r, chunk));
+        if (q < C::kTM) {
+            const int r = wm * WM + q * 32 + frow;
+            F[q] = *reinterpret_cast<const v4i*>(sA + r * kBK + 16 * swz(r, chunk));
+        } else {
+            const int r = wn * WN + (q - C::kTM) * 32 + frow;
+            F[q] = *reinterpret_cast<const v4i*>(sA + C::kTileA + r * kBK + 16 * swz(r, chunk));
         }
     };
-    auto mfmas = [&](const Frag& F) {
+    // one k-step: the 16 MFMAs on Fc, MFMA q followed by fragment read q of
+    // (rs, rk) into Fn (q < 8) and, when ld, by load q/2 of tile lkt into
+    // stage ls (odd q)
+    auto kstep = [&](const Frag& Fc, Frag& Fn, bool rd, int rs, int rk, bool ld, int lkt, int ls) {
 #pragma unroll
-        for (int i = 0; i < C::kTM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::kTN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F[i], F[C::kTM + j], acc[i][j], 0, 0, 0);
+        for (int q = 0; q < 16; ++q) {
+            const int i = q / C::kTN, j = q % C::kTN;
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Fc[i], Fc[C::kTM + j], acc[i][j], 0, 0, 0);
+            if (rd && q < C::kTM + C::kTN) read1(rs, rk, Fn, q);
+            if (ld && (q & 1)) load1(lkt, ls, q >> 1);
+            GEMM_SCHED_FENCE();
+        }
     };
-    // wait until tile t has landed in LDS for every wave (loads of the tiles
-    // after it, up to min(KT-1, newest), may stay in flight), then barrier
-    auto land = [&](int t, int newest) {
-        const int last = newest < KT - 1 ? newest : KT - 1;
-        const int ahead = last - t;
-        if (ahead >= 2) wait_vmcnt<2 * C::kLoads>();
-        else if (ahead == 1) wait_vmcnt<C::kLoads>();
-        else wait_vmcnt<0>();
+    auto barrier = [] {
         // bare barrier: a fence here would wait for every load in flight
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
@@ -253,23 +283,25 @@ __global__ __launch_bounds__(256, 1) void gemm_i8_kernel(GemmArgs a) {
     Frag F0, F1;
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
-        if (s < KT) issue(s, s);
-    land(0, kStages - 2);
-    read_frags(0, 0, F0);
-    // every tile but the last hands over to the next one; the last is peeled
-    // so that the loop body has no branch between LDS reads and their use
+#pragma unroll
+        for (int i = 0; i < C::kLoads; ++i) load1(s < KT ? s : KT - 1, s, i);
+    wait_vmcnt<2 * C::kLoads>();          // tile 0 landed (tiles 1, 2 may be in flight)
+    barrier();
+#pragma unroll
+    for (int q = 0; q < C::kTM + C::kTN; ++q) read1(0, 0, F0, q);
+    GEMM_SCHED_FENCE();
     for (int kt = 0; kt < KT - 1; ++kt) {
-        read_frags(kt % kStages, 1, F1);
-        mfmas(F0);
-        // tile kt-1's stage is free once every wave passes this barrier
-        land(kt + 1, kt + kStages - 2);
-        if (kt + kStages - 1 < KT) issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
-        read_frags((kt + 1) % kStages, 0, F0);
-        mfmas(F1);
+        kstep(F0, F1, true, kt % kStages, 1, false, 0, 0);
+        // tile kt+1 landed for every wave, and every wave is past its reads
+        // of tile kt-1, whose stage the loads below refill
+        wait_vmcnt<C::kLoads>();
+        barrier();
+        const int lkt = kt + kStages - 1 < KT ? kt + kStages - 1 : KT - 1;
+        kstep(F1, F0, true, (kt + 1) % kStages, 0, true, lkt, (kt + kStages - 1) % kStages);
     }
-    read_frags((KT - 1) % kStages, 1, F1);
-    mfmas(F0);
-    mfmas(F1);
+    kstep(F0, F1, true, (KT - 1) % kStages, 1, false, 0, 0);
+    kstep(F1, F0, false, 0, 0, false, 0, 0);
+    wait_vmcnt<0>();                       // no load into LDS outlives the loop
 
     // ---- epilogue: Y = fl(acc) * s_y (+ addend), or the SwiGLU activation ----
     const float s_y = a.scal->s_y;
@@ -343,6 +375,8 @@ static hipError_t launch_gemm_epi(const GemmArgs& a, hipStream_t st) {
     static_assert(C::kLoadsA * C::kWaves * 16 == BM && C::kLoadsB * C::kWaves * 16 == BN, "load split");
     static_assert(2 * C::kLoads < 64, "vmcnt range");
     const size_t lds = (size_t)kStages * C::kStage;
+    // operand panels are addressed through 32-bit buffer offsets
+    if ((int64_t)(BM > BN ? BM : BN) * a.Kp > INT32_MAX) return hipErrorInvalidValue;
     static bool attr = false;
     if (!attr) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_i8_kernel<BM, BN, WM, WN, EPI>),

@@ -25,11 +25,13 @@
 
 namespace brl {
 
+// rbc1, rbc2: binary64 reciprocals of the bias corrections (nonzero for
+// step >= 1), so m / bc1 and v / bc2 cost one binary64 multiply each
 __device__ __forceinline__ void adamw_elem(float& p, float g, float& m, float& v, const brl_adamw_scalars& s,
-                                           int decay) {
+                                           double rbc1, double rbc2, int decay) {
     m = f_add(f_mul(s.beta1, m), f_mul(s.c1, g));
     v = f_add(f_mul(s.beta2, v), f_mul(s.c2, f_mul(g, g)));
-    const float u = f_div(f_div(m, s.bc1), f_add(f_sqrt(f_div(v, s.bc2)), s.eps));
+    const float u = f_div(f_div_by(m, rbc1), f_add(f_sqrt(f_div_by(v, rbc2)), s.eps));
     if (decay) p = f_sub(p, f_mul(s.d, p));
     p = f_sub(p, f_mul(s.lr, u));
 }
@@ -39,12 +41,13 @@ __global__ __launch_bounds__(256) void adamw_v4_kernel(vf4* __restrict__ p, cons
                                                        brl_adamw_scalars s, int decay) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n4) return;
+    const double rbc1 = 1.0 / (double)flush_f32(s.bc1), rbc2 = 1.0 / (double)flush_f32(s.bc2);
     vf4 pp = __builtin_nontemporal_load(p + i), gg = __builtin_nontemporal_load(g + i);
     vf4 mm = __builtin_nontemporal_load(m + i), vv = __builtin_nontemporal_load(v + i);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         float pe = pp[e], me = mm[e], ve = vv[e];
-        adamw_elem(pe, gg[e], me, ve, s, decay);
+        adamw_elem(pe, gg[e], me, ve, s, rbc1, rbc2, decay);
         pp[e] = pe; mm[e] = me; vv[e] = ve;
     }
     __builtin_nontemporal_store(pp, p + i);
@@ -57,8 +60,9 @@ __global__ __launch_bounds__(256) void adamw_scalar_kernel(float* __restrict__ p
                                                            int64_t n, brl_adamw_scalars s, int decay) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
+    const double rbc1 = 1.0 / (double)flush_f32(s.bc1), rbc2 = 1.0 / (double)flush_f32(s.bc2);
     float pe = p[i], me = m[i], ve = v[i];
-    adamw_elem(pe, g[i], me, ve, s, decay);
+    adamw_elem(pe, g[i], me, ve, s, rbc1, rbc2, decay);
     p[i] = pe; m[i] = me; v[i] = ve;
 }
 

@@ -181,6 +181,48 @@ def test_fwd_zero_weights_and_empty_rows():
     assert_bitwise(s_w, np.array([oracle.weight_scale(W)]), "s_w (M=0)")
 
 
+def _boundary_inputs(s, seed, rows=48, cols=96):
+    """X whose quotients by the step s sit within a few ulp of the points
+    where the quantiser's result changes: the rounding midpoints k + 1/2 and
+    the range ends +-127, +-127.5; the rest of X is N(0, 1)."""
+    s = np.float32(s)
+    vals = []
+    for t in [k + 0.5 for k in range(-128, 128)] + [-127.0, 127.0]:
+        v = np.float32(np.float64(t) * np.float64(s)).view(np.int32)
+        vals += [np.int32(v + d).view(np.float32) for d in range(-3, 4)]
+    vals = np.array(vals, np.float32)
+    X = np.random.default_rng(seed).standard_normal(rows * cols).astype(np.float32)
+    X[:vals.size] = vals
+    return X.reshape(rows, cols), vals
+
+
+@pytest.mark.parametrize("s", [0.05, 0.0371, 1.0 / 3.0, 2.5e-3])
+def test_quantizer_at_rounding_boundaries(s):
+    """Forward (q_x) and backward (the STE mask of X) on inputs whose
+    quotients v/s lie next to rounding midpoints.  The CPU check first shows
+    the set is sensitive: a quotient formed as v * fl32(1/s) changes some
+    codes, so a kernel taking that shortcut would fail here."""
+    from fractions import Fraction
+    X, vals = _boundary_inputs(s, seed=int(s * 1e4))
+    sf = np.float32(s)
+    exact = [Fraction(float(v)) / Fraction(float(sf)) for v in vals]
+    naive = [np.float32(v * np.float32(np.float32(1.0) / sf)) for v in vals]
+    correct = [np.float32(float(q)) for q in exact]      # round-to-nearest of the exact quotient
+    assert any(np.rint(a) != np.rint(b) for a, b in zip(naive, correct)), \
+        "boundary set does not separate the shortcut"
+    assert all(np.float32(oracle.div(v, sf)) == c for v, c in zip(vals, correct))
+    W = np.random.default_rng(3).standard_normal((80, X.shape[1])).astype(np.float32) * np.float32(0.02)
+    Y, _, _ = brl.qat_linear_fwd(_cuda(X), _cuda(W), float(sf))
+    assert_bitwise(Y, oracle.linear_fwd(X, W, sf), "Y")
+    dY = np.random.default_rng(4).standard_normal((X.shape[0], 80)).astype(np.float32) * np.float32(1e-3)
+    wX, wW = oracle.linear_bwd(dY, X, W, sf)
+    for engine in ENGINES:
+        with tuning(brl.TUNE_BWD_ENGINE, engine):
+            dX, dW = brl.qat_linear_bwd(_cuda(dY), _cuda(X), _cuda(W), float(sf))
+        assert_bitwise(dX, wX, f"dX (engine {engine})")
+        assert_bitwise(dW, wW, f"dW (engine {engine})")
+
+
 # ---- linear layer: backward -----------------------------------------------------------
 class tuning:
     """Set a launch-shape knob for the duration of a with-block."""
