@@ -65,6 +65,7 @@ def lib():
         "or_treefold": (i32, [P, i32, i64, P]),
         "or_l2norm": (f32, [P, i64]),
         "or_clip": (f32, [P, i64, f32, f32, f32]),
+        "or_attn_fwd": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64]),
         "or_num_threads": (i32, []),
         "or_set_threads": (None, [i32]),
     }
@@ -311,6 +312,20 @@ def adamw(p, g, m, v, sc: dict, decay: bool = True):
     g = _f32(g)
     lib().or_adamw(_p(p), _p(g), _p(m), _p(v), p.size, sc["beta1"], sc["beta2"], sc["c1"], sc["c2"],
                    sc["bc1"], sc["bc2"], sc["eps"], sc["lr"], sc["d"], 1 if decay else 0)
+
+
+def attn_fwd(Q, K, V, window: int, s_v: float) -> np.ndarray:
+    """Attention with int8 P.V on [B, S, H, D] arrays (Q: Hq heads, K and V:
+    Hkv heads); returns O [B, S, Hq, D].  See or_attn_fwd for the readings."""
+    Q, K, V = _f32(Q), _f32(K), _f32(V)
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    assert K.shape == (B, S, Hkv, D) and V.shape == K.shape
+    O = np.empty_like(Q)
+    rc = lib().or_attn_fwd(_p(Q), _p(K), _p(V), B, S, Hq, Hkv, D, Hq * D, Hkv * D, Hkv * D, int(window),
+                           np.float32(s_v), _p(O), Hq * D)
+    assert rc == 0, f"or_attn_fwd failed ({rc})"
+    return O
 
 
 def num_threads() -> int:

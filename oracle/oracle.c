@@ -584,6 +584,91 @@ void or_adamw(float* p, const float* g, float* m, float* v, int64_t n, float bet
     PARALLEL_END
 }
 
+/* ------------------------------------------------------------------------ */
+/* Attention with int8 P.V (onedev.kr summary, "Use", attention paragraph:   */
+/* the P.V product of flash attention on int8 tensor cores, the QK^T logits  */
+/* and the softmax kept in high precision; GQA with 16 query heads sharing   */
+/* 4 KV heads; 512-token sliding window, full causal on some layers).        */
+/* ------------------------------------------------------------------------ */
+/* Element (b, i, h, d) of Q is Q[(b*S + i)*ldq + h*D + d]; K, V, O alike.
+ * Query head h reads KV head h / (Hq / Hkv).  Row i attends to keys
+ * j in [lo, i], lo = max(0, i - window + 1) (window <= 0: lo = 0).
+ * Readings (the pages fix none of these steps):
+ *   s_ij = CanonSum_d(q_id * k_jd) * c,  c = 1 / sqrt(D) (each op rounded);
+ *   m_i  = max over the row's keys (the first key, then strictly larger ones);
+ *   p_ij = E(s_ij - m_i) for the row's keys, +0 for every other key;
+ *   l_i  = CanonSum over the whole key axis j = 0..S-1 of p_ij;
+ *   q_p  = clamp(rne(p * 127), 0, 127);  q_v = the LSQ quantiser with step s_v;
+ *   acc_id = sum_j q_p,ij * q_v,jd       (exact integers);
+ *   O_id = (fl(acc_id) * s_v) / (l_i * 127).                                 */
+int or_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
+                int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
+                float* O, int64_t ldo) {
+    fp_env_default();
+    e_init();
+    if (Hkv <= 0 || Hq % Hkv != 0) return -1;
+    const int64_t group = Hq / Hkv;
+    const float c = or_div(1.0f, or_sqrt((float)(double)D));
+    /* quantised V, [B, S, Hkv, D] */
+    int8_t* qv = (int8_t*)malloc((size_t)(B * S * Hkv * D > 0 ? B * S * Hkv * D : 1));
+    PARALLEL_BEGIN
+    #pragma omp for schedule(static)
+    for (int64_t r = 0; r < B * S; ++r)
+        for (int64_t h = 0; h < Hkv; ++h)
+            for (int64_t d = 0; d < D; ++d) {
+                uint8_t in;
+                quantize_one(V[r * ldv + h * D + d], s_v, &qv[(r * Hkv + h) * D + d], &in);
+            }
+    PARALLEL_END
+    int bad = 0;
+    PARALLEL_BEGIN
+    float* prod = (float*)malloc(sizeof(float) * (size_t)D);
+    float* p = (float*)malloc(sizeof(float) * (size_t)S);
+    float* s = (float*)malloc(sizeof(float) * (size_t)S);
+    float* scratch = (float*)malloc(sizeof(float) * (size_t)(S / OR_BLOCK + D / OR_BLOCK + 2));
+    int64_t* acc = (int64_t*)malloc(sizeof(int64_t) * (size_t)D);
+    #pragma omp for schedule(dynamic, 16)
+    for (int64_t row = 0; row < B * S * Hq; ++row) {
+        const int64_t h = row % Hq, i = (row / Hq) % S, b = row / (Hq * S);
+        const int64_t hk = h / group;
+        const int64_t lo = (window > 0 && i - window + 1 > 0) ? i - window + 1 : 0;
+        const float* q = Q + (b * S + i) * ldq + h * D;
+        for (int64_t j = lo; j <= i; ++j) {
+            const float* k = K + (b * S + j) * ldk + hk * D;
+            for (int64_t d = 0; d < D; ++d) prod[d] = or_mul(q[d], k[d]);
+            s[j] = or_mul(canon_sum(prod, D, scratch), c);
+        }
+        float m = s[lo];
+        for (int64_t j = lo + 1; j <= i; ++j)
+            if (s[j] > m) m = s[j];
+        for (int64_t j = 0; j < S; ++j) p[j] = 0.0f;
+        for (int64_t j = lo; j <= i; ++j) p[j] = or_exp(or_sub(s[j], m));
+        const float l = canon_sum(p, S, scratch);
+        for (int64_t d = 0; d < D; ++d) acc[d] = 0;
+        for (int64_t j = lo; j <= i; ++j) {
+            float r = or_rne(or_mul(p[j], 127.0f));
+            if (r > 127.0f) r = 127.0f;
+            if (r < 0.0f) r = 0.0f;
+            const int64_t qp = (int64_t)r;
+            const int8_t* vq = qv + ((b * S + j) * Hkv + hk) * D;
+            for (int64_t d = 0; d < D; ++d) acc[d] += qp * (int64_t)vq[d];
+        }
+        const float t = or_mul(l, 127.0f);
+        float* o = O + (b * S + i) * ldo + h * D;
+        for (int64_t d = 0; d < D; ++d) {
+            if (acc[d] > INT32_MAX || acc[d] < INT32_MIN) {
+                #pragma omp atomic write
+                bad = 1;
+            }
+            o[d] = or_div(or_mul(or_i2f((int32_t)acc[d]), s_v), t);
+        }
+    }
+    free(prod); free(p); free(s); free(scratch); free(acc);
+    PARALLEL_END
+    free(qv);
+    return bad ? -2 : 0;
+}
+
 void or_set_threads(int n) {
 #ifdef _OPENMP
     if (n > 0) omp_set_num_threads(n);
