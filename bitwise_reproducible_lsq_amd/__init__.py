@@ -59,6 +59,7 @@ _SIGS = {
     "brl_state_hash": (i32, [P, P, i32, P, P, sz, P]),
     "brl_adamw_scalars_for_step": (i32, [i64, C.c_double, P, P]),
     "adamw_step": (i32, [P, P, P, P, i64, P, i32, P]),
+    "attn_fwd": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64, P]),
     "brl_set_tuning": (i64, [i32, i64]),
     "brl_status_string": (C.c_char_p, [i32]),
     "brl_last_error": (C.c_char_p, []),
@@ -286,6 +287,38 @@ def adamw_step(p: torch.Tensor, g: torch.Tensor, m: torch.Tensor, v: torch.Tenso
             raise ValueError("p, g, m, v must have the same size")
     _check(lib().adamw_step(_ptr(p), _ptr(g), _ptr(m), _ptr(v), p.numel(), C.byref(sc), 1 if decay else 0,
                             _stream(stream)))
+
+
+def _heads_view(t: torch.Tensor, name: str):
+    """[B, S, H, D] float32 view on the GPU whose (H, D) part is dense and
+    whose rows are evenly spaced; returns (pointer, row stride)."""
+    _f32(t, name)
+    if not t.is_cuda or t.dim() != 4:
+        raise ValueError(f"{name} must be a [B, S, H, D] GPU tensor")
+    B, S, H, D = t.shape
+    if t.stride(3) != 1 or (H > 1 and t.stride(2) != D) or (B > 1 and t.stride(0) != S * t.stride(1)):
+        raise ValueError(f"{name}: heads and head dimension must be dense, rows evenly spaced")
+    return C.c_void_p(t.data_ptr()), t.stride(1) if S > 1 else H * D
+
+
+def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, window: int, s_v: float,
+             O: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Attention with int8 P.V (attn_fwd).  Q [B, S, Hq, D], K and V
+    [B, S, Hkv, D], views with evenly spaced rows (column slices of the QKV
+    projection output work); returns O [B, S, Hq, D]."""
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    if K.shape != (B, S, Hkv, D) or V.shape != K.shape:
+        raise ValueError("Q, K, V shapes disagree")
+    if O is None:
+        O = torch.empty((B, S, Hq, D), dtype=torch.float32, device=Q.device)
+    q, ldq = _heads_view(Q, "Q")
+    k, ldk = _heads_view(K, "K")
+    v, ldv = _heads_view(V, "V")
+    o, ldo = _heads_view(O, "O")
+    _check(lib().attn_fwd(q, k, v, B, S, Hq, Hkv, D, ldq, ldk, ldv, int(window), float(s_v), o, ldo,
+                          _stream(stream)))
+    return O
 
 
 def probe_f32(op: str, a: torch.Tensor, b: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

@@ -484,6 +484,26 @@ brl_status adamw_step(float* p, const float* g, float* m, float* v, int64_t n, c
     return check_hip(launch_adamw(p, g, m, v, n, *sc, decay != 0, static_cast<hipStream_t>(stream)), "AdamW");
 }
 
+brl_status attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
+                    int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
+                    float* O, int64_t ldo, void* stream) {
+    if (B < 0 || S < 0) return fail(BRL_ESHAPE, "attn_fwd: B, S must be >= 0");
+    if (D != 128) return fail(BRL_ESHAPE, "attn_fwd: head dimension must be 128");
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return fail(BRL_ESHAPE, "attn_fwd: Hq must be a positive multiple of Hkv");
+    if (S > 133143) return fail(BRL_ESHAPE, "attn_fwd: S too large for int32 P.V accumulators");
+    if (ldq < Hq * D || ldo < Hq * D || ldk < Hkv * D || ldv < Hkv * D)
+        return fail(BRL_ESHAPE, "attn_fwd: row stride smaller than heads * D");
+    if ((ldq | ldk | ldv | ldo) & 3) return fail(BRL_EINVAL, "attn_fwd: row strides must be multiples of 4");
+    if (B * S == 0) return BRL_OK;
+    if (!Q || !K || !V || !O) return fail(BRL_EINVAL, "attn_fwd: null tensor");
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    if (!al16(Q) || !al16(K) || !al16(V) || !al16(O)) return fail(BRL_EINVAL, "attn_fwd: pointers must be 16-byte aligned");
+    if (!(s_v == s_v)) return fail(BRL_EINVAL, "attn_fwd: s_v is NaN");
+    return check_hip(launch_attn_fwd(Q, K, V, B, S, Hq, Hkv, ldq, ldk, ldv, window, s_v, O, ldo, exp_constants(),
+                                     static_cast<hipStream_t>(stream)),
+                     "attention");
+}
+
 int64_t brl_set_tuning(int32_t knob, int64_t value) {
     if (knob < 0 || knob > 3) return -1;
     if (knob == BRL_TUNE_BWD_CHUNK_LOG2 && value > 7) value = 7;

@@ -1,0 +1,299 @@
+// attn.hip -- attention with int8 P.V, high-precision logits and softmax.
+//
+// Open-1B summary on onedev.kr, "Use", attention paragraph: inside flash
+// attention the P.V product runs on int8 matrix units while the QK^T logits
+// and the softmax stay in high precision; grouped-query attention (16 query
+// heads over 4 KV heads), a 512-token sliding window with full causal
+// attention on some layers.  The pages fix no step of the arithmetic; this
+// library's reading (every binary32 operation rounded on its own, FTZ):
+//   s_ij = CanonSum_d(q_id * k_jd) * c,       c = 1 / sqrt(D)
+//   m_i  = max of s_ij over the row's keys j in [lo_i, i]
+//   p_ij = E(s_ij - m_i) on the row's keys, +0 on every other key
+//   l_i  = CanonSum of p_ij over the whole key axis j = 0 .. S-1
+//   q_p  = clamp(rne(p * 127), 0, 127),  q_v = LSQ quantiser with step s_v
+//   O_id = (fl(sum_j q_p,ij * q_v,jd) * s_v) / (l_i * 127)
+// with E the library's own binary32 exp.  The integer product is exact and
+// order-free, so only the logits and l_i carry an order, and both are fixed
+// by absolute positions (d, and the key index j), not by tiles.
+//
+// One workgroup per (batch, query head, block of 64 queries); two passes over
+// the 64-key tiles that meet the rows' key ranges:
+//   pass 1: logits (VALU, 4 x 4 per thread, d-blocks of 32 summed left to
+//           right then as a pairwise tree) -> row maxima (order-free);
+//   pass 2: the same logits -> p -> the 32-key block sums (one thread per
+//           row, sequential) pushed on the row's binary-counter stack at their
+//           absolute block index; q_p and q_v staged as int8 in LDS and
+//           multiplied on v_mfma_i32_32x32x32_i8 into int32 accumulators.
+// Blocks before the first real one are +0 subtrees (the stack starts zeroed)
+// and merging with +0 is exact, so this is CanonSum over the whole axis.
+#include "internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace brl {
+
+typedef int v4i_a __attribute__((ext_vector_type(4)));
+typedef int v16i_a __attribute__((ext_vector_type(16)));
+
+constexpr int kAD = 128;          // head dimension
+constexpr int kAQ = 64;           // queries per workgroup
+constexpr int kAK = 64;           // keys per tile
+constexpr int kAPitch = kAK + 1;  // fp32 p tile row pitch
+constexpr int kAStack = 16;       // stack levels: up to 2^16 key blocks
+
+struct AttnArgs {
+    const float* Q;
+    const float* K;
+    const float* V;
+    float* O;
+    int64_t S, Hq, Hkv, ldq, ldk, ldv, ldo, window;
+    float c, s_v;
+    ExpConsts ek;
+};
+
+struct AttnSmem {
+    float qs[kAD][kAQ];             // Q tile, d-major
+    float ks[kAD][kAK];             // K tile, d-major
+    float pf[kAQ][kAPitch];         // p tile (pass 2); partial maxima (pass 1)
+    int8_t pq[kAQ][kAK];            // q_p, rows of 64 keys, 16-byte chunks swizzled
+    int8_t vq[kAD][kAK];            // q_v transposed: row d holds 64 keys, swizzled
+    float st[kAQ][kAStack];         // per-row binary-counter stacks
+    float rowmax[kAQ];
+    float rowdiv[kAQ];              // l_i * 127
+};
+
+__device__ __forceinline__ int aswz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+
+// 16 logits of this thread: rows 4ti..4ti+3, keys 4tj..4tj+3 of the tile
+__device__ __forceinline__ void attn_logits(const AttnSmem& sm, int ti, int tj, float c, float s[4][4]) {
+    float b01[4][4], b2[4][4], cur[4][4];
+#pragma unroll
+    for (int blk = 0; blk < kAD / 32; ++blk) {
+#pragma unroll 4
+        for (int dd = 0; dd < 32; ++dd) {
+            const int d = blk * 32 + dd;
+            const vf4 a = *reinterpret_cast<const vf4*>(&sm.qs[d][4 * ti]);
+            const vf4 b = *reinterpret_cast<const vf4*>(&sm.ks[d][4 * tj]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    const float pr = f_mul(a[x], b[y]);
+                    cur[x][y] = dd == 0 ? pr : f_add(cur[x][y], pr);
+                }
+        }
+        // tree over the four d-blocks: (b0 + b1) + (b2 + b3)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                if (blk == 0) b01[x][y] = cur[x][y];
+                if (blk == 1) b01[x][y] = f_add(b01[x][y], cur[x][y]);
+                if (blk == 2) b2[x][y] = cur[x][y];
+                if (blk == 3) s[x][y] = f_mul(f_add(b01[x][y], f_add(b2[x][y], cur[x][y])), c);
+            }
+    }
+}
+
+// 64 rows (rows_left of them real) x 128 floats of head `head` into dst[d][row]
+__device__ __forceinline__ void attn_load_kt(const float* src, int64_t ld, int64_t row0, int64_t rows_left,
+                                             int64_t head, float (*dst)[kAK]) {
+    for (int e = threadIdx.x; e < kAK * (kAD / 4); e += 256) {
+        const int r = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
+        vf4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (r < rows_left) v = *reinterpret_cast<const vf4*>(src + (row0 + r) * ld + head * kAD + d4);
+        dst[d4 + 0][r] = v.x;
+        dst[d4 + 1][r] = v.y;
+        dst[d4 + 2][r] = v.z;
+        dst[d4 + 3][r] = v.w;
+    }
+}
+
+__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ti = tid >> 4, tj = tid & 15;
+
+    // block -> (b, h, query block) in 32-bit unsigned arithmetic (the host
+    // checks that the grid fits)
+    const unsigned nqb = (unsigned)((a.S + kAQ - 1) / kAQ), hq = (unsigned)a.Hq;
+    const unsigned qb = blockIdx.x % nqb;
+    const unsigned bh = blockIdx.x / nqb;
+    const int64_t h = bh % hq;
+    const int64_t b = bh / hq;
+    const int64_t hk = (unsigned)h / (hq / (unsigned)a.Hkv);
+    const int64_t q0 = qb * kAQ;
+    const int64_t qrows = a.S - q0 < kAQ ? a.S - q0 : kAQ;
+    const int64_t base = b * a.S;                    // first row of this batch entry
+
+    // key range of the block: [klo, khi]
+    const int64_t klo = a.window > 0 ? (q0 - a.window + 1 > 0 ? q0 - a.window + 1 : 0) : 0;
+    const int64_t khi = q0 + qrows - 1;
+    const int64_t kt0 = klo / kAK, kt1 = khi / kAK;
+
+    attn_load_kt(a.Q, a.ldq, base + q0, qrows, h, sm.qs);
+    for (int e = tid; e < kAQ * kAStack; e += 256) sm.st[e / kAStack][e % kAStack] = 0.0f;
+
+    auto allowed = [&](int64_t i, int64_t j) {
+        const int64_t lo = a.window > 0 ? i - a.window + 1 : 0;
+        return i < a.S && j <= i && j >= lo;
+    };
+
+    // ---- pass 1: row maxima ----
+    float mx[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) mx[x] = __int_as_float(0xff800000);
+    for (int64_t kt = kt0; kt <= kt1; ++kt) {
+        const int64_t j0 = kt * kAK;
+        __syncthreads();
+        attn_load_kt(a.K, a.ldk, base + j0, a.S - j0, hk, sm.ks);
+        __syncthreads();
+        float s[4][4];
+        attn_logits(sm, ti, tj, a.c, s);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y)
+                if (allowed(q0 + 4 * ti + x, j0 + 4 * tj + y) && s[x][y] > mx[x]) mx[x] = s[x][y];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 4; ++x) sm.pf[4 * ti + x][tj] = mx[x];
+    __syncthreads();
+    if (tid < kAQ) {
+        float m = sm.pf[tid][0];
+        for (int u = 1; u < 16; ++u) m = sm.pf[tid][u] > m ? sm.pf[tid][u] : m;
+        sm.rowmax[tid] = m;
+    }
+
+    // ---- pass 2: p, row sums, int8 P.V ----
+    const Quantizer qz(a.s_v);
+    const int mt = wave & 1, nt0 = (wave >> 1) * 2;
+    v16i_a acc[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[n][r] = 0;
+    const int frow = lane & 31, fchunk = lane >> 5;
+    for (int64_t kt = kt0; kt <= kt1; ++kt) {
+        const int64_t j0 = kt * kAK;
+        __syncthreads();
+        attn_load_kt(a.K, a.ldk, base + j0, a.S - j0, hk, sm.ks);
+        // V tile -> q_v, stored transposed (row d holds the tile's 64 keys)
+        for (int e = tid; e < kAK * (kAD / 4); e += 256) {
+            const int r = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
+            vf4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (j0 + r < a.S) v = *reinterpret_cast<const vf4*>(a.V + (base + j0 + r) * a.ldv + hk * kAD + d4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                bool in;
+                const int q = j0 + r < a.S ? qz.q(v[u], &in) : 0;
+                const int d = d4 + u;
+                sm.vq[d][16 * aswz(d, r >> 4) + (r & 15)] = (int8_t)q;
+            }
+        }
+        __syncthreads();
+        float s[4][4];
+        attn_logits(sm, ti, tj, a.c, s);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int i = 4 * ti + x;
+            const float m = sm.rowmax[i];
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                const int j = 4 * tj + y;
+                const float p = allowed(q0 + i, j0 + j) ? own_exp(f_sub(s[x][y], m), a.ek) : 0.0f;
+                sm.pf[i][j] = p;
+                float r = f_rne(f_mul(p, 127.0f));
+                r = r > 127.0f ? 127.0f : (r < 0.0f ? 0.0f : r);
+                sm.pq[i][16 * aswz(i, j >> 4) + (j & 15)] = (int8_t)(int)r;
+            }
+        }
+        __syncthreads();
+        // row sums of the tile's two 32-key blocks, pushed at their absolute index
+        if (tid < kAQ) {
+#pragma unroll
+            for (int blk = 0; blk < kAK / 32; ++blk) {
+                float x = sm.pf[tid][32 * blk];
+                for (int j = 1; j < 32; ++j) x = f_add(x, sm.pf[tid][32 * blk + j]);
+                unsigned cnt = (unsigned)((j0 >> 5) + blk);
+                int L = 0;
+                while (cnt & 1u) {
+                    x = f_add(sm.st[tid][L], x);
+                    cnt >>= 1;
+                    ++L;
+                }
+                sm.st[tid][L] = x;
+            }
+        }
+        // P.V on the matrix cores: this wave's 32 rows x 64 columns, k = 64 keys
+#pragma unroll
+        for (int ks = 0; ks < kAK / 32; ++ks) {
+            const int chunk = fchunk + 2 * ks;
+            const int ar = mt * 32 + frow;
+            const v4i_a A = *reinterpret_cast<const v4i_a*>(&sm.pq[ar][16 * aswz(ar, chunk)]);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int br = (nt0 + n) * 32 + frow;
+                const v4i_a Bf = *reinterpret_cast<const v4i_a*>(&sm.vq[br][16 * aswz(br, chunk)]);
+                acc[n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, Bf, acc[n], 0, 0, 0);
+            }
+        }
+    }
+    __syncthreads();
+    // l_i: final merge of the stack at the absolute block count
+    if (tid < kAQ) {
+        const unsigned count = (unsigned)(((kt1 + 1) * kAK) >> 5);
+        float root = 0.0f;
+        bool have = false;
+        for (int L = 0; L < kAStack; ++L)
+            if (count & (1u << L)) {
+                root = have ? f_add(sm.st[tid][L], root) : sm.st[tid][L];
+                have = true;
+            }
+        sm.rowdiv[tid] = f_mul(root, 127.0f);
+    }
+    __syncthreads();
+    // O = (fl(acc) * s_v) / (l * 127)
+    const int col_l = lane & 31, row_q = (lane >> 5) * 4;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = mt * 32 + (r >> 2) * 8 + row_q + (r & 3);
+            const int d = (nt0 + n) * 32 + col_l;
+            if (i < qrows) {
+                const float y = f_div(f_mul((float)acc[n][r], a.s_v), sm.rowdiv[i]);
+                a.O[(base + q0 + i) * a.ldo + h * kAD + d] = y;
+            }
+        }
+}
+
+size_t attn_smem_bytes() { return sizeof(AttnSmem); }
+
+hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
+                           int64_t Hkv, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
+                           float* O, int64_t ldo, const ExpConsts& ek, hipStream_t st) {
+    if (B == 0 || S == 0) return hipSuccess;
+    AttnArgs a;
+    a.Q = Q; a.K = K; a.V = V; a.O = O;
+    a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.window = window;
+    // c = fl(1 / fl(sqrt(D))): both binary64 results are rounded once more to
+    // binary32, which is innocuous for sqrt and division (53 >= 2 * 24 + 2)
+    a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
+    a.s_v = s_v;
+    a.ek = ek;
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnSmem));
+        attr = true;
+    }
+    const int64_t blocks = B * Hq * ceil_div(S, kAQ);
+    if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)blocks), dim3(256), sizeof(AttnSmem), st, a);
+    return hipGetLastError();
+}
+
+}  // namespace brl

@@ -149,4 +149,9 @@ hipError_t launch_probe(int op, const float* a, const float* b, float* out, int6
 
 ExpConsts exp_constants();
 
+// ---- attention (int8 P.V) ----------------------------------------------------
+hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
+                           int64_t Hkv, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
+                           float* O, int64_t ldo, const ExpConsts& ek, hipStream_t st);
+
 }  // namespace brl

@@ -236,6 +236,33 @@ BRL_API brl_status brl_adamw_scalars_for_step(int64_t step, double tokens, const
 BRL_API brl_status adamw_step(float* p, const float* g, float* m, float* v, int64_t n,
                               const brl_adamw_scalars* sc, int32_t decay, void* stream);
 
+/*
+ * Attention with int8 P.V (onedev.kr summary, "Use", attention paragraph:
+ * the P.V product of flash attention on int8 matrix units, QK^T logits and
+ * softmax in high precision; grouped-query heads; causal, with a sliding
+ * window on most layers).  The pages fix no step of the arithmetic; this
+ * library's reading, every binary32 operation rounded on its own (FTZ):
+ *   s_ij = CanonSum_d(q_id * k_jd) * c,  c = fl(1 / fl(sqrt(D)))
+ *   m_i  = max_j s_ij over the row's keys j in [lo_i, i],
+ *          lo_i = max(0, i - window + 1) (window <= 0: lo_i = 0)
+ *   p_ij = E(s_ij - m_i) on the row's keys, +0 on all other keys
+ *          (E: the library's binary32 exp, as in the SwiGLU epilogue)
+ *   l_i  = CanonSum_j p_ij over the whole key axis j = 0 .. S-1
+ *   q_p  = clamp(rne(p * 127), 0, 127); q_v = LSQ quantiser, step s_v
+ *   O_id = (fl(sum_j q_p,ij * q_v,jd) * s_v) / (l_i * 127)
+ * Layout: element (b, i, h, d) of Q at Q[(b*S + i)*ldq + h*D + d] (K, V, O
+ * alike, with Hkv heads for K and V); query head h reads KV head
+ * h / (Hq / Hkv).  The QKV projection's output [B*S, (Hq + 2*Hkv)*D] serves
+ * directly: Q, K, V at column offsets 0, Hq*D, (Hq + Hkv)*D, ld = row width.
+ * D must be 128; Hq a positive multiple of Hkv; S <= 133143 (int32 P.V
+ * accumulators); every ld a multiple of 4 and >= heads*D; Q, K, V, O device
+ * pointers 16-byte aligned; O must not overlap Q, K or V.  Inputs must be
+ * finite.  No workspace; asynchronous on `stream`.
+ */
+BRL_API brl_status attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
+                            int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window,
+                            float s_v, float* O, int64_t ldo, void* stream);
+
 /* Conformance probe of the device's binary32 operations, as the kernels use
  * them: out[i] = op(a[i], b[i]) for op 0 add, 1 sub, 2 mul, 3 div, 4 sqrt (a),
  * 5 int32 bits of a -> float, 6 round-to-nearest-even integral (a),

@@ -1,0 +1,93 @@
+"""GPU parity of attn_fwd (int8 P.V attention) against the CPU oracle, bit
+for bit: ragged sequence lengths, sliding windows shorter and longer than the
+query block, full causal attention, grouped-query head counts, column slices
+of a QKV projection output as Q/K/V, and a row-stride-only O view."""
+import numpy as np
+import pytest
+import torch
+
+import bitwise_reproducible_lsq_amd as brl
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def _bits(x):
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(x, np.float32).view(np.uint32)
+
+
+def assert_bitwise(got, want, what):
+    g, w = _bits(got), _bits(want)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    bad = np.flatnonzero(g.ravel() != w.ravel())
+    if bad.size:
+        i = bad[0]
+        raise AssertionError(f"{what}: {bad.size} of {g.size} differ; first at flat {i} "
+                             f"(index {np.unravel_index(i, g.shape)}): got {g.ravel()[i]:#010x} "
+                             f"want {w.ravel()[i]:#010x}")
+
+
+def _inputs(B, S, Hq, Hkv, seed, scale=1.0):
+    g = np.random.default_rng(seed)
+    Q = (g.standard_normal((B, S, Hq, D)) * scale).astype(np.float32)
+    K = g.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    V = g.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    return Q, K, V
+
+
+CASES = [
+    # B, S, Hq, Hkv, window, s_v
+    (1, 1, 1, 1, 0, 0.05),
+    (1, 64, 2, 1, 0, 0.05),
+    (2, 200, 4, 2, 0, 0.05),
+    (2, 200, 4, 2, 64, 0.05),
+    (1, 130, 8, 1, 37, 0.0371),
+    (1, 150, 4, 4, 1, 0.05),
+    (1, 100, 4, 2, 500, 0.05),        # window longer than the sequence
+    (1, 333, 16, 4, 130, 0.05),
+]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,window,s_v", CASES)
+def test_attention_parity(B, S, Hq, Hkv, window, s_v):
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=S + 7 * Hq + window, scale=0.3)
+    O = brl.attn_fwd(torch.from_numpy(Q).cuda(), torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(),
+                     window, s_v)
+    torch.cuda.synchronize()
+    assert_bitwise(O, oracle.attn_fwd(Q, K, V, window, s_v), f"O (B={B} S={S} Hq={Hq} Hkv={Hkv} w={window})")
+
+
+def test_attention_on_qkv_projection_slices():
+    """Q, K, V as column slices of one [B*S, (Hq + 2 Hkv) * D] buffer (the
+    QKV projection's output), O written into a wider buffer."""
+    B, S, Hq, Hkv, window, s_v = 2, 190, 4, 1, 96, 0.05
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=3, scale=0.3)
+    Y = np.concatenate([Q.reshape(B * S, -1), K.reshape(B * S, -1), V.reshape(B * S, -1)], axis=1)
+    Yd = torch.from_numpy(np.ascontiguousarray(Y)).cuda()
+    q = Yd[:, :Hq * D].view(B, S, Hq, D)
+    k = Yd[:, Hq * D:(Hq + Hkv) * D].view(B, S, Hkv, D)
+    v = Yd[:, (Hq + Hkv) * D:].view(B, S, Hkv, D)
+    wide = torch.full((B * S, Hq * D + 64), 7.0, device="cuda")
+    O = wide[:, :Hq * D].view(B, S, Hq, D)
+    brl.attn_fwd(q, k, v, window, s_v, O=O)
+    torch.cuda.synchronize()
+    assert_bitwise(O, oracle.attn_fwd(Q, K, V, window, s_v), "O (QKV slices)")
+    assert torch.all(wide[:, Hq * D:] == 7.0)
+
+
+def test_attention_large_logits_and_repeat():
+    """Logits spread over tens of units (most p underflow to small values or
+    +0) and two calls give the same bits."""
+    B, S, Hq, Hkv, window, s_v = 1, 257, 4, 2, 0, 0.05
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=9, scale=2.0)
+    args = [torch.from_numpy(t).cuda() for t in (Q, K, V)]
+    O1 = brl.attn_fwd(*args, window, s_v)
+    O2 = brl.attn_fwd(*args, window, s_v)
+    torch.cuda.synchronize()
+    want = oracle.attn_fwd(Q, K, V, window, s_v)
+    assert_bitwise(O1, want, "O (large logits)")
+    assert_bitwise(O2, want, "O (repeat)")

@@ -222,3 +222,24 @@ def test_adamw_rejects_bad_arguments_without_launching():
     assert L.adamw_step(C.c_void_p(0x10001), p, p, p, 4, C.byref(sc), 1, None) == brl.BRL_EINVAL
     assert L.brl_adamw_scalars_for_step(0, 1.0, None, C.byref(sc)) == brl.BRL_EINVAL
     assert L.brl_adamw_scalars_for_step(1, float("nan"), None, C.byref(sc)) == brl.BRL_EINVAL
+
+
+def test_attention_rejects_bad_arguments_without_launching():
+    L = brl.lib()
+    p = C.c_void_p(0x10000)
+    ok = dict(B=1, S=64, Hq=4, Hkv=2, D=128, ldq=512, ldk=256, ldv=256, ldo=512)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.attn_fwd(kw.get("Q", p), p, p, a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["ldq"], a["ldk"],
+                          a["ldv"], 0, 0.05, kw.get("O", p), a["ldo"], None)
+
+    assert call(D=64) == brl.BRL_ESHAPE
+    assert call(Hq=3) == brl.BRL_ESHAPE
+    assert call(Hkv=0) == brl.BRL_ESHAPE
+    assert call(S=133144) == brl.BRL_ESHAPE
+    assert call(ldq=500) == brl.BRL_ESHAPE
+    assert call(ldk=258) == brl.BRL_EINVAL
+    assert call(Q=None) == brl.BRL_EINVAL
+    assert call(O=C.c_void_p(0x10004)) == brl.BRL_EINVAL
+    assert call(S=0) == brl.BRL_OK            # nothing to do, nothing launched
