@@ -20,12 +20,16 @@
 // the 64-key tiles that meet the rows' key ranges:
 //   pass 1: logits (VALU, 4 x 4 per thread, d-blocks of 32 summed left to
 //           right then as a pairwise tree) -> row maxima (order-free);
-//   pass 2: the same logits -> p -> the 32-key block sums (one thread per
-//           row, sequential) pushed on the row's binary-counter stack at their
-//           absolute block index; q_p and q_v staged as int8 in LDS and
-//           multiplied on v_mfma_i32_32x32x32_i8 into int32 accumulators.
-// Blocks before the first real one are +0 subtrees (the stack starts zeroed)
+//   pass 2: the same logits -> p -> the 32-key block sums, each a left-to-
+//           right chain through the 8 lanes that hold its keys (DPP shifts
+//           within a 16-lane row); a tile's two blocks are a complete pair
+//           (their absolute indices are 2kt, 2kt+1), so their sum is pushed on
+//           the row's binary-counter stack of pairs at index kt; q_p and q_v
+//           staged as int8 in LDS and multiplied on v_mfma_i32_32x32x32_i8
+//           into int32 accumulators.
+// Pairs before the first real one are +0 subtrees (the stack starts zeroed)
 // and merging with +0 is exact, so this is CanonSum over the whole axis.
+// LDS is kept under 80 KB so that two workgroups share a CU.
 #include "internal.hpp"
 
 #pragma clang fp contract(off)
@@ -38,8 +42,7 @@ typedef int v16i_a __attribute__((ext_vector_type(16)));
 constexpr int kAD = 128;          // head dimension
 constexpr int kAQ = 64;           // queries per workgroup
 constexpr int kAK = 64;           // keys per tile
-constexpr int kAPitch = kAK + 1;  // fp32 p tile row pitch
-constexpr int kAStack = 16;       // stack levels: up to 2^16 key blocks
+constexpr int kAStack = 12;       // pair-stack levels: up to 2^12 key tiles
 
 struct AttnArgs {
     const float* Q;
@@ -54,13 +57,18 @@ struct AttnArgs {
 struct AttnSmem {
     float qs[kAD][kAQ];             // Q tile, d-major
     float ks[kAD][kAK];             // K tile, d-major
-    float pf[kAQ][kAPitch];         // p tile (pass 2); partial maxima (pass 1)
-    int8_t pq[kAQ][kAK];            // q_p, rows of 64 keys, 16-byte chunks swizzled
-    int8_t vq[kAD][kAK];            // q_v transposed: row d holds 64 keys, swizzled
-    float st[kAQ][kAStack];         // per-row binary-counter stacks
+    union {
+        struct {
+            int8_t pq[kAQ][kAK];    // q_p, rows of 64 keys, 16-byte chunks swizzled
+            int8_t vq[kAD][kAK];    // q_v transposed: row d holds 64 keys, swizzled
+        } pv;
+        float pmax[kAQ][16];        // pass 1: partial row maxima
+    } u;
+    float st[kAQ][kAStack];         // per-row stacks of key-tile pair sums
     float rowmax[kAQ];
     float rowdiv[kAQ];              // l_i * 127
 };
+static_assert(sizeof(AttnSmem) <= 81920, "two workgroups per CU");
 
 __device__ __forceinline__ int aswz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
 
@@ -95,18 +103,34 @@ __device__ __forceinline__ void attn_logits(const AttnSmem& sm, int ti, int tj, 
     }
 }
 
-// 64 rows (rows_left of them real) x 128 floats of head `head` into dst[d][row]
+// 64 rows (rows_left of them real) x 128 floats of head `head` into
+// dst[d][row]: each item is 4 rows x 4 d, loaded as four 16-byte rows and
+// stored as four 16-byte columns
 __device__ __forceinline__ void attn_load_kt(const float* src, int64_t ld, int64_t row0, int64_t rows_left,
                                              int64_t head, float (*dst)[kAK]) {
-    for (int e = threadIdx.x; e < kAK * (kAD / 4); e += 256) {
-        const int r = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
-        vf4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (r < rows_left) v = *reinterpret_cast<const vf4*>(src + (row0 + r) * ld + head * kAD + d4);
-        dst[d4 + 0][r] = v.x;
-        dst[d4 + 1][r] = v.y;
-        dst[d4 + 2][r] = v.z;
-        dst[d4 + 3][r] = v.w;
+#pragma unroll
+    for (int it = 0; it < (kAK / 4) * (kAD / 4) / 256; ++it) {
+        const int e = threadIdx.x + 256 * it;
+        const int rq = e & 15, dq = e >> 4;
+        vf4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = 4 * rq + u;
+            v[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (r < rows_left) v[u] = *reinterpret_cast<const vf4*>(src + (row0 + r) * ld + head * kAD + 4 * dq);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            *reinterpret_cast<vf4*>(&dst[4 * dq + u][4 * rq]) = vf4{v[0][u], v[1][u], v[2][u], v[3][u]};
     }
+}
+
+// left-to-right running sum handed from lane to lane + 1 within a 16-lane row
+__device__ __forceinline__ float dpp_shr1(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_shr8(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
 }
 
 __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
@@ -159,11 +183,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int x = 0; x < 4; ++x) sm.pf[4 * ti + x][tj] = mx[x];
+    for (int x = 0; x < 4; ++x) sm.u.pmax[4 * ti + x][tj] = mx[x];
     __syncthreads();
     if (tid < kAQ) {
-        float m = sm.pf[tid][0];
-        for (int u = 1; u < 16; ++u) m = sm.pf[tid][u] > m ? sm.pf[tid][u] : m;
+        float m = sm.u.pmax[tid][0];
+        for (int u = 1; u < 16; ++u) m = sm.u.pmax[tid][u] > m ? sm.u.pmax[tid][u] : m;
         sm.rowmax[tid] = m;
     }
 
@@ -180,71 +204,102 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
         const int64_t j0 = kt * kAK;
         __syncthreads();
         attn_load_kt(a.K, a.ldk, base + j0, a.S - j0, hk, sm.ks);
-        // V tile -> q_v, stored transposed (row d holds the tile's 64 keys)
-        for (int e = tid; e < kAK * (kAD / 4); e += 256) {
-            const int r = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
-            vf4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (j0 + r < a.S) v = *reinterpret_cast<const vf4*>(a.V + (base + j0 + r) * a.ldv + hk * kAD + d4);
+        // V tile -> q_v, stored transposed (row d holds the tile's 64 keys):
+        // each item is 4 keys x 4 d, stored as four 4-byte key runs
+#pragma unroll
+        for (int it = 0; it < (kAK / 4) * (kAD / 4) / 256; ++it) {
+            const int e = tid + 256 * it;
+            const int rq = e & 15, dq = e >> 4;
+            vf4 v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                bool in;
-                const int q = j0 + r < a.S ? qz.q(v[u], &in) : 0;
-                const int d = d4 + u;
-                sm.vq[d][16 * aswz(d, r >> 4) + (r & 15)] = (int8_t)q;
+                const int64_t j = j0 + 4 * rq + u;
+                v[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
+                if (j < a.S) v[u] = *reinterpret_cast<const vf4*>(a.V + (base + j) * a.ldv + hk * kAD + 4 * dq);
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                uint32_t packed = 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    bool in;
+                    const int q = j0 + 4 * rq + u < a.S ? qz.q(v[u][w], &in) : 0;
+                    packed |= (uint32_t)(uint8_t)(int8_t)q << (8 * u);
+                }
+                const int d = 4 * dq + w, r = 4 * rq;
+                *reinterpret_cast<uint32_t*>(&sm.u.pv.vq[d][16 * aswz(d, r >> 4) + (r & 15)]) = packed;
             }
         }
         __syncthreads();
         float s[4][4];
         attn_logits(sm, ti, tj, a.c, s);
+        float pair[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int i = 4 * ti + x;
             const float m = sm.rowmax[i];
+            float p[4];
+            uint32_t packed = 0;
 #pragma unroll
             for (int y = 0; y < 4; ++y) {
                 const int j = 4 * tj + y;
-                const float p = allowed(q0 + i, j0 + j) ? own_exp(f_sub(s[x][y], m), a.ek) : 0.0f;
-                sm.pf[i][j] = p;
-                float r = f_rne(f_mul(p, 127.0f));
+                p[y] = allowed(q0 + i, j0 + j) ? own_exp(f_sub(s[x][y], m), a.ek) : 0.0f;
+                float r = f_rne(f_mul(p[y], 127.0f));
                 r = r > 127.0f ? 127.0f : (r < 0.0f ? 0.0f : r);
-                sm.pq[i][16 * aswz(i, j >> 4) + (j & 15)] = (int8_t)(int)r;
+                packed |= (uint32_t)(int)r << (8 * y);
             }
-        }
-        __syncthreads();
-        // row sums of the tile's two 32-key blocks, pushed at their absolute index
-        if (tid < kAQ) {
+            *reinterpret_cast<uint32_t*>(&sm.u.pv.pq[i][16 * aswz(i, tj >> 2) + 4 * (tj & 3)]) = packed;
+            // 32-key block sums: lanes tj = 8k .. 8k+7 hold block k's keys in
+            // order; the running sum walks through them one lane at a time
+            float run = 0.0f;
 #pragma unroll
-            for (int blk = 0; blk < kAK / 32; ++blk) {
-                float x = sm.pf[tid][32 * blk];
-                for (int j = 1; j < 32; ++j) x = f_add(x, sm.pf[tid][32 * blk + j]);
-                unsigned cnt = (unsigned)((j0 >> 5) + blk);
+            for (int t = 0; t < 8; ++t) {
+                const float in = dpp_shr1(run);
+                if ((tj & 7) == t) {
+                    float x0 = t == 0 ? p[0] : f_add(in, p[0]);
+                    x0 = f_add(x0, p[1]);
+                    x0 = f_add(x0, p[2]);
+                    run = f_add(x0, p[3]);
+                }
+            }
+            // lane tj = 15: block 1's sum; block 0's sits in lane tj = 7
+            pair[x] = f_add(dpp_shr8(run), run);
+        }
+        // push the tile's pair sum (complete subtree of blocks 2kt, 2kt+1)
+        if (tj == 15) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int i = 4 * ti + x;
+                float v = pair[x];
+                unsigned cnt = (unsigned)kt;
                 int L = 0;
                 while (cnt & 1u) {
-                    x = f_add(sm.st[tid][L], x);
+                    v = f_add(sm.st[i][L], v);
                     cnt >>= 1;
                     ++L;
                 }
-                sm.st[tid][L] = x;
+                sm.st[i][L] = v;
             }
         }
+        __syncthreads();
         // P.V on the matrix cores: this wave's 32 rows x 64 columns, k = 64 keys
 #pragma unroll
         for (int ks = 0; ks < kAK / 32; ++ks) {
             const int chunk = fchunk + 2 * ks;
             const int ar = mt * 32 + frow;
-            const v4i_a A = *reinterpret_cast<const v4i_a*>(&sm.pq[ar][16 * aswz(ar, chunk)]);
+            const v4i_a A = *reinterpret_cast<const v4i_a*>(&sm.u.pv.pq[ar][16 * aswz(ar, chunk)]);
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
                 const int br = (nt0 + n) * 32 + frow;
-                const v4i_a Bf = *reinterpret_cast<const v4i_a*>(&sm.vq[br][16 * aswz(br, chunk)]);
+                const v4i_a Bf = *reinterpret_cast<const v4i_a*>(&sm.u.pv.vq[br][16 * aswz(br, chunk)]);
                 acc[n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, Bf, acc[n], 0, 0, 0);
             }
         }
     }
     __syncthreads();
-    // l_i: final merge of the stack at the absolute block count
+    // l_i: final merge of the pair stack at the absolute tile count
     if (tid < kAQ) {
-        const unsigned count = (unsigned)(((kt1 + 1) * kAK) >> 5);
+        const unsigned count = (unsigned)(kt1 + 1);
         float root = 0.0f;
         bool have = false;
         for (int L = 0; L < kAStack; ++L)

@@ -66,6 +66,7 @@ def lib():
         "or_l2norm": (f32, [P, i64]),
         "or_clip": (f32, [P, i64, f32, f32, f32]),
         "or_attn_fwd": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64]),
+        "or_attn_fwd_rows": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64, P, i64]),
         "or_num_threads": (i32, []),
         "or_set_threads": (None, [i32]),
     }
@@ -326,6 +327,20 @@ def attn_fwd(Q, K, V, window: int, s_v: float) -> np.ndarray:
                            np.float32(s_v), _p(O), Hq * D)
     assert rc == 0, f"or_attn_fwd failed ({rc})"
     return O
+
+
+def attn_fwd_rows(Q, K, V, window: int, s_v: float, rows) -> np.ndarray:
+    """Rows of attn_fwd's output picked by flat id (b*S + i)*Hq + h:
+    returns [len(rows), D]."""
+    Q, K, V = _f32(Q), _f32(K), _f32(V)
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    rows = np.ascontiguousarray(rows, np.int64)
+    out = np.empty((rows.size, D), np.float32)
+    rc = lib().or_attn_fwd_rows(_p(Q), _p(K), _p(V), B, S, Hq, Hkv, D, Hq * D, Hkv * D, Hkv * D, int(window),
+                                np.float32(s_v), _p(rows), rows.size, _p(out), D)
+    assert rc == 0, f"or_attn_fwd_rows failed ({rc})"
+    return out
 
 
 def num_threads() -> int:

@@ -601,15 +601,45 @@ void or_adamw(float* p, const float* g, float* m, float* v, int64_t n, float bet
  *   q_p  = clamp(rne(p * 127), 0, 127);  q_v = the LSQ quantiser with step s_v;
  *   acc_id = sum_j q_p,ij * q_v,jd       (exact integers);
  *   O_id = (fl(acc_id) * s_v) / (l_i * 127).                                 */
-int or_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
-                int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
-                float* O, int64_t ldo) {
-    fp_env_default();
-    e_init();
-    if (Hkv <= 0 || Hq % Hkv != 0) return -1;
-    const int64_t group = Hq / Hkv;
-    const float c = or_div(1.0f, or_sqrt((float)(double)D));
-    /* quantised V, [B, S, Hkv, D] */
+/* One output row (b, i, h) of the attention: O row (D floats) into o. */
+static int attn_row(const float* Q, const float* K, const int8_t* qv, int64_t S, int64_t Hq, int64_t Hkv,
+                    int64_t D, int64_t ldq, int64_t ldk, int64_t window, float s_v, float c, int64_t b, int64_t i,
+                    int64_t h, float* prod, float* p, float* s, float* scratch, int64_t* acc, float* o) {
+    const int64_t hk = h / (Hq / Hkv);
+    const int64_t lo = (window > 0 && i - window + 1 > 0) ? i - window + 1 : 0;
+    const float* q = Q + (b * S + i) * ldq + h * D;
+    for (int64_t j = lo; j <= i; ++j) {
+        const float* k = K + (b * S + j) * ldk + hk * D;
+        for (int64_t d = 0; d < D; ++d) prod[d] = or_mul(q[d], k[d]);
+        s[j] = or_mul(canon_sum(prod, D, scratch), c);
+    }
+    float m = s[lo];
+    for (int64_t j = lo + 1; j <= i; ++j)
+        if (s[j] > m) m = s[j];
+    for (int64_t j = 0; j < S; ++j) p[j] = 0.0f;
+    for (int64_t j = lo; j <= i; ++j) p[j] = or_exp(or_sub(s[j], m));
+    const float l = canon_sum(p, S, scratch);
+    for (int64_t d = 0; d < D; ++d) acc[d] = 0;
+    for (int64_t j = lo; j <= i; ++j) {
+        float r = or_rne(or_mul(p[j], 127.0f));
+        if (r > 127.0f) r = 127.0f;
+        if (r < 0.0f) r = 0.0f;
+        const int64_t qp = (int64_t)r;
+        const int8_t* vq = qv + ((b * S + j) * Hkv + hk) * D;
+        for (int64_t d = 0; d < D; ++d) acc[d] += qp * (int64_t)vq[d];
+    }
+    const float t = or_mul(l, 127.0f);
+    int bad = 0;
+    for (int64_t d = 0; d < D; ++d) {
+        if (acc[d] > INT32_MAX || acc[d] < INT32_MIN) bad = 1;
+        o[d] = or_div(or_mul(or_i2f((int32_t)acc[d]), s_v), t);
+    }
+    return bad;
+}
+
+/* Quantised V, [B, S, Hkv, D]. */
+static int8_t* attn_quantize_v(const float* V, int64_t B, int64_t S, int64_t Hkv, int64_t D, int64_t ldv,
+                               float s_v) {
     int8_t* qv = (int8_t*)malloc((size_t)(B * S * Hkv * D > 0 ? B * S * Hkv * D : 1));
     PARALLEL_BEGIN
     #pragma omp for schedule(static)
@@ -620,6 +650,19 @@ int or_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64
                 quantize_one(V[r * ldv + h * D + d], s_v, &qv[(r * Hkv + h) * D + d], &in);
             }
     PARALLEL_END
+    return qv;
+}
+
+/* Rows given as flat ids (b*S + i)*Hq + h, or every row when rows == NULL
+ * (then out row r is O row r).  out: nrows x D floats, row pitch ldo. */
+int or_attn_fwd_rows(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
+                     int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
+                     const int64_t* rows, int64_t nrows, float* out, int64_t ldo) {
+    fp_env_default();
+    e_init();
+    if (Hkv <= 0 || Hq % Hkv != 0) return -1;
+    const float c = or_div(1.0f, or_sqrt((float)(double)D));
+    int8_t* qv = attn_quantize_v(V, B, S, Hkv, D, ldv, s_v);
     int bad = 0;
     PARALLEL_BEGIN
     float* prod = (float*)malloc(sizeof(float) * (size_t)D);
@@ -628,45 +671,29 @@ int or_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64
     float* scratch = (float*)malloc(sizeof(float) * (size_t)(S / OR_BLOCK + D / OR_BLOCK + 2));
     int64_t* acc = (int64_t*)malloc(sizeof(int64_t) * (size_t)D);
     #pragma omp for schedule(dynamic, 16)
-    for (int64_t row = 0; row < B * S * Hq; ++row) {
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t row = rows ? rows[r] : r;
         const int64_t h = row % Hq, i = (row / Hq) % S, b = row / (Hq * S);
-        const int64_t hk = h / group;
-        const int64_t lo = (window > 0 && i - window + 1 > 0) ? i - window + 1 : 0;
-        const float* q = Q + (b * S + i) * ldq + h * D;
-        for (int64_t j = lo; j <= i; ++j) {
-            const float* k = K + (b * S + j) * ldk + hk * D;
-            for (int64_t d = 0; d < D; ++d) prod[d] = or_mul(q[d], k[d]);
-            s[j] = or_mul(canon_sum(prod, D, scratch), c);
-        }
-        float m = s[lo];
-        for (int64_t j = lo + 1; j <= i; ++j)
-            if (s[j] > m) m = s[j];
-        for (int64_t j = 0; j < S; ++j) p[j] = 0.0f;
-        for (int64_t j = lo; j <= i; ++j) p[j] = or_exp(or_sub(s[j], m));
-        const float l = canon_sum(p, S, scratch);
-        for (int64_t d = 0; d < D; ++d) acc[d] = 0;
-        for (int64_t j = lo; j <= i; ++j) {
-            float r = or_rne(or_mul(p[j], 127.0f));
-            if (r > 127.0f) r = 127.0f;
-            if (r < 0.0f) r = 0.0f;
-            const int64_t qp = (int64_t)r;
-            const int8_t* vq = qv + ((b * S + j) * Hkv + hk) * D;
-            for (int64_t d = 0; d < D; ++d) acc[d] += qp * (int64_t)vq[d];
-        }
-        const float t = or_mul(l, 127.0f);
-        float* o = O + (b * S + i) * ldo + h * D;
-        for (int64_t d = 0; d < D; ++d) {
-            if (acc[d] > INT32_MAX || acc[d] < INT32_MIN) {
-                #pragma omp atomic write
-                bad = 1;
-            }
-            o[d] = or_div(or_mul(or_i2f((int32_t)acc[d]), s_v), t);
+        if (attn_row(Q, K, qv, S, Hq, Hkv, D, ldq, ldk, window, s_v, c, b, i, h, prod, p, s, scratch, acc,
+                     out + r * ldo)) {
+            #pragma omp atomic write
+            bad = 1;
         }
     }
     free(prod); free(p); free(s); free(scratch); free(acc);
     PARALLEL_END
     free(qv);
     return bad ? -2 : 0;
+}
+
+/* Attention with int8 P.V (onedev.kr summary, "Use", attention paragraph;
+ * readings above attn_row): every row, O row (b, i, h) at
+ * O[(b*S + i)*ldo + h*D]. */
+int or_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
+                int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
+                float* O, int64_t ldo) {
+    if (ldo != Hq * D) return -1;     /* rows are then O + row * D */
+    return or_attn_fwd_rows(Q, K, V, B, S, Hq, Hkv, D, ldq, ldk, ldv, window, s_v, NULL, B * S * Hq, O, D);
 }
 
 void or_set_threads(int n) {

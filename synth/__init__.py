@@ -25,7 +25,8 @@ import numpy as np
 
 S_X = 0.05          # activation step (one value for every layer; see the design doc readings)
 
-TENSOR_ID = {"X": 1, "W": 2, "dY": 3, "gate": 4, "lin": 5, "mask": 6, "sub": 7, "addend": 8}
+TENSOR_ID = {"X": 1, "W": 2, "dY": 3, "gate": 4, "lin": 5, "mask": 6, "sub": 7, "addend": 8,
+             "Q": 9, "K": 10, "V": 11}
 
 
 @dataclass(frozen=True)
@@ -122,6 +123,38 @@ def linear_inputs(case: LinearCase, M: int | None = None) -> LinearInputs:
     dY = normal(case.seed, "dY", (M, n_out), case.dy_std)
     dY = inject_subnormals(dY, case.seed, case.subnormal_frac)
     return LinearInputs(case, X, W, dY)
+
+
+@dataclass(frozen=True)
+class AttentionCase:
+    """Attention of one Open-1B layer at the per-GPU microbatch: 4 sequences
+    of 4096 tokens, 16 query heads over 4 KV heads of 128 (onedev.kr summary,
+    "Use"); window 512 on most layers, 0 (full causal) on every fifth and the
+    last.  Q and K ~ N(0, 1) stand in for the QK-normalised (unit RMS, no gain)
+    projections, V ~ N(0, 1)."""
+    name: str
+    seed: int
+    B: int = 4
+    S: int = 4096
+    Hq: int = 16
+    Hkv: int = 4
+    window: int = 512
+    s_v: float = S_X
+
+
+ATTENTION_CASES = {
+    "attn_window": AttentionCase("attn_window", 5),
+    "attn_causal": AttentionCase("attn_causal", 6, window=0),
+}
+
+
+def attention_inputs(case: AttentionCase, S: int | None = None):
+    """Host Q [B,S,Hq,128], K and V [B,S,Hkv,128] for an attention case."""
+    S = case.S if S is None else S
+    Q = normal(case.seed, "Q", (case.B, S, case.Hq, 128), 1.0)
+    K = normal(case.seed, "K", (case.B, S, case.Hkv, 128), 1.0)
+    V = normal(case.seed, "V", (case.B, S, case.Hkv, 128), 1.0)
+    return Q, K, V
 
 
 def small_case(name: str, seed: int, M: int, K: int, N: int, **kw) -> LinearCase:

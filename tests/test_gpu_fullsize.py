@@ -152,3 +152,23 @@ def test_replay_full_size():
     assert_bitwise(out, T, "clipped TreeFold")
     for r in range(R - 1):
         assert_bitwise(st.acc[r], A[r], f"A_{r}")
+
+
+@pytest.mark.parametrize("name", ["attn_window", "attn_causal"])
+def test_attention_full_size(name):
+    """One Open-1B layer's attention at the microbatch (4 x 4096 tokens, 16/4
+    heads): rows at the sequence start, at query-tile and window edges and
+    at the end, plus random rows, for several heads of both KV groups' ends."""
+    case = synth.ATTENTION_CASES[name]
+    Q, K, V = synth.attention_inputs(case)
+    O = brl.attn_fwd(_cuda(Q), _cuda(K), _cuda(V), case.window, case.s_v)
+    torch.cuda.synchronize()
+    Oh = O.cpu().numpy().reshape(-1, 128)
+    edges = [0, 1, 63, 64, 65, 511, 512, 513, 1023, 2048, case.S - 1]
+    rows = []
+    for b, h in [(0, 0), (1, 3), (2, 4), (3, 15)]:
+        for i in _sample(case.S, edges, 6, seed=b * 16 + h):
+            rows.append((b * case.S + int(i)) * case.Hq + h)
+    rows = np.array(rows, np.int64)
+    want = oracle.attn_fwd_rows(Q, K, V, case.window, case.s_v, rows)
+    assert_bitwise(Oh[rows], want, f"O rows ({name})")

@@ -148,3 +148,11 @@ def test_row_sum_runs_over_the_whole_key_axis():
 def test_exp_of_zero_is_one():
     assert oracle.exp(np.float32(0.0)) == np.float32(1.0)
     assert oracle.exp(np.float32(-0.0)) == np.float32(1.0)
+
+
+def test_sampled_rows_agree_with_the_full_call():
+    Q, K, V = _inputs(2, 90, 4, 2, seed=13)
+    O = oracle.attn_fwd(Q, K, V, 20, 0.05)
+    rows = np.array([0, 5, 77, 2 * 90 * 4 - 1, 90 * 4 + 17])
+    got = oracle.attn_fwd_rows(Q, K, V, 20, 0.05, rows)
+    assert np.array_equal(got, O.reshape(-1, D)[rows])
