@@ -55,6 +55,45 @@ HASH_STATE_TENSORS = 8
 # AdamW (the next row after the clip, measured beside the step): per parameter
 # read p, g, m, v and write p, m, v.
 ADAMW_BYTES_PER_ELEM = 28                                   # 8 x 805 MB = 6.44 GB
+# Attention with int8 P.V (measured beside the step, not part of `value`): the
+# method's logits are 2*D binary32 operations each (D products, D - 1 adds and
+# the scale), counted once per (row, allowed key); the int8 P.V product is on
+# the matrix cores and small beside them.
+ATTN_D = 128
+
+
+def attention_bench(torch, brl, dev):
+    """attn_fwd on one Open-1B layer's microbatch (4 x 4096 tokens, 16 query /
+    4 KV heads of 128), window 512 and full causal; device-generated inputs
+    (parity at this size is a GPU test)."""
+    B, S, Hq, Hkv = 4, 4096, 16, 4
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    Q = torch.randn(B, S, Hq, ATTN_D, generator=g, device=dev)
+    K = torch.randn(B, S, Hkv, ATTN_D, generator=g, device=dev)
+    V = torch.randn(B, S, Hkv, ATTN_D, generator=g, device=dev)
+    O = torch.empty_like(Q)
+    out = {"shape": {"B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "D": ATTN_D, "s_v": 0.05}}
+    for name, window in (("window_512", 512), ("causal", 0)):
+        logits = B * Hq * sum(min(i + 1, window) if window > 0 else i + 1 for i in range(S))
+        brl.attn_fwd(Q, K, V, window, 0.05, O=O)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(3):
+            brl.attn_fwd(Q, K, V, window, 0.05, O=O)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / 3
+        ops = 2.0 * ATTN_D * logits
+        out[name] = {"ms": round(ms, 4), "logits": logits,
+                     "roofline": {"bound": "alu", "achieved": round(ops / (ms * 1e-3) / 1e12, 3),
+                                  "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
+                                  "frac": round(ops / (ms * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4),
+                                  "note": "2*D binary32 ops per allowed logit, counted once"}}
+    del Q, K, V, O
+    return out
 
 
 def measured_traffic(kernel: str):
@@ -302,9 +341,11 @@ def main():
                      "note": (f"{HASH_VALU_PER_BLOCK} VALU instructions per 64-byte SHA-256 block, "
                               f"{HASH_ALIGNBIT_PER_BLOCK} of them half-rate rotations")},
     }
+    del hstate
+    result["attention"] = attention_bench(torch, brl, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
-        result["cpu_baseline"]["state_hash_GBps"] = cpu_hash_rate([p.cpu().numpy() for p in hstate[:1]])
+        result["cpu_baseline"]["state_hash_GBps"] = cpu_hash_rate([partials[0].cpu().numpy()])
     print(json.dumps(result), flush=True)
 
 
