@@ -67,6 +67,8 @@ def lib():
         "or_clip": (f32, [P, i64, f32, f32, f32]),
         "or_attn_fwd": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64]),
         "or_attn_fwd_rows": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64, P, i64]),
+        "or_attn_bwd_dq_rows": (i32, [P, P, P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P,
+                                      i64, P, i64]),
         "or_num_threads": (i32, []),
         "or_set_threads": (None, [i32]),
     }
@@ -341,6 +343,27 @@ def attn_fwd_rows(Q, K, V, window: int, s_v: float, rows) -> np.ndarray:
                                 np.float32(s_v), _p(rows), rows.size, _p(out), D)
     assert rc == 0, f"or_attn_fwd_rows failed ({rc})"
     return out
+
+
+def attn_bwd_dq(Q, K, V, O, dO, window: int, s_v: float, rows=None) -> np.ndarray:
+    """Fixed-point-accumulated dQ of the attention (see or_attn_bwd_dq_rows):
+    rows by flat id (b*S + i)*Hq + h, all rows by default; returns
+    [len(rows), D] (or [B, S, Hq, D] for all rows)."""
+    Q, K, V, O, dO = _f32(Q), _f32(K), _f32(V), _f32(O), _f32(dO)
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    assert O.shape == Q.shape and dO.shape == Q.shape
+    if rows is None:
+        out = np.empty((B * S * Hq, D), np.float32)
+        rp, n = None, B * S * Hq
+    else:
+        rows = np.ascontiguousarray(rows, np.int64)
+        out = np.empty((rows.size, D), np.float32)
+        rp, n = _p(rows), rows.size
+    rc = lib().or_attn_bwd_dq_rows(_p(Q), _p(K), _p(V), _p(O), _p(dO), B, S, Hq, Hkv, D, Hq * D, Hkv * D,
+                                   Hkv * D, Hq * D, int(window), np.float32(s_v), rp, n, _p(out), D)
+    assert rc == 0, f"or_attn_bwd_dq_rows failed ({rc})"
+    return out.reshape(B, S, Hq, D) if rows is None else out
 
 
 def num_threads() -> int:

@@ -696,6 +696,103 @@ int or_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64
     return or_attn_fwd_rows(Q, K, V, B, S, Hq, Hkv, D, ldq, ldk, ldv, window, s_v, NULL, B * S * Hq, O, D);
 }
 
+/* ∇Q of the attention (onedev.kr summary, "Use", attention paragraph: the
+ * attention backward accumulates ∇Q in 64-bit fixed point).  Readings, with
+ * s, m, p, l, q_v as in the forward and O the forward's output:
+ *   P_ij  = p_ij / l_i
+ *   dP_ij = CanonSum_d(dO_id * V^_jd),  V^ = fl(q_v * s_v)
+ *   Delta_i = CanonSum_d(dO_id * O_id)
+ *   dS_ij = P_ij * (dP_ij - Delta_i) on the row's keys, +0 on other keys
+ *   u_igd = CanonSum over the 64 key positions 64g .. 64g+63 of dS_ij * K_jd
+ *           (zeros past the row's keys and past S)
+ *   dQ_id = (fl(sum_g rne(u_igd * 2^40)) * 2^-40) * c
+ * The tile sums u are fixed-point numbers with 40 fraction bits, summed as
+ * exact int64 (any order gives the same sum); the total is rounded once to
+ * binary32.  Returns -3 if a term or the sum leaves the int64 range. */
+#define OR_ATTN_TILE 64
+#define OR_DQ_FRAC 40
+int or_attn_bwd_dq_rows(const float* Q, const float* K, const float* V, const float* O, const float* dO,
+                        int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk,
+                        int64_t ldv, int64_t ldo, int64_t window, float s_v, const int64_t* rows, int64_t nrows,
+                        float* out, int64_t ldout) {
+    fp_env_default();
+    e_init();
+    if (Hkv <= 0 || Hq % Hkv != 0) return -1;
+    const int64_t group = Hq / Hkv;
+    const float c = or_div(1.0f, or_sqrt((float)(double)D));
+    int8_t* qv = attn_quantize_v(V, B, S, Hkv, D, ldv, s_v);
+    const int64_t ntile = (S + OR_ATTN_TILE - 1) / OR_ATTN_TILE;
+    int bad = 0;
+    PARALLEL_BEGIN
+    float* prod = (float*)malloc(sizeof(float) * (size_t)(D > OR_ATTN_TILE ? D : OR_ATTN_TILE));
+    float* p = (float*)malloc(sizeof(float) * (size_t)S);
+    float* s = (float*)malloc(sizeof(float) * (size_t)S);
+    float* ds = (float*)malloc(sizeof(float) * (size_t)(ntile * OR_ATTN_TILE));
+    float* scratch = (float*)malloc(sizeof(float) * (size_t)(S / OR_BLOCK + D / OR_BLOCK + 4));
+    int64_t* acc = (int64_t*)malloc(sizeof(int64_t) * (size_t)D);
+    #pragma omp for schedule(dynamic, 8)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t row = rows ? rows[r] : r;
+        const int64_t h = row % Hq, i = (row / Hq) % S, b = row / (Hq * S);
+        const int64_t hk = h / group;
+        const int64_t lo = (window > 0 && i - window + 1 > 0) ? i - window + 1 : 0;
+        const float* q = Q + (b * S + i) * ldq + h * D;
+        const float* go = dO + (b * S + i) * ldo + h * D;
+        const float* o = O + (b * S + i) * ldo + h * D;
+        /* forward quantities */
+        for (int64_t j = lo; j <= i; ++j) {
+            const float* k = K + (b * S + j) * ldk + hk * D;
+            for (int64_t d = 0; d < D; ++d) prod[d] = or_mul(q[d], k[d]);
+            s[j] = or_mul(canon_sum(prod, D, scratch), c);
+        }
+        float m = s[lo];
+        for (int64_t j = lo + 1; j <= i; ++j)
+            if (s[j] > m) m = s[j];
+        for (int64_t j = 0; j < S; ++j) p[j] = 0.0f;
+        for (int64_t j = lo; j <= i; ++j) p[j] = or_exp(or_sub(s[j], m));
+        const float l = canon_sum(p, S, scratch);
+        /* backward */
+        for (int64_t d = 0; d < D; ++d) prod[d] = or_mul(go[d], o[d]);
+        const float delta = canon_sum(prod, D, scratch);
+        for (int64_t j = 0; j < ntile * OR_ATTN_TILE; ++j) ds[j] = 0.0f;
+        for (int64_t j = lo; j <= i; ++j) {
+            const int8_t* vq = qv + ((b * S + j) * Hkv + hk) * D;
+            for (int64_t d = 0; d < D; ++d) prod[d] = or_mul(go[d], or_mul(or_i2f(vq[d]), s_v));
+            const float dp = canon_sum(prod, D, scratch);
+            ds[j] = or_mul(or_div(p[j], l), or_sub(dp, delta));
+        }
+        for (int64_t d = 0; d < D; ++d) acc[d] = 0;
+        for (int64_t g = 0; g < ntile; ++g) {
+            for (int64_t d = 0; d < D; ++d) {
+                for (int64_t t = 0; t < OR_ATTN_TILE; ++t) {
+                    const int64_t j = g * OR_ATTN_TILE + t;
+                    const float kv = j < S ? K[(b * S + j) * ldk + hk * D + d] : 0.0f;
+                    prod[t] = or_mul(ds[j], kv);
+                }
+                const float u = canon_sum(prod, OR_ATTN_TILE, scratch);
+                const double x = rint((double)u * 0x1p40);
+                if (!(fabs(x) < 0x1p62)) {
+                    #pragma omp atomic write
+                    bad = 3;
+                    continue;
+                }
+                const int64_t fx = (int64_t)x;
+                if (__builtin_add_overflow(acc[d], fx, &acc[d])) {
+                    #pragma omp atomic write
+                    bad = 3;
+                }
+            }
+        }
+        float* dq = out + r * ldout;
+        for (int64_t d = 0; d < D; ++d)
+            dq[d] = or_mul(or_mul(round_flush((double)(float)acc[d]), 0x1p-40f), c);
+    }
+    free(prod); free(p); free(s); free(ds); free(scratch); free(acc);
+    PARALLEL_END
+    free(qv);
+    return bad ? -bad : 0;
+}
+
 void or_set_threads(int n) {
 #ifdef _OPENMP
     if (n > 0) omp_set_num_threads(n);

@@ -156,3 +156,97 @@ def test_sampled_rows_agree_with_the_full_call():
     rows = np.array([0, 5, 77, 2 * 90 * 4 - 1, 90 * 4 + 17])
     got = oracle.attn_fwd_rows(Q, K, V, 20, 0.05, rows)
     assert np.array_equal(got, O.reshape(-1, D)[rows])
+
+
+# ---- dQ with fixed-point accumulation ----------------------------------------------
+def _dequant_v(V, s_v):
+    return (_quantize_v(V, s_v).astype(np.float32) * np.float32(s_v)).astype(np.float64)
+
+
+def _f64_dq(Q, K, Vh, dO, window):
+    """Gradient of f(Q) = sum(dO * softmax(Q K^T / sqrt(D)) Vh) in float64,
+    with the bound term |K| weighted by P for the error budget."""
+    B, S, Hq, _ = Q.shape
+    Hkv = K.shape[2]
+    c = 1.0 / np.sqrt(D)
+    dq = np.zeros(Q.shape)
+    wk = np.zeros(Q.shape)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // (Hq // Hkv)
+            for i in range(S):
+                lo = _lo(i, window)
+                k = K[b, lo:i + 1, hk].astype(np.float64)
+                s = k @ Q[b, i, h].astype(np.float64) * c
+                P = np.exp(s - s.max())
+                P /= P.sum()
+                dp = Vh[b, lo:i + 1, hk] @ dO[b, i, h].astype(np.float64)
+                dq[b, i, h] = c * ((P * (dp - P @ dp)) @ k)
+                wk[b, i, h] = c * (P @ np.abs(k))
+    return dq, wk
+
+
+def _f64_loss(Q, K, Vh, dO, window):
+    B, S, Hq, _ = Q.shape
+    Hkv = K.shape[2]
+    tot = 0.0
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // (Hq // Hkv)
+            for i in range(S):
+                lo = _lo(i, window)
+                s = K[b, lo:i + 1, hk].astype(np.float64) @ Q[b, i, h].astype(np.float64) / np.sqrt(D)
+                P = np.exp(s - s.max())
+                tot += (P / P.sum()) @ Vh[b, lo:i + 1, hk] @ dO[b, i, h].astype(np.float64)
+    return tot
+
+
+def test_dq_zero_output_gradient_gives_zero():
+    Q, K, V = _inputs(1, 40, 2, 1, seed=21)
+    O = oracle.attn_fwd(Q, K, V, 0, 0.05)
+    dq = oracle.attn_bwd_dq(Q, K, V, O, np.zeros_like(O), 0, 0.05)
+    assert np.all(dq.view(np.uint32) == 0)
+
+
+@pytest.mark.parametrize("window", [0, 20])
+def test_dq_matches_the_float64_gradient_within_the_quantisation_bound(window):
+    """The float64 gradient of sum(dO * softmax(QK^T/sqrt(D)) V^) (itself
+    checked by central differences) bounds the oracle's dQ: the only
+    departures are the forward's quantised P inside Delta = dO . O (at most
+    (1/2 + 2^-16 * 127)/127 of sum|v^|/l per unit of |dO|, times the
+    P-weighted |K| c), binary32 rounding (1e-5 relative) and the 2^-40
+    fixed-point grid.  The same data with Delta left out leaves the bound."""
+    B, S, Hq, Hkv, s_v = 1, 50, 2, 1, 0.05
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=31, q_scale=0.5)
+    g = np.random.default_rng(32)
+    dO = (g.standard_normal(Q.shape) * 1e-2).astype(np.float32)
+    O = oracle.attn_fwd(Q, K, V, window, s_v)
+    dq = oracle.attn_bwd_dq(Q, K, V, O, dO, window, s_v).astype(np.float64)
+    Vh = _dequant_v(V, s_v)
+    ref, wk = _f64_dq(Q, K, Vh, dO, window)
+    # the float64 gradient against central differences of the float64 loss
+    for (i, h, d) in [(0, 0, 0), (17, 1, 5), (49, 0, 127)]:
+        e = 1e-3
+        Qp, Qm = Q.astype(np.float64).copy(), Q.astype(np.float64).copy()
+        Qp[0, i, h, d] += e
+        Qm[0, i, h, d] -= e
+        fd = (_f64_loss(Qp, K, Vh, dO, window) - _f64_loss(Qm, K, Vh, dO, window)) / (2 * e)
+        assert abs(fd - ref[0, i, h, d]) <= 1e-6 * max(1.0, abs(fd)) + 1e-9
+    _, terms = _f64_attention(Q, K, Vh.astype(np.float32), window, 1.0 / np.sqrt(D))
+    delta_err = np.abs(dO).astype(np.float64).sum(axis=3, keepdims=True) * (0.5 / 127 + 2.0 ** -16) \
+        * terms.max(axis=3, keepdims=True)
+    bound = wk * delta_err + 1e-5 * np.abs(ref) + 1e-7 + S * 2.0 ** -40
+    assert np.all(np.abs(dq - ref) <= bound)
+    no_delta, _ = _f64_dq(Q, K, Vh, dO, window)
+    # planted mistake: without the Delta term the gradient is far off
+    planted = np.zeros_like(no_delta)
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(S):
+                lo = _lo(i, window)
+                k = K[b, lo:i + 1, 0].astype(np.float64)
+                s = k @ Q[b, i, h].astype(np.float64) / np.sqrt(D)
+                P = np.exp(s - s.max())
+                P /= P.sum()
+                planted[b, i, h] = (P * (Vh[b, lo:i + 1, 0] @ dO[b, i, h].astype(np.float64))) @ k / np.sqrt(D)
+    assert np.any(np.abs(dq - planted) > bound)
