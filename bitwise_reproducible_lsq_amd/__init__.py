@@ -59,7 +59,8 @@ _SIGS = {
     "brl_state_hash": (i32, [P, P, i32, P, P, sz, P]),
     "brl_adamw_scalars_for_step": (i32, [i64, C.c_double, P, P]),
     "adamw_step": (i32, [P, P, P, P, i64, P, i32, P]),
-    "attn_fwd": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64, P]),
+    "attn_fwd": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64, P, P]),
+    "attn_bwd_dq": (i32, [P, P, P, P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, P]),
     "brl_set_tuning": (i64, [i32, i64]),
     "brl_status_string": (C.c_char_p, [i32]),
     "brl_last_error": (C.c_char_p, []),
@@ -302,23 +303,50 @@ def _heads_view(t: torch.Tensor, name: str):
 
 
 def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, window: int, s_v: float,
-             O: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+             O: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Attention with int8 P.V (attn_fwd).  Q [B, S, Hq, D], K and V
     [B, S, Hkv, D], views with evenly spaced rows (column slices of the QKV
-    projection output work); returns O [B, S, Hq, D]."""
+    projection output work); returns O [B, S, Hq, D].  stats, if given, is a
+    float32 [B, S, Hq, 2] tensor receiving (m_i, l_i) for attn_bwd_dq."""
     B, S, Hq, D = Q.shape
     Hkv = K.shape[2]
     if K.shape != (B, S, Hkv, D) or V.shape != K.shape:
         raise ValueError("Q, K, V shapes disagree")
     if O is None:
         O = torch.empty((B, S, Hq, D), dtype=torch.float32, device=Q.device)
+    if stats is not None and (stats.shape != (B, S, Hq, 2) or stats.dtype != torch.float32):
+        raise ValueError("stats must be float32 [B, S, Hq, 2]")
     q, ldq = _heads_view(Q, "Q")
     k, ldk = _heads_view(K, "K")
     v, ldv = _heads_view(V, "V")
     o, ldo = _heads_view(O, "O")
     _check(lib().attn_fwd(q, k, v, B, S, Hq, Hkv, D, ldq, ldk, ldv, int(window), float(s_v), o, ldo,
-                          _stream(stream)))
+                          _ptr(stats), _stream(stream)))
     return O
+
+
+def attn_bwd_dq(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor, dO: torch.Tensor,
+                stats: torch.Tensor, window: int, s_v: float, dQ: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """dQ of attn_fwd with 64-bit fixed-point accumulation (attn_bwd_dq).
+    O, dO and dQ are dense [B, S, Hq, D]; stats as written by attn_fwd."""
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    for t, n in ((O, "O"), (dO, "dO")):
+        _f32(t, n)
+        if t.shape != Q.shape:
+            raise ValueError(f"{n} must have Q's shape")
+    if stats.shape != (B, S, Hq, 2) or stats.dtype != torch.float32:
+        raise ValueError("stats must be float32 [B, S, Hq, 2]")
+    if dQ is None:
+        dQ = torch.empty((B, S, Hq, D), dtype=torch.float32, device=Q.device)
+    q, ldq = _heads_view(Q, "Q")
+    k, ldk = _heads_view(K, "K")
+    v, ldv = _heads_view(V, "V")
+    ld = Hq * D
+    _check(lib().attn_bwd_dq(q, k, v, _ptr(O), _ptr(dO), _ptr(stats), B, S, Hq, Hkv, D, ldq, ldk, ldv, ld,
+                             int(window), float(s_v), _ptr(dQ), _stream(stream)))
+    return dQ
 
 
 def probe_f32(op: str, a: torch.Tensor, b: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

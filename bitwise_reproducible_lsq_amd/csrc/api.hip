@@ -484,24 +484,50 @@ brl_status adamw_step(float* p, const float* g, float* m, float* v, int64_t n, c
     return check_hip(launch_adamw(p, g, m, v, n, *sc, decay != 0, static_cast<hipStream_t>(stream)), "AdamW");
 }
 
+static brl_status attn_check(const char* who, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                             int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, float s_v) {
+    if (B < 0 || S < 0) return fail(BRL_ESHAPE, "%s: B, S must be >= 0", who);
+    if (D != 128) return fail(BRL_ESHAPE, "%s: head dimension must be 128", who);
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return fail(BRL_ESHAPE, "%s: Hq must be a positive multiple of Hkv", who);
+    if (S > 133143) return fail(BRL_ESHAPE, "%s: S too large for int32 P.V accumulators", who);
+    if (ldq < Hq * D || ldo < Hq * D || ldk < Hkv * D || ldv < Hkv * D)
+        return fail(BRL_ESHAPE, "%s: row stride smaller than heads * D", who);
+    if ((ldq | ldk | ldv | ldo) & 3) return fail(BRL_EINVAL, "%s: row strides must be multiples of 4", who);
+    if (!(s_v == s_v)) return fail(BRL_EINVAL, "%s: s_v is NaN", who);
+    return BRL_OK;
+}
+
+static bool al16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 brl_status attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
                     int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
-                    float* O, int64_t ldo, void* stream) {
-    if (B < 0 || S < 0) return fail(BRL_ESHAPE, "attn_fwd: B, S must be >= 0");
-    if (D != 128) return fail(BRL_ESHAPE, "attn_fwd: head dimension must be 128");
-    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return fail(BRL_ESHAPE, "attn_fwd: Hq must be a positive multiple of Hkv");
-    if (S > 133143) return fail(BRL_ESHAPE, "attn_fwd: S too large for int32 P.V accumulators");
-    if (ldq < Hq * D || ldo < Hq * D || ldk < Hkv * D || ldv < Hkv * D)
-        return fail(BRL_ESHAPE, "attn_fwd: row stride smaller than heads * D");
-    if ((ldq | ldk | ldv | ldo) & 3) return fail(BRL_EINVAL, "attn_fwd: row strides must be multiples of 4");
+                    float* O, int64_t ldo, float* stats, void* stream) {
+    brl_status rc = attn_check("attn_fwd", B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo, s_v);
+    if (rc != BRL_OK) return rc;
     if (B * S == 0) return BRL_OK;
     if (!Q || !K || !V || !O) return fail(BRL_EINVAL, "attn_fwd: null tensor");
-    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-    if (!al16(Q) || !al16(K) || !al16(V) || !al16(O)) return fail(BRL_EINVAL, "attn_fwd: pointers must be 16-byte aligned");
-    if (!(s_v == s_v)) return fail(BRL_EINVAL, "attn_fwd: s_v is NaN");
-    return check_hip(launch_attn_fwd(Q, K, V, B, S, Hq, Hkv, ldq, ldk, ldv, window, s_v, O, ldo, exp_constants(),
-                                     static_cast<hipStream_t>(stream)),
+    if (!al16p(Q) || !al16p(K) || !al16p(V) || !al16p(O))
+        return fail(BRL_EINVAL, "attn_fwd: pointers must be 16-byte aligned");
+    if (stats && !aligned4(stats)) return fail(BRL_EINVAL, "attn_fwd: stats must be 4-byte aligned");
+    return check_hip(launch_attn_fwd(Q, K, V, B, S, Hq, Hkv, ldq, ldk, ldv, window, s_v, O, ldo, stats,
+                                     exp_constants(), static_cast<hipStream_t>(stream)),
                      "attention");
+}
+
+brl_status attn_bwd_dq(const float* Q, const float* K, const float* V, const float* O, const float* dO,
+                       const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t ldq,
+                       int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dQ,
+                       void* stream) {
+    brl_status rc = attn_check("attn_bwd_dq", B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo, s_v);
+    if (rc != BRL_OK) return rc;
+    if (B * S == 0) return BRL_OK;
+    if (!Q || !K || !V || !O || !dO || !stats || !dQ) return fail(BRL_EINVAL, "attn_bwd_dq: null tensor");
+    if (!al16p(Q) || !al16p(K) || !al16p(V) || !al16p(O) || !al16p(dO) || !al16p(dQ))
+        return fail(BRL_EINVAL, "attn_bwd_dq: pointers must be 16-byte aligned");
+    if (!aligned4(stats)) return fail(BRL_EINVAL, "attn_bwd_dq: stats must be 4-byte aligned");
+    return check_hip(launch_attn_bwd_dq(Q, K, V, O, dO, stats, B, S, Hq, Hkv, ldq, ldk, ldv, ldo, window, s_v, dQ,
+                                        exp_constants(), static_cast<hipStream_t>(stream)),
+                     "attention dQ");
 }
 
 int64_t brl_set_tuning(int32_t knob, int64_t value) {

@@ -49,6 +49,7 @@ struct AttnArgs {
     const float* K;
     const float* V;
     float* O;
+    float* stats;          // optional (m_i, l_i) per row (b*S + i)*Hq + h
     int64_t S, Hq, Hkv, ldq, ldk, ldv, ldo, window;
     float c, s_v;
     ExpConsts ek;
@@ -72,16 +73,18 @@ static_assert(sizeof(AttnSmem) <= 81920, "two workgroups per CU");
 
 __device__ __forceinline__ int aswz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
 
-// 16 logits of this thread: rows 4ti..4ti+3, keys 4tj..4tj+3 of the tile
-__device__ __forceinline__ void attn_logits(const AttnSmem& sm, int ti, int tj, float c, float s[4][4]) {
+// CanonSum over d of A[d][4ti + x] * B[d][4tj + y] for this thread's 4 x 4
+// outputs: d-blocks of 32 summed left to right, then (b0 + b1) + (b2 + b3)
+__device__ __forceinline__ void canon_dot4x4(const float (*A)[kAQ], const float (*B)[kAK], int ti, int tj,
+                                             float s[4][4]) {
     float b01[4][4], b2[4][4], cur[4][4];
 #pragma unroll
     for (int blk = 0; blk < kAD / 32; ++blk) {
 #pragma unroll 4
         for (int dd = 0; dd < 32; ++dd) {
             const int d = blk * 32 + dd;
-            const vf4 a = *reinterpret_cast<const vf4*>(&sm.qs[d][4 * ti]);
-            const vf4 b = *reinterpret_cast<const vf4*>(&sm.ks[d][4 * tj]);
+            const vf4 a = *reinterpret_cast<const vf4*>(&A[d][4 * ti]);
+            const vf4 b = *reinterpret_cast<const vf4*>(&B[d][4 * tj]);
 #pragma unroll
             for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -90,7 +93,6 @@ __device__ __forceinline__ void attn_logits(const AttnSmem& sm, int ti, int tj, 
                     cur[x][y] = dd == 0 ? pr : f_add(cur[x][y], pr);
                 }
         }
-        // tree over the four d-blocks: (b0 + b1) + (b2 + b3)
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -98,9 +100,19 @@ __device__ __forceinline__ void attn_logits(const AttnSmem& sm, int ti, int tj, 
                 if (blk == 0) b01[x][y] = cur[x][y];
                 if (blk == 1) b01[x][y] = f_add(b01[x][y], cur[x][y]);
                 if (blk == 2) b2[x][y] = cur[x][y];
-                if (blk == 3) s[x][y] = f_mul(f_add(b01[x][y], f_add(b2[x][y], cur[x][y])), c);
+                if (blk == 3) s[x][y] = f_add(b01[x][y], f_add(b2[x][y], cur[x][y]));
             }
     }
+}
+
+// 16 logits of this thread: rows 4ti..4ti+3, keys 4tj..4tj+3 of the tile
+__device__ __forceinline__ void attn_logits_from(const float (*qs)[kAQ], const float (*ks)[kAK], int ti, int tj,
+                                                 float c, float s[4][4]) {
+    canon_dot4x4(qs, ks, ti, tj, s);
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) s[x][y] = f_mul(s[x][y], c);
 }
 
 // 64 rows (rows_left of them real) x 128 floats of head `head` into
@@ -174,7 +186,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
         attn_load_kt(a.K, a.ldk, base + j0, a.S - j0, hk, sm.ks);
         __syncthreads();
         float s[4][4];
-        attn_logits(sm, ti, tj, a.c, s);
+        attn_logits_from(sm.qs, sm.ks, ti, tj, a.c, s);
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -232,7 +244,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
         }
         __syncthreads();
         float s[4][4];
-        attn_logits(sm, ti, tj, a.c, s);
+        attn_logits_from(sm.qs, sm.ks, ti, tj, a.c, s);
         float pair[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -308,6 +320,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
                 have = true;
             }
         sm.rowdiv[tid] = f_mul(root, 127.0f);
+        if (a.stats && tid < qrows) {
+            float* st2 = a.stats + 2 * ((base + q0 + tid) * a.Hq + h);
+            st2[0] = sm.rowmax[tid];
+            st2[1] = root;
+        }
     }
     __syncthreads();
     // O = (fl(acc) * s_v) / (l * 127)
@@ -325,14 +342,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
         }
 }
 
-size_t attn_smem_bytes() { return sizeof(AttnSmem); }
-
 hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
                            int64_t Hkv, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
-                           float* O, int64_t ldo, const ExpConsts& ek, hipStream_t st) {
+                           float* O, int64_t ldo, float* stats, const ExpConsts& ek, hipStream_t st) {
     if (B == 0 || S == 0) return hipSuccess;
     AttnArgs a;
-    a.Q = Q; a.K = K; a.V = V; a.O = O;
+    a.Q = Q; a.K = K; a.V = V; a.O = O; a.stats = stats;
     a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.window = window;
     // c = fl(1 / fl(sqrt(D))): both binary64 results are rounded once more to
     // binary32, which is innocuous for sqrt and division (53 >= 2 * 24 + 2)
@@ -348,6 +363,218 @@ hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64
     const int64_t blocks = B * Hq * ceil_div(S, kAQ);
     if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)blocks), dim3(256), sizeof(AttnSmem), st, a);
+    return hipGetLastError();
+}
+
+// ---- dQ with 64-bit fixed-point accumulation ------------------------------------
+// The attention backward accumulates dQ in 64-bit fixed point (onedev.kr
+// summary, "Use", attention paragraph).  This library's reading, with s, m,
+// p, l as in the forward (m and l from the forward's stats) and O its output:
+//   P_ij = p_ij / l_i;  dP_ij = CanonSum_d(dO_id * V^_jd), V^ = fl(q_v * s_v);
+//   Delta_i = CanonSum_d(dO_id * O_id);
+//   dS_ij = P_ij * (dP_ij - Delta_i) on the row's keys, +0 elsewhere;
+//   u_igd = CanonSum over the 64 key positions of tile g of dS_ij * K_jd;
+//   dQ_id = (fl(sum_g rne(u_igd * 2^40)) * 2^-40) * c.
+// The tile sums become int64 with 40 fraction bits and add exactly, in any
+// order: one workgroup per (batch, head, 64-query block) walks the key tiles
+// and keeps 32 int64 accumulators per thread.
+constexpr int kDqFrac = 40;
+
+struct AttnBwdArgs {
+    const float* Q;
+    const float* K;
+    const float* V;
+    const float* O;
+    const float* dO;
+    const float* stats;
+    float* dQ;
+    int64_t S, Hq, Hkv, ldq, ldk, ldv, ldo, window;
+    float c, s_v;
+    ExpConsts ek;
+};
+
+struct AttnBwdSmem {
+    float qs[kAD][kAQ];             // Q tile, d-major
+    float gs[kAD][kAQ];             // dO tile, d-major
+    float ks[kAD][kAK];             // K tile, d-major (logits)
+    union {
+        float vs[kAD][kAK];         // V^ tile, d-major (dP)
+        float kt[kAK][kAD];         // K tile, key-major (dQ)
+    } u;
+    float ds[kAQ][kAK + 1];         // dS tile
+    float rowm[kAQ], rowl[kAQ], rowdelta[kAQ];
+};
+
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    AttnBwdSmem& sm = *reinterpret_cast<AttnBwdSmem*>(smem_raw);
+    const int tid = threadIdx.x;
+    const int ti = tid >> 4, tj = tid & 15;
+
+    const unsigned nqb = (unsigned)((a.S + kAQ - 1) / kAQ), hq = (unsigned)a.Hq;
+    const unsigned qb = blockIdx.x % nqb;
+    const unsigned bh = blockIdx.x / nqb;
+    const int64_t h = bh % hq;
+    const int64_t b = bh / hq;
+    const int64_t hk = (unsigned)h / (hq / (unsigned)a.Hkv);
+    const int64_t q0 = (int64_t)qb * kAQ;
+    const int64_t qrows = a.S - q0 < kAQ ? a.S - q0 : kAQ;
+    const int64_t base = b * a.S;
+    const int64_t klo = a.window > 0 ? (q0 - a.window + 1 > 0 ? q0 - a.window + 1 : 0) : 0;
+    const int64_t khi = q0 + qrows - 1;
+    const int64_t kt0 = klo / kAK, kt1 = khi / kAK;
+
+    attn_load_kt(a.Q, a.ldq, base + q0, qrows, h, sm.qs);
+    attn_load_kt(a.dO, a.ldo, base + q0, qrows, h, sm.gs);
+    if (tid < kAQ) {
+        float m = 0.0f, l = 1.0f, delta = 0.0f;
+        if (tid < qrows) {
+            const int64_t row = base + q0 + tid;
+            m = a.stats[2 * (row * a.Hq + h)];
+            l = a.stats[2 * (row * a.Hq + h) + 1];
+            // Delta = CanonSum_d(dO * O): four d-blocks, then the pair tree
+            const float* go = a.dO + row * a.ldo + h * kAD;
+            const float* o = a.O + row * a.ldo + h * kAD;
+            float bs[4];
+            for (int blk = 0; blk < 4; ++blk) {
+                float x = f_mul(go[32 * blk], o[32 * blk]);
+                for (int d = 1; d < 32; ++d) x = f_add(x, f_mul(go[32 * blk + d], o[32 * blk + d]));
+                bs[blk] = x;
+            }
+            delta = f_add(f_add(bs[0], bs[1]), f_add(bs[2], bs[3]));
+        }
+        sm.rowm[tid] = m;
+        sm.rowl[tid] = l;
+        sm.rowdelta[tid] = delta;
+    }
+    auto allowed = [&](int64_t i, int64_t j) {
+        const int64_t lo = a.window > 0 ? i - a.window + 1 : 0;
+        return i < a.S && j <= i && j >= lo;
+    };
+    const Quantizer qz(a.s_v);
+    // dQ outputs of this thread: row r = tid / 4, d = d0 .. d0 + 31
+    const int r = tid >> 2, d0 = (tid & 3) * 32;
+    int64_t acc[32];
+#pragma unroll
+    for (int x = 0; x < 32; ++x) acc[x] = 0;
+
+    for (int64_t kt = kt0; kt <= kt1; ++kt) {
+        const int64_t j0 = kt * kAK;
+        __syncthreads();
+        attn_load_kt(a.K, a.ldk, base + j0, a.S - j0, hk, sm.ks);
+        // V^ = fl(q_v * s_v), d-major
+#pragma unroll
+        for (int it = 0; it < (kAK / 4) * (kAD / 4) / 256; ++it) {
+            const int e = tid + 256 * it;
+            const int rq = e & 15, dq = e >> 4;
+            vf4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t j = j0 + 4 * rq + u;
+                v[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
+                if (j < a.S) v[u] = *reinterpret_cast<const vf4*>(a.V + (base + j) * a.ldv + hk * kAD + 4 * dq);
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                vf4 o;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    bool in;
+                    o[u] = j0 + 4 * rq + u < a.S ? f_mul((float)qz.q(v[u][w], &in), a.s_v) : 0.0f;
+                }
+                *reinterpret_cast<vf4*>(&sm.u.vs[4 * dq + w][4 * rq]) = o;
+            }
+        }
+        __syncthreads();
+        float sc[4][4], dp[4][4];
+        attn_logits_from(sm.qs, sm.ks, ti, tj, a.c, sc);
+        canon_dot4x4(sm.gs, sm.u.vs, ti, tj, dp);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int i = 4 * ti + x;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                const int j = 4 * tj + y;
+                float dsv = 0.0f;
+                if (allowed(q0 + i, j0 + j)) {
+                    const float p = own_exp(f_sub(sc[x][y], sm.rowm[i]), a.ek);
+                    dsv = f_mul(f_div(p, sm.rowl[i]), f_sub(dp[x][y], sm.rowdelta[i]));
+                }
+                sm.ds[i][j] = dsv;
+            }
+        }
+        __syncthreads();
+        // K tile again, key-major, over the V^ buffer
+#pragma unroll
+        for (int it = 0; it < kAK * (kAD / 4) / 256; ++it) {
+            const int e = tid + 256 * it;
+            const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
+            vf4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (j0 + row < a.S) v = *reinterpret_cast<const vf4*>(a.K + (base + j0 + row) * a.ldk + hk * kAD + d4);
+            *reinterpret_cast<vf4*>(&sm.u.kt[row][d4]) = v;
+        }
+        __syncthreads();
+        // tile sums u over the 64 keys: two 32-key blocks left to right, then the pair
+        float b0[32], cur[32];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            for (int jj = 0; jj < 32; ++jj) {
+                const int j = 32 * blk + jj;
+                const float dsv = sm.ds[r][j];
+#pragma unroll
+                for (int q4 = 0; q4 < 8; ++q4) {
+                    const vf4 kv = *reinterpret_cast<const vf4*>(&sm.u.kt[j][d0 + 4 * q4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float pr = f_mul(dsv, kv[e]);
+                        cur[4 * q4 + e] = jj == 0 ? pr : f_add(cur[4 * q4 + e], pr);
+                    }
+                }
+            }
+            if (blk == 0) {
+#pragma unroll
+                for (int x = 0; x < 32; ++x) b0[x] = cur[x];
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < 32; ++x) {
+            const float u = f_add(b0[x], cur[x]);
+            acc[x] += (int64_t)__builtin_rint((double)u * 0x1p40);
+        }
+    }
+    // dQ = (fl(acc) * 2^-40) * c
+    if (r < qrows) {
+        float* out = a.dQ + (base + q0 + r) * a.ldo + h * kAD + d0;
+#pragma unroll
+        for (int q4 = 0; q4 < 8; ++q4) {
+            vf4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = f_mul(f_mul((float)acc[4 * q4 + e], 0x1p-40f), a.c);
+            *reinterpret_cast<vf4*>(out + 4 * q4) = o;
+        }
+    }
+}
+
+hipError_t launch_attn_bwd_dq(const float* Q, const float* K, const float* V, const float* O, const float* dO,
+                              const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t ldq,
+                              int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dQ,
+                              const ExpConsts& ek, hipStream_t st) {
+    if (B == 0 || S == 0) return hipSuccess;
+    AttnBwdArgs a;
+    a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.stats = stats; a.dQ = dQ;
+    a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.window = window;
+    a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
+    a.s_v = s_v;
+    a.ek = ek;
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnBwdSmem));
+        attr = true;
+    }
+    const int64_t blocks = B * Hq * ceil_div(S, kAQ);
+    if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)blocks), dim3(256), sizeof(AttnBwdSmem), st, a);
     return hipGetLastError();
 }
 

@@ -257,11 +257,36 @@ BRL_API brl_status adamw_step(float* p, const float* g, float* m, float* v, int6
  * D must be 128; Hq a positive multiple of Hkv; S <= 133143 (int32 P.V
  * accumulators); every ld a multiple of 4 and >= heads*D; Q, K, V, O device
  * pointers 16-byte aligned; O must not overlap Q, K or V.  Inputs must be
- * finite.  No workspace; asynchronous on `stream`.
+ * finite.  stats (nullable, device, [B*S*Hq][2] floats, row (b*S + i)*Hq + h)
+ * receives (m_i, l_i) for the backward.  No workspace; asynchronous on
+ * `stream`.
  */
 BRL_API brl_status attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
                             int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window,
-                            float s_v, float* O, int64_t ldo, void* stream);
+                            float s_v, float* O, int64_t ldo, float* stats, void* stream);
+
+/*
+ * dQ of attn_fwd with 64-bit fixed-point accumulation (onedev.kr summary,
+ * "Use", attention paragraph: the attention backward accumulates the query
+ * gradient in 64-bit fixed point).  This library's reading, with s, m, p, l,
+ * q_v as in attn_fwd, O its output and dO the output gradient:
+ *   P_ij = p_ij / l_i;  V^_jd = fl(q_v,jd * s_v)
+ *   dP_ij = CanonSum_d(dO_id * V^_jd);  Delta_i = CanonSum_d(dO_id * O_id)
+ *   dS_ij = P_ij * (dP_ij - Delta_i) on the row's keys, +0 elsewhere
+ *   u_igd = CanonSum over key positions 64g .. 64g+63 of dS_ij * K_jd
+ *   dQ_id = (fl(sum_g rne(u_igd * 2^40)) * 2^-40) * c
+ * The tile sums are int64 fixed-point numbers with 40 fraction bits, added
+ * exactly (their order cannot change the sum); the total is rounded once.
+ * Valid while every |u| < 2^22 and |sum| < 2^23 (gradient scale; not
+ * checked).  stats: the (m_i, l_i) that attn_fwd wrote for the same Q, K, V,
+ * window.  O, dO and dQ share the layout and row stride ldo of Q's shape;
+ * other arguments and requirements as attn_fwd.  dQ must not overlap the
+ * inputs.  Asynchronous on `stream`.
+ */
+BRL_API brl_status attn_bwd_dq(const float* Q, const float* K, const float* V, const float* O, const float* dO,
+                               const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                               int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v,
+                               float* dQ, void* stream);
 
 /* Conformance probe of the device's binary32 operations, as the kernels use
  * them: out[i] = op(a[i], b[i]) for op 0 add, 1 sub, 2 mul, 3 div, 4 sqrt (a),

@@ -91,3 +91,30 @@ def test_attention_large_logits_and_repeat():
     want = oracle.attn_fwd(Q, K, V, window, s_v)
     assert_bitwise(O1, want, "O (large logits)")
     assert_bitwise(O2, want, "O (repeat)")
+
+
+DQ_CASES = [
+    # B, S, Hq, Hkv, window, s_v
+    (1, 1, 1, 1, 0, 0.05),
+    (1, 64, 2, 1, 0, 0.05),
+    (2, 150, 4, 2, 0, 0.05),
+    (1, 200, 4, 2, 64, 0.0371),
+    (1, 333, 16, 4, 130, 0.05),
+    (1, 100, 4, 4, 1, 0.05),
+]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,window,s_v", DQ_CASES)
+def test_attention_dq_parity(B, S, Hq, Hkv, window, s_v):
+    """dQ with 64-bit fixed-point accumulation, bit for bit, from the
+    forward's own O and (m, l) statistics."""
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=3 * S + Hq + window, scale=0.3)
+    dO = (np.random.default_rng(S + window).standard_normal((B, S, Hq, D)) * 1e-2).astype(np.float32)
+    q, k, v = (torch.from_numpy(t).cuda() for t in (Q, K, V))
+    stats = torch.empty((B, S, Hq, 2), dtype=torch.float32, device="cuda")
+    O = brl.attn_fwd(q, k, v, window, s_v, stats=stats)
+    dQ = brl.attn_bwd_dq(q, k, v, O, torch.from_numpy(dO).cuda(), stats, window, s_v)
+    torch.cuda.synchronize()
+    Oh = O.cpu().numpy()
+    assert_bitwise(Oh, oracle.attn_fwd(Q, K, V, window, s_v), "O")
+    assert_bitwise(dQ, oracle.attn_bwd_dq(Q, K, V, Oh, dO, window, s_v), f"dQ (S={S} w={window})")

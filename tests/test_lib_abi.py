@@ -232,7 +232,7 @@ def test_attention_rejects_bad_arguments_without_launching():
     def call(**kw):
         a = {**ok, **kw}
         return L.attn_fwd(kw.get("Q", p), p, p, a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["ldq"], a["ldk"],
-                          a["ldv"], 0, 0.05, kw.get("O", p), a["ldo"], None)
+                          a["ldv"], 0, 0.05, kw.get("O", p), a["ldo"], None, None)
 
     assert call(D=64) == brl.BRL_ESHAPE
     assert call(Hq=3) == brl.BRL_ESHAPE
@@ -243,3 +243,7 @@ def test_attention_rejects_bad_arguments_without_launching():
     assert call(Q=None) == brl.BRL_EINVAL
     assert call(O=C.c_void_p(0x10004)) == brl.BRL_EINVAL
     assert call(S=0) == brl.BRL_OK            # nothing to do, nothing launched
+    assert L.attn_bwd_dq(p, p, p, p, p, p, 1, 64, 4, 2, 64, 512, 256, 256, 512, 0, 0.05, p, None) == brl.BRL_ESHAPE
+    assert L.attn_bwd_dq(p, p, p, p, p, None, 1, 64, 4, 2, 128, 512, 256, 256, 512, 0, 0.05, p, None) == brl.BRL_EINVAL
+    assert L.attn_bwd_dq(p, p, p, p, C.c_void_p(0x10008), p, 1, 64, 4, 2, 128, 512, 256, 256, 512, 0, 0.05, p,
+                         None) == brl.BRL_EINVAL
