@@ -73,6 +73,9 @@ def attention_bench(torch, brl, dev):
     K = torch.randn(B, S, Hkv, ATTN_D, generator=g, device=dev)
     V = torch.randn(B, S, Hkv, ATTN_D, generator=g, device=dev)
     O = torch.empty_like(Q)
+    dO = torch.randn(B, S, Hq, ATTN_D, generator=g, device=dev).mul_(1e-3)
+    dQ = torch.empty_like(Q)
+    stats = torch.empty(B, S, Hq, 2, device=dev)
     out = {"shape": {"B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "D": ATTN_D, "s_v": 0.05}}
     for name, window in (("window_512", 512), ("causal", 0)):
         logits = B * Hq * sum(min(i + 1, window) if window > 0 else i + 1 for i in range(S))
@@ -92,7 +95,24 @@ def attention_bench(torch, brl, dev):
                                   "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
                                   "frac": round(ops / (ms * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4),
                                   "note": "2*D binary32 ops per allowed logit, counted once"}}
-    del Q, K, V, O
+        # dQ with 64-bit fixed-point accumulation: logits, dP and the dS.K
+        # products, 3 * 2*D binary32 ops per allowed (row, key)
+        brl.attn_fwd(Q, K, V, window, 0.05, O=O, stats=stats)
+        brl.attn_bwd_dq(Q, K, V, O, dO, stats, window, 0.05, dQ=dQ)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(3):
+            brl.attn_bwd_dq(Q, K, V, O, dO, stats, window, 0.05, dQ=dQ)
+        b.record()
+        torch.cuda.synchronize()
+        ms_dq = a.elapsed_time(b) / 3
+        ops_dq = 3 * ops
+        out[name]["dq"] = {"ms": round(ms_dq, 4),
+                           "roofline": {"bound": "alu", "achieved": round(ops_dq / (ms_dq * 1e-3) / 1e12, 3),
+                                        "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
+                                        "frac": round(ops_dq / (ms_dq * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4),
+                                        "note": "3 * 2*D binary32 ops per allowed (row, key)"}}
+    del Q, K, V, O, dO, dQ, stats
     return out
 
 

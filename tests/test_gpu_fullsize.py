@@ -172,3 +172,27 @@ def test_attention_full_size(name):
     rows = np.array(rows, np.int64)
     want = oracle.attn_fwd_rows(Q, K, V, case.window, case.s_v, rows)
     assert_bitwise(Oh[rows], want, f"O rows ({name})")
+
+
+@pytest.mark.parametrize("name", ["attn_window", "attn_causal"])
+def test_attention_dq_full_size(name):
+    """dQ (64-bit fixed-point accumulation) at one Open-1B layer, on sampled
+    rows, from the forward's own O and statistics; dO ~ N(0, 1e-3)."""
+    case = synth.ATTENTION_CASES[name]
+    Q, K, V = synth.attention_inputs(case)
+    dO = synth.normal(case.seed, "dY", Q.shape, 1e-3)
+    q, k, v = _cuda(Q), _cuda(K), _cuda(V)
+    stats = torch.empty((case.B, case.S, case.Hq, 2), dtype=torch.float32, device=DEV)
+    O = brl.attn_fwd(q, k, v, case.window, case.s_v, stats=stats)
+    dQ = brl.attn_bwd_dq(q, k, v, O, _cuda(dO), stats, case.window, case.s_v)
+    torch.cuda.synchronize()
+    Oh = O.cpu().numpy()
+    dQh = dQ.cpu().numpy().reshape(-1, 128)
+    edges = [0, 1, 63, 64, 511, 512, 2048, case.S - 1]
+    rows = []
+    for b, h in [(0, 0), (3, 15)]:
+        for i in _sample(case.S, edges, 3, seed=b * 16 + h + 1):
+            rows.append((b * case.S + int(i)) * case.Hq + h)
+    rows = np.array(rows, np.int64)
+    want = oracle.attn_bwd_dq(Q, K, V, Oh, dO, case.window, case.s_v, rows=rows)
+    assert_bitwise(dQh[rows], want, f"dQ rows ({name})")
