@@ -176,3 +176,30 @@ def replay_partial_host(seed: int, v: int, length: int, std: float = 1e-4) -> np
     """Host-side partial for small CPU-only replay cases."""
     g = np.random.Generator(np.random.Philox(key=(int(seed) << 32) | (1000 + v)))
     return (g.standard_normal(length, dtype=np.float64) * std).astype(np.float32)
+
+
+# ---- synthetic corpus for the data stream -------------------------------------------
+SEPARATOR = 0
+VOCAB = 50304
+
+
+def corpus(seed: int = 7, scale: int = 1):
+    """Sources standing in for a training mix (the pages' corpus is not
+    available): (name, weight, shards), each shard a list of int32 token
+    arrays.  Document lengths are log-normal (median ~660 tokens, a long
+    tail up to 20000), tokens uniform in [1, VOCAB) (0 is the separator)."""
+    g = np.random.default_rng(seed)
+    spec = [("web/cc-2024", 6, 4, 30), ("code/github", 2, 3, 20), ("math/proofs", 1, 2, 12),
+            ("books/long", 1, 1, 4)]
+    out = []
+    for name, weight, n_shards, n_docs in spec:
+        shards = []
+        for _ in range(n_shards):
+            docs = []
+            for _ in range(int(g.integers(max(1, n_docs // 2), n_docs * scale + 1))):
+                mu = 9.0 if name.startswith("books") else 6.5
+                n = int(min(20000, max(1, round(g.lognormal(mu, 1.0)))))
+                docs.append(g.integers(1, VOCAB, n).astype(np.int32))
+            shards.append(docs)
+        out.append((name, weight, shards))
+    return out
