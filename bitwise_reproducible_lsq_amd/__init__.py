@@ -61,6 +61,14 @@ _SIGS = {
     "adamw_step": (i32, [P, P, P, P, i64, P, i32, P]),
     "attn_fwd": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64, P, P]),
     "attn_bwd_dq": (i32, [P, P, P, P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, P]),
+    "brl_stream_create": (i32, [C.c_uint64, i32, P, i32, C.POINTER(C.c_void_p)]),
+    "brl_stream_destroy": (None, [P]),
+    "brl_stream_next": (i32, [P, i64, P, C.POINTER(C.c_int64)]),
+    "brl_stream_step": (i32, [P, i64, i32, i32, P]),
+    "brl_stream_record_bytes": (i64, [P]),
+    "brl_stream_save": (i32, [P, P, i64]),
+    "brl_stream_load": (i32, [P, P, i64]),
+    "brl_philox_u32": (i32, [C.c_uint64, C.c_uint32, C.c_uint64, i64, P, P]),
     "brl_set_tuning": (i64, [i32, i64]),
     "brl_status_string": (C.c_char_p, [i32]),
     "brl_last_error": (C.c_char_p, []),
@@ -347,6 +355,81 @@ def attn_bwd_dq(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tens
     _check(lib().attn_bwd_dq(q, k, v, _ptr(O), _ptr(dO), _ptr(stats), B, S, Hq, Hkv, D, ldq, ldk, ldv, ld,
                              int(window), float(s_v), _ptr(dQ), _stream(stream)))
     return dQ
+
+
+STREAM_WINDOW = 4097
+
+
+class _StreamSource(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("weight", C.c_int64), ("n_shards", C.c_int32),
+                ("shard_docs", C.c_void_p), ("doc_offsets", C.c_void_p), ("tokens", C.c_void_p)]
+
+
+class DataStream:
+    """The topology-invariant data stream (brl_stream_*), host side.  corpus:
+    list of (name, weight, shards), each shard a list of int32 token arrays;
+    the flattened copy made here lives as long as the stream."""
+
+    def __init__(self, seed: int, separator: int, corpus):
+        import numpy as np
+        self._keep = []
+        srcs = (_StreamSource * len(corpus))()
+        for k, (name, weight, shards) in enumerate(corpus):
+            docs = [np.ascontiguousarray(d, np.int32) for sh in shards for d in sh]
+            tokens = np.concatenate(docs) if docs else np.zeros(1, np.int32)
+            offs = np.zeros(len(docs) + 1, np.int64)
+            offs[1:] = np.cumsum([d.size for d in docs])
+            counts = np.array([len(sh) for sh in shards], np.int64)
+            bname = name.encode("utf-8")
+            self._keep += [tokens, offs, counts, bname]
+            srcs[k] = _StreamSource(bname, int(weight), len(shards), counts.ctypes.data, offs.ctypes.data,
+                                    tokens.ctypes.data)
+        self._keep.append(srcs)
+        h = C.c_void_p()
+        _check(lib().brl_stream_create(int(seed) & (2 ** 64 - 1), int(separator), srcs, len(corpus), C.byref(h)))
+        self._h = h
+
+    def next(self, count: int):
+        """(index of the first window, int32 [count, 4097])."""
+        import numpy as np
+        out = np.empty((count, STREAM_WINDOW), np.int32)
+        first = C.c_int64()
+        _check(lib().brl_stream_next(self._h, count, out.ctypes.data, C.byref(first)))
+        return first.value, out
+
+    def step(self, global_batch: int, ranks: int, rank: int):
+        import numpy as np
+        out = np.empty((global_batch // max(ranks, 1), STREAM_WINDOW), np.int32)
+        _check(lib().brl_stream_step(self._h, global_batch, ranks, rank, out.ctypes.data))
+        return out
+
+    def save(self) -> bytes:
+        n = lib().brl_stream_record_bytes(self._h)
+        buf = (C.c_uint8 * n)()
+        _check(lib().brl_stream_save(self._h, buf, n))
+        return bytes(buf)
+
+    def load(self, record: bytes) -> None:
+        buf = (C.c_uint8 * len(record)).from_buffer_copy(record)
+        _check(lib().brl_stream_load(self._h, buf, len(record)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib().brl_stream_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+
+def philox_u32(key: int, stream: int, first: int, n: int, out: Optional[torch.Tensor] = None,
+               hip_stream=None) -> torch.Tensor:
+    """Device draws out[k] = draw(key, stream, first + k) as int32 bit patterns."""
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device="cuda")
+    _check(lib().brl_philox_u32(int(key) & (2 ** 64 - 1), int(stream) & 0xFFFFFFFF, int(first), n, _ptr(out),
+                                _stream(hip_stream)))
+    return out
 
 
 def probe_f32(op: str, a: torch.Tensor, b: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbrlsq.so")
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = ["api.hip", "canon.hip", "fwd.hip", "bwd.hip", "replay.hip", "hash.hip", "optim.hip", "attn.hip"]
+SOURCES = ["api.hip", "canon.hip", "fwd.hip", "bwd.hip", "replay.hip", "hash.hip", "optim.hip", "attn.hip", "stream.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

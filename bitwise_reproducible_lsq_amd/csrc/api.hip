@@ -71,6 +71,10 @@ static brl_status check_hip(hipError_t e, const char* what) {
 
 static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 
+// error reporting for the entry points defined in other translation units
+brl_status report_error(brl_status s, const char* msg) { return fail(s, "%s", msg); }
+brl_status report_hip(hipError_t e, const char* what) { return check_hip(e, what); }
+
 // ---- workspace layout --------------------------------------------------------------
 struct Carver {
     char* base;

@@ -149,6 +149,10 @@ hipError_t launch_probe(int op, const float* a, const float* b, float* out, int6
 
 ExpConsts exp_constants();
 
+// error reporting for entry points outside api.hip (thread-local last error)
+brl_status report_error(brl_status s, const char* msg);
+brl_status report_hip(hipError_t e, const char* what);
+
 // ---- attention (int8 P.V) ----------------------------------------------------
 hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
                            int64_t Hkv, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,

@@ -288,6 +288,69 @@ BRL_API brl_status attn_bwd_dq(const float* Q, const float* K, const float* V, c
                                int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v,
                                float* dQ, void* stream);
 
+/*
+ * Topology-invariant data stream (onedev.kr summary, "What differs": one
+ * canonical stream independent of world size and rank, three generators --
+ * source interleaving seeded by the training seed alone, shard order seeded
+ * by (seed, SHA-256(source name), epoch), document order seeded by (seed,
+ * SHA-256(source name), epoch, shard) -- documents joined with a separator
+ * and cut into windows of 4,097 tokens; rank r of R owns windows m with
+ * m mod R = r; a rank-independent resume record) with counter-based draws
+ * ("How": values as pure functions of the seed and a logical position).
+ * This library's reading:
+ *   draw(key, stream, i): word i mod 4 of Philox4x32-10 (Salmon et al.,
+ *     SC'11) with counter (i div 4 as two 32-bit words, stream, 0);
+ *   bounded(x, n) = (x * n) >> 32;
+ *   an order of n items: Fisher-Yates from the top, draw t (stream 0)
+ *     swapping position n-1-t with bounded(draw, n-t);
+ *   shard-order key: first 8 bytes, little endian, of SHA-256("shard" |
+ *     le64 seed | SHA-256(name) | le64 epoch); document-order key likewise
+ *     from "doc" | ... | le64 shard;
+ *   source of document draw t: the first source whose cumulative weight
+ *     exceeds bounded(draw(seed, 0x6d6978, t), total weight);
+ *   a source moves to its next epoch when a document is requested after its
+ *     last shard; shards without documents are skipped.
+ * The corpus stays caller-owned and must outlive the stream (it is read,
+ * never copied).  A source: NUL-terminated UTF-8 name, weight >= 0, shard
+ * document counts, shard-major ascending token offsets (one more than the
+ * document count), token ids.  Every source with weight > 0 needs a
+ * document.  The stream object is host memory owned by the caller (create /
+ * destroy); calls on one stream must not overlap.
+ */
+#define BRL_STREAM_WINDOW 4097
+typedef struct brl_stream brl_stream;
+typedef struct brl_stream_source {
+    const char* name;
+    int64_t weight;
+    int32_t n_shards;
+    const int64_t* shard_docs;    /* [n_shards] */
+    const int64_t* doc_offsets;   /* [sum(shard_docs) + 1] */
+    const int32_t* tokens;
+} brl_stream_source;
+BRL_API brl_status brl_stream_create(uint64_t seed, int32_t separator, const brl_stream_source* sources,
+                                     int32_t n_sources, brl_stream** out);
+BRL_API void brl_stream_destroy(brl_stream* s);
+/* The next `count` windows of the global stream into out (host, count x 4097
+ * int32); *first_window (nullable) receives the index m of the first. */
+BRL_API brl_status brl_stream_next(brl_stream* s, int64_t count, int32_t* out, int64_t* first_window);
+/* One global batch of `global_batch` windows (a multiple of ranks); out
+ * (host, global_batch / ranks x 4097) receives the windows of `rank`. */
+BRL_API brl_status brl_stream_step(brl_stream* s, int64_t global_batch, int32_t ranks, int32_t rank,
+                                   int32_t* out);
+/* Resume record: "BRLSTRM1" | le64 seed | le32 sources | le32 separator |
+ * le64 next window | le64 mix draws | per source: SHA-256(name), le64 epoch,
+ * le64 shard position, le64 document position, le64 documents consumed |
+ * le64 buffered tokens | buffered tokens (le32; the tail of the last
+ * document taken, which can exceed one window).  Independent of R.  Loading
+ * checks seed, separator and source digests. */
+BRL_API int64_t brl_stream_record_bytes(const brl_stream* s);
+BRL_API brl_status brl_stream_save(const brl_stream* s, uint8_t* buf, int64_t cap);
+BRL_API brl_status brl_stream_load(brl_stream* s, const uint8_t* buf, int64_t n);
+/* Device draws: out[k] = draw(key, stream, first + k) for k < n (device
+ * pointer, 4-byte aligned). */
+BRL_API brl_status brl_philox_u32(uint64_t key, uint32_t stream, uint64_t first, int64_t n, uint32_t* out,
+                                  void* hip_stream);
+
 /* Conformance probe of the device's binary32 operations, as the kernels use
  * them: out[i] = op(a[i], b[i]) for op 0 add, 1 sub, 2 mul, 3 div, 4 sqrt (a),
  * 5 int32 bits of a -> float, 6 round-to-nearest-even integral (a),
