@@ -62,6 +62,48 @@ ADAMW_BYTES_PER_ELEM = 28                                   # 8 x 805 MB = 6.44 
 ATTN_D = 128
 
 
+def stream_bench(torch, brl, dev, with_cpu: bool):
+    """The data stream (host, C++) on the synthetic corpus, and the device
+    Philox draws (16 B written per 4-word block)."""
+    import synth
+    corpus = synth.corpus(7, scale=8)
+    st = brl.DataStream(1, synth.SEPARATOR, corpus)
+    st.next(8)
+    t0 = time.perf_counter()
+    n_win = 400
+    st.next(n_win)
+    dt = time.perf_counter() - t0
+    out = {"data_stream": {"windows": n_win, "s": round(dt, 4), "windows_per_s": round(n_win / dt, 1),
+                           "tokens_per_s": round(n_win * brl.STREAM_WINDOW / dt, 1), "threads": 1}}
+    if with_cpu:
+        from oracle import datastream as ds
+        orc = ds.Stream(1, [ds.Source(n, w, sh) for n, w, sh in corpus], synth.SEPARATOR)
+        t0 = time.perf_counter()
+        for _ in range(20):
+            orc.next_window()
+        out["data_stream"]["oracle_windows_per_s"] = round(20 / (time.perf_counter() - t0), 2)
+    n = 1 << 28
+    buf = torch.empty(n, dtype=torch.int32, device=dev)
+    brl.philox_u32(5, 0, 0, n, out=buf)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        brl.philox_u32(5, 0, 0, n, out=buf)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 3
+    gbps = 4.0 * n / (ms * 1e-3) / 1e9
+    out["philox"] = {"draws": n, "ms": round(ms, 4), "draws_per_s": round(n / (ms * 1e-3), 1),
+                     "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                  "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                                  "note": "4 B written per draw; about 140 VALU issue slots per 4-word block "
+                                          "(10 rounds of two 32x32->64 multiplies), close to the HBM ridge"}}
+    del buf
+    return out
+
+
 def attention_bench(torch, brl, dev):
     """attn_fwd on one Open-1B layer's microbatch (4 x 4096 tokens, 16 query /
     4 KV heads of 128), window 512 and full causal; device-generated inputs
@@ -363,6 +405,7 @@ def main():
     }
     del hstate
     result["attention"] = attention_bench(torch, brl, dev)
+    result.update(stream_bench(torch, brl, dev, not args.no_cpu_baseline))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
         result["cpu_baseline"]["state_hash_GBps"] = cpu_hash_rate([partials[0].cpu().numpy()])
