@@ -405,6 +405,8 @@ def main():
     }
     del hstate
     result["attention"] = attention_bench(torch, brl, dev)
+    if not args.no_cpu_baseline:
+        result["attention"]["cpu_baseline"] = cpu_attention_rate()
     result.update(stream_bench(torch, brl, dev, not args.no_cpu_baseline))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
@@ -419,6 +421,33 @@ def cpu_hash_rate(tensors) -> float:
     sh.state_hash(tensors)
     dt = time.perf_counter() - t0
     return round(sum(t.nbytes for t in tensors) / dt / 1e9, 3)
+
+
+def cpu_attention_rate():
+    """The attention oracle on sampled rows of the window-512 layer: rows/s
+    and the same algorithmic ops per second as the GPU figure (2*D per
+    allowed logit; dQ three such products)."""
+    import numpy as np
+
+    import oracle
+    import synth
+    case = synth.ATTENTION_CASES["attn_window"]
+    Q, K, V = synth.attention_inputs(case)
+    g = np.random.default_rng(0)
+    rows = np.sort(g.choice(case.B * case.S * case.Hq, 256, replace=False))
+    keys = sum(min(int(r // case.Hq) % case.S + 1, case.window) for r in rows)
+    t0 = time.perf_counter()
+    O = oracle.attn_fwd_rows(Q, K, V, case.window, case.s_v, rows)
+    t_fwd = time.perf_counter() - t0
+    Ofull = np.zeros_like(Q).reshape(-1, ATTN_D)
+    Ofull[rows] = O
+    dO = synth.normal(case.seed, "dY", Q.shape, 1e-3)
+    t0 = time.perf_counter()
+    oracle.attn_bwd_dq(Q, K, V, Ofull.reshape(Q.shape), dO, case.window, case.s_v, rows=rows)
+    t_dq = time.perf_counter() - t0
+    return {"kind": "oracle", "cores": oracle.num_threads(), "sample": f"256 random rows of the window-512 layer",
+            "fwd_T_ops_per_s": round(2.0 * ATTN_D * keys / t_fwd / 1e12, 6),
+            "dq_T_ops_per_s": round(3 * 2.0 * ATTN_D * keys / t_dq / 1e12, 6)}
 
 
 def cpu_baseline(inp, budget_s: float):
