@@ -63,7 +63,14 @@ struct AttnSmem {
             int8_t pq[kAQ][kAK];    // q_p, rows of 64 keys, 16-byte chunks swizzled
             int8_t vq[kAD][kAK];    // q_v transposed: row d holds 64 keys, swizzled
         } pv;
-        float pmax[kAQ][16];        // pass 1: partial row maxima
+        struct {
+            float nq[kAQ];          // pass 1: Euclidean norms of the Q rows (rounded up)
+            float hmax[2][kAQ];     // pass 1: approximate row maxima of the tile's key halves
+            float arun[kAQ];        // pass 1: running approximate row maxima
+            float nkp[4][kAK];      // pass 1: partial squared norms of the K rows
+            int ncand;              // pass 1: candidates of the tile
+            uint16_t cand[kAQ * kAK];   // pass 1: (row << 6) | key
+        } p1;
     } u;
     float st[kAQ][kAStack];         // per-row stacks of key-tile pair sums
     float rowmax[kAQ];
@@ -145,7 +152,7 @@ __device__ __forceinline__ float dpp_shr8(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
 }
 
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -176,31 +183,122 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a) {
         return i < a.S && j <= i && j >= lo;
     };
 
-    // ---- pass 1: row maxima ----
-    float mx[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) mx[x] = __int_as_float(0xff800000);
+    // ---- pass 1: exact row maxima from a cheap approximation ----
+    // a_ij = fl(sum_d bf16(q_id) bf16(k_jd) in fp32) * c on the matrix cores
+    // differs from the exact logit s_ij by at most E_ij = c * 0.0158 *
+    // |q_i| |k_j| (bf16 operands: 2^-7 relative each; fp32 sums of 128 terms
+    // in any order: gamma_128; the canonical sum: gamma_35; Cauchy-Schwarz
+    // for sum |q_d k_d|).  With A the largest a over the row's keys seen so
+    // far, a key whose a_ij < A - 2E_ij cannot hold the row's maximum, so the
+    // exact logit is computed (in the canonical order of pass 2) only for the
+    // others, and m_i is the largest of those.  A only grows, so the test
+    // against the running value keeps every key the final value would.
+    const int wmt = wave & 1, wnt = wave >> 1;     // this wave's 32 x 32 sub-tile of the 64 x 64 tile
+    typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+    typedef float v16f_a __attribute__((ext_vector_type(16)));
+    __syncthreads();                               // the Q tile is in LDS
+    if (tid < kAQ) {
+        float n2 = 0.0f;
+        for (int d = 0; d < kAD; ++d) n2 = f_add(n2, f_mul(sm.qs[d][tid], sm.qs[d][tid]));
+        sm.u.p1.nq[tid] = f_mul(f_sqrt(n2), 1.0f + 0x1p-10f);
+        sm.u.p1.arun[tid] = __int_as_float(0xff800000);
+        // order-preserving integer image of -inf (negative floats: bits ^ 0x7fffffff)
+        reinterpret_cast<int*>(sm.rowmax)[tid] = (int)(0xff800000u ^ 0x7fffffffu);
+    }
+    const float ebound = f_mul(a.c, 0.0158f);
     for (int64_t kt = kt0; kt <= kt1; ++kt) {
         const int64_t j0 = kt * kAK;
         __syncthreads();
         attn_load_kt(a.K, a.ldk, base + j0, a.S - j0, hk, sm.ks);
         __syncthreads();
-        float s[4][4];
-        attn_logits_from(sm.qs, sm.ks, ti, tj, a.c, s);
+        {
+            // |k_j|^2 in four partial sums of 32 terms (any order: a bound)
+            const int key = tid & 63, part = tid >> 6;
+            float n2 = 0.0f;
+            for (int d = 32 * part; d < 32 * part + 32; ++d) n2 = f_add(n2, f_mul(sm.ks[d][key], sm.ks[d][key]));
+            sm.u.p1.nkp[part][key] = n2;
+            if (tid == 0) sm.u.p1.ncand = 0;
+        }
+        v16f_a ap = {};
+        {
+            const int key = wnt * 32 + (lane & 31), row = wmt * 32 + (lane & 31);
+#pragma unroll 2
+            for (int ks = 0; ks < kAD / 16; ++ks) {
+                v8bf qb, kb;
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+                for (int e = 0; e < 8; ++e) {
+                    qb[e] = (__bf16)sm.qs[16 * ks + 8 * (lane >> 5) + e][row];
+                    kb[e] = (__bf16)sm.ks[16 * ks + 8 * (lane >> 5) + e][key];
+                }
+                ap = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb, kb, ap, 0, 0, 0);
+            }
+        }
+        // element r of this lane: row wmt*32 + 8(r>>2) + 4(lane>>5) + (r&3), key wnt*32 + (lane&31)
+        const int jl = wnt * 32 + (lane & 31);
+        float hm[16];
 #pragma unroll
-            for (int y = 0; y < 4; ++y)
-                if (allowed(q0 + 4 * ti + x, j0 + 4 * tj + y) && s[x][y] > mx[x]) mx[x] = s[x][y];
+        for (int r = 0; r < 16; ++r) {
+            const int il = wmt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            ap[r] = f_mul(ap[r], a.c);
+            hm[r] = allowed(q0 + il, j0 + jl) ? ap[r] : __int_as_float(0xff800000);
+        }
+        // row maxima over the 32 keys of the half (lanes with equal lane >> 5)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int sh = 16; sh >= 1; sh >>= 1) {
+                const float o = __shfl_xor(hm[r], sh, 32);
+                hm[r] = o > hm[r] ? o : hm[r];
+            }
+        if ((lane & 31) == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.u.p1.hmax[wnt][wmt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)] = hm[r];
+        }
+        __syncthreads();
+        if (tid < kAQ) {
+            float m = sm.u.p1.arun[tid];
+            m = sm.u.p1.hmax[0][tid] > m ? sm.u.p1.hmax[0][tid] : m;
+            m = sm.u.p1.hmax[1][tid] > m ? sm.u.p1.hmax[1][tid] : m;
+            sm.u.p1.arun[tid] = m;
+        }
+        __syncthreads();
+        // candidates: listed, then their exact logits (pass 2's order) taken
+        // one per thread into an order-free maximum
+        {
+            const float n2 = f_add(f_add(sm.u.p1.nkp[0][jl], sm.u.p1.nkp[1][jl]),
+                                   f_add(sm.u.p1.nkp[2][jl], sm.u.p1.nkp[3][jl]));
+            const float nk = f_mul(f_sqrt(n2), 1.0f + 0x1p-10f);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int il = wmt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (!allowed(q0 + il, j0 + jl)) continue;
+                const float e2 = f_add(f_mul(f_mul(f_mul(ebound, sm.u.p1.nq[il]), nk), 2.0f), 0x1p-80f);
+                if (ap[r] >= f_sub(sm.u.p1.arun[il], e2))
+                    sm.u.p1.cand[atomicAdd(&sm.u.p1.ncand, 1)] = (uint16_t)((il << 6) | jl);
+            }
+        }
+        __syncthreads();
+        const int ncand = sm.u.p1.ncand;
+        for (int c = tid; c < ncand; c += 256) {
+            const int il = sm.u.p1.cand[c] >> 6, jc = sm.u.p1.cand[c] & 63;
+            float b01 = 0.0f, b2 = 0.0f, cur = 0.0f;
+            for (int blk = 0; blk < kAD / 32; ++blk) {
+                cur = f_mul(sm.qs[32 * blk][il], sm.ks[32 * blk][jc]);
+                for (int dd = 1; dd < 32; ++dd)
+                    cur = f_add(cur, f_mul(sm.qs[32 * blk + dd][il], sm.ks[32 * blk + dd][jc]));
+                if (blk == 0) b01 = cur;
+                if (blk == 1) b01 = f_add(b01, cur);
+                if (blk == 2) b2 = cur;
+            }
+            const float sx = f_mul(f_add(b01, f_add(b2, cur)), a.c);
+            const int bits = __float_as_int(sx);
+            atomicMax(reinterpret_cast<int*>(&sm.rowmax[il]), bits >= 0 ? bits : bits ^ 0x7fffffff);
+        }
     }
     __syncthreads();
-#pragma unroll
-    for (int x = 0; x < 4; ++x) sm.u.pmax[4 * ti + x][tj] = mx[x];
-    __syncthreads();
     if (tid < kAQ) {
-        float m = sm.u.pmax[tid][0];
-        for (int u = 1; u < 16; ++u) m = sm.u.pmax[tid][u] > m ? sm.u.pmax[tid][u] : m;
-        sm.rowmax[tid] = m;
+        const int key = __float_as_int(sm.rowmax[tid]);
+        sm.rowmax[tid] = __int_as_float(key >= 0 ? key : key ^ 0x7fffffff);
     }
 
     // ---- pass 2: p, row sums, int8 P.V ----

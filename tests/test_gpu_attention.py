@@ -118,3 +118,20 @@ def test_attention_dq_parity(B, S, Hq, Hkv, window, s_v):
     Oh = O.cpu().numpy()
     assert_bitwise(Oh, oracle.attn_fwd(Q, K, V, window, s_v), "O")
     assert_bitwise(dQ, oracle.attn_bwd_dq(Q, K, V, Oh, dO, window, s_v), f"dQ (S={S} w={window})")
+
+
+@pytest.mark.parametrize("window", [0, 40])
+def test_attention_equal_and_near_equal_logits(window):
+    """Every key a candidate of the first pass: Q = 0 (all logits 0) and keys
+    that differ by a few ulp (logits closer than the approximation's bound),
+    so the exact maximum comes from the candidate path alone."""
+    B, S, Hq, Hkv, s_v = 1, 150, 4, 2, 0.05
+    g = np.random.default_rng(window)
+    V = g.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    base = g.standard_normal(D).astype(np.float32)
+    K = np.tile(base, (B, S, Hkv, 1)).astype(np.float32)
+    K += (g.integers(-3, 4, K.shape) * np.spacing(np.abs(K))).astype(np.float32)
+    for Q in (np.zeros((B, S, Hq, D), np.float32), g.standard_normal((B, S, Hq, D)).astype(np.float32)):
+        O = brl.attn_fwd(*(torch.from_numpy(t).cuda() for t in (Q, K, V)), window, s_v)
+        torch.cuda.synchronize()
+        assert_bitwise(O, oracle.attn_fwd(Q, K, V, window, s_v), f"O (near-equal logits, window {window})")
