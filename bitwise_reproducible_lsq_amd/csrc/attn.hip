@@ -112,6 +112,42 @@ __device__ __forceinline__ void canon_dot4x4(const float (*A)[kAQ], const float 
     }
 }
 
+// The same sums for NX rows x NY keys per thread (rows NX*ti.., keys NY*tj..);
+// each output sees exactly the operations of canon_dot4x4.
+template <int NX, int NY>
+__device__ __forceinline__ void canon_dot(const float (*A)[kAQ], const float (*B)[kAK], int ti, int tj,
+                                          float (&s)[NX][NY]) {
+    float b01[NX][NY], b2[NX][NY], cur[NX][NY];
+#pragma unroll
+    for (int blk = 0; blk < kAD / 32; ++blk) {
+#pragma unroll 4
+        for (int dd = 0; dd < 32; ++dd) {
+            const int d = blk * 32 + dd;
+            float a[NX], b[NY];
+#pragma unroll
+            for (int x = 0; x < NX; ++x) a[x] = A[d][NX * ti + x];
+#pragma unroll
+            for (int y = 0; y < NY; ++y) b[y] = B[d][NY * tj + y];
+#pragma unroll
+            for (int x = 0; x < NX; ++x)
+#pragma unroll
+                for (int y = 0; y < NY; ++y) {
+                    const float pr = f_mul(a[x], b[y]);
+                    cur[x][y] = dd == 0 ? pr : f_add(cur[x][y], pr);
+                }
+        }
+#pragma unroll
+        for (int x = 0; x < NX; ++x)
+#pragma unroll
+            for (int y = 0; y < NY; ++y) {
+                if (blk == 0) b01[x][y] = cur[x][y];
+                if (blk == 1) b01[x][y] = f_add(b01[x][y], cur[x][y]);
+                if (blk == 2) b2[x][y] = cur[x][y];
+                if (blk == 3) s[x][y] = f_add(b01[x][y], f_add(b2[x][y], cur[x][y]));
+            }
+    }
+}
+
 // 16 logits of this thread: rows 4ti..4ti+3, keys 4tj..4tj+3 of the tile
 __device__ __forceinline__ void attn_logits_from(const float (*qs)[kAQ], const float (*ks)[kAK], int ti, int tj,
                                                  float c, float s[4][4]) {
@@ -125,11 +161,12 @@ __device__ __forceinline__ void attn_logits_from(const float (*qs)[kAQ], const f
 // 64 rows (rows_left of them real) x 128 floats of head `head` into
 // dst[d][row]: each item is 4 rows x 4 d, loaded as four 16-byte rows and
 // stored as four 16-byte columns
+template <int NT = 256>
 __device__ __forceinline__ void attn_load_kt(const float* src, int64_t ld, int64_t row0, int64_t rows_left,
                                              int64_t head, float (*dst)[kAK]) {
 #pragma unroll
-    for (int it = 0; it < (kAK / 4) * (kAD / 4) / 256; ++it) {
-        const int e = threadIdx.x + 256 * it;
+    for (int it = 0; it < (kAK / 4) * (kAD / 4) / NT; ++it) {
+        const int e = threadIdx.x + NT * it;
         const int rq = e & 15, dq = e >> 4;
         vf4 v[4];
 #pragma unroll
@@ -503,11 +540,13 @@ struct AttnBwdSmem {
     float rowm[kAQ], rowl[kAQ], rowdelta[kAQ];
 };
 
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+constexpr int kDqThreads = 512;
+
+__global__ __launch_bounds__(kDqThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     AttnBwdSmem& sm = *reinterpret_cast<AttnBwdSmem*>(smem_raw);
     const int tid = threadIdx.x;
-    const int ti = tid >> 4, tj = tid & 15;
+    const int ti = tid >> 5, tj = tid & 31;         // 4 rows x 2 keys of the 64 x 64 tile
 
     const unsigned nqb = (unsigned)((a.S + kAQ - 1) / kAQ), hq = (unsigned)a.Hq;
     const unsigned qb = blockIdx.x % nqb;
@@ -522,8 +561,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     const int64_t khi = q0 + qrows - 1;
     const int64_t kt0 = klo / kAK, kt1 = khi / kAK;
 
-    attn_load_kt(a.Q, a.ldq, base + q0, qrows, h, sm.qs);
-    attn_load_kt(a.dO, a.ldo, base + q0, qrows, h, sm.gs);
+    attn_load_kt<kDqThreads>(a.Q, a.ldq, base + q0, qrows, h, sm.qs);
+    attn_load_kt<kDqThreads>(a.dO, a.ldo, base + q0, qrows, h, sm.gs);
     if (tid < kAQ) {
         float m = 0.0f, l = 1.0f, delta = 0.0f;
         if (tid < qrows) {
@@ -550,20 +589,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
         return i < a.S && j <= i && j >= lo;
     };
     const Quantizer qz(a.s_v);
-    // dQ outputs of this thread: row r = tid / 4, d = d0 .. d0 + 31
-    const int r = tid >> 2, d0 = (tid & 3) * 32;
-    int64_t acc[32];
+    // dQ outputs of this thread: row r = tid / 8, d = d0 .. d0 + 15
+    const int r = tid >> 3, d0 = (tid & 7) * 16;
+    int64_t acc[16];
 #pragma unroll
-    for (int x = 0; x < 32; ++x) acc[x] = 0;
+    for (int x = 0; x < 16; ++x) acc[x] = 0;
 
     for (int64_t kt = kt0; kt <= kt1; ++kt) {
         const int64_t j0 = kt * kAK;
         __syncthreads();
-        attn_load_kt(a.K, a.ldk, base + j0, a.S - j0, hk, sm.ks);
+        attn_load_kt<kDqThreads>(a.K, a.ldk, base + j0, a.S - j0, hk, sm.ks);
         // V^ = fl(q_v * s_v), d-major
 #pragma unroll
-        for (int it = 0; it < (kAK / 4) * (kAD / 4) / 256; ++it) {
-            const int e = tid + 256 * it;
+        for (int it = 0; it < (kAK / 4) * (kAD / 4) / kDqThreads; ++it) {
+            const int e = tid + kDqThreads * it;
             const int rq = e & 15, dq = e >> 4;
             vf4 v[4];
 #pragma unroll
@@ -584,15 +623,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
             }
         }
         __syncthreads();
-        float sc[4][4], dp[4][4];
-        attn_logits_from(sm.qs, sm.ks, ti, tj, a.c, sc);
-        canon_dot4x4(sm.gs, sm.u.vs, ti, tj, dp);
+        float sc[4][2], dp[4][2];
+        canon_dot<4, 2>(sm.qs, sm.ks, ti, tj, sc);
+        canon_dot<4, 2>(sm.gs, sm.u.vs, ti, tj, dp);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int i = 4 * ti + x;
 #pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                const int j = 4 * tj + y;
+            for (int y = 0; y < 2; ++y) {
+                const int j = 2 * tj + y;
+                sc[x][y] = f_mul(sc[x][y], a.c);
                 float dsv = 0.0f;
                 if (allowed(q0 + i, j0 + j)) {
                     const float p = own_exp(f_sub(sc[x][y], sm.rowm[i]), a.ek);
@@ -604,8 +644,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
         __syncthreads();
         // K tile again, key-major, over the V^ buffer
 #pragma unroll
-        for (int it = 0; it < kAK * (kAD / 4) / 256; ++it) {
-            const int e = tid + 256 * it;
+        for (int it = 0; it < kAK * (kAD / 4) / kDqThreads; ++it) {
+            const int e = tid + kDqThreads * it;
             const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
             vf4 v = {0.0f, 0.0f, 0.0f, 0.0f};
             if (j0 + row < a.S) v = *reinterpret_cast<const vf4*>(a.K + (base + j0 + row) * a.ldk + hk * kAD + d4);
@@ -613,14 +653,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
         }
         __syncthreads();
         // tile sums u over the 64 keys: two 32-key blocks left to right, then the pair
-        float b0[32], cur[32];
+        float b0[16], cur[16];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             for (int jj = 0; jj < 32; ++jj) {
                 const int j = 32 * blk + jj;
                 const float dsv = sm.ds[r][j];
 #pragma unroll
-                for (int q4 = 0; q4 < 8; ++q4) {
+                for (int q4 = 0; q4 < 4; ++q4) {
                     const vf4 kv = *reinterpret_cast<const vf4*>(&sm.u.kt[j][d0 + 4 * q4]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -631,11 +671,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
             }
             if (blk == 0) {
 #pragma unroll
-                for (int x = 0; x < 32; ++x) b0[x] = cur[x];
+                for (int x = 0; x < 16; ++x) b0[x] = cur[x];
             }
         }
 #pragma unroll
-        for (int x = 0; x < 32; ++x) {
+        for (int x = 0; x < 16; ++x) {
             const float u = f_add(b0[x], cur[x]);
             acc[x] += (int64_t)__builtin_rint((double)u * 0x1p40);
         }
@@ -644,7 +684,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     if (r < qrows) {
         float* out = a.dQ + (base + q0 + r) * a.ldo + h * kAD + d0;
 #pragma unroll
-        for (int q4 = 0; q4 < 8; ++q4) {
+        for (int q4 = 0; q4 < 4; ++q4) {
             vf4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = f_mul(f_mul((float)acc[4 * q4 + e], 0x1p-40f), a.c);
@@ -672,7 +712,7 @@ hipError_t launch_attn_bwd_dq(const float* Q, const float* K, const float* V, co
     }
     const int64_t blocks = B * Hq * ceil_div(S, kAQ);
     if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)blocks), dim3(256), sizeof(AttnBwdSmem), st, a);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)blocks), dim3(kDqThreads), sizeof(AttnBwdSmem), st, a);
     return hipGetLastError();
 }
 
