@@ -164,9 +164,8 @@ __device__ __forceinline__ void attn_logits_from(const float (*qs)[kAQ], const f
 template <int NT = 256>
 __device__ __forceinline__ void attn_load_kt(const float* src, int64_t ld, int64_t row0, int64_t rows_left,
                                              int64_t head, float (*dst)[kAK]) {
-#pragma unroll
-    for (int it = 0; it < (kAK / 4) * (kAD / 4) / NT; ++it) {
-        const int e = threadIdx.x + NT * it;
+    static_assert(NT <= (kAK / 4) * (kAD / 4) * 2, "at most two threads per 16-byte column item");
+    for (int e = threadIdx.x; e < (kAK / 4) * (kAD / 4); e += NT) {
         const int rq = e & 15, dq = e >> 4;
         vf4 v[4];
 #pragma unroll
@@ -540,13 +539,13 @@ struct AttnBwdSmem {
     float rowm[kAQ], rowl[kAQ], rowdelta[kAQ];
 };
 
-constexpr int kDqThreads = 512;
+constexpr int kDqThreads = 1024;
 
 __global__ __launch_bounds__(kDqThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     AttnBwdSmem& sm = *reinterpret_cast<AttnBwdSmem*>(smem_raw);
     const int tid = threadIdx.x;
-    const int ti = tid >> 5, tj = tid & 31;         // 4 rows x 2 keys of the 64 x 64 tile
+    const int ti = tid >> 5, tj = tid & 31;         // 2 rows x 2 keys of the 64 x 64 tile
 
     const unsigned nqb = (unsigned)((a.S + kAQ - 1) / kAQ), hq = (unsigned)a.Hq;
     const unsigned qb = blockIdx.x % nqb;
@@ -589,11 +588,11 @@ __global__ __launch_bounds__(kDqThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
         return i < a.S && j <= i && j >= lo;
     };
     const Quantizer qz(a.s_v);
-    // dQ outputs of this thread: row r = tid / 8, d = d0 .. d0 + 15
-    const int r = tid >> 3, d0 = (tid & 7) * 16;
-    int64_t acc[16];
+    // dQ outputs of this thread: row r = tid / 16, d = d0 .. d0 + 7
+    const int r = tid >> 4, d0 = (tid & 15) * 8;
+    int64_t acc[8];
 #pragma unroll
-    for (int x = 0; x < 16; ++x) acc[x] = 0;
+    for (int x = 0; x < 8; ++x) acc[x] = 0;
 
     for (int64_t kt = kt0; kt <= kt1; ++kt) {
         const int64_t j0 = kt * kAK;
@@ -601,8 +600,7 @@ __global__ __launch_bounds__(kDqThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
         attn_load_kt<kDqThreads>(a.K, a.ldk, base + j0, a.S - j0, hk, sm.ks);
         // V^ = fl(q_v * s_v), d-major
 #pragma unroll
-        for (int it = 0; it < (kAK / 4) * (kAD / 4) / kDqThreads; ++it) {
-            const int e = tid + kDqThreads * it;
+        for (int e = tid; e < (kAK / 4) * (kAD / 4); e += kDqThreads) {
             const int rq = e & 15, dq = e >> 4;
             vf4 v[4];
 #pragma unroll
@@ -623,12 +621,12 @@ __global__ __launch_bounds__(kDqThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
             }
         }
         __syncthreads();
-        float sc[4][2], dp[4][2];
-        canon_dot<4, 2>(sm.qs, sm.ks, ti, tj, sc);
-        canon_dot<4, 2>(sm.gs, sm.u.vs, ti, tj, dp);
+        float sc[2][2], dp[2][2];
+        canon_dot<2, 2>(sm.qs, sm.ks, ti, tj, sc);
+        canon_dot<2, 2>(sm.gs, sm.u.vs, ti, tj, dp);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int i = 4 * ti + x;
+        for (int x = 0; x < 2; ++x) {
+            const int i = 2 * ti + x;
 #pragma unroll
             for (int y = 0; y < 2; ++y) {
                 const int j = 2 * tj + y;
@@ -644,8 +642,7 @@ __global__ __launch_bounds__(kDqThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
         __syncthreads();
         // K tile again, key-major, over the V^ buffer
 #pragma unroll
-        for (int it = 0; it < kAK * (kAD / 4) / kDqThreads; ++it) {
-            const int e = tid + kDqThreads * it;
+        for (int e = tid; e < kAK * (kAD / 4); e += kDqThreads) {
             const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
             vf4 v = {0.0f, 0.0f, 0.0f, 0.0f};
             if (j0 + row < a.S) v = *reinterpret_cast<const vf4*>(a.K + (base + j0 + row) * a.ldk + hk * kAD + d4);
@@ -653,14 +650,14 @@ __global__ __launch_bounds__(kDqThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
         }
         __syncthreads();
         // tile sums u over the 64 keys: two 32-key blocks left to right, then the pair
-        float b0[16], cur[16];
+        float b0[8], cur[8];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             for (int jj = 0; jj < 32; ++jj) {
                 const int j = 32 * blk + jj;
                 const float dsv = sm.ds[r][j];
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
+                for (int q4 = 0; q4 < 2; ++q4) {
                     const vf4 kv = *reinterpret_cast<const vf4*>(&sm.u.kt[j][d0 + 4 * q4]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -671,11 +668,11 @@ __global__ __launch_bounds__(kDqThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
             }
             if (blk == 0) {
 #pragma unroll
-                for (int x = 0; x < 16; ++x) b0[x] = cur[x];
+                for (int x = 0; x < 8; ++x) b0[x] = cur[x];
             }
         }
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
+        for (int x = 0; x < 8; ++x) {
             const float u = f_add(b0[x], cur[x]);
             acc[x] += (int64_t)__builtin_rint((double)u * 0x1p40);
         }
@@ -684,7 +681,7 @@ __global__ __launch_bounds__(kDqThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
     if (r < qrows) {
         float* out = a.dQ + (base + q0 + r) * a.ldo + h * kAD + d0;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
+        for (int q4 = 0; q4 < 2; ++q4) {
             vf4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = f_mul(f_mul((float)acc[4 * q4 + e], 0x1p-40f), a.c);
