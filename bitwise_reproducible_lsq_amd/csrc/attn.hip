@@ -64,10 +64,10 @@ struct AttnSmem {
             int8_t vq[kAD][kAK];    // q_v transposed: row d holds 64 keys, swizzled
         } pv;
         struct {
-            float nq[kAQ];          // pass 1: Euclidean norms of the Q rows (rounded up)
+            double nq[kAQ];         // pass 1: Euclidean norms of the Q rows (rounded up)
             float hmax[2][kAQ];     // pass 1: approximate row maxima of the tile's key halves
             float arun[kAQ];        // pass 1: running approximate row maxima
-            float nkp[4][kAK];      // pass 1: partial squared norms of the K rows
+            double nkp[4][kAK];     // pass 1: partial squared norms of the K rows
             int ncand;              // pass 1: candidates of the tile
             uint16_t cand[kAQ * kAK];   // pass 1: (row << 6) | key
         } p1;
@@ -222,9 +222,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // ---- pass 1: exact row maxima from a cheap approximation ----
     // a_ij = fl(sum_d bf16(q_id) bf16(k_jd) in fp32) * c on the matrix cores
     // differs from the exact logit s_ij by at most E_ij = c * 0.0158 *
-    // |q_i| |k_j| (bf16 operands: 2^-7 relative each; fp32 sums of 128 terms
-    // in any order: gamma_128; the canonical sum: gamma_35; Cauchy-Schwarz
-    // for sum |q_d k_d|).  With A the largest a over the row's keys seen so
+    // |q_i| |k_j| + 2^-80 (bf16 operands: 2^-7 relative each; fp32 sums of
+    // 128 terms in any order: gamma_128; the canonical sum: gamma_35;
+    // Cauchy-Schwarz for sum |q_d k_d|; products flushed below 2^-126 in
+    // either sum: under 2^-119 in all).  Norms and bound are formed in
+    // binary64, where no square of a binary32 value under- or overflows.  With A the largest a over the row's keys seen so
     // far, a key whose a_ij < A - 2E_ij cannot hold the row's maximum, so the
     // exact logit is computed (in the canonical order of pass 2) only for the
     // others, and m_i is the largest of those.  A only grows, so the test
@@ -234,14 +236,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     typedef float v16f_a __attribute__((ext_vector_type(16)));
     __syncthreads();                               // the Q tile is in LDS
     if (tid < kAQ) {
-        float n2 = 0.0f;
-        for (int d = 0; d < kAD; ++d) n2 = f_add(n2, f_mul(sm.qs[d][tid], sm.qs[d][tid]));
-        sm.u.p1.nq[tid] = f_mul(f_sqrt(n2), 1.0f + 0x1p-10f);
+        double n2 = 0.0;
+        for (int d = 0; d < kAD; ++d) n2 += (double)sm.qs[d][tid] * (double)sm.qs[d][tid];
+        sm.u.p1.nq[tid] = __builtin_sqrt(n2) * (1.0 + 0x1p-30);
         sm.u.p1.arun[tid] = __int_as_float(0xff800000);
         // order-preserving integer image of -inf (negative floats: bits ^ 0x7fffffff)
         reinterpret_cast<int*>(sm.rowmax)[tid] = (int)(0xff800000u ^ 0x7fffffffu);
     }
-    const float ebound = f_mul(a.c, 0.0158f);
+    const double ebound = (double)a.c * 0.0158;
     for (int64_t kt = kt0; kt <= kt1; ++kt) {
         const int64_t j0 = kt * kAK;
         __syncthreads();
@@ -250,8 +252,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         {
             // |k_j|^2 in four partial sums of 32 terms (any order: a bound)
             const int key = tid & 63, part = tid >> 6;
-            float n2 = 0.0f;
-            for (int d = 32 * part; d < 32 * part + 32; ++d) n2 = f_add(n2, f_mul(sm.ks[d][key], sm.ks[d][key]));
+            double n2 = 0.0;
+            for (int d = 32 * part; d < 32 * part + 32; ++d) n2 += (double)sm.ks[d][key] * (double)sm.ks[d][key];
             sm.u.p1.nkp[part][key] = n2;
             if (tid == 0) sm.u.p1.ncand = 0;
         }
@@ -301,15 +303,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         // candidates: listed, then their exact logits (pass 2's order) taken
         // one per thread into an order-free maximum
         {
-            const float n2 = f_add(f_add(sm.u.p1.nkp[0][jl], sm.u.p1.nkp[1][jl]),
-                                   f_add(sm.u.p1.nkp[2][jl], sm.u.p1.nkp[3][jl]));
-            const float nk = f_mul(f_sqrt(n2), 1.0f + 0x1p-10f);
+            const double nk = __builtin_sqrt((sm.u.p1.nkp[0][jl] + sm.u.p1.nkp[1][jl]) +
+                                             (sm.u.p1.nkp[2][jl] + sm.u.p1.nkp[3][jl])) * (1.0 + 0x1p-30);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int il = wmt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (!allowed(q0 + il, j0 + jl)) continue;
-                const float e2 = f_add(f_mul(f_mul(f_mul(ebound, sm.u.p1.nq[il]), nk), 2.0f), 0x1p-80f);
-                if (ap[r] >= f_sub(sm.u.p1.arun[il], e2))
+                const double e2 = 2.0 * (ebound * sm.u.p1.nq[il] * nk + 0x1p-80);
+                if ((double)ap[r] >= (double)sm.u.p1.arun[il] - e2)
                     sm.u.p1.cand[atomicAdd(&sm.u.p1.ncand, 1)] = (uint16_t)((il << 6) | jl);
             }
         }

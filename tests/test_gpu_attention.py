@@ -135,3 +135,18 @@ def test_attention_equal_and_near_equal_logits(window):
         O = brl.attn_fwd(*(torch.from_numpy(t).cuda() for t in (Q, K, V)), window, s_v)
         torch.cuda.synchronize()
         assert_bitwise(O, oracle.attn_fwd(Q, K, V, window, s_v), f"O (near-equal logits, window {window})")
+
+
+@pytest.mark.parametrize("q_scale,k_scale", [(1e-20, 1e19), (3e17, 1e-18), (1.0, 40.0)])
+def test_attention_extreme_scales(q_scale, k_scale):
+    """Q and K of very different magnitudes (squared norms far outside
+    binary32's range on one side), and logits spread over hundreds of units:
+    the first pass's pruning bound must stay valid."""
+    B, S, Hq, Hkv, window, s_v = 1, 130, 4, 2, 50, 0.05
+    g = np.random.default_rng(int(abs(np.log10(q_scale))) + 1)
+    Q = (g.standard_normal((B, S, Hq, D)) * q_scale).astype(np.float32)
+    K = (g.standard_normal((B, S, Hkv, D)) * k_scale).astype(np.float32)
+    V = g.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    O = brl.attn_fwd(*(torch.from_numpy(t).cuda() for t in (Q, K, V)), window, s_v)
+    torch.cuda.synchronize()
+    assert_bitwise(O, oracle.attn_fwd(Q, K, V, window, s_v), f"O (scales {q_scale}, {k_scale})")
