@@ -69,6 +69,8 @@ def lib():
         "or_attn_fwd_rows": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64, P, i64]),
         "or_attn_bwd_dq_rows": (i32, [P, P, P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P,
                                       i64, P, i64]),
+        "or_attn_bwd_dkdv_rows": (i32, [P, P, P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32,
+                                        P, i64, P, P, i64]),
         "or_num_threads": (i32, []),
         "or_set_threads": (None, [i32]),
     }
@@ -364,6 +366,30 @@ def attn_bwd_dq(Q, K, V, O, dO, window: int, s_v: float, rows=None) -> np.ndarra
                                    Hkv * D, Hq * D, int(window), np.float32(s_v), rp, n, _p(out), D)
     assert rc == 0, f"or_attn_bwd_dq_rows failed ({rc})"
     return out.reshape(B, S, Hq, D) if rows is None else out
+
+
+def attn_bwd_dkdv(Q, K, V, O, dO, window: int, s_v: float, rows=None):
+    """Fixed-point-accumulated dK and dV of the attention (see
+    or_attn_bwd_dkdv_rows): key rows by flat id (b*S + j)*Hkv + hk, all rows
+    by default; returns (dK, dV), each [len(rows), D] (or [B, S, Hkv, D])."""
+    Q, K, V, O, dO = _f32(Q), _f32(K), _f32(V), _f32(O), _f32(dO)
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    assert K.shape == (B, S, Hkv, D) and V.shape == K.shape
+    assert O.shape == Q.shape and dO.shape == Q.shape
+    if rows is None:
+        n, rp = B * S * Hkv, None
+    else:
+        rows = np.ascontiguousarray(rows, np.int64)
+        n, rp = rows.size, _p(rows)
+    dk = np.empty((n, D), np.float32)
+    dv = np.empty((n, D), np.float32)
+    rc = lib().or_attn_bwd_dkdv_rows(_p(Q), _p(K), _p(V), _p(O), _p(dO), B, S, Hq, Hkv, D, Hq * D, Hkv * D,
+                                     Hkv * D, Hq * D, int(window), np.float32(s_v), rp, n, _p(dk), _p(dv), D)
+    assert rc == 0, f"or_attn_bwd_dkdv_rows failed ({rc})"
+    if rows is None:
+        return dk.reshape(B, S, Hkv, D), dv.reshape(B, S, Hkv, D)
+    return dk, dv
 
 
 def num_threads() -> int:

@@ -793,6 +793,153 @@ int or_attn_bwd_dq_rows(const float* Q, const float* K, const float* V, const fl
     return bad ? -bad : 0;
 }
 
+/* dK and dV of the attention (onedev.kr summary, "Use", attention paragraph:
+ * the pages give the 64-bit fixed-point accumulation for the query gradient
+ * and say nothing of the key and value gradients).  Readings, with s, m, p,
+ * l, q_v, V^, P, dP, Delta and dS as in or_attn_bwd_dq_rows:
+ *   w_hgjd = CanonSum over the 64 query positions 64g .. 64g+63 of
+ *            P_ij * dO_id   (query head h of j's group; +0 terms for rows
+ *            that do not attend key j and past S)
+ *   z_hgjd = the same sum of dS_ij * Q_id
+ *   dV_jd  = q_v in range ? fl(sum_{h,g} rne(w * 2^40)) * 2^-40 : +0
+ *   dK_jd  = (fl(sum_{h,g} rne(z * 2^40)) * 2^-40) * c
+ * i.e. the query-tile sums take the fixed-point format of dQ, and the sum
+ * over tiles and over the group's query heads is exact (order-free).  The
+ * masks are the STE of the LSQ quantiser of V; the quantiser of p is passed
+ * straight through (P = p / l, as in dS).
+ * Key rows by flat id (b*S + j)*Hkv + hk (all rows when rows == NULL);
+ * out rows r: dK at dk + r*ldout, dV at dv + r*ldout.  Returns -3 if a term
+ * or a sum leaves the int64 range. */
+static void attn_row_stats(const float* Q, const float* K, const float* O, const float* dO, int64_t S,
+                           int64_t Hq, int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldo,
+                           int64_t window, float c, int64_t b, int64_t i, int64_t h, float* s, float* p,
+                           float* prod, float* scratch, float* out3) {
+    const int64_t hk = h / (Hq / Hkv);
+    const int64_t lo = (window > 0 && i - window + 1 > 0) ? i - window + 1 : 0;
+    const float* q = Q + (b * S + i) * ldq + h * D;
+    for (int64_t j = lo; j <= i; ++j) {
+        const float* k = K + (b * S + j) * ldk + hk * D;
+        for (int64_t d = 0; d < D; ++d) prod[d] = or_mul(q[d], k[d]);
+        s[j] = or_mul(canon_sum(prod, D, scratch), c);
+    }
+    float m = s[lo];
+    for (int64_t j = lo + 1; j <= i; ++j)
+        if (s[j] > m) m = s[j];
+    for (int64_t j = 0; j < S; ++j) p[j] = 0.0f;
+    for (int64_t j = lo; j <= i; ++j) p[j] = or_exp(or_sub(s[j], m));
+    const float* go = dO + (b * S + i) * ldo + h * D;
+    const float* o = O + (b * S + i) * ldo + h * D;
+    for (int64_t d = 0; d < D; ++d) prod[d] = or_mul(go[d], o[d]);
+    out3[0] = m;
+    out3[1] = canon_sum(p, S, scratch);
+    out3[2] = canon_sum(prod, D, scratch);
+}
+
+static int fx_add(int64_t* acc, float u) {
+    const double x = rint((double)u * 0x1p40);
+    if (!(fabs(x) < 0x1p62)) return 1;
+    return __builtin_add_overflow(*acc, (int64_t)x, acc) ? 1 : 0;
+}
+
+int or_attn_bwd_dkdv_rows(const float* Q, const float* K, const float* V, const float* O, const float* dO,
+                          int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk,
+                          int64_t ldv, int64_t ldo, int64_t window, float s_v, const int64_t* rows,
+                          int64_t nrows, float* dk, float* dv, int64_t ldout) {
+    fp_env_default();
+    e_init();
+    if (Hkv <= 0 || Hq % Hkv != 0) return -1;
+    const int64_t group = Hq / Hkv;
+    const float c = or_div(1.0f, or_sqrt((float)(double)D));
+    int8_t* qv = attn_quantize_v(V, B, S, Hkv, D, ldv, s_v);
+    /* (m_i, l_i, Delta_i) of every query row that attends one of the key rows */
+    const int64_t nq = B * S * Hq;
+    float* st = (float*)malloc(sizeof(float) * (size_t)(3 * nq > 0 ? 3 * nq : 1));
+    uint8_t* need = (uint8_t*)calloc((size_t)(nq > 0 ? nq : 1), 1);
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t row = rows ? rows[r] : r;
+        const int64_t hk = row % Hkv, j = (row / Hkv) % S, b = row / (Hkv * S);
+        const int64_t ihi = (window > 0 && j + window - 1 < S - 1) ? j + window - 1 : S - 1;
+        for (int64_t i = j; i <= ihi; ++i)
+            for (int64_t h = hk * group; h < (hk + 1) * group; ++h) need[(b * S + i) * Hq + h] = 1;
+    }
+    int bad = 0;
+    PARALLEL_BEGIN
+    float* prod = (float*)malloc(sizeof(float) * (size_t)(D > OR_ATTN_TILE ? D : OR_ATTN_TILE));
+    float* p = (float*)malloc(sizeof(float) * (size_t)S);
+    float* s = (float*)malloc(sizeof(float) * (size_t)S);
+    float* scratch = (float*)malloc(sizeof(float) * (size_t)(S / OR_BLOCK + D / OR_BLOCK + 4));
+    float* tw = (float*)malloc(sizeof(float) * (size_t)(OR_ATTN_TILE * D));
+    float* tz = (float*)malloc(sizeof(float) * (size_t)(OR_ATTN_TILE * D));
+    int64_t* accv = (int64_t*)malloc(sizeof(int64_t) * (size_t)D);
+    int64_t* acck = (int64_t*)malloc(sizeof(int64_t) * (size_t)D);
+    #pragma omp for schedule(dynamic, 16)
+    for (int64_t qrow = 0; qrow < nq; ++qrow) {
+        if (!need[qrow]) continue;
+        const int64_t h = qrow % Hq, i = (qrow / Hq) % S, b = qrow / (Hq * S);
+        attn_row_stats(Q, K, O, dO, S, Hq, Hkv, D, ldq, ldk, ldo, window, c, b, i, h, s, p, prod, scratch,
+                       st + 3 * qrow);
+    }
+    #pragma omp for schedule(dynamic, 4)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t row = rows ? rows[r] : r;
+        const int64_t hk = row % Hkv, j = (row / Hkv) % S, b = row / (Hkv * S);
+        const float* k = K + (b * S + j) * ldk + hk * D;
+        const int8_t* vq = qv + ((b * S + j) * Hkv + hk) * D;
+        for (int64_t d = 0; d < D; ++d) accv[d] = acck[d] = 0;
+        for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {
+            for (int64_t g = j / OR_ATTN_TILE; g * OR_ATTN_TILE < S; ++g) {
+                /* terms of the tile's 64 query positions, position-major */
+                int any = 0;
+                for (int64_t t = 0; t < OR_ATTN_TILE; ++t) {
+                    const int64_t i = g * OR_ATTN_TILE + t;
+                    const int64_t lo = (window > 0 && i - window + 1 > 0) ? i - window + 1 : 0;
+                    float P = 0.0f, dS = 0.0f;
+                    if (i < S && j <= i && j >= lo) {
+                        any = 1;
+                        const float* st3 = st + 3 * ((b * S + i) * Hq + h);
+                        const float* q = Q + (b * S + i) * ldq + h * D;
+                        const float* go = dO + (b * S + i) * ldo + h * D;
+                        for (int64_t d = 0; d < D; ++d) prod[d] = or_mul(q[d], k[d]);
+                        const float sij = or_mul(canon_sum(prod, D, scratch), c);
+                        P = or_div(or_exp(or_sub(sij, st3[0])), st3[1]);
+                        for (int64_t d = 0; d < D; ++d) prod[d] = or_mul(go[d], or_mul(or_i2f(vq[d]), s_v));
+                        const float dp = canon_sum(prod, D, scratch);
+                        dS = or_mul(P, or_sub(dp, st3[2]));
+                    }
+                    for (int64_t d = 0; d < D; ++d) {
+                        const float gv = i < S ? dO[(b * S + i) * ldo + h * D + d] : 0.0f;
+                        const float qd = i < S ? Q[(b * S + i) * ldq + h * D + d] : 0.0f;
+                        tw[d * OR_ATTN_TILE + t] = or_mul(P, gv);
+                        tz[d * OR_ATTN_TILE + t] = or_mul(dS, qd);
+                    }
+                }
+                if (!any) break;     /* no later tile attends key j either */
+                for (int64_t d = 0; d < D; ++d) {
+                    int e = fx_add(&accv[d], canon_sum(tw + d * OR_ATTN_TILE, OR_ATTN_TILE, scratch));
+                    e |= fx_add(&acck[d], canon_sum(tz + d * OR_ATTN_TILE, OR_ATTN_TILE, scratch));
+                    if (e) {
+                        #pragma omp atomic write
+                        bad = 3;
+                    }
+                }
+            }
+        }
+        float* ok = dk + r * ldout;
+        float* ov = dv + r * ldout;
+        for (int64_t d = 0; d < D; ++d) {
+            int8_t q;
+            uint8_t in;
+            quantize_one(V[(b * S + j) * ldv + hk * D + d], s_v, &q, &in);
+            ov[d] = in ? or_mul(round_flush((double)(float)accv[d]), 0x1p-40f) : 0.0f;
+            ok[d] = or_mul(or_mul(round_flush((double)(float)acck[d]), 0x1p-40f), c);
+        }
+    }
+    free(prod); free(p); free(s); free(scratch); free(tw); free(tz); free(accv); free(acck);
+    PARALLEL_END
+    free(st); free(need); free(qv);
+    return bad ? -bad : 0;
+}
+
 void or_set_threads(int n) {
 #ifdef _OPENMP
     if (n > 0) omp_set_num_threads(n);
