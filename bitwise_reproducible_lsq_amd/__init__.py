@@ -61,6 +61,8 @@ _SIGS = {
     "adamw_step": (i32, [P, P, P, P, i64, P, i32, P]),
     "attn_fwd": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64, P, P]),
     "attn_bwd_dq": (i32, [P, P, P, P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, P]),
+    "attn_bwd_dkdv": (i32, [P, P, P, P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, P, i64,
+                            P]),
     "brl_stream_create": (i32, [C.c_uint64, i32, P, i32, C.POINTER(C.c_void_p)]),
     "brl_stream_destroy": (None, [P]),
     "brl_stream_next": (i32, [P, i64, P, C.POINTER(C.c_int64)]),
@@ -355,6 +357,41 @@ def attn_bwd_dq(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tens
     _check(lib().attn_bwd_dq(q, k, v, _ptr(O), _ptr(dO), _ptr(stats), B, S, Hq, Hkv, D, ldq, ldk, ldv, ld,
                              int(window), float(s_v), _ptr(dQ), _stream(stream)))
     return dQ
+
+
+def attn_bwd_dkdv(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor, dO: torch.Tensor,
+                  stats: torch.Tensor, window: int, s_v: float, dK: Optional[torch.Tensor] = None,
+                  dV: Optional[torch.Tensor] = None, stream=None):
+    """dK and dV of attn_fwd with 64-bit fixed-point accumulation
+    (attn_bwd_dkdv).  O and dO dense [B, S, Hq, D]; stats as written by
+    attn_fwd; dK and dV [B, S, Hkv, D] views sharing one row stride (column
+    slices of a QKV gradient buffer work).  Returns (dK, dV)."""
+    B, S, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    for t, n in ((O, "O"), (dO, "dO")):
+        _f32(t, n)
+        if t.shape != Q.shape or not t.is_contiguous():
+            raise ValueError(f"{n} must be a dense tensor of Q's shape")
+    if stats.shape != (B, S, Hq, 2) or stats.dtype != torch.float32 or not stats.is_contiguous():
+        raise ValueError("stats must be a dense float32 [B, S, Hq, 2] tensor")
+    if dK is None and dV is None:
+        g = torch.empty((B, S, 2, Hkv, D), dtype=torch.float32, device=Q.device)
+        dK, dV = g[:, :, 0], g[:, :, 1]
+    elif dK is None or dV is None:
+        raise ValueError("give both dK and dV or neither")
+    for t, n in ((dK, "dK"), (dV, "dV")):
+        if t.shape != K.shape:
+            raise ValueError(f"{n} must have K's shape")
+    pk, ldg = _heads_view(dK, "dK")
+    pv, ldg2 = _heads_view(dV, "dV")
+    if ldg != ldg2:
+        raise ValueError("dK and dV must share one row stride")
+    q, ldq = _heads_view(Q, "Q")
+    k, ldk = _heads_view(K, "K")
+    v, ldv = _heads_view(V, "V")
+    _check(lib().attn_bwd_dkdv(q, k, v, _ptr(O), _ptr(dO), _ptr(stats), B, S, Hq, Hkv, D, ldq, ldk, ldv, Hq * D,
+                               int(window), float(s_v), pk, pv, ldg, _stream(stream)))
+    return dK, dV
 
 
 STREAM_WINDOW = 4097

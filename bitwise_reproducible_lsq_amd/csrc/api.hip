@@ -534,6 +534,25 @@ brl_status attn_bwd_dq(const float* Q, const float* K, const float* V, const flo
                      "attention dQ");
 }
 
+brl_status attn_bwd_dkdv(const float* Q, const float* K, const float* V, const float* O, const float* dO,
+                         const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                         int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dK,
+                         float* dV, int64_t ldg, void* stream) {
+    brl_status rc = attn_check("attn_bwd_dkdv", B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo, s_v);
+    if (rc != BRL_OK) return rc;
+    if (ldg < Hkv * D) return fail(BRL_ESHAPE, "attn_bwd_dkdv: row stride smaller than heads * D");
+    if (ldg & 3) return fail(BRL_EINVAL, "attn_bwd_dkdv: row strides must be multiples of 4");
+    if (B * S == 0) return BRL_OK;
+    if (!Q || !K || !V || !O || !dO || !stats || !dK || !dV)
+        return fail(BRL_EINVAL, "attn_bwd_dkdv: null tensor");
+    if (!al16p(Q) || !al16p(K) || !al16p(V) || !al16p(O) || !al16p(dO) || !al16p(dK) || !al16p(dV))
+        return fail(BRL_EINVAL, "attn_bwd_dkdv: pointers must be 16-byte aligned");
+    if (!aligned4(stats)) return fail(BRL_EINVAL, "attn_bwd_dkdv: stats must be 4-byte aligned");
+    return check_hip(launch_attn_bwd_dkdv(Q, K, V, O, dO, stats, B, S, Hq, Hkv, ldq, ldk, ldv, ldo, window, s_v,
+                                          dK, dV, ldg, exp_constants(), static_cast<hipStream_t>(stream)),
+                     "attention dK/dV");
+}
+
 int64_t brl_set_tuning(int32_t knob, int64_t value) {
     if (knob < 0 || knob > 3) return -1;
     if (knob == BRL_TUNE_BWD_CHUNK_LOG2 && value > 7) value = 7;

@@ -714,4 +714,280 @@ hipError_t launch_attn_bwd_dq(const float* Q, const float* K, const float* V, co
     return hipGetLastError();
 }
 
+
+// dK and dV of the attention.  The pages give the 64-bit fixed-point
+// accumulation for dQ only; this library reads the same format into the key
+// and value gradients (s, m, p, l, P, dP, Delta, dS as for dQ):
+//   w_hgjd = CanonSum over the 64 query positions of tile g of P_ij * dO_id
+//   z_hgjd = the same sum of dS_ij * Q_id
+//   dV_jd  = V_jd in the quantiser's range ? fl(sum_{h,g} rne(w * 2^40)) * 2^-40 : +0
+//   dK_jd  = (fl(sum_{h,g} rne(z * 2^40)) * 2^-40) * c
+// over the query heads h of the KV head and every query tile g; rows that do
+// not attend key j give +0 terms.  The sum over tiles and heads is exact, so
+// one workgroup per (key tile, batch, KV head) walks its heads and query
+// tiles in any order.  K and V^ stay in LDS for the whole walk; each visit
+// brings one query tile of Q and dO (row-major, rows padded so that the
+// two rows a wave reads per step sit in different banks).
+constexpr int kKvThreads = 1024;
+constexpr int kKvRow = kAD + 4;
+
+struct AttnKvArgs {
+    const float* Q;
+    const float* K;
+    const float* V;
+    const float* O;
+    const float* dO;
+    const float* stats;
+    float* dK;
+    float* dV;
+    int64_t S, Hq, Hkv, B, ldq, ldk, ldv, ldo, ldg, window;
+    float c, s_v;
+    ExpConsts ek;
+};
+
+struct AttnKvSmem {
+    float ks[kAD][kAK];             // K tile, d-major (logits)
+    float vs[kAD][kAK];             // V^ tile, d-major (dP)
+    float qr[kAQ][kKvRow];          // Q tile, row-major (logits, dK)
+    float gr[kAQ][kKvRow];          // dO tile, row-major (dP, dV)
+    float pt[kAQ][kAK + 1];         // P, then dS
+    float rowm[kAQ], rowl[kAQ], rowdelta[kAQ];
+};
+static_assert(sizeof(AttnKvSmem) <= 163840, "LDS of one CU");
+
+// canon_dot's sums with a row-major left operand: A[row][d]
+template <int NX, int NY>
+__device__ __forceinline__ void canon_dot_rm(const float (*A)[kKvRow], const float (*B)[kAK], int ti, int tj,
+                                             float (&s)[NX][NY]) {
+    float b01[NX][NY], b2[NX][NY], cur[NX][NY];
+#pragma unroll
+    for (int blk = 0; blk < kAD / 32; ++blk) {
+#pragma unroll 2
+        for (int dd = 0; dd < 32; ++dd) {
+            const int d = blk * 32 + dd;
+            float a[NX], b[NY];
+#pragma unroll
+            for (int x = 0; x < NX; ++x) a[x] = A[NX * ti + x][d];
+#pragma unroll
+            for (int y = 0; y < NY; ++y) b[y] = B[d][NY * tj + y];
+#pragma unroll
+            for (int x = 0; x < NX; ++x)
+#pragma unroll
+                for (int y = 0; y < NY; ++y) {
+                    const float pr = f_mul(a[x], b[y]);
+                    cur[x][y] = dd == 0 ? pr : f_add(cur[x][y], pr);
+                }
+        }
+#pragma unroll
+        for (int x = 0; x < NX; ++x)
+#pragma unroll
+            for (int y = 0; y < NY; ++y) {
+                if (blk == 0) b01[x][y] = cur[x][y];
+                if (blk == 1) b01[x][y] = f_add(b01[x][y], cur[x][y]);
+                if (blk == 2) b2[x][y] = cur[x][y];
+                if (blk == 3) s[x][y] = f_add(b01[x][y], f_add(b2[x][y], cur[x][y]));
+            }
+    }
+}
+
+// the tile sum over 64 query positions of T[i][j] * R[i][d0 + e] for this
+// thread's key j and 8 values of d: two 32-row blocks left to right, then the
+// pair; each sum goes into its int64 accumulator with 40 fraction bits
+__device__ __forceinline__ void kv_tile_sums(const float (*T)[kAK + 1], const float (*R)[kKvRow], int j, int d0,
+                                             int64_t (&acc)[8]) {
+    float b0[8], cur[8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll 4
+        for (int ii = 0; ii < 32; ++ii) {
+            const int i = 32 * blk + ii;
+            const float t = T[i][j];
+#pragma unroll
+            for (int q4 = 0; q4 < 2; ++q4) {
+                const vf4 r = *reinterpret_cast<const vf4*>(&R[i][d0 + 4 * q4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float pr = f_mul(t, r[e]);
+                    cur[4 * q4 + e] = ii == 0 ? pr : f_add(cur[4 * q4 + e], pr);
+                }
+            }
+        }
+        if (blk == 0) {
+#pragma unroll
+            for (int x = 0; x < 8; ++x) b0[x] = cur[x];
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[x] += (int64_t)__builtin_rint((double)f_add(b0[x], cur[x]) * 0x1p40);
+}
+
+__global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    AttnKvSmem& sm = *reinterpret_cast<AttnKvSmem*>(smem_raw);
+    const int tid = threadIdx.x;
+    const int ti = tid >> 5, tj = tid & 31;         // 2 rows x 2 keys of the 64 x 64 tile
+
+    // key tiles slowest, so that the longest walks (first tiles, causal) start first
+    const unsigned nbh = (unsigned)(a.B * a.Hkv), hkv = (unsigned)a.Hkv;
+    const unsigned kt = blockIdx.x / nbh;
+    const unsigned bh = blockIdx.x % nbh;
+    const int64_t hk = bh % hkv;
+    const int64_t b = bh / hkv;
+    const int64_t group = (unsigned)a.Hq / hkv;
+    const int64_t j0 = (int64_t)kt * kAK;
+    const int64_t krows = a.S - j0 < kAK ? a.S - j0 : kAK;
+    const int64_t base = b * a.S;
+    const int64_t ihi_all = a.window > 0 ? (j0 + krows - 1 + a.window - 1 < a.S - 1 ? j0 + krows - 1 + a.window - 1
+                                                                                   : a.S - 1)
+                                         : a.S - 1;
+    const int64_t qt0 = j0 / kAQ, qt1 = ihi_all / kAQ;
+
+    attn_load_kt<kKvThreads>(a.K, a.ldk, base + j0, krows, hk, sm.ks);
+    const Quantizer qz(a.s_v);
+    for (int e = tid; e < (kAK / 4) * (kAD / 4); e += kKvThreads) {
+        const int rq = e & 15, dq = e >> 4;
+        vf4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t j = j0 + 4 * rq + u;
+            v[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (j < a.S) v[u] = *reinterpret_cast<const vf4*>(a.V + (base + j) * a.ldv + hk * kAD + 4 * dq);
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            vf4 o;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                bool in;
+                o[u] = j0 + 4 * rq + u < a.S ? f_mul((float)qz.q(v[u][w], &in), a.s_v) : 0.0f;
+            }
+            *reinterpret_cast<vf4*>(&sm.vs[4 * dq + w][4 * rq]) = o;
+        }
+    }
+
+    // outputs of this thread: key jr = tid / 16, d = d0 .. d0 + 7
+    const int jr = tid >> 4, d0 = (tid & 15) * 8;
+    int64_t accv[8], acck[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) accv[x] = acck[x] = 0;
+
+    for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {
+        for (int64_t qt = qt0; qt <= qt1; ++qt) {
+            const int64_t i0 = qt * kAQ;
+            const int64_t qrows = a.S - i0 < kAQ ? a.S - i0 : kAQ;
+            __syncthreads();
+            // Q and dO rows of the tile, row-major
+            for (int e = tid; e < kAQ * (kAD / 4); e += kKvThreads) {
+                const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
+                vf4 q = {0.0f, 0.0f, 0.0f, 0.0f}, g = q;
+                if (row < qrows) {
+                    q = *reinterpret_cast<const vf4*>(a.Q + (base + i0 + row) * a.ldq + h * kAD + d4);
+                    g = *reinterpret_cast<const vf4*>(a.dO + (base + i0 + row) * a.ldo + h * kAD + d4);
+                }
+                *reinterpret_cast<vf4*>(&sm.qr[row][d4]) = q;
+                *reinterpret_cast<vf4*>(&sm.gr[row][d4]) = g;
+            }
+            // row statistics; Delta = CanonSum_d(dO * O): four lanes per row
+            // hold the d-blocks, then the pair tree through two lane swaps
+            if (tid < 4 * kAQ) {
+                const int row = tid >> 2, blk = tid & 3;
+                float x = 0.0f;
+                if (row < qrows) {
+                    const float* go = a.dO + (base + i0 + row) * a.ldo + h * kAD + 32 * blk;
+                    const float* o = a.O + (base + i0 + row) * a.ldo + h * kAD + 32 * blk;
+                    x = f_mul(go[0], o[0]);
+                    for (int d = 1; d < 32; ++d) x = f_add(x, f_mul(go[d], o[d]));
+                }
+                x = f_add(x, __shfl_xor(x, 1));
+                x = f_add(x, __shfl_xor(x, 2));
+                if (blk == 0) {
+                    float m = 0.0f, l = 1.0f;
+                    if (row < qrows) {
+                        const int64_t r = (base + i0 + row) * a.Hq + h;
+                        m = a.stats[2 * r];
+                        l = a.stats[2 * r + 1];
+                    }
+                    sm.rowm[row] = m;
+                    sm.rowl[row] = l;
+                    sm.rowdelta[row] = row < qrows ? x : 0.0f;
+                }
+            }
+            __syncthreads();
+            float sc[2][2], dp[2][2], dsv[2][2];
+            canon_dot_rm<2, 2>(sm.qr, sm.ks, ti, tj, sc);
+            canon_dot_rm<2, 2>(sm.gr, sm.vs, ti, tj, dp);
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int il = 2 * ti + x;
+                const int64_t i = i0 + il;
+                const int64_t lo = a.window > 0 ? i - a.window + 1 : 0;
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    const int jl = 2 * tj + y;
+                    const int64_t j = j0 + jl;
+                    float P = 0.0f;
+                    dsv[x][y] = 0.0f;
+                    if (i < a.S && j <= i && j >= lo) {
+                        const float p = own_exp(f_sub(f_mul(sc[x][y], a.c), sm.rowm[il]), a.ek);
+                        P = f_div(p, sm.rowl[il]);
+                        dsv[x][y] = f_mul(P, f_sub(dp[x][y], sm.rowdelta[il]));
+                    }
+                    sm.pt[il][jl] = P;
+                }
+            }
+            __syncthreads();
+            kv_tile_sums(sm.pt, sm.gr, jr, d0, accv);
+            __syncthreads();
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y) sm.pt[2 * ti + x][2 * tj + y] = dsv[x][y];
+            __syncthreads();
+            kv_tile_sums(sm.pt, sm.qr, jr, d0, acck);
+        }
+    }
+    if (jr < krows) {
+        const int64_t row = base + j0 + jr;
+        const float* v = a.V + row * a.ldv + hk * kAD + d0;
+        float* ok = a.dK + row * a.ldg + hk * kAD + d0;
+        float* ov = a.dV + row * a.ldg + hk * kAD + d0;
+#pragma unroll
+        for (int q4 = 0; q4 < 2; ++q4) {
+            const vf4 vv = *reinterpret_cast<const vf4*>(v + 4 * q4);
+            vf4 k4, v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                k4[e] = f_mul(f_mul((float)acck[4 * q4 + e], 0x1p-40f), a.c);
+                v4[e] = qz.in_range(vv[e]) ? f_mul((float)accv[4 * q4 + e], 0x1p-40f) : 0.0f;
+            }
+            *reinterpret_cast<vf4*>(ok + 4 * q4) = k4;
+            *reinterpret_cast<vf4*>(ov + 4 * q4) = v4;
+        }
+    }
+}
+
+hipError_t launch_attn_bwd_dkdv(const float* Q, const float* K, const float* V, const float* O, const float* dO,
+                                const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t ldq,
+                                int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dK,
+                                float* dV, int64_t ldg, const ExpConsts& ek, hipStream_t st) {
+    if (B == 0 || S == 0) return hipSuccess;
+    AttnKvArgs a;
+    a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.stats = stats; a.dK = dK; a.dV = dV;
+    a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.B = B;
+    a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.ldg = ldg; a.window = window;
+    a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
+    a.s_v = s_v;
+    a.ek = ek;
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnKvSmem));
+        attr = true;
+    }
+    const int64_t blocks = B * Hkv * ceil_div(S, kAK);
+    if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)blocks), dim3(kKvThreads), sizeof(AttnKvSmem), st, a);
+    return hipGetLastError();
+}
+
 }  // namespace brl

@@ -161,5 +161,9 @@ hipError_t launch_attn_bwd_dq(const float* Q, const float* K, const float* V, co
                               const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t ldq,
                               int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dQ,
                               const ExpConsts& ek, hipStream_t st);
+hipError_t launch_attn_bwd_dkdv(const float* Q, const float* K, const float* V, const float* O, const float* dO,
+                                const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t ldq,
+                                int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dK,
+                                float* dV, int64_t ldg, const ExpConsts& ek, hipStream_t st);
 
 }  // namespace brl

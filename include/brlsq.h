@@ -289,6 +289,31 @@ BRL_API brl_status attn_bwd_dq(const float* Q, const float* K, const float* V, c
                                float* dQ, void* stream);
 
 /*
+ * dK and dV of attn_fwd (onedev.kr summary, "Use", attention paragraph: the
+ * pages give 64-bit fixed-point accumulation for the query gradient and
+ * nothing for the key and value gradients; this library reads the same
+ * format into both).  With P, dP, Delta and dS as in attn_bwd_dq:
+ *   w_hgjd = CanonSum over the 64 query positions 64g .. 64g+63 of P_ij * dO_id
+ *   z_hgjd = the same sum of dS_ij * Q_id
+ *   dV_jd  = (-127 <= v_jd / s_v <= 127) ? fl(sum_{h,g} rne(w * 2^40)) * 2^-40 : +0
+ *   dK_jd  = (fl(sum_{h,g} rne(z * 2^40)) * 2^-40) * c
+ * summed over the query heads h of KV head j's group and every query tile g
+ * (+0 terms for rows that do not attend key j and past S); the int64 sums
+ * are exact, so their order cannot change them.  The range mask is the
+ * straight-through estimator of V's LSQ quantiser; p's quantiser passes
+ * straight through (P = p / l).  Valid while every |w|, |z| < 2^22 and each
+ * sum < 2^23 in magnitude (gradient scale; not checked).
+ * dK and dV: [B, S, Hkv, D] with row stride ldg (a multiple of 4, >= Hkv*D),
+ * e.g. column slices of a [B*S, (Hq + 2*Hkv)*D] gradient buffer; they must
+ * not overlap each other or the inputs.  Other arguments and requirements as
+ * attn_bwd_dq.  Asynchronous on `stream`.
+ */
+BRL_API brl_status attn_bwd_dkdv(const float* Q, const float* K, const float* V, const float* O, const float* dO,
+                                 const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                                 int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v,
+                                 float* dK, float* dV, int64_t ldg, void* stream);
+
+/*
  * Topology-invariant data stream (onedev.kr summary, "What differs": one
  * canonical stream independent of world size and rank, three generators --
  * source interleaving seeded by the training seed alone, shard order seeded

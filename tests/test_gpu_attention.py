@@ -150,3 +150,78 @@ def test_attention_extreme_scales(q_scale, k_scale):
     O = brl.attn_fwd(*(torch.from_numpy(t).cuda() for t in (Q, K, V)), window, s_v)
     torch.cuda.synchronize()
     assert_bitwise(O, oracle.attn_fwd(Q, K, V, window, s_v), f"O (scales {q_scale}, {k_scale})")
+
+
+KV_CASES = [
+    # B, S, Hq, Hkv, window, s_v
+    (1, 1, 1, 1, 0, 0.05),
+    (1, 64, 2, 1, 0, 0.05),
+    (2, 150, 4, 2, 0, 0.05),
+    (1, 200, 4, 2, 64, 0.0371),
+    (1, 333, 16, 4, 130, 0.05),
+    (1, 100, 4, 4, 1, 0.05),
+    (1, 190, 8, 2, 500, 0.05),        # window longer than the sequence
+]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,window,s_v", KV_CASES)
+def test_attention_dkdv_parity(B, S, Hq, Hkv, window, s_v):
+    """dK and dV with 64-bit fixed-point accumulation, bit for bit, from the
+    forward's own O and (m, l) statistics; a few V entries outside the
+    quantiser's range get +0."""
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=5 * S + Hq + window, scale=0.3)
+    V.reshape(-1)[::977] = 7.5                 # 150 steps at s_v = 0.05: clamped
+    dO = (np.random.default_rng(S + window + 1).standard_normal((B, S, Hq, D)) * 1e-2).astype(np.float32)
+    q, k, v = (torch.from_numpy(t).cuda() for t in (Q, K, V))
+    stats = torch.empty((B, S, Hq, 2), dtype=torch.float32, device="cuda")
+    O = brl.attn_fwd(q, k, v, window, s_v, stats=stats)
+    dK, dV = brl.attn_bwd_dkdv(q, k, v, O, torch.from_numpy(dO).cuda(), stats, window, s_v)
+    torch.cuda.synchronize()
+    Oh = O.cpu().numpy()
+    assert_bitwise(Oh, oracle.attn_fwd(Q, K, V, window, s_v), "O")
+    wk, wv = oracle.attn_bwd_dkdv(Q, K, V, Oh, dO, window, s_v)
+    assert_bitwise(dK, wk, f"dK (S={S} w={window})")
+    assert_bitwise(dV, wv, f"dV (S={S} w={window})")
+
+
+def test_attention_dkdv_into_qkv_gradient_slices():
+    """Q, K, V as column slices of the QKV projection output and dK, dV
+    written as column slices of one [B*S, (Hq + 2 Hkv) * D] gradient buffer;
+    the dQ columns stay untouched."""
+    B, S, Hq, Hkv, window, s_v = 2, 170, 4, 1, 96, 0.05
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=11, scale=0.3)
+    dO = (np.random.default_rng(12).standard_normal((B, S, Hq, D)) * 1e-2).astype(np.float32)
+    Y = np.concatenate([Q.reshape(B * S, -1), K.reshape(B * S, -1), V.reshape(B * S, -1)], axis=1)
+    Yd = torch.from_numpy(np.ascontiguousarray(Y)).cuda()
+    q = Yd[:, :Hq * D].view(B, S, Hq, D)
+    k = Yd[:, Hq * D:(Hq + Hkv) * D].view(B, S, Hkv, D)
+    v = Yd[:, (Hq + Hkv) * D:].view(B, S, Hkv, D)
+    stats = torch.empty((B, S, Hq, 2), dtype=torch.float32, device="cuda")
+    O = brl.attn_fwd(q, k, v, window, s_v, stats=stats)
+    G = torch.full((B * S, (Hq + 2 * Hkv) * D), 3.0, device="cuda")
+    dK = G[:, Hq * D:(Hq + Hkv) * D].view(B, S, Hkv, D)
+    dV = G[:, (Hq + Hkv) * D:].view(B, S, Hkv, D)
+    brl.attn_bwd_dkdv(q, k, v, O, torch.from_numpy(dO).cuda(), stats, window, s_v, dK=dK, dV=dV)
+    torch.cuda.synchronize()
+    wk, wv = oracle.attn_bwd_dkdv(Q, K, V, O.cpu().numpy(), dO, window, s_v)
+    assert_bitwise(dK, wk, "dK (slices)")
+    assert_bitwise(dV, wv, "dV (slices)")
+    assert torch.all(G[:, :Hq * D] == 3.0)
+
+
+def test_attention_dkdv_repeat_and_zero_gradient():
+    """Two calls give the same bits; dO = 0 gives +0 everywhere."""
+    B, S, Hq, Hkv, window, s_v = 1, 257, 4, 2, 0, 0.05
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=13, scale=2.0)
+    dO = (np.random.default_rng(14).standard_normal((B, S, Hq, D)) * 1e-2).astype(np.float32)
+    q, k, v, g = (torch.from_numpy(t).cuda() for t in (Q, K, V, dO))
+    stats = torch.empty((B, S, Hq, 2), dtype=torch.float32, device="cuda")
+    O = brl.attn_fwd(q, k, v, window, s_v, stats=stats)
+    k1, v1 = brl.attn_bwd_dkdv(q, k, v, O, g, stats, window, s_v)
+    k2, v2 = brl.attn_bwd_dkdv(q, k, v, O, g, stats, window, s_v)
+    k0, v0 = brl.attn_bwd_dkdv(q, k, v, O, torch.zeros_like(g), stats, window, s_v)
+    torch.cuda.synchronize()
+    wk, wv = oracle.attn_bwd_dkdv(Q, K, V, O.cpu().numpy(), dO, window, s_v)
+    for t, w, n in ((k1, wk, "dK"), (v1, wv, "dV"), (k2, wk, "dK repeat"), (v2, wv, "dV repeat")):
+        assert_bitwise(t, w, n)
+    assert np.all(_bits(k0) == 0) and np.all(_bits(v0) == 0)

@@ -196,3 +196,30 @@ def test_attention_dq_full_size(name):
     rows = np.array(rows, np.int64)
     want = oracle.attn_bwd_dq(Q, K, V, Oh, dO, case.window, case.s_v, rows=rows)
     assert_bitwise(dQh[rows], want, f"dQ rows ({name})")
+
+
+@pytest.mark.parametrize("name", ["attn_window", "attn_causal"])
+def test_attention_dkdv_full_size(name):
+    """dK and dV (64-bit fixed-point accumulation) at one Open-1B layer, on
+    sampled key rows of one KV head per case (the first and the last), from
+    the forward's own O and statistics; dO ~ N(0, 1e-3)."""
+    case = synth.ATTENTION_CASES[name]
+    Q, K, V = synth.attention_inputs(case)
+    dO = synth.normal(case.seed, "dY", Q.shape, 1e-3)
+    q, k, v = _cuda(Q), _cuda(K), _cuda(V)
+    stats = torch.empty((case.B, case.S, case.Hq, 2), dtype=torch.float32, device=DEV)
+    O = brl.attn_fwd(q, k, v, case.window, case.s_v, stats=stats)
+    dK, dV = brl.attn_bwd_dkdv(q, k, v, O, _cuda(dO), stats, case.window, case.s_v)
+    torch.cuda.synchronize()
+    Oh = O.cpu().numpy()
+    dKh = dK.cpu().numpy().reshape(-1, 128)
+    dVh = dV.cpu().numpy().reshape(-1, 128)
+    b, hk = (0, 0) if name == "attn_window" else (case.B - 1, case.Hkv - 1)
+    edges = [0, 63, 64, 511, 512, case.S - 65, case.S - 1] if name == "attn_window" else \
+        [2048, 3071, 4031, 4032, case.S - 1]
+    rows = np.array([(b * case.S + int(j)) * case.Hkv + hk
+                     for j in _sample(case.S, edges, 2, seed=7 + hk) if name == "attn_window" or j >= 2048],
+                    np.int64)
+    wk, wv = oracle.attn_bwd_dkdv(Q, K, V, Oh, dO, case.window, case.s_v, rows=rows)
+    assert_bitwise(dKh[rows], wk, f"dK rows ({name})")
+    assert_bitwise(dVh[rows], wv, f"dV rows ({name})")

@@ -247,3 +247,13 @@ def test_attention_rejects_bad_arguments_without_launching():
     assert L.attn_bwd_dq(p, p, p, p, p, None, 1, 64, 4, 2, 128, 512, 256, 256, 512, 0, 0.05, p, None) == brl.BRL_EINVAL
     assert L.attn_bwd_dq(p, p, p, p, C.c_void_p(0x10008), p, 1, 64, 4, 2, 128, 512, 256, 256, 512, 0, 0.05, p,
                          None) == brl.BRL_EINVAL
+    def kvcall(D=128, ldg=256, stats=p, dV=p, S=64):
+        return L.attn_bwd_dkdv(p, p, p, p, p, stats, 1, S, 4, 2, D, 512, 256, 256, 512, 0, 0.05, p, dV, ldg, None)
+
+    assert kvcall(D=64) == brl.BRL_ESHAPE
+    assert kvcall(ldg=128) == brl.BRL_ESHAPE
+    assert kvcall(ldg=258) == brl.BRL_EINVAL
+    assert kvcall(stats=None) == brl.BRL_EINVAL
+    assert kvcall(dV=None) == brl.BRL_EINVAL
+    assert kvcall(dV=C.c_void_p(0x10004)) == brl.BRL_EINVAL
+    assert kvcall(S=0) == brl.BRL_OK           # nothing to do, nothing launched
