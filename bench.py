@@ -105,9 +105,9 @@ def stream_bench(torch, brl, dev, with_cpu: bool):
 
 
 def attention_bench(torch, brl, dev):
-    """attn_fwd on one Open-1B layer's microbatch (4 x 4096 tokens, 16 query /
-    4 KV heads of 128), window 512 and full causal; device-generated inputs
-    (parity at this size is a GPU test)."""
+    """attn_fwd, attn_bwd_dq and attn_bwd_dkdv on one Open-1B layer's
+    microbatch (4 x 4096 tokens, 16 query / 4 KV heads of 128), window 512 and
+    full causal; device-generated inputs (parity at this size is a GPU test)."""
     B, S, Hq, Hkv = 4, 4096, 16, 4
     g = torch.Generator(device=dev)
     g.manual_seed(5)
@@ -117,6 +117,7 @@ def attention_bench(torch, brl, dev):
     O = torch.empty_like(Q)
     dO = torch.randn(B, S, Hq, ATTN_D, generator=g, device=dev).mul_(1e-3)
     dQ = torch.empty_like(Q)
+    dK, dV = torch.empty_like(K), torch.empty_like(V)
     stats = torch.empty(B, S, Hq, 2, device=dev)
     out = {"shape": {"B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "D": ATTN_D, "s_v": 0.05}}
     for name, window in (("window_512", 512), ("causal", 0)):
@@ -154,7 +155,22 @@ def attention_bench(torch, brl, dev):
                                         "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
                                         "frac": round(ops_dq / (ms_dq * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4),
                                         "note": "3 * 2*D binary32 ops per allowed (row, key)"}}
-    del Q, K, V, O, dO, dQ, stats
+        # dK and dV: logits, dP, P.dO and dS.Q, 4 * 2*D ops per allowed (row, key)
+        brl.attn_bwd_dkdv(Q, K, V, O, dO, stats, window, 0.05, dK=dK, dV=dV)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(3):
+            brl.attn_bwd_dkdv(Q, K, V, O, dO, stats, window, 0.05, dK=dK, dV=dV)
+        b.record()
+        torch.cuda.synchronize()
+        ms_kv = a.elapsed_time(b) / 3
+        ops_kv = 4 * ops
+        out[name]["dkdv"] = {"ms": round(ms_kv, 4),
+                             "roofline": {"bound": "alu", "achieved": round(ops_kv / (ms_kv * 1e-3) / 1e12, 3),
+                                          "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
+                                          "frac": round(ops_kv / (ms_kv * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4),
+                                          "note": "4 * 2*D binary32 ops per allowed (row, key)"}}
+    del Q, K, V, O, dO, dQ, dK, dV, stats
     return out
 
 
@@ -424,9 +440,9 @@ def cpu_hash_rate(tensors) -> float:
 
 
 def cpu_attention_rate():
-    """The attention oracle on sampled rows of the window-512 layer: rows/s
-    and the same algorithmic ops per second as the GPU figure (2*D per
-    allowed logit; dQ three such products)."""
+    """The attention oracle on sampled rows of the window-512 layer: the same
+    algorithmic ops per second as the GPU figure (2*D per allowed logit; dQ
+    three such products, dK/dV four)."""
     import numpy as np
 
     import oracle
@@ -445,9 +461,17 @@ def cpu_attention_rate():
     t0 = time.perf_counter()
     oracle.attn_bwd_dq(Q, K, V, Ofull.reshape(Q.shape), dO, case.window, case.s_v, rows=rows)
     t_dq = time.perf_counter() - t0
-    return {"kind": "oracle", "cores": oracle.num_threads(), "sample": f"256 random rows of the window-512 layer",
+    kv_rows = np.sort(g.choice(case.B * case.S * case.Hkv, 8, replace=False))
+    group = case.Hq // case.Hkv
+    pairs = sum(group * min(case.S - int(r // case.Hkv) % case.S, case.window) for r in kv_rows)
+    t0 = time.perf_counter()
+    oracle.attn_bwd_dkdv(Q, K, V, Ofull.reshape(Q.shape), dO, case.window, case.s_v, rows=kv_rows)
+    t_kv = time.perf_counter() - t0
+    return {"kind": "oracle", "cores": oracle.num_threads(),
+            "sample": "256 random rows (fwd, dQ) and 8 random key rows (dK/dV) of the window-512 layer",
             "fwd_T_ops_per_s": round(2.0 * ATTN_D * keys / t_fwd / 1e12, 6),
-            "dq_T_ops_per_s": round(3 * 2.0 * ATTN_D * keys / t_dq / 1e12, 6)}
+            "dq_T_ops_per_s": round(3 * 2.0 * ATTN_D * keys / t_dq / 1e12, 6),
+            "dkdv_T_ops_per_s": round(4 * 2.0 * ATTN_D * pairs / t_kv / 1e12, 8)}
 
 
 def cpu_baseline(inp, budget_s: float):

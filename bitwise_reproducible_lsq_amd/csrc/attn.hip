@@ -725,11 +725,27 @@ hipError_t launch_attn_bwd_dq(const float* Q, const float* K, const float* V, co
 // over the query heads h of the KV head and every query tile g; rows that do
 // not attend key j give +0 terms.  The sum over tiles and heads is exact, so
 // one workgroup per (key tile, batch, KV head) walks its heads and query
-// tiles in any order.  K and V^ stay in LDS for the whole walk; each visit
-// brings one query tile of Q and dO (row-major, rows padded so that the
-// two rows a wave reads per step sit in different banks).
+// tiles in any order.  K and q_v stay in LDS for the whole walk; each visit
+// brings one query tile of Q and dO.
+//
+// Every product is formed on the matrix cores, as in the linear backward: a
+// 16x16x1 fp32 MFMA with a K of one and an accumulator input of -0 returns
+// fl(a*b) for each of its (a, b) pairs, bit-identical to v_mul_f32 (FTZ), and
+// the VALU adds the products in the canonical order.  Lane l feeds A row l
+// and B column l % 16; register 4*beta + e of lane l receives row
+// 16*beta + 4*(l / 16) + e, column l % 16 (64 rows x 16 columns per MFMA).
+//   phase 1 (16 waves): logits (waves 0-3) and dP (waves 4-7) for key slab
+//     16*(w % 4) .. +15 over d-blocks 0 and 1; waves 8-15 the same over
+//     d-blocks 2 and 3; the pair sums meet in LDS as (b0 + b1) + (b2 + b3);
+//   an elementwise pass forms P and dS for the 64 x 64 tile;
+//   phase 2 (16 waves): the tile sums over the 64 query positions (two
+//     32-blocks, then the pair) of P x dO (waves 0-7) and dS x Q (waves
+//     8-15) for d slab 16*(w % 8) .. +15, each into 16 int64 accumulators.
+typedef float v16f_a __attribute__((ext_vector_type(16)));
+
 constexpr int kKvThreads = 1024;
-constexpr int kKvRow = kAD + 4;
+constexpr int kKvRow = kAD + 4;     // floats per LDS row of K, Q and dO
+constexpr int kKvRowQ = kAD + 16;   // bytes per LDS row of q_v
 
 struct AttnKvArgs {
     const float* Q;
@@ -746,86 +762,84 @@ struct AttnKvArgs {
 };
 
 struct AttnKvSmem {
-    float ks[kAD][kAK];             // K tile, d-major (logits)
-    float vs[kAD][kAK];             // V^ tile, d-major (dP)
-    float qr[kAQ][kKvRow];          // Q tile, row-major (logits, dK)
-    float gr[kAQ][kKvRow];          // dO tile, row-major (dP, dV)
-    float pt[kAQ][kAK + 1];         // P, then dS
+    float kr[kAK][kKvRow];          // K tile, key-major
+    float qr[kAQ][kKvRow];          // Q tile, row-major
+    float gr[kAQ][kKvRow];          // dO tile, row-major
+    float pt[kAQ][kAK + 1];         // logits, then P
+    float dt[kAQ][kAK + 1];         // dP, then dS
+    int8_t vq[kAK][kKvRowQ];        // q_v tile, key-major
     float rowm[kAQ], rowl[kAQ], rowdelta[kAQ];
 };
 static_assert(sizeof(AttnKvSmem) <= 163840, "LDS of one CU");
 
-// canon_dot's sums with a row-major left operand: A[row][d]
-template <int NX, int NY>
-__device__ __forceinline__ void canon_dot_rm(const float (*A)[kKvRow], const float (*B)[kAK], int ti, int tj,
-                                             float (&s)[NX][NY]) {
-    float b01[NX][NY], b2[NX][NY], cur[NX][NY];
+__device__ __forceinline__ v16f_a mfma_prod(float a, float b) {
+    v16f_a cneg;
 #pragma unroll
-    for (int blk = 0; blk < kAD / 32; ++blk) {
-#pragma unroll 2
-        for (int dd = 0; dd < 32; ++dd) {
-            const int d = blk * 32 + dd;
-            float a[NX], b[NY];
-#pragma unroll
-            for (int x = 0; x < NX; ++x) a[x] = A[NX * ti + x][d];
-#pragma unroll
-            for (int y = 0; y < NY; ++y) b[y] = B[d][NY * tj + y];
-#pragma unroll
-            for (int x = 0; x < NX; ++x)
-#pragma unroll
-                for (int y = 0; y < NY; ++y) {
-                    const float pr = f_mul(a[x], b[y]);
-                    cur[x][y] = dd == 0 ? pr : f_add(cur[x][y], pr);
-                }
-        }
-#pragma unroll
-        for (int x = 0; x < NX; ++x)
-#pragma unroll
-            for (int y = 0; y < NY; ++y) {
-                if (blk == 0) b01[x][y] = cur[x][y];
-                if (blk == 1) b01[x][y] = f_add(b01[x][y], cur[x][y]);
-                if (blk == 2) b2[x][y] = cur[x][y];
-                if (blk == 3) s[x][y] = f_add(b01[x][y], f_add(b2[x][y], cur[x][y]));
-            }
-    }
+    for (int r = 0; r < 16; ++r) cneg[r] = -0.0f;
+    return __builtin_amdgcn_mfma_f32_16x16x1f32(a, b, cneg, 0, 0, 0);
 }
 
-// the tile sum over 64 query positions of T[i][j] * R[i][d0 + e] for this
-// thread's key j and 8 values of d: two 32-row blocks left to right, then the
-// pair; each sum goes into its int64 accumulator with 40 fraction bits
-__device__ __forceinline__ void kv_tile_sums(const float (*T)[kAK + 1], const float (*R)[kKvRow], int j, int d0,
-                                             int64_t (&acc)[8]) {
-    float b0[8], cur[8];
+// phase 1 of one wave: the sums of d-blocks 2*half and 2*half + 1 (each left
+// to right over its 32 steps), added as b_{2 half} + b_{2 half + 1}; A from
+// row `lane` of arow's tile, B from one key row (fp32, or q_v dequantised)
+template <bool DQV>
+__device__ __forceinline__ v16f_a kv_phase1(const float* arow, const float* brow, const int8_t* bq, float s_v,
+                                            int half) {
+    v16f_a acc, first;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll 4
-        for (int ii = 0; ii < 32; ++ii) {
-            const int i = 32 * blk + ii;
-            const float t = T[i][j];
+    for (int bb = 0; bb < 2; ++bb) {
+        const int d0 = 32 * (2 * half + bb);
 #pragma unroll
-            for (int q4 = 0; q4 < 2; ++q4) {
-                const vf4 r = *reinterpret_cast<const vf4*>(&R[i][d0 + 4 * q4]);
+        for (int s4 = 0; s4 < 8; ++s4) {
+            const int d = d0 + 4 * s4;
+            const vf4 av = *reinterpret_cast<const vf4*>(arow + d);
+            vf4 bv;
+            if constexpr (DQV) {
+                const int q4 = *reinterpret_cast<const int*>(bq + d);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float pr = f_mul(t, r[e]);
-                    cur[4 * q4 + e] = ii == 0 ? pr : f_add(cur[4 * q4 + e], pr);
-                }
+                for (int e = 0; e < 4; ++e) bv[e] = f_mul((float)(int8_t)(q4 >> (8 * e)), s_v);
+            } else {
+                bv = *reinterpret_cast<const vf4*>(brow + d);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const v16f_a p = mfma_prod(av[e], bv[e]);
+                if (s4 == 0 && e == 0) acc = p;
+                else acc = acc + p;
             }
         }
-        if (blk == 0) {
-#pragma unroll
-            for (int x = 0; x < 8; ++x) b0[x] = cur[x];
-        }
+        if (bb == 0) first = acc;
     }
+    return first + acc;
+}
+
+// phase 2 of one wave: the tile sum over the 64 query positions of
+// T[i][key] * R[i][dcol], two 32-blocks left to right and then the pair, into
+// int64 accumulators with 40 fraction bits
+__device__ __forceinline__ void kv_phase2(const float (*T)[kAK + 1], const float (*R)[kKvRow], int lane, int dcol,
+                                          int64_t (&fx)[16]) {
+    v16f_a acc, first;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) acc[x] += (int64_t)__builtin_rint((double)f_add(b0[x], cur[x]) * 0x1p40);
+    for (int bb = 0; bb < 2; ++bb) {
+#pragma unroll 8
+        for (int ii = 0; ii < 32; ++ii) {
+            const int i = 32 * bb + ii;
+            const v16f_a p = mfma_prod(T[i][lane], R[i][dcol]);
+            if (ii == 0) acc = p;
+            else acc = acc + p;
+        }
+        if (bb == 0) first = acc;
+    }
+    const v16f_a u = first + acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) fx[r] += (int64_t)__builtin_rint((double)u[r] * 0x1p40);
 }
 
 __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     AttnKvSmem& sm = *reinterpret_cast<AttnKvSmem*>(smem_raw);
-    const int tid = threadIdx.x;
-    const int ti = tid >> 5, tj = tid & 31;         // 2 rows x 2 keys of the 64 x 64 tile
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     // key tiles slowest, so that the longest walks (first tiles, causal) start first
     const unsigned nbh = (unsigned)(a.B * a.Hkv), hkv = (unsigned)a.Hkv;
@@ -841,35 +855,35 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a)
                                                                                    : a.S - 1)
                                          : a.S - 1;
     const int64_t qt0 = j0 / kAQ, qt1 = ihi_all / kAQ;
+    const int s32 = (int)a.S;
+    const int win = (a.window <= 0 || a.window >= a.S) ? 0 : (int)a.window;   // 0: no window
 
-    attn_load_kt<kKvThreads>(a.K, a.ldk, base + j0, krows, hk, sm.ks);
+    // K rows and q_v rows of the key tile (zeros past S)
     const Quantizer qz(a.s_v);
-    for (int e = tid; e < (kAK / 4) * (kAD / 4); e += kKvThreads) {
-        const int rq = e & 15, dq = e >> 4;
-        vf4 v[4];
+    for (int e = tid; e < kAK * (kAD / 4); e += kKvThreads) {
+        const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
+        vf4 k = {0.0f, 0.0f, 0.0f, 0.0f}, v = k;
+        if (row < krows) {
+            k = *reinterpret_cast<const vf4*>(a.K + (base + j0 + row) * a.ldk + hk * kAD + d4);
+            v = *reinterpret_cast<const vf4*>(a.V + (base + j0 + row) * a.ldv + hk * kAD + d4);
+        }
+        *reinterpret_cast<vf4*>(&sm.kr[row][d4]) = k;
+        unsigned q4 = 0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int64_t j = j0 + 4 * rq + u;
-            v[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (j < a.S) v[u] = *reinterpret_cast<const vf4*>(a.V + (base + j) * a.ldv + hk * kAD + 4 * dq);
+            bool in;
+            q4 |= (unsigned)(uint8_t)(int8_t)qz.q(v[u], &in) << (8 * u);
         }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            vf4 o;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                bool in;
-                o[u] = j0 + 4 * rq + u < a.S ? f_mul((float)qz.q(v[u][w], &in), a.s_v) : 0.0f;
-            }
-            *reinterpret_cast<vf4*>(&sm.vs[4 * dq + w][4 * rq]) = o;
-        }
+        *reinterpret_cast<unsigned*>(&sm.vq[row][d4]) = row < krows ? q4 : 0u;
     }
 
-    // outputs of this thread: key jr = tid / 16, d = d0 .. d0 + 7
-    const int jr = tid >> 4, d0 = (tid & 15) * 8;
-    int64_t accv[8], acck[8];
+    // wave roles
+    const int p1_dp = (w >> 2) & 1, p1_slab = w & 3, p1_half = w >> 3;
+    const int p2_dk = w >> 3, p2_slab = w & 7;
+    const int jcol = 16 * p1_slab + (lane & 15);
+    int64_t fx[16];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) accv[x] = acck[x] = 0;
+    for (int r = 0; r < 16; ++r) fx[r] = 0;
 
     for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {
         for (int64_t qt = qt0; qt <= qt1; ++qt) {
@@ -913,55 +927,59 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a)
                 }
             }
             __syncthreads();
-            float sc[2][2], dp[2][2], dsv[2][2];
-            canon_dot_rm<2, 2>(sm.qr, sm.ks, ti, tj, sc);
-            canon_dot_rm<2, 2>(sm.gr, sm.vs, ti, tj, dp);
+            // phase 1: logits and dP of the 64 x 64 tile, d-blocks in halves
+            {
+                const v16f_a part = p1_dp ? kv_phase1<true>(&sm.gr[lane][0], nullptr, &sm.vq[jcol][0], a.s_v, p1_half)
+                                          : kv_phase1<false>(&sm.qr[lane][0], &sm.kr[jcol][0], nullptr, a.s_v,
+                                                             p1_half);
+                float (*T)[kAK + 1] = p1_dp ? sm.dt : sm.pt;
+                if (p1_half) {
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int il = 2 * ti + x;
-                const int64_t i = i0 + il;
-                const int64_t lo = a.window > 0 ? i - a.window + 1 : 0;
+                    for (int r = 0; r < 16; ++r) T[16 * (r >> 2) + 4 * (lane >> 4) + (r & 3)][jcol] = part[r];
+                }
+                __syncthreads();
+                if (!p1_half) {
 #pragma unroll
-                for (int y = 0; y < 2; ++y) {
-                    const int jl = 2 * tj + y;
-                    const int64_t j = j0 + jl;
-                    float P = 0.0f;
-                    dsv[x][y] = 0.0f;
-                    if (i < a.S && j <= i && j >= lo) {
-                        const float p = own_exp(f_sub(f_mul(sc[x][y], a.c), sm.rowm[il]), a.ek);
-                        P = f_div(p, sm.rowl[il]);
-                        dsv[x][y] = f_mul(P, f_sub(dp[x][y], sm.rowdelta[il]));
+                    for (int r = 0; r < 16; ++r) {
+                        float& t = T[16 * (r >> 2) + 4 * (lane >> 4) + (r & 3)][jcol];
+                        t = f_add(part[r], t);
                     }
-                    sm.pt[il][jl] = P;
                 }
             }
             __syncthreads();
-            kv_tile_sums(sm.pt, sm.gr, jr, d0, accv);
-            __syncthreads();
+            // P and dS of the tile (32-bit positions: S < 2^31)
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
-#pragma unroll
-                for (int y = 0; y < 2; ++y) sm.pt[2 * ti + x][2 * tj + y] = dsv[x][y];
+            for (int e = 0; e < (kAQ * kAK) / kKvThreads; ++e) {
+                const int idx = tid + kKvThreads * e;
+                const int il = idx >> 6, jl = idx & 63;
+                const int i = (int)i0 + il, j = (int)j0 + jl;
+                float P = 0.0f, dS = 0.0f;
+                if (i < s32 && j <= i && (win == 0 || j > i - win)) {
+                    const float p = own_exp(f_sub(f_mul(sm.pt[il][jl], a.c), sm.rowm[il]), a.ek);
+                    P = f_div(p, sm.rowl[il]);
+                    dS = f_mul(P, f_sub(sm.dt[il][jl], sm.rowdelta[il]));
+                }
+                sm.pt[il][jl] = P;
+                sm.dt[il][jl] = dS;
+            }
             __syncthreads();
-            kv_tile_sums(sm.pt, sm.qr, jr, d0, acck);
+            // phase 2: tile sums of P x dO (dV) and dS x Q (dK)
+            if (p2_dk) kv_phase2(sm.dt, sm.qr, lane, 16 * p2_slab + (lane & 15), fx);
+            else kv_phase2(sm.pt, sm.gr, lane, 16 * p2_slab + (lane & 15), fx);
         }
     }
-    if (jr < krows) {
-        const int64_t row = base + j0 + jr;
-        const float* v = a.V + row * a.ldv + hk * kAD + d0;
-        float* ok = a.dK + row * a.ldg + hk * kAD + d0;
-        float* ov = a.dV + row * a.ldg + hk * kAD + d0;
+    // lane l, register r: key 16*(r/4) + 4*(l/16) + r%4 of the tile, d = 16*slab + l%16
+    const int d = 16 * p2_slab + (lane & 15);
 #pragma unroll
-        for (int q4 = 0; q4 < 2; ++q4) {
-            const vf4 vv = *reinterpret_cast<const vf4*>(v + 4 * q4);
-            vf4 k4, v4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                k4[e] = f_mul(f_mul((float)acck[4 * q4 + e], 0x1p-40f), a.c);
-                v4[e] = qz.in_range(vv[e]) ? f_mul((float)accv[4 * q4 + e], 0x1p-40f) : 0.0f;
-            }
-            *reinterpret_cast<vf4*>(ok + 4 * q4) = k4;
-            *reinterpret_cast<vf4*>(ov + 4 * q4) = v4;
+    for (int r = 0; r < 16; ++r) {
+        const int jl = 16 * (r >> 2) + 4 * (lane >> 4) + (r & 3);
+        if (jl >= krows) continue;
+        const int64_t row = base + j0 + jl;
+        if (p2_dk) {
+            a.dK[row * a.ldg + hk * kAD + d] = f_mul(f_mul((float)fx[r], 0x1p-40f), a.c);
+        } else {
+            const float v = a.V[row * a.ldv + hk * kAD + d];
+            a.dV[row * a.ldg + hk * kAD + d] = qz.in_range(v) ? f_mul((float)fx[r], 0x1p-40f) : 0.0f;
         }
     }
 }
