@@ -734,18 +734,19 @@ hipError_t launch_attn_bwd_dq(const float* Q, const float* K, const float* V, co
 // the VALU adds the products in the canonical order.  Lane l feeds A row l
 // and B column l % 16; register 4*beta + e of lane l receives row
 // 16*beta + 4*(l / 16) + e, column l % 16 (64 rows x 16 columns per MFMA).
-//   phase 1 (16 waves): logits (waves 0-3) and dP (waves 4-7) for key slab
-//     16*(w % 4) .. +15 over d-blocks 0 and 1; waves 8-15 the same over
-//     d-blocks 2 and 3; the pair sums meet in LDS as (b0 + b1) + (b2 + b3);
+//   phase 1 (8 waves): logits (waves 0-3) and dP (waves 4-7) for key slab
+//     16*(w % 4) .. +15, the four d-blocks left to right, then
+//     (b0 + b1) + (b2 + b3); stored key-major;
 //   an elementwise pass forms P and dS for the 64 x 64 tile;
-//   phase 2 (16 waves): the tile sums over the 64 query positions (two
-//     32-blocks, then the pair) of P x dO (waves 0-7) and dS x Q (waves
-//     8-15) for d slab 16*(w % 8) .. +15, each into 16 int64 accumulators.
+//   phase 2 (8 waves): the tile sums over the 64 query positions (two
+//     32-blocks, then the pair) of P x dO, then of dS x Q, for d slab
+//     16*w .. +15, each into 16 int64 accumulators.
 typedef float v16f_a __attribute__((ext_vector_type(16)));
 
-constexpr int kKvThreads = 1024;
+constexpr int kKvThreads = 512;
 constexpr int kKvRow = kAD + 4;     // floats per LDS row of K, Q and dO
 constexpr int kKvRowQ = kAD + 16;   // bytes per LDS row of q_v
+constexpr int kKvRowT = kAQ + 4;    // floats per LDS row of the key-major tiles
 
 struct AttnKvArgs {
     const float* Q;
@@ -765,8 +766,8 @@ struct AttnKvSmem {
     float kr[kAK][kKvRow];          // K tile, key-major
     float qr[kAQ][kKvRow];          // Q tile, row-major
     float gr[kAQ][kKvRow];          // dO tile, row-major
-    float pt[kAQ][kAK + 1];         // logits, then P
-    float dt[kAQ][kAK + 1];         // dP, then dS
+    float pt[kAK][kKvRowT];         // logits, then P (key-major)
+    float dt[kAK][kKvRowT];         // dP, then dS (key-major)
     int8_t vq[kAK][kKvRowQ];        // q_v tile, key-major
     float rowm[kAQ], rowl[kAQ], rowdelta[kAQ];
 };
@@ -779,54 +780,99 @@ __device__ __forceinline__ v16f_a mfma_prod(float a, float b) {
     return __builtin_amdgcn_mfma_f32_16x16x1f32(a, b, cneg, 0, 0, 0);
 }
 
-// phase 1 of one wave: the sums of d-blocks 2*half and 2*half + 1 (each left
-// to right over its 32 steps), added as b_{2 half} + b_{2 half + 1}; A from
-// row `lane` of arow's tile, B from one key row (fp32, or q_v dequantised)
+// KV_STEP(acc): the adds of a step stay at their place in the program (an
+// empty asm that takes the running sums in and out), so the next MFMA is
+// issued before them and no product waits in a register for later adds.
+#define KV_STEP(acc) __asm__ volatile("" : "+v"(acc))
+// Both phases run one product chain per wave, software-pipelined: the MFMA
+// of step s + 1 is issued before the adds of step s (a scheduling fence after
+// each step keeps that order), and the operands of the next 4 steps are read
+// while the current 4 are consumed.
+
+// phase 1 of one wave: CanonSum over d of A[lane][d] * B[key][d] for 64
+// rows x 16 keys: d-blocks of 32 left to right, then (b0 + b1) + (b2 + b3);
+// B is fp32, or q_v dequantised on the fly
 template <bool DQV>
-__device__ __forceinline__ v16f_a kv_phase1(const float* arow, const float* brow, const int8_t* bq, float s_v,
-                                            int half) {
-    v16f_a acc, first;
+__device__ __forceinline__ vf4 kv_b4(const float* brow, const int8_t* bq, float s_v, int d) {
+    vf4 bv;
+    if constexpr (DQV) {
+        const int q4 = *reinterpret_cast<const int*>(bq + d);
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-        const int d0 = 32 * (2 * half + bb);
+        for (int e = 0; e < 4; ++e) bv[e] = f_mul((float)(int8_t)(q4 >> (8 * e)), s_v);
+    } else {
+        bv = *reinterpret_cast<const vf4*>(brow + d);
+    }
+    return bv;
+}
+
+template <bool DQV>
+__device__ __forceinline__ v16f_a kv_phase1(const float* arow, const float* brow, const int8_t* bq, float s_v) {
+    v16f_a b01, b2, acc;
+#pragma unroll 1
+    for (int blk = 0; blk < kAD / 32; ++blk) {
+        const int d0 = 32 * blk;
+        v16f_a n;
+        vf4 a_cur = *reinterpret_cast<const vf4*>(arow + d0), b_cur = kv_b4<DQV>(brow, bq, s_v, d0), a_nxt, b_nxt;
+        v16f_a p = mfma_prod(a_cur[0], b_cur[0]);
 #pragma unroll
-        for (int s4 = 0; s4 < 8; ++s4) {
-            const int d = d0 + 4 * s4;
-            const vf4 av = *reinterpret_cast<const vf4*>(arow + d);
-            vf4 bv;
-            if constexpr (DQV) {
-                const int q4 = *reinterpret_cast<const int*>(bq + d);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) bv[e] = f_mul((float)(int8_t)(q4 >> (8 * e)), s_v);
-            } else {
-                bv = *reinterpret_cast<const vf4*>(brow + d);
+        for (int g = 0; g < 8; ++g) {
+            if (g + 1 < 8) {
+                a_nxt = *reinterpret_cast<const vf4*>(arow + d0 + 4 * (g + 1));
+                b_nxt = kv_b4<DQV>(brow, bq, s_v, d0 + 4 * (g + 1));
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const v16f_a p = mfma_prod(av[e], bv[e]);
-                if (s4 == 0 && e == 0) acc = p;
+                const int st = 4 * g + e;
+                if (st + 1 < 32) n = e < 3 ? mfma_prod(a_cur[e + 1], b_cur[e + 1]) : mfma_prod(a_nxt[0], b_nxt[0]);
+                if (st == 0) acc = p;
                 else acc = acc + p;
+                KV_STEP(acc);
+                p = n;
             }
+            a_cur = a_nxt;
+            b_cur = b_nxt;
         }
-        if (bb == 0) first = acc;
+        if (blk == 0) b01 = acc;
+        else if (blk == 1) b01 = b01 + acc;
+        else if (blk == 2) b2 = acc;
     }
-    return first + acc;
+    return b01 + (b2 + acc);
 }
 
 // phase 2 of one wave: the tile sum over the 64 query positions of
-// T[i][key] * R[i][dcol], two 32-blocks left to right and then the pair, into
-// int64 accumulators with 40 fraction bits
-__device__ __forceinline__ void kv_phase2(const float (*T)[kAK + 1], const float (*R)[kKvRow], int lane, int dcol,
+// T[key][i] * R[i][dcol] (keys from the lanes), two 32-blocks left to right
+// and then the pair, into int64 accumulators with 40 fraction bits
+__device__ __forceinline__ void kv_phase2(const float (*T)[kKvRowT], const float (*R)[kKvRow], int lane, int dcol,
                                           int64_t (&fx)[16]) {
     v16f_a acc, first;
-#pragma unroll
+#pragma unroll 1
     for (int bb = 0; bb < 2; ++bb) {
-#pragma unroll 8
-        for (int ii = 0; ii < 32; ++ii) {
-            const int i = 32 * bb + ii;
-            const v16f_a p = mfma_prod(T[i][lane], R[i][dcol]);
-            if (ii == 0) acc = p;
-            else acc = acc + p;
+        const int i0 = 32 * bb;
+        v16f_a n;
+        vf4 a_cur = *reinterpret_cast<const vf4*>(&T[lane][i0]), a_nxt;
+        float r_cur[4], r_nxt[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r_cur[e] = R[i0 + e][dcol];
+        v16f_a p = mfma_prod(a_cur[0], r_cur[0]);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            if (g + 1 < 8) {
+                a_nxt = *reinterpret_cast<const vf4*>(&T[lane][i0 + 4 * (g + 1)]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r_nxt[e] = R[i0 + 4 * (g + 1) + e][dcol];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int st = 4 * g + e;
+                if (st + 1 < 32) n = e < 3 ? mfma_prod(a_cur[e + 1], r_cur[e + 1]) : mfma_prod(a_nxt[0], r_nxt[0]);
+                if (st == 0) acc = p;
+                else acc = acc + p;
+                KV_STEP(acc);
+                p = n;
+            }
+            a_cur = a_nxt;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r_cur[e] = r_nxt[e];
         }
         if (bb == 0) first = acc;
     }
@@ -877,13 +923,13 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a)
         *reinterpret_cast<unsigned*>(&sm.vq[row][d4]) = row < krows ? q4 : 0u;
     }
 
-    // wave roles
-    const int p1_dp = (w >> 2) & 1, p1_slab = w & 3, p1_half = w >> 3;
-    const int p2_dk = w >> 3, p2_slab = w & 7;
+    // wave roles: phase 1 (logits or dP, key slab), phase 2 (d slab)
+    const int p1_dp = w >> 2, p1_slab = w & 3;
     const int jcol = 16 * p1_slab + (lane & 15);
-    int64_t fx[16];
+    const int dcol = 16 * w + (lane & 15);
+    int64_t fv[16], fk[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) fx[r] = 0;
+    for (int r = 0; r < 16; ++r) fv[r] = fk[r] = 0;
 
     for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {
         for (int64_t qt = qt0; qt <= qt1; ++qt) {
@@ -927,60 +973,47 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a)
                 }
             }
             __syncthreads();
-            // phase 1: logits and dP of the 64 x 64 tile, d-blocks in halves
+            // phase 1: logits and dP of the 64 x 64 tile, stored key-major
             {
-                const v16f_a part = p1_dp ? kv_phase1<true>(&sm.gr[lane][0], nullptr, &sm.vq[jcol][0], a.s_v, p1_half)
-                                          : kv_phase1<false>(&sm.qr[lane][0], &sm.kr[jcol][0], nullptr, a.s_v,
-                                                             p1_half);
-                float (*T)[kAK + 1] = p1_dp ? sm.dt : sm.pt;
-                if (p1_half) {
+                const v16f_a part = p1_dp ? kv_phase1<true>(&sm.gr[lane][0], nullptr, &sm.vq[jcol][0], a.s_v)
+                                          : kv_phase1<false>(&sm.qr[lane][0], &sm.kr[jcol][0], nullptr, a.s_v);
+                float (*T)[kKvRowT] = p1_dp ? sm.dt : sm.pt;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) T[16 * (r >> 2) + 4 * (lane >> 4) + (r & 3)][jcol] = part[r];
-                }
-                __syncthreads();
-                if (!p1_half) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float& t = T[16 * (r >> 2) + 4 * (lane >> 4) + (r & 3)][jcol];
-                        t = f_add(part[r], t);
-                    }
-                }
+                for (int beta = 0; beta < 4; ++beta)
+                    *reinterpret_cast<vf4*>(&T[jcol][16 * beta + 4 * (lane >> 4)]) =
+                        vf4{part[4 * beta], part[4 * beta + 1], part[4 * beta + 2], part[4 * beta + 3]};
             }
             __syncthreads();
             // P and dS of the tile (32-bit positions: S < 2^31)
 #pragma unroll
             for (int e = 0; e < (kAQ * kAK) / kKvThreads; ++e) {
                 const int idx = tid + kKvThreads * e;
-                const int il = idx >> 6, jl = idx & 63;
+                const int jl = idx >> 6, il = idx & 63;
                 const int i = (int)i0 + il, j = (int)j0 + jl;
                 float P = 0.0f, dS = 0.0f;
                 if (i < s32 && j <= i && (win == 0 || j > i - win)) {
-                    const float p = own_exp(f_sub(f_mul(sm.pt[il][jl], a.c), sm.rowm[il]), a.ek);
+                    const float p = own_exp(f_sub(f_mul(sm.pt[jl][il], a.c), sm.rowm[il]), a.ek);
                     P = f_div(p, sm.rowl[il]);
-                    dS = f_mul(P, f_sub(sm.dt[il][jl], sm.rowdelta[il]));
+                    dS = f_mul(P, f_sub(sm.dt[jl][il], sm.rowdelta[il]));
                 }
-                sm.pt[il][jl] = P;
-                sm.dt[il][jl] = dS;
+                sm.pt[jl][il] = P;
+                sm.dt[jl][il] = dS;
             }
             __syncthreads();
             // phase 2: tile sums of P x dO (dV) and dS x Q (dK)
-            if (p2_dk) kv_phase2(sm.dt, sm.qr, lane, 16 * p2_slab + (lane & 15), fx);
-            else kv_phase2(sm.pt, sm.gr, lane, 16 * p2_slab + (lane & 15), fx);
+            kv_phase2(sm.pt, sm.gr, lane, dcol, fv);
+            kv_phase2(sm.dt, sm.qr, lane, dcol, fk);
         }
     }
-    // lane l, register r: key 16*(r/4) + 4*(l/16) + r%4 of the tile, d = 16*slab + l%16
-    const int d = 16 * p2_slab + (lane & 15);
+    // lane l, register r: key 16*(r/4) + 4*(l/16) + r%4 of the tile, d = dcol
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int jl = 16 * (r >> 2) + 4 * (lane >> 4) + (r & 3);
         if (jl >= krows) continue;
         const int64_t row = base + j0 + jl;
-        if (p2_dk) {
-            a.dK[row * a.ldg + hk * kAD + d] = f_mul(f_mul((float)fx[r], 0x1p-40f), a.c);
-        } else {
-            const float v = a.V[row * a.ldv + hk * kAD + d];
-            a.dV[row * a.ldg + hk * kAD + d] = qz.in_range(v) ? f_mul((float)fx[r], 0x1p-40f) : 0.0f;
-        }
+        a.dK[row * a.ldg + hk * kAD + dcol] = f_mul(f_mul((float)fk[r], 0x1p-40f), a.c);
+        const float v = a.V[row * a.ldv + hk * kAD + dcol];
+        a.dV[row * a.ldg + hk * kAD + dcol] = qz.in_range(v) ? f_mul((float)fv[r], 0x1p-40f) : 0.0f;
     }
 }
 
