@@ -112,42 +112,6 @@ __device__ __forceinline__ void canon_dot4x4(const float (*A)[kAQ], const float 
     }
 }
 
-// The same sums for NX rows x NY keys per thread (rows NX*ti.., keys NY*tj..);
-// each output sees exactly the operations of canon_dot4x4.
-template <int NX, int NY>
-__device__ __forceinline__ void canon_dot(const float (*A)[kAQ], const float (*B)[kAK], int ti, int tj,
-                                          float (&s)[NX][NY]) {
-    float b01[NX][NY], b2[NX][NY], cur[NX][NY];
-#pragma unroll
-    for (int blk = 0; blk < kAD / 32; ++blk) {
-#pragma unroll 4
-        for (int dd = 0; dd < 32; ++dd) {
-            const int d = blk * 32 + dd;
-            float a[NX], b[NY];
-#pragma unroll
-            for (int x = 0; x < NX; ++x) a[x] = A[d][NX * ti + x];
-#pragma unroll
-            for (int y = 0; y < NY; ++y) b[y] = B[d][NY * tj + y];
-#pragma unroll
-            for (int x = 0; x < NX; ++x)
-#pragma unroll
-                for (int y = 0; y < NY; ++y) {
-                    const float pr = f_mul(a[x], b[y]);
-                    cur[x][y] = dd == 0 ? pr : f_add(cur[x][y], pr);
-                }
-        }
-#pragma unroll
-        for (int x = 0; x < NX; ++x)
-#pragma unroll
-            for (int y = 0; y < NY; ++y) {
-                if (blk == 0) b01[x][y] = cur[x][y];
-                if (blk == 1) b01[x][y] = f_add(b01[x][y], cur[x][y]);
-                if (blk == 2) b2[x][y] = cur[x][y];
-                if (blk == 3) s[x][y] = f_add(b01[x][y], f_add(b2[x][y], cur[x][y]));
-            }
-    }
-}
-
 // 16 logits of this thread: rows 4ti..4ti+3, keys 4tj..4tj+3 of the tile
 __device__ __forceinline__ void attn_logits_from(const float (*qs)[kAQ], const float (*ks)[kAK], int ti, int tj,
                                                  float c, float s[4][4]) {
@@ -511,9 +475,8 @@ hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64
 //   u_igd = CanonSum over the 64 key positions of tile g of dS_ij * K_jd;
 //   dQ_id = (fl(sum_g rne(u_igd * 2^40)) * 2^-40) * c.
 // The tile sums become int64 with 40 fraction bits and add exactly, in any
-// order: one workgroup per (batch, head, 64-query block) walks the key tiles
-// and keeps 32 int64 accumulators per thread.
-constexpr int kDqFrac = 40;
+// order (the kernel follows the key and value gradients below, on the same
+// matrix-core engine).
 
 struct AttnBwdArgs {
     const float* Q;
@@ -527,193 +490,6 @@ struct AttnBwdArgs {
     float c, s_v;
     ExpConsts ek;
 };
-
-struct AttnBwdSmem {
-    float qs[kAD][kAQ];             // Q tile, d-major
-    float gs[kAD][kAQ];             // dO tile, d-major
-    float ks[kAD][kAK];             // K tile, d-major (logits)
-    union {
-        float vs[kAD][kAK];         // V^ tile, d-major (dP)
-        float kt[kAK][kAD];         // K tile, key-major (dQ)
-    } u;
-    float ds[kAQ][kAK + 1];         // dS tile
-    float rowm[kAQ], rowl[kAQ], rowdelta[kAQ];
-};
-
-constexpr int kDqThreads = 1024;
-
-__global__ __launch_bounds__(kDqThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) {
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-    AttnBwdSmem& sm = *reinterpret_cast<AttnBwdSmem*>(smem_raw);
-    const int tid = threadIdx.x;
-    const int ti = tid >> 5, tj = tid & 31;         // 2 rows x 2 keys of the 64 x 64 tile
-
-    const unsigned nqb = (unsigned)((a.S + kAQ - 1) / kAQ), hq = (unsigned)a.Hq;
-    const unsigned qb = blockIdx.x % nqb;
-    const unsigned bh = blockIdx.x / nqb;
-    const int64_t h = bh % hq;
-    const int64_t b = bh / hq;
-    const int64_t hk = (unsigned)h / (hq / (unsigned)a.Hkv);
-    const int64_t q0 = (int64_t)qb * kAQ;
-    const int64_t qrows = a.S - q0 < kAQ ? a.S - q0 : kAQ;
-    const int64_t base = b * a.S;
-    const int64_t klo = a.window > 0 ? (q0 - a.window + 1 > 0 ? q0 - a.window + 1 : 0) : 0;
-    const int64_t khi = q0 + qrows - 1;
-    const int64_t kt0 = klo / kAK, kt1 = khi / kAK;
-
-    attn_load_kt<kDqThreads>(a.Q, a.ldq, base + q0, qrows, h, sm.qs);
-    attn_load_kt<kDqThreads>(a.dO, a.ldo, base + q0, qrows, h, sm.gs);
-    if (tid < kAQ) {
-        float m = 0.0f, l = 1.0f, delta = 0.0f;
-        if (tid < qrows) {
-            const int64_t row = base + q0 + tid;
-            m = a.stats[2 * (row * a.Hq + h)];
-            l = a.stats[2 * (row * a.Hq + h) + 1];
-            // Delta = CanonSum_d(dO * O): four d-blocks, then the pair tree
-            const float* go = a.dO + row * a.ldo + h * kAD;
-            const float* o = a.O + row * a.ldo + h * kAD;
-            float bs[4];
-            for (int blk = 0; blk < 4; ++blk) {
-                float x = f_mul(go[32 * blk], o[32 * blk]);
-                for (int d = 1; d < 32; ++d) x = f_add(x, f_mul(go[32 * blk + d], o[32 * blk + d]));
-                bs[blk] = x;
-            }
-            delta = f_add(f_add(bs[0], bs[1]), f_add(bs[2], bs[3]));
-        }
-        sm.rowm[tid] = m;
-        sm.rowl[tid] = l;
-        sm.rowdelta[tid] = delta;
-    }
-    auto allowed = [&](int64_t i, int64_t j) {
-        const int64_t lo = a.window > 0 ? i - a.window + 1 : 0;
-        return i < a.S && j <= i && j >= lo;
-    };
-    const Quantizer qz(a.s_v);
-    // dQ outputs of this thread: row r = tid / 16, d = d0 .. d0 + 7
-    const int r = tid >> 4, d0 = (tid & 15) * 8;
-    int64_t acc[8];
-#pragma unroll
-    for (int x = 0; x < 8; ++x) acc[x] = 0;
-
-    for (int64_t kt = kt0; kt <= kt1; ++kt) {
-        const int64_t j0 = kt * kAK;
-        __syncthreads();
-        attn_load_kt<kDqThreads>(a.K, a.ldk, base + j0, a.S - j0, hk, sm.ks);
-        // V^ = fl(q_v * s_v), d-major
-#pragma unroll
-        for (int e = tid; e < (kAK / 4) * (kAD / 4); e += kDqThreads) {
-            const int rq = e & 15, dq = e >> 4;
-            vf4 v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t j = j0 + 4 * rq + u;
-                v[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
-                if (j < a.S) v[u] = *reinterpret_cast<const vf4*>(a.V + (base + j) * a.ldv + hk * kAD + 4 * dq);
-            }
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                vf4 o;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    bool in;
-                    o[u] = j0 + 4 * rq + u < a.S ? f_mul((float)qz.q(v[u][w], &in), a.s_v) : 0.0f;
-                }
-                *reinterpret_cast<vf4*>(&sm.u.vs[4 * dq + w][4 * rq]) = o;
-            }
-        }
-        __syncthreads();
-        float sc[2][2], dp[2][2];
-        canon_dot<2, 2>(sm.qs, sm.ks, ti, tj, sc);
-        canon_dot<2, 2>(sm.gs, sm.u.vs, ti, tj, dp);
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int i = 2 * ti + x;
-#pragma unroll
-            for (int y = 0; y < 2; ++y) {
-                const int j = 2 * tj + y;
-                sc[x][y] = f_mul(sc[x][y], a.c);
-                float dsv = 0.0f;
-                if (allowed(q0 + i, j0 + j)) {
-                    const float p = own_exp(f_sub(sc[x][y], sm.rowm[i]), a.ek);
-                    dsv = f_mul(f_div(p, sm.rowl[i]), f_sub(dp[x][y], sm.rowdelta[i]));
-                }
-                sm.ds[i][j] = dsv;
-            }
-        }
-        __syncthreads();
-        // K tile again, key-major, over the V^ buffer
-#pragma unroll
-        for (int e = tid; e < kAK * (kAD / 4); e += kDqThreads) {
-            const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
-            vf4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (j0 + row < a.S) v = *reinterpret_cast<const vf4*>(a.K + (base + j0 + row) * a.ldk + hk * kAD + d4);
-            *reinterpret_cast<vf4*>(&sm.u.kt[row][d4]) = v;
-        }
-        __syncthreads();
-        // tile sums u over the 64 keys: two 32-key blocks left to right, then the pair
-        float b0[8], cur[8];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            for (int jj = 0; jj < 32; ++jj) {
-                const int j = 32 * blk + jj;
-                const float dsv = sm.ds[r][j];
-#pragma unroll
-                for (int q4 = 0; q4 < 2; ++q4) {
-                    const vf4 kv = *reinterpret_cast<const vf4*>(&sm.u.kt[j][d0 + 4 * q4]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float pr = f_mul(dsv, kv[e]);
-                        cur[4 * q4 + e] = jj == 0 ? pr : f_add(cur[4 * q4 + e], pr);
-                    }
-                }
-            }
-            if (blk == 0) {
-#pragma unroll
-                for (int x = 0; x < 8; ++x) b0[x] = cur[x];
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            const float u = f_add(b0[x], cur[x]);
-            acc[x] += (int64_t)__builtin_rint((double)u * 0x1p40);
-        }
-    }
-    // dQ = (fl(acc) * 2^-40) * c
-    if (r < qrows) {
-        float* out = a.dQ + (base + q0 + r) * a.ldo + h * kAD + d0;
-#pragma unroll
-        for (int q4 = 0; q4 < 2; ++q4) {
-            vf4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = f_mul(f_mul((float)acc[4 * q4 + e], 0x1p-40f), a.c);
-            *reinterpret_cast<vf4*>(out + 4 * q4) = o;
-        }
-    }
-}
-
-hipError_t launch_attn_bwd_dq(const float* Q, const float* K, const float* V, const float* O, const float* dO,
-                              const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t ldq,
-                              int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dQ,
-                              const ExpConsts& ek, hipStream_t st) {
-    if (B == 0 || S == 0) return hipSuccess;
-    AttnBwdArgs a;
-    a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.stats = stats; a.dQ = dQ;
-    a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.window = window;
-    a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
-    a.s_v = s_v;
-    a.ek = ek;
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnBwdSmem));
-        attr = true;
-    }
-    const int64_t blocks = B * Hq * ceil_div(S, kAQ);
-    if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)blocks), dim3(kDqThreads), sizeof(AttnBwdSmem), st, a);
-    return hipGetLastError();
-}
-
 
 // dK and dV of the attention.  The pages give the 64-bit fixed-point
 // accumulation for dQ only; this library reads the same format into the key
@@ -1038,6 +814,168 @@ hipError_t launch_attn_bwd_dkdv(const float* Q, const float* K, const float* V, 
     const int64_t blocks = B * Hkv * ceil_div(S, kAK);
     if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)blocks), dim3(kKvThreads), sizeof(AttnKvSmem), st, a);
+    return hipGetLastError();
+}
+
+// dQ on the same engine.  One workgroup (8 waves) per (batch, query head,
+// block of 64 queries) keeps the Q and dO rows and walks the key tiles; per
+// tile: phase 1 as for dK/dV (logits and dP of the 64 x 64 tile, stored
+// row-major), dS elementwise, then each wave's tile sum over the 64 key
+// positions of dS x K for d slab 16*w .. +15 into 16 int64 accumulators.
+struct AttnDqSmem {
+    float qr[kAQ][kKvRow];          // Q rows of the block
+    float gr[kAQ][kKvRow];          // dO rows of the block
+    float kr[kAK][kKvRow];          // K tile, key-major
+    float st[kAQ][kKvRowT];         // logits of the tile (row-major)
+    float dt[kAQ][kKvRowT];         // dP, then dS (row-major)
+    int8_t vq[kAK][kKvRowQ];        // q_v tile, key-major
+    float rowm[kAQ], rowl[kAQ], rowdelta[kAQ];
+};
+static_assert(sizeof(AttnDqSmem) <= 163840, "LDS of one CU");
+
+__global__ __launch_bounds__(kKvThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    AttnDqSmem& sm = *reinterpret_cast<AttnDqSmem*>(smem_raw);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const unsigned nqb = (unsigned)((a.S + kAQ - 1) / kAQ), hq = (unsigned)a.Hq;
+    const unsigned qb = blockIdx.x % nqb;
+    const unsigned bh = blockIdx.x / nqb;
+    const int64_t h = bh % hq;
+    const int64_t b = bh / hq;
+    const int64_t hk = (unsigned)h / (hq / (unsigned)a.Hkv);
+    const int64_t q0 = (int64_t)qb * kAQ;
+    const int64_t qrows = a.S - q0 < kAQ ? a.S - q0 : kAQ;
+    const int64_t base = b * a.S;
+    const int64_t klo = a.window > 0 ? (q0 - a.window + 1 > 0 ? q0 - a.window + 1 : 0) : 0;
+    const int64_t khi = q0 + qrows - 1;
+    const int64_t kt0 = klo / kAK, kt1 = khi / kAK;
+    const int s32 = (int)a.S;
+    const int win = (a.window <= 0 || a.window >= a.S) ? 0 : (int)a.window;   // 0: no window
+
+    // Q and dO rows of the block, row-major (zeros past S)
+    for (int e = tid; e < kAQ * (kAD / 4); e += kKvThreads) {
+        const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
+        vf4 q = {0.0f, 0.0f, 0.0f, 0.0f}, g = q;
+        if (row < qrows) {
+            q = *reinterpret_cast<const vf4*>(a.Q + (base + q0 + row) * a.ldq + h * kAD + d4);
+            g = *reinterpret_cast<const vf4*>(a.dO + (base + q0 + row) * a.ldo + h * kAD + d4);
+        }
+        *reinterpret_cast<vf4*>(&sm.qr[row][d4]) = q;
+        *reinterpret_cast<vf4*>(&sm.gr[row][d4]) = g;
+    }
+    // row statistics; Delta = CanonSum_d(dO * O): four lanes per row hold the
+    // d-blocks, then the pair tree through two lane swaps
+    if (tid < 4 * kAQ) {
+        const int row = tid >> 2, blk = tid & 3;
+        float x = 0.0f;
+        if (row < qrows) {
+            const float* go = a.dO + (base + q0 + row) * a.ldo + h * kAD + 32 * blk;
+            const float* o = a.O + (base + q0 + row) * a.ldo + h * kAD + 32 * blk;
+            x = f_mul(go[0], o[0]);
+            for (int d = 1; d < 32; ++d) x = f_add(x, f_mul(go[d], o[d]));
+        }
+        x = f_add(x, __shfl_xor(x, 1));
+        x = f_add(x, __shfl_xor(x, 2));
+        if (blk == 0) {
+            float m = 0.0f, l = 1.0f;
+            if (row < qrows) {
+                const int64_t r = (base + q0 + row) * a.Hq + h;
+                m = a.stats[2 * r];
+                l = a.stats[2 * r + 1];
+            }
+            sm.rowm[row] = m;
+            sm.rowl[row] = l;
+            sm.rowdelta[row] = row < qrows ? x : 0.0f;
+        }
+    }
+
+    const Quantizer qz(a.s_v);
+    const int p1_dp = w >> 2, p1_slab = w & 3;
+    const int jcol = 16 * p1_slab + (lane & 15);
+    const int dcol = 16 * w + (lane & 15);
+    int64_t fx[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) fx[r] = 0;
+
+    for (int64_t kt = kt0; kt <= kt1; ++kt) {
+        const int64_t j0 = kt * kAK;
+        const int64_t krows = a.S - j0 < kAK ? a.S - j0 : kAK;
+        __syncthreads();
+        // K rows and q_v rows of the tile (zeros past S)
+        for (int e = tid; e < kAK * (kAD / 4); e += kKvThreads) {
+            const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
+            vf4 k = {0.0f, 0.0f, 0.0f, 0.0f}, v = k;
+            if (row < krows) {
+                k = *reinterpret_cast<const vf4*>(a.K + (base + j0 + row) * a.ldk + hk * kAD + d4);
+                v = *reinterpret_cast<const vf4*>(a.V + (base + j0 + row) * a.ldv + hk * kAD + d4);
+            }
+            *reinterpret_cast<vf4*>(&sm.kr[row][d4]) = k;
+            unsigned q4 = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                bool in;
+                q4 |= (unsigned)(uint8_t)(int8_t)qz.q(v[u], &in) << (8 * u);
+            }
+            *reinterpret_cast<unsigned*>(&sm.vq[row][d4]) = row < krows ? q4 : 0u;
+        }
+        __syncthreads();
+        // phase 1: logits and dP of the 64 x 64 tile, stored row-major
+        {
+            const v16f_a part = p1_dp ? kv_phase1<true>(&sm.gr[lane][0], nullptr, &sm.vq[jcol][0], a.s_v)
+                                      : kv_phase1<false>(&sm.qr[lane][0], &sm.kr[jcol][0], nullptr, a.s_v);
+            float (*T)[kKvRowT] = p1_dp ? sm.dt : sm.st;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) T[16 * (r >> 2) + 4 * (lane >> 4) + (r & 3)][jcol] = part[r];
+        }
+        __syncthreads();
+        // dS of the tile (32-bit positions: S < 2^31)
+#pragma unroll
+        for (int e = 0; e < (kAQ * kAK) / kKvThreads; ++e) {
+            const int idx = tid + kKvThreads * e;
+            const int il = idx >> 6, jl = idx & 63;
+            const int i = (int)q0 + il, j = (int)j0 + jl;
+            float dS = 0.0f;
+            if (i < s32 && j <= i && (win == 0 || j > i - win)) {
+                const float p = own_exp(f_sub(f_mul(sm.st[il][jl], a.c), sm.rowm[il]), a.ek);
+                dS = f_mul(f_div(p, sm.rowl[il]), f_sub(sm.dt[il][jl], sm.rowdelta[il]));
+            }
+            sm.dt[il][jl] = dS;
+        }
+        __syncthreads();
+        // phase 2: tile sums of dS x K
+        kv_phase2(sm.dt, sm.kr, lane, dcol, fx);
+    }
+    // dQ = (fl(acc) * 2^-40) * c; lane l, register r: row 16*(r/4) + 4*(l/16) + r%4
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int il = 16 * (r >> 2) + 4 * (lane >> 4) + (r & 3);
+        if (il >= qrows) continue;
+        a.dQ[(base + q0 + il) * a.ldo + h * kAD + dcol] = f_mul(f_mul((float)fx[r], 0x1p-40f), a.c);
+    }
+}
+
+hipError_t launch_attn_bwd_dq(const float* Q, const float* K, const float* V, const float* O, const float* dO,
+                              const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t ldq,
+                              int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dQ,
+                              const ExpConsts& ek, hipStream_t st) {
+    if (B == 0 || S == 0) return hipSuccess;
+    AttnBwdArgs a;
+    a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.stats = stats; a.dQ = dQ;
+    a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.window = window;
+    a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
+    a.s_v = s_v;
+    a.ek = ek;
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnDqSmem));
+        attr = true;
+    }
+    const int64_t blocks = B * Hq * ceil_div(S, kAQ);
+    if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)blocks), dim3(kKvThreads), sizeof(AttnDqSmem), st, a);
     return hipGetLastError();
 }
 
