@@ -159,10 +159,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     const int ti = tid >> 4, tj = tid & 15;
 
     // block -> (b, h, query block) in 32-bit unsigned arithmetic (the host
-    // checks that the grid fits)
+    // checks that the grid fits); query blocks slowest and from the last, so
+    // that the longest walks (last blocks, causal) start first
     const unsigned nqb = (unsigned)((a.S + kAQ - 1) / kAQ), hq = (unsigned)a.Hq;
-    const unsigned qb = blockIdx.x % nqb;
-    const unsigned bh = blockIdx.x / nqb;
+    const unsigned nbh = gridDim.x / nqb;
+    const unsigned qb = nqb - 1 - blockIdx.x / nbh;
+    const unsigned bh = blockIdx.x % nbh;
     const int64_t h = bh % hq;
     const int64_t b = bh / hq;
     const int64_t hk = (unsigned)h / (hq / (unsigned)a.Hkv);
@@ -486,7 +488,7 @@ struct AttnBwdArgs {
     const float* dO;
     const float* stats;
     float* dQ;
-    int64_t S, Hq, Hkv, ldq, ldk, ldv, ldo, window;
+    int64_t S, Hq, Hkv, B, ldq, ldk, ldv, ldo, window;
     float c, s_v;
     ExpConsts ek;
 };
@@ -839,9 +841,12 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+    // query blocks slowest and from the last, so that the longest walks
+    // (last blocks, causal) start first
     const unsigned nqb = (unsigned)((a.S + kAQ - 1) / kAQ), hq = (unsigned)a.Hq;
-    const unsigned qb = blockIdx.x % nqb;
-    const unsigned bh = blockIdx.x / nqb;
+    const unsigned nbh = (unsigned)(a.B * a.Hq);
+    const unsigned qb = nqb - 1 - blockIdx.x / nbh;
+    const unsigned bh = blockIdx.x % nbh;
     const int64_t h = bh % hq;
     const int64_t b = bh / hq;
     const int64_t hk = (unsigned)h / (hq / (unsigned)a.Hkv);
@@ -963,7 +968,8 @@ hipError_t launch_attn_bwd_dq(const float* Q, const float* K, const float* V, co
     if (B == 0 || S == 0) return hipSuccess;
     AttnBwdArgs a;
     a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.stats = stats; a.dQ = dQ;
-    a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.window = window;
+    a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.B = B;
+    a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.window = window;
     a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
     a.s_v = s_v;
     a.ek = ek;
