@@ -659,6 +659,77 @@ __device__ __forceinline__ void kv_phase2(const float (*T)[kKvRowT], const float
     for (int r = 0; r < 16; ++r) fx[r] += (int64_t)__builtin_rint((double)u[r] * 0x1p40);
 }
 
+// 64 rows of Q and dO (query head h) from row `row0` on, row-major into qr
+// and gr; zeros for rows past `rows`
+__device__ __forceinline__ void kv_load_qg(const float* Q, int64_t ldq, const float* dO, int64_t ldo, int64_t row0,
+                                           int64_t rows, int64_t h, float (*qr)[kKvRow], float (*gr)[kKvRow]) {
+    for (int e = threadIdx.x; e < kAQ * (kAD / 4); e += kKvThreads) {
+        const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
+        vf4 q = {0.0f, 0.0f, 0.0f, 0.0f}, g = q;
+        if (row < rows) {
+            q = *reinterpret_cast<const vf4*>(Q + (row0 + row) * ldq + h * kAD + d4);
+            g = *reinterpret_cast<const vf4*>(dO + (row0 + row) * ldo + h * kAD + d4);
+        }
+        *reinterpret_cast<vf4*>(&qr[row][d4]) = q;
+        *reinterpret_cast<vf4*>(&gr[row][d4]) = g;
+    }
+}
+
+// 64 rows of K and of q_v (KV head hk) from row `row0` on, key-major into kr
+// and vq; zeros (and q_v = 0) for rows past `rows`
+__device__ __forceinline__ void kv_load_kv(const float* K, int64_t ldk, const float* V, int64_t ldv, int64_t row0,
+                                           int64_t rows, int64_t hk, const Quantizer& qz, float (*kr)[kKvRow],
+                                           int8_t (*vq)[kKvRowQ]) {
+    for (int e = threadIdx.x; e < kAK * (kAD / 4); e += kKvThreads) {
+        const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
+        vf4 k = {0.0f, 0.0f, 0.0f, 0.0f}, v = k;
+        if (row < rows) {
+            k = *reinterpret_cast<const vf4*>(K + (row0 + row) * ldk + hk * kAD + d4);
+            v = *reinterpret_cast<const vf4*>(V + (row0 + row) * ldv + hk * kAD + d4);
+        }
+        *reinterpret_cast<vf4*>(&kr[row][d4]) = k;
+        unsigned q4 = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            bool in;
+            q4 |= (unsigned)(uint8_t)(int8_t)qz.q(v[u], &in) << (8 * u);
+        }
+        *reinterpret_cast<unsigned*>(&vq[row][d4]) = row < rows ? q4 : 0u;
+    }
+}
+
+// (m_i, l_i) from the forward's statistics and Delta_i = CanonSum_d(dO * O)
+// for 64 rows from `row0` on (query head h): four lanes per row hold the
+// d-blocks, then the pair tree through two lane swaps; rows past `rows` get
+// (0, 1, 0).  Threads 0 .. 255 (four whole waves) take part.
+__device__ __forceinline__ void kv_row_stats(const float* dO, const float* O, int64_t ldo, const float* stats,
+                                             int64_t Hq, int64_t row0, int64_t rows, int64_t h, float* rowm,
+                                             float* rowl, float* rowdelta) {
+    const int tid = threadIdx.x;
+    if (tid >= 4 * kAQ) return;
+    const int row = tid >> 2, blk = tid & 3;
+    float x = 0.0f;
+    if (row < rows) {
+        const float* go = dO + (row0 + row) * ldo + h * kAD + 32 * blk;
+        const float* o = O + (row0 + row) * ldo + h * kAD + 32 * blk;
+        x = f_mul(go[0], o[0]);
+        for (int d = 1; d < 32; ++d) x = f_add(x, f_mul(go[d], o[d]));
+    }
+    x = f_add(x, __shfl_xor(x, 1));
+    x = f_add(x, __shfl_xor(x, 2));
+    if (blk == 0) {
+        float m = 0.0f, l = 1.0f;
+        if (row < rows) {
+            const int64_t r = (row0 + row) * Hq + h;
+            m = stats[2 * r];
+            l = stats[2 * r + 1];
+        }
+        rowm[row] = m;
+        rowl[row] = l;
+        rowdelta[row] = row < rows ? x : 0.0f;
+    }
+}
+
 __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     AttnKvSmem& sm = *reinterpret_cast<AttnKvSmem*>(smem_raw);
@@ -684,22 +755,7 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a)
 
     // K rows and q_v rows of the key tile (zeros past S)
     const Quantizer qz(a.s_v);
-    for (int e = tid; e < kAK * (kAD / 4); e += kKvThreads) {
-        const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
-        vf4 k = {0.0f, 0.0f, 0.0f, 0.0f}, v = k;
-        if (row < krows) {
-            k = *reinterpret_cast<const vf4*>(a.K + (base + j0 + row) * a.ldk + hk * kAD + d4);
-            v = *reinterpret_cast<const vf4*>(a.V + (base + j0 + row) * a.ldv + hk * kAD + d4);
-        }
-        *reinterpret_cast<vf4*>(&sm.kr[row][d4]) = k;
-        unsigned q4 = 0;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            bool in;
-            q4 |= (unsigned)(uint8_t)(int8_t)qz.q(v[u], &in) << (8 * u);
-        }
-        *reinterpret_cast<unsigned*>(&sm.vq[row][d4]) = row < krows ? q4 : 0u;
-    }
+    kv_load_kv(a.K, a.ldk, a.V, a.ldv, base + j0, krows, hk, qz, sm.kr, sm.vq);
 
     // wave roles: phase 1 (logits or dP, key slab), phase 2 (d slab)
     const int p1_dp = w >> 2, p1_slab = w & 3;
@@ -714,42 +770,8 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a)
             const int64_t i0 = qt * kAQ;
             const int64_t qrows = a.S - i0 < kAQ ? a.S - i0 : kAQ;
             __syncthreads();
-            // Q and dO rows of the tile, row-major
-            for (int e = tid; e < kAQ * (kAD / 4); e += kKvThreads) {
-                const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
-                vf4 q = {0.0f, 0.0f, 0.0f, 0.0f}, g = q;
-                if (row < qrows) {
-                    q = *reinterpret_cast<const vf4*>(a.Q + (base + i0 + row) * a.ldq + h * kAD + d4);
-                    g = *reinterpret_cast<const vf4*>(a.dO + (base + i0 + row) * a.ldo + h * kAD + d4);
-                }
-                *reinterpret_cast<vf4*>(&sm.qr[row][d4]) = q;
-                *reinterpret_cast<vf4*>(&sm.gr[row][d4]) = g;
-            }
-            // row statistics; Delta = CanonSum_d(dO * O): four lanes per row
-            // hold the d-blocks, then the pair tree through two lane swaps
-            if (tid < 4 * kAQ) {
-                const int row = tid >> 2, blk = tid & 3;
-                float x = 0.0f;
-                if (row < qrows) {
-                    const float* go = a.dO + (base + i0 + row) * a.ldo + h * kAD + 32 * blk;
-                    const float* o = a.O + (base + i0 + row) * a.ldo + h * kAD + 32 * blk;
-                    x = f_mul(go[0], o[0]);
-                    for (int d = 1; d < 32; ++d) x = f_add(x, f_mul(go[d], o[d]));
-                }
-                x = f_add(x, __shfl_xor(x, 1));
-                x = f_add(x, __shfl_xor(x, 2));
-                if (blk == 0) {
-                    float m = 0.0f, l = 1.0f;
-                    if (row < qrows) {
-                        const int64_t r = (base + i0 + row) * a.Hq + h;
-                        m = a.stats[2 * r];
-                        l = a.stats[2 * r + 1];
-                    }
-                    sm.rowm[row] = m;
-                    sm.rowl[row] = l;
-                    sm.rowdelta[row] = row < qrows ? x : 0.0f;
-                }
-            }
+            kv_load_qg(a.Q, a.ldq, a.dO, a.ldo, base + i0, qrows, h, sm.qr, sm.gr);
+            kv_row_stats(a.dO, a.O, a.ldo, a.stats, a.Hq, base + i0, qrows, h, sm.rowm, sm.rowl, sm.rowdelta);
             __syncthreads();
             // phase 1: logits and dP of the 64 x 64 tile, stored key-major
             {
@@ -859,42 +881,8 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
     const int s32 = (int)a.S;
     const int win = (a.window <= 0 || a.window >= a.S) ? 0 : (int)a.window;   // 0: no window
 
-    // Q and dO rows of the block, row-major (zeros past S)
-    for (int e = tid; e < kAQ * (kAD / 4); e += kKvThreads) {
-        const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
-        vf4 q = {0.0f, 0.0f, 0.0f, 0.0f}, g = q;
-        if (row < qrows) {
-            q = *reinterpret_cast<const vf4*>(a.Q + (base + q0 + row) * a.ldq + h * kAD + d4);
-            g = *reinterpret_cast<const vf4*>(a.dO + (base + q0 + row) * a.ldo + h * kAD + d4);
-        }
-        *reinterpret_cast<vf4*>(&sm.qr[row][d4]) = q;
-        *reinterpret_cast<vf4*>(&sm.gr[row][d4]) = g;
-    }
-    // row statistics; Delta = CanonSum_d(dO * O): four lanes per row hold the
-    // d-blocks, then the pair tree through two lane swaps
-    if (tid < 4 * kAQ) {
-        const int row = tid >> 2, blk = tid & 3;
-        float x = 0.0f;
-        if (row < qrows) {
-            const float* go = a.dO + (base + q0 + row) * a.ldo + h * kAD + 32 * blk;
-            const float* o = a.O + (base + q0 + row) * a.ldo + h * kAD + 32 * blk;
-            x = f_mul(go[0], o[0]);
-            for (int d = 1; d < 32; ++d) x = f_add(x, f_mul(go[d], o[d]));
-        }
-        x = f_add(x, __shfl_xor(x, 1));
-        x = f_add(x, __shfl_xor(x, 2));
-        if (blk == 0) {
-            float m = 0.0f, l = 1.0f;
-            if (row < qrows) {
-                const int64_t r = (base + q0 + row) * a.Hq + h;
-                m = a.stats[2 * r];
-                l = a.stats[2 * r + 1];
-            }
-            sm.rowm[row] = m;
-            sm.rowl[row] = l;
-            sm.rowdelta[row] = row < qrows ? x : 0.0f;
-        }
-    }
+    kv_load_qg(a.Q, a.ldq, a.dO, a.ldo, base + q0, qrows, h, sm.qr, sm.gr);
+    kv_row_stats(a.dO, a.O, a.ldo, a.stats, a.Hq, base + q0, qrows, h, sm.rowm, sm.rowl, sm.rowdelta);
 
     const Quantizer qz(a.s_v);
     const int p1_dp = w >> 2, p1_slab = w & 3;
@@ -908,23 +896,7 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
         const int64_t j0 = kt * kAK;
         const int64_t krows = a.S - j0 < kAK ? a.S - j0 : kAK;
         __syncthreads();
-        // K rows and q_v rows of the tile (zeros past S)
-        for (int e = tid; e < kAK * (kAD / 4); e += kKvThreads) {
-            const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
-            vf4 k = {0.0f, 0.0f, 0.0f, 0.0f}, v = k;
-            if (row < krows) {
-                k = *reinterpret_cast<const vf4*>(a.K + (base + j0 + row) * a.ldk + hk * kAD + d4);
-                v = *reinterpret_cast<const vf4*>(a.V + (base + j0 + row) * a.ldv + hk * kAD + d4);
-            }
-            *reinterpret_cast<vf4*>(&sm.kr[row][d4]) = k;
-            unsigned q4 = 0;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                bool in;
-                q4 |= (unsigned)(uint8_t)(int8_t)qz.q(v[u], &in) << (8 * u);
-            }
-            *reinterpret_cast<unsigned*>(&sm.vq[row][d4]) = row < krows ? q4 : 0u;
-        }
+        kv_load_kv(a.K, a.ldk, a.V, a.ldv, base + j0, krows, hk, qz, sm.kr, sm.vq);
         __syncthreads();
         // phase 1: logits and dP of the 64 x 64 tile, stored row-major
         {
