@@ -161,6 +161,7 @@ KV_CASES = [
     (1, 333, 16, 4, 130, 0.05),
     (1, 100, 4, 4, 1, 0.05),
     (1, 190, 8, 2, 500, 0.05),        # window longer than the sequence
+    (2, 129, 8, 1, 70, 0.05),         # eight query heads per KV head
 ]
 
 
