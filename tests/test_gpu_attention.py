@@ -226,3 +226,30 @@ def test_attention_dkdv_repeat_and_zero_gradient():
     for t, w, n in ((k1, wk, "dK"), (v1, wv, "dV"), (k2, wk, "dK repeat"), (v2, wv, "dV repeat")):
         assert_bitwise(t, w, n)
     assert np.all(_bits(k0) == 0) and np.all(_bits(v0) == 0)
+
+
+def test_attention_backward_with_subnormal_inputs():
+    """1% of the entries of Q, K, V and dO at subnormal magnitudes (read as
+    zero by every binary32 operation) and some exact zeros: the forward, dQ,
+    dK and dV stay bit-identical to the oracle."""
+    B, S, Hq, Hkv, window, s_v = 1, 140, 4, 2, 60, 0.05
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=17, scale=0.3)
+    g = np.random.default_rng(18)
+    dO = (g.standard_normal((B, S, Hq, D)) * 1e-2).astype(np.float32)
+    for t in (Q, K, V, dO):
+        flat = t.reshape(-1)
+        idx = g.choice(flat.size, flat.size // 100, replace=False)
+        flat[idx] = (g.choice([-1.0, 1.0], idx.size) * g.uniform(1e-45, 1e-38, idx.size)).astype(np.float32)
+        flat[g.choice(flat.size, flat.size // 200, replace=False)] = 0.0
+    q, k, v, go = (torch.from_numpy(t).cuda() for t in (Q, K, V, dO))
+    stats = torch.empty((B, S, Hq, 2), dtype=torch.float32, device="cuda")
+    O = brl.attn_fwd(q, k, v, window, s_v, stats=stats)
+    dQ = brl.attn_bwd_dq(q, k, v, O, go, stats, window, s_v)
+    dK, dV = brl.attn_bwd_dkdv(q, k, v, O, go, stats, window, s_v)
+    torch.cuda.synchronize()
+    Oh = O.cpu().numpy()
+    assert_bitwise(Oh, oracle.attn_fwd(Q, K, V, window, s_v), "O (subnormal inputs)")
+    assert_bitwise(dQ, oracle.attn_bwd_dq(Q, K, V, Oh, dO, window, s_v), "dQ (subnormal inputs)")
+    wk, wv = oracle.attn_bwd_dkdv(Q, K, V, Oh, dO, window, s_v)
+    assert_bitwise(dK, wk, "dK (subnormal inputs)")
+    assert_bitwise(dV, wv, "dV (subnormal inputs)")
