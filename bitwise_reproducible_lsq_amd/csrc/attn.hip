@@ -16,13 +16,17 @@
 // order-free, so only the logits and l_i carry an order, and both are fixed
 // by absolute positions (d, and the key index j), not by tiles.
 //
-// One workgroup per (batch, query head, block of 64 queries); two passes over
-// the 64-key tiles that meet the rows' key ranges:
-//   pass 1: logits (VALU, 4 x 4 per thread, d-blocks of 32 summed left to
-//           right then as a pairwise tree) -> row maxima (order-free);
-//   pass 2: the same logits -> p -> the 32-key block sums, each a left-to-
-//           right chain through the 8 lanes that hold its keys (DPP shifts
-//           within a 16-lane row); a tile's two blocks are a complete pair
+// Forward: one workgroup per (batch, query head, block of 64 queries); two
+// passes over the 64-key tiles that meet the rows' key ranges:
+//   pass 1: the exact row maxima (order-free): bf16 logits on the matrix
+//           cores bound every exact logit within a proven margin; only keys
+//           that can still hold the maximum get their exact logit, in pass
+//           2's order, into an atomic maximum;
+//   pass 2: exact logits (VALU, 4 x 4 per thread, d-blocks of 32 summed left
+//           to right, then as a pairwise tree) -> p -> the 32-key block
+//           sums, each a left-to-right chain through the 8 lanes that hold
+//           its keys (DPP shifts within a 16-lane row); a tile's two blocks
+//           are a complete pair
 //           (their absolute indices are 2kt, 2kt+1), so their sum is pushed on
 //           the row's binary-counter stack of pairs at index kt; q_p and q_v
 //           staged as int8 in LDS and multiplied on v_mfma_i32_32x32x32_i8
@@ -30,6 +34,9 @@
 // Pairs before the first real one are +0 subtrees (the stack starts zeroed)
 // and merging with +0 is exact, so this is CanonSum over the whole axis.
 // LDS is kept under 80 KB so that two workgroups share a CU.
+//
+// Backward (further down): dQ, dK and dV with 64-bit fixed-point
+// accumulation, their products formed on the matrix cores.
 #include "internal.hpp"
 
 #pragma clang fp contract(off)
