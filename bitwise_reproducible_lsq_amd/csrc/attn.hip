@@ -565,18 +565,16 @@ __device__ __forceinline__ v16f_a mfma_prod(float a, float b) {
     return __builtin_amdgcn_mfma_f32_16x16x1f32(a, b, cneg, 0, 0, 0);
 }
 
-// KV_STEP(acc): the adds of a step stay at their place in the program (an
-// empty asm that takes the running sums in and out), so the next MFMA is
-// issued before them and no product waits in a register for later adds.
-#define KV_STEP(acc) __asm__ volatile("" : "+v"(acc))
 // Both phases run one product chain per wave, software-pipelined: the MFMA
-// of step s + 1 is issued before the adds of step s (a scheduling fence after
-// each step keeps that order), and the operands of the next 4 steps are read
-// while the current 4 are consumed.
+// of step s + 1 is issued before the adds of step s, and the operands of the
+// next 4 steps are read while the current 4 are consumed.  KV_STEP(acc)
+// keeps the adds of a step at their place in the program (an empty asm that
+// takes the running sums in and out); without it the compiler hoists all
+// MFMAs of a block ahead of the adds and runs out of registers.
+#define KV_STEP(acc) __asm__ volatile("" : "+v"(acc))
 
-// phase 1 of one wave: CanonSum over d of A[lane][d] * B[key][d] for 64
-// rows x 16 keys: d-blocks of 32 left to right, then (b0 + b1) + (b2 + b3);
-// B is fp32, or q_v dequantised on the fly
+// four B operands (d .. d+3) of one key row: fp32, or q_v dequantised as
+// fl(q_v * s_v)
 template <bool DQV>
 __device__ __forceinline__ vf4 kv_b4(const float* brow, const int8_t* bq, float s_v, int d) {
     vf4 bv;
@@ -590,6 +588,8 @@ __device__ __forceinline__ vf4 kv_b4(const float* brow, const int8_t* bq, float 
     return bv;
 }
 
+// phase 1 of one wave: CanonSum over d of A[lane][d] * B[key][d] for 64
+// rows x 16 keys: d-blocks of 32 left to right, then (b0 + b1) + (b2 + b3)
 template <bool DQV>
 __device__ __forceinline__ v16f_a kv_phase1(const float* arow, const float* brow, const int8_t* bq, float s_v) {
     v16f_a b01, b2, acc;
