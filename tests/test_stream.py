@@ -90,3 +90,27 @@ def test_bad_arguments():
         s.load(other.save())                                         # record of another seed
     with pytest.raises(brl.BrlError):
         s.load(b"not a record")
+
+
+def test_resume_with_a_different_rank_count():
+    """Elastic resume: four ranks each walk the global stream for two
+    batches of 8 windows and keep windows m with m mod 4 = r; their resume
+    records are byte-identical; two ranks loaded with that record continue
+    with windows m mod 2 = r of the same global stream."""
+    corpus = synth.corpus(7, 1)
+    G = 8
+    _, ref = brl.DataStream(33, synth.SEPARATOR, corpus).next(5 * G)
+    records = []
+    for r in range(4):
+        st = brl.DataStream(33, synth.SEPARATOR, corpus)
+        got = np.concatenate([st.step(G, 4, r) for _ in range(2)])
+        assert np.array_equal(got, ref[:2 * G][r::4])
+        records.append(st.save())
+        st.close()
+    assert all(rec == records[0] for rec in records)
+    for r in range(2):
+        st = brl.DataStream(33, synth.SEPARATOR, corpus)
+        st.load(records[0])
+        got = np.concatenate([st.step(G, 2, r) for _ in range(3)])
+        assert np.array_equal(got, ref[2 * G:][r::2])
+        st.close()
