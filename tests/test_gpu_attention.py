@@ -253,3 +253,25 @@ def test_attention_backward_with_subnormal_inputs():
     wk, wv = oracle.attn_bwd_dkdv(Q, K, V, Oh, dO, window, s_v)
     assert_bitwise(dK, wk, "dK (subnormal inputs)")
     assert_bitwise(dV, wv, "dV (subnormal inputs)")
+
+
+def test_attention_backward_binding_rejects_bad_outputs():
+    """The binding refuses dK/dV of the wrong shape, only one of the two, or
+    with different row strides, before anything is launched."""
+    B, S, Hq, Hkv, window, s_v = 1, 64, 4, 2, 0, 0.05
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=19)
+    q, k, v = (torch.from_numpy(t).cuda() for t in (Q, K, V))
+    stats = torch.empty((B, S, Hq, 2), dtype=torch.float32, device="cuda")
+    O = brl.attn_fwd(q, k, v, window, s_v, stats=stats)
+    go = torch.zeros_like(O)
+    with pytest.raises(ValueError):
+        brl.attn_bwd_dkdv(q, k, v, O, go, stats, window, s_v, dK=torch.empty_like(k))
+    with pytest.raises(ValueError):
+        brl.attn_bwd_dkdv(q, k, v, O, go, stats, window, s_v, dK=torch.empty_like(q), dV=torch.empty_like(q))
+    wide = torch.empty((B * S, 3 * Hkv * D), device="cuda")
+    with pytest.raises(ValueError):
+        brl.attn_bwd_dkdv(q, k, v, O, go, stats, window, s_v, dK=torch.empty_like(k),
+                          dV=wide[:, :Hkv * D].view(B, S, Hkv, D))
+    with pytest.raises(ValueError):
+        brl.attn_bwd_dkdv(q, k, v, O, go, stats[..., :1], window, s_v)
+    torch.cuda.synchronize()
