@@ -275,3 +275,27 @@ def test_attention_backward_binding_rejects_bad_outputs():
     with pytest.raises(ValueError):
         brl.attn_bwd_dkdv(q, k, v, O, go, stats[..., :1], window, s_v)
     torch.cuda.synchronize()
+
+
+def test_attention_kernels_repeat_ten_times_bit_identically():
+    """Ten runs of each attention kernel on one input agree bit for bit (the
+    forward's row maxima come from an integer atomic maximum, and the
+    gradients from exact int64 sums, so no run may differ)."""
+    B, S, Hq, Hkv, window, s_v = 2, 300, 8, 2, 100, 0.05
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=23, scale=0.5)
+    dO = (np.random.default_rng(24).standard_normal((B, S, Hq, D)) * 1e-2).astype(np.float32)
+    q, k, v, go = (torch.from_numpy(t).cuda() for t in (Q, K, V, dO))
+    first = None
+    for _ in range(10):
+        stats = torch.empty((B, S, Hq, 2), dtype=torch.float32, device="cuda")
+        O = brl.attn_fwd(q, k, v, window, s_v, stats=stats)
+        dQ = brl.attn_bwd_dq(q, k, v, O, go, stats, window, s_v)
+        dK, dV = brl.attn_bwd_dkdv(q, k, v, O, go, stats, window, s_v)
+        cur = [t.view(torch.int32).clone() for t in (O, stats, dQ, dK, dV)]
+        if first is None:
+            first = cur
+        else:
+            for name, a, b in zip(["O", "stats", "dQ", "dK", "dV"], first, cur):
+                assert torch.equal(a, b), f"{name} differs between runs"
+    torch.cuda.synchronize()
+    assert_bitwise(first[0].view(torch.float32), oracle.attn_fwd(Q, K, V, window, s_v), "O")
