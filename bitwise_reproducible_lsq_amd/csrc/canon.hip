@@ -4,11 +4,14 @@
 // first term, then a level-by-level pairwise tree over the block sums.
 //
 // Work split: pass 1 gives each workgroup an aligned run of WGB block sums and
-// reduces them to one subtree root; later passes reduce aligned runs of WGB
-// roots.  Aligned power-of-two runs are complete subtrees of the canonical
-// tree (and a short final run is the canonical tree of its own leaves), so the
-// result is independent of WGB.  The last pass also computes the scalar that
-// follows the sum (weight step, or norm and clip coefficient).
+// reduces them to one subtree root; while more than 64K roots remain, further
+// passes reduce aligned runs of WGB roots; one single-workgroup pass then
+// reduces the rest (each thread an aligned run in registers, then the
+// workgroup tree).  Aligned power-of-two runs are complete subtrees of the
+// canonical tree (and a short final run is the canonical tree of its own
+// leaves), so the result is independent of the split.  The last pass also
+// computes the scalar that follows the sum (weight step, or norm and clip
+// coefficient).
 #include "internal.hpp"
 
 #pragma clang fp contract(off)
@@ -107,6 +110,52 @@ __global__ __launch_bounds__(WGB) void canon_tree_kernel(const float* __restrict
     }
 }
 
+// Final pass in one workgroup of kTailThreads: thread t first reduces the
+// aligned run of RUN roots [t*RUN, (t+1)*RUN) in registers, level by level
+// (a complete subtree, or for the short last run the canonical tree of its
+// own leaves), then the workgroup tree combines the run roots.  One launch
+// replaces the chain of canon_tree_kernel passes once Q <= kTailThreads*RUN.
+constexpr int kTailThreads = 1024;
+constexpr int kTailMaxRun = 64;
+
+template <int RUN>
+__global__ __launch_bounds__(kTailThreads) void canon_tail_kernel(const float* __restrict__ in, int64_t Q,
+                                                                  CanonFinishArgs fin) {
+    __shared__ float lds[kTailThreads];
+    const int t = threadIdx.x;
+    const int64_t first = (int64_t)t * RUN;
+    const int64_t left = Q - first;
+    const int cnt = left <= 0 ? 0 : (left < RUN ? (int)left : RUN);
+    float v[RUN];
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) v[i] = i < cnt ? in[first + i] : 0.0f;
+#pragma unroll
+    for (int w = 1; w < RUN; w *= 2)
+#pragma unroll
+        for (int i = 0; i + w < RUN; i += 2 * w)
+            if (i + w < cnt) v[i] = f_add(v[i], v[i + w]);
+    const int runs = (int)((Q + RUN - 1) / RUN);
+    const float r = wg_pair_tree(v[0], runs, lds);
+    if (t == 0) canon_finish(r, fin);
+}
+
+static hipError_t launch_canon_tail(const float* in, int64_t Q, const CanonFinishArgs& fin, hipStream_t st) {
+    int run = 1;
+    while ((int64_t)run * kTailThreads < Q) run *= 2;
+    const dim3 g(1), b(kTailThreads);
+    switch (run) {
+        case 1: hipLaunchKernelGGL(canon_tail_kernel<1>, g, b, 0, st, in, Q, fin); break;
+        case 2: hipLaunchKernelGGL(canon_tail_kernel<2>, g, b, 0, st, in, Q, fin); break;
+        case 4: hipLaunchKernelGGL(canon_tail_kernel<4>, g, b, 0, st, in, Q, fin); break;
+        case 8: hipLaunchKernelGGL(canon_tail_kernel<8>, g, b, 0, st, in, Q, fin); break;
+        case 16: hipLaunchKernelGGL(canon_tail_kernel<16>, g, b, 0, st, in, Q, fin); break;
+        case 32: hipLaunchKernelGGL(canon_tail_kernel<32>, g, b, 0, st, in, Q, fin); break;
+        case 64: hipLaunchKernelGGL(canon_tail_kernel<64>, g, b, 0, st, in, Q, fin); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 int64_t canon_partials(int64_t n) {
     const int64_t wgb = 64;   // smallest allowed WGB gives the largest count
     int64_t J = ceil_div(n, kBlock);
@@ -130,15 +179,15 @@ static hipError_t canon_run(int map, const float* x, int64_t n, float* partials,
                            x, n, partials, last, fin);
     float* in = partials;
     float* out = partials + q + 1;
-    while (q > 1) {
+    while (q > (int64_t)kTailThreads * kTailMaxRun) {
         int64_t nq = ceil_div(q, WGB);
-        last = nq == 1;
         hipLaunchKernelGGL((canon_tree_kernel<WGB>), dim3((unsigned)nq), dim3(WGB), 0, st,
-                           in, q, out, last, fin);
+                           in, q, out, 0, fin);
         in = out;
         out = out + nq + 1;
         q = nq;
     }
+    if (q > 1) return launch_canon_tail(in, q, fin, st);
     return hipGetLastError();
 }
 

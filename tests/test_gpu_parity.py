@@ -443,6 +443,24 @@ def test_norm_reduce_wg_invariance():
         brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, old)
 
 
+@pytest.mark.parametrize("n, wg", [
+    (64 * 32 * 10001 + 3, 64),       # 10002 roots: runs of 16, last run of 2
+    (2**26 + 5, 64),                 # 32769 roots: runs of 64, last run of 1
+    (2**27 + 12345, 64),             # 65543 roots: one 64-wide pass, then 1025 roots in runs of 2
+])
+def test_norm_tail_runs(n, wg):
+    """The last CanonSum pass reduces aligned runs of roots per thread before
+    the workgroup tree; run lengths and ragged last runs leave the bits alone."""
+    g = np.random.default_rng(n).standard_normal(n, dtype=np.float32)
+    wnu = oracle.l2norm(g)
+    old = brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, wg)
+    try:
+        nu = brl.grad_l2norm_clip(_cuda(g), 1e30)
+        assert_bitwise(nu, np.array([wnu]), f"nu n={n} wg={wg}")
+    finally:
+        brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, old)
+
+
 def test_replay_stream_shape_invariance():
     """The number of 16-byte vectors per thread in the streaming kernels
     changes only the launch shape."""
