@@ -148,9 +148,11 @@ hipError_t launch_dequant(const float* v, int64_t rows, int64_t cols, const floa
 // staging registers; per-lane offsets fixed for the whole loop, the k offset
 // in a scalar register) through a ring of kStages LDS stages, so loads run
 // kStages-1 tiles ahead of the MFMAs.  LDS rows are 64 bytes, unpadded; the
-// four 16-byte chunks of row r are stored XOR-swizzled by (r >> 1) & 3, which
-// puts the 16-byte fragment reads of 8 consecutive rows in 8 distinct bank
-// groups.
+// four 16-byte chunks of row r are stored XOR-swizzled by (r >> 2) & 3.  The
+// LDS serves a 16-byte-per-lane read 16 lanes per clock across its 64 banks;
+// the swizzle puts the fragment reads of 16 consecutive rows (4 rows per
+// 256-byte bank window, 4 distinct chunk slots each) on 16 distinct 16-byte
+// bank groups, so the reads are conflict-free.
 //
 // Schedule: with one wave per SIMD, any instruction that stalls the wave
 // idles its matrix core, so every k-step issues its 16 MFMAs with the
@@ -175,7 +177,7 @@ struct GemmCfg {
     static constexpr int kLoads = kLoadsA + kLoadsB;                // per wave per stage
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
 // 16 bytes per lane from base[off + soff] (a raw buffer over `bytes` bytes;
 // reads past the end return zero) into LDS at lds + 16 * lane
