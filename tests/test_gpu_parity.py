@@ -444,13 +444,16 @@ def test_norm_reduce_wg_invariance():
 
 
 @pytest.mark.parametrize("n, wg", [
-    (64 * 32 * 10001 + 3, 64),       # 10002 roots: runs of 16, last run of 2
-    (2**26 + 5, 64),                 # 32769 roots: runs of 64, last run of 1
-    (2**27 + 12345, 64),             # 65543 roots: one 64-wide pass, then 1025 roots in runs of 2
+    (64 * 32 * 2401 + 35, 64),       # 2402 roots: one tail pass, runs of 4, last run of 2
+    (64 * 32 * 10001 + 3, 64),       # 10002 roots: a 64-wide pass (157 roots), then the tail
+    (2**26 + 5, 64),                 # 32769 roots: a 64-wide pass (513 roots), then the tail
+    (2**27 + 12345, 64),             # 65543 roots: a 64-wide pass, then 1025 roots in runs of 2
 ])
 def test_norm_tail_runs(n, wg):
     """The last CanonSum pass reduces aligned runs of roots per thread before
-    the workgroup tree; run lengths and ragged last runs leave the bits alone."""
+    the workgroup tree, after as many coalesced passes as the root count
+    needs; run lengths, ragged last runs and the number of passes leave the
+    bits alone."""
     g = np.random.default_rng(n).standard_normal(n, dtype=np.float32)
     wnu = oracle.l2norm(g)
     old = brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, wg)
