@@ -85,7 +85,7 @@ struct AttnSmem {
 };
 static_assert(sizeof(AttnSmem) <= 81920, "two workgroups per CU");
 
-__device__ __forceinline__ int aswz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+__device__ __forceinline__ int aswz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
 // CanonSum over d of A[d][4ti + x] * B[d][4tj + y] for this thread's 4 x 4
 // outputs: d-blocks of 32 summed left to right, then (b0 + b1) + (b2 + b3)
