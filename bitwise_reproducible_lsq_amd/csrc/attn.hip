@@ -462,12 +462,11 @@ hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64
     a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
     a.s_v = s_v;
     a.ek = ek;
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnSmem));
-        attr = true;
-    }
+    // the limit is set on every call: it is per device, and the call is cheap
+    if (const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnSmem));
+        e != hipSuccess)
+        return e;
     const int64_t blocks = B * Hq * ceil_div(S, kAQ);
     if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)blocks), dim3(256), sizeof(AttnSmem), st, a);
@@ -836,12 +835,11 @@ hipError_t launch_attn_bwd_dkdv(const float* Q, const float* K, const float* V, 
     a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
     a.s_v = s_v;
     a.ek = ek;
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnKvSmem));
-        attr = true;
-    }
+    // the limit is set on every call: it is per device, and the call is cheap
+    if (const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnKvSmem));
+        e != hipSuccess)
+        return e;
     const int64_t blocks = B * Hkv * ceil_div(S, kAK);
     if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)blocks), dim3(kKvThreads), sizeof(AttnKvSmem), st, a);
@@ -952,12 +950,11 @@ hipError_t launch_attn_bwd_dq(const float* Q, const float* K, const float* V, co
     a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
     a.s_v = s_v;
     a.ek = ek;
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnDqSmem));
-        attr = true;
-    }
+    // the limit is set on every call: it is per device, and the call is cheap
+    if (const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnDqSmem));
+        e != hipSuccess)
+        return e;
     const int64_t blocks = B * Hq * ceil_div(S, kAQ);
     if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)blocks), dim3(kKvThreads), sizeof(AttnDqSmem), st, a);

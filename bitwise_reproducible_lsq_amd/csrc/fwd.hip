@@ -379,12 +379,11 @@ static hipError_t launch_gemm_epi(const GemmArgs& a, hipStream_t st) {
     const size_t lds = (size_t)kStages * C::kStage;
     // operand panels are addressed through 32-bit buffer offsets
     if ((int64_t)(BM > BN ? BM : BN) * a.Kp > INT32_MAX) return hipErrorInvalidValue;
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_i8_kernel<BM, BN, WM, WN, EPI>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        attr = true;
-    }
+    // the limit is set on every call: it is per device, and the call is cheap
+    if (const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_i8_kernel<BM, BN, WM, WN, EPI>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        e != hipSuccess)
+        return e;
     const int64_t tiles = (a.Mp / BM) * (a.Nvp / BN);
     hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM, WN, EPI>), dim3((unsigned)tiles), dim3(C::kThreads), lds,
                        st, a);

@@ -221,10 +221,11 @@ static uint64_t isqrt(unsigned __int128 x) {       // floor(square root of x)
     return r;
 }
 
+// Built once, on first use; a function-local static's initialisation is
+// thread-safe, so concurrent first calls see the complete table.
 static const ShaConsts& sha_consts() {
-    static ShaConsts c;
-    static bool ready = false;
-    if (!ready) {
+    static const ShaConsts c = [] {
+        ShaConsts t{};
         int primes[64], np = 0;
         for (int v = 2; np < 64; ++v) {
             bool prime = true;
@@ -233,11 +234,11 @@ static const ShaConsts& sha_consts() {
             if (prime) primes[np++] = v;
         }
         for (int i = 0; i < 64; ++i)   // first 32 fractional bits of cbrt(p): floor(cbrt(p * 2^96)) mod 2^32
-            c.k[i] = (uint32_t)icbrt((unsigned __int128)primes[i] << 96);
+            t.k[i] = (uint32_t)icbrt((unsigned __int128)primes[i] << 96);
         for (int i = 0; i < 8; ++i)    // first 32 fractional bits of sqrt(p): floor(sqrt(p * 2^64)) mod 2^32
-            c.h0[i] = (uint32_t)isqrt((unsigned __int128)primes[i] << 64);
-        ready = true;
-    }
+            t.h0[i] = (uint32_t)isqrt((unsigned __int128)primes[i] << 64);
+        return t;
+    }();
     return c;
 }
 

@@ -93,12 +93,10 @@ hipError_t launch_philox_u32(uint64_t key, uint32_t stream, uint64_t first, int6
 
 // ---- host SHA-256 (for source names and key derivation) -----------------------------
 static void sha256_host(const uint8_t* msg, size_t n, uint8_t out[32]) {
-    static uint32_t K[64], H0[8];
-    static bool ready = false;
-    if (!ready) {
-        sha256_constants(K, H0);
-        ready = true;
-    }
+    struct Tables { uint32_t K[64], H0[8]; };
+    static const Tables tab = [] { Tables t; sha256_constants(t.K, t.H0); return t; }();   // thread-safe init
+    const uint32_t* K = tab.K;
+    const uint32_t* H0 = tab.H0;
     auto rotr = [](uint32_t x, int r) { return (x >> r) | (x << (32 - r)); };
     uint32_t h[8];
     memcpy(h, H0, sizeof(h));
