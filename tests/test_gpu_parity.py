@@ -272,6 +272,41 @@ def test_bwd_matrix_core_ragged_reductions(M, K, N):
         assert_bitwise(dW, wW, "dW (unaligned dY)")
 
 
+def test_bwd_finish_alignment_paths():
+    """The chunk-root finish reads the mask source and writes the output as
+    16-byte vectors only when both are 16-byte aligned; tensors at 4-byte but
+    not 16-byte aligned addresses take its per-element path.  Both give the
+    oracle's bits, also when dW accumulates (dW + dW = 2 dW exactly, the
+    oracle's outputs being normal numbers or zeros)."""
+    M, K, N = 300, 72, 200
+    inp = _case_inputs(M, K, N, seed=77, sub=0.01)
+    wX, wW = oracle.linear_bwd(inp.dY, inp.X, inp.W, synth.S_X)
+
+    def odd(a):
+        flat = torch.empty(a.size + 1, dtype=torch.float32, device="cuda")
+        t = flat[1:].view(*a.shape)
+        t.copy_(_cuda(a))
+        assert t.data_ptr() % 16 != 0
+        return t
+
+    dY = _cuda(inp.dY)
+    cases = [("aligned", _cuda(inp.X), _cuda(inp.W), False),
+             ("mask sources unaligned", odd(inp.X), odd(inp.W), False),
+             ("outputs unaligned", _cuda(inp.X), _cuda(inp.W), True)]
+    with tuning(brl.TUNE_BWD_CHUNK_LOG2, 1):     # several chunk roots per output at this size
+        for what, X, W, odd_out in cases:
+            if odd_out:
+                dX, dW = odd(np.zeros((M, K), np.float32)), odd(np.zeros((N, K), np.float32))
+            else:
+                dX = torch.empty((M, K), dtype=torch.float32, device="cuda")
+                dW = torch.empty((N, K), dtype=torch.float32, device="cuda")
+            brl.qat_linear_bwd(dY, X, W, synth.S_X, dX=dX, dW=dW)
+            assert_bitwise(dX, wX, f"dX ({what})")
+            assert_bitwise(dW, wW, f"dW ({what})")
+            brl.qat_linear_bwd(dY, X, W, synth.S_X, need_dX=False, dW=dW, dW_accumulate=True)
+            assert_bitwise(dW, np.float32(2) * wW, f"dW accumulated ({what})")
+
+
 def test_bwd_tiny_workload():
     inp = synth.linear_inputs(synth.CASES["tiny"])
     dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), _cuda(inp.X), _cuda(inp.W), synth.S_X)
