@@ -98,6 +98,41 @@ def test_block_sum_is_sequential_from_first_term():
         assert _bits(got) == _bits(want), (c["name"], got, want)
 
 
+def _block_sums(p, width=32):
+    b = []
+    for j in range(0, len(p), width):
+        s = p[j]
+        for x in p[j + 1: j + width]:
+            s = np.float32(s + x)
+        b.append(s)
+    return b
+
+
+def test_golden_alternatives_differ():
+    """Cases that list the values of other orders must be separated by them:
+    the midpoint split and the plain sequential sum are recomputed here in
+    host binary32 and give the stated, different bits."""
+    case = json.load(open(os.path.join(GOLDEN, "canon_sum_cases.json")))
+    checked = 0
+    for c in case["cases"]:
+        alt = c.get("alternatives")
+        if not alt:
+            continue
+        p = np.array(c["input"], np.float32)
+        want = np.float32(c["expect"])
+        b = _block_sums(p)
+        got = {"midpoint": eval_tree(tree_midpoint(0, len(b)), b)}
+        seq = p[0]
+        for x in p[1:]:
+            seq = np.float32(seq + x)
+        got["sequential"] = seq
+        for name, v in alt.items():
+            assert _bits(got[name]) == _bits(np.float32(v)), (c["name"], name, got[name])
+            assert _bits(got[name]) != _bits(want), (c["name"], name)
+            checked += 1
+    assert checked >= 1
+
+
 def test_exact_sums():
     g = np.random.default_rng(0)
     for n in (1, 5, 31, 32, 33, 64, 95, 96, 97, 1000, 3000):
