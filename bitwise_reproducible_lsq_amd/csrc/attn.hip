@@ -72,8 +72,8 @@ struct AttnSmem {
         } pv;
         struct {
             double nq[kAQ];         // pass 1: Euclidean norms of the Q rows (rounded up)
-            float hmax[2][kAQ];     // pass 1: approximate row maxima of the tile's key halves
-            float arun[kAQ];        // pass 1: running approximate row maxima
+            float hmax[2][kAQ];     // pass 1: largest lower bounds a - E of the tile's key halves
+            float lbound[kAQ];      // pass 1: running lower bound L_i of the row maximum
             double nkp[4][kAK];     // pass 1: partial squared norms of the K rows
             int ncand;              // pass 1: candidates of the tile
             uint16_t cand[kAQ * kAK];   // pass 1: (row << 6) | key
@@ -198,12 +198,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     // |q_i| |k_j| + 2^-80 (bf16 operands: 2^-7 relative each; fp32 sums of
     // 128 terms in any order: gamma_128; the canonical sum: gamma_35;
     // Cauchy-Schwarz for sum |q_d k_d|; products flushed below 2^-126 in
-    // either sum: under 2^-119 in all).  Norms and bound are formed in
-    // binary64, where no square of a binary32 value under- or overflows.  With A the largest a over the row's keys seen so
-    // far, a key whose a_ij < A - 2E_ij cannot hold the row's maximum, so the
-    // exact logit is computed (in the canonical order of pass 2) only for the
-    // others, and m_i is the largest of those.  A only grows, so the test
-    // against the running value keeps every key the final value would.
+    // either sum: under 2^-119 in all; about twice the worst case).  Norms
+    // and bound are formed in binary64, where no square of a binary32 value
+    // under- or overflows.  So s_ij lies in [a_ij - E_ij, a_ij + E_ij], and
+    // the row maximum m_i is at least L_i = max over the row's keys of
+    // (a_il - E_il).  A key with a_ij + E_ij < L_i is below m_i and cannot
+    // hold it; every other key is a candidate whose exact logit is computed
+    // (in the canonical order of pass 2) into an order-free maximum.  L_i is
+    // kept as a running value over the tiles seen so far (rounded down to
+    // binary32), which is at most the final one, so the test against it keeps
+    // every key the final value would.
     const int wmt = wave & 1, wnt = wave >> 1;     // this wave's 32 x 32 sub-tile of the 64 x 64 tile
     typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
     typedef float v16f_a __attribute__((ext_vector_type(16)));
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         double n2 = 0.0;
         for (int d = 0; d < kAD; ++d) n2 += (double)sm.qs[d][tid] * (double)sm.qs[d][tid];
         sm.u.p1.nq[tid] = __builtin_sqrt(n2) * (1.0 + 0x1p-30);
-        sm.u.p1.arun[tid] = __int_as_float(0xff800000);
+        sm.u.p1.lbound[tid] = __int_as_float(0xff800000);
         // order-preserving integer image of -inf (negative floats: bits ^ 0x7fffffff)
         reinterpret_cast<int*>(sm.rowmax)[tid] = (int)(0xff800000u ^ 0x7fffffffu);
     }
@@ -246,14 +250,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         }
         // element r of this lane: row wmt*32 + 8(r>>2) + 4(lane>>5) + (r&3), key wnt*32 + (lane&31)
         const int jl = wnt * 32 + (lane & 31);
+        const double nk = __builtin_sqrt((sm.u.p1.nkp[0][jl] + sm.u.p1.nkp[1][jl]) +
+                                         (sm.u.p1.nkp[2][jl] + sm.u.p1.nkp[3][jl])) * (1.0 + 0x1p-30);
         float hm[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int il = wmt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             ap[r] = f_mul(ap[r], a.c);
-            hm[r] = allowed(q0 + il, j0 + jl) ? ap[r] : __int_as_float(0xff800000);
+            // a - E in binary64, moved down by more than one binary32
+            // rounding before it is rounded, so the binary32 value is a lower
+            // bound too; no bound from a key whose a or E is not finite
+            const double lb = (double)ap[r] - (ebound * sm.u.p1.nq[il] * nk + 0x1p-80);
+            const float lf = (float)(lb - __builtin_fabs(lb) * 0x1p-23 - 0x1p-125);
+            const bool usable = allowed(q0 + il, j0 + jl) && __builtin_isfinite(lb);
+            hm[r] = usable ? lf : __int_as_float(0xff800000);
         }
-        // row maxima over the 32 keys of the half (lanes with equal lane >> 5)
+        // largest lower bound over the 32 keys of the half (lanes with equal lane >> 5)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
 #pragma unroll
@@ -267,23 +279,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         }
         __syncthreads();
         if (tid < kAQ) {
-            float m = sm.u.p1.arun[tid];
+            float m = sm.u.p1.lbound[tid];
             m = sm.u.p1.hmax[0][tid] > m ? sm.u.p1.hmax[0][tid] : m;
             m = sm.u.p1.hmax[1][tid] > m ? sm.u.p1.hmax[1][tid] : m;
-            sm.u.p1.arun[tid] = m;
+            sm.u.p1.lbound[tid] = m;
         }
         __syncthreads();
-        // candidates: listed, then their exact logits (pass 2's order) taken
-        // one per thread into an order-free maximum
+        // candidates (a + E >= L, or not comparable): listed, then their exact
+        // logits (pass 2's order) taken one per thread into an order-free maximum
         {
-            const double nk = __builtin_sqrt((sm.u.p1.nkp[0][jl] + sm.u.p1.nkp[1][jl]) +
-                                             (sm.u.p1.nkp[2][jl] + sm.u.p1.nkp[3][jl])) * (1.0 + 0x1p-30);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int il = wmt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (!allowed(q0 + il, j0 + jl)) continue;
-                const double e2 = 2.0 * (ebound * sm.u.p1.nq[il] * nk + 0x1p-80);
-                if ((double)ap[r] >= (double)sm.u.p1.arun[il] - e2)
+                const double e = ebound * sm.u.p1.nq[il] * nk + 0x1p-80;
+                if (!((double)ap[r] + e < (double)sm.u.p1.lbound[il]))
                     sm.u.p1.cand[atomicAdd(&sm.u.p1.ncand, 1)] = (uint16_t)((il << 6) | jl);
             }
         }

@@ -299,3 +299,94 @@ def test_attention_kernels_repeat_ten_times_bit_identically():
                 assert torch.equal(a, b), f"{name} differs between runs"
     torch.cuda.synchronize()
     assert_bitwise(first[0].view(torch.float32), oracle.attn_fwd(Q, K, V, window, s_v), "O")
+
+
+# ---- keys of unequal norm: the first pass must keep the true row maximum ----
+def _witness_inputs(S=160):
+    """Every query is all ones.  Keys 5, 40 and 70 are the high-norm key l
+    (bf16 operands 64(1+2^-7) and -64: approximate logit 2.83, exact 0.011,
+    bound 11.4); keys 7, 30 and 60 are 0.125 everywhere (exact logit 1.414,
+    the rows' maximum, bound 0.022); the other keys are small.  Pairs sit in
+    one key tile, in the other order, and across a tile boundary."""
+    g = np.random.default_rng(77)
+    Q = np.ones((1, S, 1, D), np.float32)
+    K = (g.standard_normal((1, S, 1, D)) * 1e-3).astype(np.float32)
+    hi = np.float32(64.0 * (1 + 2.0 ** -8 + 2.0 ** -16))
+    lo = np.float32(-64.0 * (1 + 2.0 ** -8 - 2.0 ** -16))
+    kl = np.where(np.arange(D) % 2 == 0, hi, lo).astype(np.float32)
+    for j in (5, 40, 70):
+        K[0, j, 0] = kl
+    for j in (7, 30, 60):
+        K[0, j, 0] = 0.125
+    V = g.standard_normal((1, S, 1, D)).astype(np.float32)
+    dO = (g.standard_normal((1, S, 1, D)) * 1e-2).astype(np.float32)
+    return Q, K, V, dO
+
+
+def _full_check(Q, K, V, dO, window, s_v, what, O_bwd=None):
+    """Forward (O and its statistics) and the three gradients against the
+    oracle; the gradients take the forward's O, or O_bwd when given."""
+    q, k, v = (torch.from_numpy(t).cuda() for t in (Q, K, V))
+    B, S, Hq, _ = Q.shape
+    stats = torch.empty((B, S, Hq, 2), dtype=torch.float32, device="cuda")
+    O = brl.attn_fwd(q, k, v, window, s_v, stats=stats)
+    g = torch.from_numpy(dO).cuda()
+    Ob = O if O_bwd is None else torch.from_numpy(O_bwd).cuda()
+    dQ = brl.attn_bwd_dq(q, k, v, Ob, g, stats, window, s_v)
+    dK, dV = brl.attn_bwd_dkdv(q, k, v, Ob, g, stats, window, s_v)
+    torch.cuda.synchronize()
+    assert_bitwise(O, oracle.attn_fwd(Q, K, V, window, s_v), f"O ({what})")
+    Oh = Ob.cpu().numpy()
+    assert_bitwise(dQ, oracle.attn_bwd_dq(Q, K, V, Oh, dO, window, s_v), f"dQ ({what})")
+    wk, wv = oracle.attn_bwd_dkdv(Q, K, V, Oh, dO, window, s_v)
+    assert_bitwise(dK, wk, f"dK ({what})")
+    assert_bitwise(dV, wv, f"dV ({what})")
+    return stats.cpu().numpy()
+
+
+@pytest.mark.parametrize("window", [0, 64])
+def test_attention_keys_of_unequal_norm_witness(window):
+    """O, (m, l), dQ, dK and dV on the witness row: m_i is the exact logit of
+    the 0.125 key (16 c) for every row that attends one, never the larger
+    approximate logit's key."""
+    Q, K, V, dO = _witness_inputs()
+    st = _full_check(Q, K, V, dO, window, 0.05, f"witness w={window}")
+    c = np.float32(np.float32(1.0) / np.sqrt(np.float32(D)))
+    m_j = np.float32(np.float32(16.0) * c)      # 128 products 0.125 summed exactly, times c
+    for i in range(Q.shape[1]):
+        lo = max(0, i - window + 1) if window > 0 else 0
+        if any(lo <= j <= i for j in (7, 30, 60)):
+            assert _bits(st[0, i, 0, 0]) == _bits(m_j), (i, st[0, i, 0, 0])
+
+
+@pytest.mark.parametrize("window", [0, 64])
+def test_attention_keys_with_spread_norms(window):
+    """Per-key norms spread over 1e-2 .. 1e2 within every row, GQA 4/2."""
+    g = np.random.default_rng(300 + window)
+    B, S, Hq, Hkv, s_v = 1, 200, 4, 2, 0.05
+    Q = (g.standard_normal((B, S, Hq, D)) * 0.3).astype(np.float32)
+    K = (g.standard_normal((B, S, Hkv, D)) * 10.0 ** g.uniform(-2, 2, (B, S, Hkv, 1))).astype(np.float32)
+    V = g.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    dO = (g.standard_normal((B, S, Hq, D)) * 1e-2).astype(np.float32)
+    _full_check(Q, K, V, dO, window, s_v, f"spread norms w={window}")
+
+
+def test_attention_fixed_point_ties_on_device():
+    """The crafted inputs of the CPU pins of the fixed-point format (tile sums
+    at exact ties of the 2^-40 grid, terms in both 32-halves of a 64-tile and
+    on both sides of position 64), with the pins' O = 0 given to the
+    gradients: the kernels give the oracle's bits."""
+    from tests.test_oracle_order_pins import _case_a, WIN
+    Q, K, V, O, dO, _, _ = _case_a()
+    _full_check(Q, K, V, dO, WIN, 1.0, "fixed-point ties, Q = 0", O_bwd=O)
+    # the same with K = 0 and Q carrying the terms (the dK pin's layout)
+    Q2 = np.zeros_like(Q)
+    Q2[0, 63, 0, 1] = Q2[0, 64, 0, 1] = np.float32(2.0 ** -35)
+    Q2[0, 80, 0, 2] = Q2[0, 100, 0, 2] = np.float32(2.0 ** -35)
+    Q2[0, 64, 0, 3] = np.float32(3 * 2.0 ** -35)
+    dO2 = np.zeros_like(dO)
+    for i in (63, 64, 80, 100):
+        dO2[0, i, 0, 0] = 1.0
+    V2 = np.zeros_like(V)
+    V2[0, 40, 0, 0] = V2[0, 64, 0, 0] = 1.0
+    _full_check(Q2, np.zeros_like(K), V2, dO2, WIN, 1.0, "fixed-point ties, K = 0", O_bwd=np.zeros_like(O))
