@@ -24,7 +24,6 @@ LIB_PATH = os.path.join(_HERE, "libbrlsq.so")
 BRL_OK, BRL_EINVAL, BRL_ESHAPE, BRL_EORDER, BRL_EDEVICE, BRL_EWORKSPACE = 0, -1, -2, -3, -4, -5
 EPILOGUE_NONE, EPILOGUE_SWIGLU = 0, 1
 OP_FWD, OP_BWD, OP_NORM, OP_HASH = 0, 1, 2, 3
-TUNE_BWD_CHUNK_LOG2, TUNE_REDUCE_WG_BLOCKS, TUNE_STREAM_VEC, TUNE_BWD_ENGINE = 0, 1, 2, 3
 MAX_REPLICAS = 64
 
 PROBE_OPS = {"add": 0, "sub": 1, "mul": 2, "div": 3, "sqrt": 4, "i2f": 5, "rne": 6, "exp": 7, "mfma_mul": 8}
@@ -36,10 +35,17 @@ class BrlError(RuntimeError):
         self.status = status
 
 
+class Tuning(C.Structure):
+    """Launch shapes of one call (brl_tuning): they never change results.
+    Zero fields select the defaults."""
+    _fields_ = [("bwd_chunk_log2", C.c_int32), ("reduce_wg_blocks", C.c_int32), ("stream_vec", C.c_int32),
+                ("bwd_engine", C.c_int32)]
+
+
 class ReduceStateC(C.Structure):
     _fields_ = [("replicas", C.c_int32), ("shards", C.c_int32), ("len", C.c_int64),
                 ("next", C.c_int32), ("flags", C.c_uint32), ("pending", C.c_void_p),
-                ("acc", C.c_void_p * MAX_REPLICAS)]
+                ("acc", C.c_void_p * MAX_REPLICAS), ("tune", Tuning)]
 
 
 REDUCE_PARTIALS_PERSIST = 1
@@ -49,12 +55,12 @@ _lib = None
 P, i64, i32, f32, sz = C.c_void_p, C.c_int64, C.c_int32, C.c_float, C.c_size_t
 
 _SIGS = {
-    "brl_workspace_bytes": (sz, [i32, i64, i64, i64]),
-    "qat_linear_fwd": (i32, [P, P, i64, i64, i64, f32, P, i32, P, P, P, P, sz, P]),
-    "qat_linear_bwd": (i32, [P, P, P, P, i64, i64, i64, f32, i32, P, P, i32, P, sz, P]),
+    "brl_workspace_bytes": (sz, [i32, i64, i64, i64, P]),
+    "qat_linear_fwd": (i32, [P, P, i64, i64, i64, f32, P, i32, P, P, P, P, sz, P, P]),
+    "qat_linear_bwd": (i32, [P, P, P, P, i64, i64, i64, f32, i32, P, P, i32, P, sz, P, P]),
     "brl_reduce_init": (i32, [C.POINTER(ReduceStateC), i32, i32, i64, P]),
     "ordered_reduce": (i32, [C.POINTER(ReduceStateC), P, P, P]),
-    "grad_l2norm_clip": (i32, [P, i64, f32, f32, P, P, sz, P]),
+    "grad_l2norm_clip": (i32, [P, i64, f32, f32, P, P, sz, P, P]),
     "brl_probe_f32": (i32, [i32, P, P, P, i64, P]),
     "brl_state_hash": (i32, [P, P, i32, P, P, sz, P]),
     "brl_adamw_scalars_for_step": (i32, [i64, C.c_double, P, P]),
@@ -71,7 +77,6 @@ _SIGS = {
     "brl_stream_save": (i32, [P, P, i64]),
     "brl_stream_load": (i32, [P, P, i64]),
     "brl_philox_u32": (i32, [C.c_uint64, C.c_uint32, C.c_uint64, i64, P, P]),
-    "brl_set_tuning": (i64, [i32, i64]),
     "brl_status_string": (C.c_char_p, [i32]),
     "brl_last_error": (C.c_char_p, []),
 }
@@ -120,30 +125,30 @@ def _stream(stream=None):
     return C.c_void_p(s.cuda_stream)
 
 
-_ws_cache: dict = {}
+def _tune(tune: Optional[Tuning]):
+    return C.byref(tune) if tune is not None else None
 
 
-def workspace(op: int, M: int, K: int, N: int, device) -> torch.Tensor:
-    """Workspace for one call (cached per device; grows as needed)."""
-    n = int(lib().brl_workspace_bytes(op, M, K, N))
+def workspace(op: int, M: int, K: int, N: int, device, tune: Optional[Tuning] = None, stream=None) -> torch.Tensor:
+    """A fresh workspace for one call from torch's caching allocator.  Memory
+    is reused only in the order of the stream it is used on: a workspace for
+    a stream other than the current one is recorded on that stream."""
+    n = int(lib().brl_workspace_bytes(op, M, K, N, _tune(tune)))
     if n == 0:
         raise BrlError(BRL_ESHAPE, f"no workspace size for op={op} M={M} K={K} N={N}")
-    dev = torch.device(device)
-    key = (dev.type, dev.index, op)
-    w = _ws_cache.get(key)
-    if w is None or w.numel() < n:
-        w = torch.empty(n, dtype=torch.uint8, device=dev)
-        _ws_cache[key] = w
+    w = torch.empty(n, dtype=torch.uint8, device=torch.device(device))
+    if stream is not None and stream != torch.cuda.current_stream(w.device):
+        w.record_stream(stream)
     return w
 
 
-def workspace_bytes(op: int, M: int, K: int, N: int) -> int:
-    return int(lib().brl_workspace_bytes(op, M, K, N))
+def workspace_bytes(op: int, M: int, K: int, N: int, tune: Optional[Tuning] = None) -> int:
+    return int(lib().brl_workspace_bytes(op, M, K, N, _tune(tune)))
 
 
 def qat_linear_fwd(X: torch.Tensor, W: torch.Tensor, s_x: float, addend: Optional[torch.Tensor] = None,
                    epilogue: int = EPILOGUE_NONE, want_ypre: bool = True, Y: Optional[torch.Tensor] = None,
-                   ws: Optional[torch.Tensor] = None, stream=None):
+                   ws: Optional[torch.Tensor] = None, stream=None, tune: Optional[Tuning] = None):
     """Y = dequant(int8 GEMM) (+ addend), or the SwiGLU activation.
     Returns (Y, Ypre or None, s_w as a 1-element device tensor)."""
     _f32(X, "X"), _f32(W, "W")
@@ -159,9 +164,9 @@ def qat_linear_fwd(X: torch.Tensor, W: torch.Tensor, s_x: float, addend: Optiona
         Ypre = torch.empty((M, N), dtype=torch.float32, device=X.device)
     s_w = torch.empty(1, dtype=torch.float32, device=X.device)
     if ws is None:
-        ws = workspace(OP_FWD, M, K, N, X.device)
+        ws = workspace(OP_FWD, M, K, N, X.device, tune, stream)
     st = lib().qat_linear_fwd(_ptr(X), _ptr(W), M, K, N, float(s_x), _ptr(addend), epilogue, _ptr(Y),
-                              _ptr(Ypre), _ptr(s_w), _ptr(ws), ws.numel(), _stream(stream))
+                              _ptr(Ypre), _ptr(s_w), _ptr(ws), ws.numel(), _tune(tune), _stream(stream))
     _check(st)
     return Y, Ypre, s_w
 
@@ -170,7 +175,7 @@ def qat_linear_bwd(dOut: torch.Tensor, X: torch.Tensor, W: torch.Tensor, s_x: fl
                    Ypre: Optional[torch.Tensor] = None, epilogue: int = EPILOGUE_NONE,
                    need_dX: bool = True, need_dW: bool = True, dW: Optional[torch.Tensor] = None,
                    dW_accumulate: bool = False, dX: Optional[torch.Tensor] = None,
-                   ws: Optional[torch.Tensor] = None, stream=None):
+                   ws: Optional[torch.Tensor] = None, stream=None, tune: Optional[Tuning] = None):
     """Straight-through backward; returns (dX or None, dW or None)."""
     M, K = X.shape
     N = W.shape[0]
@@ -185,10 +190,10 @@ def qat_linear_bwd(dOut: torch.Tensor, X: torch.Tensor, W: torch.Tensor, s_x: fl
     if not need_dW:
         dW = None
     if ws is None:
-        ws = workspace(OP_BWD, M, K, N, X.device)
+        ws = workspace(OP_BWD, M, K, N, X.device, tune, stream)
     st = lib().qat_linear_bwd(_ptr(dOut), _ptr(X), _ptr(W), _ptr(Ypre), M, K, N, float(s_x), epilogue,
                               _ptr(dX), _ptr(dW), 1 if dW_accumulate else 0, _ptr(ws), ws.numel(),
-                              _stream(stream))
+                              _tune(tune), _stream(stream))
     _check(st)
     return dX, dW
 
@@ -198,7 +203,8 @@ class ReduceState:
     (device tensors owned here) and the next virtual rank in mesh order."""
 
     def __init__(self, replicas: int, shards: int, length: int, device="cuda",
-                 acc: Optional[Sequence[torch.Tensor]] = None, partials_persist: bool = False):
+                 acc: Optional[Sequence[torch.Tensor]] = None, partials_persist: bool = False,
+                 tune: Optional[Tuning] = None):
         if acc is None:
             acc = [torch.empty(length, dtype=torch.float32, device=device) for _ in range(replicas)]
         self.acc = list(acc)
@@ -209,6 +215,8 @@ class ReduceState:
         # persist: the caller keeps each replica's shard-0 partial valid and
         # unchanged until its shard-1 call has run (see the C header)
         self.c.flags = REDUCE_PARTIALS_PERSIST if partials_persist else 0
+        if tune is not None:
+            self.c.tune = tune
 
     @property
     def next(self) -> int:
@@ -234,14 +242,14 @@ def ordered_reduce(state: ReduceState, partial: torch.Tensor, out: Optional[torc
 
 
 def grad_l2norm_clip(g: torch.Tensor, max_norm: float = 1.0, eps: float = 0.0,
-                     ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                     ws: Optional[torch.Tensor] = None, stream=None, tune: Optional[Tuning] = None) -> torch.Tensor:
     """In-place clip of g; returns the pre-clip norm as a 1-element device tensor."""
     n = g.numel()
     nu = torch.empty(1, dtype=torch.float32, device=g.device)
     if ws is None:
-        ws = workspace(OP_NORM, n, 0, 0, g.device)
+        ws = workspace(OP_NORM, n, 0, 0, g.device, tune, stream)
     _check(lib().grad_l2norm_clip(_ptr(g), n, float(max_norm), float(eps), _ptr(nu), _ptr(ws), ws.numel(),
-                                  _stream(stream)))
+                                  _tune(tune), _stream(stream)))
     return nu
 
 
@@ -255,14 +263,8 @@ def state_hash(tensors: Sequence[torch.Tensor], ws: Optional[torch.Tensor] = Non
     ptrs = (C.c_void_p * n)(*[(_ptr(t).value if t.numel() > 0 else None) for t in tensors])
     nbytes = (C.c_int64 * n)(*[t.numel() * t.element_size() for t in tensors])
     total = sum(nbytes)
-    need = int(lib().brl_workspace_bytes(OP_HASH, total, n, 0))
     if ws is None:
-        key = (dev.type, dev.index, OP_HASH)
-        w = _ws_cache.get(key)
-        if w is None or w.numel() < need:
-            w = torch.empty(need, dtype=torch.uint8, device=dev)
-            _ws_cache[key] = w
-        ws = w
+        ws = workspace(OP_HASH, total, n, 0, dev, None, stream)
     out = torch.empty(32, dtype=torch.uint8, device=dev)
     _check(lib().brl_state_hash(C.cast(ptrs, C.c_void_p), C.cast(nbytes, C.c_void_p), n, _ptr(out), _ptr(ws),
                                 ws.numel(), _stream(stream)))
@@ -473,8 +475,3 @@ def probe_f32(op: str, a: torch.Tensor, b: Optional[torch.Tensor] = None, stream
     out = torch.empty_like(a)
     _check(lib().brl_probe_f32(PROBE_OPS[op], _ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)))
     return out
-
-
-def set_tuning(knob: int, value: int) -> int:
-    """Change a launch-shape knob (never the results); returns the old value."""
-    return int(lib().brl_set_tuning(knob, value))

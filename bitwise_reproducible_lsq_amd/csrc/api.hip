@@ -6,35 +6,38 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <atomic>
-
 #include "internal.hpp"
 
 namespace brl {
 
-// ---- tuning knobs (launch shapes only) -----------------------------------------
-static std::atomic<int64_t> g_tune[4] = {{0}, {0}, {0}, {0}};
-static const int64_t kTuneDefault[4] = {0, 256, 1, 2};   // chunk depth 0: per engine
+// ---- launch shapes of one call ---------------------------------------------------
+bool resolve_tuning(const brl_tuning* t, Tuning* out) {
+    Tuning r{0, 256, 1, 2};
+    if (t) {
+        if (t->bwd_chunk_log2 < 0 || t->bwd_chunk_log2 > 7) return false;
+        r.chunk_log2 = t->bwd_chunk_log2;
+        if (t->reduce_wg_blocks != 0) {
+            if (t->reduce_wg_blocks != 64 && t->reduce_wg_blocks != 128 && t->reduce_wg_blocks != 256) return false;
+            r.wg_blocks = t->reduce_wg_blocks;
+        }
+        if (t->stream_vec != 0) {
+            if (t->stream_vec != 1 && t->stream_vec != 2 && t->stream_vec != 4) return false;
+            r.vec = t->stream_vec;
+        }
+        if (t->bwd_engine != 0) {
+            if (t->bwd_engine != 1 && t->bwd_engine != 2) return false;
+            r.engine = t->bwd_engine;
+        }
+    }
+    *out = r;
+    return true;
+}
 
-int bwd_chunk_log2(int engine) {
-    int64_t v = g_tune[BRL_TUNE_BWD_CHUNK_LOG2].load();
-    if (v > 0) return (int)v;
+int bwd_chunk_log2(const Tuning& t, int engine) {
+    if (t.chunk_log2 > 0) return t.chunk_log2;
     // defaults: the deepest stack that keeps 3 workgroups per CU
     if (engine == 2) return 6;
-    if (engine == 1) return 4;
-    return 4;   // any engine: the smaller depth (more chunk roots) bounds the workspace
-}
-int reduce_wg_blocks() {
-    int64_t v = g_tune[BRL_TUNE_REDUCE_WG_BLOCKS].load();
-    return (int)(v > 0 ? v : kTuneDefault[BRL_TUNE_REDUCE_WG_BLOCKS]);
-}
-int stream_vec() {
-    int64_t v = g_tune[BRL_TUNE_STREAM_VEC].load();
-    return (int)(v > 0 ? v : kTuneDefault[BRL_TUNE_STREAM_VEC]);
-}
-int bwd_engine() {
-    int64_t v = g_tune[BRL_TUNE_BWD_ENGINE].load();
-    return (int)(v > 0 ? v : kTuneDefault[BRL_TUNE_BWD_ENGINE]);
+    return 4;   // VALU engine, and the bound over both engines (more chunk roots)
 }
 
 // ---- the SwiGLU exp constants, derived from ln 2 ---------------------------------
@@ -70,6 +73,7 @@ static brl_status check_hip(hipError_t e, const char* what) {
 }
 
 static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+static bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
 
 // error reporting for the entry points defined in other translation units
 brl_status report_error(brl_status s, const char* msg) { return fail(s, "%s", msg); }
@@ -123,7 +127,9 @@ struct BwdLayout {
     size_t bytes;
 };
 
-static BwdLayout bwd_layout(void* ws, int64_t M, int64_t K, int64_t N, int epilogue) {
+// D: the chunk depth that sizes the chunk roots (the bound over both engines
+// when the engine is not known yet)
+static BwdLayout bwd_layout(void* ws, int64_t M, int64_t K, int64_t N, int epilogue, int D) {
     BwdLayout L;
     L.Kp = round_up(K, kKPad);
     L.Mp = round_up(M, kRowPad);
@@ -134,8 +140,8 @@ static BwdLayout bwd_layout(void* ws, int64_t M, int64_t K, int64_t N, int epilo
     L.bx = c.take<float>((size_t)(L.Mp * L.Kp));
     L.bw = c.take<float>((size_t)(L.Np * L.Kp));
     L.G = epilogue == BRL_EPILOGUE_SWIGLU ? c.take<float>((size_t)(M * N)) : nullptr;
-    int64_t r1 = ste_root_floats(M, N, K);   // dX: I = M, R = N
-    int64_t r2 = ste_root_floats(N, M, K);   // dW: I = N, R = M
+    int64_t r1 = ste_root_floats(M, N, K, D);   // dX: I = M, R = N
+    int64_t r2 = ste_root_floats(N, M, K, D);   // dW: I = N, R = M
     L.roots = c.take<float>((size_t)(r1 > r2 ? r1 : r2));
     L.bytes = c.off + 256;
     return L;
@@ -187,13 +193,16 @@ static HashLayout hash_layout(void* ws, int64_t leaves, int64_t count) {
     return L;
 }
 
-size_t brl_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N) {
+size_t brl_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, const brl_tuning* tune) {
+    Tuning t;
+    if (!resolve_tuning(tune, &t)) return 0;
     switch (op) {
         case BRL_OP_HASH:
             if (M < 0 || K < 1 || K > ((int64_t)1 << 31)) return 0;
             return hash_layout(nullptr, M / kHashLeafBytes + K, K).bytes;
         case BRL_OP_FWD: return sizes_ok(M, K, N) ? fwd_layout(nullptr, M, K, N, BRL_EPILOGUE_SWIGLU).bytes : 0;
-        case BRL_OP_BWD: return sizes_ok(M, K, N) ? bwd_layout(nullptr, M, K, N, BRL_EPILOGUE_SWIGLU).bytes : 0;
+        case BRL_OP_BWD:
+            return sizes_ok(M, K, N) ? bwd_layout(nullptr, M, K, N, BRL_EPILOGUE_SWIGLU, bwd_chunk_log2(t, 0)).bytes : 0;
         case BRL_OP_NORM: return M >= 0 ? norm_bytes(M) : 0;
         default: return 0;
     }
@@ -201,7 +210,9 @@ size_t brl_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N) {
 
 brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, int64_t N, float s_x,
                           const float* addend, int32_t epilogue, float* Y, float* Ypre, float* s_w_out,
-                          void* ws, size_t ws_bytes, void* stream) {
+                          void* ws, size_t ws_bytes, const brl_tuning* tune, void* stream) {
+    Tuning tn;
+    if (!resolve_tuning(tune, &tn)) return fail(BRL_EINVAL, "qat_linear_fwd: tuning value out of range");
     if (!sizes_ok(M, K, N)) return fail(BRL_ESHAPE, "qat_linear_fwd: bad sizes M=%lld K=%lld N=%lld",
                                         (long long)M, (long long)K, (long long)N);
     if (K > 133144) return fail(BRL_ESHAPE, "qat_linear_fwd: K=%lld could overflow int32 accumulators", (long long)K);
@@ -213,6 +224,7 @@ brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, 
     if (!aligned4(X) || !aligned4(W) || !aligned4(Y) || !aligned4(addend) || !aligned4(Ypre) || !aligned4(s_w_out))
         return fail(BRL_EINVAL, "qat_linear_fwd: pointers must be 4-byte aligned");
     const FwdLayout need = fwd_layout(nullptr, M, K, N, BRL_EPILOGUE_SWIGLU);
+    if (!aligned256(ws)) return fail(BRL_EINVAL, "qat_linear_fwd: workspace must be 256-byte aligned");
     if (!ws || ws_bytes < need.bytes)
         return fail(BRL_EWORKSPACE, "qat_linear_fwd: workspace %zu < %zu bytes", ws_bytes, need.bytes);
     FwdLayout L = fwd_layout(ws, M, K, N, epilogue);
@@ -224,7 +236,7 @@ brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, 
     fin.s_x = s_x;
     fin.scal = L.scal;
     fin.s_w_out = s_w_out;
-    brl_status s = check_hip(launch_canon(kMapAbs, W, N * K, L.partials, fin, st), "weight step");
+    brl_status s = check_hip(launch_canon(kMapAbs, W, N * K, L.partials, fin, tn.wg_blocks, st), "weight step");
     if (s || M == 0) return s;
     s = check_hip(launch_quantize(W, N, K, &L.scal->s_w, 0.0f, L.qw, L.Nvp, L.Kp,
                                   epilogue == BRL_EPILOGUE_SWIGLU ? N / 2 : 0, st), "quantize W");
@@ -240,7 +252,10 @@ brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, 
 
 brl_status qat_linear_bwd(const float* dOut, const float* X, const float* W, const float* Ypre,
                           int64_t M, int64_t K, int64_t N, float s_x, int32_t epilogue, float* dX,
-                          float* dW, int32_t dW_accumulate, void* ws, size_t ws_bytes, void* stream) {
+                          float* dW, int32_t dW_accumulate, void* ws, size_t ws_bytes, const brl_tuning* tune,
+                          void* stream) {
+    Tuning tn;
+    if (!resolve_tuning(tune, &tn)) return fail(BRL_EINVAL, "qat_linear_bwd: tuning value out of range");
     if (!sizes_ok(M, K, N)) return fail(BRL_ESHAPE, "qat_linear_bwd: bad sizes M=%lld K=%lld N=%lld",
                                         (long long)M, (long long)K, (long long)N);
     if (epilogue != BRL_EPILOGUE_NONE && epilogue != BRL_EPILOGUE_SWIGLU)
@@ -252,14 +267,28 @@ brl_status qat_linear_bwd(const float* dOut, const float* X, const float* W, con
     if (dW_accumulate != 0 && dW_accumulate != 1) return fail(BRL_EINVAL, "qat_linear_bwd: dW_accumulate must be 0 or 1");
     if (!aligned4(dOut) || !aligned4(X) || !aligned4(W) || !aligned4(Ypre) || !aligned4(dX) || !aligned4(dW))
         return fail(BRL_EINVAL, "qat_linear_bwd: pointers must be 4-byte aligned");
-    const int64_t Qx = ste_chunks(N, 0), Qw = ste_chunks(M, 0);
+    // the engine is fixed by the operands before anything is sized, and the
+    // chunk depth read once: the layout and the launches use the same values
+    const float* G = dOut;
+    const bool g_vec_shape = N % 4 == 0;
+    // (with SwiGLU, G is the workspace's copy, carved at a 256-byte offset)
+    const void* g_src = epilogue == BRL_EPILOGUE_SWIGLU ? ws : static_cast<const void*>(dOut);
+    const bool g_al16 = (reinterpret_cast<uintptr_t>(g_src) & 15) == 0;
+    // The matrix-core engine loads 16-byte pieces of G rows directly into
+    // LDS: it needs N % 4 == 0 and a 16-byte aligned G (the workspace copy
+    // is aligned); otherwise the VALU engine runs (same bits).
+    const bool g_vec = g_vec_shape && g_al16;
+    const int engine = (tn.engine == 2 && g_vec) ? 2 : 1;
+    const int D = bwd_chunk_log2(tn, engine);
+    const int64_t Qx = ste_chunks(N, D), Qw = ste_chunks(M, D);
     if (Qx > 1024 || Qw > 1024)
         return fail(BRL_ESHAPE, "qat_linear_bwd: reduction too long for the chunk setting (%lld, %lld chunks)",
                     (long long)Qx, (long long)Qw);
-    const BwdLayout need = bwd_layout(nullptr, M, K, N, BRL_EPILOGUE_SWIGLU);
+    const BwdLayout need = bwd_layout(nullptr, M, K, N, BRL_EPILOGUE_SWIGLU, D);
+    if (!aligned256(ws)) return fail(BRL_EINVAL, "qat_linear_bwd: workspace must be 256-byte aligned");
     if (!ws || ws_bytes < need.bytes)
         return fail(BRL_EWORKSPACE, "qat_linear_bwd: workspace %zu < %zu bytes", ws_bytes, need.bytes);
-    BwdLayout L = bwd_layout(ws, M, K, N, epilogue);
+    BwdLayout L = bwd_layout(ws, M, K, N, epilogue, D);
     hipStream_t st = static_cast<hipStream_t>(stream);
 
     CanonFinishArgs fin{};
@@ -267,15 +296,9 @@ brl_status qat_linear_bwd(const float* dOut, const float* X, const float* W, con
     fin.count_f = (float)(double)(N * K);
     fin.s_x = s_x;
     fin.scal = L.scal;
-    brl_status s = check_hip(launch_canon(kMapAbs, W, N * K, L.partials, fin, st), "weight step");
+    brl_status s = check_hip(launch_canon(kMapAbs, W, N * K, L.partials, fin, tn.wg_blocks, st), "weight step");
     if (s) return s;
-    const float* G = dOut;
     if (epilogue == BRL_EPILOGUE_SWIGLU && M > 0) G = L.G;
-    // The matrix-core engine loads 16-byte pieces of G rows directly into
-    // LDS: it needs N % 4 == 0 and a 16-byte aligned G; otherwise the VALU
-    // engine runs (same bits).
-    const bool g_vec = N % 4 == 0 && (reinterpret_cast<uintptr_t>(G) & 15) == 0;
-    const int engine = (bwd_engine() == 2 && g_vec) ? 2 : 1;
     if (engine == 2) {
         s = check_hip(launch_dequant(W, N, K, &L.scal->s_w, 0.0f, static_cast<float*>(L.bw), L.Np, L.Kp, st),
                       "dequantise W");
@@ -301,7 +324,7 @@ brl_status qat_linear_bwd(const float* dOut, const float* X, const float* W, con
         a.ldb = L.Kp; a.b_scale_dev = &L.scal->s_w;
         a.mask_src = X; a.mask_scale_dev = nullptr; a.mask_scale_host = s_x;
         a.out = dX; a.accumulate = 0; a.roots = L.roots;
-        s = check_hip(launch_ste(a, engine, st), "dX");
+        s = check_hip(launch_ste(a, engine, D, st), "dX");
         if (s) return s;
     }
     if (dW) {
@@ -311,7 +334,7 @@ brl_status qat_linear_bwd(const float* dOut, const float* X, const float* W, con
         a.ldb = L.Kp; a.b_scale_dev = nullptr; a.b_scale_host = s_x;
         a.mask_src = W; a.mask_scale_dev = &L.scal->s_w;
         a.out = dW; a.accumulate = dW_accumulate; a.roots = L.roots;
-        s = check_hip(launch_ste(a, engine, st), "dW");
+        s = check_hip(launch_ste(a, engine, D, st), "dW");
         if (s) return s;
     }
     return BRL_OK;
@@ -351,6 +374,8 @@ brl_status ordered_reduce(brl_reduce_state* sp, const float* partial, float* out
     if (n > 0 && !partial) return fail(BRL_EINVAL, "ordered_reduce: null partial");
     if (last && n > 0 && !out) return fail(BRL_EINVAL, "ordered_reduce: last rank needs out");
     if (!aligned4(partial) || !aligned4(out)) return fail(BRL_EINVAL, "ordered_reduce: misaligned pointer");
+    Tuning tn;
+    if (!resolve_tuning(&sp->tune, &tn)) return fail(BRL_EINVAL, "ordered_reduce: tuning value out of range");
     hipStream_t st = static_cast<hipStream_t>(stream);
     brl_status rc = BRL_OK;
     const bool defer = (sp->flags & BRL_REDUCE_PARTIALS_PERSIST) && S > 1;
@@ -361,7 +386,7 @@ brl_status ordered_reduce(brl_reduce_state* sp, const float* partial, float* out
             sp->pending = partial;
         } else if (!last) {
             const bool joint = s == 1 && sp->pending;
-            rc = check_hip(launch_accumulate(sp->acc[r], joint ? sp->pending : sp->acc[r], partial, n, s == 0, st),
+            rc = check_hip(launch_accumulate(sp->acc[r], joint ? sp->pending : sp->acc[r], partial, n, s == 0, tn.vec, st),
                            s == 0 ? "running sum (first shard)" : "running sum");
         } else {
             FoldPtrs p{};
@@ -371,7 +396,7 @@ brl_status ordered_reduce(brl_reduce_state* sp, const float* partial, float* out
                 p.a[R - 1] = partial;
                 g_last = nullptr;
             } else if (s == 1 && sp->pending) {
-                rc = check_hip(launch_accumulate(sp->acc[r], sp->pending, partial, n, 0, st), "running sum");
+                rc = check_hip(launch_accumulate(sp->acc[r], sp->pending, partial, n, 0, tn.vec, st), "running sum");
                 g_last = nullptr;
             }
             if (rc == BRL_OK) rc = check_hip(launch_fold(p, R, g_last, out, n, st), "TreeFold");
@@ -382,29 +407,44 @@ brl_status ordered_reduce(brl_reduce_state* sp, const float* partial, float* out
     return rc;
 }
 
-brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float eps, float* norm_out, void* ws,
-                            size_t ws_bytes, void* stream) {
-    if (len < 0 || len > ((int64_t)1 << 40)) return fail(BRL_ESHAPE, "grad_l2norm_clip: bad length");
-    if (len > 0 && !g) return fail(BRL_EINVAL, "grad_l2norm_clip: null gradient");
-    if (!(max_norm > 0.0f) || !isfinite(max_norm) || !(eps >= 0.0f) || !isfinite(eps))
-        return fail(BRL_EINVAL, "grad_l2norm_clip: max_norm must be finite > 0 and eps finite >= 0");
-    if (!aligned4(g) || !aligned4(norm_out)) return fail(BRL_EINVAL, "grad_l2norm_clip: misaligned pointer");
-    const size_t need = norm_bytes(len);
-    if (!ws || ws_bytes < need)
-        return fail(BRL_EWORKSPACE, "grad_l2norm_clip: workspace %zu < %zu bytes", ws_bytes, need);
+// The squared-norm CanonSum and the clip, on a workspace already checked to
+// hold norm_bytes(len) bytes at a 256-byte aligned address.
+static brl_status norm_clip_launch(float* g, int64_t len, float max_norm, float eps, float* norm_out, void* ws,
+                                   const Tuning& tn, hipStream_t st) {
     Carver c(ws);
     Scalars* scal = c.take<Scalars>(1);
     float* partials = c.take<float>((size_t)canon_partials(len));
-    hipStream_t st = static_cast<hipStream_t>(stream);
     CanonFinishArgs fin{};
     fin.mode = kFinishNorm;
     fin.max_norm = max_norm;
     fin.eps = eps;
     fin.scal = scal;
     fin.nu_out = norm_out;
-    brl_status s = check_hip(launch_canon(kMapSquare, g, len, partials, fin, st), "squared norm");
+    brl_status s = check_hip(launch_canon(kMapSquare, g, len, partials, fin, tn.wg_blocks, st), "squared norm");
     if (s) return s;
-    return check_hip(launch_clip(g, len, scal, st), "clip");
+    return check_hip(launch_clip(g, len, scal, tn.vec, st), "clip");
+}
+
+static brl_status norm_clip_check(const char* who, const float* g, int64_t len, float max_norm, float eps,
+                                  const float* norm_out) {
+    if (len < 0 || len > ((int64_t)1 << 40)) return fail(BRL_ESHAPE, "%s: bad length", who);
+    if (len > 0 && !g) return fail(BRL_EINVAL, "%s: null gradient", who);
+    if (!(max_norm > 0.0f) || !isfinite(max_norm) || !(eps >= 0.0f) || !isfinite(eps))
+        return fail(BRL_EINVAL, "%s: max_norm must be finite > 0 and eps finite >= 0", who);
+    if (!aligned4(g) || !aligned4(norm_out)) return fail(BRL_EINVAL, "%s: misaligned pointer", who);
+    return BRL_OK;
+}
+
+brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float eps, float* norm_out, void* ws,
+                            size_t ws_bytes, const brl_tuning* tune, void* stream) {
+    Tuning tn;
+    if (!resolve_tuning(tune, &tn)) return fail(BRL_EINVAL, "grad_l2norm_clip: tuning value out of range");
+    if (brl_status s = norm_clip_check("grad_l2norm_clip", g, len, max_norm, eps, norm_out)) return s;
+    const size_t need = norm_bytes(len);
+    if (!aligned256(ws)) return fail(BRL_EINVAL, "grad_l2norm_clip: workspace must be 256-byte aligned");
+    if (!ws || ws_bytes < need)
+        return fail(BRL_EWORKSPACE, "grad_l2norm_clip: workspace %zu < %zu bytes", ws_bytes, need);
+    return norm_clip_launch(g, len, max_norm, eps, norm_out, ws, tn, static_cast<hipStream_t>(stream));
 }
 
 brl_status brl_probe_f32(int32_t op, const float* a, const float* b, float* out, int64_t n, void* stream) {
@@ -431,6 +471,7 @@ brl_status brl_state_hash(const void* const* tensors, const int64_t* nbytes, int
         leaves += nbytes[i] == 0 ? 1 : ceil_div(nbytes[i], kHashLeafBytes);
     }
     const HashLayout need = hash_layout(nullptr, leaves, count);
+    if (!aligned256(ws)) return fail(BRL_EINVAL, "brl_state_hash: workspace must be 256-byte aligned");
     if (!ws || ws_bytes < need.bytes)
         return fail(BRL_EWORKSPACE, "brl_state_hash: workspace %zu < %zu bytes", ws_bytes, need.bytes);
     HashLayout L = hash_layout(ws, leaves, count);
@@ -551,17 +592,6 @@ brl_status attn_bwd_dkdv(const float* Q, const float* K, const float* V, const f
     return check_hip(launch_attn_bwd_dkdv(Q, K, V, O, dO, stats, B, S, Hq, Hkv, ldq, ldk, ldv, ldo, window, s_v,
                                           dK, dV, ldg, exp_constants(), static_cast<hipStream_t>(stream)),
                      "attention dK/dV");
-}
-
-int64_t brl_set_tuning(int32_t knob, int64_t value) {
-    if (knob < 0 || knob > 3) return -1;
-    if (knob == BRL_TUNE_BWD_CHUNK_LOG2 && value > 7) value = 7;
-    if (knob == BRL_TUNE_REDUCE_WG_BLOCKS && value > 0 && value != 64 && value != 128 && value != 256)
-        value = 256;
-    if (knob == BRL_TUNE_STREAM_VEC && value > 0 && value != 1 && value != 2 && value != 4) value = 1;
-    if (knob == BRL_TUNE_BWD_ENGINE && value > 2) value = 2;
-    int64_t old = g_tune[knob].exchange(value > 0 ? value : 0);
-    return old > 0 ? old : kTuneDefault[knob];
 }
 
 const char* brl_status_string(brl_status s) {

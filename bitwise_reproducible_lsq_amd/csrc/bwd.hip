@@ -467,12 +467,12 @@ __global__ __launch_bounds__(256) void ste_finish_kernel(SteArgs a, int64_t Q) {
     }
 }
 
-int64_t ste_chunks(int64_t R, int engine) {
-    return ceil_div(ceil_div(R, kBlock), (int64_t)1 << bwd_chunk_log2(engine));
+int64_t ste_chunks(int64_t R, int D) {
+    return ceil_div(ceil_div(R, kBlock), (int64_t)1 << D);
 }
 
-int64_t ste_root_floats(int64_t I, int64_t R, int64_t Jn) {
-    const int64_t Q = ste_chunks(R, 0);
+int64_t ste_root_floats(int64_t I, int64_t R, int64_t Jn, int D) {
+    const int64_t Q = ste_chunks(R, D);
     return Q > 1 ? Q * I * Jn : 0;
 }
 
@@ -509,9 +509,9 @@ static void ste_launch_mfma(const SteArgs& a, int D, dim3 grid, int64_t nblk, in
     }
 }
 
-hipError_t launch_ste(const SteArgs& a, int engine, hipStream_t st) {
+hipError_t launch_ste(const SteArgs& a, int engine, int D, hipStream_t st) {
     if (a.I <= 0 || a.Jn <= 0) return hipSuccess;
-    const int D = bwd_chunk_log2(engine);
+    if (D < 1 || D > 7) return hipErrorInvalidValue;
     const int64_t nblk = ceil_div(a.R, kBlock);
     if (nblk == 0) {
         const int64_t plane = a.I * a.Jn;

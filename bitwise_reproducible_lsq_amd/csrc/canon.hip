@@ -190,8 +190,8 @@ static hipError_t canon_run(int map, const float* x, int64_t n, float* partials,
 }
 
 hipError_t launch_canon(int map, const float* x, int64_t n, float* partials,
-                        const CanonFinishArgs& fin, hipStream_t st) {
-    switch (reduce_wg_blocks()) {
+                        const CanonFinishArgs& fin, int wg_blocks, hipStream_t st) {
+    switch (wg_blocks) {
         case 64: return canon_run<64>(map, x, n, partials, fin, st);
         case 128: return canon_run<128>(map, x, n, partials, fin, st);
         default: return canon_run<256>(map, x, n, partials, fin, st);

@@ -23,11 +23,19 @@ struct Scalars {
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Launch-shape knobs (never change results).
-int bwd_chunk_log2(int engine); // 32-blocks per backward chunk = 2^value (engine 0: workspace bound)
-int reduce_wg_blocks();        // 32-blocks per workgroup in CanonSum passes
-int stream_vec();              // 16-byte vectors per thread in streaming kernels (1, 2, 4)
-int bwd_engine();              // backward products: 1 VALU, 2 matrix cores (when the operands allow)
+// Launch shapes of one call (never change results), resolved from the
+// caller's brl_tuning with the defaults filled in.
+struct Tuning {
+    int chunk_log2;   // backward chunk = 2^chunk_log2 32-blocks; 0 = per engine (6 matrix cores, 4 VALU)
+    int wg_blocks;    // 32-blocks per workgroup in CanonSum passes (64, 128, 256)
+    int vec;          // 16-byte vectors per thread in streaming kernels (1, 2, 4)
+    int engine;       // backward products: 1 VALU, 2 matrix cores (when the operands allow)
+};
+// false for a value outside its range
+bool resolve_tuning(const brl_tuning* t, Tuning* out);
+// chunk depth of the backward on `engine` (1 or 2); engine 0 gives the
+// smaller depth of the two, which bounds the chunk roots for the workspace
+int bwd_chunk_log2(const Tuning& t, int engine);
 
 // ---- CanonSum over a flat vector -------------------------------------------
 enum CanonMap { kMapAbs = 0, kMapSquare = 1 };
@@ -46,7 +54,7 @@ struct CanonFinishArgs {
 // Partial buffer floats needed by launch_canon for n elements.
 int64_t canon_partials(int64_t n);
 hipError_t launch_canon(int map, const float* x, int64_t n, float* partials,
-                        const CanonFinishArgs& fin, hipStream_t st);
+                        const CanonFinishArgs& fin, int wg_blocks, hipStream_t st);
 
 // ---- quantisation and the int8 GEMM ------------------------------------------
 // GEMM tiling (forward): K padded to kKPad, rows of both operands to kRowPad.
@@ -102,10 +110,12 @@ struct SteArgs {
     int accumulate;
     float* roots;          // workspace for chunk roots [Q, I, Jn]
 };
-int64_t ste_chunks(int64_t R, int engine);
-int64_t ste_root_floats(int64_t I, int64_t R, int64_t Jn);   // bound over engines
-// engine 2 needs Bf, a_vec and I % 4 == 0 when A is r-major, R % 4 == 0 when i-major
-hipError_t launch_ste(const SteArgs& a, int engine, hipStream_t st);
+// reduction chunks of 2^D 32-blocks over R terms
+int64_t ste_chunks(int64_t R, int D);
+int64_t ste_root_floats(int64_t I, int64_t R, int64_t Jn, int D);
+// engine 2 needs Bf, a_vec and I % 4 == 0 when A is r-major, R % 4 == 0 when i-major;
+// D = chunk depth (1..7)
+hipError_t launch_ste(const SteArgs& a, int engine, int D, hipStream_t st);
 
 hipError_t launch_swiglu_bwd(const float* dA, const float* ypre, int64_t M, int64_t N, float* G,
                              const ExpConsts& ek, hipStream_t st);
@@ -136,11 +146,12 @@ void adamw_scalars(int64_t step, double tokens, const brl_adamw_config& c, brl_a
 
 // ---- replay -------------------------------------------------------------------
 // first = 1: A <- G; otherwise A <- X + G (X = A, or a deferred first shard).
-hipError_t launch_accumulate(float* A, const float* X, const float* G, int64_t n, int first, hipStream_t st);
+hipError_t launch_accumulate(float* A, const float* X, const float* G, int64_t n, int first, int vec,
+                             hipStream_t st);
 struct FoldPtrs { const float* a[64]; };
 hipError_t launch_fold(const FoldPtrs& p, int R, const float* g_last, float* out, int64_t n,
                        hipStream_t st);
-hipError_t launch_clip(float* g, int64_t n, const Scalars* scal, hipStream_t st);
+hipError_t launch_clip(float* g, int64_t n, const Scalars* scal, int vec, hipStream_t st);
 
 // out[i] = a[i] * b[i] formed by the matrix-core product of the backward
 hipError_t launch_probe_mfma(const float* a, const float* b, float* out, int64_t n, hipStream_t st);

@@ -79,12 +79,13 @@ __global__ __launch_bounds__(kStreamThreads) void accumulate_scalar_kernel(float
     if (i < n) A[i] = first ? G[i] : f_add(X[i], G[i]);
 }
 
-hipError_t launch_accumulate(float* A, const float* X, const float* G, int64_t n, int first, hipStream_t st) {
+hipError_t launch_accumulate(float* A, const float* X, const float* G, int64_t n, int first, int vec,
+                             hipStream_t st) {
     if (n <= 0) return hipSuccess;
     int64_t done = 0;
     if (aligned16(A) && aligned16(X) && aligned16(G)) {
         const int64_t n4 = n / 4;
-        const int V = stream_vec();
+        const int V = vec;
         if (n4 > 0) {
             vf4* a4 = reinterpret_cast<vf4*>(A);
             const vf4* x4 = reinterpret_cast<const vf4*>(X);
@@ -230,12 +231,12 @@ __global__ __launch_bounds__(kStreamThreads) void clip_scalar_kernel(float* __re
     if (i < n) g[i] = f_mul(g[i], s->kappa);
 }
 
-hipError_t launch_clip(float* g, int64_t n, const Scalars* scal, hipStream_t st) {
+hipError_t launch_clip(float* g, int64_t n, const Scalars* scal, int vec, hipStream_t st) {
     if (n <= 0) return hipSuccess;
     int64_t done = 0;
     if (aligned16(g)) {
         const int64_t n4 = n / 4;
-        const int V = stream_vec();
+        const int V = vec;
         if (n4 > 0) {
             vf4* g4 = reinterpret_cast<vf4*>(g);
             const dim3 grid(stream_grid(n4, V)), blk(kStreamThreads);

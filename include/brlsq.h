@@ -28,7 +28,8 @@
  * Memory and ownership.  All tensor pointers are device pointers, row-major,
  * dense (row pitch = the row length).  The caller owns every buffer,
  * including the workspace, whose size comes from brl_workspace_bytes().  The
- * library allocates no device memory.  Every call is asynchronous on the given
+ * library allocates no device memory and holds no state between calls
+ * (besides the calling thread's last error message).  Every call is asynchronous on the given
  * HIP stream (a hipStream_t passed as void*; NULL = the null stream) and never
  * synchronises the host.  Pointers must be 4-byte aligned.
  *
@@ -79,12 +80,27 @@ typedef int32_t brl_status;
 #define BRL_OP_NORM 2
 #define BRL_OP_HASH 3
 
-/* Bytes of device workspace needed by an operation.  For BRL_OP_FWD and
- * BRL_OP_BWD, M, K, N are the layer sizes (N = stacked width for SwiGLU);
- * for BRL_OP_NORM, M is the vector length and K, N are ignored; for
- * BRL_OP_HASH, M is the total byte length of the state and K its tensor
- * count (N ignored). */
-BRL_API size_t brl_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N);
+/* Launch-shape choices of one call.  They change only how work is split
+ * across workgroups or which units form the backward's products, never the
+ * results.  A zero field selects its default; a NULL pointer selects every
+ * default.  The library keeps no tuning state of its own: each call reads the
+ * struct once, at its start, and a bad value fails the call with BRL_EINVAL. */
+typedef struct brl_tuning {
+    int32_t bwd_chunk_log2;    /* 32-blocks per backward reduction chunk: 2^v, v in 1..7
+                                  (0: 6 on the matrix-core engine, 4 on the VALU engine) */
+    int32_t reduce_wg_blocks;  /* 32-blocks per workgroup in CanonSum passes: 64, 128 or 256 (0: 256) */
+    int32_t stream_vec;        /* 16-byte vectors per thread in the streaming kernels: 1, 2 or 4 (0: 1) */
+    int32_t bwd_engine;        /* backward products on 1 the VALU, 2 the matrix cores (0: 2; the matrix
+                                  cores need N % 4 == 0 and a 16-byte aligned dOut, else 1 runs) */
+} brl_tuning;
+
+/* Bytes of device workspace needed by an operation run with `tune` (NULL:
+ * the defaults; the backward's chunk roots grow as bwd_chunk_log2 shrinks).
+ * For BRL_OP_FWD and BRL_OP_BWD, M, K, N are the layer sizes (N = stacked
+ * width for SwiGLU); for BRL_OP_NORM, M is the vector length and K, N are
+ * ignored; for BRL_OP_HASH, M is the total byte length of the state and K
+ * its tensor count (N ignored).  Returns 0 for bad sizes or tuning. */
+BRL_API size_t brl_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, const brl_tuning* tune);
 
 /*
  * qat_linear_fwd -- LSQ int8 quantisation-aware linear forward.
@@ -102,12 +118,15 @@ BRL_API size_t brl_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N);
  *   backward).  addend (if any) is added before the activation.
  * s_x: the activation step, finite and > 0.
  * s_w_out: NULL or a device float that receives s_w.
+ * ws: device workspace of at least brl_workspace_bytes(BRL_OP_FWD, M, K, N,
+ * tune) bytes, owned by the caller; calls that overlap in time must not
+ * share one.  tune: NULL or the call's launch shapes (see brl_tuning).
  * Requires |acc| < 2^31, guaranteed for K <= 133144.
  */
 BRL_API brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, int64_t N,
                           float s_x, const float* addend, int32_t epilogue,
                           float* Y, float* Ypre, float* s_w_out,
-                          void* ws, size_t ws_bytes, void* stream);
+                          void* ws, size_t ws_bytes, const brl_tuning* tune, void* stream);
 
 /*
  * qat_linear_bwd -- straight-through backward of qat_linear_fwd.
@@ -121,11 +140,14 @@ BRL_API brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int
  * dX [M,K] and dW [N,K] may each be NULL (not computed).
  * dW_accumulate = 1: dW <- dW + (new dW), one binary32 add per element (the
  *   ascending microbatch running sum); 0: dW is overwritten.
+ * ws: at least brl_workspace_bytes(BRL_OP_BWD, M, K, N, tune) bytes, owned
+ * by the caller and not shared by overlapping calls.  tune: NULL or the
+ * call's launch shapes.
  */
 BRL_API brl_status qat_linear_bwd(const float* dOut, const float* X, const float* W, const float* Ypre,
                           int64_t M, int64_t K, int64_t N, float s_x, int32_t epilogue,
                           float* dX, float* dW, int32_t dW_accumulate,
-                          void* ws, size_t ws_bytes, void* stream);
+                          void* ws, size_t ws_bytes, const brl_tuning* tune, void* stream);
 
 #define BRL_MAX_REPLICAS 64
 
@@ -133,7 +155,9 @@ BRL_API brl_status qat_linear_bwd(const float* dOut, const float* X, const float
  * buffers of len floats (A_r), owned by the caller; next is the virtual rank
  * v = r*shards + s that ordered_reduce expects next.  flags: 0 or
  * BRL_REDUCE_PARTIALS_PERSIST, set by the caller after brl_reduce_init;
- * pending is the library's own bookkeeping. */
+ * tune: the launch shapes of the replay's kernels (zeroed by brl_reduce_init:
+ * the defaults; the caller may set it afterwards); pending is the library's
+ * own bookkeeping. */
 #define BRL_REDUCE_PARTIALS_PERSIST 1u
 typedef struct brl_reduce_state {
     int32_t replicas;
@@ -143,6 +167,7 @@ typedef struct brl_reduce_state {
     uint32_t flags;
     const float* pending;
     float* acc[BRL_MAX_REPLICAS];
+    brl_tuning tune;
 } brl_reduce_state;
 
 /* Fill a reduce state: 1 <= replicas <= 64, shards >= 1, len >= 0, acc[0..replicas)
@@ -179,9 +204,12 @@ BRL_API brl_status ordered_reduce(brl_reduce_state* st, const float* partial, fl
  *   otherwise g is left unchanged.
  * norm_out: NULL or a device float receiving nu (before clipping).
  * max_norm > 0 and eps >= 0, both finite.
+ * ws: at least brl_workspace_bytes(BRL_OP_NORM, len, 0, 0, tune) bytes,
+ * owned by the caller and not shared by overlapping calls.  tune: NULL or
+ * the call's launch shapes.
  */
 BRL_API brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float eps, float* norm_out,
-                            void* ws, size_t ws_bytes, void* stream);
+                            void* ws, size_t ws_bytes, const brl_tuning* tune, void* stream);
 
 /*
  * brl_state_hash -- on-device hash of a training state (a list of tensors).
@@ -200,7 +228,7 @@ BRL_API brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float
  * (tensors[i] may be NULL when nbytes[i] == 0); nbytes: host array of byte
  * lengths >= 0; digest: device pointer receiving the 32 root bytes.  The host
  * arrays are read during the call only.  Workspace from
- * brl_workspace_bytes(BRL_OP_HASH, sum of nbytes, count, 0).
+ * brl_workspace_bytes(BRL_OP_HASH, sum of nbytes, count, 0, NULL).
  */
 BRL_API brl_status brl_state_hash(const void* const* tensors, const int64_t* nbytes, int32_t count,
                                   uint8_t* digest, void* ws, size_t ws_bytes, void* stream);
@@ -384,17 +412,6 @@ BRL_API brl_status brl_philox_u32(uint64_t key, uint32_t stream, uint64_t first,
  * n >= 0. */
 BRL_API brl_status brl_probe_f32(int32_t op, const float* a, const float* b, float* out, int64_t n,
                          void* stream);
-
-/* Launch-shape tuning knobs.  They change only how work is split across
- * workgroups or which units form the products, never the results.  Returns the previous value, or -1 for an
- * unknown knob; value <= 0 restores the default.  Process-wide. */
-#define BRL_TUNE_BWD_CHUNK_LOG2   0   /* 32-blocks per backward reduction chunk: 2^v, 1..7 (default 0:
-                                         6 on the matrix-core engine, 4 on the VALU engine) */
-#define BRL_TUNE_REDUCE_WG_BLOCKS 1   /* 32-blocks per workgroup in CanonSum passes: 64,128,256 */
-#define BRL_TUNE_STREAM_VEC       2   /* 16-byte vectors per thread in streaming kernels: 1, 2, 4 */
-#define BRL_TUNE_BWD_ENGINE       3   /* backward products on 1 the VALU, 2 the matrix cores (default; needs
-                                         N % 4 == 0 and a 16-byte aligned dOut, else 1 runs) */
-BRL_API int64_t brl_set_tuning(int32_t knob, int64_t value);
 
 BRL_API const char* brl_status_string(brl_status s);
 BRL_API const char* brl_last_error(void);

@@ -2,8 +2,10 @@
 synchronisation inside), so a HIP graph can capture them.  One graph holds
 the linear forward and backward and the attention forward with its three
 gradients.  It is replayed three times, with eager work between the replays
-that overwrites its outputs and reuses the shared workspace, and every
-replay must equal the eager results bit for bit."""
+that overwrites its outputs and runs the forward on other inputs (with a
+workspace of its own: the binding takes one per call, and the graph keeps
+the ones it captured), and every replay must equal the eager results bit
+for bit."""
 import numpy as np
 import pytest
 import torch
@@ -60,7 +62,7 @@ def test_linear_and_attention_replay_in_a_hip_graph():
     for rep in range(3):
         for t in outs:
             t.fill_(7.0)
-        brl.qat_linear_fwd(Xo, Wo, synth.S_X)          # eager work on the shared workspace
+        brl.qat_linear_fwd(Xo, Wo, synth.S_X)          # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()

@@ -217,26 +217,12 @@ def test_quantizer_at_rounding_boundaries(s):
     dY = np.random.default_rng(4).standard_normal((X.shape[0], 80)).astype(np.float32) * np.float32(1e-3)
     wX, wW = oracle.linear_bwd(dY, X, W, sf)
     for engine in ENGINES:
-        with tuning(brl.TUNE_BWD_ENGINE, engine):
-            dX, dW = brl.qat_linear_bwd(_cuda(dY), _cuda(X), _cuda(W), float(sf))
+        dX, dW = brl.qat_linear_bwd(_cuda(dY), _cuda(X), _cuda(W), float(sf), tune=brl.Tuning(bwd_engine=engine))
         assert_bitwise(dX, wX, f"dX (engine {engine})")
         assert_bitwise(dW, wW, f"dW (engine {engine})")
 
 
 # ---- linear layer: backward -----------------------------------------------------------
-class tuning:
-    """Set a launch-shape knob for the duration of a with-block."""
-
-    def __init__(self, knob, value):
-        self.knob, self.value = knob, value
-
-    def __enter__(self):
-        self.old = brl.set_tuning(self.knob, self.value)
-
-    def __exit__(self, *exc):
-        brl.set_tuning(self.knob, self.old)
-
-
 ENGINES = [1, 2]   # products on the VALU / on the matrix cores
 
 
@@ -244,8 +230,8 @@ ENGINES = [1, 2]   # products on the VALU / on the matrix cores
 @pytest.mark.parametrize("M,K,N", SHAPES)
 def test_bwd_parity(M, K, N, engine):
     inp = _case_inputs(M, K, N, seed=M * 3 + K + N, sub=0.01)
-    with tuning(brl.TUNE_BWD_ENGINE, engine):
-        dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), _cuda(inp.X), _cuda(inp.W), synth.S_X)
+    dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), _cuda(inp.X), _cuda(inp.W), synth.S_X,
+                                tune=brl.Tuning(bwd_engine=engine))
     wX, wW = oracle.linear_bwd(inp.dY, inp.X, inp.W, synth.S_X)
     assert_bitwise(dX, wX, f"dX (engine {engine})")
     assert_bitwise(dW, wW, f"dW (engine {engine})")
@@ -259,17 +245,17 @@ def test_bwd_matrix_core_ragged_reductions(M, K, N):
     inp = _case_inputs(M, K, N, seed=M + 7 * N, sub=0.01)
     wX, wW = oracle.linear_bwd(inp.dY, inp.X, inp.W, synth.S_X)
     X, W = _cuda(inp.X), _cuda(inp.W)
-    with tuning(brl.TUNE_BWD_ENGINE, 2):
-        dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), X, W, synth.S_X)
-        assert_bitwise(dX, wX, "dX")
-        assert_bitwise(dW, wW, "dW")
-        flat = torch.empty(M * N + 1, dtype=torch.float32, device="cuda")
-        dY_odd = flat[1:].view(M, N)
-        dY_odd.copy_(_cuda(inp.dY))
-        assert dY_odd.data_ptr() % 16 != 0
-        dX, dW = brl.qat_linear_bwd(dY_odd, X, W, synth.S_X)
-        assert_bitwise(dX, wX, "dX (unaligned dY)")
-        assert_bitwise(dW, wW, "dW (unaligned dY)")
+    mc = brl.Tuning(bwd_engine=2)
+    dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), X, W, synth.S_X, tune=mc)
+    assert_bitwise(dX, wX, "dX")
+    assert_bitwise(dW, wW, "dW")
+    flat = torch.empty(M * N + 1, dtype=torch.float32, device="cuda")
+    dY_odd = flat[1:].view(M, N)
+    dY_odd.copy_(_cuda(inp.dY))
+    assert dY_odd.data_ptr() % 16 != 0
+    dX, dW = brl.qat_linear_bwd(dY_odd, X, W, synth.S_X, tune=mc)
+    assert_bitwise(dX, wX, "dX (unaligned dY)")
+    assert_bitwise(dW, wW, "dW (unaligned dY)")
 
 
 def test_bwd_finish_alignment_paths():
@@ -293,18 +279,18 @@ def test_bwd_finish_alignment_paths():
     cases = [("aligned", _cuda(inp.X), _cuda(inp.W), False),
              ("mask sources unaligned", odd(inp.X), odd(inp.W), False),
              ("outputs unaligned", _cuda(inp.X), _cuda(inp.W), True)]
-    with tuning(brl.TUNE_BWD_CHUNK_LOG2, 1):     # several chunk roots per output at this size
-        for what, X, W, odd_out in cases:
-            if odd_out:
-                dX, dW = odd(np.zeros((M, K), np.float32)), odd(np.zeros((N, K), np.float32))
-            else:
-                dX = torch.empty((M, K), dtype=torch.float32, device="cuda")
-                dW = torch.empty((N, K), dtype=torch.float32, device="cuda")
-            brl.qat_linear_bwd(dY, X, W, synth.S_X, dX=dX, dW=dW)
-            assert_bitwise(dX, wX, f"dX ({what})")
-            assert_bitwise(dW, wW, f"dW ({what})")
-            brl.qat_linear_bwd(dY, X, W, synth.S_X, need_dX=False, dW=dW, dW_accumulate=True)
-            assert_bitwise(dW, np.float32(2) * wW, f"dW accumulated ({what})")
+    tune = brl.Tuning(bwd_chunk_log2=1)      # several chunk roots per output at this size
+    for what, X, W, odd_out in cases:
+        if odd_out:
+            dX, dW = odd(np.zeros((M, K), np.float32)), odd(np.zeros((N, K), np.float32))
+        else:
+            dX = torch.empty((M, K), dtype=torch.float32, device="cuda")
+            dW = torch.empty((N, K), dtype=torch.float32, device="cuda")
+        brl.qat_linear_bwd(dY, X, W, synth.S_X, dX=dX, dW=dW, tune=tune)
+        assert_bitwise(dX, wX, f"dX ({what})")
+        assert_bitwise(dW, wW, f"dW ({what})")
+        brl.qat_linear_bwd(dY, X, W, synth.S_X, need_dX=False, dW=dW, dW_accumulate=True, tune=tune)
+        assert_bitwise(dW, np.float32(2) * wW, f"dW accumulated ({what})")
 
 
 def test_bwd_tiny_workload():
@@ -323,8 +309,7 @@ def test_bwd_long_reductions_and_masks(engine):
     inp = _case_inputs(M, K, N, seed=21, x_kind="silu_x_normal")
     X = inp.X * np.float32(2.0)
     assert (np.abs(X / synth.S_X) > 127).any()
-    with tuning(brl.TUNE_BWD_ENGINE, engine):
-        dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), _cuda(X), _cuda(inp.W), synth.S_X)
+    dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), _cuda(X), _cuda(inp.W), synth.S_X, tune=brl.Tuning(bwd_engine=engine))
     wX, wW = oracle.linear_bwd(inp.dY, X, inp.W, synth.S_X)
     assert_bitwise(dX, wX, "dX")
     assert_bitwise(dW, wW, "dW")
@@ -336,8 +321,8 @@ def test_bwd_swiglu_parity(engine):
     inp = _case_inputs(M, K, N, seed=31, swiglu=True)
     X, W = _cuda(inp.X), _cuda(inp.W)
     _, Ypre, _ = brl.qat_linear_fwd(X, W, synth.S_X, epilogue=brl.EPILOGUE_SWIGLU)
-    with tuning(brl.TUNE_BWD_ENGINE, engine):
-        dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), X, W, synth.S_X, Ypre=Ypre, epilogue=brl.EPILOGUE_SWIGLU)
+    dX, dW = brl.qat_linear_bwd(_cuda(inp.dY), X, W, synth.S_X, Ypre=Ypre, epilogue=brl.EPILOGUE_SWIGLU,
+                                tune=brl.Tuning(bwd_engine=engine))
     _, wPre = oracle.linear_fwd(inp.X, inp.W, synth.S_X, epilogue=1)
     G = oracle.swiglu_bwd(wPre, inp.dY)
     wX, wW = oracle.linear_bwd(G, inp.X, inp.W, synth.S_X)
@@ -352,10 +337,9 @@ def test_bwd_microbatch_running_sum(engine):
     X, W, dY = _cuda(inp.X), _cuda(inp.W), _cuda(inp.dY)
     mb = M // B
     dW = None
-    with tuning(brl.TUNE_BWD_ENGINE, engine):
-        for b in range(B):
-            _, dW = brl.qat_linear_bwd(dY[b * mb:(b + 1) * mb], X[b * mb:(b + 1) * mb], W, synth.S_X,
-                                       need_dX=False, dW=dW, dW_accumulate=b > 0)
+    for b in range(B):
+        _, dW = brl.qat_linear_bwd(dY[b * mb:(b + 1) * mb], X[b * mb:(b + 1) * mb], W, synth.S_X,
+                                   need_dX=False, dW=dW, dW_accumulate=b > 0, tune=brl.Tuning(bwd_engine=engine))
     want = oracle.dw_rows(np.ascontiguousarray(inp.dY.T), inp.X, inp.W, synth.S_X, np.arange(N), mb=mb)
     assert_bitwise(dW, want, "dW (4 microbatches)")
 
@@ -375,22 +359,12 @@ def test_bwd_launch_shape_invariance():
     inp = _case_inputs(M, K, N, seed=51)
     wX, wW = oracle.linear_bwd(inp.dY, inp.X, inp.W, synth.S_X)
     X, W, dY = _cuda(inp.X), _cuda(inp.W), _cuda(inp.dY)
-    old_c = brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, 0)
-    old_r = brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, 0)
-    old_e = brl.set_tuning(brl.TUNE_BWD_ENGINE, 0)
-    try:
-        for e in ENGINES:
-            brl.set_tuning(brl.TUNE_BWD_ENGINE, e)
-            for c, r in [(1, 64), (2, 128), (3, 256), (4, 64), (5, 128), (6, 256), (7, 64)]:
-                brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, c)
-                brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, r)
-                dX, dW = brl.qat_linear_bwd(dY, X, W, synth.S_X)
-                assert_bitwise(dX, wX, f"dX chunk=2^{c} wg={r} engine={e}")
-                assert_bitwise(dW, wW, f"dW chunk=2^{c} wg={r} engine={e}")
-    finally:
-        brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, old_c)
-        brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, old_r)
-        brl.set_tuning(brl.TUNE_BWD_ENGINE, old_e)
+    for e in ENGINES:
+        for c, r in [(1, 64), (2, 128), (3, 256), (4, 64), (5, 128), (6, 256), (7, 64)]:
+            tune = brl.Tuning(bwd_chunk_log2=c, reduce_wg_blocks=r, bwd_engine=e)
+            dX, dW = brl.qat_linear_bwd(dY, X, W, synth.S_X, tune=tune)
+            assert_bitwise(dX, wX, f"dX chunk=2^{c} wg={r} engine={e}")
+            assert_bitwise(dW, wW, f"dW chunk=2^{c} wg={r} engine={e}")
 
 
 def test_repeat_runs_identical():
@@ -408,16 +382,16 @@ def test_repeat_runs_identical():
 
 
 # ---- replay -----------------------------------------------------------------------------
-def _replay_gpu(partials_np, R, S, max_norm=1.0, persist=False):
+def _replay_gpu(partials_np, R, S, max_norm=1.0, persist=False, tune=None):
     L = partials_np[0].size
-    st = brl.ReduceState(R, S, L, device=DEV, partials_persist=persist)
+    st = brl.ReduceState(R, S, L, device=DEV, partials_persist=persist, tune=tune)
     out = None
     keep = []      # with persist the shard-0 partials must outlive the shard-1 call
     for v in range(R * S):
         g = _cuda(partials_np[v])
         keep.append(g)
         out = brl.ordered_reduce(st, g)
-    nu = brl.grad_l2norm_clip(out, max_norm)
+    nu = brl.grad_l2norm_clip(out, max_norm, tune=tune)
     torch.cuda.synchronize()
     return out, nu, st
 
@@ -468,14 +442,9 @@ def test_norm_reduce_wg_invariance():
     n = 5_000_003
     g = np.random.default_rng(7).standard_normal(n).astype(np.float32)
     wnu = oracle.l2norm(g)
-    old = brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, 0)
-    try:
-        for wg in (64, 128, 256):
-            brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, wg)
-            nu = brl.grad_l2norm_clip(_cuda(g), 1e30)
-            assert_bitwise(nu, np.array([wnu]), f"nu wg={wg}")
-    finally:
-        brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, old)
+    for wg in (64, 128, 256):
+        nu = brl.grad_l2norm_clip(_cuda(g), 1e30, tune=brl.Tuning(reduce_wg_blocks=wg))
+        assert_bitwise(nu, np.array([wnu]), f"nu wg={wg}")
 
 
 @pytest.mark.parametrize("n, wg", [
@@ -491,12 +460,8 @@ def test_norm_tail_runs(n, wg):
     bits alone."""
     g = np.random.default_rng(n).standard_normal(n, dtype=np.float32)
     wnu = oracle.l2norm(g)
-    old = brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, wg)
-    try:
-        nu = brl.grad_l2norm_clip(_cuda(g), 1e30)
-        assert_bitwise(nu, np.array([wnu]), f"nu n={n} wg={wg}")
-    finally:
-        brl.set_tuning(brl.TUNE_REDUCE_WG_BLOCKS, old)
+    nu = brl.grad_l2norm_clip(_cuda(g), 1e30, tune=brl.Tuning(reduce_wg_blocks=wg))
+    assert_bitwise(nu, np.array([wnu]), f"nu n={n} wg={wg}")
 
 
 def test_replay_stream_shape_invariance():
@@ -505,12 +470,7 @@ def test_replay_stream_shape_invariance():
     R, S, L = 6, 3, 100_003
     parts = [synth.replay_partial_host(9, v, L, std=1e-2) for v in range(R * S)]
     T, wnu, _ = oracle.replay(parts, R, S)
-    old = brl.set_tuning(brl.TUNE_STREAM_VEC, 0)
-    try:
-        for vec in (1, 2, 4):
-            brl.set_tuning(brl.TUNE_STREAM_VEC, vec)
-            out, nu, _ = _replay_gpu(parts, R, S)
-            assert_bitwise(out, T, f"TreeFold vec={vec}")
-            assert_bitwise(nu, np.array([wnu]), f"nu vec={vec}")
-    finally:
-        brl.set_tuning(brl.TUNE_STREAM_VEC, old)
+    for vec in (1, 2, 4):
+        out, nu, _ = _replay_gpu(parts, R, S, tune=brl.Tuning(stream_vec=vec))
+        assert_bitwise(out, T, f"TreeFold vec={vec}")
+        assert_bitwise(nu, np.array([wnu]), f"nu vec={vec}")

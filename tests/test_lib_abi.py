@@ -3,6 +3,7 @@ include/brlsq.h declares, validates arguments before touching the device,
 and its gfx950 code contains no fused or packed fp32 arithmetic outside the
 correctly rounded division sequence.  No kernel is launched here."""
 import ctypes as C
+import subprocess
 import os
 import re
 
@@ -43,7 +44,7 @@ def test_workspace_query_is_host_only():
 def _fwd(M=4, K=4, N=4, s_x=0.05, X=1, W=1, Y=1, ws=1, ws_bytes=1 << 20, epi=0):
     L = brl.lib()
     p = lambda v: C.c_void_p(0x10000) if v else None
-    return L.qat_linear_fwd(p(X), p(W), M, K, N, s_x, None, epi, p(Y), None, None, p(ws), ws_bytes, None)
+    return L.qat_linear_fwd(p(X), p(W), M, K, N, s_x, None, epi, p(Y), None, None, p(ws), ws_bytes, None, None)
 
 
 def test_fwd_rejects_bad_arguments_without_launching():
@@ -64,10 +65,13 @@ def test_fwd_rejects_bad_arguments_without_launching():
 def test_bwd_rejects_bad_arguments_without_launching():
     L = brl.lib()
     p = C.c_void_p(0x10000)
-    assert L.qat_linear_bwd(p, p, p, None, 4, 4, 4, 0.05, 1, p, p, 0, p, 1 << 20, None) == brl.BRL_EINVAL
-    assert L.qat_linear_bwd(p, p, p, None, 4, 4, 4, 0.05, 0, p, p, 2, p, 1 << 20, None) == brl.BRL_EINVAL
-    assert L.qat_linear_bwd(p, p, p, None, 4, -4, 4, 0.05, 0, p, p, 0, p, 1 << 20, None) == brl.BRL_ESHAPE
-    assert L.qat_linear_bwd(p, p, p, None, 4, 4, 4, 0.05, 0, p, p, 0, p, 8, None) == brl.BRL_EWORKSPACE
+    assert L.qat_linear_bwd(p, p, p, None, 4, 4, 4, 0.05, 1, p, p, 0, p, 1 << 20, None, None) == brl.BRL_EINVAL
+    assert L.qat_linear_bwd(p, p, p, None, 4, 4, 4, 0.05, 0, p, p, 2, p, 1 << 20, None, None) == brl.BRL_EINVAL
+    assert L.qat_linear_bwd(p, p, p, None, 4, -4, 4, 0.05, 0, p, p, 0, p, 1 << 20, None, None) == brl.BRL_ESHAPE
+    assert L.qat_linear_bwd(p, p, p, None, 4, 4, 4, 0.05, 0, p, p, 0, p, 8, None, None) == brl.BRL_EWORKSPACE
+    # a workspace that is not 256-byte aligned
+    assert L.qat_linear_bwd(p, p, p, None, 4, 4, 4, 0.05, 0, p, p, 0, C.c_void_p(0x10010), 1 << 20, None,
+                            None) == brl.BRL_EINVAL
 
 
 def test_state_hash_rejects_bad_arguments_without_launching():
@@ -108,16 +112,63 @@ def test_reduce_state_order_is_enforced_on_the_host():
 def test_norm_rejects_bad_arguments():
     L = brl.lib()
     p = C.c_void_p(0x10000)
-    assert L.grad_l2norm_clip(p, 16, 0.0, 0.0, None, p, 1 << 20, None) == brl.BRL_EINVAL
-    assert L.grad_l2norm_clip(p, 16, 1.0, -1.0, None, p, 1 << 20, None) == brl.BRL_EINVAL
-    assert L.grad_l2norm_clip(p, -1, 1.0, 0.0, None, p, 1 << 20, None) == brl.BRL_ESHAPE
-    assert L.grad_l2norm_clip(p, 16, 1.0, 0.0, None, p, 4, None) == brl.BRL_EWORKSPACE
+    assert L.grad_l2norm_clip(p, 16, 0.0, 0.0, None, p, 1 << 20, None, None) == brl.BRL_EINVAL
+    assert L.grad_l2norm_clip(p, 16, 1.0, -1.0, None, p, 1 << 20, None, None) == brl.BRL_EINVAL
+    assert L.grad_l2norm_clip(p, -1, 1.0, 0.0, None, p, 1 << 20, None, None) == brl.BRL_ESHAPE
+    assert L.grad_l2norm_clip(p, 16, 1.0, 0.0, None, p, 4, None, None) == brl.BRL_EWORKSPACE
 
 
-def test_tuning_knobs():
-    old = brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, 3)
-    assert brl.set_tuning(brl.TUNE_BWD_CHUNK_LOG2, old) == 3
-    assert brl.set_tuning(9, 1) == -1
+def test_tuning_is_per_call_and_checked():
+    """Launch shapes travel with each call (no library state): bad values
+    fail the call before any launch, the workspace query follows the chunk
+    depth it is given, and a reduce state carries its own copy."""
+    L = brl.lib()
+    p = C.c_void_p(0x10000)
+    bad = [brl.Tuning(bwd_chunk_log2=8), brl.Tuning(bwd_chunk_log2=-1), brl.Tuning(reduce_wg_blocks=100),
+           brl.Tuning(stream_vec=3), brl.Tuning(bwd_engine=3)]
+    for t in bad:
+        assert L.qat_linear_bwd(p, p, p, None, 4, 4, 4, 0.05, 0, p, p, 0, p, 1 << 20, C.byref(t), None) \
+            == brl.BRL_EINVAL
+        assert L.qat_linear_fwd(p, p, 4, 4, 4, 0.05, None, 0, p, None, None, p, 1 << 20, C.byref(t), None) \
+            == brl.BRL_EINVAL
+        assert L.grad_l2norm_clip(p, 16, 1.0, 0.0, None, p, 1 << 20, C.byref(t), None) == brl.BRL_EINVAL
+        assert brl.workspace_bytes(brl.OP_BWD, 4096, 64, 4096, t) == 0
+    assert b"tuning" in L.brl_last_error()
+    d = brl.workspace_bytes(brl.OP_BWD, 4096, 64, 4096)
+    assert brl.workspace_bytes(brl.OP_BWD, 4096, 64, 4096, brl.Tuning(bwd_chunk_log2=1)) > d
+    assert brl.workspace_bytes(brl.OP_BWD, 4096, 64, 4096, brl.Tuning(bwd_chunk_log2=4)) == d
+    st = brl.ReduceStateC()
+    bufs = (C.c_void_p * 2)(*([0x10000] * 2))
+    assert L.brl_reduce_init(C.byref(st), 2, 2, 16, C.cast(bufs, C.c_void_p)) == brl.BRL_OK
+    assert (st.tune.bwd_chunk_log2, st.tune.reduce_wg_blocks, st.tune.stream_vec, st.tune.bwd_engine) == (0, 0, 0, 0)
+    st.tune.stream_vec = 3
+    assert L.ordered_reduce(C.byref(st), p, None, None) == brl.BRL_EINVAL
+    assert st.next == 0
+
+
+def test_library_holds_no_writable_state():
+    """The library's own writable symbols are only: the host handles of its
+    kernels (registered with the HIP runtime), two constant tables computed
+    once on first use (SHA-256 constants from integer roots) with their
+    initialisation guards, the host shadow of a read-only device constant,
+    and the calling thread's last-error message (thread-local).  No tuning
+    knob, cache or counter lives between calls."""
+    out = subprocess.run(["nm", "-C", "--defined-only", brl.LIB_PATH], capture_output=True, text=True).stdout
+    allowed = ("brl::sha_consts()::c", "brl::sha256_host(", "guard variable for brl::", "brl::kNegZero4",
+               "brl::g_err")
+    ours = []
+    for line in out.splitlines():
+        parts = line.split(maxsplit=2)
+        if len(parts) != 3 or parts[1] not in "bBdDvV" or "brl::" not in parts[2]:
+            continue
+        name = parts[2]
+        if "_kernel" in name and "(" in name:
+            continue
+        if not name.startswith(allowed):
+            ours.append(name)
+    assert ours == [], ours
+    tls = subprocess.run(["readelf", "-sW", brl.LIB_PATH], capture_output=True, text=True).stdout
+    assert [l.split()[-1] for l in tls.splitlines() if " TLS " in l] == ["_ZN3brlL5g_errE"]
 
 
 # ---- generated gfx950 code -------------------------------------------------------
