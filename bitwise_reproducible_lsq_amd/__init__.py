@@ -61,6 +61,7 @@ _SIGS = {
     "brl_reduce_init": (i32, [C.POINTER(ReduceStateC), i32, i32, i64, P]),
     "ordered_reduce": (i32, [C.POINTER(ReduceStateC), P, P, P]),
     "grad_l2norm_clip": (i32, [P, i64, f32, f32, P, P, sz, P, P]),
+    "grad_l2norm_clip_noalloc": (i32, [P, i64, f32, f32, P, P, P]),
     "brl_probe_f32": (i32, [i32, P, P, P, i64, P]),
     "brl_state_hash": (i32, [P, P, i32, P, P, sz, P]),
     "brl_adamw_scalars_for_step": (i32, [i64, C.c_double, P, P]),
@@ -250,6 +251,22 @@ def grad_l2norm_clip(g: torch.Tensor, max_norm: float = 1.0, eps: float = 0.0,
         ws = workspace(OP_NORM, n, 0, 0, g.device, tune, stream)
     _check(lib().grad_l2norm_clip(_ptr(g), n, float(max_norm), float(eps), _ptr(nu), _ptr(ws), ws.numel(),
                                   _tune(tune), _stream(stream)))
+    return nu
+
+
+NOALLOC_NORM_MAX_LEN = 1056565248
+
+
+def grad_l2norm_clip_noalloc(g: torch.Tensor, max_norm: float = 1.0, eps: float = 0.0, nu: Optional[torch.Tensor] = None,
+                             stream=None, tune: Optional[Tuning] = None) -> torch.Tensor:
+    """grad_l2norm_clip without a workspace (the library's per-device scratch
+    array; at most NOALLOC_NORM_MAX_LEN elements; calls overlapping on one
+    device race).  Returns the pre-clip norm in nu (allocated here if None)."""
+    n = g.numel()
+    if nu is None:
+        nu = torch.empty(1, dtype=torch.float32, device=g.device)
+    _check(lib().grad_l2norm_clip_noalloc(_ptr(g), n, float(max_norm), float(eps), _ptr(nu), _tune(tune),
+                                          _stream(stream)))
     return nu
 
 

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "internal.hpp"
 
 namespace brl {
@@ -444,6 +446,54 @@ brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float eps, fl
     if (!aligned256(ws)) return fail(BRL_EINVAL, "grad_l2norm_clip: workspace must be 256-byte aligned");
     if (!ws || ws_bytes < need)
         return fail(BRL_EWORKSPACE, "grad_l2norm_clip: workspace %zu < %zu bytes", ws_bytes, need);
+    return norm_clip_launch(g, len, max_norm, eps, norm_out, ws, tn, static_cast<hipStream_t>(stream));
+}
+
+// ---- the norm and clip without a caller workspace ---------------------------------
+// For callers that cannot allocate (graph capture, tight serving loops): the
+// squared-norm CanonSum's roots and the call's scalars live in `scratch`, a
+// file-scope device array of kNormScratchBytes that every device the library
+// runs on holds for the life of the process.  Its device address is taken once
+// per device with hipGetSymbolAddress (the array's name in host code is only a
+// host-side stand-in) and kept in g_scratch_dev.  Calls on one device share the
+// array: calls that overlap in time on one device race.  Nothing in it needs
+// clearing: every root and scalar is written before it is read in the call.
+constexpr size_t kNormScratchBytes = (size_t)2 << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) char scratch[kNormScratchBytes];
+static std::atomic<void*> g_scratch_dev[kScratchDevices];
+
+static brl_status scratch_for_current_device(void** out) {
+    int dev = -1;
+    if (const hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+        return check_hip(e, "grad_l2norm_clip_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(BRL_EDEVICE, "grad_l2norm_clip_noalloc: device %d beyond the %d the library tracks", dev,
+                    kScratchDevices);
+    void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess)
+            return check_hip(e, "grad_l2norm_clip_noalloc: hipGetSymbolAddress");
+        if (!p || !aligned256(p)) return fail(BRL_EDEVICE, "grad_l2norm_clip_noalloc: bad scratch address");
+        g_scratch_dev[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return BRL_OK;
+}
+
+brl_status grad_l2norm_clip_noalloc(float* g, int64_t len, float max_norm, float eps, float* norm_out,
+                                    const brl_tuning* tune, void* stream) {
+    Tuning tn;
+    if (!resolve_tuning(tune, &tn)) return fail(BRL_EINVAL, "grad_l2norm_clip_noalloc: tuning value out of range");
+    if (brl_status s = norm_clip_check("grad_l2norm_clip_noalloc", g, len, max_norm, eps, norm_out)) return s;
+    const size_t need = norm_bytes(len);
+    if (need > kNormScratchBytes)
+        return fail(BRL_ESHAPE,
+                    "grad_l2norm_clip_noalloc: len %lld needs %zu bytes of scratch, more than its %zu (at most "
+                    "%lld elements)",
+                    (long long)len, need, kNormScratchBytes, (long long)BRL_NOALLOC_NORM_MAX_LEN);
+    void* ws = nullptr;
+    if (brl_status s = scratch_for_current_device(&ws)) return s;
     return norm_clip_launch(g, len, max_norm, eps, norm_out, ws, tn, static_cast<hipStream_t>(stream));
 }
 

@@ -212,6 +212,22 @@ BRL_API brl_status grad_l2norm_clip(float* g, int64_t len, float max_norm, float
                             void* ws, size_t ws_bytes, const brl_tuning* tune, void* stream);
 
 /*
+ * grad_l2norm_clip_noalloc -- grad_l2norm_clip for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation and the same bits,
+ * with no workspace argument.  The call allocates nothing; its CanonSum roots
+ * and scalars live in a 2 MiB device array inside the library, one per device,
+ * held until the process ends, so len is limited to BRL_NOALLOC_NORM_MAX_LEN
+ * elements (a longer len returns BRL_ESHAPE and launches nothing).  The
+ * stream must belong to the calling thread's current device.  Every call on
+ * one device uses that device's array: calls that overlap in time on one
+ * device race, and must be ordered by the caller (one stream, or events).
+ */
+#define BRL_NOALLOC_NORM_MAX_LEN 1056565248LL
+BRL_API brl_status grad_l2norm_clip_noalloc(float* g, int64_t len, float max_norm, float eps, float* norm_out,
+                                            const brl_tuning* tune, void* stream);
+
+/*
  * brl_state_hash -- on-device hash of a training state (a list of tensors).
  * The pages store a hash of the state after every step and require a
  * replayed step to reproduce it; they name moving that hashing from the host

@@ -151,18 +151,21 @@ def test_library_holds_no_writable_state():
     kernels (registered with the HIP runtime), two constant tables computed
     once on first use (SHA-256 constants from integer roots) with their
     initialisation guards, the host shadow of a read-only device constant,
-    and the calling thread's last-error message (thread-local).  No tuning
-    knob, cache or counter lives between calls."""
+    the no-alloc norm's device scratch array with its per-device address
+    table (set once per device), and the calling thread's last-error message
+    (thread-local).  No tuning knob, cache or counter lives between calls."""
     out = subprocess.run(["nm", "-C", "--defined-only", brl.LIB_PATH], capture_output=True, text=True).stdout
+    runtime = ("__hip_", "_DYNAMIC", "_GLOBAL_OFFSET_TABLE_", "__dso_handle", "DW.ref.", "__do_init", "__do_fini",
+               "__init", "__fini", "completed.", "__TMC_END__", "__bss_start", "_edata", "_end")
     allowed = ("brl::sha_consts()::c", "brl::sha256_host(", "guard variable for brl::", "brl::kNegZero4",
-               "brl::g_err")
+               "brl::g_err", "scratch", "g_scratch_dev")
     ours = []
     for line in out.splitlines():
         parts = line.split(maxsplit=2)
-        if len(parts) != 3 or parts[1] not in "bBdDvV" or "brl::" not in parts[2]:
+        if len(parts) != 3 or parts[1] not in "bBdDvV":
             continue
         name = parts[2]
-        if "_kernel" in name and "(" in name:
+        if name.startswith(runtime) or ("_kernel" in name and "(" in name):
             continue
         if not name.startswith(allowed):
             ours.append(name)
@@ -308,3 +311,19 @@ def test_attention_rejects_bad_arguments_without_launching():
     assert kvcall(dV=None) == brl.BRL_EINVAL
     assert kvcall(dV=C.c_void_p(0x10004)) == brl.BRL_EINVAL
     assert kvcall(S=0) == brl.BRL_OK           # nothing to do, nothing launched
+
+
+def test_noalloc_norm_rejects_before_any_device_call():
+    """The no-alloc norm checks its arguments and the length bound of its
+    scratch array on the host, before it touches a device."""
+    L = brl.lib()
+    p = C.c_void_p(0x10000)
+    assert L.grad_l2norm_clip_noalloc(p, brl.NOALLOC_NORM_MAX_LEN + 1, 1.0, 0.0, None, None, None) == brl.BRL_ESHAPE
+    assert b"scratch" in L.brl_last_error()
+    assert L.grad_l2norm_clip_noalloc(p, 16, 0.0, 0.0, None, None, None) == brl.BRL_EINVAL
+    assert L.grad_l2norm_clip_noalloc(p, -1, 1.0, 0.0, None, None, None) == brl.BRL_ESHAPE
+    t = brl.Tuning(stream_vec=3)
+    assert L.grad_l2norm_clip_noalloc(p, 16, 1.0, 0.0, None, C.byref(t), None) == brl.BRL_EINVAL
+    # the bound is the longest length whose roots and scalars fit the 2 MiB array
+    assert brl.workspace_bytes(brl.OP_NORM, brl.NOALLOC_NORM_MAX_LEN, 0, 0) <= 2 << 20
+    assert brl.workspace_bytes(brl.OP_NORM, brl.NOALLOC_NORM_MAX_LEN + 1, 0, 0) > 2 << 20
