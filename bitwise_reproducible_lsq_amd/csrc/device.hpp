@@ -4,10 +4,12 @@
 // order, multiply and add never fused, subnormals flushed to zero.  The
 // kernels are compiled with the f32 denormal mode "flush inputs and outputs"
 // and contraction off, so a plain `a + b` / `a * b` is one v_add_f32 /
-// v_mul_f32 that rounds to nearest even and flushes.  Division and square
-// root go through binary64 (correctly rounded there, and 53 >= 2*24+2 makes
-// the second rounding to binary32 innocuous) with explicit flushing on both
-// sides, so no fp32 fused multiply-add appears anywhere in the library.
+// v_mul_f32 that rounds to nearest even and flushes.  Division is the
+// compiler's correctly rounded binary32 sequence (the only place where an fp32
+// multiply-add appears: inside it, between v_div_scale_f32 and
+// v_div_fixup_f32); square root goes through binary64 (correctly rounded
+// there, and 53 >= 2*24+2 makes the second rounding to binary32 innocuous)
+// with explicit flushing on both sides.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -38,10 +40,12 @@ __device__ __forceinline__ float f_add(float a, float b) { return a + b; }
 __device__ __forceinline__ float f_sub(float a, float b) { return a - b; }
 __device__ __forceinline__ float f_mul(float a, float b) { return a * b; }
 
-__device__ __forceinline__ float f_div(float a, float b) {
-    double q = (double)flush_f32(a) / (double)flush_f32(b);
-    return flush_f32((float)q);
-}
+// One correctly rounded binary32 division.  In the flush mode its operands
+// read subnormals as zeros of the same sign and a subnormal quotient is
+// flushed; a quotient of two binary32 values never falls strictly between
+// 2^-126 (1 - 2^-24) and 2^-126, the band where flushing before and after
+// rounding would differ, so the result is the one f_div of binary64 gives.
+__device__ __forceinline__ float f_div(float a, float b) { return a / b; }
 
 // a / b for a divisor b fixed across many calls, given rb = fl64(1/flush(b)):
 // the same correctly rounded binary32 quotient as f_div (see Quantizer below

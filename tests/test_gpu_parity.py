@@ -474,3 +474,36 @@ def test_replay_stream_shape_invariance():
         out, nu, _ = _replay_gpu(parts, R, S, tune=brl.Tuning(stream_vec=vec))
         assert_bitwise(out, T, f"TreeFold vec={vec}")
         assert_bitwise(nu, np.array([wnu]), f"nu vec={vec}")
+
+
+def test_division_on_crafted_classes():
+    """The device's binary32 division (the compiler's correctly rounded
+    sequence) equals the oracle's binary64-then-rounded quotient on classes
+    aimed at its corners: random bit patterns over the whole exponent range,
+    quotients around 2^-126 (the flush threshold), subnormal operands and
+    zeros of both signs, quotients near overflow, and exact quotients."""
+    g = np.random.default_rng(11)
+    n = 1 << 15
+    sign = lambda: g.integers(0, 2, n, dtype=np.uint32) << 31
+    man = lambda: g.integers(0, 1 << 23, n, dtype=np.uint32)
+    classes = []
+    ea = g.integers(1, 255, n, dtype=np.uint32); eb = g.integers(1, 255, n, dtype=np.uint32)
+    classes.append((sign() | (ea << 23) | man(), sign() | (eb << 23) | man()))
+    ea = g.integers(1, 100, n, dtype=np.uint32); eb = ea + 126 + g.integers(-2, 2, n).astype(np.uint32)
+    classes.append((sign() | (ea << 23) | man(), sign() | (np.minimum(eb, 254) << 23) | man()))
+    sub = g.integers(0, 3, n)
+    a_bits = np.where(sub == 0, sign() | man(), sign() | (np.uint32(127) << 23) | man()).astype(np.uint32)
+    b_bits = np.where(sub == 1, sign() | man(), np.where(sub == 2, sign(), sign() | (np.uint32(127) << 23) | man()))
+    classes.append((a_bits, b_bits.astype(np.uint32)))
+    ea = g.integers(200, 255, n, dtype=np.uint32); eb = g.integers(1, 60, n, dtype=np.uint32)
+    classes.append((sign() | (ea << 23) | man(), sign() | (eb << 23) | man()))
+    q = (g.integers(1, 1 << 12, n) * 2).astype(np.float32)
+    d = g.integers(1, 1 << 11, n).astype(np.float32)
+    classes.append(((q * d).astype(np.float32).view(np.uint32), d.view(np.uint32)))
+    for ci, (ab, bb) in enumerate(classes):
+        a, b = ab.view(np.float32), bb.view(np.float32)
+        got = brl.probe_f32("div", _cuda(a), _cuda(b)).cpu().numpy()
+        want = np.array([oracle.div(x, y) for x, y in zip(a, b)], np.float32)
+        nan = np.isnan(got) & np.isnan(want)
+        bad = np.flatnonzero((_bits(got) != _bits(want)) & ~nan)
+        assert bad.size == 0, (ci, [(a[i], b[i], got[i], want[i]) for i in bad[:5]])
