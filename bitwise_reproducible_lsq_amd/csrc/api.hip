@@ -232,6 +232,7 @@ brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, 
     FwdLayout L = fwd_layout(ws, M, K, N, epilogue);
     hipStream_t st = static_cast<hipStream_t>(stream);
 
+    const int64_t swiglu_half = epilogue == BRL_EPILOGUE_SWIGLU ? N / 2 : 0;
     CanonFinishArgs fin{};
     fin.mode = kFinishScale;
     fin.count_f = (float)(double)(N * K);
@@ -240,8 +241,7 @@ brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, 
     fin.s_w_out = s_w_out;
     brl_status s = check_hip(launch_canon(kMapAbs, W, N * K, L.partials, fin, tn.wg_blocks, st), "weight step");
     if (s || M == 0) return s;
-    s = check_hip(launch_quantize(W, N, K, &L.scal->s_w, 0.0f, L.qw, L.Nvp, L.Kp,
-                                  epilogue == BRL_EPILOGUE_SWIGLU ? N / 2 : 0, st), "quantize W");
+    s = check_hip(launch_quantize(W, N, K, &L.scal->s_w, 0.0f, L.qw, L.Nvp, L.Kp, swiglu_half, st), "quantize W");
     if (s) return s;
     s = check_hip(launch_quantize(X, M, K, nullptr, s_x, L.qx, L.Mp, L.Kp, 0, st), "quantize X");
     if (s) return s;

@@ -440,16 +440,23 @@ __global__ __launch_bounds__(256) void ste_finish_kernel(SteArgs a, int64_t Q) {
     }
     T root;
     stack_final<T, 0, kFinishLevels>(st, (unsigned)Q, root, false);
-    // one quantiser per thread (its binary64 reciprocal is formed once);
-    // 16-byte mask loads and output stores when both tensors allow them
+    // one quantiser per thread (its reciprocals are formed once); the mask on
+    // the fast path, redone on the exact one for a wave with a value whose
+    // quotient lies near +-127; 16-byte mask loads and output stores when
+    // both tensors allow them
     const Quantizer qz(a.mask_scale_dev ? *a.mask_scale_dev : a.mask_scale_host);
     const bool vec = V == 4 && ((reinterpret_cast<uintptr_t>(a.mask_src) | reinterpret_cast<uintptr_t>(a.out)) & 15) == 0;
     if constexpr (V == 4) {
         if (vec) {
             const vf4 x = *reinterpret_cast<const vf4*>(a.mask_src + idx);
             vf4 o;
+            bool unsure = false;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = qz.in_range(x[e]) ? root[e] : 0.0f;
+            for (int e = 0; e < 4; ++e) o[e] = qz.in_range_fast(x[e], &unsure) ? root[e] : 0.0f;
+            if (__ballot(unsure)) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = qz.in_range(x[e]) ? root[e] : 0.0f;
+            }
             if (a.accumulate) {
                 const vf4 prev = *reinterpret_cast<const vf4*>(a.out + idx);
 #pragma unroll

@@ -26,8 +26,7 @@ __device__ __forceinline__ float canon_map(float v) {
 
 __device__ void canon_finish(float S, const CanonFinishArgs& f) {
     if (f.mode == kFinishScale) {
-        float mu = f_div(S, f.count_f);
-        float s_w = f_div(f_mul(2.0f, mu), f_sqrt((float)kQmax));
+        const float s_w = weight_step(S, f.count_f);
         f.scal->s_w = s_w;
         f.scal->s_y = f_mul(f.s_x, s_w);
         if (f.s_w_out) *f.s_w_out = s_w;

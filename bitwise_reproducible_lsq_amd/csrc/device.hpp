@@ -63,18 +63,31 @@ __device__ __forceinline__ float f_rne(float t) { return __builtin_rintf(t); }
 
 // LSQ quantiser with step s: q = clamp(rne(v/s), -127, 127),
 // in = (-127 <= v/s <= 127); a zero step maps everything to q = 0, in range.
-// The quotient comes from the binary64 reciprocal of the step:
+//
+// Exact path.  The quotient comes from the binary64 reciprocal of the step:
 // fl32(fl64(v * fl64(1/s))) is the correctly rounded binary32 v/s.  The
 // binary64 product is within 2^-51.9 (relative) of v/s, while the exact
 // quotient of two binary32 numbers that is not itself a rounding boundary
 // is at least 2^-49 (relative) away from every one of them: the midpoints
 // between neighbouring binary32 values and the underflow threshold.  So the
 // product lies in the same rounding interval as v/s.
+//
+// Fast path.  t = v * fl32(1/s) in binary32 is within 3 * 2^-24 |v/s| of the
+// correctly rounded quotient T (two roundings in t, one in T).  For |v/s| <=
+// 128 that is under 2^-15, so when t lies at least 2^-15 from every midpoint
+// k + 1/2 (the points where rne changes), T lies strictly on the same side of
+// each of them and rne(T) = rne(t); likewise for the range test when t lies
+// at least 2^-15 from +-127.  Above 128 in magnitude both give the clamped
+// code and an out-of-range mask (and the 2^-15 test is only conservative).
+// The fast forms report `unsure` when t is closer than that; callers then
+// redo their values on the exact path (a wave at a time: about 1 in 16000
+// uniformly placed quotients is unsure).  Subnormal v reads as zero in both.
 struct Quantizer {
     float s;
     double rs;
+    float rf;
     __device__ __forceinline__ explicit Quantizer(float step)
-        : s(flush_f32(step)), rs(s == 0.0f ? 0.0 : 1.0 / (double)s) {}
+        : s(flush_f32(step)), rs(s == 0.0f ? 0.0 : 1.0 / (double)s), rf(s == 0.0f ? 0.0f : 1.0f / s) {}
     __device__ __forceinline__ float quotient(float v) const {
         return flush_f32((float)((double)flush_f32(v) * rs));
     }
@@ -92,7 +105,29 @@ struct Quantizer {
         const float t = quotient(v);
         return (t >= -(float)kQmax) && (t <= (float)kQmax);
     }
+    // q(v) when *unsure stays false; sets *unsure (never clears it) otherwise
+    __device__ __forceinline__ int q_fast(float v, bool* unsure) const {
+        const float t = v * rf;                  // s == 0: rf = 0, t = 0, q = 0
+        const float r = f_rne(t);
+        *unsure |= __builtin_fabsf(t - r) > 0.5f - 0x1p-15f;
+        float c = r > (float)kQmax ? (float)kQmax : r;
+        c = c < -(float)kQmax ? -(float)kQmax : c;
+        return (int)c;
+    }
+    // in_range(v) when *unsure stays false; sets *unsure otherwise
+    __device__ __forceinline__ bool in_range_fast(float v, bool* unsure) const {
+        const float t = v * rf;
+        *unsure |= __builtin_fabsf(__builtin_fabsf(t) - (float)kQmax) < 0x1p-15f;
+        return s == 0.0f || __builtin_fabsf(t) <= (float)kQmax;
+    }
 };
+
+// The weight step from S = CanonSum(|w|) over `count` weights:
+// s_w = (2 * (S / fl(count))) / fl(sqrt(127)).
+__device__ __forceinline__ float weight_step(float S, float count_f) {
+    const float mu = f_div(S, count_f);
+    return f_div(f_mul(2.0f, mu), f_sqrt((float)kQmax));
+}
 
 // ---- the library's own binary32 exp (SwiGLU) ------------------------------
 // E(x): Cody-Waite reduction x = k*ln2 + r with k = rne(x * log2(e)), ln2

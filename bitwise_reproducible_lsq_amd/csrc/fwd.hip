@@ -42,16 +42,15 @@ __device__ __forceinline__ int64_t quantize_src_row(int64_t ro, int64_t rows, in
     return ro;
 }
 
-__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ v, int64_t rows,
-                                                       int64_t cols, const float* __restrict__ s_dev,
-                                                       float s_host, int8_t* __restrict__ q,
-                                                       int64_t rows_p, int64_t cols_p,
-                                                       int64_t swiglu_half) {
-    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+// The quantiser's work of block (bx, by) of a (., gy) grid.
+__device__ __forceinline__ void quantize_part(const float* __restrict__ v, int64_t rows, int64_t cols,
+                                              const Quantizer& qz, int8_t* __restrict__ q, int64_t rows_p,
+                                              int64_t cols_p, int64_t swiglu_half, int64_t bx, int64_t by,
+                                              int64_t gy) {
+    const int64_t c0 = (bx * 256 + threadIdx.x) * 4;
     if (c0 >= cols_p) return;
-    const Quantizer qz(s_dev ? *s_dev : s_host);
     const bool vec = ((cols & 3) == 0) && ((reinterpret_cast<uintptr_t>(v) & 15) == 0) && c0 + 4 <= cols;
-    for (int64_t rb = (int64_t)blockIdx.y * kQRows; rb < rows_p; rb += (int64_t)gridDim.y * kQRows) {
+    for (int64_t rb = by * kQRows; rb < rows_p; rb += gy * kQRows) {
         vf4 x[kQRows];
         bool ok[kQRows];
 #pragma unroll
@@ -70,21 +69,46 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
                     if (c0 + e < cols) x[u][e] = src[c0 + e];
             }
         }
+        // codes on the fast path; a wave with any value near a rounding
+        // midpoint redoes all of its values on the exact path
+        uint32_t packed[kQRows];
+        bool unsure = false;
 #pragma unroll
         for (int u = 0; u < kQRows; ++u) {
-            if (rb + u >= rows_p) break;
-            uint32_t packed = 0;
-            if (ok[u]) {
+            packed[u] = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int qv = (ok[u] && c0 + e < cols) ? qz.q_fast(x[u][e], &unsure) : 0;
+                packed[u] |= (uint32_t)(uint8_t)(int8_t)qv << (8 * e);
+            }
+        }
+        if (__ballot(unsure)) {
+#pragma unroll
+            for (int u = 0; u < kQRows; ++u) {
+                packed[u] = 0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     bool in;
-                    const int qv = (c0 + e < cols) ? qz.q(x[u][e], &in) : 0;
-                    packed |= (uint32_t)(uint8_t)(int8_t)qv << (8 * e);
+                    const int qv = (ok[u] && c0 + e < cols) ? qz.q(x[u][e], &in) : 0;
+                    packed[u] |= (uint32_t)(uint8_t)(int8_t)qv << (8 * e);
                 }
             }
-            *reinterpret_cast<uint32_t*>(q + (rb + u) * cols_p + c0) = packed;
+        }
+#pragma unroll
+        for (int u = 0; u < kQRows; ++u) {
+            if (rb + u >= rows_p) break;
+            *reinterpret_cast<uint32_t*>(q + (rb + u) * cols_p + c0) = packed[u];
         }
     }
+}
+
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ v, int64_t rows,
+                                                       int64_t cols, const float* __restrict__ s_dev,
+                                                       float s_host, int8_t* __restrict__ q,
+                                                       int64_t rows_p, int64_t cols_p,
+                                                       int64_t swiglu_half) {
+    const Quantizer qz(s_dev ? *s_dev : s_host);
+    quantize_part(v, rows, cols, qz, q, rows_p, cols_p, swiglu_half, blockIdx.x, blockIdx.y, gridDim.y);
 }
 
 hipError_t launch_quantize(const float* v, int64_t rows, int64_t cols, const float* s_dev,
@@ -111,21 +135,26 @@ __global__ __launch_bounds__(256) void dequant_kernel(const float* __restrict__ 
     const Quantizer qz(s);
     const bool vec_rows = ((cols & 3) == 0) && ((reinterpret_cast<uintptr_t>(v) & 15) == 0);
     for (int64_t r = blockIdx.y; r < rows_p; r += gridDim.y) {
-        vf4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+        vf4 x = {0.0f, 0.0f, 0.0f, 0.0f};
         if (r < rows) {
             const float* src = v + r * cols;
-            bool in;
             if (vec_rows && c0 + 4 <= cols) {
-                const vf4 x = *reinterpret_cast<const vf4*>(src + c0);
-                o.x = f_mul((float)qz.q(x.x, &in), s);
-                o.y = f_mul((float)qz.q(x.y, &in), s);
-                o.z = f_mul((float)qz.q(x.z, &in), s);
-                o.w = f_mul((float)qz.q(x.w, &in), s);
+                x = *reinterpret_cast<const vf4*>(src + c0);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (c0 + e < cols) o[e] = f_mul((float)qz.q(src[c0 + e], &in), s);
+                    if (c0 + e < cols) x[e] = src[c0 + e];
             }
+        }
+        // zeros past the data quantise to 0 and dequantise to +0
+        vf4 o;
+        bool unsure = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = f_mul((float)qz.q_fast(x[e], &unsure), s);
+        if (__ballot(unsure)) {
+            bool in;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = f_mul((float)qz.q(x[e], &in), s);
         }
         *reinterpret_cast<vf4*>(out + r * cols_p + c0) = o;
     }
