@@ -1,6 +1,8 @@
 """Parity at the full workload sizes, in the launch configuration bench.py
-times, against the oracle on sampled outputs it can compute one by one
-(rows of Y and dX, rows of dW) -- and for the replay, on every element.
+times, against the oracle: every element of the forward's outputs (Y, and
+Ypre with the SwiGLU activation), one row of dX in every 64-row tile (the
+rows at tile, workgroup and microbatch edges included) and one row of dW in
+every 64-row tile of W -- and for the replay, every element.
 
 Workloads (seeded, synthetic; shapes of the Open-1B recipe on the onedev.kr
 summary, "Use" and "Limits": 16,384 tokens per GPU microbatch, GQA with 16
@@ -52,7 +54,21 @@ def _cuda(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-TILE_EDGES_M = [0, 1, 63, 64, 255, 256, 4095, 4096, 8191, 16383]
+TILE_EDGES_M = [0, 1, 63, 64, 255, 256, 4095, 4096, 8191, 8192, 12287, 12288, 16383]
+
+
+def _per_tile(n, edges, seed, tile=64):
+    """One row in every `tile` rows (its position varying from tile to tile)
+    plus the given edge rows."""
+    g = np.random.default_rng(seed)
+    s = set(e for e in edges if 0 <= e < n)
+    for t0 in range(0, n, tile):
+        s.add(int(t0 + g.integers(0, min(tile, n - t0))))
+    return np.array(sorted(s), np.int64)
+
+
+def _all_rows(case):
+    return np.arange(case.M, dtype=np.int64)
 
 
 def test_qkv_full_size():
@@ -64,10 +80,10 @@ def test_qkv_full_size():
     torch.cuda.synchronize()
     w_sw = oracle.weight_scale(inp.W)
     assert_bitwise(s_w, np.array([w_sw]), "s_w")
-    rows = _sample(case.M, TILE_EDGES_M, 8, 1)
-    assert_bitwise(Y[rows], oracle.fwd_rows(inp.X, inp.W, case.s_x, rows=rows, s_w=w_sw), "Y rows")
+    assert_bitwise(Y, oracle.fwd_rows(inp.X, inp.W, case.s_x, rows=_all_rows(case), s_w=w_sw), "Y (every row)")
+    rows = _per_tile(case.M, TILE_EDGES_M, 1)
     assert_bitwise(dX[rows], oracle.dx_rows(inp.dY[rows], inp.X, inp.W, case.s_x, rows, s_w=w_sw), "dX rows")
-    wr = _sample(case.N, [0, 1, 2047, 2048, 2559, 2560, 3071], 5, 2)
+    wr = _per_tile(case.N, [0, 1, 2047, 2048, 2559, 2560, 3071], 2)
     want = oracle.dw_rows(np.ascontiguousarray(inp.dY[:, wr].T), inp.X, inp.W, case.s_x, wr, s_w=w_sw)
     assert_bitwise(dW[wr], want, "dW rows")
 
@@ -82,21 +98,25 @@ def test_swiglu_gate_up_full_size():
     torch.cuda.synchronize()
     w_sw = oracle.weight_scale(inp.W)
     assert_bitwise(s_w, np.array([w_sw]), "s_w")
-    rows = _sample(case.M, TILE_EDGES_M, 4, 3)
-    wA, wPre = oracle.fwd_rows(inp.X, inp.W, case.s_x, rows=rows, epilogue=1, s_w=w_sw)
-    assert_bitwise(Ypre[rows], wPre, "Ypre rows")
-    assert_bitwise(A[rows], wA, "SwiGLU rows")
-    G_rows = oracle.swiglu_bwd(wPre, inp.dY[rows])
+    wA, wPre = oracle.fwd_rows(inp.X, inp.W, case.s_x, rows=_all_rows(case), epilogue=1, s_w=w_sw)
+    assert_bitwise(Ypre, wPre, "Ypre (every row)")
+    assert_bitwise(A, wA, "SwiGLU activation (every row)")
+    rows = _per_tile(case.M, TILE_EDGES_M, 3)
+    G_rows = oracle.swiglu_bwd(wPre[rows], inp.dY[rows])
     assert_bitwise(dX[rows], oracle.dx_rows(G_rows, inp.X, inp.W, case.s_x, rows, s_w=w_sw), "dX rows")
-    js = _sample(H, [0, 63, 64, 5631], 2, 4)
+    # dW rows n and n + H need the gate and up columns j = n of the
+    # pre-activation over all M rows (the oracle's own, from above)
+    js = _per_tile(H, [0, 63, 64, 5631], 4)
     cols = np.concatenate([js, js + H])
-    Yc = oracle.fwd_cols(inp.X, inp.W, case.s_x, cols, s_w=w_sw)          # [2J, M]
-    Gc = []
+    pair_cols = np.ascontiguousarray(wPre[:, cols])                    # [M, 2J]: gate cols, then up cols
+    dY_cols = []
+    G_gate, G_up = [], []
     for t, j in enumerate(js):
-        pair = np.ascontiguousarray(np.stack([Yc[t], Yc[t + len(js)]], axis=1))   # [M, 2] = (g, u)
+        pair = np.ascontiguousarray(np.stack([pair_cols[:, t], pair_cols[:, t + len(js)]], axis=1))   # (g, u)
         d = oracle.swiglu_bwd(pair, np.ascontiguousarray(inp.dY[:, j:j + 1]))
-        Gc.append((d[:, 0].copy(), d[:, 1].copy()))
-    dY_cols = np.stack([g for g, _ in Gc] + [u for _, u in Gc])
+        G_gate.append(d[:, 0].copy())
+        G_up.append(d[:, 1].copy())
+    dY_cols = np.stack(G_gate + G_up)
     want = oracle.dw_rows(dY_cols, inp.X, inp.W, case.s_x, cols, s_w=w_sw)
     assert_bitwise(dW[cols], want, "dW rows (gate and up)")
 
@@ -116,10 +136,10 @@ def test_down_proj_full_size_microbatches():
     torch.cuda.synchronize()
     w_sw = oracle.weight_scale(inp.W)
     assert (np.abs(inp.X / case.s_x) > 127).any(), "some activations should clip"
-    rows = _sample(case.M, TILE_EDGES_M, 6, 5)
-    assert_bitwise(Y[rows], oracle.fwd_rows(inp.X, inp.W, case.s_x, rows=rows, s_w=w_sw), "Y rows")
+    assert_bitwise(Y, oracle.fwd_rows(inp.X, inp.W, case.s_x, rows=_all_rows(case), s_w=w_sw), "Y (every row)")
+    rows = _per_tile(case.M, TILE_EDGES_M, 5)
     assert_bitwise(dX[rows], oracle.dx_rows(inp.dY[rows], inp.X, inp.W, case.s_x, rows, s_w=w_sw), "dX rows")
-    wr = _sample(case.N, [0, 1, 2047], 3, 6)
+    wr = _per_tile(case.N, [0, 1, 2047], 6)
     want = oracle.dw_rows(np.ascontiguousarray(inp.dY[:, wr].T), inp.X, inp.W, case.s_x, wr, mb=mb, s_w=w_sw)
     assert_bitwise(dW[wr], want, "dW rows (4 microbatches)")
 
