@@ -2,13 +2,22 @@
 reduction on one MI355X.
 
 One step = the whole hot path on synthetic inputs already resident in HBM:
-  (1) qat_linear_fwd + qat_linear_bwd of the attention QKV projection
-      (GQA 16 query / 4 KV heads of 128: X [16384, 2048], W [3072, 2048],
-      dY [16384, 3072], seed 1), and
+  (1) qat_linear_fwd + qat_linear_bwd of the three linear layers of one
+      Open-1B block at the per-GPU microbatch of 16384 tokens:
+        - attention QKV projection (GQA 16 query / 4 KV heads of 128):
+          X [16384, 2048], W [3072, 2048], dY [16384, 3072], seed 1;
+        - SwiGLU gate+up projection with its activation: X [16384, 2048],
+          W [11264, 2048] (gate and up stacked), dA [16384, 5632], seed 2;
+        - down projection: H [16384, 5632], W [2048, 5632], dY [16384,
+          2048], seed 3, backward over 4 microbatches of 4096 rows with dW
+          accumulated in ascending order (the forward is row by row, so it
+          runs as one call);
   (2) the single-device replay of one step's gradient reduction: 48 virtual
       ranks (6 replicas x 8 shards) of 201,326,592 fp32 each, fed in mesh
       order to ordered_reduce, then grad_l2norm_clip (max norm 1.0).
-value = fwd+bwd int8-QAT linear throughput in TOPS (6*M*N*K ops / time);
+value = fwd+bwd int8-QAT linear throughput of the three layers in TOPS
+(sum of 6*M*N*K over the layers / their time); per-layer figures, each
+phase against its roofline, are under "configs".
 ordered_reduce_GBps = algorithmic replay bytes / replay time.
 
 Prints one JSON line.  --gpus above 1 is refused (one GPU).
@@ -60,6 +69,8 @@ ADAMW_BYTES_PER_ELEM = 28                                   # 8 x 805 MB = 6.44 
 # the scale), counted once per (row, allowed key); the int8 P.V product is on
 # the matrix cores and small beside them.
 ATTN_D = 128
+# the linear layers of one step (names of synth.CASES), in the order they run
+LAYERS = ("qkv", "swiglu_gate_up", "down_proj")
 
 
 def stream_bench(torch, brl, dev, with_cpu: bool):
@@ -257,37 +268,59 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    case = synth.CASES["qkv"]
     rcase = synth.REPLAY
     L = args.replay_length or rcase.length
     R, S = rcase.replicas, rcase.shards
-    M, K, N = case.M, case.K, case.N
 
     # ---- inputs, resident before timing ------------------------------------------
-    inp = synth.linear_inputs(case)
-    X = torch.from_numpy(inp.X).to(dev)
-    W = torch.from_numpy(inp.W).to(dev)
-    dY = torch.from_numpy(inp.dY).to(dev)
+    layers = []
+    for name in LAYERS:
+        case = synth.CASES[name]
+        inp = synth.linear_inputs(case)
+        M, K, N = case.M, case.K, case.N
+        epi = brl.EPILOGUE_SWIGLU if case.swiglu else brl.EPILOGUE_NONE
+        lay = {"name": name, "case": case, "inp": inp, "M": M, "K": K, "N": N, "epi": epi,
+               "mb": case.microbatches,
+               "X": torch.from_numpy(inp.X).to(dev), "W": torch.from_numpy(inp.W).to(dev),
+               "dY": torch.from_numpy(inp.dY).to(dev),
+               "Y": torch.empty((M, N // 2 if case.swiglu else N), dtype=torch.float32, device=dev),
+               "Ypre": torch.empty((M, N), dtype=torch.float32, device=dev) if case.swiglu else None,
+               "dX": torch.empty((M, K), dtype=torch.float32, device=dev),
+               "dW": torch.empty((N, K), dtype=torch.float32, device=dev),
+               "ws_f": brl.workspace(brl.OP_FWD, M, K, N, dev),
+               "ws_b": brl.workspace(brl.OP_BWD, M // case.microbatches, K, N, dev)}
+        layers.append(lay)
     partials = [synth.replay_partial(rcase, v, device=dev, length=L) for v in range(R * S)]
     # all partials stay resident, so each replica's first two shards combine in one pass
     state = brl.ReduceState(R, S, L, device=dev, partials_persist=True)
     out = torch.empty(L, dtype=torch.float32, device=dev)
-    ws_f = brl.workspace(brl.OP_FWD, M, K, N, dev)
-    ws_b = brl.workspace(brl.OP_BWD, M, K, N, dev)
     ws_n = brl.workspace(brl.OP_NORM, L, 0, 0, dev)
-    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    dX = torch.empty((M, K), dtype=torch.float32, device=dev)
-    dW = torch.empty((N, K), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     timer = Timer(torch)
 
+    def fwd(lay):
+        brl.qat_linear_fwd(lay["X"], lay["W"], synth.S_X, epilogue=lay["epi"], Y=lay["Y"], ws=lay["ws_f"],
+                           Ypre=lay["Ypre"])
+
+    def bwd(lay, need_dX=True, need_dW=True):
+        M, mb = lay["M"], lay["mb"]
+        rows = M // mb
+        for b in range(mb):
+            sl = slice(b * rows, (b + 1) * rows)
+            brl.qat_linear_bwd(lay["dY"][sl], lay["X"][sl], lay["W"], synth.S_X,
+                               Ypre=lay["Ypre"][sl] if lay["Ypre"] is not None else None, epilogue=lay["epi"],
+                               need_dX=need_dX, need_dW=need_dW,
+                               dX=lay["dX"][sl] if need_dX else None, dW=lay["dW"] if need_dW else None,
+                               dW_accumulate=need_dW and b > 0, ws=lay["ws_b"])
+
     def step(timed: bool):
         with timer.region("linear"):
-            with timer.region("fwd"):
-                brl.qat_linear_fwd(X, W, synth.S_X, Y=Y, ws=ws_f)
-            with timer.region("bwd"):
-                brl.qat_linear_bwd(dY, X, W, synth.S_X, dX=dX, dW=dW, ws=ws_b)
+            for lay in layers:
+                with timer.region(lay["name"] + ".fwd"):
+                    fwd(lay)
+                with timer.region(lay["name"] + ".bwd"):
+                    bwd(lay)
         state.reset()
         with timer.region("replay"):
             for r in range(R):
@@ -321,15 +354,13 @@ def main():
 
     K_ = args.steps
     lin_ms = timer.ms("linear")[0] / K_
-    fwd_ms = timer.ms("fwd")[0] / K_
-    bwd_ms = timer.ms("bwd")[0] / K_
     rep_ms = timer.ms("replay")[0] / K_
     acc_ms = timer.ms("accumulate")[0]
     acc_n = timer.counts.get("accumulate_launches", 0)
     nc_ms = timer.ms("norm_clip")[0] / K_
     acc_avg_ms = acc_ms / max(acc_n, 1)
 
-    # phase split of the backward (separate, after the timed steps)
+    # phase split of each layer (separate, after the timed steps)
     def avg_call(fn, reps=3):
         fn()
         torch.cuda.synchronize()
@@ -342,24 +373,44 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    # AdamW over the reduced, clipped gradient (L parameters; p, m, v synthetic)
-    ap = synth.replay_partial(rcase, 100, device=dev, length=L)
-    am = torch.zeros(L, dtype=torch.float32, device=dev)
-    av = torch.zeros(L, dtype=torch.float32, device=dev)
-    asc = brl.adamw_scalars_for_step(1000, 3.0e9)
-    adamw_ms = avg_call(lambda: brl.adamw_step(ap, out, am, av, asc), reps=3)
-    adamw_gbps = ADAMW_BYTES_PER_ELEM * L / (adamw_ms * 1e-3) / 1e9
-    del ap, am, av
-    # state hash of a 6.44 GB state (the first 8 replay partials as its tensors)
-    hstate = partials[:HASH_STATE_TENSORS]
-    hash_bytes = sum(t.numel() * 4 for t in hstate)
-    hash_ms = avg_call(lambda: brl.state_hash(hstate), reps=3)
-    pre_ms = avg_call(lambda: brl.qat_linear_bwd(dY, X, W, synth.S_X, need_dX=False, need_dW=False, ws=ws_b))
-    dx_ms = avg_call(lambda: brl.qat_linear_bwd(dY, X, W, synth.S_X, dX=dX, need_dW=False, ws=ws_b)) - pre_ms
-    dw_ms = avg_call(lambda: brl.qat_linear_bwd(dY, X, W, synth.S_X, dW=dW, need_dX=False, ws=ws_b)) - pre_ms
+    def frac(v, peak):
+        return round(v / peak, 4)
 
-    ops = 2.0 * M * N * K
-    tops = 3 * ops / (lin_ms * 1e-3) / 1e12
+    configs = {}
+    total_ops = 0.0
+    for lay in layers:
+        M, K, N, name = lay["M"], lay["K"], lay["N"], lay["name"]
+        ops = 2.0 * M * N * K
+        total_ops += 3 * ops
+        f_ms = timer.ms(name + ".fwd")[0] / K_
+        b_ms = timer.ms(name + ".bwd")[0] / K_
+        pre_ms = avg_call(lambda: bwd(lay, need_dX=False, need_dW=False))
+        dx_ms = avg_call(lambda: bwd(lay, need_dX=True, need_dW=False)) - pre_ms
+        dw_ms = avg_call(lambda: bwd(lay, need_dX=False, need_dW=True)) - pre_ms
+        t_fwd = ops / (f_ms * 1e-3) / 1e12
+        t_dx = ops / (dx_ms * 1e-3) / 1e12
+        t_dw = ops / (dw_ms * 1e-3) / 1e12
+        t_all = 3 * ops / ((f_ms + b_ms) * 1e-3) / 1e12
+        # combined roofline: the forward at the i8 peak plus dX and dW at the VALU ceiling
+        t_min = ops / (PEAK_I8_TOPS * 1e12) + 2 * ops / (PEAK_VALU_F32_TOPS * 1e12)
+        configs[name] = {
+            "M": M, "K": K, "N": N, "seed": lay["case"].seed,
+            "epilogue": "swiglu" if lay["epi"] else "none", "bwd_microbatches": lay["mb"],
+            "ms": {"fwd": round(f_ms, 4), "bwd": round(b_ms, 4), "bwd_prelude": round(pre_ms, 4),
+                   "dX": round(dx_ms, 4), "dW": round(dw_ms, 4), "fwd_bwd": round(f_ms + b_ms, 4)},
+            "fwd": {"bound": "mfma", "achieved": round(t_fwd, 2), "peak": PEAK_I8_TOPS, "unit": "TOPS",
+                    "frac": frac(t_fwd, PEAK_I8_TOPS)},
+            "dX": {"bound": "alu", "achieved": round(t_dx, 3), "peak": round(PEAK_VALU_F32_TOPS, 2),
+                   "unit": "TFLOP/s", "frac": frac(t_dx, PEAK_VALU_F32_TOPS)},
+            "dW": {"bound": "alu", "achieved": round(t_dw, 3), "peak": round(PEAK_VALU_F32_TOPS, 2),
+                   "unit": "TFLOP/s", "frac": frac(t_dw, PEAK_VALU_F32_TOPS)},
+            "fwd_bwd": {"achieved": round(t_all, 3), "unit": "TOPS",
+                        "combined_peak": round(3 * ops / t_min / 1e12, 2),
+                        "frac": round(t_all / (3 * ops / t_min / 1e12), 4),
+                        "frac_of_i8_peak": frac(t_all, PEAK_I8_TOPS)},
+        }
+
+    tops = total_ops / (lin_ms * 1e-3) / 1e12
     replay_bytes = REPLAY_BYTES_PER_ELEM * L
     replay_gbps = replay_bytes / (rep_ms * 1e-3) / 1e9
     acc_bytes = 12.0 * L
@@ -379,18 +430,18 @@ def main():
         "dtype": "i8->i32 fwd GEMM; f32 bwd and replay",
         "data": "synthetic (seeded Philox Gaussians; device-generated replay partials)",
         "config": {
-            "workload": "QKV projection M=16384 K=2048 N=3072 fwd+bwd (seed 1) + replay 6x8 ranks "
-                        f"x {L} fp32 (seed 4), clip 1.0",
-            "M": M, "K": K, "N": N, "s_x": synth.S_X,
-            "replicas": R, "shards": S, "replay_length": L,
+            "workload": "Open-1B block linears at M=16384 fwd+bwd: QKV 2048->3072 (seed 1), SwiGLU gate+up "
+                        "2048->2x5632 with activation (seed 2), down 5632->2048 with 4 microbatches (seed 3); "
+                        f"+ replay 6x8 ranks x {L} fp32 (seed 4), clip 1.0",
+            "layers": {lay["name"]: [lay["M"], lay["K"], lay["N"]] for lay in layers},
+            "s_x": synth.S_X, "replicas": R, "shards": S, "replay_length": L,
         },
         "ordered_reduce_GBps": round(replay_gbps, 1),
         "phases_ms": {
-            "fwd": round(fwd_ms, 4), "bwd": round(bwd_ms, 4), "bwd_prelude": round(pre_ms, 4),
-            "dX": round(dx_ms, 4), "dW": round(dw_ms, 4), "linear_fwd_bwd": round(lin_ms, 4),
-            "replay": round(rep_ms, 4), "accumulate_avg": round(acc_avg_ms, 5),
-            "norm_clip": round(nc_ms, 4),
+            "linear_fwd_bwd": round(lin_ms, 4), "replay": round(rep_ms, 4),
+            "accumulate_avg": round(acc_avg_ms, 5), "norm_clip": round(nc_ms, 4),
         },
+        "configs": configs,
         "roofline": {
             "kernel": f"accumulate_v4_kernel (ordered_reduce running sum, {acc_n // max(K_, 1)} launches "
                       "per step, timed with one event pair per run of consecutive launches)",
@@ -405,17 +456,23 @@ def main():
         "rooflines_other": {
             "replay_total": {"bound": "hbm", "achieved": round(replay_gbps, 1), "peak": PEAK_HBM_GBPS,
                              "unit": "GB/s", "frac": round(replay_gbps / PEAK_HBM_GBPS, 4)},
-            "fwd_call": {"bound": "mfma", "achieved": round(ops / (fwd_ms * 1e-3) / 1e12, 2),
-                         "peak": PEAK_I8_TOPS, "unit": "TOPS",
-                         "frac": round(ops / (fwd_ms * 1e-3) / 1e12 / PEAK_I8_TOPS, 4)},
-            "dX": {"bound": "alu", "achieved": round(ops / (dx_ms * 1e-3) / 1e12, 3),
-                   "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
-                   "frac": round(ops / (dx_ms * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4)},
-            "dW": {"bound": "alu", "achieved": round(ops / (dw_ms * 1e-3) / 1e12, 3),
-                   "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
-                   "frac": round(ops / (dw_ms * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4)},
+            "fwd_call": dict(configs["qkv"]["fwd"], layer="qkv"),
+            "dX": dict(configs["qkv"]["dX"], layer="qkv"),
+            "dW": dict(configs["qkv"]["dW"], layer="qkv"),
         },
     }
+    # AdamW over the reduced, clipped gradient (L parameters; p, m, v synthetic)
+    ap = synth.replay_partial(rcase, 100, device=dev, length=L)
+    am = torch.zeros(L, dtype=torch.float32, device=dev)
+    av = torch.zeros(L, dtype=torch.float32, device=dev)
+    asc = brl.adamw_scalars_for_step(1000, 3.0e9)
+    adamw_ms = avg_call(lambda: brl.adamw_step(ap, out, am, av, asc), reps=3)
+    adamw_gbps = ADAMW_BYTES_PER_ELEM * L / (adamw_ms * 1e-3) / 1e9
+    del ap, am, av
+    # state hash of a 6.44 GB state (the first 8 replay partials as its tensors)
+    hstate = partials[:HASH_STATE_TENSORS]
+    hash_bytes = sum(t.numel() * 4 for t in hstate)
+    hash_ms = avg_call(lambda: brl.state_hash(hstate), reps=3)
     result["adamw"] = {
         "params": L, "ms": round(adamw_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(adamw_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -438,7 +495,7 @@ def main():
         result["attention"]["cpu_baseline"] = cpu_attention_rate()
     result.update(stream_bench(torch, brl, dev, not args.no_cpu_baseline))
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(layers[0]["inp"], args.cpu_seconds)
         result["cpu_baseline"]["state_hash_GBps"] = cpu_hash_rate([partials[0].cpu().numpy()])
     print(json.dumps(result), flush=True)
 
@@ -485,6 +542,16 @@ def cpu_attention_rate():
             "fwd_T_ops_per_s": round(2.0 * ATTN_D * keys / t_fwd / 1e12, 6),
             "dq_T_ops_per_s": round(3 * 2.0 * ATTN_D * keys / t_dq / 1e12, 6),
             "dkdv_T_ops_per_s": round(4 * 2.0 * ATTN_D * pairs / t_kv / 1e12, 8)}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(inp, budget_s: float):
@@ -534,10 +601,28 @@ def cpu_baseline(inp, budget_s: float):
         oracle.replay(parts, 6, 8)
         t_rep += time.perf_counter() - t0
         reps += 1
+    # the tiny layer (256 x 512 x 512, seed 42, with subnormal dY) forward and
+    # backward on one thread
+    tiny = synth.linear_inputs(synth.CASES["tiny"])
+    threads = oracle.num_threads()
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.linear_fwd(tiny.X, tiny.W, synth.S_X)
+        oracle.linear_bwd(tiny.dY, tiny.X, tiny.W, synth.S_X)
+        t_tiny = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(threads)
+    tc = tiny.case
     return {
         "value": round(ops / t_lin / 1e12, 6),
         "unit": "TOPS",
-        "cores": oracle.num_threads(),
+        "cores": threads,
+        "nproc": os.cpu_count(),
+        "cpu_affinity": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
+        "tiny_1thread": {"TOPS": round(6.0 * tc.M * tc.N * tc.K / t_tiny / 1e12, 6), "s": round(t_tiny, 3),
+                         "shape": [tc.M, tc.K, tc.N]},
         "kind": "oracle",
         "sample": (f"QKV layer: {len(rows)} rows of Y and dX, {len(wr)} rows of dW "
                    f"({ops / 1e9:.1f} G ops, {t_lin:.1f} s); replay of 48 ranks x {Ls} elements "

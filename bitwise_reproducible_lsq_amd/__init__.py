@@ -149,9 +149,11 @@ def workspace_bytes(op: int, M: int, K: int, N: int, tune: Optional[Tuning] = No
 
 def qat_linear_fwd(X: torch.Tensor, W: torch.Tensor, s_x: float, addend: Optional[torch.Tensor] = None,
                    epilogue: int = EPILOGUE_NONE, want_ypre: bool = True, Y: Optional[torch.Tensor] = None,
-                   ws: Optional[torch.Tensor] = None, stream=None, tune: Optional[Tuning] = None):
-    """Y = dequant(int8 GEMM) (+ addend), or the SwiGLU activation.
-    Returns (Y, Ypre or None, s_w as a 1-element device tensor)."""
+                   ws: Optional[torch.Tensor] = None, stream=None, tune: Optional[Tuning] = None,
+                   Ypre: Optional[torch.Tensor] = None):
+    """Y = dequant(int8 GEMM) (+ addend), or the SwiGLU activation.  With
+    SwiGLU the pre-activation goes to Ypre (given, or allocated when
+    want_ypre).  Returns (Y, Ypre or None, s_w as a 1-element device tensor)."""
     _f32(X, "X"), _f32(W, "W")
     M, K = X.shape
     N, K2 = W.shape
@@ -160,9 +162,13 @@ def qat_linear_fwd(X: torch.Tensor, W: torch.Tensor, s_x: float, addend: Optiona
     n_out = N // 2 if epilogue == EPILOGUE_SWIGLU else N
     if Y is None:
         Y = torch.empty((M, n_out), dtype=torch.float32, device=X.device)
-    Ypre = None
-    if epilogue == EPILOGUE_SWIGLU and want_ypre:
+    if epilogue != EPILOGUE_SWIGLU:
+        Ypre = None
+    elif Ypre is None and want_ypre:
         Ypre = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    for t, shape, name in ((Y, (M, n_out), "Y"), (Ypre, (M, N), "Ypre")):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be float32 {shape}")
     s_w = torch.empty(1, dtype=torch.float32, device=X.device)
     if ws is None:
         ws = workspace(OP_FWD, M, K, N, X.device, tune, stream)
