@@ -301,16 +301,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         const int ncand = sm.u.p1.ncand;
         for (int c = tid; c < ncand; c += 256) {
             const int il = sm.u.p1.cand[c] >> 6, jc = sm.u.p1.cand[c] & 63;
-            float b01 = 0.0f, b2 = 0.0f, cur = 0.0f;
-            for (int blk = 0; blk < kAD / 32; ++blk) {
-                cur = f_mul(sm.qs[32 * blk][il], sm.ks[32 * blk][jc]);
-                for (int dd = 1; dd < 32; ++dd)
-                    cur = f_add(cur, f_mul(sm.qs[32 * blk + dd][il], sm.ks[32 * blk + dd][jc]));
-                if (blk == 0) b01 = cur;
-                if (blk == 1) b01 = f_add(b01, cur);
-                if (blk == 2) b2 = cur;
-            }
-            const float sx = f_mul(f_add(b01, f_add(b2, cur)), a.c);
+            // the four d-blocks' left-to-right chains side by side (they are
+            // independent), then (b0 + b1) + (b2 + b3)
+            float cur[kAD / 32];
+#pragma unroll
+            for (int blk = 0; blk < kAD / 32; ++blk) cur[blk] = f_mul(sm.qs[32 * blk][il], sm.ks[32 * blk][jc]);
+#pragma unroll 8
+            for (int dd = 1; dd < 32; ++dd)
+#pragma unroll
+                for (int blk = 0; blk < kAD / 32; ++blk)
+                    cur[blk] = f_add(cur[blk], f_mul(sm.qs[32 * blk + dd][il], sm.ks[32 * blk + dd][jc]));
+            const float sx = f_mul(f_add(f_add(cur[0], cur[1]), f_add(cur[2], cur[3])), a.c);
             const int bits = __float_as_int(sx);
             atomicMax(reinterpret_cast<int*>(&sm.rowmax[il]), bits >= 0 ? bits : bits ^ 0x7fffffff);
         }
@@ -347,17 +348,33 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
                 v[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
                 if (j < a.S) v[u] = *reinterpret_cast<const vf4*>(a.V + (base + j) * a.ldv + hk * kAD + 4 * dq);
             }
+            // codes on the quantiser's fast path; a wave with a value near a
+            // rounding midpoint redoes its values on the exact path (rows
+            // past S were loaded as zeros and quantise to 0)
+            uint32_t packed[4];
+            bool unsure = false;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                uint32_t packed = 0;
+                packed[w] = 0;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    bool in;
-                    const int q = j0 + 4 * rq + u < a.S ? qz.q(v[u][w], &in) : 0;
-                    packed |= (uint32_t)(uint8_t)(int8_t)q << (8 * u);
+                for (int u = 0; u < 4; ++u)
+                    packed[w] |= (uint32_t)(uint8_t)(int8_t)qz.q_fast(v[u][w], &unsure) << (8 * u);
+            }
+            if (__ballot(unsure)) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    packed[w] = 0;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        bool in;
+                        packed[w] |= (uint32_t)(uint8_t)(int8_t)qz.q(v[u][w], &in) << (8 * u);
+                    }
                 }
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
                 const int d = 4 * dq + w, r = 4 * rq;
-                *reinterpret_cast<uint32_t*>(&sm.u.pv.vq[d][16 * aswz(d, r >> 4) + (r & 15)]) = packed;
+                *reinterpret_cast<uint32_t*>(&sm.u.pv.vq[d][16 * aswz(d, r >> 4) + (r & 15)]) = packed[w];
             }
         }
         __syncthreads();
