@@ -37,8 +37,15 @@ METRIC = "bit-exact int8 QAT linear TOPS fwd+bwd (M=16384); ordered-reduce GB/s"
 
 # MI355X published peaks (dense) and the derived fp32 VALU rate without FMA
 # or packed instructions: 256 CU x 4 SIMD x 32 lanes per clock x 2.4 GHz
-# (a wave64 v_add_f32 / v_mul_f32 retires in two clocks; measured 62-65 T
-# ops/s sustained on MI355X).  The published 157.3 TFLOP/s counts packed FMA.
+# (a wave64 v_add_f32 / v_mul_f32 with vector-register operands issues in two
+# clocks; the published 157.3 TFLOP/s counts each FMA as two operations).
+# The library's rate probe (brl_probe_rate, timed under "measured_peaks")
+# sustains 67 T ops/s for those, 37 with a scalar-register operand, 71 for
+# 32-bit integer ops, 77.7 T products/s on the K=1 fp32 MFMA and 4970 TOPS on
+# the i8 MFMA.  dX and dW pair each matrix-core product with one VALU add (2
+# ops); the probe of that pattern alone, with no memory traffic, sustains
+# about 35 T multiply-adds/s = 70 T ops/s (the two units do not overlap in
+# it), reported beside the published-rate fraction as "frac_of_engine".
 PEAK_HBM_GBPS = 8000.0
 PEAK_I8_TOPS = 5030.0
 PEAK_VALU_F32_TOPS = 256 * 128 * 2.4e9 / 1e12         # 78.64 T ops/s
@@ -54,8 +61,9 @@ REPLAY_BYTES_PER_ELEM = 6 * 7 * 12 + 28 + 8           # 540
 # State hash (the next row after the hot path, measured beside it, not part of
 # `value`): the compiled SHA-256 block loop of the leaf kernel issues
 # HASH_VALU_PER_BLOCK VALU instructions per 64-byte block, HASH_ALIGNBIT_PER_BLOCK
-# of them v_alignbit_b32 (the rotations), which gfx950 issues at half the rate
-# of the other integer ops (measured: 34 vs 57-60 T lane-ops/s).  A CPU test
+# of them v_alignbit_b32 (the rotations), which gfx950 issues at about half the
+# rate of the other integer ops (34 T lane-ops/s measured, against 71 for
+# shifts and xors in the rate probe).  A CPU test
 # recounts both in the generated assembly.  VALU bound: 78.64e12 issue slots/s
 # over (2 x alignbit + the rest) slots per block, times 64 bytes.
 HASH_VALU_PER_BLOCK = 1561
@@ -185,11 +193,42 @@ def attention_bench(torch, brl, dev):
     return out
 
 
+def measured_peaks(torch, brl):
+    """Sustained rates of the units the rooflines price against, measured by
+    the library's rate probe (full grid, 8 independent chains per thread):
+    binary32 adds and multiplies on the VALU, products of the K=1 fp32 MFMA,
+    and integer ops (2 per multiply-accumulate) of the i8 MFMA 32x32x32."""
+    out = {}
+    iters = {"v_add_f32": 100000, "v_mul_f32": 100000, "v_add_f32_sgpr": 50000, "valu_u32": 50000,
+             "mfma_k1_f32": 20000, "k1_engine": 20000, "mfma_i8": 8000}
+    buf = torch.empty(int(brl.lib().brl_probe_rate_threads()), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    for unit, n in iters.items():
+        brl.probe_rate(unit, 16, buf)
+        ms = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            brl.probe_rate(unit, n, buf)
+            e1.record(st)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        ops = buf.numel() * brl.RATE_OPS_PER_STEP[unit] * n
+        out[unit] = {"T_ops_per_s": round(ops / (min(ms) * 1e-3) / 1e12, 2), "ms": round(min(ms), 3), "iters": n}
+    out["note"] = ("v_add_f32 / v_mul_f32: binary32 operations with vector-register operands (_sgpr: one "
+                   "scalar-register operand); valu_u32: 32-bit shifts and xors; mfma_k1_f32: products of "
+                   "v_mfma_f32_16x16x1_4b_f32; k1_engine: multiply-adds of that MFMA (-0 accumulator) "
+                   "followed by a v_add_f32 per product, no memory traffic; mfma_i8: integer ops of "
+                   "v_mfma_i32_32x32x32_i8")
+    return out
+
+
 def measured_traffic(kernel: str):
     """HBM bytes per dispatch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE passes, calibrated with a copy kernel of
     known size), or None when the kernel sources changed since they were taken."""
     import hashlib
+    from bitwise_reproducible_lsq_amd import build as brl_build
     path = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.json")
     if not os.path.exists(path):
         return None
@@ -198,6 +237,10 @@ def measured_traffic(kernel: str):
         f = os.path.join(ROOT, src)
         if not os.path.exists(f) or hashlib.sha256(open(f, "rb").read()).hexdigest() != digest:
             return None
+    # the compiler flags of the replay unit (include paths left out: they differ between machines)
+    flags = [f for f in brl_build.FLAGS + brl_build.EXTRA.get("replay.hip", []) if not f.startswith("-I")]
+    if hashlib.sha256(json.dumps(flags).encode()).hexdigest() != rec.get("replay_flags_sha256"):
+        return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else int(round(k["bytes"]))
 
@@ -297,6 +340,8 @@ def main():
     ws_n = brl.workspace(brl.OP_NORM, L, 0, 0, dev)
     torch.cuda.synchronize()
 
+    peaks = measured_peaks(torch, brl)
+    engine_tops = 2 * peaks["k1_engine"]["T_ops_per_s"]
     timer = Timer(torch)
 
     def fwd(lay):
@@ -401,9 +446,11 @@ def main():
             "fwd": {"bound": "mfma", "achieved": round(t_fwd, 2), "peak": PEAK_I8_TOPS, "unit": "TOPS",
                     "frac": frac(t_fwd, PEAK_I8_TOPS)},
             "dX": {"bound": "alu", "achieved": round(t_dx, 3), "peak": round(PEAK_VALU_F32_TOPS, 2),
-                   "unit": "TFLOP/s", "frac": frac(t_dx, PEAK_VALU_F32_TOPS)},
+                   "unit": "TFLOP/s", "frac": frac(t_dx, PEAK_VALU_F32_TOPS),
+                   "frac_of_engine": frac(t_dx, engine_tops)},
             "dW": {"bound": "alu", "achieved": round(t_dw, 3), "peak": round(PEAK_VALU_F32_TOPS, 2),
-                   "unit": "TFLOP/s", "frac": frac(t_dw, PEAK_VALU_F32_TOPS)},
+                   "unit": "TFLOP/s", "frac": frac(t_dw, PEAK_VALU_F32_TOPS),
+                   "frac_of_engine": frac(t_dw, engine_tops)},
             "fwd_bwd": {"achieved": round(t_all, 3), "unit": "TOPS",
                         "combined_peak": round(3 * ops / t_min / 1e12, 2),
                         "frac": round(t_all / (3 * ops / t_min / 1e12), 4),
@@ -490,6 +537,7 @@ def main():
                               f"{HASH_ALIGNBIT_PER_BLOCK} of them half-rate rotations")},
     }
     del hstate
+    result["measured_peaks"] = peaks
     result["attention"] = attention_bench(torch, brl, dev)
     if not args.no_cpu_baseline:
         result["attention"]["cpu_baseline"] = cpu_attention_rate()

@@ -26,7 +26,8 @@ EPILOGUE_NONE, EPILOGUE_SWIGLU = 0, 1
 OP_FWD, OP_BWD, OP_NORM, OP_HASH = 0, 1, 2, 3
 MAX_REPLICAS = 64
 
-PROBE_OPS = {"add": 0, "sub": 1, "mul": 2, "div": 3, "sqrt": 4, "i2f": 5, "rne": 6, "exp": 7, "mfma_mul": 8}
+PROBE_OPS = {"add": 0, "sub": 1, "mul": 2, "div": 3, "sqrt": 4, "i2f": 5, "rne": 6, "exp": 7, "mfma_mul": 8,
+             "mfma_fma": 9}
 
 
 class BrlError(RuntimeError):
@@ -78,6 +79,8 @@ _SIGS = {
     "brl_stream_save": (i32, [P, P, i64]),
     "brl_stream_load": (i32, [P, P, i64]),
     "brl_philox_u32": (i32, [C.c_uint64, C.c_uint32, C.c_uint64, i64, P, P]),
+    "brl_probe_rate": (i32, [i32, i64, P, i64, P]),
+    "brl_probe_rate_threads": (i64, []),
     "brl_status_string": (C.c_char_p, [i32]),
     "brl_last_error": (C.c_char_p, []),
 }
@@ -497,4 +500,23 @@ def philox_u32(key: int, stream: int, first: int, n: int, out: Optional[torch.Te
 def probe_f32(op: str, a: torch.Tensor, b: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     out = torch.empty_like(a)
     _check(lib().brl_probe_f32(PROBE_OPS[op], _ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)))
+    return out
+
+
+RATE_UNITS = {"v_add_f32": 0, "v_mul_f32": 1, "mfma_k1_f32": 2, "mfma_i8": 3, "valu_u32": 4,
+              "v_add_f32_sgpr": 5, "k1_engine": 6}
+# operations each thread performs per step of the rate probe (per lane: the
+# MFMA counts are per wave, divided over its 64 lanes; k1_engine counts
+# multiply-adds, a matrix-core product and a VALU add each)
+RATE_OPS_PER_STEP = {"v_add_f32": 8, "v_mul_f32": 8, "mfma_k1_f32": 8 * 1024 / 64, "mfma_i8": 8 * 65536 / 64,
+                     "valu_u32": 16, "v_add_f32_sgpr": 8, "k1_engine": 4 * 1024 / 64}
+
+
+def probe_rate(unit: str, iters: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Launch the sustained-rate probe of one unit (brl_probe_rate); time it
+    with events around the call.  Returns the output buffer."""
+    n = int(lib().brl_probe_rate_threads())
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device="cuda")
+    _check(lib().brl_probe_rate(RATE_UNITS[unit], int(iters), _ptr(out), out.numel(), _stream(stream)))
     return out

@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbrlsq.so")
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = ["api.hip", "canon.hip", "fwd.hip", "bwd.hip", "replay.hip", "hash.hip", "optim.hip", "attn.hip", "stream.hip"]
+SOURCES = ["api.hip", "canon.hip", "fwd.hip", "bwd.hip", "replay.hip", "hash.hip", "optim.hip", "attn.hip", "stream.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -43,8 +43,11 @@ def _run(cmd):
 # Per-unit extra flags.  The backward's binary-counter stack stores each
 # finished subtree to a level chosen by a uniform branch; sinking those
 # stores into one store through a pointer phi would keep the stack in
-# scratch memory instead of registers.
-EXTRA = {"bwd.hip": ["-mllvm", "-simplifycfg-sink-common=false", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# scratch memory instead of registers.  The backward and the rate probes
+# keep MFMA results in ordinary vector registers, where the VALU reads them
+# without accumulator-register moves.
+EXTRA = {"bwd.hip": ["-mllvm", "-simplifycfg-sink-common=false", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

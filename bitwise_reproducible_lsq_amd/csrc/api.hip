@@ -498,13 +498,28 @@ brl_status grad_l2norm_clip_noalloc(float* g, int64_t len, float max_norm, float
 }
 
 brl_status brl_probe_f32(int32_t op, const float* a, const float* b, float* out, int64_t n, void* stream) {
-    if (op < 0 || op > 8) return fail(BRL_EINVAL, "brl_probe_f32: unknown op %d", op);
+    if (op < 0 || op > 9) return fail(BRL_EINVAL, "brl_probe_f32: unknown op %d", op);
     if (n < 0) return fail(BRL_ESHAPE, "brl_probe_f32: n < 0");
-    if (n > 0 && (!a || !out || ((op <= 3 || op == 8) && !b))) return fail(BRL_EINVAL, "brl_probe_f32: null pointer");
+    if (n > 0 && (!a || !out || ((op <= 3 || op >= 8) && !b))) return fail(BRL_EINVAL, "brl_probe_f32: null pointer");
     if (op == 8)
         return check_hip(launch_probe_mfma(a, b, out, n, static_cast<hipStream_t>(stream)), "probe");
+    if (op == 9)
+        return check_hip(launch_probe_mfma_fma(a, b, out, n, static_cast<hipStream_t>(stream)), "probe");
     return check_hip(launch_probe(op, a, b, out, n, exp_constants(), static_cast<hipStream_t>(stream)), "probe");
 }
+
+brl_status brl_probe_rate(int32_t what, int64_t iters, float* out, int64_t out_len, void* stream) {
+    if (what < 0 || what > 6) return fail(BRL_EINVAL, "brl_probe_rate: unknown unit %d", what);
+    if (iters < 1 || iters > ((int64_t)1 << 30)) return fail(BRL_ESHAPE, "brl_probe_rate: iters out of range");
+    if (!out || !aligned4(out)) return fail(BRL_EINVAL, "brl_probe_rate: bad output pointer");
+    if (out_len < probe_rate_threads())
+        return fail(BRL_ESHAPE, "brl_probe_rate: out needs %lld floats", (long long)probe_rate_threads());
+    // c: a step that keeps every chain finite for any iteration count
+    const float c = (what == 1 || what == 3) ? 1.0f : 0.5f;
+    return check_hip(launch_probe_rate(what, iters, c, out, static_cast<hipStream_t>(stream)), "rate probe");
+}
+
+int64_t brl_probe_rate_threads(void) { return probe_rate_threads(); }
 
 brl_status brl_state_hash(const void* const* tensors, const int64_t* nbytes, int32_t count, uint8_t* digest,
                           void* ws, size_t ws_bytes, void* stream) {

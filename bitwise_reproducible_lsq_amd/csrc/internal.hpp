@@ -157,6 +157,12 @@ hipError_t launch_clip(float* g, int64_t n, const Scalars* scal, int vec, hipStr
 hipError_t launch_probe_mfma(const float* a, const float* b, float* out, int64_t n, hipStream_t st);
 hipError_t launch_probe(int op, const float* a, const float* b, float* out, int64_t n,
                         const ExpConsts& ek, hipStream_t st);
+// out[i] = a[i]*a[i] + b[i] as the K=1 fp32 MFMA forms it (accumulator input b[i])
+hipError_t launch_probe_mfma_fma(const float* a, const float* b, float* out, int64_t n, hipStream_t st);
+// sustained-rate probes (probe.hip): what 0 v_add_f32, 1 v_mul_f32, 2 K=1 fp32
+// MFMA, 3 i8 MFMA 32x32x32; out has probe_rate_threads() floats
+hipError_t launch_probe_rate(int what, int64_t iters, float c, float* out, hipStream_t st);
+int64_t probe_rate_threads();
 
 ExpConsts exp_constants();
 

@@ -424,10 +424,28 @@ BRL_API brl_status brl_philox_u32(uint64_t key, uint32_t stream, uint64_t first,
  * them: out[i] = op(a[i], b[i]) for op 0 add, 1 sub, 2 mul, 3 div, 4 sqrt (a),
  * 5 int32 bits of a -> float, 6 round-to-nearest-even integral (a),
  * 7 the SwiGLU exp E(a), 8 the product a*b as the backward's matrix-core
- * engine forms it (K=1 fp32 MFMA with a -0 accumulator).  Device pointers,
- * n >= 0. */
+ * engine forms it (K=1 fp32 MFMA with a -0 accumulator), 9 a*a + b from the
+ * same K=1 MFMA with the accumulator input b (the library never uses it that
+ * way: it rounds product and sum once, which the method forbids).  Device
+ * pointers, n >= 0. */
 BRL_API brl_status brl_probe_f32(int32_t op, const float* a, const float* b, float* out, int64_t n,
                          void* stream);
+
+/* Sustained-rate probe of the units the kernels run on, behind the rooflines
+ * the library's benchmark reports: a grid that fills the chip
+ * (brl_probe_rate_threads() threads), each thread running 8 independent
+ * chains of `iters` steps of: what 0 v_add_f32 (8 binary32 adds per step),
+ * 1 v_mul_f32 (8 multiplies per step), 2 the K=1 fp32 MFMA (8 per step per
+ * wave, 1024 products each), 3 the i8 MFMA 32x32x32 (8 per step per wave,
+ * 65536 integer ops each), 4 32-bit integer VALU (a shift and an xor, 16
+ * instructions per step), 5 v_add_f32 with a scalar-register operand,
+ * 6 the backward's product engine without memory traffic (4 K=1 fp32 MFMAs
+ * with a -0 accumulator and the 64 v_add_f32 that sum their products: 4096
+ * multiply-adds per wave per step).  out: device, at least brl_probe_rate_threads()
+ * floats, receives each thread's chain results (values of no meaning).  The
+ * caller times the call with events on `stream`. */
+BRL_API brl_status brl_probe_rate(int32_t what, int64_t iters, float* out, int64_t out_len, void* stream);
+BRL_API int64_t brl_probe_rate_threads(void);
 
 BRL_API const char* brl_status_string(brl_status s);
 BRL_API const char* brl_last_error(void);
