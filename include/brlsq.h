@@ -87,7 +87,7 @@ typedef int32_t brl_status;
  * struct once, at its start, and a bad value fails the call with BRL_EINVAL. */
 typedef struct brl_tuning {
     int32_t bwd_chunk_log2;    /* 32-blocks per backward reduction chunk: 2^v, v in 1..7
-                                  (0: 6 on the matrix-core engine, 4 on the VALU engine) */
+                                  (0: 7 on the matrix-core engine, 4 on the VALU engine) */
     int32_t reduce_wg_blocks;  /* 32-blocks per workgroup in CanonSum passes: 64, 128 or 256 (0: 256) */
     int32_t stream_vec;        /* 16-byte vectors per thread in the streaming kernels: 1, 2 or 4 (0: 1) */
     int32_t bwd_engine;        /* backward products on 1 the VALU, 2 the matrix cores (0: 2; the matrix
