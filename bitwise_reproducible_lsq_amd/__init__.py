@@ -67,7 +67,8 @@ _SIGS = {
     "brl_state_hash": (i32, [P, P, i32, P, P, sz, P]),
     "brl_adamw_scalars_for_step": (i32, [i64, C.c_double, P, P]),
     "adamw_step": (i32, [P, P, P, P, i64, P, i32, P]),
-    "attn_fwd": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64, P, P]),
+    "attn_fwd": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64, P, P, sz, P]),
+    "attn_fwd_workspace_bytes": (sz, [i64, i64, i64, i64, i64]),
     "attn_bwd_dq": (i32, [P, P, P, P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, P]),
     "attn_bwd_dkdv": (i32, [P, P, P, P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, P, i64,
                             P]),
@@ -358,8 +359,14 @@ def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, window: int, s_v
     k, ldk = _heads_view(K, "K")
     v, ldv = _heads_view(V, "V")
     o, ldo = _heads_view(O, "O")
+    nws = int(lib().attn_fwd_workspace_bytes(B, S, Hq, Hkv, int(window)))
+    if nws == 0:
+        raise BrlError(BRL_ESHAPE, f"attn_fwd: no workspace size for B={B} S={S} Hq={Hq} Hkv={Hkv}")
+    ws = torch.empty(nws, dtype=torch.uint8, device=Q.device)
+    if stream is not None and stream != torch.cuda.current_stream(Q.device):
+        ws.record_stream(stream)
     _check(lib().attn_fwd(q, k, v, B, S, Hq, Hkv, D, ldq, ldk, ldv, int(window), float(s_v), o, ldo,
-                          _ptr(stats), _stream(stream)))
+                          _ptr(stats), _ptr(ws), ws.numel(), _stream(stream)))
     return O
 
 

@@ -614,9 +614,15 @@ static brl_status attn_check(const char* who, int64_t B, int64_t S, int64_t Hq, 
 
 static bool al16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+size_t attn_fwd_workspace_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t window) {
+    if (B < 0 || S < 0 || S > 133143 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return 0;
+    if (B * Hq * ((S + 63) / 64) > 0xffffffffLL) return 0;
+    return attn_fwd_ws_bytes(B, S, Hq, window);
+}
+
 brl_status attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
                     int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
-                    float* O, int64_t ldo, float* stats, void* stream) {
+                    float* O, int64_t ldo, float* stats, void* ws, size_t ws_bytes, void* stream) {
     brl_status rc = attn_check("attn_fwd", B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo, s_v);
     if (rc != BRL_OK) return rc;
     if (B * S == 0) return BRL_OK;
@@ -624,8 +630,12 @@ brl_status attn_fwd(const float* Q, const float* K, const float* V, int64_t B, i
     if (!al16p(Q) || !al16p(K) || !al16p(V) || !al16p(O))
         return fail(BRL_EINVAL, "attn_fwd: pointers must be 16-byte aligned");
     if (stats && !aligned4(stats)) return fail(BRL_EINVAL, "attn_fwd: stats must be 4-byte aligned");
+    if (B * Hq * ((S + 63) / 64) > 0xffffffffLL) return fail(BRL_ESHAPE, "attn_fwd: too many query blocks");
+    const size_t need = attn_fwd_ws_bytes(B, S, Hq, window);
+    if (!aligned256(ws)) return fail(BRL_EINVAL, "attn_fwd: workspace must be 256-byte aligned");
+    if (!ws || ws_bytes < need) return fail(BRL_EWORKSPACE, "attn_fwd: workspace %zu < %zu bytes", ws_bytes, need);
     return check_hip(launch_attn_fwd(Q, K, V, B, S, Hq, Hkv, ldq, ldk, ldv, window, s_v, O, ldo, stats,
-                                     exp_constants(), static_cast<hipStream_t>(stream)),
+                                     static_cast<float*>(ws), exp_constants(), static_cast<hipStream_t>(stream)),
                      "attention");
 }
 

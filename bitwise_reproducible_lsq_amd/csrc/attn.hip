@@ -16,21 +16,20 @@
 // order-free, so only the logits and l_i carry an order, and both are fixed
 // by absolute positions (d, and the key index j), not by tiles.
 //
-// Forward: one workgroup per (batch, query head, block of 64 queries); two
-// passes over the 64-key tiles that meet the rows' key ranges:
-//   pass 1: the exact row maxima (order-free): bf16 logits on the matrix
-//           cores bound every exact logit within a proven margin; only keys
-//           that can still hold the maximum get their exact logit, in pass
-//           2's order, into an atomic maximum;
-//   pass 2: exact logits (VALU, 4 x 4 per thread, d-blocks of 32 summed left
-//           to right, then as a pairwise tree) -> p -> the 32-key block
-//           sums, each a left-to-right chain through the 8 lanes that hold
-//           its keys (DPP shifts within a 16-lane row); a tile's two blocks
-//           are a complete pair
-//           (their absolute indices are 2kt, 2kt+1), so their sum is pushed on
-//           the row's binary-counter stack of pairs at index kt; q_p and q_v
-//           staged as int8 in LDS and multiplied on v_mfma_i32_32x32x32_i8
-//           into int32 accumulators.
+// Forward: a persistent grid of workgroups, each walking (batch, query head,
+// block of 64 queries) items, longest first; two passes over the 64-key
+// tiles that meet the block's key range:
+//   pass 1: exact logits (VALU, 4 x 4 per thread, d-blocks of 32 summed left
+//           to right, then as a pairwise tree), stored in the workgroup's
+//           slot of the workspace, and the exact row maxima (order-free);
+//   pass 2: the stored logits -> p -> the 32-key block sums, each a
+//           left-to-right chain through the 8 lanes that hold its keys (DPP
+//           shifts within a 16-lane row); a tile's two blocks are a complete
+//           pair (their absolute indices are 2kt, 2kt+1), so their sum is
+//           pushed on the row's binary-counter stack of pairs at index kt;
+//           q_p and q_v staged as int8 in LDS and multiplied on
+//           v_mfma_i32_32x32x32_i8 into int32 accumulators.
+// Each thread reads back in pass 2 exactly the logits it wrote in pass 1.
 // Pairs before the first real one are +0 subtrees (the stack starts zeroed)
 // and merging with +0 is exact, so this is CanonSum over the whole axis.
 // LDS is kept under 80 KB so that two workgroups share a CU.
@@ -57,27 +56,22 @@ struct AttnArgs {
     const float* V;
     float* O;
     float* stats;          // optional (m_i, l_i) per row (b*S + i)*Hq + h
-    int64_t S, Hq, Hkv, ldq, ldk, ldv, ldo, window;
+    float* logits;         // slot_floats floats per workgroup: [tile][64 rows][64 keys]
+    int64_t B, S, Hq, Hkv, ldq, ldk, ldv, ldo, window, slot_floats;
     float c, s_v;
     ExpConsts ek;
 };
 
 struct AttnSmem {
-    float qs[kAD][kAQ];             // Q tile, d-major
-    float ks[kAD][kAK];             // K tile, d-major
     union {
+        struct {
+            float qs[kAD][kAQ];     // Q tile, d-major
+            float ks[kAD][kAK];     // K tile, d-major
+        } a;                        // pass 1
         struct {
             int8_t pq[kAQ][kAK];    // q_p, rows of 64 keys, 16-byte chunks swizzled
             int8_t vq[kAD][kAK];    // q_v transposed: row d holds 64 keys, swizzled
-        } pv;
-        struct {
-            double nq[kAQ];         // pass 1: Euclidean norms of the Q rows (rounded up)
-            float hmax[2][kAQ];     // pass 1: largest lower bounds a - E of the tile's key halves
-            float lbound[kAQ];      // pass 1: running lower bound L_i of the row maximum
-            double nkp[4][kAK];     // pass 1: partial squared norms of the K rows
-            int ncand;              // pass 1: candidates of the tile
-            uint16_t cand[kAQ * kAK];   // pass 1: (row << 6) | key
-        } p1;
+        } pv;                       // pass 2
     } u;
     float st[kAQ][kAStack];         // per-row stacks of key-tile pair sums
     float rowmax[kAQ];
@@ -159,331 +153,292 @@ __device__ __forceinline__ float dpp_shr8(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
 }
 
+// order-preserving integer image of a binary32 value (negative values:
+// bits ^ 0x7fffffff), so that an integer maximum is the float maximum
+__device__ __forceinline__ int max_image(float f) {
+    const int b = __float_as_int(f);
+    return b >= 0 ? b : b ^ 0x7fffffff;
+}
+__device__ __forceinline__ float from_max_image(int k) { return __int_as_float(k >= 0 ? k : k ^ 0x7fffffff); }
+
+// key tiles [kt0, kt1] that meet the key ranges of query block qb
+__host__ __device__ __forceinline__ void attn_tile_range(int64_t S, int64_t window, int64_t qb, int64_t* kt0,
+                                                         int64_t* kt1) {
+    const int64_t q0 = qb * kAQ;
+    const int64_t qrows = S - q0 < kAQ ? S - q0 : kAQ;
+    const int64_t klo = window > 0 ? (q0 - window + 1 > 0 ? q0 - window + 1 : 0) : 0;
+    *kt0 = klo / kAK;
+    *kt1 = (q0 + qrows - 1) / kAK;
+}
+
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ti = tid >> 4, tj = tid & 15;
 
-    // block -> (b, h, query block) in 32-bit unsigned arithmetic (the host
-    // checks that the grid fits); query blocks slowest and from the last, so
-    // that the longest walks (last blocks, causal) start first
-    const unsigned nqb = (unsigned)((a.S + kAQ - 1) / kAQ), hq = (unsigned)a.Hq;
-    const unsigned nbh = gridDim.x / nqb;
-    const unsigned qb = nqb - 1 - blockIdx.x / nbh;
-    const unsigned bh = blockIdx.x % nbh;
-    const int64_t h = bh % hq;
-    const int64_t b = bh / hq;
-    const int64_t hk = (unsigned)h / (hq / (unsigned)a.Hkv);
-    const int64_t q0 = qb * kAQ;
-    const int64_t qrows = a.S - q0 < kAQ ? a.S - q0 : kAQ;
-    const int64_t base = b * a.S;                    // first row of this batch entry
-
-    // key range of the block: [klo, khi]
-    const int64_t klo = a.window > 0 ? (q0 - a.window + 1 > 0 ? q0 - a.window + 1 : 0) : 0;
-    const int64_t khi = q0 + qrows - 1;
-    const int64_t kt0 = klo / kAK, kt1 = khi / kAK;
-
-    attn_load_kt(a.Q, a.ldq, base + q0, qrows, h, sm.qs);
-    for (int e = tid; e < kAQ * kAStack; e += 256) sm.st[e / kAStack][e % kAStack] = 0.0f;
-
-    auto allowed = [&](int64_t i, int64_t j) {
-        const int64_t lo = a.window > 0 ? i - a.window + 1 : 0;
-        return i < a.S && j <= i && j >= lo;
-    };
-
-    // ---- pass 1: exact row maxima from a cheap approximation ----
-    // a_ij = fl(sum_d bf16(q_id) bf16(k_jd) in fp32) * c on the matrix cores
-    // differs from the exact logit s_ij by at most E_ij = c * 0.0158 *
-    // |q_i| |k_j| + 2^-80 (bf16 operands: 2^-7 relative each; fp32 sums of
-    // 128 terms in any order: gamma_128; the canonical sum: gamma_35;
-    // Cauchy-Schwarz for sum |q_d k_d|; products flushed below 2^-126 in
-    // either sum: under 2^-119 in all; about twice the worst case).  Norms
-    // and bound are formed in binary64, where no square of a binary32 value
-    // under- or overflows.  So s_ij lies in [a_ij - E_ij, a_ij + E_ij], and
-    // the row maximum m_i is at least L_i = max over the row's keys of
-    // (a_il - E_il).  A key with a_ij + E_ij < L_i is below m_i and cannot
-    // hold it; every other key is a candidate whose exact logit is computed
-    // (in the canonical order of pass 2) into an order-free maximum.  L_i is
-    // kept as a running value over the tiles seen so far (rounded down to
-    // binary32), which is at most the final one, so the test against it keeps
-    // every key the final value would.
-    const int wmt = wave & 1, wnt = wave >> 1;     // this wave's 32 x 32 sub-tile of the 64 x 64 tile
-    typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-    typedef float v16f_a __attribute__((ext_vector_type(16)));
-    __syncthreads();                               // the Q tile is in LDS
-    if (tid < kAQ) {
-        double n2 = 0.0;
-        for (int d = 0; d < kAD; ++d) n2 += (double)sm.qs[d][tid] * (double)sm.qs[d][tid];
-        sm.u.p1.nq[tid] = __builtin_sqrt(n2) * (1.0 + 0x1p-30);
-        sm.u.p1.lbound[tid] = __int_as_float(0xff800000);
-        // order-preserving integer image of -inf (negative floats: bits ^ 0x7fffffff)
-        reinterpret_cast<int*>(sm.rowmax)[tid] = (int)(0xff800000u ^ 0x7fffffffu);
-    }
-    const double ebound = (double)a.c * 0.0158;
-    for (int64_t kt = kt0; kt <= kt1; ++kt) {
-        const int64_t j0 = kt * kAK;
-        __syncthreads();
-        attn_load_kt(a.K, a.ldk, base + j0, a.S - j0, hk, sm.ks);
-        __syncthreads();
-        {
-            // |k_j|^2 in four partial sums of 32 terms (any order: a bound)
-            const int key = tid & 63, part = tid >> 6;
-            double n2 = 0.0;
-            for (int d = 32 * part; d < 32 * part + 32; ++d) n2 += (double)sm.ks[d][key] * (double)sm.ks[d][key];
-            sm.u.p1.nkp[part][key] = n2;
-            if (tid == 0) sm.u.p1.ncand = 0;
-        }
-        v16f_a ap = {};
-        {
-            const int key = wnt * 32 + (lane & 31), row = wmt * 32 + (lane & 31);
-#pragma unroll 2
-            for (int ks = 0; ks < kAD / 16; ++ks) {
-                v8bf qb, kb;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    qb[e] = (__bf16)sm.qs[16 * ks + 8 * (lane >> 5) + e][row];
-                    kb[e] = (__bf16)sm.ks[16 * ks + 8 * (lane >> 5) + e][key];
-                }
-                ap = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb, kb, ap, 0, 0, 0);
-            }
-        }
-        // element r of this lane: row wmt*32 + 8(r>>2) + 4(lane>>5) + (r&3), key wnt*32 + (lane&31)
-        const int jl = wnt * 32 + (lane & 31);
-        const double nk = __builtin_sqrt((sm.u.p1.nkp[0][jl] + sm.u.p1.nkp[1][jl]) +
-                                         (sm.u.p1.nkp[2][jl] + sm.u.p1.nkp[3][jl])) * (1.0 + 0x1p-30);
-        float hm[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int il = wmt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            ap[r] = f_mul(ap[r], a.c);
-            // a - E in binary64, moved down by more than one binary32
-            // rounding before it is rounded, so the binary32 value is a lower
-            // bound too; no bound from a key whose a or E is not finite
-            const double lb = (double)ap[r] - (ebound * sm.u.p1.nq[il] * nk + 0x1p-80);
-            const float lf = (float)(lb - __builtin_fabs(lb) * 0x1p-23 - 0x1p-125);
-            const bool usable = allowed(q0 + il, j0 + jl) && __builtin_isfinite(lb);
-            hm[r] = usable ? lf : __int_as_float(0xff800000);
-        }
-        // largest lower bound over the 32 keys of the half (lanes with equal lane >> 5)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-#pragma unroll
-            for (int sh = 16; sh >= 1; sh >>= 1) {
-                const float o = __shfl_xor(hm[r], sh, 32);
-                hm[r] = o > hm[r] ? o : hm[r];
-            }
-        if ((lane & 31) == 0) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.u.p1.hmax[wnt][wmt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)] = hm[r];
-        }
-        __syncthreads();
-        if (tid < kAQ) {
-            float m = sm.u.p1.lbound[tid];
-            m = sm.u.p1.hmax[0][tid] > m ? sm.u.p1.hmax[0][tid] : m;
-            m = sm.u.p1.hmax[1][tid] > m ? sm.u.p1.hmax[1][tid] : m;
-            sm.u.p1.lbound[tid] = m;
-        }
-        __syncthreads();
-        // candidates (a + E >= L, or not comparable): listed, then their exact
-        // logits (pass 2's order) taken one per thread into an order-free maximum
-        {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int il = wmt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (!allowed(q0 + il, j0 + jl)) continue;
-                const double e = ebound * sm.u.p1.nq[il] * nk + 0x1p-80;
-                if (!((double)ap[r] + e < (double)sm.u.p1.lbound[il]))
-                    sm.u.p1.cand[atomicAdd(&sm.u.p1.ncand, 1)] = (uint16_t)((il << 6) | jl);
-            }
-        }
-        __syncthreads();
-        const int ncand = sm.u.p1.ncand;
-        for (int c = tid; c < ncand; c += 256) {
-            const int il = sm.u.p1.cand[c] >> 6, jc = sm.u.p1.cand[c] & 63;
-            // the four d-blocks' left-to-right chains side by side (they are
-            // independent), then (b0 + b1) + (b2 + b3)
-            float cur[kAD / 32];
-#pragma unroll
-            for (int blk = 0; blk < kAD / 32; ++blk) cur[blk] = f_mul(sm.qs[32 * blk][il], sm.ks[32 * blk][jc]);
-#pragma unroll 8
-            for (int dd = 1; dd < 32; ++dd)
-#pragma unroll
-                for (int blk = 0; blk < kAD / 32; ++blk)
-                    cur[blk] = f_add(cur[blk], f_mul(sm.qs[32 * blk + dd][il], sm.ks[32 * blk + dd][jc]));
-            const float sx = f_mul(f_add(f_add(cur[0], cur[1]), f_add(cur[2], cur[3])), a.c);
-            const int bits = __float_as_int(sx);
-            atomicMax(reinterpret_cast<int*>(&sm.rowmax[il]), bits >= 0 ? bits : bits ^ 0x7fffffff);
-        }
-    }
-    __syncthreads();
-    if (tid < kAQ) {
-        const int key = __float_as_int(sm.rowmax[tid]);
-        sm.rowmax[tid] = __int_as_float(key >= 0 ? key : key ^ 0x7fffffff);
-    }
-
-    // ---- pass 2: p, row sums, int8 P.V ----
+    // items in 32-bit unsigned arithmetic (the host checks that they fit);
+    // query blocks slowest and from the last, so that the longest walks
+    // (last blocks, causal) start first
+    const unsigned nqb = (unsigned)((a.S + kAQ - 1) / kAQ);
+    const unsigned nbh = (unsigned)(a.B * a.Hq), hq = (unsigned)a.Hq;
+    const unsigned nitems = nqb * nbh;
+    float* slot = a.logits + (int64_t)blockIdx.x * a.slot_floats;
     const Quantizer qz(a.s_v);
     const int mt = wave & 1, nt0 = (wave >> 1) * 2;
-    v16i_a acc[2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[n][r] = 0;
     const int frow = lane & 31, fchunk = lane >> 5;
-    for (int64_t kt = kt0; kt <= kt1; ++kt) {
-        const int64_t j0 = kt * kAK;
-        __syncthreads();
-        attn_load_kt(a.K, a.ldk, base + j0, a.S - j0, hk, sm.ks);
-        // V tile -> q_v, stored transposed (row d holds the tile's 64 keys):
-        // each item is 4 keys x 4 d, stored as four 4-byte key runs
+
+    for (unsigned item = blockIdx.x; item < nitems; item += gridDim.x) {
+        const unsigned qb = nqb - 1 - item / nbh;
+        const unsigned bh = item % nbh;
+        const int64_t h = bh % hq;
+        const int64_t b = bh / hq;
+        const int64_t hk = (unsigned)h / (hq / (unsigned)a.Hkv);
+        const int64_t q0 = (int64_t)qb * kAQ;
+        const int64_t qrows = a.S - q0 < kAQ ? a.S - q0 : kAQ;
+        const int64_t base = b * a.S;                // first row of this batch entry
+        int64_t kt0, kt1;
+        attn_tile_range(a.S, a.window, qb, &kt0, &kt1);
+
+        auto allowed = [&](int64_t i, int64_t j) {
+            const int64_t lo = a.window > 0 ? i - a.window + 1 : 0;
+            return i < a.S && j <= i && j >= lo;
+        };
+
+        __syncthreads();                             // the previous item is done with LDS
+        attn_load_kt(a.Q, a.ldq, base + q0, qrows, h, sm.u.a.qs);
+        for (int e = tid; e < kAQ * kAStack; e += 256) sm.st[e / kAStack][e % kAStack] = 0.0f;
+
+        // ---- pass 1: exact logits into the slot, exact row maxima ----
+        int mimg[4];
 #pragma unroll
-        for (int it = 0; it < (kAK / 4) * (kAD / 4) / 256; ++it) {
-            const int e = tid + 256 * it;
-            const int rq = e & 15, dq = e >> 4;
-            vf4 v[4];
+        for (int x = 0; x < 4; ++x) mimg[x] = max_image(__int_as_float(0xff800000));
+        for (int64_t kt = kt0; kt <= kt1; ++kt) {
+            const int64_t j0 = kt * kAK;
+            __syncthreads();
+            attn_load_kt(a.K, a.ldk, base + j0, a.S - j0, hk, sm.u.a.ks);
+            __syncthreads();
+            float s[4][4];
+            attn_logits_from(sm.u.a.qs, sm.u.a.ks, ti, tj, a.c, s);
+            float* dst = slot + (kt - kt0) * (kAQ * kAK);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t j = j0 + 4 * rq + u;
-                v[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
-                if (j < a.S) v[u] = *reinterpret_cast<const vf4*>(a.V + (base + j) * a.ldv + hk * kAD + 4 * dq);
+            for (int x = 0; x < 4; ++x) {
+                const int i = 4 * ti + x;
+                *reinterpret_cast<vf4*>(dst + i * kAK + 4 * tj) = vf4{s[x][0], s[x][1], s[x][2], s[x][3]};
+#pragma unroll
+                for (int y = 0; y < 4; ++y)
+                    if (allowed(q0 + i, j0 + 4 * tj + y)) {
+                        const int k = max_image(s[x][y]);
+                        mimg[x] = k > mimg[x] ? k : mimg[x];
+                    }
             }
-            // codes on the quantiser's fast path; a wave with a value near a
-            // rounding midpoint redoes its values on the exact path (rows
-            // past S were loaded as zeros and quantise to 0)
-            uint32_t packed[4];
-            bool unsure = false;
+        }
+        // the 16 threads of a row group (consecutive lanes) combine their maxima
+        float m[4];
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                packed[w] = 0;
+        for (int x = 0; x < 4; ++x) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    packed[w] |= (uint32_t)(uint8_t)(int8_t)qz.q_fast(v[u][w], &unsure) << (8 * u);
+            for (int sh = 1; sh < 16; sh <<= 1) {
+                const int o = __shfl_xor(mimg[x], sh, 16);
+                mimg[x] = o > mimg[x] ? o : mimg[x];
             }
-            if (__ballot(unsure)) {
+            m[x] = from_max_image(mimg[x]);
+        }
+        if (tj == 0) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) sm.rowmax[4 * ti + x] = m[x];
+        }
+
+        // ---- pass 2: p, row sums, int8 P.V ----
+        v16i_a acc[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[n][r] = 0;
+        for (int64_t kt = kt0; kt <= kt1; ++kt) {
+            const int64_t j0 = kt * kAK;
+            // this thread's logits of the tile, as it stored them in pass 1
+            const float* src = slot + (kt - kt0) * (kAQ * kAK);
+            vf4 sv[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) sv[x] = *reinterpret_cast<const vf4*>(src + (4 * ti + x) * kAK + 4 * tj);
+            // every thread is past the previous tile's P.V reads (and, for the
+            // first tile, past pass 1's reads of the Q and K tiles)
+            __syncthreads();
+            // V tile -> q_v, stored transposed (row d holds the tile's 64 keys):
+            // each item is 4 keys x 4 d, stored as four 4-byte key runs
+#pragma unroll
+            for (int it = 0; it < (kAK / 4) * (kAD / 4) / 256; ++it) {
+                const int e = tid + 256 * it;
+                const int rq = e & 15, dq = e >> 4;
+                vf4 v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t j = j0 + 4 * rq + u;
+                    v[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
+                    if (j < a.S) v[u] = *reinterpret_cast<const vf4*>(a.V + (base + j) * a.ldv + hk * kAD + 4 * dq);
+                }
+                // codes on the quantiser's fast path; a wave with a value near a
+                // rounding midpoint redoes its values on the exact path (rows
+                // past S were loaded as zeros and quantise to 0)
+                uint32_t packed[4];
+                bool unsure = false;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     packed[w] = 0;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        bool in;
-                        packed[w] |= (uint32_t)(uint8_t)(int8_t)qz.q(v[u][w], &in) << (8 * u);
+                    for (int u = 0; u < 4; ++u)
+                        packed[w] |= (uint32_t)(uint8_t)(int8_t)qz.q_fast(v[u][w], &unsure) << (8 * u);
+                }
+                if (__ballot(unsure)) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        packed[w] = 0;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            bool in;
+                            packed[w] |= (uint32_t)(uint8_t)(int8_t)qz.q(v[u][w], &in) << (8 * u);
+                        }
                     }
                 }
-            }
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const int d = 4 * dq + w, r = 4 * rq;
-                *reinterpret_cast<uint32_t*>(&sm.u.pv.vq[d][16 * aswz(d, r >> 4) + (r & 15)]) = packed[w];
-            }
-        }
-        __syncthreads();
-        float s[4][4];
-        attn_logits_from(sm.qs, sm.ks, ti, tj, a.c, s);
-        float pair[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int i = 4 * ti + x;
-            const float m = sm.rowmax[i];
-            float p[4];
-            uint32_t packed = 0;
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                const int j = 4 * tj + y;
-                p[y] = allowed(q0 + i, j0 + j) ? own_exp(f_sub(s[x][y], m), a.ek) : 0.0f;
-                float r = f_rne(f_mul(p[y], 127.0f));
-                r = r > 127.0f ? 127.0f : (r < 0.0f ? 0.0f : r);
-                packed |= (uint32_t)(int)r << (8 * y);
-            }
-            *reinterpret_cast<uint32_t*>(&sm.u.pv.pq[i][16 * aswz(i, tj >> 2) + 4 * (tj & 3)]) = packed;
-            // 32-key block sums: lanes tj = 8k .. 8k+7 hold block k's keys in
-            // order; the running sum walks through them one lane at a time
-            float run = 0.0f;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float in = dpp_shr1(run);
-                if ((tj & 7) == t) {
-                    float x0 = t == 0 ? p[0] : f_add(in, p[0]);
-                    x0 = f_add(x0, p[1]);
-                    x0 = f_add(x0, p[2]);
-                    run = f_add(x0, p[3]);
+                for (int w = 0; w < 4; ++w) {
+                    const int d = 4 * dq + w, r = 4 * rq;
+                    *reinterpret_cast<uint32_t*>(&sm.u.pv.vq[d][16 * aswz(d, r >> 4) + (r & 15)]) = packed[w];
                 }
             }
-            // lane tj = 15: block 1's sum; block 0's sits in lane tj = 7
-            pair[x] = f_add(dpp_shr8(run), run);
-        }
-        // push the tile's pair sum (complete subtree of blocks 2kt, 2kt+1)
-        if (tj == 15) {
+            float pair[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int i = 4 * ti + x;
-                float v = pair[x];
-                unsigned cnt = (unsigned)kt;
-                int L = 0;
-                while (cnt & 1u) {
-                    v = f_add(sm.st[i][L], v);
-                    cnt >>= 1;
-                    ++L;
+                float p[4];
+                uint32_t packed = 0;
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    const int j = 4 * tj + y;
+                    p[y] = allowed(q0 + i, j0 + j) ? own_exp(f_sub(sv[x][y], m[x]), a.ek) : 0.0f;
+                    float r = f_rne(f_mul(p[y], 127.0f));
+                    r = r > 127.0f ? 127.0f : (r < 0.0f ? 0.0f : r);
+                    packed |= (uint32_t)(int)r << (8 * y);
                 }
-                sm.st[i][L] = v;
+                *reinterpret_cast<uint32_t*>(&sm.u.pv.pq[i][16 * aswz(i, tj >> 2) + 4 * (tj & 3)]) = packed;
+                // 32-key block sums: lanes tj = 8k .. 8k+7 hold block k's keys in
+                // order; the running sum walks through them one lane at a time
+                float run = 0.0f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float in = dpp_shr1(run);
+                    if ((tj & 7) == t) {
+                        float x0 = t == 0 ? p[0] : f_add(in, p[0]);
+                        x0 = f_add(x0, p[1]);
+                        x0 = f_add(x0, p[2]);
+                        run = f_add(x0, p[3]);
+                    }
+                }
+                // lane tj = 15: block 1's sum; block 0's sits in lane tj = 7
+                pair[x] = f_add(dpp_shr8(run), run);
+            }
+            // push the tile's pair sum (complete subtree of blocks 2kt, 2kt+1)
+            if (tj == 15) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int i = 4 * ti + x;
+                    float v = pair[x];
+                    unsigned cnt = (unsigned)kt;
+                    int L = 0;
+                    while (cnt & 1u) {
+                        v = f_add(sm.st[i][L], v);
+                        cnt >>= 1;
+                        ++L;
+                    }
+                    sm.st[i][L] = v;
+                }
+            }
+            __syncthreads();
+            // P.V on the matrix cores: this wave's 32 rows x 64 columns, k = 64 keys
+#pragma unroll
+            for (int ks = 0; ks < kAK / 32; ++ks) {
+                const int chunk = fchunk + 2 * ks;
+                const int ar = mt * 32 + frow;
+                const v4i_a A = *reinterpret_cast<const v4i_a*>(&sm.u.pv.pq[ar][16 * aswz(ar, chunk)]);
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    const int br = (nt0 + n) * 32 + frow;
+                    const v4i_a Bf = *reinterpret_cast<const v4i_a*>(&sm.u.pv.vq[br][16 * aswz(br, chunk)]);
+                    acc[n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, Bf, acc[n], 0, 0, 0);
+                }
             }
         }
         __syncthreads();
-        // P.V on the matrix cores: this wave's 32 rows x 64 columns, k = 64 keys
-#pragma unroll
-        for (int ks = 0; ks < kAK / 32; ++ks) {
-            const int chunk = fchunk + 2 * ks;
-            const int ar = mt * 32 + frow;
-            const v4i_a A = *reinterpret_cast<const v4i_a*>(&sm.u.pv.pq[ar][16 * aswz(ar, chunk)]);
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int br = (nt0 + n) * 32 + frow;
-                const v4i_a Bf = *reinterpret_cast<const v4i_a*>(&sm.u.pv.vq[br][16 * aswz(br, chunk)]);
-                acc[n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, Bf, acc[n], 0, 0, 0);
+        // l_i: final merge of the pair stack at the absolute tile count
+        if (tid < kAQ) {
+            const unsigned count = (unsigned)(kt1 + 1);
+            float root = 0.0f;
+            bool have = false;
+            for (int L = 0; L < kAStack; ++L)
+                if (count & (1u << L)) {
+                    root = have ? f_add(sm.st[tid][L], root) : sm.st[tid][L];
+                    have = true;
+                }
+            sm.rowdiv[tid] = f_mul(root, 127.0f);
+            if (a.stats && tid < qrows) {
+                float* st2 = a.stats + 2 * ((base + q0 + tid) * a.Hq + h);
+                st2[0] = sm.rowmax[tid];
+                st2[1] = root;
             }
         }
+        __syncthreads();
+        // O = (fl(acc) * s_v) / (l * 127)
+        const int col_l = lane & 31, row_q = (lane >> 5) * 4;
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = mt * 32 + (r >> 2) * 8 + row_q + (r & 3);
+                const int d = (nt0 + n) * 32 + col_l;
+                if (i < qrows) {
+                    const float y = f_div(f_mul((float)acc[n][r], a.s_v), sm.rowdiv[i]);
+                    a.O[(base + q0 + i) * a.ldo + h * kAD + d] = y;
+                }
+            }
     }
-    __syncthreads();
-    // l_i: final merge of the pair stack at the absolute tile count
-    if (tid < kAQ) {
-        const unsigned count = (unsigned)(kt1 + 1);
-        float root = 0.0f;
-        bool have = false;
-        for (int L = 0; L < kAStack; ++L)
-            if (count & (1u << L)) {
-                root = have ? f_add(sm.st[tid][L], root) : sm.st[tid][L];
-                have = true;
-            }
-        sm.rowdiv[tid] = f_mul(root, 127.0f);
-        if (a.stats && tid < qrows) {
-            float* st2 = a.stats + 2 * ((base + q0 + tid) * a.Hq + h);
-            st2[0] = sm.rowmax[tid];
-            st2[1] = root;
-        }
+}
+
+// Tiles of the longest key walk of any query block, and the persistent grid:
+// two workgroups per CU on the 256 CUs of an MI355X (each walks items until
+// none is left, so the grid size changes only the split of the work)
+constexpr int64_t kAttnGrid = 512;
+
+int64_t attn_fwd_max_tiles(int64_t S, int64_t window) {
+    int64_t best = 0;
+    for (int64_t qb = 0; qb * kAQ < S; ++qb) {
+        int64_t kt0, kt1;
+        attn_tile_range(S, window, qb, &kt0, &kt1);
+        best = kt1 - kt0 + 1 > best ? kt1 - kt0 + 1 : best;
     }
-    __syncthreads();
-    // O = (fl(acc) * s_v) / (l * 127)
-    const int col_l = lane & 31, row_q = (lane >> 5) * 4;
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = mt * 32 + (r >> 2) * 8 + row_q + (r & 3);
-            const int d = (nt0 + n) * 32 + col_l;
-            if (i < qrows) {
-                const float y = f_div(f_mul((float)acc[n][r], a.s_v), sm.rowdiv[i]);
-                a.O[(base + q0 + i) * a.ldo + h * kAD + d] = y;
-            }
-        }
+    return best;
+}
+
+int64_t attn_fwd_grid(int64_t B, int64_t S, int64_t Hq) {
+    const int64_t items = B * Hq * ceil_div(S, kAQ);
+    return items < kAttnGrid ? items : kAttnGrid;
+}
+
+size_t attn_fwd_ws_bytes(int64_t B, int64_t S, int64_t Hq, int64_t window) {
+    if (B <= 0 || S <= 0) return 256;
+    return (size_t)attn_fwd_grid(B, S, Hq) * (size_t)attn_fwd_max_tiles(S, window) * (size_t)(kAQ * kAK) *
+               sizeof(float) + 256;
 }
 
 hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
                            int64_t Hkv, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
-                           float* O, int64_t ldo, float* stats, const ExpConsts& ek, hipStream_t st) {
+                           float* O, int64_t ldo, float* stats, float* logits, const ExpConsts& ek,
+                           hipStream_t st) {
     if (B == 0 || S == 0) return hipSuccess;
     AttnArgs a;
-    a.Q = Q; a.K = K; a.V = V; a.O = O; a.stats = stats;
-    a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.window = window;
+    a.Q = Q; a.K = K; a.V = V; a.O = O; a.stats = stats; a.logits = logits;
+    a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.window = window;
+    a.slot_floats = attn_fwd_max_tiles(S, window) * (kAQ * kAK);
     // c = fl(1 / fl(sqrt(D))): both binary64 results are rounded once more to
     // binary32, which is innocuous for sqrt and division (53 >= 2 * 24 + 2)
     a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
@@ -494,9 +449,8 @@ hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnSmem));
         e != hipSuccess)
         return e;
-    const int64_t blocks = B * Hq * ceil_div(S, kAQ);
-    if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)blocks), dim3(256), sizeof(AttnSmem), st, a);
+    if (B * Hq * ceil_div(S, kAQ) > 0xffffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)attn_fwd_grid(B, S, Hq)), dim3(256), sizeof(AttnSmem), st, a);
     return hipGetLastError();
 }
 

@@ -302,12 +302,21 @@ BRL_API brl_status adamw_step(float* p, const float* g, float* m, float* v, int6
  * accumulators); every ld a multiple of 4 and >= heads*D; Q, K, V, O device
  * pointers 16-byte aligned; O must not overlap Q, K or V.  Inputs must be
  * finite.  stats (nullable, device, [B*S*Hq][2] floats, row (b*S + i)*Hq + h)
- * receives (m_i, l_i) for the backward.  No workspace; asynchronous on
- * `stream`.
+ * receives (m_i, l_i) for the backward.  ws: device workspace of at least
+ * attn_fwd_workspace_bytes(B, S, Hq, Hkv, window) bytes, 256-byte aligned,
+ * caller-owned, used only during the call (it holds the exact logits between
+ * the two passes); BRL_EWORKSPACE if too small.  Asynchronous on `stream`.
  */
 BRL_API brl_status attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
                             int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window,
-                            float s_v, float* O, int64_t ldo, float* stats, void* stream);
+                            float s_v, float* O, int64_t ldo, float* stats, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Bytes of workspace attn_fwd needs for these sizes (0 for sizes it rejects).
+ * It grows with the longest key walk of a query block (the window, or S for
+ * full causal attention) and not with B or the head count beyond 512
+ * (query block, head) items. */
+BRL_API size_t attn_fwd_workspace_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t window);
 
 /*
  * dQ of attn_fwd with 64-bit fixed-point accumulation (onedev.kr summary,

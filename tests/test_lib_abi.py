@@ -285,8 +285,9 @@ def test_attention_rejects_bad_arguments_without_launching():
 
     def call(**kw):
         a = {**ok, **kw}
+        ws = kw.get("ws", C.c_void_p(0x100000))
         return L.attn_fwd(kw.get("Q", p), p, p, a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["ldq"], a["ldk"],
-                          a["ldv"], 0, 0.05, kw.get("O", p), a["ldo"], None, None)
+                          a["ldv"], 0, 0.05, kw.get("O", p), a["ldo"], None, ws, kw.get("ws_bytes", 0), None)
 
     assert call(D=64) == brl.BRL_ESHAPE
     assert call(Hq=3) == brl.BRL_ESHAPE
@@ -297,6 +298,14 @@ def test_attention_rejects_bad_arguments_without_launching():
     assert call(Q=None) == brl.BRL_EINVAL
     assert call(O=C.c_void_p(0x10004)) == brl.BRL_EINVAL
     assert call(S=0) == brl.BRL_OK            # nothing to do, nothing launched
+    need = L.attn_fwd_workspace_bytes(1, 64, 4, 2, 0)
+    assert need >= 64 * 64 * 4 and L.attn_fwd_workspace_bytes(1, 64, 3, 2, 0) == 0
+    assert call(ws_bytes=need - 1) == brl.BRL_EWORKSPACE
+    assert call(ws=C.c_void_p(0x100010), ws_bytes=need) == brl.BRL_EINVAL     # not 256-byte aligned
+    # the workspace holds one slot of 64 x 64 logits per key tile of the longest walk, per workgroup:
+    # window 512 from a tile-aligned query block reaches back 511 keys, 9 tiles with its own
+    assert L.attn_fwd_workspace_bytes(4, 4096, 16, 4, 512) == 512 * 9 * 64 * 64 * 4 + 256
+    assert L.attn_fwd_workspace_bytes(4, 4096, 16, 4, 0) == 512 * 64 * 64 * 64 * 4 + 256
     assert L.attn_bwd_dq(p, p, p, p, p, p, 1, 64, 4, 2, 64, 512, 256, 256, 512, 0, 0.05, p, None) == brl.BRL_ESHAPE
     assert L.attn_bwd_dq(p, p, p, p, p, None, 1, 64, 4, 2, 128, 512, 256, 256, 512, 0, 0.05, p, None) == brl.BRL_EINVAL
     assert L.attn_bwd_dq(p, p, p, p, C.c_void_p(0x10008), p, 1, 64, 4, 2, 128, 512, 256, 256, 512, 0, 0.05, p,
