@@ -617,7 +617,7 @@ static bool al16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) 
 size_t attn_fwd_workspace_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t window) {
     if (B < 0 || S < 0 || S > 133143 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return 0;
     if (B * Hq * ((S + 63) / 64) > 0xffffffffLL) return 0;
-    return attn_fwd_ws_bytes(B, S, Hq, window);
+    return attn_fwd_ws_bytes(B, S, Hq, Hkv, window);
 }
 
 brl_status attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
@@ -631,7 +631,7 @@ brl_status attn_fwd(const float* Q, const float* K, const float* V, int64_t B, i
         return fail(BRL_EINVAL, "attn_fwd: pointers must be 16-byte aligned");
     if (stats && !aligned4(stats)) return fail(BRL_EINVAL, "attn_fwd: stats must be 4-byte aligned");
     if (B * Hq * ((S + 63) / 64) > 0xffffffffLL) return fail(BRL_ESHAPE, "attn_fwd: too many query blocks");
-    const size_t need = attn_fwd_ws_bytes(B, S, Hq, window);
+    const size_t need = attn_fwd_ws_bytes(B, S, Hq, Hkv, window);
     if (!aligned256(ws)) return fail(BRL_EINVAL, "attn_fwd: workspace must be 256-byte aligned");
     if (!ws || ws_bytes < need) return fail(BRL_EWORKSPACE, "attn_fwd: workspace %zu < %zu bytes", ws_bytes, need);
     return check_hip(launch_attn_fwd(Q, K, V, B, S, Hq, Hkv, ldq, ldk, ldv, window, s_v, O, ldo, stats,

@@ -57,7 +57,8 @@ struct AttnArgs {
     float* O;
     float* stats;          // optional (m_i, l_i) per row (b*S + i)*Hq + h
     float* logits;         // slot_floats floats per workgroup: [tile][64 rows][64 keys]
-    int64_t B, S, Hq, Hkv, ldq, ldk, ldv, ldo, window, slot_floats;
+    const int8_t* vcodes;  // q_v tiles [B][Hkv][tiles][kAD * kAK], laid out as sm.u.pv.vq
+    int64_t B, S, Hq, Hkv, ldq, ldk, ldv, ldo, window, slot_floats, vtiles;
     float c, s_v;
     ExpConsts ek;
 };
@@ -153,6 +154,66 @@ __device__ __forceinline__ float dpp_shr8(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
 }
 
+// q_v of one 64-key tile of V (keys j0 .. j0+63 of rows base + j, KV head
+// hk) into the tile layout the P.V product reads: row d holds the 64 keys'
+// codes, its 16-byte chunks swizzled by aswz.  Each of the 256 threads owns
+// items of 4 keys x 4 d, stored as four 4-byte key runs.  Codes on the
+// quantiser's fast path; a wave with a value near a rounding midpoint redoes
+// its values on the exact path.  Keys at or past S quantise zeros (code 0).
+__device__ __forceinline__ void attn_quant_v_tile(const float* V, int64_t ldv, int64_t base, int64_t j0, int64_t S,
+                                                  int64_t hk, const Quantizer& qz, int8_t* tile) {
+#pragma unroll
+    for (int it = 0; it < (kAK / 4) * (kAD / 4) / 256; ++it) {
+        const int e = threadIdx.x + 256 * it;
+        const int rq = e & 15, dq = e >> 4;
+        vf4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t j = j0 + 4 * rq + u;
+            v[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (j < S) v[u] = *reinterpret_cast<const vf4*>(V + (base + j) * ldv + hk * kAD + 4 * dq);
+        }
+        uint32_t packed[4];
+        bool unsure = false;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            packed[w] = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                packed[w] |= (uint32_t)(uint8_t)(int8_t)qz.q_fast(v[u][w], &unsure) << (8 * u);
+        }
+        if (__ballot(unsure)) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                packed[w] = 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    bool in;
+                    packed[w] |= (uint32_t)(uint8_t)(int8_t)qz.q(v[u][w], &in) << (8 * u);
+                }
+            }
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int d = 4 * dq + w, r = 4 * rq;
+            *reinterpret_cast<uint32_t*>(tile + d * kAK + 16 * aswz(d, r >> 4) + (r & 15)) = packed[w];
+        }
+    }
+}
+
+// q_v of every key tile, once per (batch, KV head): workgroup (b, hk, kt)
+// writes tile kt of [B][Hkv][tiles][kAD * kAK] codes
+__global__ __launch_bounds__(256) void attn_quant_v_kernel(const float* __restrict__ V, int64_t ldv, int64_t S,
+                                                           int64_t Hkv, int64_t tiles, float s_v,
+                                                           int8_t* __restrict__ codes) {
+    // 32-bit unsigned index arithmetic (the host checks that the grid fits)
+    const unsigned t = (unsigned)tiles, bh = blockIdx.x / t;
+    const int64_t kt = blockIdx.x % t;
+    const int64_t hk = bh % (unsigned)Hkv, b = bh / (unsigned)Hkv;
+    const Quantizer qz(s_v);
+    attn_quant_v_tile(V, ldv, b * S, kt * kAK, S, hk, qz, codes + blockIdx.x * (int64_t)(kAD * kAK));
+}
+
 // order-preserving integer image of a binary32 value (negative values:
 // bits ^ 0x7fffffff), so that an integer maximum is the float maximum
 __device__ __forceinline__ int max_image(float f) {
@@ -184,7 +245,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     const unsigned nbh = (unsigned)(a.B * a.Hq), hq = (unsigned)a.Hq;
     const unsigned nitems = nqb * nbh;
     float* slot = a.logits + (int64_t)blockIdx.x * a.slot_floats;
-    const Quantizer qz(a.s_v);
     const int mt = wave & 1, nt0 = (wave >> 1) * 2;
     const int frow = lane & 31, fchunk = lane >> 5;
 
@@ -262,51 +322,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
             vf4 sv[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) sv[x] = *reinterpret_cast<const vf4*>(src + (4 * ti + x) * kAK + 4 * tj);
+            // the tile's q_v codes (8 KB), copied as they lie
+            const v4i_a* vsrc = reinterpret_cast<const v4i_a*>(a.vcodes + ((b * a.Hkv + hk) * a.vtiles + kt) *
+                                                                           (int64_t)(kAD * kAK));
+            v4i_a vt[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) vt[k] = vsrc[tid + 256 * k];
             // every thread is past the previous tile's P.V reads (and, for the
             // first tile, past pass 1's reads of the Q and K tiles)
             __syncthreads();
-            // V tile -> q_v, stored transposed (row d holds the tile's 64 keys):
-            // each item is 4 keys x 4 d, stored as four 4-byte key runs
 #pragma unroll
-            for (int it = 0; it < (kAK / 4) * (kAD / 4) / 256; ++it) {
-                const int e = tid + 256 * it;
-                const int rq = e & 15, dq = e >> 4;
-                vf4 v[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int64_t j = j0 + 4 * rq + u;
-                    v[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
-                    if (j < a.S) v[u] = *reinterpret_cast<const vf4*>(a.V + (base + j) * a.ldv + hk * kAD + 4 * dq);
-                }
-                // codes on the quantiser's fast path; a wave with a value near a
-                // rounding midpoint redoes its values on the exact path (rows
-                // past S were loaded as zeros and quantise to 0)
-                uint32_t packed[4];
-                bool unsure = false;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    packed[w] = 0;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        packed[w] |= (uint32_t)(uint8_t)(int8_t)qz.q_fast(v[u][w], &unsure) << (8 * u);
-                }
-                if (__ballot(unsure)) {
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        packed[w] = 0;
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            bool in;
-                            packed[w] |= (uint32_t)(uint8_t)(int8_t)qz.q(v[u][w], &in) << (8 * u);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const int d = 4 * dq + w, r = 4 * rq;
-                    *reinterpret_cast<uint32_t*>(&sm.u.pv.vq[d][16 * aswz(d, r >> 4) + (r & 15)]) = packed[w];
-                }
-            }
+            for (int k = 0; k < 2; ++k) reinterpret_cast<v4i_a*>(&sm.u.pv.vq[0][0])[tid + 256 * k] = vt[k];
             float pair[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
@@ -424,10 +450,15 @@ int64_t attn_fwd_grid(int64_t B, int64_t S, int64_t Hq) {
     return items < kAttnGrid ? items : kAttnGrid;
 }
 
-size_t attn_fwd_ws_bytes(int64_t B, int64_t S, int64_t Hq, int64_t window) {
-    if (B <= 0 || S <= 0) return 256;
+// workspace: the logit slots, then the q_v codes (both 256-byte aligned)
+static size_t attn_fwd_slots_bytes(int64_t B, int64_t S, int64_t Hq, int64_t window) {
     return (size_t)attn_fwd_grid(B, S, Hq) * (size_t)attn_fwd_max_tiles(S, window) * (size_t)(kAQ * kAK) *
-               sizeof(float) + 256;
+           sizeof(float);
+}
+
+size_t attn_fwd_ws_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t window) {
+    if (B <= 0 || S <= 0) return 256;
+    return attn_fwd_slots_bytes(B, S, Hq, window) + (size_t)(B * Hkv * ceil_div(S, kAK)) * (kAD * kAK) + 256;
 }
 
 hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
@@ -439,6 +470,9 @@ hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64
     a.Q = Q; a.K = K; a.V = V; a.O = O; a.stats = stats; a.logits = logits;
     a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.window = window;
     a.slot_floats = attn_fwd_max_tiles(S, window) * (kAQ * kAK);
+    a.vtiles = ceil_div(S, kAK);
+    int8_t* codes = reinterpret_cast<int8_t*>(logits) + attn_fwd_slots_bytes(B, S, Hq, window);
+    a.vcodes = codes;
     // c = fl(1 / fl(sqrt(D))): both binary64 results are rounded once more to
     // binary32, which is innocuous for sqrt and division (53 >= 2 * 24 + 2)
     a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
@@ -450,6 +484,8 @@ hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64
         e != hipSuccess)
         return e;
     if (B * Hq * ceil_div(S, kAQ) > 0xffffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_quant_v_kernel, dim3((unsigned)(B * Hkv * a.vtiles)), dim3(256), 0, st, V, ldv, S, Hkv,
+                       a.vtiles, s_v, codes);
     hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)attn_fwd_grid(B, S, Hq)), dim3(256), sizeof(AttnSmem), st, a);
     return hipGetLastError();
 }

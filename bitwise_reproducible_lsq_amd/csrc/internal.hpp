@@ -171,8 +171,9 @@ brl_status report_error(brl_status s, const char* msg);
 brl_status report_hip(hipError_t e, const char* what);
 
 // ---- attention (int8 P.V) ----------------------------------------------------
-// workspace of attn_fwd: one slot of stored logits per workgroup of its grid
-size_t attn_fwd_ws_bytes(int64_t B, int64_t S, int64_t Hq, int64_t window);
+// workspace of attn_fwd: one slot of stored logits per workgroup of its grid,
+// then the q_v codes of every key tile
+size_t attn_fwd_ws_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t window);
 hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
                            int64_t Hkv, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
                            float* O, int64_t ldo, float* stats, float* logits, const ExpConsts& ek,

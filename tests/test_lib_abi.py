@@ -302,10 +302,12 @@ def test_attention_rejects_bad_arguments_without_launching():
     assert need >= 64 * 64 * 4 and L.attn_fwd_workspace_bytes(1, 64, 3, 2, 0) == 0
     assert call(ws_bytes=need - 1) == brl.BRL_EWORKSPACE
     assert call(ws=C.c_void_p(0x100010), ws_bytes=need) == brl.BRL_EINVAL     # not 256-byte aligned
-    # the workspace holds one slot of 64 x 64 logits per key tile of the longest walk, per workgroup:
-    # window 512 from a tile-aligned query block reaches back 511 keys, 9 tiles with its own
-    assert L.attn_fwd_workspace_bytes(4, 4096, 16, 4, 512) == 512 * 9 * 64 * 64 * 4 + 256
-    assert L.attn_fwd_workspace_bytes(4, 4096, 16, 4, 0) == 512 * 64 * 64 * 64 * 4 + 256
+    # the workspace holds one slot of 64 x 64 logits per key tile of the longest walk, per workgroup
+    # (window 512 from a tile-aligned query block reaches back 511 keys: 9 tiles with its own), then
+    # the int8 codes of V, 128 x 64 per key tile and KV head
+    codes = 4 * 4 * 64 * 128 * 64
+    assert L.attn_fwd_workspace_bytes(4, 4096, 16, 4, 512) == 512 * 9 * 64 * 64 * 4 + codes + 256
+    assert L.attn_fwd_workspace_bytes(4, 4096, 16, 4, 0) == 512 * 64 * 64 * 64 * 4 + codes + 256
     assert L.attn_bwd_dq(p, p, p, p, p, p, 1, 64, 4, 2, 64, 512, 256, 256, 512, 0, 0.05, p, None) == brl.BRL_ESHAPE
     assert L.attn_bwd_dq(p, p, p, p, p, None, 1, 64, 4, 2, 128, 512, 256, 256, 512, 0, 0.05, p, None) == brl.BRL_EINVAL
     assert L.attn_bwd_dq(p, p, p, p, C.c_void_p(0x10008), p, 1, 64, 4, 2, 128, 512, 256, 256, 512, 0, 0.05, p,
