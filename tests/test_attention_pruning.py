@@ -1,20 +1,22 @@
-"""The attention forward's first pass: which keys may be skipped when the
-exact row maximum is formed.
+"""Skipping keys when a row's exact maximum is formed from approximate
+logits: a record of why such a rule must bound from both sides.
 
-The forward (attn_fwd; onedev.kr summary of Open-1B, "Use", attention
-paragraph: logits and softmax in high precision) needs the exact maximum
-m_i of the canonical binary32 logits of each row.  A cheap pass forms
-approximate logits a_ij from bf16 operands on the matrix cores; each lies
-within E_ij = c * 0.0158 * |q_i| |k_j| + 2^-80 of the exact logit s_ij.
-Only keys that may still hold the maximum get their exact logit.
+The attention forward (attn_fwd; onedev.kr summary of Open-1B, "Use",
+attention paragraph: logits and softmax in high precision) needs the exact
+maximum m_i of the canonical binary32 logits of each row.  It now computes
+every logit exactly once and keeps them in its workspace, so it skips no
+key.  An earlier version first formed approximate logits a_ij from bf16
+operands on the matrix cores, each within E_ij = c * 0.0158 * |q_i| |k_j| +
+2^-80 of the exact logit s_ij, and computed exact logits only for keys that
+could still hold the maximum.
 
-This file emulates that pass on the host (bf16 round-to-nearest-even of the
-operands, fp32 sums in several orders, the kernel's bound) and checks the
-rule the kernel uses: keep key j unless a_ij + E_ij < L_i, with L_i the
-largest a_il - E_il over the row's keys.  It also shows that the earlier
-rule, which dropped j when a_ij < A_i - 2 E_ij with A_i the largest
-approximate logit, loses the true maximum on a constructed row whose keys
-differ in norm.
+This file emulates that approximation on the host (bf16 round-to-nearest-
+even of the operands, fp32 sums in several orders, the bound) and checks
+the sound rule (keep key j unless a_ij + E_ij < L_i, with L_i the largest
+a_il - E_il over the row's keys).  It also shows that the first rule, which
+dropped j when a_ij < A_i - 2 E_ij with A_i the largest approximate logit,
+loses the true maximum on a constructed row whose keys differ in norm.  The
+GPU tests run the same witness through the kernels.
 """
 import numpy as np
 
