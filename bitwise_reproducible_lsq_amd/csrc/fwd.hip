@@ -116,8 +116,11 @@ hipError_t launch_quantize(const float* v, int64_t rows, int64_t cols, const flo
                            int64_t swiglu_half, hipStream_t st) {
     if (rows_p <= 0 || cols_p <= 0) return hipSuccess;
     const unsigned gx = (unsigned)ceil_div(cols_p / 4, 256);
+    // at most 2048 row groups of workgroups, so large inputs take a few
+    // grid-stride iterations per thread: X of the QKV layer 35.3 -> 33.5 us,
+    // of the down projection 90 -> 84 us, against one iteration per thread
     const int64_t blocks = ceil_div(rows_p, kQRows);
-    const unsigned gy = (unsigned)(blocks < 65535 ? blocks : 65535);
+    const unsigned gy = (unsigned)(blocks < 2048 ? blocks : 2048);
     hipLaunchKernelGGL(quantize_kernel, dim3(gx, gy), dim3(256), 0, st, v, rows, cols, s_dev, s_host,
                        q, rows_p, cols_p, swiglu_half);
     return hipGetLastError();
