@@ -19,9 +19,11 @@
 // Forward: a persistent grid of workgroups, each walking (batch, query head,
 // block of 64 queries) items, longest first; two passes over the 64-key
 // tiles that meet the block's key range:
-//   pass 1: exact logits (VALU, 4 x 4 per thread, d-blocks of 32 summed left
-//           to right, then as a pairwise tree), stored in the workgroup's
-//           slot of the workspace, and the exact row maxima (order-free);
+//   pass 1: exact logits on the product engine below (the matrix cores form
+//           each product, rounded on its own; the VALU adds d-blocks of 32
+//           left to right, then the pairwise tree), stored in the
+//           workgroup's slot of the workspace, and the exact row maxima
+//           (order-free integer maxima);
 //   pass 2: the stored logits -> p -> the 32-key block sums, each a
 //           left-to-right chain through the 8 lanes that hold its keys (DPP
 //           shifts within a 16-lane row); a tile's two blocks are a complete
@@ -29,7 +31,8 @@
 //           pushed on the row's binary-counter stack of pairs at index kt;
 //           q_p and q_v staged as int8 in LDS and multiplied on
 //           v_mfma_i32_32x32x32_i8 into int32 accumulators.
-// Each thread reads back in pass 2 exactly the logits it wrote in pass 1.
+// Pass 2 reads the logits with another thread mapping (4 x 4 per thread)
+// after a workgroup barrier.
 // Pairs before the first real one are +0 subtrees (the stack starts zeroed)
 // and merging with +0 is exact, so this is CanonSum over the whole axis.
 // LDS is kept under 80 KB so that two workgroups share a CU.
@@ -50,6 +53,13 @@ constexpr int kAQ = 64;           // queries per workgroup
 constexpr int kAK = 64;           // keys per tile
 constexpr int kAStack = 12;       // pair-stack levels: up to 2^12 key tiles
 
+typedef float v16f_a __attribute__((ext_vector_type(16)));
+
+constexpr int kKvThreads = 512;
+constexpr int kKvRow = kAD + 4;     // floats per LDS row of K, Q and dO
+constexpr int kKvRowQ = kAD + 16;   // bytes per LDS row of q_v
+constexpr int kKvRowT = kAQ + 4;    // floats per LDS row of the key-major tiles
+
 struct AttnArgs {
     const float* Q;
     const float* K;
@@ -66,8 +76,8 @@ struct AttnArgs {
 struct AttnSmem {
     union {
         struct {
-            float qs[kAD][kAQ];     // Q tile, d-major
-            float ks[kAD][kAK];     // K tile, d-major
+            float qr[kAQ][kKvRow];  // Q tile, row-major
+            float kr[kAK][kKvRow];  // K tile, key-major
         } a;                        // pass 1
         struct {
             int8_t pq[kAQ][kAK];    // q_p, rows of 64 keys, 16-byte chunks swizzled
@@ -75,76 +85,12 @@ struct AttnSmem {
         } pv;                       // pass 2
     } u;
     float st[kAQ][kAStack];         // per-row stacks of key-tile pair sums
-    float rowmax[kAQ];
+    int rowmax[kAQ];                // row maxima as order-preserving integer images
     float rowdiv[kAQ];              // l_i * 127
 };
 static_assert(sizeof(AttnSmem) <= 81920, "two workgroups per CU");
 
 __device__ __forceinline__ int aswz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
-
-// CanonSum over d of A[d][4ti + x] * B[d][4tj + y] for this thread's 4 x 4
-// outputs: d-blocks of 32 summed left to right, then (b0 + b1) + (b2 + b3)
-__device__ __forceinline__ void canon_dot4x4(const float (*A)[kAQ], const float (*B)[kAK], int ti, int tj,
-                                             float s[4][4]) {
-    float b01[4][4], b2[4][4], cur[4][4];
-#pragma unroll
-    for (int blk = 0; blk < kAD / 32; ++blk) {
-#pragma unroll 4
-        for (int dd = 0; dd < 32; ++dd) {
-            const int d = blk * 32 + dd;
-            const vf4 a = *reinterpret_cast<const vf4*>(&A[d][4 * ti]);
-            const vf4 b = *reinterpret_cast<const vf4*>(&B[d][4 * tj]);
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-#pragma unroll
-                for (int y = 0; y < 4; ++y) {
-                    const float pr = f_mul(a[x], b[y]);
-                    cur[x][y] = dd == 0 ? pr : f_add(cur[x][y], pr);
-                }
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                if (blk == 0) b01[x][y] = cur[x][y];
-                if (blk == 1) b01[x][y] = f_add(b01[x][y], cur[x][y]);
-                if (blk == 2) b2[x][y] = cur[x][y];
-                if (blk == 3) s[x][y] = f_add(b01[x][y], f_add(b2[x][y], cur[x][y]));
-            }
-    }
-}
-
-// 16 logits of this thread: rows 4ti..4ti+3, keys 4tj..4tj+3 of the tile
-__device__ __forceinline__ void attn_logits_from(const float (*qs)[kAQ], const float (*ks)[kAK], int ti, int tj,
-                                                 float c, float s[4][4]) {
-    canon_dot4x4(qs, ks, ti, tj, s);
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) s[x][y] = f_mul(s[x][y], c);
-}
-
-// 64 rows (rows_left of them real) x 128 floats of head `head` into
-// dst[d][row]: each item is 4 rows x 4 d, loaded as four 16-byte rows and
-// stored as four 16-byte columns
-template <int NT = 256>
-__device__ __forceinline__ void attn_load_kt(const float* src, int64_t ld, int64_t row0, int64_t rows_left,
-                                             int64_t head, float (*dst)[kAK]) {
-    static_assert(NT <= (kAK / 4) * (kAD / 4) * 2, "at most two threads per 16-byte column item");
-    for (int e = threadIdx.x; e < (kAK / 4) * (kAD / 4); e += NT) {
-        const int rq = e & 15, dq = e >> 4;
-        vf4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int r = 4 * rq + u;
-            v[u] = vf4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (r < rows_left) v[u] = *reinterpret_cast<const vf4*>(src + (row0 + r) * ld + head * kAD + 4 * dq);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            *reinterpret_cast<vf4*>(&dst[4 * dq + u][4 * rq]) = vf4{v[0][u], v[1][u], v[2][u], v[3][u]};
-    }
-}
 
 // left-to-right running sum handed from lane to lane + 1 within a 16-lane row
 __device__ __forceinline__ float dpp_shr1(float x) {
@@ -214,6 +160,90 @@ __global__ __launch_bounds__(256) void attn_quant_v_kernel(const float* __restri
     attn_quant_v_tile(V, ldv, b * S, kt * kAK, S, hk, qz, codes + blockIdx.x * (int64_t)(kAD * kAK));
 }
 
+// ---- the product engine shared by the forward's logits and the backward ----
+// A 16x16x1 fp32 MFMA with a K of one and an accumulator input of -0 forms
+// fl(a*b) for each of its 1024 (a, b) pairs, bit-identical to v_mul_f32
+// (FTZ); the VALU adds the products in the canonical order.  Lane l feeds A
+// row l and B column l % 16; register 4*beta + e of lane l receives row
+// 16*beta + 4*(l / 16) + e, column l % 16.
+__device__ __forceinline__ v16f_a mfma_prod(float a, float b) {
+    v16f_a cneg;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cneg[r] = -0.0f;
+    return __builtin_amdgcn_mfma_f32_16x16x1f32(a, b, cneg, 0, 0, 0);
+}
+
+// Both phases run one product chain per wave, software-pipelined: the MFMA
+// of step s + 1 is issued before the adds of step s, and the operands of the
+// next 4 steps are read while the current 4 are consumed.  KV_STEP(acc)
+// keeps the adds of a step at their place in the program (an empty asm that
+// takes the running sums in and out); without it the compiler hoists all
+// MFMAs of a block ahead of the adds and runs out of registers.
+#define KV_STEP(acc) __asm__ volatile("" : "+v"(acc))
+
+// four B operands (d .. d+3) of one key row: fp32, or q_v dequantised as
+// fl(q_v * s_v)
+template <bool DQV>
+__device__ __forceinline__ vf4 kv_b4(const float* brow, const int8_t* bq, float s_v, int d) {
+    vf4 bv;
+    if constexpr (DQV) {
+        const int q4 = *reinterpret_cast<const int*>(bq + d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] = f_mul((float)(int8_t)(q4 >> (8 * e)), s_v);
+    } else {
+        bv = *reinterpret_cast<const vf4*>(brow + d);
+    }
+    return bv;
+}
+
+// phase 1 of one wave: CanonSum over d of A[lane][d] * B[key][d] for 64
+// rows x 16 keys: d-blocks of 32 left to right, then (b0 + b1) + (b2 + b3)
+template <bool DQV>
+__device__ __forceinline__ v16f_a kv_phase1(const float* arow, const float* brow, const int8_t* bq, float s_v) {
+    v16f_a b01, b2, acc;
+#pragma unroll 1
+    for (int blk = 0; blk < kAD / 32; ++blk) {
+        const int d0 = 32 * blk;
+        v16f_a n;
+        vf4 a_cur = *reinterpret_cast<const vf4*>(arow + d0), b_cur = kv_b4<DQV>(brow, bq, s_v, d0), a_nxt, b_nxt;
+        v16f_a p = mfma_prod(a_cur[0], b_cur[0]);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            if (g + 1 < 8) {
+                a_nxt = *reinterpret_cast<const vf4*>(arow + d0 + 4 * (g + 1));
+                b_nxt = kv_b4<DQV>(brow, bq, s_v, d0 + 4 * (g + 1));
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int st = 4 * g + e;
+                if (st + 1 < 32) n = e < 3 ? mfma_prod(a_cur[e + 1], b_cur[e + 1]) : mfma_prod(a_nxt[0], b_nxt[0]);
+                if (st == 0) acc = p;
+                else acc = acc + p;
+                KV_STEP(acc);
+                p = n;
+            }
+            a_cur = a_nxt;
+            b_cur = b_nxt;
+        }
+        if (blk == 0) b01 = acc;
+        else if (blk == 1) b01 = b01 + acc;
+        else if (blk == 2) b2 = acc;
+    }
+    return b01 + (b2 + acc);
+}
+
+// 64 rows of one head (rows past `rows_left` as zeros), row-major into dst
+__device__ __forceinline__ void attn_load_rows(const float* src, int64_t ld, int64_t row0, int64_t rows_left,
+                                               int64_t head, float (*dst)[kKvRow]) {
+#pragma unroll 4
+    for (int e = threadIdx.x; e < kAQ * (kAD / 4); e += 256) {
+        const int row = e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
+        vf4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (row < rows_left) v = *reinterpret_cast<const vf4*>(src + (row0 + row) * ld + head * kAD + d4);
+        *reinterpret_cast<vf4*>(&dst[row][d4]) = v;
+    }
+}
+
 // order-preserving integer image of a binary32 value (negative values:
 // bits ^ 0x7fffffff), so that an integer maximum is the float maximum
 __device__ __forceinline__ int max_image(float f) {
@@ -266,48 +296,43 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         };
 
         __syncthreads();                             // the previous item is done with LDS
-        attn_load_kt(a.Q, a.ldq, base + q0, qrows, h, sm.u.a.qs);
+        attn_load_rows(a.Q, a.ldq, base + q0, qrows, h, sm.u.a.qr);
         for (int e = tid; e < kAQ * kAStack; e += 256) sm.st[e / kAStack][e % kAStack] = 0.0f;
+        if (tid < kAQ) sm.rowmax[tid] = max_image(__int_as_float(0xff800000));
 
-        // ---- pass 1: exact logits into the slot, exact row maxima ----
-        int mimg[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) mimg[x] = max_image(__int_as_float(0xff800000));
+        // ---- pass 1: exact logits on the product engine, stored; row maxima ----
+        // wave w: keys 16w .. 16w+15 of the tile for all 64 rows; register r
+        // of lane l holds row 16(r >> 2) + 4(l >> 4) + (r & 3), key 16w + l % 16
+        const int jl = 16 * wave + (lane & 15);
         for (int64_t kt = kt0; kt <= kt1; ++kt) {
             const int64_t j0 = kt * kAK;
             __syncthreads();
-            attn_load_kt(a.K, a.ldk, base + j0, a.S - j0, hk, sm.u.a.ks);
+            attn_load_rows(a.K, a.ldk, base + j0, a.S - j0, hk, sm.u.a.kr);
             __syncthreads();
-            float s[4][4];
-            attn_logits_from(sm.u.a.qs, sm.u.a.ks, ti, tj, a.c, s);
-            float* dst = slot + (kt - kt0) * (kAQ * kAK);
+            const v16f_a sx = kv_phase1<false>(&sm.u.a.qr[lane][0], &sm.u.a.kr[jl][0], nullptr, 0.0f);
+            float* dst = slot + (kt - kt0) * (kAQ * kAK) + 4 * (lane >> 4) * kAK + jl;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int i = 4 * ti + x;
-                *reinterpret_cast<vf4*>(dst + i * kAK + 4 * tj) = vf4{s[x][0], s[x][1], s[x][2], s[x][3]};
+            for (int r = 0; r < 16; ++r) {
+                const int il = 16 * (r >> 2) + 4 * (lane >> 4) + (r & 3);
+                const float v = f_mul(sx[r], a.c);
+                dst[(16 * (r >> 2) + (r & 3)) * kAK] = v;
+                // the row's maximum over the tile's 16 keys of this lane group,
+                // then over the four waves (integer maxima: any order gives
+                // the same bits)
+                int k = allowed(q0 + il, j0 + jl) ? max_image(v) : max_image(__int_as_float(0xff800000));
 #pragma unroll
-                for (int y = 0; y < 4; ++y)
-                    if (allowed(q0 + i, j0 + 4 * tj + y)) {
-                        const int k = max_image(s[x][y]);
-                        mimg[x] = k > mimg[x] ? k : mimg[x];
-                    }
+                for (int sh = 1; sh < 16; sh <<= 1) {
+                    const int o = __shfl_xor(k, sh, 16);
+                    k = o > k ? o : k;
+                }
+                if ((lane & 15) == 0) atomicMax(&sm.rowmax[il], k);
             }
         }
-        // the 16 threads of a row group (consecutive lanes) combine their maxima
+        // the maxima, and every thread's logit stores, visible to the workgroup
+        __syncthreads();
         float m[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-#pragma unroll
-            for (int sh = 1; sh < 16; sh <<= 1) {
-                const int o = __shfl_xor(mimg[x], sh, 16);
-                mimg[x] = o > mimg[x] ? o : mimg[x];
-            }
-            m[x] = from_max_image(mimg[x]);
-        }
-        if (tj == 0) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) sm.rowmax[4 * ti + x] = m[x];
-        }
+        for (int x = 0; x < 4; ++x) m[x] = from_max_image(sm.rowmax[4 * ti + x]);
 
         // ---- pass 2: p, row sums, int8 P.V ----
         v16i_a acc[2];
@@ -409,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
             sm.rowdiv[tid] = f_mul(root, 127.0f);
             if (a.stats && tid < qrows) {
                 float* st2 = a.stats + 2 * ((base + q0 + tid) * a.Hq + h);
-                st2[0] = sm.rowmax[tid];
+                st2[0] = from_max_image(sm.rowmax[tid]);
                 st2[1] = root;
             }
         }
@@ -542,13 +567,6 @@ struct AttnBwdArgs {
 //   phase 2 (8 waves): the tile sums over the 64 query positions (two
 //     32-blocks, then the pair) of P x dO, then of dS x Q, for d slab
 //     16*w .. +15, each into 16 int64 accumulators.
-typedef float v16f_a __attribute__((ext_vector_type(16)));
-
-constexpr int kKvThreads = 512;
-constexpr int kKvRow = kAD + 4;     // floats per LDS row of K, Q and dO
-constexpr int kKvRowQ = kAD + 16;   // bytes per LDS row of q_v
-constexpr int kKvRowT = kAQ + 4;    // floats per LDS row of the key-major tiles
-
 struct AttnKvArgs {
     const float* Q;
     const float* K;
@@ -573,72 +591,6 @@ struct AttnKvSmem {
     float rowm[kAQ], rowl[kAQ], rowdelta[kAQ];
 };
 static_assert(sizeof(AttnKvSmem) <= 163840, "LDS of one CU");
-
-__device__ __forceinline__ v16f_a mfma_prod(float a, float b) {
-    v16f_a cneg;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) cneg[r] = -0.0f;
-    return __builtin_amdgcn_mfma_f32_16x16x1f32(a, b, cneg, 0, 0, 0);
-}
-
-// Both phases run one product chain per wave, software-pipelined: the MFMA
-// of step s + 1 is issued before the adds of step s, and the operands of the
-// next 4 steps are read while the current 4 are consumed.  KV_STEP(acc)
-// keeps the adds of a step at their place in the program (an empty asm that
-// takes the running sums in and out); without it the compiler hoists all
-// MFMAs of a block ahead of the adds and runs out of registers.
-#define KV_STEP(acc) __asm__ volatile("" : "+v"(acc))
-
-// four B operands (d .. d+3) of one key row: fp32, or q_v dequantised as
-// fl(q_v * s_v)
-template <bool DQV>
-__device__ __forceinline__ vf4 kv_b4(const float* brow, const int8_t* bq, float s_v, int d) {
-    vf4 bv;
-    if constexpr (DQV) {
-        const int q4 = *reinterpret_cast<const int*>(bq + d);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bv[e] = f_mul((float)(int8_t)(q4 >> (8 * e)), s_v);
-    } else {
-        bv = *reinterpret_cast<const vf4*>(brow + d);
-    }
-    return bv;
-}
-
-// phase 1 of one wave: CanonSum over d of A[lane][d] * B[key][d] for 64
-// rows x 16 keys: d-blocks of 32 left to right, then (b0 + b1) + (b2 + b3)
-template <bool DQV>
-__device__ __forceinline__ v16f_a kv_phase1(const float* arow, const float* brow, const int8_t* bq, float s_v) {
-    v16f_a b01, b2, acc;
-#pragma unroll 1
-    for (int blk = 0; blk < kAD / 32; ++blk) {
-        const int d0 = 32 * blk;
-        v16f_a n;
-        vf4 a_cur = *reinterpret_cast<const vf4*>(arow + d0), b_cur = kv_b4<DQV>(brow, bq, s_v, d0), a_nxt, b_nxt;
-        v16f_a p = mfma_prod(a_cur[0], b_cur[0]);
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            if (g + 1 < 8) {
-                a_nxt = *reinterpret_cast<const vf4*>(arow + d0 + 4 * (g + 1));
-                b_nxt = kv_b4<DQV>(brow, bq, s_v, d0 + 4 * (g + 1));
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int st = 4 * g + e;
-                if (st + 1 < 32) n = e < 3 ? mfma_prod(a_cur[e + 1], b_cur[e + 1]) : mfma_prod(a_nxt[0], b_nxt[0]);
-                if (st == 0) acc = p;
-                else acc = acc + p;
-                KV_STEP(acc);
-                p = n;
-            }
-            a_cur = a_nxt;
-            b_cur = b_nxt;
-        }
-        if (blk == 0) b01 = acc;
-        else if (blk == 1) b01 = b01 + acc;
-        else if (blk == 2) b2 = acc;
-    }
-    return b01 + (b2 + acc);
-}
 
 // phase 2 of one wave: the tile sum over the 64 query positions of
 // T[key][i] * R[i][dcol] (keys from the lanes), two 32-blocks left to right
