@@ -14,6 +14,12 @@
 //   WHAT 4: 32-bit integer VALU (x_i <- x_i ^ (x_i >> 3): v_lshrrev_b32 and
 //           v_xor_b32), 16 instructions per step
 //   WHAT 5: v_add_f32 as WHAT 0 but with c in a scalar register
+//   WHAT 7: v_mfma_i32_32x32x32_i8 on operands that change from one MFMA to
+//           the next, as a GEMM's do: 16 A and 8 B fragments of hashed bits
+//           held in registers, each step four rounds of a 4 x 2 grid of
+//           them (32 MFMAs, 8 accumulators, no other instructions).  The
+//           matrix core's power, and so the clock it sustains, depends on
+//           how many operand bits toggle
 //   WHAT 6: the backward's product engine without its memory traffic: per
 //           step 4 K = 1 fp32 MFMAs with a -0 accumulator and the 64 v_add_f32
 //           that add their products into 4 running sums (4096 multiply-adds
@@ -103,6 +109,37 @@ __global__ __launch_bounds__(kRateThreads) void probe_rate_kernel(int64_t iters,
 #pragma unroll
         for (int i = 0; i < 8; ++i) t ^= x[i];
         r = (float)(t & 0xFFFFFFu);
+    } else if constexpr (WHAT == 7) {
+        v16ip acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][e] = 0;
+        // fragment f (A: f < 16, B: f >= 16), register k: a xorshift of a
+        // hash of (thread, f, k)
+        v4ip fr[24];
+#pragma unroll
+        for (int f = 0; f < 24; ++f)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                unsigned x = ((unsigned)gid + 1u) * 0x9E3779B1u + (unsigned)(4 * f + k + 1) * 0x85EBCA77u;
+                x ^= x << 13;
+                x ^= x >> 17;
+                x ^= x << 5;
+                fr[f][k] = (int)x;
+            }
+        for (int64_t s = 0; s < iters; ++s)
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    acc[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fr[4 * p + q / 2], fr[16 + 2 * p + q % 2], acc[q], 0, 0, 0);
+        unsigned t = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) t += (unsigned)acc[i][e];
+        r = (float)(t & 0xFFFFFFu);
     } else {
         v16ip acc[8];
 #pragma unroll
@@ -134,6 +171,7 @@ hipError_t launch_probe_rate(int what, int64_t iters, float c, float* out, hipSt
         case 4: hipLaunchKernelGGL(probe_rate_kernel<4>, g, b, 0, st, iters, c, out); break;
         case 5: hipLaunchKernelGGL(probe_rate_kernel<5>, g, b, 0, st, iters, c, out); break;
         case 6: hipLaunchKernelGGL(probe_rate_kernel<6>, g, b, 0, st, iters, c, out); break;
+        case 7: hipLaunchKernelGGL(probe_rate_kernel<7>, g, b, 0, st, iters, c, out); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

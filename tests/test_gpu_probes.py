@@ -103,7 +103,46 @@ def _rate_expected(unit: str, iters: int, n: int) -> np.ndarray:
     return (8 * iters * col).astype(np.float32)
 
 
-@pytest.mark.parametrize("unit", list(brl.RATE_UNITS))
+def _i8_data_wave_sums(iters: int, n: int) -> np.ndarray:
+    """Per-wave sums of the data-toggling i8 probe's outputs, mod 2^24.
+
+    Fragment f of lane l holds 16 bytes (byte 4k + m = byte m of its register
+    k); A fragments are f < 16, B fragments f >= 16, and each step runs, for
+    p = 0..3, the grid A_{4p+i} x B_{16+2p+j}.  Rows of A come from lanes i
+    and i + 32 (columns of B likewise) with the same byte-to-k assignment for
+    A and B, so the sum of all 32 x 32 outputs of one MFMA is, whatever that
+    assignment, the sum over the lane half h and byte b of (sum of A's bytes
+    over the 32 lanes of h) x (the same for B)."""
+    gid = np.arange(n, dtype=np.uint32)
+    fr = []
+    with np.errstate(over="ignore"):            # uint32 arithmetic wraps, as on the device
+        for f in range(24):
+            regs = []
+            for k in range(4):
+                x = (gid + np.uint32(1)) * np.uint32(0x9E3779B1) + np.uint32(4 * f + k + 1) * np.uint32(0x85EBCA77)
+                x = x ^ (x << np.uint32(13))
+                x = x ^ (x >> np.uint32(17))
+                x = x ^ (x << np.uint32(5))
+                regs.append(x)
+            # [waves, half, 32 lanes, 16 bytes] -> byte sums over the lanes of a half
+            fr.append(np.stack(regs, axis=1).view(np.int8).reshape(n // 64, 2, 32, 16).astype(np.int64).sum(axis=2))
+    total = np.zeros(n // 64, np.int64)
+    for p in range(4):
+        for q in range(8):
+            total += (fr[4 * p + q // 2] * fr[16 + 2 * p + q % 2]).sum(axis=(1, 2))
+    return (iters * total) % (1 << 24)
+
+
+def test_i8_probe_with_changing_operands_computes_its_products():
+    iters = 40
+    out = brl.probe_rate("mfma_i8_data", iters)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.int64).reshape(-1, 64).sum(axis=1) % (1 << 24)
+    want = _i8_data_wave_sums(iters, out.numel())
+    assert np.array_equal(got, want), (got[:4], want[:4])
+
+
+@pytest.mark.parametrize("unit", [u for u in brl.RATE_UNITS if u != "mfma_i8_data"])
 def test_rate_probe_chains_end_where_they_should(unit):
     iters = 40
     out = brl.probe_rate(unit, iters)
