@@ -122,9 +122,10 @@ def test_attention_dq_parity(B, S, Hq, Hkv, window, s_v):
 
 @pytest.mark.parametrize("window", [0, 40])
 def test_attention_equal_and_near_equal_logits(window):
-    """Every key a candidate of the first pass: Q = 0 (all logits 0) and keys
-    that differ by a few ulp (logits closer than the approximation's bound),
-    so the exact maximum comes from the candidate path alone."""
+    """Equal and near-equal logits: Q = 0 (all logits 0) and keys that differ
+    by a few ulp, so the row maximum is a tie or a near tie among many keys
+    (the case that made every key a candidate of the earlier approximate
+    first pass)."""
     B, S, Hq, Hkv, s_v = 1, 150, 4, 2, 0.05
     g = np.random.default_rng(window)
     V = g.standard_normal((B, S, Hkv, D)).astype(np.float32)
@@ -140,8 +141,8 @@ def test_attention_equal_and_near_equal_logits(window):
 @pytest.mark.parametrize("q_scale,k_scale", [(1e-20, 1e19), (3e17, 1e-18), (1.0, 40.0)])
 def test_attention_extreme_scales(q_scale, k_scale):
     """Q and K of very different magnitudes (squared norms far outside
-    binary32's range on one side), and logits spread over hundreds of units:
-    the first pass's pruning bound must stay valid."""
+    binary32's range on one side), and logits spread over hundreds of units
+    (the cases that stressed the earlier approximate pass's error bound)."""
     B, S, Hq, Hkv, window, s_v = 1, 130, 4, 2, 50, 0.05
     g = np.random.default_rng(int(abs(np.log10(q_scale))) + 1)
     Q = (g.standard_normal((B, S, Hq, D)) * q_scale).astype(np.float32)
@@ -301,7 +302,7 @@ def test_attention_kernels_repeat_ten_times_bit_identically():
     assert_bitwise(first[0].view(torch.float32), oracle.attn_fwd(Q, K, V, window, s_v), "O")
 
 
-# ---- keys of unequal norm: the first pass must keep the true row maximum ----
+# ---- keys of unequal norm: the row maximum must be the exact one ----
 def _witness_inputs(S=160):
     """Every query is all ones.  Keys 5, 40 and 70 are the high-norm key l
     (bf16 operands 64(1+2^-7) and -64: approximate logit 2.83, exact 0.011,
@@ -347,8 +348,9 @@ def _full_check(Q, K, V, dO, window, s_v, what, O_bwd=None):
 @pytest.mark.parametrize("window", [0, 64])
 def test_attention_keys_of_unequal_norm_witness(window):
     """O, (m, l), dQ, dK and dV on the witness row: m_i is the exact logit of
-    the 0.125 key (16 c) for every row that attends one, never the larger
-    approximate logit's key."""
+    the 0.125 key (16 c) for every row that attends one, never the key whose
+    bf16 logit is larger (the witness that defeated the earlier pruning
+    rule)."""
     Q, K, V, dO = _witness_inputs()
     st = _full_check(Q, K, V, dO, window, 0.05, f"witness w={window}")
     c = np.float32(np.float32(1.0) / np.sqrt(np.float32(D)))
@@ -390,3 +392,28 @@ def test_attention_fixed_point_ties_on_device():
     V2 = np.zeros_like(V)
     V2[0, 40, 0, 0] = V2[0, 64, 0, 0] = 1.0
     _full_check(Q2, np.zeros_like(K), V2, dO2, WIN, 1.0, "fixed-point ties, K = 0", O_bwd=np.zeros_like(O))
+
+
+def test_attention_workgroups_walk_several_items():
+    """The forward runs a persistent grid of at most 512 workgroups, each
+    walking (batch, query head, query block) items and reusing one slot of
+    the workspace for every item's stored logits.  2 x 16 heads x 18 query
+    blocks = 576 items, so some workgroups take two items of different
+    lengths (last blocks first); every output and statistic must still be
+    the oracle's."""
+    B, S, Hq, Hkv, window, s_v = 2, 1100, 16, 4, 100, 0.05
+    assert B * Hq * ((S + 63) // 64) > 512
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=41, scale=0.3)
+    dO = (np.random.default_rng(43).standard_normal((B, S, Hq, D)) * 1e-2).astype(np.float32)
+    q, k, v = (torch.from_numpy(t).cuda() for t in (Q, K, V))
+    stats = torch.empty((B, S, Hq, 2), dtype=torch.float32, device="cuda")
+    O = brl.attn_fwd(q, k, v, window, s_v, stats=stats)
+    # dQ reads the statistics (m, l) the forward wrote for every row
+    rows = np.arange(0, B * S * Hq, 97)
+    dQ = brl.attn_bwd_dq(q, k, v, O, torch.from_numpy(dO).cuda(), stats, window, s_v)
+    torch.cuda.synchronize()
+    Oh = O.cpu().numpy()
+    assert_bitwise(Oh, oracle.attn_fwd(Q, K, V, window, s_v), "O (several items per workgroup)")
+    want = oracle.attn_bwd_dq(Q, K, V, Oh, dO, window, s_v, rows=rows)
+    got = dQ.cpu().numpy().reshape(B * S * Hq, D)[rows]
+    assert_bitwise(got, np.asarray(want).reshape(got.shape), "dQ rows (several items per workgroup)")
