@@ -342,7 +342,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
             for (int r = 0; r < 16; ++r) acc[n][r] = 0;
         for (int64_t kt = kt0; kt <= kt1; ++kt) {
             const int64_t j0 = kt * kAK;
-            // this thread's logits of the tile, as it stored them in pass 1
+            // the tile's logits of this thread's 4 x 4 block, stored in pass 1
+            // by the lanes of the product engine (the barrier after pass 1
+            // made them visible to the workgroup)
             const float* src = slot + (kt - kt0) * (kAQ * kAK);
             vf4 sv[4];
 #pragma unroll
