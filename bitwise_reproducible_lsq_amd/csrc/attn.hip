@@ -250,6 +250,13 @@ __device__ __forceinline__ int max_image(float f) {
     const int b = __float_as_int(f);
     return b >= 0 ? b : b ^ 0x7fffffff;
 }
+// the larger of k and k from the lane `sh` places away in its DPP row of 16
+// lanes (row_ror:sh): four of these give every lane its row's maximum
+template <int SH>
+__device__ __forceinline__ int max_ror(int k) {
+    const int o = __builtin_amdgcn_update_dpp(0, k, 0x120 + SH, 0xf, 0xf, false);
+    return o > k ? o : k;
+}
 __device__ __forceinline__ float from_max_image(int k) { return __int_as_float(k >= 0 ? k : k ^ 0x7fffffff); }
 
 // key tiles [kt0, kt1] that meet the key ranges of query block qb
@@ -290,9 +297,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         int64_t kt0, kt1;
         attn_tile_range(a.S, a.window, qb, &kt0, &kt1);
 
-        auto allowed = [&](int64_t i, int64_t j) {
-            const int64_t lo = a.window > 0 ? i - a.window + 1 : 0;
-            return i < a.S && j <= i && j >= lo;
+        // row il of the block may attend key jl of the tile at key offset
+        // dlt = j0 - q0 (32-bit: the host bounds S); `full`: every row of the
+        // block may attend every key of the tile
+        const int nrows = (int)qrows;
+        const int win = (a.window <= 0 || a.window >= a.S) ? 0 : (int)a.window;   // 0: no window
+        auto allowed = [&](int dlt, int il, int jl) {
+            const int t = dlt + jl - il;                      // key - row
+            return (il < nrows) & (t <= 0) & ((win == 0) | (t > -win));
+        };
+        auto full_tile = [&](int dlt) {
+            return nrows == kAQ && dlt + kAK - 1 <= 0 && (win == 0 || dlt - (kAQ - 1) > -win);
         };
 
         __syncthreads();                             // the previous item is done with LDS
@@ -304,29 +319,39 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         // wave w: keys 16w .. 16w+15 of the tile for all 64 rows; register r
         // of lane l holds row 16(r >> 2) + 4(l >> 4) + (r & 3), key 16w + l % 16
         const int jl = 16 * wave + (lane & 15);
+        // this lane's maxima of its 16 rows over its keys of every tile, as
+        // order-preserving integer images (any order gives the same bits)
+        int kmax[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) kmax[r] = max_image(__int_as_float(0xff800000));
         for (int64_t kt = kt0; kt <= kt1; ++kt) {
             const int64_t j0 = kt * kAK;
+            const int dlt = (int)(j0 - q0);
             __syncthreads();
             attn_load_rows(a.K, a.ldk, base + j0, a.S - j0, hk, sm.u.a.kr);
             __syncthreads();
             const v16f_a sx = kv_phase1<false>(&sm.u.a.qr[lane][0], &sm.u.a.kr[jl][0], nullptr, 0.0f);
             float* dst = slot + (kt - kt0) * (kAQ * kAK) + 4 * (lane >> 4) * kAK + jl;
+            const bool full = full_tile(dlt);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int il = 16 * (r >> 2) + 4 * (lane >> 4) + (r & 3);
                 const float v = f_mul(sx[r], a.c);
                 dst[(16 * (r >> 2) + (r & 3)) * kAK] = v;
-                // the row's maximum over the tile's 16 keys of this lane group,
-                // then over the four waves (integer maxima: any order gives
-                // the same bits)
-                int k = allowed(q0 + il, j0 + jl) ? max_image(v) : max_image(__int_as_float(0xff800000));
-#pragma unroll
-                for (int sh = 1; sh < 16; sh <<= 1) {
-                    const int o = __shfl_xor(k, sh, 16);
-                    k = o > k ? o : k;
-                }
-                if ((lane & 15) == 0) atomicMax(&sm.rowmax[il], k);
+                const int k = (full | allowed(dlt, il, jl)) ? max_image(v) : max_image(__int_as_float(0xff800000));
+                kmax[r] = k > kmax[r] ? k : kmax[r];
             }
+        }
+        // each row's maximum over the 16 lanes of its lane group (rotations
+        // within a DPP row of 16 lanes), then over the four waves
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            int k = kmax[r];
+            k = max_ror<1>(k);
+            k = max_ror<2>(k);
+            k = max_ror<4>(k);
+            k = max_ror<8>(k);
+            if ((lane & 15) == 0) atomicMax(&sm.rowmax[16 * (r >> 2) + 4 * (lane >> 4) + (r & 3)], k);
         }
         // the maxima, and every thread's logit stores, visible to the workgroup
         __syncthreads();
@@ -342,6 +367,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
             for (int r = 0; r < 16; ++r) acc[n][r] = 0;
         for (int64_t kt = kt0; kt <= kt1; ++kt) {
             const int64_t j0 = kt * kAK;
+            const int dlt = (int)(j0 - q0);
+            const bool full = full_tile(dlt);
             // the tile's logits of this thread's 4 x 4 block, stored in pass 1
             // by the lanes of the product engine (the barrier after pass 1
             // made them visible to the workgroup)
@@ -369,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
                 for (int y = 0; y < 4; ++y) {
                     const int j = 4 * tj + y;
-                    p[y] = allowed(q0 + i, j0 + j) ? own_exp(f_sub(sv[x][y], m[x]), a.ek) : 0.0f;
+                    p[y] = (full | allowed(dlt, i, j)) ? own_exp(f_sub(sv[x][y], m[x]), a.ek) : 0.0f;
                     float r = f_rne(f_mul(p[y], 127.0f));
                     r = r > 127.0f ? 127.0f : (r < 0.0f ? 0.0f : r);
                     packed |= (uint32_t)(int)r << (8 * y);
