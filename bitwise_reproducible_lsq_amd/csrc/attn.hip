@@ -80,9 +80,9 @@ struct AttnSmem {
             float kr[kAK][kKvRow];  // K tile, key-major
         } a;                        // pass 1
         struct {
-            int8_t pq[kAQ][kAK];    // q_p, rows of 64 keys, 16-byte chunks swizzled
-            int8_t vq[kAD][kAK];    // q_v transposed: row d holds 64 keys, swizzled
-        } pv;                       // pass 2
+            int8_t pq[2][kAQ][kAK]; // q_p, rows of 64 keys, 16-byte chunks swizzled
+            int8_t vq[2][kAD][kAK]; // q_v transposed: row d holds 64 keys, swizzled
+        } pv;                       // pass 2, double-buffered by key tile
     } u;
     float st[kAQ][kAStack];         // per-row stacks of key-tile pair sums
     int rowmax[kAQ];                // row maxima as order-preserving integer images
@@ -232,6 +232,19 @@ __device__ __forceinline__ v16f_a kv_phase1(const float* arow, const float* brow
     return b01 + (b2 + acc);
 }
 
+// rows 16w .. 16w+15 of one head for wave w (rows past `rows_left` as
+// zeros), row-major into dst: the rows that wave's products read
+__device__ __forceinline__ void attn_load_wave_rows(const float* src, int64_t ld, int64_t row0, int64_t rows_left,
+                                                    int64_t head, float (*dst)[kKvRow], int wave, int lane) {
+#pragma unroll
+    for (int e = lane; e < 16 * (kAD / 4); e += 64) {
+        const int row = 16 * wave + e / (kAD / 4), d4 = (e % (kAD / 4)) * 4;
+        vf4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (row < rows_left) v = *reinterpret_cast<const vf4*>(src + (row0 + row) * ld + head * kAD + d4);
+        *reinterpret_cast<vf4*>(&dst[row][d4]) = v;
+    }
+}
+
 // 64 rows of one head (rows past `rows_left` as zeros), row-major into dst
 __device__ __forceinline__ void attn_load_rows(const float* src, int64_t ld, int64_t row0, int64_t rows_left,
                                                int64_t head, float (*dst)[kKvRow]) {
@@ -324,12 +337,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         int kmax[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) kmax[r] = max_image(__int_as_float(0xff800000));
+        __syncthreads();                             // the Q tile is in LDS
         for (int64_t kt = kt0; kt <= kt1; ++kt) {
             const int64_t j0 = kt * kAK;
             const int dlt = (int)(j0 - q0);
-            __syncthreads();
-            attn_load_rows(a.K, a.ldk, base + j0, a.S - j0, hk, sm.u.a.kr);
-            __syncthreads();
+            // each wave reads only its own 16 key rows, so it loads them itself
+            // (after its own reads of the previous tile's rows): no workgroup
+            // barrier inside pass 1
+            attn_load_wave_rows(a.K, a.ldk, base + j0, a.S - j0, hk, sm.u.a.kr, wave, lane);
             const v16f_a sx = kv_phase1<false>(&sm.u.a.qr[lane][0], &sm.u.a.kr[jl][0], nullptr, 0.0f);
             float* dst = slot + (kt - kt0) * (kAQ * kAK) + 4 * (lane >> 4) * kAK + jl;
             const bool full = full_tile(dlt);
@@ -365,28 +380,40 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         for (int n = 0; n < 2; ++n)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[n][r] = 0;
+        // a tile's logits of this thread's 4 x 4 block, stored in pass 1 by
+        // the lanes of the product engine (the barrier after pass 1 made them
+        // visible to the workgroup), and its q_v codes (8 KB, copied into LDS
+        // as they lie), loaded one tile ahead of their use
+        const v4i_a* vbase = reinterpret_cast<const v4i_a*>(a.vcodes + (b * a.Hkv + hk) * a.vtiles *
+                                                                            (int64_t)(kAD * kAK));
+        vf4 svn[4];
+        v4i_a vtn[2];
+        auto fetch = [&](int64_t kt) {
+            const float* src = slot + (kt - kt0) * (kAQ * kAK);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) svn[x] = *reinterpret_cast<const vf4*>(src + (4 * ti + x) * kAK + 4 * tj);
+            const v4i_a* vsrc = vbase + kt * (kAD * kAK / 16);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) vtn[k] = vsrc[tid + 256 * k];
+        };
+        fetch(kt0);
         for (int64_t kt = kt0; kt <= kt1; ++kt) {
             const int64_t j0 = kt * kAK;
             const int dlt = (int)(j0 - q0);
             const bool full = full_tile(dlt);
-            // the tile's logits of this thread's 4 x 4 block, stored in pass 1
-            // by the lanes of the product engine (the barrier after pass 1
-            // made them visible to the workgroup)
-            const float* src = slot + (kt - kt0) * (kAQ * kAK);
+            const int buf = (int)((kt - kt0) & 1);
             vf4 sv[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) sv[x] = *reinterpret_cast<const vf4*>(src + (4 * ti + x) * kAK + 4 * tj);
-            // the tile's q_v codes (8 KB), copied as they lie
-            const v4i_a* vsrc = reinterpret_cast<const v4i_a*>(a.vcodes + ((b * a.Hkv + hk) * a.vtiles + kt) *
-                                                                           (int64_t)(kAD * kAK));
             v4i_a vt[2];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) vt[k] = vsrc[tid + 256 * k];
-            // every thread is past the previous tile's P.V reads (and, for the
-            // first tile, past pass 1's reads of the Q and K tiles)
-            __syncthreads();
+            for (int x = 0; x < 4; ++x) sv[x] = svn[x];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) reinterpret_cast<v4i_a*>(&sm.u.pv.vq[0][0])[tid + 256 * k] = vt[k];
+            for (int k = 0; k < 2; ++k) vt[k] = vtn[k];
+            if (kt < kt1) fetch(kt + 1);
+            // buffer `buf` was last read by the P.V of tile kt - 2, which every
+            // wave finished before the barrier of tile kt - 1 (for the first
+            // two tiles: pass 1's reads, finished before the barrier after it)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) reinterpret_cast<v4i_a*>(&sm.u.pv.vq[buf][0][0])[tid + 256 * k] = vt[k];
             float pair[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
@@ -396,24 +423,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
                 for (int y = 0; y < 4; ++y) {
                     const int j = 4 * tj + y;
-                    p[y] = (full | allowed(dlt, i, j)) ? own_exp(f_sub(sv[x][y], m[x]), a.ek) : 0.0f;
+                    const float e = own_exp(f_sub(sv[x][y], m[x]), a.ek);
+                    p[y] = (full | allowed(dlt, i, j)) ? e : 0.0f;
                     float r = f_rne(f_mul(p[y], 127.0f));
                     r = r > 127.0f ? 127.0f : (r < 0.0f ? 0.0f : r);
                     packed |= (uint32_t)(int)r << (8 * y);
                 }
-                *reinterpret_cast<uint32_t*>(&sm.u.pv.pq[i][16 * aswz(i, tj >> 2) + 4 * (tj & 3)]) = packed;
+                *reinterpret_cast<uint32_t*>(&sm.u.pv.pq[buf][i][16 * aswz(i, tj >> 2) + 4 * (tj & 3)]) = packed;
                 // 32-key block sums: lanes tj = 8k .. 8k+7 hold block k's keys in
                 // order; the running sum walks through them one lane at a time
+                // (every lane computes each step, the lane whose turn it is keeps it)
                 float run = 0.0f;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const float in = dpp_shr1(run);
-                    if ((tj & 7) == t) {
-                        float x0 = t == 0 ? p[0] : f_add(in, p[0]);
-                        x0 = f_add(x0, p[1]);
-                        x0 = f_add(x0, p[2]);
-                        run = f_add(x0, p[3]);
-                    }
+                    float x0 = t == 0 ? p[0] : f_add(in, p[0]);
+                    x0 = f_add(x0, p[1]);
+                    x0 = f_add(x0, p[2]);
+                    x0 = f_add(x0, p[3]);
+                    run = (tj & 7) == t ? x0 : run;
                 }
                 // lane tj = 15: block 1's sum; block 0's sits in lane tj = 7
                 pair[x] = f_add(dpp_shr8(run), run);
@@ -440,11 +468,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
             for (int ks = 0; ks < kAK / 32; ++ks) {
                 const int chunk = fchunk + 2 * ks;
                 const int ar = mt * 32 + frow;
-                const v4i_a A = *reinterpret_cast<const v4i_a*>(&sm.u.pv.pq[ar][16 * aswz(ar, chunk)]);
+                const v4i_a A = *reinterpret_cast<const v4i_a*>(&sm.u.pv.pq[buf][ar][16 * aswz(ar, chunk)]);
 #pragma unroll
                 for (int n = 0; n < 2; ++n) {
                     const int br = (nt0 + n) * 32 + frow;
-                    const v4i_a Bf = *reinterpret_cast<const v4i_a*>(&sm.u.pv.vq[br][16 * aswz(br, chunk)]);
+                    const v4i_a Bf = *reinterpret_cast<const v4i_a*>(&sm.u.pv.vq[buf][br][16 * aswz(br, chunk)]);
                     acc[n] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, Bf, acc[n], 0, 0, 0);
                 }
             }

@@ -143,19 +143,22 @@ __device__ __forceinline__ float pow2_f32(int e) {   // -126 <= e <= 127
     return __int_as_float((e + 127) << 23);
 }
 
+// The reduction and the polynomial run on every lane (on 0 where x is NaN or
+// out of range) and the special cases are selected afterwards, so a wave
+// takes no branch.
 __device__ __forceinline__ float own_exp(float x, const ExpConsts& K) {
-    if (x != x) return x;
-    if (x > 89.0f) return __int_as_float(0x7f800000);
-    if (x < -104.0f) return 0.0f;
-    float k = f_rne(f_mul(x, K.l2e));
-    float r = f_sub(f_sub(x, f_mul(k, K.ln2_hi)), f_mul(k, K.ln2_lo));
+    const bool nan = x != x, big = x > 89.0f, small = x < -104.0f;
+    const float xr = (nan | big | small) ? 0.0f : x;
+    float k = f_rne(f_mul(xr, K.l2e));
+    float r = f_sub(f_sub(xr, f_mul(k, K.ln2_hi)), f_mul(k, K.ln2_lo));
     float p = K.c[7];
 #pragma unroll
     for (int i = 6; i >= 0; --i) p = f_add(f_mul(p, r), K.c[i]);
     int ki = (int)k;
     int k1 = ki / 2;
     int k2 = ki - k1;
-    return f_mul(f_mul(p, pow2_f32(k1)), pow2_f32(k2));
+    const float y = f_mul(f_mul(p, pow2_f32(k1)), pow2_f32(k2));
+    return nan ? x : big ? __int_as_float(0x7f800000) : small ? 0.0f : y;
 }
 
 // SwiGLU forward pieces: s = 1/(1 + E(-g)), h = g*s, a = h*u.

@@ -78,6 +78,11 @@ def test_device_binary32_ops_match_oracle(op):
         a[:521] = (np.arange(-260, 261) / 2).astype(np.float32)
     if op == "exp":
         a = np.random.default_rng(6).uniform(-110, 95, 20000).astype(np.float32)
+        # the range ends, the special values and the signed zeros
+        edge = [89.0, np.nextafter(np.float32(89), np.float32(90)), np.nextafter(np.float32(89), np.float32(0)),
+                -104.0, np.nextafter(np.float32(-104), np.float32(-105)),
+                np.nextafter(np.float32(-104), np.float32(0)), 0.0, -0.0, np.inf, -np.inf, np.nan, 1e-30, -1e-30]
+        a[:len(edge)] = np.array(edge, np.float32)
     got = brl.probe_f32(op, _cuda(a), _cuda(b)).cpu().numpy()
     fn = {"add": oracle.add, "sub": oracle.sub, "mul": oracle.mul, "mfma_mul": oracle.mul, "div": oracle.div,
           "sqrt": lambda x, y: oracle.sqrt(x), "rne": lambda x, y: oracle.rne(x),
