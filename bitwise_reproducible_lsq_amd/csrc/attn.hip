@@ -46,6 +46,7 @@
 namespace brl {
 
 typedef int v4i_a __attribute__((ext_vector_type(4)));
+typedef unsigned v4u_a __attribute__((ext_vector_type(4)));
 typedef int v16i_a __attribute__((ext_vector_type(16)));
 
 constexpr int kAD = 128;          // head dimension
@@ -95,6 +96,9 @@ __device__ __forceinline__ int aswz(int row, int chunk) { return chunk ^ ((row >
 // left-to-right running sum handed from lane to lane + 1 within a 16-lane row
 __device__ __forceinline__ float dpp_shr1(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_shr2(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
 }
 __device__ __forceinline__ float dpp_shr8(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
@@ -286,7 +290,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int ti = tid >> 4, tj = tid & 15;
 
     // items in 32-bit unsigned arithmetic (the host checks that they fit);
     // query blocks slowest and from the last, so that the longest walks
@@ -370,9 +373,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         }
         // the maxima, and every thread's logit stores, visible to the workgroup
         __syncthreads();
-        float m[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) m[x] = from_max_image(sm.rowmax[4 * ti + x]);
+        // pass 2 thread mapping: row pi = tid / 4 (wave w: rows 16w .. 16w+15),
+        // keys 16 pk .. 16 pk + 15 of each tile
+        const int pi = tid >> 2, pk = tid & 3;
+        const float mrow = from_max_image(sm.rowmax[pi]);
 
         // ---- pass 2: p, row sums, int8 P.V ----
         v16i_a acc[2];
@@ -380,8 +384,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         for (int n = 0; n < 2; ++n)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[n][r] = 0;
-        // a tile's logits of this thread's 4 x 4 block, stored in pass 1 by
-        // the lanes of the product engine (the barrier after pass 1 made them
+        // a tile's logits of this thread's 16 keys, stored in pass 1 by the
+        // lanes of the product engine (the barrier after pass 1 made them
         // visible to the workgroup), and its q_v codes (8 KB, copied into LDS
         // as they lie), loaded one tile ahead of their use
         const v4i_a* vbase = reinterpret_cast<const v4i_a*>(a.vcodes + (b * a.Hkv + hk) * a.vtiles *
@@ -391,7 +395,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         auto fetch = [&](int64_t kt) {
             const float* src = slot + (kt - kt0) * (kAQ * kAK);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) svn[x] = *reinterpret_cast<const vf4*>(src + (4 * ti + x) * kAK + 4 * tj);
+            for (int u = 0; u < 4; ++u) svn[u] = *reinterpret_cast<const vf4*>(src + pi * kAK + 16 * pk + 4 * u);
             const v4i_a* vsrc = vbase + kt * (kAD * kAK / 16);
 #pragma unroll
             for (int k = 0; k < 2; ++k) vtn[k] = vsrc[tid + 256 * k];
@@ -414,53 +418,41 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
             // two tiles: pass 1's reads, finished before the barrier after it)
 #pragma unroll
             for (int k = 0; k < 2; ++k) reinterpret_cast<v4i_a*>(&sm.u.pv.vq[buf][0][0])[tid + 256 * k] = vt[k];
-            float pair[4];
+            float p[16];
+            uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int i = 4 * ti + x;
-                float p[4];
-                uint32_t packed = 0;
-#pragma unroll
-                for (int y = 0; y < 4; ++y) {
-                    const int j = 4 * tj + y;
-                    const float e = own_exp(f_sub(sv[x][y], m[x]), a.ek);
-                    p[y] = (full | allowed(dlt, i, j)) ? e : 0.0f;
-                    float r = f_rne(f_mul(p[y], 127.0f));
-                    r = r > 127.0f ? 127.0f : (r < 0.0f ? 0.0f : r);
-                    packed |= (uint32_t)(int)r << (8 * y);
-                }
-                *reinterpret_cast<uint32_t*>(&sm.u.pv.pq[buf][i][16 * aswz(i, tj >> 2) + 4 * (tj & 3)]) = packed;
-                // 32-key block sums: lanes tj = 8k .. 8k+7 hold block k's keys in
-                // order; the running sum walks through them one lane at a time
-                // (every lane computes each step, the lane whose turn it is keeps it)
-                float run = 0.0f;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const float in = dpp_shr1(run);
-                    float x0 = t == 0 ? p[0] : f_add(in, p[0]);
-                    x0 = f_add(x0, p[1]);
-                    x0 = f_add(x0, p[2]);
-                    x0 = f_add(x0, p[3]);
-                    run = (tj & 7) == t ? x0 : run;
-                }
-                // lane tj = 15: block 1's sum; block 0's sits in lane tj = 7
-                pair[x] = f_add(dpp_shr8(run), run);
+            for (int e = 0; e < 16; ++e) {
+                const float ex = own_exp(f_sub(sv[e >> 2][e & 3], mrow), a.ek);
+                p[e] = (full | allowed(dlt, pi, 16 * pk + e)) ? ex : 0.0f;
+                float r = f_rne(f_mul(p[e], 127.0f));
+                r = r > 127.0f ? 127.0f : (r < 0.0f ? 0.0f : r);
+                packed[e >> 2] |= (uint32_t)(int)r << (8 * (e & 3));
             }
-            // push the tile's pair sum (complete subtree of blocks 2kt, 2kt+1)
-            if (tj == 15) {
+            *reinterpret_cast<v4u_a*>(&sm.u.pv.pq[buf][pi][16 * aswz(pi, pk)]) =
+                v4u_a{packed[0], packed[1], packed[2], packed[3]};
+            // 32-key block sums, left to right: block k's keys lie in lanes
+            // pk = 2k (first half) and 2k + 1.  Every lane forms both chains;
+            // the first half's sum is kept from lanes pk even, the block's from
+            // lanes pk odd.
+            float h = p[0];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int i = 4 * ti + x;
-                    float v = pair[x];
-                    unsigned cnt = (unsigned)kt;
-                    int L = 0;
-                    while (cnt & 1u) {
-                        v = f_add(sm.st[i][L], v);
-                        cnt >>= 1;
-                        ++L;
-                    }
-                    sm.st[i][L] = v;
+            for (int e = 1; e < 16; ++e) h = f_add(h, p[e]);
+            float blk = f_add(dpp_shr1(h), p[0]);
+#pragma unroll
+            for (int e = 1; e < 16; ++e) blk = f_add(blk, p[e]);
+            // lane pk = 3: block 0's sum (from lane pk = 1) + block 1's, the
+            // complete subtree of blocks 2kt, 2kt + 1, pushed on the row's stack
+            const float pair = f_add(dpp_shr2(blk), blk);
+            if (pk == 3) {
+                float v = pair;
+                unsigned cnt = (unsigned)kt;
+                int L = 0;
+                while (cnt & 1u) {
+                    v = f_add(sm.st[pi][L], v);
+                    cnt >>= 1;
+                    ++L;
                 }
+                sm.st[pi][L] = v;
             }
             __syncthreads();
             // P.V on the matrix cores: this wave's 32 rows x 64 columns, k = 64 keys
