@@ -139,26 +139,20 @@ struct ExpConsts {
     float c[8];
 };
 
-__device__ __forceinline__ float pow2_f32(int e) {   // -126 <= e <= 127
-    return __int_as_float((e + 127) << 23);
-}
-
-// The reduction and the polynomial run on every lane (on 0 where x is NaN or
-// out of range) and the special cases are selected afterwards, so a wave
-// takes no branch.
+// x is clamped into [-104, 89]: the steps give +0 at -104 and +inf at 89,
+// as the definition does beyond them, so only NaN is selected afterwards and
+// a wave takes no branch.  The scaling by 2^k is one ldexp: p * 2^k is exact
+// while it is a normal number, overflows to +inf as the two multiplies do,
+// and below 2^-126 is flushed to +0 by the FTZ mode either way.
 __device__ __forceinline__ float own_exp(float x, const ExpConsts& K) {
-    const bool nan = x != x, big = x > 89.0f, small = x < -104.0f;
-    const float xr = (nan | big | small) ? 0.0f : x;
+    const float xr = __builtin_fminf(__builtin_fmaxf(x, -104.0f), 89.0f);
     float k = f_rne(f_mul(xr, K.l2e));
     float r = f_sub(f_sub(xr, f_mul(k, K.ln2_hi)), f_mul(k, K.ln2_lo));
     float p = K.c[7];
 #pragma unroll
     for (int i = 6; i >= 0; --i) p = f_add(f_mul(p, r), K.c[i]);
-    int ki = (int)k;
-    int k1 = ki / 2;
-    int k2 = ki - k1;
-    const float y = f_mul(f_mul(p, pow2_f32(k1)), pow2_f32(k2));
-    return nan ? x : big ? __int_as_float(0x7f800000) : small ? 0.0f : y;
+    const float y = __builtin_amdgcn_ldexpf(p, (int)k);
+    return x != x ? x : y;
 }
 
 // SwiGLU forward pieces: s = 1/(1 + E(-g)), h = g*s, a = h*u.
