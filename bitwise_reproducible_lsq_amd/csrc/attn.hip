@@ -712,11 +712,18 @@ __device__ __forceinline__ void kv_load_kv(const float* K, int64_t ldk, const fl
             v = *reinterpret_cast<const vf4*>(V + (row0 + row) * ldv + hk * kAD + d4);
         }
         *reinterpret_cast<vf4*>(&kr[row][d4]) = k;
+        // the exact fast path, with the exact quotient where a lane is unsure
         unsigned q4 = 0;
+        bool unsure = false;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            bool in;
-            q4 |= (unsigned)(uint8_t)(int8_t)qz.q(v[u], &in) << (8 * u);
+        for (int u = 0; u < 4; ++u) q4 |= (unsigned)(uint8_t)(int8_t)qz.q_fast(v[u], &unsure) << (8 * u);
+        if (__ballot(unsure)) {
+            q4 = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                bool in;
+                q4 |= (unsigned)(uint8_t)(int8_t)qz.q(v[u], &in) << (8 * u);
+            }
         }
         *reinterpret_cast<unsigned*>(&vq[row][d4]) = row < rows ? q4 : 0u;
     }
