@@ -202,7 +202,8 @@ def measured_peaks(torch, brl):
     and integer ops (2 per multiply-accumulate) of the i8 MFMA 32x32x32."""
     out = {}
     iters = {"v_add_f32": 100000, "v_mul_f32": 100000, "v_add_f32_sgpr": 50000, "valu_u32": 50000,
-             "mfma_k1_f32": 20000, "k1_engine": 20000, "mfma_i8": 8000, "mfma_i8_data": 2000}
+             "mfma_k1_f32": 20000, "k1_engine": 20000, "k1_engine_data": 5000, "mfma_i8": 8000,
+             "mfma_i8_data": 2000}
     buf = torch.empty(int(brl.lib().brl_probe_rate_threads()), dtype=torch.float32, device="cuda")
     st = torch.cuda.current_stream()
     for unit, n in iters.items():
@@ -220,7 +221,8 @@ def measured_peaks(torch, brl):
     out["note"] = ("v_add_f32 / v_mul_f32: binary32 operations with vector-register operands (_sgpr: one "
                    "scalar-register operand); valu_u32: 32-bit shifts and xors; mfma_k1_f32: products of "
                    "v_mfma_f32_16x16x1_4b_f32; k1_engine: multiply-adds of that MFMA (-0 accumulator) "
-                   "followed by a v_add_f32 per product, no memory traffic; mfma_i8: integer ops of "
+                   "followed by a v_add_f32 per product, no memory traffic; k1_engine_data: the same on "
+                   "operands that change from one MFMA to the next; mfma_i8: integer ops of "
                    "v_mfma_i32_32x32x32_i8 on fixed operands; mfma_i8_data: the same with operands that change "
                    "from one MFMA to the next, as in a GEMM")
     return out

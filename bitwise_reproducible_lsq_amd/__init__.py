@@ -511,13 +511,13 @@ def probe_f32(op: str, a: torch.Tensor, b: Optional[torch.Tensor] = None, stream
 
 
 RATE_UNITS = {"v_add_f32": 0, "v_mul_f32": 1, "mfma_k1_f32": 2, "mfma_i8": 3, "valu_u32": 4,
-              "v_add_f32_sgpr": 5, "k1_engine": 6, "mfma_i8_data": 7}
+              "v_add_f32_sgpr": 5, "k1_engine": 6, "mfma_i8_data": 7, "k1_engine_data": 8}
 # operations each thread performs per step of the rate probe (per lane: the
 # MFMA counts are per wave, divided over its 64 lanes; k1_engine counts
 # multiply-adds, a matrix-core product and a VALU add each)
 RATE_OPS_PER_STEP = {"v_add_f32": 8, "v_mul_f32": 8, "mfma_k1_f32": 8 * 1024 / 64, "mfma_i8": 8 * 65536 / 64,
                      "valu_u32": 16, "v_add_f32_sgpr": 8, "k1_engine": 4 * 1024 / 64,
-                     "mfma_i8_data": 32 * 65536 / 64}
+                     "mfma_i8_data": 32 * 65536 / 64, "k1_engine_data": 16 * 1024 / 64}
 
 
 def probe_rate(unit: str, iters: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

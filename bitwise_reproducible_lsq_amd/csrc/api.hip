@@ -514,7 +514,7 @@ brl_status brl_probe_f32(int32_t op, const float* a, const float* b, float* out,
 }
 
 brl_status brl_probe_rate(int32_t what, int64_t iters, float* out, int64_t out_len, void* stream) {
-    if (what < 0 || what > 7) return fail(BRL_EINVAL, "brl_probe_rate: unknown unit %d", what);
+    if (what < 0 || what > 8) return fail(BRL_EINVAL, "brl_probe_rate: unknown unit %d", what);
     if (iters < 1 || iters > ((int64_t)1 << 30)) return fail(BRL_ESHAPE, "brl_probe_rate: iters out of range");
     if (!out || !aligned4(out)) return fail(BRL_EINVAL, "brl_probe_rate: bad output pointer");
     if (out_len < probe_rate_threads())

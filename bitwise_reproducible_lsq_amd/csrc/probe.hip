@@ -24,6 +24,11 @@
 //           step 4 K = 1 fp32 MFMAs with a -0 accumulator and the 64 v_add_f32
 //           that add their products into 4 running sums (4096 multiply-adds
 //           per wave)
+//   WHAT 8: the same engine on operands that change from one MFMA to the
+//           next, as the backward's do: 16 A and 16 B values per lane of
+//           hashed sign and significand (magnitudes in [1, 2)), each step
+//           four rounds of 4 MFMAs (16 distinct operand pairs) and their
+//           256 adds per lane (16384 multiply-adds per wave)
 // The results are stored so that no chain is dead code.
 //
 // probe_mfma_fma_kernel: the K = 1 fp32 MFMA with a non-zero accumulator
@@ -94,6 +99,41 @@ __global__ __launch_bounds__(kRateThreads) void probe_rate_kernel(int64_t iters,
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][e] = f_add(acc[i][e], p[i][e]);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r = f_add(r, acc[i][e]);
+    } else if constexpr (WHAT == 8) {
+        v16fp acc[4], p[4], cneg;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) cneg[e] = -0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = cneg;
+        // operand f of side `ab` (0: A, 1: B): a xorshift of a hash of
+        // (thread, 2f + ab), sign and significand kept, exponent 0
+        float av[16], bv[16];
+#pragma unroll
+        for (int f = 0; f < 16; ++f)
+#pragma unroll
+            for (int ab = 0; ab < 2; ++ab) {
+                unsigned x = ((unsigned)gid + 1u) * 0x9E3779B1u + (unsigned)(2 * f + ab + 1) * 0x85EBCA77u;
+                x ^= x << 13;
+                x ^= x >> 17;
+                x ^= x << 5;
+                const float v = __int_as_float((int)((x & 0x807FFFFFu) | 0x3F800000u));
+                if (ab == 0) av[f] = v;
+                else bv[f] = v;
+            }
+        for (int64_t s = 0; s < iters; ++s)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_mfma_f32_16x16x1f32(av[4 * u + i], bv[4 * u + i], cneg, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][e] = f_add(acc[i][e], p[i][e]);
+            }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -172,6 +212,7 @@ hipError_t launch_probe_rate(int what, int64_t iters, float c, float* out, hipSt
         case 5: hipLaunchKernelGGL(probe_rate_kernel<5>, g, b, 0, st, iters, c, out); break;
         case 6: hipLaunchKernelGGL(probe_rate_kernel<6>, g, b, 0, st, iters, c, out); break;
         case 7: hipLaunchKernelGGL(probe_rate_kernel<7>, g, b, 0, st, iters, c, out); break;
+        case 8: hipLaunchKernelGGL(probe_rate_kernel<8>, g, b, 0, st, iters, c, out); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

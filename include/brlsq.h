@@ -451,7 +451,10 @@ BRL_API brl_status brl_probe_f32(int32_t op, const float* a, const float* b, flo
  * 6 the backward's product engine without memory traffic (4 K=1 fp32 MFMAs
  * with a -0 accumulator and the 64 v_add_f32 that sum their products: 4096
  * multiply-adds per wave per step), 7 the i8 MFMA on operands that change
- * from one MFMA to the next (32 per step per wave, 65536 integer ops each).
+ * from one MFMA to the next (32 per step per wave, 65536 integer ops each),
+ * 8 the product engine of 6 on operands that change from one MFMA to the
+ * next (16 MFMAs and their 256 adds per lane per step: 16384 multiply-adds
+ * per wave per step).
  * out: device, at least brl_probe_rate_threads()
  * floats, receives each thread's chain results (values of no meaning).  The
  * caller times the call with events on `stream`. */

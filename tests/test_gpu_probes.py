@@ -142,7 +142,57 @@ def test_i8_probe_with_changing_operands_computes_its_products():
     assert np.array_equal(got, want), (got[:4], want[:4])
 
 
-@pytest.mark.parametrize("unit", [u for u in brl.RATE_UNITS if u != "mfma_i8_data"])
+def _k1_data_threads(iters: int, gids: np.ndarray) -> np.ndarray:
+    """Outputs of the data-toggling product-engine probe for whole waves.
+
+    Operand f of side ab (0: A, 1: B) of thread g is the binary32 with the
+    sign and significand of xorshift(hash(g, 2f + ab)) and exponent 0.  In
+    the 4-block 16x16x1 MFMA, lane l, register 4b + e receives block b's
+    row 4(l / 16) + e, column l % 16: the product of A from lane
+    16b + 4(l / 16) + e and B from lane 16b + l % 16.  Chain i adds, per
+    step and round u, the products of operand pair 4u + i; the output is
+    the sum of the 64 chain values, chain by chain, register by register.
+    Every product and sum is rounded to binary32 by numpy."""
+    g = gids.astype(np.uint32)
+    vals = {}
+    with np.errstate(over="ignore"):
+        for f in range(16):
+            for ab in range(2):
+                x = (g + np.uint32(1)) * np.uint32(0x9E3779B1) + np.uint32(2 * f + ab + 1) * np.uint32(0x85EBCA77)
+                x = x ^ (x << np.uint32(13))
+                x = x ^ (x >> np.uint32(17))
+                x = x ^ (x << np.uint32(5))
+                vals[f, ab] = ((x & np.uint32(0x807FFFFF)) | np.uint32(0x3F800000)).view(np.float32).reshape(-1, 64)
+    lane = np.arange(64)
+    # [lane, register] -> source lanes of A and B
+    src_a = np.array([[16 * (r // 4) + 4 * (l // 16) + r % 4 for r in range(16)] for l in lane])
+    src_b = np.array([[16 * (r // 4) + l % 16 for r in range(16)] for l in lane])
+    acc = np.zeros((4, len(gids) // 64, 64, 16), np.float32)
+    prods = [(vals[f, 0][:, src_a] * vals[f, 1][:, src_b]).astype(np.float32) for f in range(16)]
+    for _ in range(iters):
+        for u in range(4):
+            for i in range(4):
+                acc[i] = (acc[i] + prods[4 * u + i]).astype(np.float32)
+    out = np.zeros((len(gids) // 64, 64), np.float32)
+    for i in range(4):
+        for r in range(16):
+            out = (out + acc[i][:, :, r]).astype(np.float32)
+    return out.reshape(-1)
+
+
+def test_product_engine_probe_with_changing_operands_computes_its_sums():
+    iters = 40
+    out = brl.probe_rate("k1_engine_data", iters)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    # whole waves from the first, a middle and the last workgroup
+    gids = np.concatenate([np.arange(0, 256), np.arange(2048 * 256, 2048 * 256 + 256),
+                           np.arange(got.size - 256, got.size)])
+    want = _k1_data_threads(iters, gids)
+    assert np.array_equal(got[gids].view(np.uint32), want.view(np.uint32)), (got[gids][:4], want[:4])
+
+
+@pytest.mark.parametrize("unit", [u for u in brl.RATE_UNITS if u not in ("mfma_i8_data", "k1_engine_data")])
 def test_rate_probe_chains_end_where_they_should(unit):
     iters = 40
     out = brl.probe_rate(unit, iters)
