@@ -22,17 +22,18 @@
 //   pass 1: exact logits on the product engine below (the matrix cores form
 //           each product, rounded on its own; the VALU adds d-blocks of 32
 //           left to right, then the pairwise tree), stored in the
-//           workgroup's slot of the workspace, and the exact row maxima
-//           (order-free integer maxima);
-//   pass 2: the stored logits -> p -> the 32-key block sums, each a
-//           left-to-right chain through the 8 lanes that hold its keys (DPP
-//           shifts within a 16-lane row); a tile's two blocks are a complete
-//           pair (their absolute indices are 2kt, 2kt+1), so their sum is
-//           pushed on the row's binary-counter stack of pairs at index kt;
-//           q_p and q_v staged as int8 in LDS and multiplied on
-//           v_mfma_i32_32x32x32_i8 into int32 accumulators.
-// Pass 2 reads the logits with another thread mapping (4 x 4 per thread)
-// after a workgroup barrier.
+//           workgroup's slot of the workspace; each lane keeps running
+//           maxima of its rows (order-free integer maxima), reduced over
+//           the workgroup once per item;
+//   pass 2: the stored logits -> p -> the 32-key block sums, each two
+//           16-add chains of one row's consecutive keys joined by a DPP
+//           shift; a tile's two blocks are a complete pair (their absolute
+//           indices are 2kt, 2kt+1), so their sum is pushed on the row's
+//           binary-counter stack of pairs at index kt; q_p and q_v staged as
+//           int8 in LDS and multiplied on v_mfma_i32_32x32x32_i8 into int32
+//           accumulators.
+// Pass 2 reads the logits with another thread mapping (one row and 16 keys
+// per thread) after a workgroup barrier.
 // Pairs before the first real one are +0 subtrees (the stack starts zeroed)
 // and merging with +0 is exact, so this is CanonSum over the whole axis.
 // LDS is kept under 80 KB so that two workgroups share a CU.
