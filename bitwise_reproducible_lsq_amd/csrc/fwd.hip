@@ -349,6 +349,43 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_i8_kern
     if constexpr (EPI == BRL_EPILOGUE_SWIGLU) {
         // wave columns: tiles [0, kTN/2) are gate, [kTN/2, kTN) the matching up
         const int64_t H = a.N / 2;
+        // whole tile inside Y (its rows, and the gate columns of its virtual
+        // column groups), no addend, offsets within the tile below 2^29:
+        // branch-free stores at 32-bit offsets from the tile's corner
+        const bool full = (m0 + BM <= a.M) && (n0 / 2 + BN / 2 <= H) && !a.addend &&
+                          (int64_t)BM * a.N < ((int64_t)1 << 29);   // byte offsets below 2^31
+        if (full) {
+            // a wave's virtual columns are one gate/up group pair: gate
+            // column gcol0 + c and up column H + gcol0 + c, c < kSwigluGroup;
+            // stores at 32-bit byte offsets from uniform bases
+            const int64_t gcol0 = (n0 + wn * WN) / 2;
+            const unsigned N4 = 4u * (unsigned)a.N, H4 = 4u * (unsigned)H;
+            char* Yt = reinterpret_cast<char*>(a.Y + m0 * H + gcol0);
+            auto tile = [&](auto pre) {
+                char* Pt = reinterpret_cast<char*>(a.Ypre + m0 * a.N + gcol0);
+#pragma unroll
+                for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const unsigned rl = (unsigned)(wm * WM + i * 32 + (r >> 2) * 8 + row_q + (r & 3));
+#pragma unroll
+                        for (int j = 0; j < C::kTN / 2; ++j) {
+                            const unsigned c4 = 4u * (unsigned)(j * 32 + col_l);
+                            const float g = f_mul((float)acc[i][j][r], s_y);
+                            const float u = f_mul((float)acc[i][j + C::kTN / 2][r], s_y);
+                            if constexpr (decltype(pre)::value) {
+                                *reinterpret_cast<float*>(Pt + (rl * N4 + c4)) = g;
+                                *reinterpret_cast<float*>(Pt + (rl * N4 + H4 + c4)) = u;
+                            }
+                            const float sg = swiglu_sigma(g, a.ek);
+                            *reinterpret_cast<float*>(Yt + (rl * H4 + c4)) = f_mul(f_mul(g, sg), u);
+                        }
+                    }
+            };
+            if (a.Ypre) tile(std::true_type{});
+            else tile(std::false_type{});
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i)
 #pragma unroll

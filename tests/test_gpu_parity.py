@@ -165,12 +165,20 @@ def test_fwd_addend():
     assert_bitwise(Y, oracle.linear_fwd(inp.X, inp.W, synth.S_X, addend=add), "Y+C")
 
 
-@pytest.mark.parametrize("M,K,N", [(200, 96, 256), (70, 64, 198), (256, 512, 512)])
-def test_fwd_swiglu_parity(M, K, N):
+# (256, 512, 512) and (512, 128, 1024) are whole 256 x 256 tiles (the
+# epilogue's branch-free path); (300, 64, 640) mixes whole tiles with tiles
+# cut by M and by the gate columns in one launch
+@pytest.mark.parametrize("want_ypre", [True, False])
+@pytest.mark.parametrize("M,K,N", [(200, 96, 256), (70, 64, 198), (256, 512, 512), (512, 128, 1024), (300, 64, 640)])
+def test_fwd_swiglu_parity(M, K, N, want_ypre):
     inp = _case_inputs(M, K, N, seed=11, swiglu=True)
-    Y, Ypre, _ = brl.qat_linear_fwd(_cuda(inp.X), _cuda(inp.W), synth.S_X, epilogue=brl.EPILOGUE_SWIGLU)
+    Y, Ypre, _ = brl.qat_linear_fwd(_cuda(inp.X), _cuda(inp.W), synth.S_X, epilogue=brl.EPILOGUE_SWIGLU,
+                                    want_ypre=want_ypre)
     wantY, wantPre = oracle.linear_fwd(inp.X, inp.W, synth.S_X, epilogue=1)
-    assert_bitwise(Ypre, wantPre, "Ypre")
+    if want_ypre:
+        assert_bitwise(Ypre, wantPre, "Ypre")
+    else:
+        assert Ypre is None
     assert_bitwise(Y, wantY, "SwiGLU(Y)")
 
 
