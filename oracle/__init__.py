@@ -281,11 +281,11 @@ def replay(partials, R, S, max_norm=1.0, eps=0.0):
     return T, nu, A
 
 
-# ---- AdamW (NEXT-2) ---------------------------------------------------------------
+# ---- AdamW ----------------------------------------------------------------------
 # Recipe (onedev.kr summary, "Limits", recipe paragraph): AdamW(0.9, 0.95, 1e-8),
 # decoupled weight decay 0.1 except input embedding, norm weights and RoPE table;
 # linear warm-up to 4.5e-4 over about 2.1B tokens, then one cosine decay to 10% of
-# the peak at 400B tokens, keyed to consumed tokens.  Reading R19 (see or_adamw in
+# the peak at 400B tokens, keyed to consumed tokens.  The reading taken (see or_adamw in
 # oracle.c): the step's scalars in binary64, each rounded once to binary32.
 ADAMW = dict(beta1=0.9, beta2=0.95, eps=1e-8, wd=0.1, peak_lr=4.5e-4, min_lr=4.5e-5,
              warmup_tokens=2.1e9, total_tokens=400e9)

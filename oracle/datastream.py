@@ -16,8 +16,8 @@ position, Philox) and section "What differs" (the data stream):
   * a rank-independent resume record: documents consumed per source, epoch
     counters, the mix generator's state, the partial window in the packing
     buffer.
-Where the pages stop, this module takes the readings listed in the design doc
-(reading R22): how a tuple becomes a Philox key, how draws become bounded
+Where the pages stop, this module takes its own readings, stated where they
+are used: how a tuple becomes a Philox key, how draws become bounded
 integers and permutations, how sources are weighted.
 
 Philox4x32-10 is written from its published definition (Salmon, Moraes, Dror

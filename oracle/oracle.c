@@ -19,9 +19,9 @@
  *     audit replay = running-sum reduce-scatter over virtual ranks in mesh
  *     order (replica-major, shard-minor), then TreeFold in the pairing order
  *     of a recursive-doubling all-reduce.
- * Points the pages leave open take the readings listed in the design doc
- * ("Readings"): RNE everywhere, clamp to [-127,127], 32-wide sequential
- * blocks then a level-by-level pairwise tree, STE mask = select +0.
+ * Points the pages leave open take these readings: RNE everywhere, clamp
+ * to [-127,127], 32-wide sequential blocks then a level-by-level pairwise
+ * tree, STE mask = select +0.
  *
  * Arithmetic model.  Every binary32 operation (add, sub, mul, div, sqrt) is
  * computed in IEEE double from the (DAZ-flushed) float operands and rounded
@@ -555,7 +555,7 @@ float or_clip(float* T, int64_t len, float nu, float max_norm, float eps) {
  * 2.1B tokens, then one cosine decay to 10% of the peak at the 400B-token
  * budget, keyed to consumed tokens (onedev.kr summary, "Limits", recipe
  * paragraph).  The pages fix neither the operation order nor how the step's
- * scalars are formed; the reading taken (R19):
+ * scalars are formed; the reading taken:
  *   step scalars, in binary64 from the step t >= 1 and the tokens consumed,
  *   each rounded once to binary32: lr, c1 = 1 - beta1, c2 = 1 - beta2,
  *   bc1 = 1 - beta1^t, bc2 = 1 - beta2^t, d = lr * wd;

@@ -23,7 +23,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-S_X = 0.05          # activation step (one value for every layer; see the design doc readings)
+S_X = 0.05          # activation step: a caller constant, one value for every layer
 
 TENSOR_ID = {"X": 1, "W": 2, "dY": 3, "gate": 4, "lin": 5, "mask": 6, "sub": 7, "addend": 8,
              "Q": 9, "K": 10, "V": 11}

@@ -3,7 +3,7 @@ ordered reduction, norm, clip, AdamW update -- reproduces its state hash bit
 for bit, and each of the deviations the method rules out changes the hash:
 a corrupted partial, a wrong mesh order, a wrong TreeFold pairing, a fused
 multiply-add in the optimizer (onedev.kr summary, sections "How" and "Limits",
-audit paragraph; the state hash of reading R18)."""
+audit paragraph; the state hash is this library's reading, a tree of SHA-256 digests)."""
 import numpy as np
 
 import oracle

@@ -1,9 +1,9 @@
 """Pins for CanonSum: 32-wide sequential blocks, then a fixed pairwise tree.
 
 The order is the one the method fixes for every reduction (onedev.kr summary,
-"How": one reduction order on all hardware).  The block width and the
-"blocks first, then a pairwise tree" shape are the reading stated in
-the design doc.  Pins: exact-sum inputs, hand-derived order-revealing inputs
+"How": one reduction order on all hardware).  The block width (32) and the
+"blocks first, then a pairwise tree" shape are this library's reading of
+it.  Pins: exact-sum inputs, hand-derived order-revealing inputs
 (tests/golden/canon_sum_cases.json), agreement with an independently written
 description of the same tree (split at the largest power of two) evaluated in
 host binary32, and sensitivity checks showing that other plausible orders

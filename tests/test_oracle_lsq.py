@@ -5,8 +5,8 @@ Method: onedev.kr summary of Open-1B, section "Use" (LSQ int8 QAT on every
 attention/FFN linear, weight step 2*mean(|w|)/sqrt(q_max) recomputed every
 step, SwiGLU gate and up computed by one GEMM) and section "How" (unfused
 multiply then add, fixed reduction order, FTZ).  Readings for what the pages
-leave open (RNE, clamp [-127,127], select +0 outside the STE range, s_x a
-caller constant) are listed in the design doc.
+leave open: RNE, clamp [-127,127], select +0 outside the STE range, s_x a
+caller constant.
 """
 import json
 import os

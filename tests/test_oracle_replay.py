@@ -7,7 +7,7 @@ shard-minor, one partial resident at a time; TreeFold in the pairing order of
 the cluster's recursive-doubling all-reduce) and recipe paragraph (global L2
 gradient-norm clipping at 1.0).  For six replicas the fold of ranks 4 and 5
 into 0 and 1 before recursive doubling is the plain reading of recursive
-doubling on a non-power-of-two group (readings).
+doubling on a non-power-of-two group.
 """
 import itertools
 
