@@ -128,7 +128,10 @@ def stream_bench(torch, brl, dev, with_cpu: bool):
 def attention_bench(torch, brl, dev):
     """attn_fwd, attn_bwd_dq and attn_bwd_dkdv on one Open-1B layer's
     microbatch (4 x 4096 tokens, 16 query / 4 KV heads of 128), window 512 and
-    full causal; device-generated inputs (parity at this size is a GPU test)."""
+    full causal; device-generated inputs (parity at this size is a GPU test).
+    Each kernel is timed on its own (the backward forming the logits again),
+    then the training path: the forward keeping its logits and the backward
+    reading them."""
     B, S, Hq, Hkv = 4, 4096, 16, 4
     g = torch.Generator(device=dev)
     g.manual_seed(5)
@@ -141,56 +144,56 @@ def attention_bench(torch, brl, dev):
     dK, dV = torch.empty_like(K), torch.empty_like(V)
     stats = torch.empty(B, S, Hq, 2, device=dev)
     out = {"shape": {"B": B, "S": S, "Hq": Hq, "Hkv": Hkv, "D": ATTN_D, "s_v": 0.05}}
-    for name, window in (("window_512", 512), ("causal", 0)):
-        logits = B * Hq * sum(min(i + 1, window) if window > 0 else i + 1 for i in range(S))
-        brl.attn_fwd(Q, K, V, window, 0.05, O=O)
+
+    def timed(fn, reps=3):
+        fn()
+        fn()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        for _ in range(3):
-            brl.attn_fwd(Q, K, V, window, 0.05, O=O)
+        for _ in range(reps):
+            fn()
         b.record()
         torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / 3
-        ops = 2.0 * ATTN_D * logits
-        out[name] = {"ms": round(ms, 4), "logits": logits,
-                     "roofline": {"bound": "alu", "achieved": round(ops / (ms * 1e-3) / 1e12, 3),
-                                  "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
-                                  "frac": round(ops / (ms * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4),
-                                  "note": "2*D binary32 ops per allowed logit, counted once"}}
-        # dQ with 64-bit fixed-point accumulation: logits, dP and the dS.K
-        # products, 3 * 2*D binary32 ops per allowed (row, key)
+        return a.elapsed_time(b) / reps
+
+    def line(ms, ops, note):
+        return {"ms": round(ms, 4),
+                "roofline": {"bound": "alu", "achieved": round(ops / (ms * 1e-3) / 1e12, 3),
+                             "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
+                             "frac": round(ops / (ms * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4), "note": note}}
+
+    for name, window in (("window_512", 512), ("causal", 0)):
+        logits = B * Hq * sum(min(i + 1, window) if window > 0 else i + 1 for i in range(S))
+        ops = 2.0 * ATTN_D * logits             # one binary32 product and add per (row, key, d)
+        ms = timed(lambda: brl.attn_fwd(Q, K, V, window, 0.05, O=O), reps=10)
+        out[name] = line(ms, ops, "2*D binary32 ops per allowed logit, counted once")
+        out[name]["logits"] = logits
+        # dQ with 64-bit fixed-point accumulation: logits, dP and the dS.K products
         brl.attn_fwd(Q, K, V, window, 0.05, O=O, stats=stats)
-        brl.attn_bwd_dq(Q, K, V, O, dO, stats, window, 0.05, dQ=dQ)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(3):
-            brl.attn_bwd_dq(Q, K, V, O, dO, stats, window, 0.05, dQ=dQ)
-        b.record()
-        torch.cuda.synchronize()
-        ms_dq = a.elapsed_time(b) / 3
-        ops_dq = 3 * ops
-        out[name]["dq"] = {"ms": round(ms_dq, 4),
-                           "roofline": {"bound": "alu", "achieved": round(ops_dq / (ms_dq * 1e-3) / 1e12, 3),
-                                        "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
-                                        "frac": round(ops_dq / (ms_dq * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4),
-                                        "note": "3 * 2*D binary32 ops per allowed (row, key)"}}
-        # dK and dV: logits, dP, P.dO and dS.Q, 4 * 2*D ops per allowed (row, key)
-        brl.attn_bwd_dkdv(Q, K, V, O, dO, stats, window, 0.05, dK=dK, dV=dV)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(3):
-            brl.attn_bwd_dkdv(Q, K, V, O, dO, stats, window, 0.05, dK=dK, dV=dV)
-        b.record()
-        torch.cuda.synchronize()
-        ms_kv = a.elapsed_time(b) / 3
-        ops_kv = 4 * ops
-        out[name]["dkdv"] = {"ms": round(ms_kv, 4),
-                             "roofline": {"bound": "alu", "achieved": round(ops_kv / (ms_kv * 1e-3) / 1e12, 3),
-                                          "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
-                                          "frac": round(ops_kv / (ms_kv * 1e-3) / 1e12 / PEAK_VALU_F32_TOPS, 4),
-                                          "note": "4 * 2*D binary32 ops per allowed (row, key)"}}
+        ms_dq = timed(lambda: brl.attn_bwd_dq(Q, K, V, O, dO, stats, window, 0.05, dQ=dQ))
+        out[name]["dq"] = line(ms_dq, 3 * ops, "3 * 2*D binary32 ops per allowed (row, key)")
+        # dK and dV: logits, dP, P.dO and dS.Q
+        ms_kv = timed(lambda: brl.attn_bwd_dkdv(Q, K, V, O, dO, stats, window, 0.05, dK=dK, dV=dV))
+        out[name]["dkdv"] = line(ms_kv, 4 * ops, "4 * 2*D binary32 ops per allowed (row, key)")
+        # the training path: the forward keeps its logits (attn_fwd_keep_logits), the
+        # backward reads them (attn_bwd_dq_logits, attn_bwd_dkdv_logits)
+        L = brl.attn_logits_buffer(B, S, Hq, window, dev)
+        ms_fk = timed(lambda: brl.attn_fwd(Q, K, V, window, 0.05, O=O, stats=stats, logits=L), reps=10)
+        ms_dqk = timed(lambda: brl.attn_bwd_dq(Q, K, V, O, dO, stats, window, 0.05, dQ=dQ, logits=L))
+        ms_kvk = timed(lambda: brl.attn_bwd_dkdv(Q, K, V, O, dO, stats, window, 0.05, dK=dK, dV=dV, logits=L))
+        tot = ms_fk + ms_dqk + ms_kvk
+        out[name]["kept_logits"] = {
+            "bytes": L.numel() * 4,
+            "fwd": line(ms_fk, ops, "2*D ops per allowed logit; the logits written to HBM for the backward"),
+            "dq": line(ms_dqk, 2 * ops, "2 * 2*D ops per allowed (row, key): dP and dS.K"),
+            "dkdv": line(ms_kvk, 3 * ops, "3 * 2*D ops per allowed (row, key): dP, P.dO and dS.Q"),
+            "layer_fwd_bwd": line(tot, 5 * ops, "fwd + dQ + dK/dV against 5 * 2*D ops per allowed (row, key): "
+                                               "the logits, dP, dS.K, P.dO and dS.Q, each once (dP is formed "
+                                               "by both backward kernels, counted once)")}
+        del L
+        torch.cuda.empty_cache()
     del Q, K, V, O, dO, dQ, dK, dV, stats
     return out
 

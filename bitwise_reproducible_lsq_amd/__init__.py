@@ -69,6 +69,13 @@ _SIGS = {
     "adamw_step": (i32, [P, P, P, P, i64, P, i32, P]),
     "attn_fwd": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64, P, P, sz, P]),
     "attn_fwd_workspace_bytes": (sz, [i64, i64, i64, i64, i64]),
+    "attn_fwd_keep_logits": (i32, [P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, i64, P, P, sz, P,
+                                   sz, P]),
+    "attn_logits_bytes": (sz, [i64, i64, i64, i64]),
+    "attn_bwd_dq_logits": (i32, [P, P, P, P, P, P, P, sz, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P,
+                                 P]),
+    "attn_bwd_dkdv_logits": (i32, [P, P, P, P, P, P, P, sz, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P,
+                                   P, i64, P]),
     "attn_bwd_dq": (i32, [P, P, P, P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, P]),
     "attn_bwd_dkdv": (i32, [P, P, P, P, P, P, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, f32, P, P, i64,
                             P]),
@@ -341,12 +348,35 @@ def _heads_view(t: torch.Tensor, name: str):
     return C.c_void_p(t.data_ptr()), t.stride(1) if S > 1 else H * D
 
 
+def attn_logits_bytes(B: int, S: int, Hq: int, window: int) -> int:
+    """Bytes of the logits attn_fwd keeps when given a logits buffer."""
+    return int(lib().attn_logits_bytes(B, S, Hq, int(window)))
+
+
+def attn_logits_buffer(B: int, S: int, Hq: int, window: int, device="cuda") -> torch.Tensor:
+    """A float32 buffer for the logits attn_fwd keeps (attn_fwd_keep_logits)
+    and attn_bwd_dq / attn_bwd_dkdv read."""
+    n = attn_logits_bytes(B, S, Hq, window)
+    if n == 0 and B * S > 0:
+        raise BrlError(BRL_ESHAPE, f"attn_logits_bytes: no size for B={B} S={S} Hq={Hq}")
+    return torch.empty(max(n // 4, 1), dtype=torch.float32, device=device)
+
+
+def _logits_arg(logits: torch.Tensor, B: int, S: int, Hq: int, window: int):
+    if logits.dtype != torch.float32 or not logits.is_contiguous() or not logits.is_cuda:
+        raise ValueError("logits must be a dense float32 device tensor (attn_logits_buffer)")
+    return _ptr(logits), logits.numel() * 4
+
+
 def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, window: int, s_v: float,
-             O: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+             O: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None, stream=None,
+             logits: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Attention with int8 P.V (attn_fwd).  Q [B, S, Hq, D], K and V
     [B, S, Hkv, D], views with evenly spaced rows (column slices of the QKV
     projection output work); returns O [B, S, Hq, D].  stats, if given, is a
-    float32 [B, S, Hq, 2] tensor receiving (m_i, l_i) for attn_bwd_dq."""
+    float32 [B, S, Hq, 2] tensor receiving (m_i, l_i) for attn_bwd_dq.
+    logits, if given (attn_logits_buffer), receives the exact logits for the
+    backward (attn_fwd_keep_logits)."""
     B, S, Hq, D = Q.shape
     Hkv = K.shape[2]
     if K.shape != (B, S, Hkv, D) or V.shape != K.shape:
@@ -365,16 +395,23 @@ def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, window: int, s_v
     ws = torch.empty(nws, dtype=torch.uint8, device=Q.device)
     if stream is not None and stream != torch.cuda.current_stream(Q.device):
         ws.record_stream(stream)
-    _check(lib().attn_fwd(q, k, v, B, S, Hq, Hkv, D, ldq, ldk, ldv, int(window), float(s_v), o, ldo,
-                          _ptr(stats), _ptr(ws), ws.numel(), _stream(stream)))
+    if logits is None:
+        _check(lib().attn_fwd(q, k, v, B, S, Hq, Hkv, D, ldq, ldk, ldv, int(window), float(s_v), o, ldo,
+                              _ptr(stats), _ptr(ws), ws.numel(), _stream(stream)))
+    else:
+        lp, lb = _logits_arg(logits, B, S, Hq, window)
+        _check(lib().attn_fwd_keep_logits(q, k, v, B, S, Hq, Hkv, D, ldq, ldk, ldv, int(window), float(s_v), o, ldo,
+                                          _ptr(stats), lp, lb, _ptr(ws), ws.numel(), _stream(stream)))
     return O
 
 
 def attn_bwd_dq(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor, dO: torch.Tensor,
                 stats: torch.Tensor, window: int, s_v: float, dQ: Optional[torch.Tensor] = None,
-                stream=None) -> torch.Tensor:
+                stream=None, logits: Optional[torch.Tensor] = None) -> torch.Tensor:
     """dQ of attn_fwd with 64-bit fixed-point accumulation (attn_bwd_dq).
-    O, dO and dQ are dense [B, S, Hq, D]; stats as written by attn_fwd."""
+    O, dO and dQ are dense [B, S, Hq, D]; stats as written by attn_fwd.
+    logits, if given, the ones attn_fwd kept for the same inputs
+    (attn_bwd_dq_logits: the same bits, one product fewer)."""
     B, S, Hq, D = Q.shape
     Hkv = K.shape[2]
     for t, n in ((O, "O"), (dO, "dO")):
@@ -389,18 +426,24 @@ def attn_bwd_dq(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tens
     k, ldk = _heads_view(K, "K")
     v, ldv = _heads_view(V, "V")
     ld = Hq * D
-    _check(lib().attn_bwd_dq(q, k, v, _ptr(O), _ptr(dO), _ptr(stats), B, S, Hq, Hkv, D, ldq, ldk, ldv, ld,
-                             int(window), float(s_v), _ptr(dQ), _stream(stream)))
+    if logits is None:
+        _check(lib().attn_bwd_dq(q, k, v, _ptr(O), _ptr(dO), _ptr(stats), B, S, Hq, Hkv, D, ldq, ldk, ldv, ld,
+                                 int(window), float(s_v), _ptr(dQ), _stream(stream)))
+    else:
+        lp, lb = _logits_arg(logits, B, S, Hq, window)
+        _check(lib().attn_bwd_dq_logits(q, k, v, _ptr(O), _ptr(dO), _ptr(stats), lp, lb, B, S, Hq, Hkv, D, ldq, ldk,
+                                        ldv, ld, int(window), float(s_v), _ptr(dQ), _stream(stream)))
     return dQ
 
 
 def attn_bwd_dkdv(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor, dO: torch.Tensor,
                   stats: torch.Tensor, window: int, s_v: float, dK: Optional[torch.Tensor] = None,
-                  dV: Optional[torch.Tensor] = None, stream=None):
+                  dV: Optional[torch.Tensor] = None, stream=None, logits: Optional[torch.Tensor] = None):
     """dK and dV of attn_fwd with 64-bit fixed-point accumulation
     (attn_bwd_dkdv).  O and dO dense [B, S, Hq, D]; stats as written by
     attn_fwd; dK and dV [B, S, Hkv, D] views sharing one row stride (column
-    slices of a QKV gradient buffer work).  Returns (dK, dV)."""
+    slices of a QKV gradient buffer work).  logits, if given, the ones
+    attn_fwd kept (attn_bwd_dkdv_logits).  Returns (dK, dV)."""
     B, S, Hq, D = Q.shape
     Hkv = K.shape[2]
     for t, n in ((O, "O"), (dO, "dO")):
@@ -424,8 +467,13 @@ def attn_bwd_dkdv(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Te
     q, ldq = _heads_view(Q, "Q")
     k, ldk = _heads_view(K, "K")
     v, ldv = _heads_view(V, "V")
-    _check(lib().attn_bwd_dkdv(q, k, v, _ptr(O), _ptr(dO), _ptr(stats), B, S, Hq, Hkv, D, ldq, ldk, ldv, Hq * D,
-                               int(window), float(s_v), pk, pv, ldg, _stream(stream)))
+    if logits is None:
+        _check(lib().attn_bwd_dkdv(q, k, v, _ptr(O), _ptr(dO), _ptr(stats), B, S, Hq, Hkv, D, ldq, ldk, ldv, Hq * D,
+                                   int(window), float(s_v), pk, pv, ldg, _stream(stream)))
+    else:
+        lp, lb = _logits_arg(logits, B, S, Hq, window)
+        _check(lib().attn_bwd_dkdv_logits(q, k, v, _ptr(O), _ptr(dO), _ptr(stats), lp, lb, B, S, Hq, Hkv, D, ldq,
+                                          ldk, ldv, Hq * D, int(window), float(s_v), pk, pv, ldg, _stream(stream)))
     return dK, dV
 
 

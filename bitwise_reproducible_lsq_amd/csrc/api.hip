@@ -620,58 +620,130 @@ size_t attn_fwd_workspace_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, i
     return attn_fwd_ws_bytes(B, S, Hq, Hkv, window);
 }
 
+size_t attn_logits_bytes(int64_t B, int64_t S, int64_t Hq, int64_t window) {
+    if (B < 0 || S < 0 || S > 133143 || Hq <= 0) return 0;
+    if (B * Hq * ((S + 63) / 64) > 0xffffffffLL) return 0;
+    return attn_keep_bytes(B, S, Hq, window);
+}
+
+// kept logits: device, 256-byte aligned, at least attn_logits_bytes
+static brl_status check_logits(const char* who, const void* logits, size_t bytes, int64_t B, int64_t S, int64_t Hq,
+                               int64_t window) {
+    const size_t need = attn_keep_bytes(B, S, Hq, window);
+    if (!logits) return fail(BRL_EINVAL, "%s: null logits", who);
+    if (!aligned256(logits)) return fail(BRL_EINVAL, "%s: logits must be 256-byte aligned", who);
+    if (bytes < need) return fail(BRL_ESHAPE, "%s: logits %zu < %zu bytes", who, bytes, need);
+    return BRL_OK;
+}
+
+static brl_status attn_fwd_impl(const char* who, const float* Q, const float* K, const float* V, int64_t B,
+                                int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv,
+                                int64_t window, float s_v, float* O, int64_t ldo, float* stats, float* keep,
+                                size_t keep_bytes, void* ws, size_t ws_bytes, void* stream) {
+    brl_status rc = attn_check(who, B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo, s_v);
+    if (rc != BRL_OK) return rc;
+    if (B * S == 0) return BRL_OK;
+    if (!Q || !K || !V || !O) return fail(BRL_EINVAL, "%s: null tensor", who);
+    if (!al16p(Q) || !al16p(K) || !al16p(V) || !al16p(O))
+        return fail(BRL_EINVAL, "%s: pointers must be 16-byte aligned", who);
+    if (stats && !aligned4(stats)) return fail(BRL_EINVAL, "%s: stats must be 4-byte aligned", who);
+    if (B * Hq * ((S + 63) / 64) > 0xffffffffLL) return fail(BRL_ESHAPE, "%s: too many query blocks", who);
+    if (keep && (rc = check_logits(who, keep, keep_bytes, B, S, Hq, window)) != BRL_OK) return rc;
+    const size_t need = attn_fwd_ws_bytes(B, S, Hq, Hkv, window);
+    if (!aligned256(ws)) return fail(BRL_EINVAL, "%s: workspace must be 256-byte aligned", who);
+    if (!ws || ws_bytes < need) return fail(BRL_EWORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+    return check_hip(launch_attn_fwd(Q, K, V, B, S, Hq, Hkv, ldq, ldk, ldv, window, s_v, O, ldo, stats,
+                                     static_cast<float*>(ws), keep, exp_constants(),
+                                     static_cast<hipStream_t>(stream)),
+                     "attention");
+}
+
 brl_status attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
                     int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
                     float* O, int64_t ldo, float* stats, void* ws, size_t ws_bytes, void* stream) {
-    brl_status rc = attn_check("attn_fwd", B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo, s_v);
+    return attn_fwd_impl("attn_fwd", Q, K, V, B, S, Hq, Hkv, D, ldq, ldk, ldv, window, s_v, O, ldo, stats, nullptr,
+                         0, ws, ws_bytes, stream);
+}
+
+brl_status attn_fwd_keep_logits(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
+                                int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window,
+                                float s_v, float* O, int64_t ldo, float* stats, float* logits, size_t logits_bytes,
+                                void* ws, size_t ws_bytes, void* stream) {
+    if (!logits && B * S != 0) return fail(BRL_EINVAL, "attn_fwd_keep_logits: null logits");
+    return attn_fwd_impl("attn_fwd_keep_logits", Q, K, V, B, S, Hq, Hkv, D, ldq, ldk, ldv, window, s_v, O, ldo,
+                         stats, logits, logits_bytes, ws, ws_bytes, stream);
+}
+
+static brl_status attn_bwd_dq_impl(const char* who, const float* Q, const float* K, const float* V, const float* O,
+                                   const float* dO, const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                   int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int64_t window,
+                                   float s_v, float* dQ, const float* keep, size_t keep_bytes, void* stream) {
+    brl_status rc = attn_check(who, B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo, s_v);
     if (rc != BRL_OK) return rc;
     if (B * S == 0) return BRL_OK;
-    if (!Q || !K || !V || !O) return fail(BRL_EINVAL, "attn_fwd: null tensor");
-    if (!al16p(Q) || !al16p(K) || !al16p(V) || !al16p(O))
-        return fail(BRL_EINVAL, "attn_fwd: pointers must be 16-byte aligned");
-    if (stats && !aligned4(stats)) return fail(BRL_EINVAL, "attn_fwd: stats must be 4-byte aligned");
-    if (B * Hq * ((S + 63) / 64) > 0xffffffffLL) return fail(BRL_ESHAPE, "attn_fwd: too many query blocks");
-    const size_t need = attn_fwd_ws_bytes(B, S, Hq, Hkv, window);
-    if (!aligned256(ws)) return fail(BRL_EINVAL, "attn_fwd: workspace must be 256-byte aligned");
-    if (!ws || ws_bytes < need) return fail(BRL_EWORKSPACE, "attn_fwd: workspace %zu < %zu bytes", ws_bytes, need);
-    return check_hip(launch_attn_fwd(Q, K, V, B, S, Hq, Hkv, ldq, ldk, ldv, window, s_v, O, ldo, stats,
-                                     static_cast<float*>(ws), exp_constants(), static_cast<hipStream_t>(stream)),
-                     "attention");
+    if (!Q || !K || !V || !O || !dO || !stats || !dQ) return fail(BRL_EINVAL, "%s: null tensor", who);
+    if (!al16p(Q) || !al16p(K) || !al16p(V) || !al16p(O) || !al16p(dO) || !al16p(dQ))
+        return fail(BRL_EINVAL, "%s: pointers must be 16-byte aligned", who);
+    if (!aligned4(stats)) return fail(BRL_EINVAL, "%s: stats must be 4-byte aligned", who);
+    if (keep && (rc = check_logits(who, keep, keep_bytes, B, S, Hq, window)) != BRL_OK) return rc;
+    return check_hip(launch_attn_bwd_dq(Q, K, V, O, dO, stats, B, S, Hq, Hkv, ldq, ldk, ldv, ldo, window, s_v, dQ,
+                                        keep, exp_constants(), static_cast<hipStream_t>(stream)),
+                     "attention dQ");
 }
 
 brl_status attn_bwd_dq(const float* Q, const float* K, const float* V, const float* O, const float* dO,
                        const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t ldq,
                        int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dQ,
                        void* stream) {
-    brl_status rc = attn_check("attn_bwd_dq", B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo, s_v);
+    return attn_bwd_dq_impl("attn_bwd_dq", Q, K, V, O, dO, stats, B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo, window, s_v,
+                            dQ, nullptr, 0, stream);
+}
+
+brl_status attn_bwd_dq_logits(const float* Q, const float* K, const float* V, const float* O, const float* dO,
+                              const float* stats, const float* logits, size_t logits_bytes, int64_t B, int64_t S,
+                              int64_t Hq, int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
+                              int64_t window, float s_v, float* dQ, void* stream) {
+    if (!logits && B * S != 0) return fail(BRL_EINVAL, "attn_bwd_dq_logits: null logits");
+    return attn_bwd_dq_impl("attn_bwd_dq_logits", Q, K, V, O, dO, stats, B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo,
+                            window, s_v, dQ, logits, logits_bytes, stream);
+}
+
+static brl_status attn_bwd_dkdv_impl(const char* who, const float* Q, const float* K, const float* V, const float* O,
+                                     const float* dO, const float* stats, int64_t B, int64_t S, int64_t Hq,
+                                     int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
+                                     int64_t window, float s_v, float* dK, float* dV, int64_t ldg, const float* keep,
+                                     size_t keep_bytes, void* stream) {
+    brl_status rc = attn_check(who, B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo, s_v);
     if (rc != BRL_OK) return rc;
+    if (ldg < Hkv * D) return fail(BRL_ESHAPE, "%s: row stride smaller than heads * D", who);
+    if (ldg & 3) return fail(BRL_EINVAL, "%s: row strides must be multiples of 4", who);
     if (B * S == 0) return BRL_OK;
-    if (!Q || !K || !V || !O || !dO || !stats || !dQ) return fail(BRL_EINVAL, "attn_bwd_dq: null tensor");
-    if (!al16p(Q) || !al16p(K) || !al16p(V) || !al16p(O) || !al16p(dO) || !al16p(dQ))
-        return fail(BRL_EINVAL, "attn_bwd_dq: pointers must be 16-byte aligned");
-    if (!aligned4(stats)) return fail(BRL_EINVAL, "attn_bwd_dq: stats must be 4-byte aligned");
-    return check_hip(launch_attn_bwd_dq(Q, K, V, O, dO, stats, B, S, Hq, Hkv, ldq, ldk, ldv, ldo, window, s_v, dQ,
-                                        exp_constants(), static_cast<hipStream_t>(stream)),
-                     "attention dQ");
+    if (!Q || !K || !V || !O || !dO || !stats || !dK || !dV) return fail(BRL_EINVAL, "%s: null tensor", who);
+    if (!al16p(Q) || !al16p(K) || !al16p(V) || !al16p(O) || !al16p(dO) || !al16p(dK) || !al16p(dV))
+        return fail(BRL_EINVAL, "%s: pointers must be 16-byte aligned", who);
+    if (!aligned4(stats)) return fail(BRL_EINVAL, "%s: stats must be 4-byte aligned", who);
+    if (keep && (rc = check_logits(who, keep, keep_bytes, B, S, Hq, window)) != BRL_OK) return rc;
+    return check_hip(launch_attn_bwd_dkdv(Q, K, V, O, dO, stats, B, S, Hq, Hkv, ldq, ldk, ldv, ldo, window, s_v,
+                                          dK, dV, ldg, keep, exp_constants(), static_cast<hipStream_t>(stream)),
+                     "attention dK/dV");
 }
 
 brl_status attn_bwd_dkdv(const float* Q, const float* K, const float* V, const float* O, const float* dO,
                          const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
                          int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dK,
                          float* dV, int64_t ldg, void* stream) {
-    brl_status rc = attn_check("attn_bwd_dkdv", B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo, s_v);
-    if (rc != BRL_OK) return rc;
-    if (ldg < Hkv * D) return fail(BRL_ESHAPE, "attn_bwd_dkdv: row stride smaller than heads * D");
-    if (ldg & 3) return fail(BRL_EINVAL, "attn_bwd_dkdv: row strides must be multiples of 4");
-    if (B * S == 0) return BRL_OK;
-    if (!Q || !K || !V || !O || !dO || !stats || !dK || !dV)
-        return fail(BRL_EINVAL, "attn_bwd_dkdv: null tensor");
-    if (!al16p(Q) || !al16p(K) || !al16p(V) || !al16p(O) || !al16p(dO) || !al16p(dK) || !al16p(dV))
-        return fail(BRL_EINVAL, "attn_bwd_dkdv: pointers must be 16-byte aligned");
-    if (!aligned4(stats)) return fail(BRL_EINVAL, "attn_bwd_dkdv: stats must be 4-byte aligned");
-    return check_hip(launch_attn_bwd_dkdv(Q, K, V, O, dO, stats, B, S, Hq, Hkv, ldq, ldk, ldv, ldo, window, s_v,
-                                          dK, dV, ldg, exp_constants(), static_cast<hipStream_t>(stream)),
-                     "attention dK/dV");
+    return attn_bwd_dkdv_impl("attn_bwd_dkdv", Q, K, V, O, dO, stats, B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo, window,
+                              s_v, dK, dV, ldg, nullptr, 0, stream);
+}
+
+brl_status attn_bwd_dkdv_logits(const float* Q, const float* K, const float* V, const float* O, const float* dO,
+                                const float* stats, const float* logits, size_t logits_bytes, int64_t B, int64_t S,
+                                int64_t Hq, int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv,
+                                int64_t ldo, int64_t window, float s_v, float* dK, float* dV, int64_t ldg,
+                                void* stream) {
+    if (!logits && B * S != 0) return fail(BRL_EINVAL, "attn_bwd_dkdv_logits: null logits");
+    return attn_bwd_dkdv_impl("attn_bwd_dkdv_logits", Q, K, V, O, dO, stats, B, S, Hq, Hkv, D, ldq, ldk, ldv, ldo,
+                              window, s_v, dK, dV, ldg, logits, logits_bytes, stream);
 }
 
 const char* brl_status_string(brl_status s) {

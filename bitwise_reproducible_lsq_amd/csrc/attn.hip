@@ -69,6 +69,7 @@ struct AttnArgs {
     float* O;
     float* stats;          // optional (m_i, l_i) per row (b*S + i)*Hq + h
     float* logits;         // slot_floats floats per workgroup: [tile][64 rows][64 keys]
+    float* keep;           // optional: slot_floats floats per item, kept for the backward
     const int8_t* vcodes;  // q_v tiles [B][Hkv][tiles][kAD * kAK], laid out as sm.u.pv.vq
     int64_t B, S, Hq, Hkv, ldq, ldk, ldv, ldo, window, slot_floats, vtiles;
     float c, s_v;
@@ -237,6 +238,41 @@ __device__ __forceinline__ v16f_a kv_phase1(const float* arow, const float* brow
     return b01 + (b2 + acc);
 }
 
+// half of kv_phase1: the d-blocks at d_first and d_first + 32, left to right
+// within each, then b_first + b_second (so kv_phase1 = pair(0) + pair(64))
+template <bool DQV>
+__device__ __forceinline__ v16f_a kv_phase1_pair(const float* arow, const float* brow, const int8_t* bq, float s_v,
+                                                 int d_first) {
+    v16f_a first, acc;
+#pragma unroll 1
+    for (int blk = 0; blk < 2; ++blk) {
+        const int d0 = d_first + 32 * blk;
+        v16f_a n;
+        vf4 a_cur = *reinterpret_cast<const vf4*>(arow + d0), b_cur = kv_b4<DQV>(brow, bq, s_v, d0), a_nxt, b_nxt;
+        v16f_a p = mfma_prod(a_cur[0], b_cur[0]);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            if (g + 1 < 8) {
+                a_nxt = *reinterpret_cast<const vf4*>(arow + d0 + 4 * (g + 1));
+                b_nxt = kv_b4<DQV>(brow, bq, s_v, d0 + 4 * (g + 1));
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int st = 4 * g + e;
+                if (st + 1 < 32) n = e < 3 ? mfma_prod(a_cur[e + 1], b_cur[e + 1]) : mfma_prod(a_nxt[0], b_nxt[0]);
+                if (st == 0) acc = p;
+                else acc = acc + p;
+                KV_STEP(acc);
+                p = n;
+            }
+            a_cur = a_nxt;
+            b_cur = b_nxt;
+        }
+        if (blk == 0) first = acc;
+    }
+    return first + acc;
+}
+
 // rows 16w .. 16w+15 of one head for wave w (rows past `rows_left` as
 // zeros), row-major into dst: the rows that wave's products read
 __device__ __forceinline__ void attn_load_wave_rows(const float* src, int64_t ld, int64_t row0, int64_t rows_left,
@@ -298,11 +334,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     const unsigned nqb = (unsigned)((a.S + kAQ - 1) / kAQ);
     const unsigned nbh = (unsigned)(a.B * a.Hq), hq = (unsigned)a.Hq;
     const unsigned nitems = nqb * nbh;
-    float* slot = a.logits + (int64_t)blockIdx.x * a.slot_floats;
     const int mt = wave & 1, nt0 = (wave >> 1) * 2;
     const int frow = lane & 31, fchunk = lane >> 5;
 
     for (unsigned item = blockIdx.x; item < nitems; item += gridDim.x) {
+        // the item's logits: in the workgroup's slot, or kept per item
+        float* slot = a.keep ? a.keep + (int64_t)item * a.slot_floats : a.logits + (int64_t)blockIdx.x * a.slot_floats;
         const unsigned qb = nqb - 1 - item / nbh;
         const unsigned bh = item % nbh;
         const int64_t h = bh % hq;
@@ -525,6 +562,14 @@ int64_t attn_fwd_grid(int64_t B, int64_t S, int64_t Hq) {
     return items < kAttnGrid ? items : kAttnGrid;
 }
 
+// logits kept for the backward: one slot per (query block, batch x head)
+// item, in the forward's item order
+size_t attn_keep_bytes(int64_t B, int64_t S, int64_t Hq, int64_t window) {
+    if (B <= 0 || S <= 0) return 0;
+    return (size_t)(B * Hq * ceil_div(S, kAQ)) * (size_t)attn_fwd_max_tiles(S, window) * (size_t)(kAQ * kAK) *
+           sizeof(float);
+}
+
 // workspace: the logit slots, then the q_v codes (both 256-byte aligned)
 static size_t attn_fwd_slots_bytes(int64_t B, int64_t S, int64_t Hq, int64_t window) {
     return (size_t)attn_fwd_grid(B, S, Hq) * (size_t)attn_fwd_max_tiles(S, window) * (size_t)(kAQ * kAK) *
@@ -538,11 +583,11 @@ size_t attn_fwd_ws_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t 
 
 hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
                            int64_t Hkv, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
-                           float* O, int64_t ldo, float* stats, float* logits, const ExpConsts& ek,
+                           float* O, int64_t ldo, float* stats, float* logits, float* keep, const ExpConsts& ek,
                            hipStream_t st) {
     if (B == 0 || S == 0) return hipSuccess;
     AttnArgs a;
-    a.Q = Q; a.K = K; a.V = V; a.O = O; a.stats = stats; a.logits = logits;
+    a.Q = Q; a.K = K; a.V = V; a.O = O; a.stats = stats; a.logits = logits; a.keep = keep;
     a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.window = window;
     a.slot_floats = attn_fwd_max_tiles(S, window) * (kAQ * kAK);
     a.vtiles = ceil_div(S, kAK);
@@ -586,7 +631,8 @@ struct AttnBwdArgs {
     const float* dO;
     const float* stats;
     float* dQ;
-    int64_t S, Hq, Hkv, B, ldq, ldk, ldv, ldo, window;
+    const float* keep;     // optional: the logits the forward kept, keep_slot floats per item
+    int64_t S, Hq, Hkv, B, ldq, ldk, ldv, ldo, window, keep_slot;
     float c, s_v;
     ExpConsts ek;
 };
@@ -626,7 +672,8 @@ struct AttnKvArgs {
     const float* stats;
     float* dK;
     float* dV;
-    int64_t S, Hq, Hkv, B, ldq, ldk, ldv, ldo, ldg, window;
+    const float* keep;     // optional: the logits the forward kept, keep_slot floats per item
+    int64_t S, Hq, Hkv, B, ldq, ldk, ldv, ldo, ldg, window, keep_slot;
     float c, s_v;
     ExpConsts ek;
 };
@@ -762,6 +809,7 @@ __device__ __forceinline__ void kv_row_stats(const float* dO, const float* O, in
     }
 }
 
+template <bool KEEP>
 __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     AttnKvSmem& sm = *reinterpret_cast<AttnKvSmem*>(smem_raw);
@@ -805,17 +853,34 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a)
             kv_load_qg(a.Q, a.ldq, a.dO, a.ldo, base + i0, qrows, h, sm.qr, sm.gr);
             kv_row_stats(a.dO, a.O, a.ldo, a.stats, a.Hq, base + i0, qrows, h, sm.rowm, sm.rowl, sm.rowdelta);
             __syncthreads();
-            // phase 1: logits and dP of the 64 x 64 tile, stored key-major
+            // phase 1: logits and dP of the 64 x 64 tile, stored key-major.
+            // With kept logits, dP only: wave w forms the d-blocks of half
+            // w / 4 for its key slab, the halves go to dt and pt and are added
+            // in the pass below, (b0 + b1) + (b2 + b3) as kv_phase1 adds them.
             {
-                const v16f_a part = p1_dp ? kv_phase1<true>(&sm.gr[lane][0], nullptr, &sm.vq[jcol][0], a.s_v)
-                                          : kv_phase1<false>(&sm.qr[lane][0], &sm.kr[jcol][0], nullptr, a.s_v);
-                float (*T)[kKvRowT] = p1_dp ? sm.dt : sm.pt;
+                v16f_a part;
+                if constexpr (KEEP)
+                    part = kv_phase1_pair<true>(&sm.gr[lane][0], nullptr, &sm.vq[jcol][0], a.s_v, 64 * p1_dp);
+                else
+                    part = p1_dp ? kv_phase1<true>(&sm.gr[lane][0], nullptr, &sm.vq[jcol][0], a.s_v)
+                                 : kv_phase1<false>(&sm.qr[lane][0], &sm.kr[jcol][0], nullptr, a.s_v);
+                float (*T)[kKvRowT] = (p1_dp != 0) == KEEP ? sm.pt : sm.dt;
 #pragma unroll
                 for (int beta = 0; beta < 4; ++beta)
                     *reinterpret_cast<vf4*>(&T[jcol][16 * beta + 4 * (lane >> 4)]) =
                         vf4{part[4 * beta], part[4 * beta + 1], part[4 * beta + 2], part[4 * beta + 3]};
             }
             __syncthreads();
+            // the kept logits of this (query block, head) item's tile: items
+            // in the forward's order, tiles from the block's first key tile
+            const float* kept = nullptr;
+            if constexpr (KEEP) {
+                int64_t kq0, kq1;
+                attn_tile_range(a.S, a.window, qt, &kq0, &kq1);
+                const int64_t nqb = (a.S + kAQ - 1) / kAQ;
+                const int64_t item = (nqb - 1 - qt) * (a.B * a.Hq) + b * a.Hq + h;
+                kept = a.keep + item * a.keep_slot + ((int64_t)kt - kq0) * (kAQ * kAK);
+            }
             // P and dS of the tile (32-bit positions: S < 2^31)
 #pragma unroll
             for (int e = 0; e < (kAQ * kAK) / kKvThreads; ++e) {
@@ -824,9 +889,11 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a)
                 const int i = (int)i0 + il, j = (int)j0 + jl;
                 float P = 0.0f, dS = 0.0f;
                 if (i < s32 && j <= i && (win == 0 || j > i - win)) {
-                    const float p = own_exp(f_sub(f_mul(sm.pt[jl][il], a.c), sm.rowm[il]), a.ek);
+                    const float sl = KEEP ? kept[il * kAK + jl] : f_mul(sm.pt[jl][il], a.c);
+                    const float dP = KEEP ? f_add(sm.dt[jl][il], sm.pt[jl][il]) : sm.dt[jl][il];
+                    const float p = own_exp(f_sub(sl, sm.rowm[il]), a.ek);
                     P = f_div(p, sm.rowl[il]);
-                    dS = f_mul(P, f_sub(sm.dt[jl][il], sm.rowdelta[il]));
+                    dS = f_mul(P, f_sub(dP, sm.rowdelta[il]));
                 }
                 sm.pt[jl][il] = P;
                 sm.dt[jl][il] = dS;
@@ -852,23 +919,31 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_kernel(AttnKvArgs a)
 hipError_t launch_attn_bwd_dkdv(const float* Q, const float* K, const float* V, const float* O, const float* dO,
                                 const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t ldq,
                                 int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dK,
-                                float* dV, int64_t ldg, const ExpConsts& ek, hipStream_t st) {
+                                float* dV, int64_t ldg, const float* keep, const ExpConsts& ek, hipStream_t st) {
     if (B == 0 || S == 0) return hipSuccess;
     AttnKvArgs a;
     a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.stats = stats; a.dK = dK; a.dV = dV;
+    a.keep = keep;
+    a.keep_slot = attn_fwd_max_tiles(S, window) * (kAQ * kAK);
     a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.B = B;
     a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.ldg = ldg; a.window = window;
     a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
     a.s_v = s_v;
     a.ek = ek;
     // the limit is set on every call: it is per device, and the call is cheap
-    if (const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnKvSmem));
+    const void* fn = keep ? reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<true>)
+                          : reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<false>);
+    if (const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnKvSmem));
         e != hipSuccess)
         return e;
     const int64_t blocks = B * Hkv * ceil_div(S, kAK);
     if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)blocks), dim3(kKvThreads), sizeof(AttnKvSmem), st, a);
+    if (keep)
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>, dim3((unsigned)blocks), dim3(kKvThreads), sizeof(AttnKvSmem),
+                           st, a);
+    else
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<false>, dim3((unsigned)blocks), dim3(kKvThreads), sizeof(AttnKvSmem),
+                           st, a);
     return hipGetLastError();
 }
 
@@ -888,6 +963,7 @@ struct AttnDqSmem {
 };
 static_assert(sizeof(AttnDqSmem) <= 163840, "LDS of one CU");
 
+template <bool KEEP>
 __global__ __launch_bounds__(kKvThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     AttnDqSmem& sm = *reinterpret_cast<AttnDqSmem*>(smem_raw);
@@ -929,15 +1005,25 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
         __syncthreads();
         kv_load_kv(a.K, a.ldk, a.V, a.ldv, base + j0, krows, hk, qz, sm.kr, sm.vq);
         __syncthreads();
-        // phase 1: logits and dP of the 64 x 64 tile, stored row-major
+        // phase 1: logits and dP of the 64 x 64 tile, stored row-major.
+        // With kept logits, dP only: wave w forms the d-blocks of half w / 4
+        // for its key slab, the halves go to dt and st and are added in the
+        // dS pass, (b0 + b1) + (b2 + b3) as kv_phase1 adds them.
         {
-            const v16f_a part = p1_dp ? kv_phase1<true>(&sm.gr[lane][0], nullptr, &sm.vq[jcol][0], a.s_v)
-                                      : kv_phase1<false>(&sm.qr[lane][0], &sm.kr[jcol][0], nullptr, a.s_v);
-            float (*T)[kKvRowT] = p1_dp ? sm.dt : sm.st;
+            v16f_a part;
+            if constexpr (KEEP)
+                part = kv_phase1_pair<true>(&sm.gr[lane][0], nullptr, &sm.vq[jcol][0], a.s_v, 64 * p1_dp);
+            else
+                part = p1_dp ? kv_phase1<true>(&sm.gr[lane][0], nullptr, &sm.vq[jcol][0], a.s_v)
+                             : kv_phase1<false>(&sm.qr[lane][0], &sm.kr[jcol][0], nullptr, a.s_v);
+            float (*T)[kKvRowT] = (p1_dp != 0) == KEEP ? sm.st : sm.dt;
 #pragma unroll
             for (int r = 0; r < 16; ++r) T[16 * (r >> 2) + 4 * (lane >> 4) + (r & 3)][jcol] = part[r];
         }
         __syncthreads();
+        // the kept logits of this item's tile (this grid's order is the
+        // forward's item order; tiles from the block's first key tile)
+        const float* kept = KEEP ? a.keep + (int64_t)blockIdx.x * a.keep_slot + (kt - kt0) * (kAQ * kAK) : nullptr;
         // dS of the tile (32-bit positions: S < 2^31)
 #pragma unroll
         for (int e = 0; e < (kAQ * kAK) / kKvThreads; ++e) {
@@ -946,8 +1032,10 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
             const int i = (int)q0 + il, j = (int)j0 + jl;
             float dS = 0.0f;
             if (i < s32 && j <= i && (win == 0 || j > i - win)) {
-                const float p = own_exp(f_sub(f_mul(sm.st[il][jl], a.c), sm.rowm[il]), a.ek);
-                dS = f_mul(f_div(p, sm.rowl[il]), f_sub(sm.dt[il][jl], sm.rowdelta[il]));
+                const float sl = KEEP ? kept[il * kAK + jl] : f_mul(sm.st[il][jl], a.c);
+                const float dP = KEEP ? f_add(sm.dt[il][jl], sm.st[il][jl]) : sm.dt[il][jl];
+                const float p = own_exp(f_sub(sl, sm.rowm[il]), a.ek);
+                dS = f_mul(f_div(p, sm.rowl[il]), f_sub(dP, sm.rowdelta[il]));
             }
             sm.dt[il][jl] = dS;
         }
@@ -967,23 +1055,31 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dq_kernel(AttnBwdArgs a) 
 hipError_t launch_attn_bwd_dq(const float* Q, const float* K, const float* V, const float* O, const float* dO,
                               const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t ldq,
                               int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dQ,
-                              const ExpConsts& ek, hipStream_t st) {
+                              const float* keep, const ExpConsts& ek, hipStream_t st) {
     if (B == 0 || S == 0) return hipSuccess;
     AttnBwdArgs a;
     a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.stats = stats; a.dQ = dQ;
+    a.keep = keep;
+    a.keep_slot = attn_fwd_max_tiles(S, window) * (kAQ * kAK);
     a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.B = B;
     a.ldq = ldq; a.ldk = ldk; a.ldv = ldv; a.ldo = ldo; a.window = window;
     a.c = (float)(1.0 / (double)(float)sqrt((double)kAD));
     a.s_v = s_v;
     a.ek = ek;
     // the limit is set on every call: it is per device, and the call is cheap
-    if (const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_dq_kernel),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnDqSmem));
+    const void* fn = keep ? reinterpret_cast<const void*>(&attn_bwd_dq_kernel<true>)
+                          : reinterpret_cast<const void*>(&attn_bwd_dq_kernel<false>);
+    if (const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(AttnDqSmem));
         e != hipSuccess)
         return e;
     const int64_t blocks = B * Hq * ceil_div(S, kAQ);
     if (blocks > 0xffffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)blocks), dim3(kKvThreads), sizeof(AttnDqSmem), st, a);
+    if (keep)
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<true>, dim3((unsigned)blocks), dim3(kKvThreads), sizeof(AttnDqSmem), st,
+                           a);
+    else
+        hipLaunchKernelGGL(attn_bwd_dq_kernel<false>, dim3((unsigned)blocks), dim3(kKvThreads), sizeof(AttnDqSmem), st,
+                           a);
     return hipGetLastError();
 }
 

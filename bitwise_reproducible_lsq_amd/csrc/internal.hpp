@@ -174,17 +174,22 @@ brl_status report_hip(hipError_t e, const char* what);
 // workspace of attn_fwd: one slot of stored logits per workgroup of its grid,
 // then the q_v codes of every key tile
 size_t attn_fwd_ws_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t window);
+// logits the forward can keep for the backward: one slot per (query block,
+// batch x query head) item, in the forward's item order
+size_t attn_keep_bytes(int64_t B, int64_t S, int64_t Hq, int64_t window);
+// keep (nullable): the forward writes every item's logits there instead of
+// its per-workgroup slots; the backward reads them instead of recomputing
 hipError_t launch_attn_fwd(const float* Q, const float* K, const float* V, int64_t B, int64_t S, int64_t Hq,
                            int64_t Hkv, int64_t ldq, int64_t ldk, int64_t ldv, int64_t window, float s_v,
-                           float* O, int64_t ldo, float* stats, float* logits, const ExpConsts& ek,
+                           float* O, int64_t ldo, float* stats, float* logits, float* keep, const ExpConsts& ek,
                            hipStream_t st);
 hipError_t launch_attn_bwd_dq(const float* Q, const float* K, const float* V, const float* O, const float* dO,
                               const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t ldq,
                               int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dQ,
-                              const ExpConsts& ek, hipStream_t st);
+                              const float* keep, const ExpConsts& ek, hipStream_t st);
 hipError_t launch_attn_bwd_dkdv(const float* Q, const float* K, const float* V, const float* O, const float* dO,
                                 const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t ldq,
                                 int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dK,
-                                float* dV, int64_t ldg, const ExpConsts& ek, hipStream_t st);
+                                float* dV, int64_t ldg, const float* keep, const ExpConsts& ek, hipStream_t st);
 
 }  // namespace brl

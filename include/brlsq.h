@@ -319,6 +319,31 @@ BRL_API brl_status attn_fwd(const float* Q, const float* K, const float* V, int6
 BRL_API size_t attn_fwd_workspace_bytes(int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t window);
 
 /*
+ * attn_fwd that also keeps its exact logits s_ij (as defined above) for the
+ * backward, which then need not form them again (attn_bwd_dq_logits,
+ * attn_bwd_dkdv_logits).  The pages keep the logits in high precision
+ * (onedev.kr summary, "Use", attention paragraph); keeping them in HBM trades
+ * memory for one of the backward's products.  logits: device, 256-byte
+ * aligned, at least attn_logits_bytes(B, S, Hq, window) bytes, caller-owned;
+ * it receives one slot per (query block qb, batch b, query head h), slot
+ * index (ceil(S/64) - 1 - qb) * (B*Hq) + b*Hq + h, each slot the block's key
+ * tiles from its first (64 x 64 binary32, row-major by query), entries off
+ * the row's keys unspecified.  BRL_ESHAPE if too small.  O and stats are the
+ * same bits as attn_fwd's; other arguments and requirements as attn_fwd.
+ * Asynchronous on `stream`.
+ */
+BRL_API brl_status attn_fwd_keep_logits(const float* Q, const float* K, const float* V, int64_t B, int64_t S,
+                                        int64_t Hq, int64_t Hkv, int64_t D, int64_t ldq, int64_t ldk, int64_t ldv,
+                                        int64_t window, float s_v, float* O, int64_t ldo, float* stats,
+                                        float* logits, size_t logits_bytes, void* ws, size_t ws_bytes,
+                                        void* stream);
+
+/* Bytes of the logits attn_fwd_keep_logits keeps for these sizes (0 for sizes
+ * it rejects): ceil(S/64) * B * Hq slots of (longest key walk of a query block,
+ * in 64-key tiles) * 16 KB. */
+BRL_API size_t attn_logits_bytes(int64_t B, int64_t S, int64_t Hq, int64_t window);
+
+/*
  * dQ of attn_fwd with 64-bit fixed-point accumulation (onedev.kr summary,
  * "Use", attention paragraph: the attention backward accumulates the query
  * gradient in 64-bit fixed point).  This library's reading, with s, m, p, l,
@@ -340,6 +365,15 @@ BRL_API brl_status attn_bwd_dq(const float* Q, const float* K, const float* V, c
                                const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
                                int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v,
                                float* dQ, void* stream);
+
+/* attn_bwd_dq reading the logits that attn_fwd_keep_logits kept for the same
+ * Q, K, V, B, S, Hq, window (logits, logits_bytes as there) instead of forming
+ * them again; the same bits as attn_bwd_dq. */
+BRL_API brl_status attn_bwd_dq_logits(const float* Q, const float* K, const float* V, const float* O,
+                                      const float* dO, const float* stats, const float* logits, size_t logits_bytes,
+                                      int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t ldq,
+                                      int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v, float* dQ,
+                                      void* stream);
 
 /*
  * dK and dV of attn_fwd (onedev.kr summary, "Use", attention paragraph: the
@@ -365,6 +399,15 @@ BRL_API brl_status attn_bwd_dkdv(const float* Q, const float* K, const float* V,
                                  const float* stats, int64_t B, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
                                  int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int64_t window, float s_v,
                                  float* dK, float* dV, int64_t ldg, void* stream);
+
+/* attn_bwd_dkdv reading the logits that attn_fwd_keep_logits kept (as
+ * attn_bwd_dq_logits); the same bits as attn_bwd_dkdv. */
+BRL_API brl_status attn_bwd_dkdv_logits(const float* Q, const float* K, const float* V, const float* O,
+                                        const float* dO, const float* stats, const float* logits,
+                                        size_t logits_bytes, int64_t B, int64_t S, int64_t Hq, int64_t Hkv,
+                                        int64_t D, int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
+                                        int64_t window, float s_v, float* dK, float* dV, int64_t ldg,
+                                        void* stream);
 
 /*
  * Topology-invariant data stream (onedev.kr summary, "What differs": one

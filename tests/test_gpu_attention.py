@@ -417,3 +417,79 @@ def test_attention_workgroups_walk_several_items():
     want = oracle.attn_bwd_dq(Q, K, V, Oh, dO, window, s_v, rows=rows)
     got = dQ.cpu().numpy().reshape(B * S * Hq, D)[rows]
     assert_bitwise(got, np.asarray(want).reshape(got.shape), "dQ rows (several items per workgroup)")
+
+
+KEEP_CASES = [
+    # B, S, Hq, Hkv, window, s_v
+    (1, 1, 1, 1, 0, 0.05),
+    (2, 150, 4, 2, 0, 0.05),
+    (1, 200, 4, 2, 64, 0.0371),
+    (1, 333, 16, 4, 130, 0.05),
+    (1, 190, 8, 2, 500, 0.05),        # window longer than the sequence
+    (2, 129, 8, 1, 70, 0.05),
+    (1, 100, 4, 4, 1, 0.05),
+]
+
+
+def _oracle_logit(Q, K, b, i, h, j, hk):
+    """s_ij = CanonSum_d(q_id * k_jd) * c with the oracle's CanonSum and
+    binary32 products and multiply (inputs are normal numbers)."""
+    prods = (Q[b, i, h].astype(np.float32) * K[b, j, hk].astype(np.float32)).astype(np.float32)
+    c = np.float32(1.0 / float(np.float32(np.sqrt(np.float64(D)))))
+    return oracle.mul(oracle.canon_sum(prods), c)
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,window,s_v", KEEP_CASES)
+def test_attention_kept_logits(B, S, Hq, Hkv, window, s_v):
+    """The forward that keeps its logits gives O and (m, l) bit for bit as
+    the plain forward and the oracle; the kept logits are the oracle's s_ij on
+    sampled allowed positions; dQ, dK and dV read from them equal the
+    oracle's bit for bit."""
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=11 * S + Hq + window, scale=0.3)
+    V.reshape(-1)[::977] = 7.5
+    dO = (np.random.default_rng(S + window + 3).standard_normal((B, S, Hq, D)) * 1e-2).astype(np.float32)
+    q, k, v = (torch.from_numpy(t).cuda() for t in (Q, K, V))
+    g = torch.from_numpy(dO).cuda()
+    st0 = torch.empty((B, S, Hq, 2), dtype=torch.float32, device="cuda")
+    st1 = torch.empty_like(st0)
+    O0 = brl.attn_fwd(q, k, v, window, s_v, stats=st0)
+    logits = brl.attn_logits_buffer(B, S, Hq, window)
+    logits.fill_(float("nan"))
+    O1 = brl.attn_fwd(q, k, v, window, s_v, stats=st1, logits=logits)
+    dQ = brl.attn_bwd_dq(q, k, v, O1, g, st1, window, s_v, logits=logits)
+    dK, dV = brl.attn_bwd_dkdv(q, k, v, O1, g, st1, window, s_v, logits=logits)
+    torch.cuda.synchronize()
+    assert_bitwise(O1, O0, "O (kept logits) vs O")
+    assert_bitwise(st1, st0, "stats (kept logits) vs stats")
+    Oh = O1.cpu().numpy()
+    assert_bitwise(Oh, oracle.attn_fwd(Q, K, V, window, s_v), "O")
+    assert_bitwise(dQ, oracle.attn_bwd_dq(Q, K, V, Oh, dO, window, s_v), f"dQ from kept logits (S={S} w={window})")
+    wk, wv = oracle.attn_bwd_dkdv(Q, K, V, Oh, dO, window, s_v)
+    assert_bitwise(dK, wk, f"dK from kept logits (S={S} w={window})")
+    assert_bitwise(dV, wv, f"dV from kept logits (S={S} w={window})")
+    # the kept slots: slot (nqb - 1 - qb) * B*Hq + b*Hq + h, tiles from the block's first key tile
+    lg = logits.cpu().numpy()
+    nqb = (S + 63) // 64
+    tiles = max(((min(qb * 64 + 63, S - 1)) // 64 - (max(0, qb * 64 - window + 1) if window > 0 else 0) // 64 + 1)
+                for qb in range(nqb))
+    assert lg.size * 4 == brl.attn_logits_bytes(B, S, Hq, window) == nqb * B * Hq * tiles * 64 * 64 * 4
+    rng = np.random.default_rng(S)
+    for _ in range(40):
+        b, h, i = int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(S))
+        lo = max(0, i - window + 1) if window > 0 else 0
+        j = int(rng.integers(lo, i + 1))
+        qb = i // 64
+        kt0 = (max(0, qb * 64 - window + 1) if window > 0 else 0) // 64
+        slot = (nqb - 1 - qb) * B * Hq + b * Hq + h
+        got = lg[(slot * tiles + j // 64 - kt0) * 4096 + (i % 64) * 64 + j % 64]
+        want = _oracle_logit(Q, K, b, i, h, j, h // (Hq // Hkv))
+        assert np.float32(got).view(np.uint32) == np.float32(want).view(np.uint32), (b, h, i, j, got, want)
+
+
+def test_attention_kept_logits_rejects_a_short_buffer():
+    B, S, Hq, Hkv = 1, 130, 4, 2
+    Q, K, V = _inputs(B, S, Hq, Hkv, seed=1)
+    q, k, v = (torch.from_numpy(t).cuda() for t in (Q, K, V))
+    short = torch.empty(brl.attn_logits_bytes(B, S, Hq, 64) // 4 - 64, dtype=torch.float32, device="cuda")
+    with pytest.raises(brl.BrlError):
+        brl.attn_fwd(q, k, v, 64, 0.05, logits=short)
