@@ -243,3 +243,36 @@ def test_attention_dkdv_full_size(name):
     wk, wv = oracle.attn_bwd_dkdv(Q, K, V, Oh, dO, case.window, case.s_v, rows=rows)
     assert_bitwise(dKh[rows], wk, f"dK rows ({name})")
     assert_bitwise(dVh[rows], wv, f"dV rows ({name})")
+
+
+@pytest.mark.parametrize("name", ["attn_window", "attn_causal"])
+def test_attention_kept_logits_full_size(name):
+    """The training path at one Open-1B layer: the forward keeping its
+    logits and dQ, dK, dV read from them equal the path that forms them
+    again, every element, and the oracle on sampled rows."""
+    case = synth.ATTENTION_CASES[name]
+    Q, K, V = synth.attention_inputs(case)
+    dO = synth.normal(case.seed, "dY", Q.shape, 1e-3)
+    q, k, v, g = _cuda(Q), _cuda(K), _cuda(V), _cuda(dO)
+    st0 = torch.empty((case.B, case.S, case.Hq, 2), dtype=torch.float32, device=DEV)
+    st1 = torch.empty_like(st0)
+    O0 = brl.attn_fwd(q, k, v, case.window, case.s_v, stats=st0)
+    dQ0 = brl.attn_bwd_dq(q, k, v, O0, g, st0, case.window, case.s_v)
+    dK0, dV0 = brl.attn_bwd_dkdv(q, k, v, O0, g, st0, case.window, case.s_v)
+    L = brl.attn_logits_buffer(case.B, case.S, case.Hq, case.window, DEV)
+    O1 = brl.attn_fwd(q, k, v, case.window, case.s_v, stats=st1, logits=L)
+    dQ1 = brl.attn_bwd_dq(q, k, v, O1, g, st1, case.window, case.s_v, logits=L)
+    dK1, dV1 = brl.attn_bwd_dkdv(q, k, v, O1, g, st1, case.window, case.s_v, logits=L)
+    torch.cuda.synchronize()
+    del L
+    for got, want, what in ((O1, O0, "O"), (st1, st0, "stats"), (dQ1, dQ0, "dQ"), (dK1, dK0, "dK"), (dV1, dV0, "dV")):
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32)), f"{what} (kept logits, {name})"
+    Oh = O1.cpu().numpy()
+    rows = np.array([(b * case.S + i) * case.Hq + h for b, h, i in [(0, 0, 0), (1, 5, 600), (3, 15, case.S - 1)]],
+                    np.int64)
+    assert_bitwise(dQ1.cpu().numpy().reshape(-1, 128)[rows],
+                   oracle.attn_bwd_dq(Q, K, V, Oh, dO, case.window, case.s_v, rows=rows), f"dQ rows ({name})")
+    krows = np.array([(b * case.S + j) * case.Hkv + hk for b, hk, j in [(0, 0, 4095), (3, 3, 4032)]], np.int64)
+    wk, wv = oracle.attn_bwd_dkdv(Q, K, V, Oh, dO, case.window, case.s_v, rows=krows)
+    assert_bitwise(dK1.cpu().numpy().reshape(-1, 128)[krows], wk, f"dK rows ({name})")
+    assert_bitwise(dV1.cpu().numpy().reshape(-1, 128)[krows], wv, f"dV rows ({name})")
