@@ -40,7 +40,7 @@ class Tuning(C.Structure):
     """Launch shapes of one call (brl_tuning): they never change results.
     Zero fields select the defaults."""
     _fields_ = [("bwd_chunk_log2", C.c_int32), ("reduce_wg_blocks", C.c_int32), ("stream_vec", C.c_int32),
-                ("bwd_engine", C.c_int32)]
+                ("bwd_engine", C.c_int32), ("fwd_prep", C.c_int32)]
 
 
 class ReduceStateC(C.Structure):

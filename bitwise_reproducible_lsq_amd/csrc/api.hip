@@ -14,7 +14,7 @@ namespace brl {
 
 // ---- launch shapes of one call ---------------------------------------------------
 bool resolve_tuning(const brl_tuning* t, Tuning* out) {
-    Tuning r{0, 256, 1, 2};
+    Tuning r{0, 256, 1, 2, 1};
     if (t) {
         if (t->bwd_chunk_log2 < 0 || t->bwd_chunk_log2 > 7) return false;
         r.chunk_log2 = t->bwd_chunk_log2;
@@ -29,6 +29,10 @@ bool resolve_tuning(const brl_tuning* t, Tuning* out) {
         if (t->bwd_engine != 0) {
             if (t->bwd_engine != 1 && t->bwd_engine != 2) return false;
             r.engine = t->bwd_engine;
+        }
+        if (t->fwd_prep != 0) {
+            if (t->fwd_prep != 1 && t->fwd_prep != 2) return false;
+            r.fwd_prep = t->fwd_prep;
         }
     }
     *out = r;
@@ -102,6 +106,7 @@ struct Carver {
 struct FwdLayout {
     int64_t Kp, Mp, Nvp;
     Scalars* scal;
+    uint64_t* sync;
     float* partials;
     int8_t* qx;
     int8_t* qw;
@@ -116,6 +121,7 @@ static FwdLayout fwd_layout(void* ws, int64_t M, int64_t K, int64_t N, int epilo
     L.Nvp = round_up(nv, kRowPad);
     Carver c(ws);
     L.scal = c.take<Scalars>(1);
+    L.sync = c.take<uint64_t>((size_t)kPrepSyncWords);
     L.partials = c.take<float>((size_t)canon_partials(N * K));
     L.qx = c.take<int8_t>((size_t)(L.Mp * L.Kp));
     L.qw = c.take<int8_t>((size_t)(L.Nvp * L.Kp));
@@ -244,12 +250,24 @@ brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, 
     fin.s_x = s_x;
     fin.scal = L.scal;
     fin.s_w_out = s_w_out;
-    brl_status s = check_hip(launch_canon(kMapAbs, W, N * K, L.partials, fin, tn.wg_blocks, st), "weight step");
-    if (s || M == 0) return s;
-    s = check_hip(launch_quantize(W, N, K, &L.scal->s_w, 0.0f, L.qw, L.Nvp, L.Kp, swiglu_half, st), "quantize W");
-    if (s) return s;
-    s = check_hip(launch_quantize(X, M, K, nullptr, s_x, L.qx, L.Mp, L.Kp, 0, st), "quantize X");
-    if (s) return s;
+    brl_status s = BRL_OK;
+    if (M > 0 && tn.fwd_prep == 1 && fwd_prep_fits(N * K)) {
+        // weight step, W codes and X codes in one launch
+        PrepArgs p{};
+        p.X = X; p.W = W; p.M = M; p.K = K; p.N = N; p.s_x = s_x;
+        p.qx = L.qx; p.qw = L.qw; p.Mp = L.Mp; p.Kp = L.Kp; p.Nvp = L.Nvp; p.swiglu_half = swiglu_half;
+        p.sync = L.sync; p.fin = fin;
+        s = check_hip(launch_fwd_prep(p, st), "forward preparation");
+        if (s) return s;
+    } else {
+        s = check_hip(launch_canon(kMapAbs, W, N * K, L.partials, fin, tn.wg_blocks, st), "weight step");
+        if (s || M == 0) return s;
+        s = check_hip(launch_quantize(W, N, K, &L.scal->s_w, 0.0f, L.qw, L.Nvp, L.Kp, swiglu_half, st),
+                      "quantize W");
+        if (s) return s;
+        s = check_hip(launch_quantize(X, M, K, nullptr, s_x, L.qx, L.Mp, L.Kp, 0, st), "quantize X");
+        if (s) return s;
+    }
     GemmArgs g{};
     g.qx = L.qx; g.qw = L.qw; g.M = M; g.N = N; g.Kp = L.Kp; g.Mp = L.Mp; g.Nvp = L.Nvp;
     g.scal = L.scal; g.addend = addend; g.Y = Y; g.Ypre = Ypre; g.epilogue = epilogue;

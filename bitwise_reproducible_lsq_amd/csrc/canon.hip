@@ -24,22 +24,6 @@ __device__ __forceinline__ float canon_map(float v) {
     else return f_mul(v, v);
 }
 
-__device__ void canon_finish(float S, const CanonFinishArgs& f) {
-    if (f.mode == kFinishScale) {
-        const float s_w = weight_step(S, f.count_f);
-        f.scal->s_w = s_w;
-        f.scal->s_y = f_mul(f.s_x, s_w);
-        if (f.s_w_out) *f.s_w_out = s_w;
-    } else {
-        float nu = f_sqrt(S);
-        int clip = nu > f.max_norm;
-        f.scal->nu = nu;
-        f.scal->clip = clip;
-        f.scal->kappa = clip ? f_div(f.max_norm, f_add(nu, f.eps)) : 1.0f;
-        if (f.nu_out) *f.nu_out = nu;
-    }
-}
-
 // Pass 1: thread t of workgroup w sums block j = w*WGB + t.  The workgroup's
 // WGB*32 elements are loaded coalesced (16-byte vectors when aligned) and
 // transposed through LDS rows of 33 floats, so that each thread then walks
@@ -123,21 +107,8 @@ template <int RUN>
 __global__ __launch_bounds__(kTailThreads) void canon_tail_kernel(const float* __restrict__ in, int64_t Q,
                                                                   CanonFinishArgs fin) {
     __shared__ float lds[kTailThreads];
-    const int t = threadIdx.x;
-    const int64_t first = (int64_t)t * RUN;
-    const int64_t left = Q - first;
-    const int cnt = left <= 0 ? 0 : (left < RUN ? (int)left : RUN);
-    float v[RUN];
-#pragma unroll
-    for (int i = 0; i < RUN; ++i) v[i] = i < cnt ? in[first + i] : 0.0f;
-#pragma unroll
-    for (int w = 1; w < RUN; w *= 2)
-#pragma unroll
-        for (int i = 0; i + w < RUN; i += 2 * w)
-            if (i + w < cnt) v[i] = f_add(v[i], v[i + w]);
-    const int runs = (int)((Q + RUN - 1) / RUN);
-    const float r = wg_pair_tree(v[0], runs, lds);
-    if (t == 0) canon_finish(r, fin);
+    const float r = canon_runs_tree<RUN>([&](int64_t j) { return in[j]; }, Q, lds);
+    if (threadIdx.x == 0) canon_finish(r, fin);
 }
 
 static hipError_t launch_canon_tail(const float* in, int64_t Q, const CanonFinishArgs& fin, hipStream_t st) {

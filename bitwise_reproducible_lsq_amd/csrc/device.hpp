@@ -184,4 +184,28 @@ __device__ __forceinline__ float wg_pair_tree(float v, int count, float* lds) {
     return r;
 }
 
+// CanonSum root of Q leaves by one workgroup of blockDim.x threads
+// (Q <= RUN * blockDim.x): thread t first reduces the aligned run [t*RUN,
+// (t+1)*RUN) in registers, level by level (a complete subtree of the
+// canonical tree, or for the short last run the canonical tree of its own
+// leaves, which is the same thing), then the workgroup tree combines the run
+// roots.  Every thread must call it; the root is returned in thread 0.
+// leaf(j) returns leaf j.
+template <int RUN, class Leaf>
+__device__ __forceinline__ float canon_runs_tree(Leaf leaf, int64_t Q, float* lds) {
+    const int64_t first = (int64_t)threadIdx.x * RUN;
+    const int64_t left = Q - first;
+    const int cnt = left <= 0 ? 0 : (left < RUN ? (int)left : RUN);
+    float v[RUN];
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) v[i] = i < cnt ? leaf(first + i) : 0.0f;
+#pragma unroll
+    for (int w = 1; w < RUN; w *= 2)
+#pragma unroll
+        for (int i = 0; i + w < RUN; i += 2 * w)
+            if (i + w < cnt) v[i] = f_add(v[i], v[i + w]);
+    const int runs = (int)((Q + RUN - 1) / RUN);
+    return wg_pair_tree(v[0], runs, lds);
+}
+
 }  // namespace brl

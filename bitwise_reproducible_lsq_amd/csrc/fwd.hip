@@ -126,6 +126,214 @@ hipError_t launch_quantize(const float* v, int64_t rows, int64_t cols, const flo
     return hipGetLastError();
 }
 
+// ---- the forward's preparation in one launch ----------------------------------------
+// The weight step, the W codes and the X codes of one forward call in one grid
+// of 256-thread workgroups, in four consecutive ranges of workgroup ids:
+//   [0, P)         CanonSum of |W|: workgroup b reduces the aligned run of 256
+//                  32-blocks that starts at block 256 b to one subtree root
+//                  and publishes it;
+//   P              the tail: waits for the P roots, reduces them in the
+//                  canonical order (canon_runs_tree), forms s_w and s_y and
+//                  publishes s_w;
+//   [P+1, P+1+XB)  the X quantiser (its step is the caller's s_x);
+//   [P+1+XB, ...)  the W quantiser (at most 1024 workgroups), which first
+//                  waits for s_w.
+// Each published value travels with its own ready tag in one 64-bit word
+// (tag in the high half, the float's bits in the low half), written and read
+// as a relaxed device-scope atomic: the reader needs that one word and
+// nothing else, so no fence is needed.  (A device-scope release or acquire
+// writes back or invalidates a whole L2; one per workgroup made this launch
+// slower than the separate launches it replaces.)  fwd_prep_clear_kernel
+// zeroes the words first.
+//
+// Only the tail and the W range wait, and only on work of lower ranges whose
+// workgroups never wait: once running, they finish.  Waiters number at most
+// 1025, fewer workgroups than the device holds at once (this kernel fits 8 per
+// CU: 2048 on 256 CUs), so the workgroups they wait for always find room to run even when
+// every waiter is resident; each wait is bounded all the same
+// (kPrepSpinLimit polls, then the error word records it), so every wave
+// exits.  Measured on the MI355X (forward call, QKV / SwiGLU gate+up / down
+// projection at 16384 tokens): 150 / 560 / 261 us against 158 / 575 / 276 us
+// for the four separate launches; the W range before the X range, or at most
+// 512 W workgroups, measured 1-2% slower.
+constexpr int64_t kPrepMaxWgW = 1024;
+constexpr uint32_t kPrepSpinLimit = 1u << 17;   // 0.1 to 0.3 s of polling
+constexpr uint64_t kPrepReady = 1ull << 32;
+
+__device__ __forceinline__ uint64_t prep_word(float v) {
+    return kPrepReady | (uint64_t)__builtin_bit_cast(uint32_t, v);
+}
+
+// The float published in *w, once its tag is up (bounded wait: on giving up,
+// records it in *err and returns whatever the word holds).
+__device__ __forceinline__ float prep_wait(const uint64_t* w, uint64_t* err) {
+    uint64_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t polls = 0;
+    while (v < kPrepReady) {
+        if (++polls == kPrepSpinLimit) {
+            __hip_atomic_store(err, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(16);
+        v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return __builtin_bit_cast(float, (uint32_t)v);
+}
+
+// |w| of the 32 weights of one block, held 4 per lane by 8 consecutive lanes
+// (lane 8j + k holds weights 4k .. 4k+3 of block j), summed left to right from
+// the first term: the running sum moves one lane up per step (row_shr:1 stays
+// inside a group of 8 lanes, which never straddles a 16-lane DPP row).  The
+// block sum ends in lane 8j + 7.
+__device__ __forceinline__ float prep_block_chain(vf4 x, int lane) {
+    const int k = lane & 7;
+    float c = 0.0f;
+#pragma unroll
+    for (int step = 0; step < 8; ++step) {
+        const float prev = __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, c), 0x111, 0xF, 0xF, false));
+        if (k == step) {
+            float v = step == 0 ? __builtin_fabsf(x.x) : f_add(prev, __builtin_fabsf(x.x));
+            v = f_add(v, __builtin_fabsf(x.y));
+            v = f_add(v, __builtin_fabsf(x.z));
+            c = f_add(v, __builtin_fabsf(x.w));
+        }
+    }
+    return c;
+}
+
+// First range, workgroup b: the subtree root of 32-blocks [256 b, 256 b + 256)
+// of |W| (flat, row-major), published in root word b.
+__device__ void prep_abs_run(const PrepArgs& a, int64_t b, float* lds, float* blk) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int64_t nW = a.N * a.K;
+    const int64_t base = b * kPrepRunBlocks * kBlock;
+    const float* src = a.W + base;
+    int count;
+    float v;
+    if (base + kPrepRunBlocks * kBlock <= nW && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+        // wave w: weights [2048 w, 2048 w + 2048) of the run as 8 coalesced
+        // 1 KiB loads; load i, lane l holds block 64 w + 8 i + l / 8
+        const vf4* s4 = reinterpret_cast<const vf4*>(src) + w * 512 + lane;
+        vf4 x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = s4[64 * i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float c = prep_block_chain(x[i], lane);
+            if ((lane & 7) == 7) blk[w * 64 + i * 8 + (lane >> 3)] = c;
+        }
+        __syncthreads();
+        v = blk[t];
+        count = (int)kPrepRunBlocks;
+    } else {
+        // the short last run (or an unaligned W): thread t walks its own block
+        const int64_t e0 = base + (int64_t)t * kBlock;
+        const int64_t left = nW - e0;
+        const int len = left <= 0 ? 0 : (left < kBlock ? (int)left : kBlock);
+        v = 0.0f;
+        if (len > 0) {
+            v = __builtin_fabsf(a.W[e0]);
+            for (int i = 1; i < len; ++i) v = f_add(v, __builtin_fabsf(a.W[e0 + i]));
+        }
+        const int64_t blocks = (nW + kBlock - 1) / kBlock - b * kPrepRunBlocks;
+        count = blocks < kPrepRunBlocks ? (int)blocks : (int)kPrepRunBlocks;
+    }
+    const float r = wg_pair_tree(v, count, lds);
+    if (t == 0) __hip_atomic_store(&a.sync[kPrepRootWord + b], prep_word(r), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The tail: CanonSum of the P roots, then s_w (published) and s_y.  Each
+// thread issues the loads of its RUN root words together and polls again only
+// for the words not yet published.
+template <int RUN>
+__device__ float prep_tail_sum(const PrepArgs& a, float* lds) {
+    const uint64_t* roots = a.sync + kPrepRootWord;
+    uint64_t* err = a.sync + kPrepErrWord;
+    const int64_t first = (int64_t)threadIdx.x * RUN;
+    uint64_t w[RUN];
+#pragma unroll
+    for (int i = 0; i < RUN; ++i)
+        w[i] = first + i < a.P ? __hip_atomic_load(roots + first + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : kPrepReady;
+    float vals[RUN];
+#pragma unroll
+    for (int i = 0; i < RUN; ++i)
+        vals[i] = w[i] >= kPrepReady ? __builtin_bit_cast(float, (uint32_t)w[i]) : prep_wait(roots + first + i, err);
+    return canon_runs_tree<RUN>([&](int64_t j) { return vals[j - first]; }, a.P, lds);
+}
+
+__device__ void prep_tail(const PrepArgs& a, float* lds) {
+    float S;
+    if (a.P <= 256) S = prep_tail_sum<1>(a, lds);
+    else if (a.P <= 512) S = prep_tail_sum<2>(a, lds);
+    else if (a.P <= 1024) S = prep_tail_sum<4>(a, lds);
+    else if (a.P <= 2048) S = prep_tail_sum<8>(a, lds);
+    else S = prep_tail_sum<16>(a, lds);
+    if (threadIdx.x == 0) {
+        canon_finish(S, a.fin);
+        __hip_atomic_store(&a.sync[kPrepStepWord], prep_word(a.fin.scal->s_w), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+__global__ __launch_bounds__(256) void fwd_prep_kernel(PrepArgs a) {
+    __shared__ float lds[256];
+    __shared__ float blk[256];
+    int64_t i = blockIdx.x;
+    if (i < a.P) {
+        prep_abs_run(a, i, lds, blk);
+        return;
+    }
+    if (i == a.P) {
+        prep_tail(a, lds);
+        return;
+    }
+    i -= a.P + 1;
+    const int64_t nx = a.xgx * a.xgy;
+    if (i < nx) {
+        const Quantizer qz(a.s_x);
+        const uint32_t iu = (uint32_t)i, gx = (uint32_t)a.xgx;   // 32-bit: no float-assisted 64-bit divide
+        quantize_part(a.X, a.M, a.K, qz, a.qx, a.Mp, a.Kp, 0, iu % gx, iu / gx, a.xgy);
+        return;
+    }
+    i -= nx;
+    if (threadIdx.x == 0) lds[0] = prep_wait(a.sync + kPrepStepWord, a.sync + kPrepErrWord);
+    __syncthreads();
+    const Quantizer qz(lds[0]);
+    const uint32_t iu = (uint32_t)i, gx = (uint32_t)a.wgx;
+    quantize_part(a.W, a.N, a.K, qz, a.qw, a.Nvp, a.Kp, a.swiglu_half, iu % gx, iu / gx, a.wgy);
+}
+
+// zeroes the step, error and root words of a launch with P roots
+__global__ __launch_bounds__(256) void fwd_prep_clear_kernel(uint64_t* sync, int64_t words) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j < words) sync[j] = 0ull;
+}
+
+hipError_t launch_fwd_prep(PrepArgs a, hipStream_t st) {
+    const int64_t nW = a.N * a.K;
+    a.P = ceil_div(ceil_div(nW, kBlock), kPrepRunBlocks);
+    if (a.P < 1 || a.P > kPrepMaxRoots || a.Mp <= 0 || a.Nvp <= 0 || a.Kp <= 0) return hipErrorInvalidValue;
+    a.wgx = ceil_div(a.Kp / 4, 256);
+    if (a.wgx > kPrepMaxWgW) return hipErrorInvalidValue;
+    const int64_t wrows = ceil_div(a.Nvp, kQRows);
+    const int64_t wcap = kPrepMaxWgW / a.wgx;
+    a.wgy = wrows < wcap ? wrows : wcap;
+    a.xgx = a.wgx;
+    const int64_t xrows = ceil_div(a.Mp, kQRows);
+    a.xgy = xrows < 2048 ? xrows : 2048;
+    const int64_t grid = a.P + 1 + a.wgx * a.wgy + a.xgx * a.xgy;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    const int64_t words = kPrepRootWord + a.P;
+    hipLaunchKernelGGL(fwd_prep_clear_kernel, dim3((unsigned)ceil_div(words, 256)), dim3(256), 0, st, a.sync,
+                       words);
+    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    hipLaunchKernelGGL(fwd_prep_kernel, dim3((unsigned)grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 // ---- dequantised operand for the backward ------------------------------------------
 // out[r][c] = fl(q(v[r][c]) * s) with q the LSQ quantiser, zero rows and
 // columns past the data; thread -> 4 consecutive columns of one padded row.

@@ -30,6 +30,7 @@ struct Tuning {
     int wg_blocks;    // 32-blocks per workgroup in CanonSum passes (64, 128, 256)
     int vec;          // 16-byte vectors per thread in streaming kernels (1, 2, 4)
     int engine;       // backward products: 1 VALU, 2 matrix cores (when the operands allow)
+    int fwd_prep;     // forward preparation: 1 one launch (where it fits), 2 separate launches
 };
 // false for a value outside its range
 bool resolve_tuning(const brl_tuning* t, Tuning* out);
@@ -50,6 +51,24 @@ struct CanonFinishArgs {
     float* s_w_out;         // optional copy of s_w
     float* nu_out;          // optional copy of nu
 };
+
+// The scalar that follows a CanonSum S (one thread): the weight step s_w and
+// s_y = s_x * s_w, or the norm nu = sqrt(S) and the clip coefficient.
+__device__ __forceinline__ void canon_finish(float S, const CanonFinishArgs& f) {
+    if (f.mode == kFinishScale) {
+        const float s_w = weight_step(S, f.count_f);
+        f.scal->s_w = s_w;
+        f.scal->s_y = f_mul(f.s_x, s_w);
+        if (f.s_w_out) *f.s_w_out = s_w;
+    } else {
+        float nu = f_sqrt(S);
+        int clip = nu > f.max_norm;
+        f.scal->nu = nu;
+        f.scal->clip = clip;
+        f.scal->kappa = clip ? f_div(f.max_norm, f_add(nu, f.eps)) : 1.0f;
+        if (f.nu_out) *f.nu_out = nu;
+    }
+}
 
 // Partial buffer floats needed by launch_canon for n elements.
 int64_t canon_partials(int64_t n);
@@ -74,6 +93,31 @@ hipError_t launch_quantize(const float* v, int64_t rows, int64_t cols, const flo
 // (cols_p a multiple of 4).
 hipError_t launch_dequant(const float* v, int64_t rows, int64_t cols, const float* s_dev, float s_host,
                           float* out, int64_t rows_p, int64_t cols_p, hipStream_t st);
+
+// The forward's preparation in one launch (weight step, W codes, X codes);
+// see fwd_prep_kernel.  sync: kPrepSyncWords 64-bit words (the step word,
+// the error word, then one word per |W| run root), cleared by the launcher.
+constexpr int64_t kPrepRunBlocks = 256;                   // 32-blocks per first-range workgroup
+constexpr int64_t kPrepMaxRoots = 256 * 16;               // roots the in-kernel tail reduces
+constexpr int64_t kPrepStepWord = 0, kPrepErrWord = 1, kPrepRootWord = 2;
+constexpr int64_t kPrepSyncWords = kPrepRootWord + kPrepMaxRoots;
+struct PrepArgs {
+    const float* X;
+    const float* W;
+    int64_t M, K, N;       // N = stacked width
+    float s_x;
+    int8_t* qx;            // [Mp, Kp]
+    int8_t* qw;            // [Nvp, Kp]
+    int64_t Mp, Kp, Nvp, swiglu_half;
+    uint64_t* sync;        // kPrepSyncWords words
+    int64_t P;             // first-range workgroups (|W| run roots)
+    int64_t wgx, wgy;      // W quantiser grid
+    int64_t xgx, xgy;      // X quantiser grid
+    CanonFinishArgs fin;
+};
+// true when one launch can prepare a forward with N*K weights
+inline bool fwd_prep_fits(int64_t nW) { return ceil_div(ceil_div(nW, kBlock), kPrepRunBlocks) <= kPrepMaxRoots; }
+hipError_t launch_fwd_prep(PrepArgs a, hipStream_t st);
 
 struct GemmArgs {
     const int8_t* qx;     // [Mp, Kp]

@@ -92,6 +92,8 @@ typedef struct brl_tuning {
     int32_t stream_vec;        /* 16-byte vectors per thread in the streaming kernels: 1, 2 or 4 (0: 1) */
     int32_t bwd_engine;        /* backward products on 1 the VALU, 2 the matrix cores (0: 2; the matrix
                                   cores need N % 4 == 0 and a 16-byte aligned dOut, else 1 runs) */
+    int32_t fwd_prep;          /* forward weight step and quantisers in 1 one launch (used while
+                                  N*K <= 2^25 and M > 0), 2 separate launches (0: 1) */
 } brl_tuning;
 
 /* Bytes of device workspace needed by an operation run with `tune` (NULL:

@@ -194,6 +194,67 @@ def test_fwd_zero_weights_and_empty_rows():
     assert_bitwise(s_w, np.array([oracle.weight_scale(W)]), "s_w (M=0)")
 
 
+# The forward's preparation (weight step, W codes, X codes) runs as one launch
+# by default and as separate launches with fwd_prep=2.  The in-launch tail
+# reduces the |W| run roots with 1, 2, 4, 8 or 16 roots per thread depending
+# on their count P (P <= 256, 512, 1024, 2048, 4096): the shapes below reach
+# every one, with a short last run where N*K is not a multiple of 8192.
+PREP_SHAPES = [
+    (70, 1000, 1500),     # P = 184, short last run
+    (64, 2048, 1100),     # P = 275
+    (96, 2048, 3000),     # P = 750
+    (64, 2048, 6000),     # P = 1500
+    (64, 4096, 4500),     # P = 2250
+    (300, 64, 9),         # P = 1 (the single run is also the last)
+]
+
+
+@pytest.mark.parametrize("M,K,N", PREP_SHAPES)
+def test_fwd_prep_one_launch(M, K, N):
+    g = np.random.default_rng(M * 7 + N)
+    W = (g.standard_normal((N, K)) * np.exp(g.uniform(-3, 3, (N, 1)))).astype(np.float32)
+    X = g.standard_normal((M, K)).astype(np.float32)
+    Xd, Wd = _cuda(X), _cuda(W)
+    Y1, _, s1 = brl.qat_linear_fwd(Xd, Wd, synth.S_X)
+    Y2, _, s2 = brl.qat_linear_fwd(Xd, Wd, synth.S_X, tune=brl.Tuning(fwd_prep=2))
+    torch.cuda.synchronize()
+    assert_bitwise(s1, np.array([oracle.weight_scale(W)]), "s_w (one launch)")
+    assert_bitwise(s2, np.array([oracle.weight_scale(W)]), "s_w (separate launches)")
+    assert_bitwise(Y1, Y2, "Y one launch vs separate launches")
+    rows = np.unique(np.r_[0, M // 2, M - 1])
+    assert_bitwise(Y1[rows], oracle.fwd_rows(X[rows], W, synth.S_X), "Y rows")
+
+
+def test_fwd_prep_unaligned_weights_and_reused_workspace():
+    """W 4 bytes off a 16-byte boundary takes the per-thread block path in
+    every run; one workspace serves calls with different weights in a row
+    (the launch clears the counter and flag it leaves behind)."""
+    M, K, N = 130, 96, 700
+    g = np.random.default_rng(5)
+    X = g.standard_normal((M, K)).astype(np.float32)
+    Xd = _cuda(X)
+    ws = brl.workspace(brl.OP_FWD, M, K, N, DEV)
+    for rep, scale in enumerate((1.0, 0.003, 40.0)):
+        W = (g.standard_normal((N, K)) * scale).astype(np.float32)
+        buf = torch.empty(N * K + 1, dtype=torch.float32, device=DEV)
+        Wd = buf[1:].view(N, K)
+        Wd.copy_(_cuda(W))
+        assert Wd.data_ptr() % 16 == 4
+        Y, _, s_w = brl.qat_linear_fwd(Xd, Wd, synth.S_X, ws=ws)
+        torch.cuda.synchronize()
+        assert_bitwise(s_w, np.array([oracle.weight_scale(W)]), f"s_w call {rep}")
+        assert_bitwise(Y, oracle.linear_fwd(X, W, synth.S_X), f"Y call {rep}")
+
+
+def test_fwd_prep_swiglu_separate_launches():
+    inp = _case_inputs(200, 96, 256, seed=12, swiglu=True)
+    Y, Ypre, _ = brl.qat_linear_fwd(_cuda(inp.X), _cuda(inp.W), synth.S_X, epilogue=brl.EPILOGUE_SWIGLU,
+                                    tune=brl.Tuning(fwd_prep=2))
+    wantY, wantPre = oracle.linear_fwd(inp.X, inp.W, synth.S_X, epilogue=1)
+    assert_bitwise(Ypre, wantPre, "Ypre")
+    assert_bitwise(Y, wantY, "SwiGLU(Y)")
+
+
 def _boundary_inputs(s, seed, rows=48, cols=96):
     """X whose quotients by the step s sit within a few ulp of the points
     where the quantiser's result changes: the rounding midpoints k + 1/2 and
