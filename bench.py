@@ -231,10 +231,12 @@ def measured_peaks(torch, brl):
     return out
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE passes, calibrated with a copy kernel of
-    known size), or None when the kernel sources changed since they were taken."""
+def measured_traffic(kernels, weights=None):
+    """HBM bytes per dispatch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE passes, calibrated with a copy kernel of known
+    size): the dispatch-weighted average over `kernels` (entries of the
+    summary), or None when a source or compiler flag of the library changed
+    since the counters were taken."""
     import hashlib
     from bitwise_reproducible_lsq_amd import build as brl_build
     path = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.json")
@@ -245,12 +247,19 @@ def measured_traffic(kernel: str):
         f = os.path.join(ROOT, src)
         if not os.path.exists(f) or hashlib.sha256(open(f, "rb").read()).hexdigest() != digest:
             return None
-    # the compiler flags of the replay unit (include paths left out: they differ between machines)
-    flags = [f for f in brl_build.FLAGS + brl_build.EXTRA.get("replay.hip", []) if not f.startswith("-I")]
-    if hashlib.sha256(json.dumps(flags).encode()).hexdigest() != rec.get("replay_flags_sha256"):
+    # compiler flags of every unit (include paths left out: they differ between machines)
+    flags = {u: [f for f in brl_build.FLAGS + brl_build.EXTRA.get(u, []) if not f.startswith("-I")]
+             for u in brl_build.SOURCES}
+    if hashlib.sha256(json.dumps(flags, sort_keys=True).encode()).hexdigest() != rec.get("flags_sha256"):
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else int(round(k["bytes"]))
+    weights = weights or [1] * len(kernels)
+    total = 0.0
+    for k, w in zip(kernels, weights):
+        e = rec.get("kernels", {}).get(k)
+        if e is None:
+            return None
+        total += w * e["bytes"]
+    return int(round(total / sum(weights)))
 
 
 def parse():
@@ -467,6 +476,31 @@ def main():
                         "frac_of_i8_peak": frac(t_all, PEAK_I8_TOPS)},
         }
 
+    # the dominant kernel by time per step: the matrix-core product kernel of
+    # dX (ste_mfma_kernel<true, 7>), one launch per microbatch of each layer;
+    # its dW twin takes about 2% less.  achieved = the launches' algorithmic
+    # operations (a product and an add per reduction step) over their time
+    dx_ops = sum(2.0 * lay["M"] * lay["N"] * lay["K"] for lay in layers)
+    dx_ms_sum = sum(configs[lay["name"]]["ms"]["dX"] for lay in layers)
+    dx_launches = sum(lay["mb"] for lay in layers)
+    dx_rate = dx_ops / (dx_ms_sum * 1e-3) / 1e12
+    dx_traffic = measured_traffic(["brl::ste_mfma_kernel<true, 7> [qkv dX]",
+                                   "brl::ste_mfma_kernel<true, 7> [swiglu_gate_up dX]",
+                                   "brl::ste_mfma_kernel<true, 7> [down_proj dX]"], weights=[1, 1, 4])
+    dx_alg = sum(4.0 * (lay["M"] * lay["N"] + lay["N"] * lay["K"] * lay["mb"] + lay["M"] * lay["K"])
+                 for lay in layers) / dx_launches
+    dx_roofline = {
+        "kernel": f"ste_mfma_kernel<true, 7> (dX: K=1 fp32 MFMA products, ordered binary32 adds; "
+                  f"{dx_launches} launches per step: QKV 1, SwiGLU gate+up 1, down projection 4 microbatches)",
+        "bound": "alu", "achieved": round(dx_rate, 3), "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
+        "frac": round(dx_rate / PEAK_VALU_F32_TOPS, 4), "frac_of_engine": round(dx_rate / engine_tops, 4),
+        "ops_per_launch": round(dx_ops / dx_launches), "ms_per_step": round(dx_ms_sum, 4),
+        "timing": "HIP events on the call stream around dX-only qat_linear_bwd calls minus the operand "
+                  "preparation alone, after the timed steps (the step's calls form dX and dW together); "
+                  "the finish pass over chunk roots is included (about 1% on gate+up)",
+        "traffic": dx_traffic, "traffic_unit": "bytes per launch (average over the step's launches)",
+        "algorithmic_bytes": round(dx_alg),
+    }
     tops = total_ops / (lin_ms * 1e-3) / 1e12
     replay_bytes = REPLAY_BYTES_PER_ELEM * L
     replay_gbps = replay_bytes / (rep_ms * 1e-3) / 1e9
@@ -499,18 +533,15 @@ def main():
             "accumulate_avg": round(acc_avg_ms, 5), "norm_clip": round(nc_ms, 4),
         },
         "configs": configs,
-        "roofline": {
-            "kernel": f"accumulate_v4_kernel (ordered_reduce running sum, {acc_n // max(K_, 1)} launches "
-                      "per step, timed with one event pair per run of consecutive launches)",
-            "bound": "hbm",
-            "achieved": round(acc_gbps, 1),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(acc_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": measured_traffic("brl::accumulate_v4_kernel<1>") if L == rcase.length else None,
-            "traffic_unit": "bytes per launch",
-        },
+        "roofline": dx_roofline,
         "rooflines_other": {
+            "running_sum": {
+                "kernel": f"accumulate_v4_kernel (ordered_reduce running sum, {acc_n // max(K_, 1)} launches "
+                          "per step, timed with one event pair per run of consecutive launches)",
+                "bound": "hbm", "achieved": round(acc_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(acc_gbps / PEAK_HBM_GBPS, 4),
+                "traffic": measured_traffic(["brl::accumulate_v4_kernel<1>"]) if L == rcase.length else None,
+                "traffic_unit": "bytes per launch"},
             "replay_total": {"bound": "hbm", "achieved": round(replay_gbps, 1), "peak": PEAK_HBM_GBPS,
                              "unit": "GB/s", "frac": round(replay_gbps / PEAK_HBM_GBPS, 4)},
             "fwd_call": dict(configs["qkv"]["fwd"], layer="qkv"),
