@@ -480,8 +480,15 @@ def main():
     # dX (ste_mfma_kernel<true, 7>), one launch per microbatch of each layer;
     # its dW twin takes about 2% less.  achieved = the launches' algorithmic
     # operations (a product and an add per reduction step) over their time
+    # time: each layer's backward inside the timed steps, less its operand
+    # preparation, split between dX and dW in the ratio of the dX-only and
+    # dW-only calls timed after the steps (those standalone calls alone run
+    # a few percent faster than inside the step)
     dx_ops = sum(2.0 * lay["M"] * lay["N"] * lay["K"] for lay in layers)
-    dx_ms_sum = sum(configs[lay["name"]]["ms"]["dX"] for lay in layers)
+    dx_ms_sum = 0.0
+    for lay in layers:
+        c = configs[lay["name"]]["ms"]
+        dx_ms_sum += (c["bwd"] - c["bwd_prelude"]) * c["dX"] / (c["dX"] + c["dW"])
     dx_launches = sum(lay["mb"] for lay in layers)
     dx_rate = dx_ops / (dx_ms_sum * 1e-3) / 1e12
     dx_traffic = measured_traffic(["brl::ste_mfma_kernel<true, 7> [qkv dX]",
@@ -495,9 +502,10 @@ def main():
         "bound": "alu", "achieved": round(dx_rate, 3), "peak": round(PEAK_VALU_F32_TOPS, 2), "unit": "TFLOP/s",
         "frac": round(dx_rate / PEAK_VALU_F32_TOPS, 4), "frac_of_engine": round(dx_rate / engine_tops, 4),
         "ops_per_launch": round(dx_ops / dx_launches), "ms_per_step": round(dx_ms_sum, 4),
-        "timing": "HIP events on the call stream around dX-only qat_linear_bwd calls minus the operand "
-                  "preparation alone, after the timed steps (the step's calls form dX and dW together); "
-                  "the finish pass over chunk roots is included (about 1% on gate+up)",
+        "timing": "each layer's qat_linear_bwd time in the timed steps (HIP events on the call stream) less "
+                  "its operand preparation, split between dX and dW in the ratio of dX-only and dW-only calls "
+                  "timed after the steps (the step's calls form dX and dW together); the finish pass over "
+                  "chunk roots is included (about 1% on gate+up)",
         "traffic": dx_traffic, "traffic_unit": "bytes per launch (average over the step's launches)",
         "algorithmic_bytes": round(dx_alg),
     }
