@@ -251,7 +251,8 @@ brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, 
     fin.scal = L.scal;
     fin.s_w_out = s_w_out;
     brl_status s = BRL_OK;
-    if (M > 0 && tn.fwd_prep == 1 && fwd_prep_fits(N * K)) {
+    const bool one_launch = M > 0 && tn.fwd_prep == 1 && fwd_prep_fits(N * K);
+    if (one_launch) {
         // weight step, W codes and X codes in one launch
         PrepArgs p{};
         p.X = X; p.W = W; p.M = M; p.K = K; p.N = N; p.s_x = s_x;
@@ -272,6 +273,7 @@ brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, 
     g.qx = L.qx; g.qw = L.qw; g.M = M; g.N = N; g.Kp = L.Kp; g.Mp = L.Mp; g.Nvp = L.Nvp;
     g.scal = L.scal; g.addend = addend; g.Y = Y; g.Ypre = Ypre; g.epilogue = epilogue;
     g.ek = exp_constants();
+    g.prep_err = one_launch ? L.sync + kPrepErrWord : nullptr;
     return check_hip(launch_gemm_i8(g, st), "int8 GEMM");
 }
 

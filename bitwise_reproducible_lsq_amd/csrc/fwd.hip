@@ -151,13 +151,13 @@ hipError_t launch_quantize(const float* v, int64_t rows, int64_t cols, const flo
 // 1025, fewer workgroups than the device holds at once (this kernel fits 8 per
 // CU: 2048 on 256 CUs), so the workgroups they wait for always find room to run even when
 // every waiter is resident; each wait is bounded all the same
-// (kPrepSpinLimit polls, then the error word records it), so every wave
-// exits.  Measured on the MI355X (forward call, QKV / SwiGLU gate+up / down
+// (kPrepSpinLimit polls, about a second; then the error word records it and
+// the GEMM writes NaN for every output), so every wave exits.  Measured on the MI355X (forward call, QKV / SwiGLU gate+up / down
 // projection at 16384 tokens): 150 / 560 / 261 us against 158 / 575 / 276 us
 // for the four separate launches; the W range before the X range, or at most
 // 512 W workgroups, measured 1-2% slower.
 constexpr int64_t kPrepMaxWgW = 1024;
-constexpr uint32_t kPrepSpinLimit = 1u << 17;   // 0.1 to 0.3 s of polling
+constexpr uint32_t kPrepSpinLimit = 1u << 20;
 constexpr uint64_t kPrepReady = 1ull << 32;
 
 __device__ __forceinline__ uint64_t prep_word(float v) {
@@ -551,7 +551,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_i8_kern
     wait_vmcnt<0>();                       // no load into LDS outlives the loop
 
     // ---- epilogue: Y = fl(acc) * s_y (+ addend), or the SwiGLU activation ----
-    const float s_y = a.scal->s_y;
+    // a preparation wait that gave up (see fwd_prep_kernel) poisons Y with NaN
+    const float s_y = (a.prep_err && *a.prep_err) ? __builtin_nanf("") : a.scal->s_y;
     const int col_l = lane & 31;
     const int row_q = (lane >> 5) * 4;
     if constexpr (EPI == BRL_EPILOGUE_SWIGLU) {

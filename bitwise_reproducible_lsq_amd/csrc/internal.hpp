@@ -130,6 +130,7 @@ struct GemmArgs {
     float* Ypre;          // SwiGLU pre-activation [M, N] or null
     int epilogue;
     ExpConsts ek;
+    const uint64_t* prep_err;   // the one-launch preparation's error word, or null
 };
 hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t st);
 

@@ -124,6 +124,11 @@ BRL_API size_t brl_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, 
  * tune) bytes, owned by the caller; calls that overlap in time must not
  * share one.  tune: NULL or the call's launch shapes (see brl_tuning).
  * Requires |acc| < 2^31, guaranteed for K <= 133144.
+ * With the one-launch preparation (tune->fwd_prep 0 or 1), workgroups of one
+ * kernel wait on values other workgroups of it publish in the workspace; the
+ * waits are bounded (about a second), and a wait that gives up, which needs
+ * the device to leave those workgroups unscheduled that long, makes every
+ * element of Y NaN instead of returning wrong numbers.
  */
 BRL_API brl_status qat_linear_fwd(const float* X, const float* W, int64_t M, int64_t K, int64_t N,
                           float s_x, const float* addend, int32_t epilogue,

@@ -225,6 +225,22 @@ def test_fwd_prep_one_launch(M, K, N):
     assert_bitwise(Y1[rows], oracle.fwd_rows(X[rows], W, synth.S_X), "Y rows")
 
 
+@pytest.mark.parametrize("N", [8192, 8200])
+def test_fwd_prep_largest_one_launch_and_beyond(N):
+    """N*K = 2^25 is the largest weight count one launch prepares (4096 run
+    roots, 16 per thread of its tail); one more row takes the separate
+    launches.  s_w and sampled rows of Y against the oracle."""
+    M, K = 64, 4096
+    g = np.random.default_rng(N)
+    W = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    X = g.standard_normal((M, K)).astype(np.float32)
+    Y, _, s_w = brl.qat_linear_fwd(_cuda(X), _cuda(W), synth.S_X)
+    torch.cuda.synchronize()
+    assert_bitwise(s_w, np.array([oracle.weight_scale(W)]), "s_w")
+    rows = np.array([0, 37, M - 1])
+    assert_bitwise(Y[rows], oracle.fwd_rows(X[rows], W, synth.S_X), "Y rows")
+
+
 def test_fwd_prep_unaligned_weights_and_reused_workspace():
     """W 4 bytes off a 16-byte boundary takes the per-thread block path in
     every run; one workspace serves calls with different weights in a row
