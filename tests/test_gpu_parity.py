@@ -225,6 +225,32 @@ def test_fwd_prep_one_launch(M, K, N):
     assert_bitwise(Y1[rows], oracle.fwd_rows(X[rows], W, synth.S_X), "Y rows")
 
 
+def test_fwd_accumulator_at_the_int32_limit():
+    """K = 133144, the largest K the forward accepts: rows of X whose codes
+    are all +127 or all -127 against a weight row whose codes are all 127
+    (the other rows zero, so the weight step is small) give |acc| =
+    127 * 127 * K = 2147479576, within 6071 of 2^31 - 1; the remaining rows
+    and columns are mixed.  Every element against the oracle."""
+    M, K, N = 5, 133144, 25
+    g = np.random.default_rng(21)
+    X = g.standard_normal((M, K)).astype(np.float32)
+    X[0] = 10.0                      # t = 200: code +127
+    X[1] = -10.0                     # code -127
+    X[2, ::2] = 10.0                 # alternating +127 / normal
+    W = np.zeros((N, K), np.float32)
+    W[0] = 1.0                       # mean |w| = 1/25: t = 140.8, code 127
+    W[3] = (g.standard_normal(K) * 0.02).astype(np.float32)
+    Y, _, s_w = brl.qat_linear_fwd(_cuda(X), _cuda(W), synth.S_X)
+    torch.cuda.synchronize()
+    assert_bitwise(s_w, np.array([oracle.weight_scale(W)]), "s_w")
+    want = oracle.linear_fwd(X, W, synth.S_X)
+    assert_bitwise(Y, want, "Y")
+    # the extreme sums really are there: acc = +-127^2 K before the scale
+    s_y = np.float32(np.float32(synth.S_X) * np.float32(oracle.weight_scale(W)))
+    assert want[0, 0] == np.float32(np.float32(127 * 127 * K) * s_y)
+    assert want[1, 0] == -want[0, 0]
+
+
 @pytest.mark.parametrize("N", [8192, 8200])
 def test_fwd_prep_largest_one_launch_and_beyond(N):
     """N*K = 2^25 is the largest weight count one launch prepares (4096 run
