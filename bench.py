@@ -52,13 +52,17 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_I8_TOPS = 5030.0
 PEAK_VALU_F32_TOPS = 256 * 128 * 2.4e9 / 1e12         # 78.64 T ops/s
 
-# Replay bytes per element index that the method must move, with at most two
-# partials resident: per replica the first two shards combine in one pass and
-# every later shard is one add (read A, read G, write A: 12 B each) -> 6 * 7 *
-# 12 = 504; TreeFold reads 6 accumulators and writes T (28 B; the squared-norm
-# CanonSum could ride on that pass, so it adds nothing); clip reads and writes
-# T (8 B).
-REPLAY_BYTES_PER_ELEM = 6 * 7 * 12 + 28 + 8           # 540
+# Replay bytes per element index that the method must move with one
+# replica's partials resident at a time (the bench keeps all 48 resident):
+# each of the first 5 replicas reads its 8 partials and writes A_r (36 B);
+# the last replica's running sum is formed inside the TreeFold, which reads
+# A_0..A_4 and the 8 partials and writes T (56 B; the squared-norm CanonSum
+# could ride on that pass, so it adds nothing); clip reads and writes T (8 B).
+# (With at most two partials resident -- one add pass per shard -- it would
+# be 6 * 7 * 12 + 28 + 8 = 540 B.)
+REPLAY_R, REPLAY_S = 6, 8
+REPLAY_BYTES_PER_ELEM = (REPLAY_R - 1) * (REPLAY_S + 1) * 4 + (REPLAY_R - 1 + REPLAY_S + 1) * 4 + 8   # 244
+RUNSUM_BYTES_PER_ELEM = (REPLAY_S + 1) * 4                                                              # 36
 
 # State hash (the next row after the hot path, measured beside it, not part of
 # `value`): the compiled SHA-256 block loop of the leaf kernel issues
@@ -352,7 +356,10 @@ def main():
         layers.append(lay)
     partials = [synth.replay_partial(rcase, v, device=dev, length=L) for v in range(R * S)]
     # all partials stay resident, so each replica's first two shards combine in one pass
-    state = brl.ReduceState(R, S, L, device=dev, partials_persist=True)
+    # all partials stay resident, so each replica's running sum is one pass
+    # over its 8 partials (the last replica's inside the TreeFold)
+    assert (R, S) == (REPLAY_R, REPLAY_S)
+    state = brl.ReduceState(R, S, L, device=dev, replica_resident=True)
     out = torch.empty(L, dtype=torch.float32, device=dev)
     ws_n = brl.workspace(brl.OP_NORM, L, 0, 0, dev)
     torch.cuda.synchronize()
@@ -387,20 +394,15 @@ def main():
         state.reset()
         with timer.region("replay"):
             for r in range(R):
-                # shard 0 launches nothing (its partial stays resident), so the
-                # calls of shards 1 .. S-1 (1 .. S-2 for the last replica, whose
-                # last call is the fold) are a run of running-sum launches only:
-                # one event pair per run keeps event overhead out of the
-                # per-launch average
-                brl.ordered_reduce(state, partials[r * S], out=out)
-                last_r = r == R - 1
-                hi = S - 1 if last_r else S
-                with timer.region("accumulate"):
-                    for s in range(1, hi):
+                # a replica's calls launch nothing until its last shard's,
+                # which launches its running sum (or, for the last replica,
+                # the TreeFold): one event pair around the replica's calls
+                # times that one kernel
+                with timer.region("runsum" if r < R - 1 else "fold"):
+                    for s in range(S):
                         brl.ordered_reduce(state, partials[r * S + s], out=out)
-                timer.count("accumulate_launches", hi - 1)
-                if last_r:
-                    brl.ordered_reduce(state, partials[r * S + S - 1], out=out)
+                if r < R - 1:
+                    timer.count("runsum_launches", 1)
             with timer.region("norm_clip"):
                 brl.grad_l2norm_clip(out, rcase.max_norm, ws=ws_n)
 
@@ -418,8 +420,9 @@ def main():
     K_ = args.steps
     lin_ms = timer.ms("linear")[0] / K_
     rep_ms = timer.ms("replay")[0] / K_
-    acc_ms = timer.ms("accumulate")[0]
-    acc_n = timer.counts.get("accumulate_launches", 0)
+    acc_ms = timer.ms("runsum")[0]
+    acc_n = timer.counts.get("runsum_launches", 0)
+    fold_ms = timer.ms("fold")[0] / K_
     nc_ms = timer.ms("norm_clip")[0] / K_
     acc_avg_ms = acc_ms / max(acc_n, 1)
 
@@ -512,7 +515,7 @@ def main():
     tops = total_ops / (lin_ms * 1e-3) / 1e12
     replay_bytes = REPLAY_BYTES_PER_ELEM * L
     replay_gbps = replay_bytes / (rep_ms * 1e-3) / 1e9
-    acc_bytes = 12.0 * L
+    acc_bytes = float(RUNSUM_BYTES_PER_ELEM) * L
     acc_gbps = acc_bytes / (acc_avg_ms * 1e-3) / 1e9
 
     result = {
@@ -536,19 +539,21 @@ def main():
             "s_x": synth.S_X, "replicas": R, "shards": S, "replay_length": L,
         },
         "ordered_reduce_GBps": round(replay_gbps, 1),
+        "ordered_reduce_bytes_per_element": REPLAY_BYTES_PER_ELEM,
         "phases_ms": {
             "linear_fwd_bwd": round(lin_ms, 4), "replay": round(rep_ms, 4),
-            "accumulate_avg": round(acc_avg_ms, 5), "norm_clip": round(nc_ms, 4),
+            "runsum_avg": round(acc_avg_ms, 5), "fold": round(fold_ms, 4), "norm_clip": round(nc_ms, 4),
         },
         "configs": configs,
         "roofline": dx_roofline,
         "rooflines_other": {
             "running_sum": {
-                "kernel": f"accumulate_v4_kernel (ordered_reduce running sum, {acc_n // max(K_, 1)} launches "
-                          "per step, timed with one event pair per run of consecutive launches)",
+                "kernel": f"runsum_v4_kernel (a replica's running sum over its {S} resident partials in one pass, "
+                          f"{acc_n // max(K_, 1)} launches per step, each timed with one event pair around the "
+                          "replica's calls)",
                 "bound": "hbm", "achieved": round(acc_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(acc_gbps / PEAK_HBM_GBPS, 4),
-                "traffic": measured_traffic(["brl::accumulate_v4_kernel<1>"]) if L == rcase.length else None,
+                "frac": round(acc_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": int(acc_bytes),
+                "traffic": measured_traffic(["brl::runsum_v4_kernel"]) if L == rcase.length else None,
                 "traffic_unit": "bytes per launch"},
             "replay_total": {"bound": "hbm", "achieved": round(replay_gbps, 1), "peak": PEAK_HBM_GBPS,
                              "unit": "GB/s", "frac": round(replay_gbps / PEAK_HBM_GBPS, 4)},

@@ -25,6 +25,7 @@ BRL_OK, BRL_EINVAL, BRL_ESHAPE, BRL_EORDER, BRL_EDEVICE, BRL_EWORKSPACE = 0, -1,
 EPILOGUE_NONE, EPILOGUE_SWIGLU = 0, 1
 OP_FWD, OP_BWD, OP_NORM, OP_HASH = 0, 1, 2, 3
 MAX_REPLICAS = 64
+MAX_SHARDS = 64
 
 PROBE_OPS = {"add": 0, "sub": 1, "mul": 2, "div": 3, "sqrt": 4, "i2f": 5, "rne": 6, "exp": 7, "mfma_mul": 8,
              "mfma_fma": 9}
@@ -46,10 +47,11 @@ class Tuning(C.Structure):
 class ReduceStateC(C.Structure):
     _fields_ = [("replicas", C.c_int32), ("shards", C.c_int32), ("len", C.c_int64),
                 ("next", C.c_int32), ("flags", C.c_uint32), ("pending", C.c_void_p),
-                ("acc", C.c_void_p * MAX_REPLICAS), ("tune", Tuning)]
+                ("acc", C.c_void_p * MAX_REPLICAS), ("tune", Tuning), ("shard_part", C.c_void_p * MAX_SHARDS)]
 
 
 REDUCE_PARTIALS_PERSIST = 1
+REDUCE_REPLICA_RESIDENT = 2
 
 
 _lib = None
@@ -222,7 +224,7 @@ class ReduceState:
 
     def __init__(self, replicas: int, shards: int, length: int, device="cuda",
                  acc: Optional[Sequence[torch.Tensor]] = None, partials_persist: bool = False,
-                 tune: Optional[Tuning] = None):
+                 tune: Optional[Tuning] = None, replica_resident: bool = False):
         if acc is None:
             acc = [torch.empty(length, dtype=torch.float32, device=device) for _ in range(replicas)]
         self.acc = list(acc)
@@ -231,8 +233,11 @@ class ReduceState:
         _check(lib().brl_reduce_init(C.byref(self.c), replicas, shards, length,
                                      C.cast(ptrs, C.c_void_p)))
         # persist: the caller keeps each replica's shard-0 partial valid and
-        # unchanged until its shard-1 call has run (see the C header)
-        self.c.flags = REDUCE_PARTIALS_PERSIST if partials_persist else 0
+        # unchanged until its shard-1 call has run; replica_resident: every
+        # partial of a replica until the replica's last-shard call has run
+        # (see the C header)
+        self.c.flags = (REDUCE_PARTIALS_PERSIST if partials_persist else 0) | \
+            (REDUCE_REPLICA_RESIDENT if replica_resident else 0)
         if tune is not None:
             self.c.tune = tune
 

@@ -405,9 +405,26 @@ brl_status ordered_reduce(brl_reduce_state* sp, const float* partial, float* out
     if (!resolve_tuning(&sp->tune, &tn)) return fail(BRL_EINVAL, "ordered_reduce: tuning value out of range");
     hipStream_t st = static_cast<hipStream_t>(stream);
     brl_status rc = BRL_OK;
-    const bool defer = (sp->flags & BRL_REDUCE_PARTIALS_PERSIST) && S > 1;
+    const bool resident = (sp->flags & BRL_REDUCE_REPLICA_RESIDENT) && S > 1 && S <= BRL_MAX_SHARDS;
+    const bool defer = !resident && (sp->flags & (BRL_REDUCE_PARTIALS_PERSIST | BRL_REDUCE_REPLICA_RESIDENT)) && S > 1;
     if (s == 0) sp->pending = nullptr;
-    if (n > 0) {
+    if (resident) {
+        // the replica's partials stay resident: its last shard's call forms
+        // the whole running sum in one pass (for the last replica, inside
+        // the TreeFold)
+        sp->shard_part[s] = partial;
+        if (n > 0 && s == S - 1) {
+            FoldPtrs parts{};
+            for (int i = 0; i < S; ++i) parts.a[i] = sp->shard_part[i];
+            if (!last) {
+                rc = check_hip(launch_runsum(sp->acc[r], parts, S, n, st), "running sum (resident shards)");
+            } else {
+                FoldPtrs p{};
+                for (int i = 0; i < R; ++i) p.a[i] = sp->acc[i];
+                rc = check_hip(launch_fold(p, R, nullptr, parts, S, out, n, st), "TreeFold");
+            }
+        }
+    } else if (n > 0) {
         if (s == 0 && defer) {
             // A_r = G_{r,0} is formed together with the next shard's add
             sp->pending = partial;
@@ -426,7 +443,7 @@ brl_status ordered_reduce(brl_reduce_state* sp, const float* partial, float* out
                 rc = check_hip(launch_accumulate(sp->acc[r], sp->pending, partial, n, 0, tn.vec, st), "running sum");
                 g_last = nullptr;
             }
-            if (rc == BRL_OK) rc = check_hip(launch_fold(p, R, g_last, out, n, st), "TreeFold");
+            if (rc == BRL_OK) rc = check_hip(launch_fold(p, R, g_last, FoldPtrs{}, 0, out, n, st), "TreeFold");
         }
     }
     if (s >= 1) sp->pending = nullptr;

@@ -194,8 +194,13 @@ void adamw_scalars(int64_t step, double tokens, const brl_adamw_config& c, brl_a
 hipError_t launch_accumulate(float* A, const float* X, const float* G, int64_t n, int first, int vec,
                              hipStream_t st);
 struct FoldPtrs { const float* a[64]; };
-hipError_t launch_fold(const FoldPtrs& p, int R, const float* g_last, float* out, int64_t n,
-                       hipStream_t st);
+// TreeFold of A_0..A_{R-1} into out.  Replica R-1's value: with nlast > 0
+// the running sum of its resident partials last.a[0..nlast) (A_{R-1} is not
+// read), else A_{R-1} completed with g_last when given.
+hipError_t launch_fold(const FoldPtrs& p, int R, const float* g_last, const FoldPtrs& last, int nlast,
+                       float* out, int64_t n, hipStream_t st);
+// A <- running sum of parts.a[0..S): ((G_0 + G_1) + G_2) + ..., S >= 1
+hipError_t launch_runsum(float* A, const FoldPtrs& parts, int S, int64_t n, hipStream_t st);
 hipError_t launch_clip(float* g, int64_t n, const Scalars* scal, int vec, hipStream_t st);
 
 // out[i] = a[i] * b[i] formed by the matrix-core product of the backward

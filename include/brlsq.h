@@ -160,12 +160,14 @@ BRL_API brl_status qat_linear_bwd(const float* dOut, const float* X, const float
 
 /* Caller-owned host struct describing one replay.  acc[r] are device
  * buffers of len floats (A_r), owned by the caller; next is the virtual rank
- * v = r*shards + s that ordered_reduce expects next.  flags: 0 or
- * BRL_REDUCE_PARTIALS_PERSIST, set by the caller after brl_reduce_init;
- * tune: the launch shapes of the replay's kernels (zeroed by brl_reduce_init:
- * the defaults; the caller may set it afterwards); pending is the library's
- * own bookkeeping. */
+ * v = r*shards + s that ordered_reduce expects next.  flags: 0,
+ * BRL_REDUCE_PARTIALS_PERSIST or BRL_REDUCE_REPLICA_RESIDENT, set by the
+ * caller after brl_reduce_init; tune: the launch shapes of the replay's
+ * kernels (zeroed by brl_reduce_init: the defaults; the caller may set it
+ * afterwards); pending and shard_part are the library's own bookkeeping. */
 #define BRL_REDUCE_PARTIALS_PERSIST 1u
+#define BRL_REDUCE_REPLICA_RESIDENT 2u
+#define BRL_MAX_SHARDS 64
 typedef struct brl_reduce_state {
     int32_t replicas;
     int32_t shards;
@@ -175,6 +177,7 @@ typedef struct brl_reduce_state {
     const float* pending;
     float* acc[BRL_MAX_REPLICAS];
     brl_tuning tune;
+    const float* shard_part[BRL_MAX_SHARDS];   /* the library's bookkeeping (BRL_REDUCE_REPLICA_RESIDENT) */
 } brl_reduce_state;
 
 /* Fill a reduce state: 1 <= replicas <= 64, shards >= 1, len >= 0, acc[0..replicas)
@@ -200,7 +203,15 @@ BRL_API brl_status brl_reduce_init(brl_reduce_state* st, int32_t replicas, int32
  * shard-0 partial of each replica must stay valid and unchanged until the
  * shard-1 call of that replica has run on the stream; the shard-0 call
  * launches nothing and the shard-1 call forms A_r = G_{r,0} + G_{r,1} in one
- * pass (same bits, one copy pass fewer per replica).
+ * pass (same bits, one copy pass fewer per replica).  With
+ * BRL_REDUCE_REPLICA_RESIDENT in st->flags (and 1 < shards <=
+ * BRL_MAX_SHARDS; otherwise it acts as BRL_REDUCE_PARTIALS_PERSIST), every
+ * partial of a replica must stay valid and unchanged until that replica's
+ * last-shard call has run on the stream: the replica's other calls launch
+ * nothing, and its last-shard call forms the whole running sum
+ * A_r = (((G_{r,0} + G_{r,1}) + G_{r,2}) + ...) + G_{r,S-1} in one pass over
+ * the S partials -- for the last replica inside the TreeFold itself.  Same
+ * bits; per element a replica then moves 4 (S + 1) bytes instead of 12 (S - 1).
  */
 BRL_API brl_status ordered_reduce(brl_reduce_state* st, const float* partial, float* out, void* stream);
 

@@ -144,16 +144,20 @@ def test_down_proj_full_size_microbatches():
     assert_bitwise(dW[wr], want, "dW rows (4 microbatches)")
 
 
-def test_replay_full_size():
+@pytest.mark.parametrize("resident", [False, True])
+def test_replay_full_size(resident):
     """All 48 ranks at 201,326,592 elements; every element of the clipped
-    TreeFold and the norm are compared."""
+    TreeFold, the norm and the running sums A_0..A_4 are compared.  The
+    partials arrive one call at a time, either released after each call or
+    (resident) kept per replica until its last shard's call, which then
+    forms the replica's running sum in one pass."""
     rc = synth.REPLAY
     R, S, L = rc.replicas, rc.shards, rc.length
-    st = brl.ReduceState(R, S, L, device=DEV)
+    st = brl.ReduceState(R, S, L, device=DEV, replica_resident=resident)
     out = torch.empty(L, dtype=torch.float32, device=DEV)
     A = [np.empty(L, np.float32) for _ in range(R)]
     host = np.empty(L, np.float32)
-    last_part = None
+    kept = []
     for v in range(R * S):
         G = synth.replay_partial(rc, v, device=DEV)
         brl.ordered_reduce(st, G, out=out)
@@ -161,6 +165,10 @@ def test_replay_full_size():
         host[:] = G.cpu().numpy()
         r, s = divmod(v, S)
         oracle.replay_accumulate(A[r], host, first=(s == 0))
+        if resident:
+            kept.append(G)
+            if s == S - 1:
+                kept.clear()       # the replica's last call has run (synchronised above)
         del G
     nu = brl.grad_l2norm_clip(out, rc.max_norm)
     torch.cuda.synchronize()

@@ -498,9 +498,9 @@ def test_repeat_runs_identical():
 
 
 # ---- replay -----------------------------------------------------------------------------
-def _replay_gpu(partials_np, R, S, max_norm=1.0, persist=False, tune=None):
+def _replay_gpu(partials_np, R, S, max_norm=1.0, persist=False, tune=None, resident=False):
     L = partials_np[0].size
-    st = brl.ReduceState(R, S, L, device=DEV, partials_persist=persist, tune=tune)
+    st = brl.ReduceState(R, S, L, device=DEV, partials_persist=persist, tune=tune, replica_resident=resident)
     out = None
     keep = []      # with persist the shard-0 partials must outlive the shard-1 call
     for v in range(R * S):
@@ -512,12 +512,18 @@ def _replay_gpu(partials_np, R, S, max_norm=1.0, persist=False, tune=None):
     return out, nu, st
 
 
-@pytest.mark.parametrize("persist", [False, True])
+@pytest.mark.parametrize("mode", ["plain", "persist", "resident"])
 @pytest.mark.parametrize("R,S,L", [(6, 8, 65536 + 5), (1, 1, 1000), (2, 3, 4097), (3, 2, 333),
-                                   (5, 1, 1024), (7, 2, 100), (16, 2, 2048), (6, 8, 3)])
-def test_replay_parity(R, S, L, persist):
+                                   (5, 1, 1024), (7, 2, 100), (16, 2, 2048), (6, 8, 3), (6, 11, 4099),
+                                   (3, 64, 257), (2, 65, 130)])
+def test_replay_parity(R, S, L, mode):
+    """Every running sum A_r (but the last, which the fold consumes) and the
+    clipped TreeFold, with the partials streamed one call at a time, with each
+    replica's shard-0 partial kept until its shard-1 call, and with every
+    partial of a replica kept until its last shard's call (one pass per
+    replica; 65 shards exceed the pointer table and take the persist path)."""
     parts = [synth.replay_partial_host(4, v, L, std=1e-2) for v in range(R * S)]
-    out, nu, st = _replay_gpu(parts, R, S, persist=persist)
+    out, nu, st = _replay_gpu(parts, R, S, persist=mode == "persist", resident=mode == "resident")
     T, wnu, A = oracle.replay(parts, R, S)
     assert_bitwise(nu, np.array([wnu]), "nu")
     assert_bitwise(out, T, "clipped TreeFold")
@@ -578,6 +584,30 @@ def test_norm_tail_runs(n, wg):
     wnu = oracle.l2norm(g)
     nu = brl.grad_l2norm_clip(_cuda(g), 1e30, tune=brl.Tuning(reduce_wg_blocks=wg))
     assert_bitwise(nu, np.array([wnu]), f"nu n={n} wg={wg}")
+
+
+def test_replay_resident_unaligned_partials():
+    """Partials 4 bytes off a 16-byte boundary take the per-element running
+    sum and fold in the one-pass mode."""
+    R, S, L = 6, 4, 1003
+    parts = [synth.replay_partial_host(6, v, L, std=1e-2) for v in range(R * S)]
+    T, wnu, A = oracle.replay(parts, R, S)
+    st = brl.ReduceState(R, S, L, device=DEV, replica_resident=True)
+    keep = []
+    out = None
+    for v in range(R * S):
+        buf = torch.empty(L + 1, dtype=torch.float32, device=DEV)
+        g = buf[1:]
+        g.copy_(_cuda(parts[v]))
+        assert g.data_ptr() % 16 == 4
+        keep.append(buf)
+        out = brl.ordered_reduce(st, g)
+    nu = brl.grad_l2norm_clip(out, 1.0)
+    torch.cuda.synchronize()
+    assert_bitwise(out, T, "clipped TreeFold")
+    assert_bitwise(nu, np.array([wnu]), "nu")
+    for r in range(R - 1):
+        assert_bitwise(st.acc[r], A[r], f"A_{r}")
 
 
 def test_replay_stream_shape_invariance():
