@@ -338,3 +338,38 @@ def test_noalloc_norm_rejects_before_any_device_call():
     # the bound is the longest length whose roots and scalars fit the 2 MiB array
     assert brl.workspace_bytes(brl.OP_NORM, brl.NOALLOC_NORM_MAX_LEN, 0, 0) <= 2 << 20
     assert brl.workspace_bytes(brl.OP_NORM, brl.NOALLOC_NORM_MAX_LEN + 1, 0, 0) > 2 << 20
+
+
+def test_ctypes_structs_match_the_header(tmp_path):
+    """The binding's ctypes mirrors of the ABI structs have the sizes and
+    field offsets the C compiler gives the header's definitions (a mismatch
+    would corrupt every call that passes one)."""
+    import shutil
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    mirrors = {
+        "brl_tuning": brl.Tuning,
+        "brl_reduce_state": brl.ReduceStateC,
+        "brl_adamw_config": brl.AdamWConfig,
+        "brl_adamw_scalars": brl.AdamWScalars,
+        "brl_stream_source": brl._StreamSource,
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "brlsq.h"', "int main(void) {"]
+    for cname, py in mirrors.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", brl_build.INCLUDE, str(src), "-o", str(exe)], check=True, capture_output=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        cname, what, val = line.split()
+        got[(cname, what)] = int(val)
+    for cname, py in mirrors.items():
+        assert got[(cname, "size")] == C.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
