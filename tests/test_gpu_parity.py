@@ -515,7 +515,7 @@ def _replay_gpu(partials_np, R, S, max_norm=1.0, persist=False, tune=None, resid
 @pytest.mark.parametrize("mode", ["plain", "persist", "resident"])
 @pytest.mark.parametrize("R,S,L", [(6, 8, 65536 + 5), (1, 1, 1000), (2, 3, 4097), (3, 2, 333),
                                    (5, 1, 1024), (7, 2, 100), (16, 2, 2048), (6, 8, 3), (6, 11, 4099),
-                                   (3, 64, 257), (2, 65, 130)])
+                                   (3, 64, 257), (2, 65, 130), (1, 4, 1001), (64, 2, 33)])
 def test_replay_parity(R, S, L, mode):
     """Every running sum A_r (but the last, which the fold consumes) and the
     clipped TreeFold, with the partials streamed one call at a time, with each
