@@ -149,7 +149,8 @@ hipError_t launch_quantize(const float* v, int64_t rows, int64_t cols, const flo
 // Only the tail and the W range wait, and only on work of lower ranges whose
 // workgroups never wait: once running, they finish.  Waiters number at most
 // 1 + min(1024, 4 per CU), fewer workgroups than the device holds at once
-// (this kernel fits 8 per CU: 2048 on 256 CUs), so the workgroups they wait for always find room to run even when
+// (this kernel fits 7 per CU, its scalar registers being the limit: 1792 on
+// 256 CUs), so the workgroups they wait for always find room to run even when
 // every waiter is resident; each wait is bounded all the same
 // (kPrepSpinLimit polls, about a second; then the error word records it and
 // the GEMM writes NaN for every output), so every wave exits.  Measured on the MI355X (forward call, QKV / SwiGLU gate+up / down
@@ -317,7 +318,7 @@ hipError_t launch_fwd_prep(PrepArgs a, hipStream_t st) {
     a.P = ceil_div(ceil_div(nW, kBlock), kPrepRunBlocks);
     if (a.P < 1 || a.P > kPrepMaxRoots || a.Mp <= 0 || a.Nvp <= 0 || a.Kp <= 0) return hipErrorInvalidValue;
     // the W range (the waiters) also stays within 4 workgroups per CU of the
-    // stream's device, half of what it holds of this kernel at once, so the
+    // stream's device, of the 7 it holds of this kernel at once, so the
     // bound holds on a device with fewer CUs (a partition of the chip, say)
     int64_t max_w = kPrepMaxWgW;
     hipDevice_t dev = 0;

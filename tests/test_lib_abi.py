@@ -215,6 +215,19 @@ def test_hot_loops_use_plain_mul_and_add():
         n_add = len(re.findall(r"\tv_add_f32", body))
         assert n_mul >= 512 and n_add >= 480, (name, n_mul, n_add)
 
+def test_forward_preparation_waiters_leave_room_for_producers():
+    """fwd_prep_kernel's waiting workgroups (at most 4 per CU, plus the tail)
+    must be fewer than the kernel's workgroups a CU holds at once, so the
+    workgroups they wait for can always run.  A 256-thread workgroup is one
+    wave on each of the 4 SIMDs, so workgroups per CU = the compiler's
+    occupancy figure (waves per SIMD); require at least 5."""
+    text = open([f for f in brl_build.asm_files() if os.path.basename(f).startswith("fwd")][0]).read()
+    body = text.split("_ZN3brl15fwd_prep_kernelENS_8PrepArgsE:")[1]
+    m = re.search(r"; Occupancy: (\d+)", body)
+    assert m, "no occupancy figure after fwd_prep_kernel"
+    assert int(m.group(1)) >= 5, m.group(0)
+
+
 def test_matrix_core_backward_keeps_products_in_vgprs():
     """The matrix-core backward forms products with the K=1 fp32 MFMA and adds
     them with v_add_f32 straight from VGPRs (no accumulator-register copies,
